@@ -1,0 +1,239 @@
+"""CPU oracle for one TSP decoder layer on one rank's share of the work.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import or call this module. The HIP library
+never uses it and shares no code with it.
+
+Everything here is plain, unblocked numpy in float64 (scipy's erf for GELU),
+written from the definitions so that it can be checked by eye.
+
+Sources (the pages describe the method; no code was published):
+  [P2] zubnet.ai news item "Zyphra TSP folds TP+SP onto one GPU axis"
+       (in Hindi). Paragraph 1: one mesh axis of size D carries both weight
+       and token sharding; each GPU keeps 1/D of the weights and 1/D of the
+       tokens; the validated model is a 7B dense decoder (hidden 4096,
+       32 layers, 32 query/KV heads, MLP 4x, bf16) at 128K tokens with D=8.
+       Paragraph 2: for attention, weight shards are broadcast one after
+       another and each GPU applies each to its own tokens, then K and V are
+       all-gathered under a zigzag partition that balances load; for the MLP,
+       weight shards travel round a ring of point-to-point transfers, so the
+       all-reduce of ordinary tensor parallelism disappears.
+       Paragraph 4: the MLP without all-reduce carries over to other setups.
+  [P1] ageofai.tools "Zyphra TSP: 2.6x Faster AI Training Review":
+       TSP merges tensor and sequence parallelism on one GPU axis (What's New).
+
+Readings where the pages are silent (each is restated where it is used):
+  R1 zigzag: the sequence is cut into 2D equal chunks; rank r owns chunks r
+     and 2D-1-r, kept in that order, ascending inside each chunk.
+  R2 attention shards are head groups: shard j holds heads j*H/D..(j+1)*H/D-1
+     of W_Q, W_K, W_V (output rows) and of W_O (input columns).
+  R3 the gathered K/V are full-sequence, all heads, in global position order.
+  R4 causal mask is inclusive (key u is visible to the query at p iff u <= p),
+     softmax scale 1/sqrt(Dh), no bias, no rotary embedding, multi-head (not
+     grouped) attention.
+  R5 the MLP is two matrices with exact (erf) GELU, width F = 4h; MLP shard j
+     holds hidden units j*F/D..(j+1)*F/D-1 (rows of W1, columns of W2).
+  R6 pre-RMSNorm residual block: h1 = x + Attn(RMSNorm(x)),
+     y = h1 + MLP(RMSNorm(h1)); eps = 1e-5; no biases.
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.special import erf as _erf
+
+__all__ = [
+    "zigzag_positions",
+    "zigzag_owner",
+    "rms_norm",
+    "gelu",
+    "causal_attention",
+    "unshard_attention_weights",
+    "unshard_mlp_weights",
+    "mlp",
+    "mlp_shard",
+    "layer_full",
+    "layer_rank",
+]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Token ownership
+# --------------------------------------------------------------------------
+def zigzag_positions(S: int, D: int, r: int) -> np.ndarray:
+    """Global positions of the S/D tokens rank r holds, in local row order.
+
+    [P2] paragraph 2 names a zigzag partition of the sequence for load
+    balance; reading R1 fixes the rule: 2D chunks of C = S/(2D) tokens, rank
+    r holds chunk r followed by chunk 2D-1-r.
+    """
+    if D < 1 or S % (2 * D) != 0 or not (0 <= r < D):
+        raise ValueError("need D >= 1, S divisible by 2D and 0 <= r < D")
+    C = S // (2 * D)
+    pos = []
+    for chunk in (r, 2 * D - 1 - r):
+        for i in range(C):
+            pos.append(chunk * C + i)
+    return np.array(pos, dtype=np.int64)
+
+
+def zigzag_owner(p: int, S: int, D: int):
+    """(rank, local row) that holds global position p under reading R1."""
+    C = S // (2 * D)
+    chunk = p // C
+    if chunk < D:
+        return chunk, p % C
+    return 2 * D - 1 - chunk, C + p % C
+
+
+# --------------------------------------------------------------------------
+# Layer pieces
+# --------------------------------------------------------------------------
+def rms_norm(x, g, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * g (reading R6)."""
+    x = _f64(x)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * _f64(g)
+
+
+def gelu(z) -> np.ndarray:
+    """Exact GELU, z * Phi(z) = z * (1 + erf(z / sqrt 2)) / 2 (reading R5)."""
+    z = _f64(z)
+    return 0.5 * z * (1.0 + _erf(z / np.sqrt(2.0)))
+
+
+def causal_attention(q, k, v, q_pos, scale: float, row_block: int = 256) -> np.ndarray:
+    """Softmax attention of queries at global positions q_pos over K/V.
+
+    q: [n, H, Dh] queries; k, v: [S, H, Dh] full-sequence keys and values in
+    global order (reading R3, the result of the all-gather in [P2] paragraph
+    2); q_pos: [n] global position of each query. For each query t and head,
+    the scores scale * <q, k_u> over keys u <= q_pos[t] (reading R4) go
+    through a softmax that weights the values.
+
+    Rows are taken row_block at a time to bound memory; each row is computed
+    independently and in full, with its own softmax over its whole prefix.
+    """
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    n, H, Dh = q.shape
+    out = np.empty((n, H, Dh), dtype=np.float64)
+    for lo in range(0, n, row_block):
+        hi = min(n, lo + row_block)
+        pos = q_pos[lo:hi]
+        L = int(pos.max()) + 1
+        visible = np.arange(L)[None, :] <= pos[:, None]
+        for hd in range(H):
+            qh = _f64(q[lo:hi, hd, :])
+            kh = _f64(k[:L, hd, :])
+            vh = _f64(v[:L, hd, :])
+            s = scale * (qh @ kh.T)
+            s = np.where(visible, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p = p / p.sum(axis=1, keepdims=True)
+            out[lo:hi, hd, :] = p @ vh
+    return out
+
+
+# --------------------------------------------------------------------------
+# Shards -> unsharded matrices
+# --------------------------------------------------------------------------
+def unshard_attention_weights(wqkv, wo, H: int, Dh: int):
+    """Rebuild W_Q, W_K, W_V [h, h] and W_O [h, h] (out, in) from the D shards.
+
+    Reading R2: shard j's rows are the Q rows, then K rows, then V rows of its
+    head group, so concatenating shard j's Q rows over j in order gives W_Q,
+    and W_O is the concatenation of the shards' columns.
+    """
+    D = len(wqkv)
+    hd = (H // D) * Dh
+    wq = np.concatenate([_f64(w)[0:hd] for w in wqkv], axis=0)
+    wk = np.concatenate([_f64(w)[hd:2 * hd] for w in wqkv], axis=0)
+    wv = np.concatenate([_f64(w)[2 * hd:3 * hd] for w in wqkv], axis=0)
+    w_o = np.concatenate([_f64(w) for w in wo], axis=1)
+    return wq, wk, wv, w_o
+
+
+def unshard_mlp_weights(w1, w2):
+    """Rebuild W1 [F, h] and W2 [h, F] (out, in) from the D shards (reading R5)."""
+    return np.concatenate([_f64(w) for w in w1], axis=0), np.concatenate([_f64(w) for w in w2], axis=1)
+
+
+# --------------------------------------------------------------------------
+# MLP
+# --------------------------------------------------------------------------
+def mlp(x, w1, w2) -> np.ndarray:
+    """Unsharded MLP branch GELU(x W1^T) W2^T from lists of shards (reading R5).
+
+    [P2] paragraphs 2 and 4: the ring applies each shard to the local tokens
+    and sums the contributions without an all-reduce; this is the unsharded
+    quantity that sum must equal.
+    """
+    W1, W2 = unshard_mlp_weights(w1, w2)
+    return gelu(_f64(x) @ W1.T) @ W2.T
+
+
+def mlp_shard(x, w1_j, w2_j) -> np.ndarray:
+    """One shard's contribution GELU(x W1_j^T) W2_j^T (reading R5)."""
+    return gelu(_f64(x) @ _f64(w1_j).T) @ _f64(w2_j).T
+
+
+# --------------------------------------------------------------------------
+# Whole layer
+# --------------------------------------------------------------------------
+def layer_full(x, w: dict, H: int, Dh: int, eps: float, scale: float) -> dict:
+    """Unsharded pre-norm decoder layer over the whole sequence (reading R6).
+
+    x: [S, h] in global order. w: the shard lists wqkv, wo, w1, w2 and gains
+    g_attn, g_mlp. TSP rearranges this computation over ranks and shards but
+    reaches the same values ([P2] paragraphs 1-2), so this is what every rank
+    must reproduce for its own rows. Returns y and the intermediates h1, k, v.
+    """
+    x = _f64(x)
+    S = x.shape[0]
+    wq, wk, wv, w_o = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh)
+    a = rms_norm(x, w["g_attn"], eps)
+    q = (a @ wq.T).reshape(S, H, Dh)
+    k = (a @ wk.T).reshape(S, H, Dh)
+    v = (a @ wv.T).reshape(S, H, Dh)
+    o = causal_attention(q, k, v, np.arange(S), scale)
+    h1 = x + o.reshape(S, H * Dh) @ w_o.T
+    m = rms_norm(h1, w["g_mlp"], eps)
+    y = h1 + mlp(m, w["w1"], w["w2"])
+    return {"y": y, "h1": h1, "q": q, "k": k, "v": v, "o": o}
+
+
+def layer_rank(x_local, w: dict, k_full, v_full, S: int, D: int, r: int,
+               H: int, Dh: int, eps: float, scale: float, rows=None) -> dict:
+    """Rank r's layer output for its S/D local tokens (reading R6).
+
+    x_local: [S/D, h] rank r's tokens in local zigzag order (R1). k_full,
+    v_full: [S, H, Dh] what the all-gather delivers ([P2] paragraph 2); the
+    rows at rank r's own positions are replaced by the K/V this rank computes
+    from x_local, the rest are used as given. rows: optional subset of local
+    rows whose output is wanted (all local rows still produce K/V, since any
+    later query may attend to them). Returns y [len(rows), h] and h1.
+    """
+    x_local = _f64(x_local)
+    n = x_local.shape[0]
+    pos = zigzag_positions(S, D, r)
+    if n != pos.shape[0]:
+        raise ValueError("x_local must hold S/D rows")
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    wq, wk, wv, w_o = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh)
+    a = rms_norm(x_local, w["g_attn"], eps)
+    k_loc = (a @ wk.T).reshape(n, H, Dh)
+    v_loc = (a @ wv.T).reshape(n, H, Dh)
+    k_all = np.array(k_full, dtype=np.float64, copy=True)
+    v_all = np.array(v_full, dtype=np.float64, copy=True)
+    k_all[pos] = k_loc
+    v_all[pos] = v_loc
+    q = (a[rows] @ wq.T).reshape(len(rows), H, Dh)
+    o = causal_attention(q, k_all, v_all, pos[rows], scale)
+    h1 = x_local[rows] + o.reshape(len(rows), H * Dh) @ w_o.T
+    m = rms_norm(h1, w["g_mlp"], eps)
+    y = h1 + mlp(m, w["w1"], w["w2"])
+    return {"y": y, "h1": h1, "pos": pos[rows]}

@@ -1,0 +1,301 @@
+"""Pins for the CPU oracle: each check comes from something other than the
+oracle itself (hand-derived fixtures, textbook values, closed forms,
+invariants, brute-force loops, or an independent library routine)."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([float(t) for t in line.split()])
+    return rows
+
+
+# ---------------------------------------------------------------- zigzag
+def test_zigzag_golden():
+    for row in _load("zigzag_S16_D4.txt"):
+        r = int(row[0])
+        assert oracle.zigzag_positions(16, 4, r).tolist() == [int(t) for t in row[1:]]
+
+
+@pytest.mark.parametrize("S,D", [(16, 4), (1024, 4), (64, 1), (96, 3), (4096, 8)])
+def test_zigzag_permutation_and_equal_work(S, D):
+    allpos = np.concatenate([oracle.zigzag_positions(S, D, r) for r in range(D)])
+    assert sorted(allpos.tolist()) == list(range(S))
+    # causal work of a rank = number of (query, key) pairs with key <= query
+    work = [int((oracle.zigzag_positions(S, D, r) + 1).sum()) for r in range(D)]
+    assert len(set(work)) == 1
+    assert work[0] * D == S * (S + 1) // 2
+
+
+def test_zigzag_d1_identity_and_owner():
+    assert oracle.zigzag_positions(32, 1, 0).tolist() == list(range(32))
+    S, D = 1024, 4
+    for r in range(D):
+        pos = oracle.zigzag_positions(S, D, r)
+        for t, p in enumerate(pos):
+            assert oracle.zigzag_owner(int(p), S, D) == (r, t)
+
+
+def test_zigzag_7b_pairs():
+    S, D = 131072, 8
+    for r in (0, 3, 7):
+        assert int((oracle.zigzag_positions(S, D, r) + 1).sum()) == 1_073_750_016
+
+
+def test_zigzag_rejects_bad_args():
+    for S, D, r in [(10, 4, 0), (16, 4, 4), (16, 4, -1), (16, 0, 0)]:
+        with pytest.raises(ValueError):
+            oracle.zigzag_positions(S, D, r)
+
+
+# ---------------------------------------------------------------- RMSNorm
+def test_rms_norm_closed_forms():
+    c, eps = 3.0, 1e-5
+    x = np.full((2, 8), c)
+    g = np.linspace(0.5, 2.0, 8)
+    y = oracle.rms_norm(x, g, eps)
+    assert np.allclose(y, c / math.sqrt(c * c + eps) * g, rtol=0, atol=1e-15)
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((5, 64))
+    y = oracle.rms_norm(x, np.ones(64), 0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, atol=1e-14)
+    # scale invariance with eps = 0
+    assert np.allclose(oracle.rms_norm(7.0 * x, np.ones(64), 0.0), y, atol=1e-14)
+
+
+def test_rms_norm_vs_torch():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((7, 48))
+    g = 1 + 0.1 * rng.standard_normal(48)
+    ref = F.rms_norm(torch.from_numpy(x), (48,), torch.from_numpy(g), eps=1e-5).numpy()
+    assert np.allclose(oracle.rms_norm(x, g, 1e-5), ref, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- GELU
+def test_gelu_golden():
+    for z, want in _load("gelu_values.txt"):
+        assert abs(float(oracle.gelu(np.array([z]))[0]) - want) <= 1e-15 * max(1.0, abs(want))
+
+
+def test_gelu_vs_math_erf_and_identities():
+    zs = np.linspace(-6, 6, 97)
+    got = oracle.gelu(zs)
+    for z, gz in zip(zs, got):
+        assert abs(gz - z * 0.5 * (1 + math.erf(z / math.sqrt(2)))) < 1e-15
+    assert np.allclose(got - oracle.gelu(-zs), zs, atol=1e-14)  # x*Phi(x) - (-x)*Phi(-x) = x
+    ref = F.gelu(torch.from_numpy(zs), approximate="none").numpy()
+    assert np.allclose(got, ref, atol=1e-15)
+    tanh_form = F.gelu(torch.from_numpy(zs), approximate="tanh").numpy()
+    assert np.abs(got - tanh_form).max() > 1e-4  # the erf form is the one pinned
+
+
+# ---------------------------------------------------------------- attention
+def _brute_attention(q, k, v, q_pos, scale):
+    n, H, Dh = q.shape
+    out = np.zeros((n, H, Dh))
+    for t in range(n):
+        for hd in range(H):
+            scores = []
+            for u in range(int(q_pos[t]) + 1):
+                scores.append(scale * sum(q[t, hd, d] * k[u, hd, d] for d in range(Dh)))
+            m = max(scores)
+            w = [math.exp(s - m) for s in scores]
+            z = sum(w)
+            for d in range(Dh):
+                out[t, hd, d] = sum(w[u] * v[u, hd, d] for u in range(len(w))) / z
+    return out
+
+
+def test_attention_bruteforce_zigzag():
+    rng = np.random.default_rng(2)
+    S, D, H, Dh = 16, 2, 2, 3
+    k = rng.standard_normal((S, H, Dh))
+    v = rng.standard_normal((S, H, Dh))
+    for r in range(D):
+        pos = oracle.zigzag_positions(S, D, r)
+        q = rng.standard_normal((len(pos), H, Dh))
+        got = oracle.causal_attention(q, k, v, pos, 0.7, row_block=3)
+        assert np.allclose(got, _brute_attention(q, k, v, pos, 0.7), atol=1e-13)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(3)
+    S, H, Dh = 12, 3, 4
+    q = rng.standard_normal((S, H, Dh))
+    k = rng.standard_normal((S, H, Dh))
+    v = rng.standard_normal((S, H, Dh))
+    pos = np.arange(S)
+    o = oracle.causal_attention(q, k, v, pos, 0.5)
+    assert np.allclose(o[0], v[0], atol=1e-15)  # the first token sees only itself
+    prefix_mean = np.cumsum(v, axis=0) / (pos + 1)[:, None, None]
+    assert np.allclose(oracle.causal_attention(q, k, v, pos, 0.0), prefix_mean, atol=1e-14)
+    k_same = np.broadcast_to(k[:1], k.shape)
+    assert np.allclose(oracle.causal_attention(q, k_same, v, pos, 0.9), prefix_mean, atol=1e-14)
+
+
+def test_attention_vs_torch_sdpa():
+    rng = np.random.default_rng(4)
+    S, H, Dh = 96, 4, 16
+    q, k, v = (rng.standard_normal((S, H, Dh)) for _ in range(3))
+    scale = 1 / math.sqrt(Dh)
+    got = oracle.causal_attention(q, k, v, np.arange(S), scale, row_block=40)
+    t = lambda a: torch.from_numpy(a).permute(1, 0, 2).contiguous()  # noqa: E731
+    ref = F.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=True, scale=scale)
+    assert np.allclose(got, ref.permute(1, 0, 2).numpy(), atol=1e-13)
+
+
+# ---------------------------------------------------------------- shards
+def _split_attention(wq, wk, wv, wo, D, H, Dh):
+    """Shard layout of the library: head group j's Q, K, V rows; W_O columns."""
+    hd = (H // D) * Dh
+    wqkv = [np.concatenate([wq[j * hd:(j + 1) * hd], wk[j * hd:(j + 1) * hd], wv[j * hd:(j + 1) * hd]]) for j in range(D)]
+    wos = [wo[:, j * hd:(j + 1) * hd] for j in range(D)]
+    return wqkv, wos
+
+
+def _split_mlp(W1, W2, D):
+    f = W1.shape[0] // D
+    return [W1[j * f:(j + 1) * f] for j in range(D)], [W2[:, j * f:(j + 1) * f] for j in range(D)]
+
+
+def test_mlp_vs_torch_and_shard_sum():
+    rng = np.random.default_rng(5)
+    n, h, Fw, D = 9, 16, 64, 4
+    x = rng.standard_normal((n, h))
+    W1 = 0.2 * rng.standard_normal((Fw, h))
+    W2 = 0.2 * rng.standard_normal((h, Fw))
+    w1, w2 = _split_mlp(W1, W2, D)
+    got = oracle.mlp(x, w1, w2)
+    tx = torch.from_numpy(x)
+    ref = F.linear(F.gelu(F.linear(tx, torch.from_numpy(W1))), torch.from_numpy(W2)).numpy()
+    assert np.allclose(got, ref, atol=1e-13)
+    # no all-reduce needed: the shard contributions sum to the unsharded branch,
+    # in any ring order
+    for r in range(D):
+        acc = np.zeros_like(got)
+        for t in range(D):
+            j = (r - t) % D
+            acc += oracle.mlp_shard(x, w1[j], w2[j])
+        assert np.allclose(acc, got, atol=1e-13)
+
+
+def _torch_layer(x, wq, wk, wv, wo, W1, W2, g1, g2, H, Dh, eps, scale):
+    tx = torch.from_numpy(x)
+    S, h = x.shape
+    a = F.rms_norm(tx, (h,), torch.from_numpy(g1), eps=eps)
+    heads = lambda m: F.linear(a, torch.from_numpy(m)).reshape(S, H, Dh).permute(1, 0, 2).contiguous()  # noqa: E731
+    o = F.scaled_dot_product_attention(heads(wq), heads(wk), heads(wv), is_causal=True, scale=scale)
+    h1 = tx + F.linear(o.permute(1, 0, 2).reshape(S, h), torch.from_numpy(wo))
+    m = F.rms_norm(h1, (h,), torch.from_numpy(g2), eps=eps)
+    return (h1 + F.linear(F.gelu(F.linear(m, torch.from_numpy(W1))), torch.from_numpy(W2))).numpy()
+
+
+def _tiny_layer(seed, S=64, D=4, H=4, Dh=8, Fw=128):
+    rng = np.random.default_rng(seed)
+    h = H * Dh
+    mats = dict(
+        wq=0.2 * rng.standard_normal((h, h)), wk=0.2 * rng.standard_normal((h, h)),
+        wv=0.2 * rng.standard_normal((h, h)), wo=0.2 * rng.standard_normal((h, h)),
+        W1=0.2 * rng.standard_normal((Fw, h)), W2=0.2 * rng.standard_normal((h, Fw)),
+        g1=1 + 0.1 * rng.standard_normal(h), g2=1 + 0.1 * rng.standard_normal(h))
+    wqkv, wos = _split_attention(mats["wq"], mats["wk"], mats["wv"], mats["wo"], D, H, Dh)
+    w1, w2 = _split_mlp(mats["W1"], mats["W2"], D)
+    w = dict(wqkv=wqkv, wo=wos, w1=w1, w2=w2, g_attn=mats["g1"], g_mlp=mats["g2"])
+    x = rng.standard_normal((S, h))
+    return x, w, mats
+
+
+def test_layer_full_vs_torch():
+    H, Dh, eps = 4, 8, 1e-5
+    scale = 1 / math.sqrt(Dh)
+    x, w, m = _tiny_layer(6, H=H, Dh=Dh)
+    got = oracle.layer_full(x, w, H, Dh, eps, scale)["y"]
+    ref = _torch_layer(x, m["wq"], m["wk"], m["wv"], m["wo"], m["W1"], m["W2"], m["g1"], m["g2"], H, Dh, eps, scale)
+    assert np.allclose(got, ref, atol=1e-12)
+
+
+def test_layer_rank_rows_equal_unsharded_layer():
+    S, D, H, Dh, eps = 64, 4, 4, 8, 1e-5
+    scale = 1 / math.sqrt(Dh)
+    x, w, _ = _tiny_layer(7, S=S, D=D, H=H, Dh=Dh)
+    full = oracle.layer_full(x, w, H, Dh, eps, scale)
+    for r in range(D):
+        pos = oracle.zigzag_positions(S, D, r)
+        # remote rows: garbage except what the all-gather would really carry
+        k_remote = full["k"].copy()
+        v_remote = full["v"].copy()
+        k_remote[pos] = 1e3
+        v_remote[pos] = -1e3
+        out = oracle.layer_rank(x[pos], w, k_remote, v_remote, S, D, r, H, Dh, eps, scale)
+        assert np.allclose(out["y"], full["y"][pos], atol=1e-12)
+        sub = oracle.layer_rank(x[pos], w, k_remote, v_remote, S, D, r, H, Dh, eps, scale, rows=[0, 5, len(pos) - 1])
+        assert np.allclose(sub["y"], full["y"][pos][[0, 5, len(pos) - 1]], atol=1e-12)
+
+
+def test_layer_rank_d1_is_plain_layer():
+    S, H, Dh, eps = 32, 2, 8, 1e-5
+    x, w, _ = _tiny_layer(8, S=S, D=1, H=H, Dh=Dh, Fw=64)
+    full = oracle.layer_full(x, w, H, Dh, eps, 0.3)
+    junk = np.zeros((S, H, Dh))
+    out = oracle.layer_rank(x, w, junk, junk, S, 1, 0, H, Dh, eps, 0.3)
+    assert np.allclose(out["y"], full["y"], atol=1e-12)
+
+
+# ---------------------------------------------------------------- planted mistakes
+def test_planted_mistakes_are_caught(monkeypatch):
+    """Each pin above fails when a plausible slip is planted in the oracle."""
+    rng = np.random.default_rng(9)
+    S, H, Dh = 10, 2, 3
+    q, k, v = (rng.standard_normal((S, H, Dh)) for _ in range(3))
+    pos = np.arange(S)
+    good = _brute_attention(q, k, v, pos, 0.6)
+    # exclusive instead of inclusive mask
+    bad = oracle.causal_attention(q, k, v, pos - 1 + (pos == 0), 0.6)
+    assert not np.allclose(bad, good, atol=1e-6)
+    # transposed q/k roles inside a head (wrong operand)
+    bad2 = oracle.causal_attention(k, q, v, pos, 0.6)
+    assert not np.allclose(bad2, good, atol=1e-6)
+    # a tanh GELU would miss the golden values
+    z = np.array([r[0] for r in _load("gelu_values.txt")])
+    want = np.array([r[1] for r in _load("gelu_values.txt")])
+    tanh_gelu = 0.5 * z * (1 + np.tanh(math.sqrt(2 / math.pi) * (z + 0.044715 * z ** 3)))
+    assert np.abs(tanh_gelu - want).max() > 1e-5
+    # a K/V layout slip (K and V rows swapped within a shard) breaks the layer pin
+    H2, Dh2, eps = 4, 8, 1e-5
+    x, w, m = _tiny_layer(6, H=H2, Dh=Dh2)
+    hd = (H2 // 4) * Dh2
+    w_bad = dict(w)
+    w_bad["wqkv"] = [np.concatenate([s[:hd], s[2 * hd:], s[hd:2 * hd]]) for s in w["wqkv"]]
+    ref = _torch_layer(x, m["wq"], m["wk"], m["wv"], m["wo"], m["W1"], m["W2"], m["g1"], m["g2"], H2, Dh2, eps, 1 / math.sqrt(Dh2))
+    assert not np.allclose(oracle.layer_full(x, w_bad, H2, Dh2, eps, 1 / math.sqrt(Dh2))["y"], ref, atol=1e-6)
+
+
+# ---------------------------------------------------------------- synth
+def test_synth_deterministic_and_bf16_rounding():
+    a = synth.normal((3, 5), 1, 7)
+    b = synth.normal((3, 5), 1, 7)
+    assert np.array_equal(a, b)
+    assert not np.array_equal(a, synth.normal((3, 5), 1, 8))
+    # RNE to bf16: ties go to even, widening is exact
+    vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 65504.0], dtype=np.float32)
+    bits = synth.f32_to_bf16(vals)
+    back = synth.bf16_to_f32(bits)
+    assert back.tolist() == [1.0, 1.0, 1.0 + 2 ** -6, -2.5, 65536.0]
+    big = synth.normal(((1 << 23) + 5,), 3, 1)  # several chunks
+    assert np.array_equal(big[: 1 << 22], synth.normal((1 << 22,), 3, 1))  # chunked streams
+    assert abs(float(big.mean())) < 2e-3 and abs(float(big.std()) - 1) < 2e-3
