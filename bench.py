@@ -1,0 +1,257 @@
+"""Throughput of the rank-local TSP layer forward on one MI355X.
+
+Default workload: one decoder layer of the 7B dense model the TSP pages
+validate (hidden 4096, 32 heads of 128, MLP 16384, bf16) at S = 131072 tokens
+on a folded axis of D = 8, rank 0: 16384 local zigzag tokens, all 8 weight
+shards applied in delivery order, attention against the full gathered K/V
+(the other ranks' rows are seeded N(0,1) inputs). One step = one
+tsp_layer_fwd call; inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line: local tokens/s, ms per step, the fraction of bf16 MFMA
+peak over the layer, the roofline entry of the dominant kernel (attention,
+timed per launch with HIP events on the launching stream) and the CPU oracle
+timed on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload layer|mlp|attn]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "local tokens/s per GPU, 7B TSP layer fwd D=8 S=128K; % bf16 MFMA peak"
+PEAK_BF16 = 2.5e15   # MI355X dense bf16/fp16 MFMA, flop/s
+PEAK_HBM = 8.0e12    # bytes/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attn_pairs(S, D, r):
+    """Unmasked (query, key) pairs of rank r: sum over local rows of pos + 1."""
+    C = S // (2 * D)
+    pos0 = r * C + np.arange(C, dtype=np.int64)
+    pos1 = (2 * D - 1 - r) * C + np.arange(C, dtype=np.int64)
+    return int((pos0 + 1).sum() + (pos1 + 1).sum())
+
+
+def layer_flops(sh, r):
+    N = sh.N
+    qkv = 2 * N * sh.h * 3 * sh.h
+    attn = 4 * sh.Dh * sh.H * attn_pairs(sh.S, sh.D, r)
+    outp = 2 * N * sh.h * sh.h
+    mlp = 2 * 2 * N * sh.h * sh.F
+    return {"qkv": qkv, "attention": attn, "outproj": outp, "mlp": mlp, "total": qkv + attn + outp + mlp}
+
+
+def traffic_from_profile(kernel_src: str, name: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if the
+    kernel source is unchanged since the counters were taken; else None."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = open(kernel_src, "rb").read()
+    if fields.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:  # pragma: no cover
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", choices=["layer", "mlp", "attn"], default="layer")
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--cpu-rows", type=int, default=384, help="rows in the CPU oracle sample (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        sys.exit(f"bench.py: only --gpus 1 is supported; this build measures one rank's share on one GPU "
+                 f"(asked for {args.gpus}).")
+
+    import torch
+
+    import synth
+    import tsp_rank_local_amd as tsp
+
+    assert torch.cuda.is_available(), "needs a GPU"
+    tsp.lib()
+    sh = synth.SEVEN_B
+    r = args.rank
+    N = sh.N
+    seed = 4
+    t_gen = time.perf_counter()
+    log(f"generating inputs: S={sh.S} D={sh.D} r={r} h={sh.h} H={sh.H} Dh={sh.Dh} F={sh.F}")
+    shape = tsp.make_shape(sh.S, sh.D, r, sh.h, sh.H, sh.Dh, sh.F, eps=sh.eps, dtype="bf16")
+    stream = torch.cuda.current_stream()
+    flops = layer_flops(sh, r)
+
+    if args.workload in ("layer", "mlp"):
+        w = synth.layer_weights(sh, seed=seed)
+        wd = {k: ([tsp.to_device(a, "bf16") for a in v] if isinstance(v, list) else tsp.to_device(v, "bf16"))
+              for k, v in w.items()}
+    if args.workload == "layer":
+        x = synth.activations(N, sh.h, seed=seed)
+        k_rem, v_rem = synth.remote_kv(sh, seed=seed)
+        xd = tsp.to_device(x, "f32")
+        kf, vf = tsp.to_device(k_rem, "bf16"), tsp.to_device(v_rem, "bf16")
+        y = torch.empty((N, sh.h), dtype=torch.float32, device="cuda")
+        ws = torch.empty(tsp.workspace_size(shape, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
+
+        def step():
+            tsp.tsp_layer_fwd(shape, wd, xd, kf, vf, y, tsp.TSP_PHASE_ALL, ws)
+        step_flops = flops["total"]
+        workload = (f"tsp_layer_fwd: one 7B dense decoder layer (h=4096, 32x128 heads, FFN 16384, bf16) on rank {r} "
+                    f"of D=8 at S=131072, 16384 local zigzag tokens")
+    elif args.workload == "mlp":
+        x = synth.activations(N, sh.h, seed=2, dtype="bf16")
+        xd = tsp.to_device(x, "bf16")
+        y = torch.empty((N, sh.h), dtype=torch.float32, device="cuda")
+        ws = torch.empty(tsp.workspace_size(shape, tsp.TSP_WS_MLP), dtype=torch.uint8, device="cuda")
+
+        def step():
+            tsp.tsp_mlp_ring(shape, xd, wd["w1"], wd["w2"], None, y, ws)
+        step_flops = flops["mlp"]
+        workload = "tsp_mlp_ring: 7B MLP ring, 16384x4096 bf16 local X, D=8 shards of 4096x2048"
+    else:
+        q = synth.attn_queries(sh, seed=3)
+        k_rem, v_rem = synth.remote_kv(sh, seed=3)
+        qd = tsp.to_device(q, "bf16")
+        kf, vf = tsp.to_device(k_rem, "bf16"), tsp.to_device(v_rem, "bf16")
+        o = torch.empty((N, sh.H, sh.Dh), dtype=torch.float32, device="cuda")
+
+        def step():
+            tsp.tsp_zigzag_attn(shape, qd, kf, vf, o, tsp.TSP_F32)
+        step_flops = flops["attention"]
+        workload = f"tsp_zigzag_attn: 32x128 heads, S=131072, 16384 zigzag queries of rank {r} of D=8"
+    torch.cuda.synchronize()
+    log(f"inputs resident in HBM ({time.perf_counter() - t_gen:.1f} s); warmup {args.warmup}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done; timing {args.steps} steps")
+
+    tsp.profile_reset()
+    tsp.profile_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tsp.profile_enable(False)
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    kernels = {}
+    for name in tsp.KERNEL_CLASSES:
+        ms, n = tsp.profile_read(name)
+        if n:
+            kernels[name] = {"ms_per_launch": ms / n, "launches_per_step": n / args.steps}
+    log(f"timed: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
+
+    tokens_per_s = N / (ms_step * 1e-3)
+    # dominant kernel: attention (73% of the layer's algorithmic flops)
+    roofline = None
+    if "attention" in kernels:
+        t_attn = kernels["attention"]["ms_per_launch"] * 1e-3
+        achieved = flops["attention"] / t_attn / 1e12
+        roofline = {"kernel": "attn_bf16_kernel<128>", "bound": "mfma", "achieved": achieved,
+                    "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_BF16,
+                    "traffic": traffic_from_profile(os.path.join(ROOT, "tsp_rank_local_amd", "csrc", "attention.hip"),
+                                                    "attention_7b")}
+    elif "mlp_up" in kernels:
+        t_up = kernels["mlp_up"]["ms_per_launch"] * 1e-3
+        f_up = 2 * N * sh.h * (sh.F // sh.D)
+        achieved = f_up / t_up / 1e12
+        roofline = {"kernel": "gemm_bf16_kernel<EpiGelu>", "bound": "mfma", "achieved": achieved,
+                    "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_BF16, "traffic": None}
+
+    cpu = None
+    if args.cpu_rows > 0 and args.workload == "layer":
+        cpu = cpu_baseline(sh, r, x, w, k_rem, v_rem, args.cpu_rows)
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload, "S": sh.S, "D": sh.D, "r": r, "h": sh.h, "H": sh.H, "Dh": sh.Dh,
+                   "F": sh.F, "local_tokens": N, "parallelism": "one rank of a D=8 folded TP+SP axis"},
+        "pct_bf16_mfma_peak": 100.0 * step_flops / (ms_step * 1e-3) / PEAK_BF16,
+        "algorithmic_tflop_per_step": step_flops / 1e12,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(sh, r, x, w, k_rem, v_rem, m):
+    """Time the fp64 oracle on m evenly strided local rows of the same layer:
+    each row's RMSNorm, Q/K/V projection, causal attention over its prefix of
+    the gathered K/V, output projection, RMSNorm and MLP. The rate scales
+    linearly with rows (every row's work is independent once K/V are
+    gathered), so tokens/s = m / t."""
+    import oracle
+    import synth
+
+    log(f"cpu baseline: oracle on {m} of {sh.N} local rows")
+    w64 = {k: ([synth.as_f32(a, "bf16").astype(np.float64) for a in v] if isinstance(v, list)
+               else synth.as_f32(v, "bf16").astype(np.float64)) for k, v in w.items()}
+    k32, v32 = synth.as_f32(k_rem, "bf16"), synth.as_f32(v_rem, "bf16")
+    rows = np.linspace(0, sh.N - 1, m).round().astype(np.int64)
+    pos = oracle.zigzag_positions(sh.S, sh.D, r)[rows]
+    t0 = time.perf_counter()
+    oracle.local_kv(x[rows], w64, sh.H, sh.Dh, sh.eps)
+    oracle.layer_rows(x[rows], pos, w64, k32, v32, sh.H, sh.Dh, sh.eps, sh.scale)
+    t = time.perf_counter() - t0
+    log(f"cpu baseline: {t:.1f} s")
+    return {"value": m / t, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{m} evenly strided local rows of the same layer (per-row Q/K/V projection, causal attention "
+                      f"over the gathered K/V prefix, output projection, MLP) in numpy float64; {t:.1f} s; "
+                      f"BLAS threads as cores, exp/erf single-threaded"}
+
+
+if __name__ == "__main__":
+    main()

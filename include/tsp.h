@@ -1,0 +1,199 @@
+/*
+ * tsp.h - C ABI of the rank-local TSP decoder-layer forward for MI355X (gfx950).
+ *
+ * TSP ("folded" tensor + sequence parallelism) puts weight sharding and token
+ * sharding on one device-mesh axis of size D: every rank keeps 1/D of each
+ * weight matrix and 1/D of the sequence tokens (zubnet.ai news item "Zyphra
+ * TSP folds TP+SP onto one GPU axis", paragraph 1). For attention the weight
+ * shards are broadcast one after another and each rank applies every shard to
+ * its own tokens, after which K and V are all-gathered under a zigzag
+ * partition; for the MLP the weight shards circulate round a ring of
+ * point-to-point transfers and each rank sums the shard contributions itself,
+ * with no all-reduce (same page, paragraph 2; paragraph 4 notes that this MLP
+ * scheme carries over to other setups).
+ *
+ * This library computes ONE rank's share of that forward pass on one GPU.
+ * The shards that the broadcasts and the ring would deliver are passed as
+ * arrays of D device pointers, and the K/V rows the all-gather would deliver
+ * are caller-filled rows of full-sequence buffers. Nothing is communicated.
+ *
+ * Readings taken where the pages are silent:
+ *  - zigzag: the sequence is cut into 2D chunks of C = S/(2D) tokens; rank r
+ *    holds chunk r then chunk 2D-1-r, ascending inside each chunk, so local
+ *    row t sits at global position  r*C + t  (t < C)  or  (2D-1-r)*C + t - C.
+ *  - attention shard j is head group j: heads j*H/D .. (j+1)*H/D-1.
+ *  - causal mask is inclusive (key u visible to query p iff u <= p); no bias,
+ *    no rotary embedding; multi-head attention with H query and H K/V heads.
+ *  - pre-RMSNorm block, eps from the shape: h1 = x + Attn(RMSNorm(x) g_attn),
+ *    y = h1 + GELU(RMSNorm(h1) g_mlp W1^T) W2^T, exact (erf) GELU, no biases.
+ *  - delivery order: attention shards j = 0..D-1 (broadcast roots in turn);
+ *    MLP shard at ring step t is j = (r - t) mod D.
+ *
+ * Conventions for every entry point:
+ *  - Tensor arguments are DEVICE pointers unless marked (host). Row-major,
+ *    innermost index last; every tensor pointer must be 16-byte aligned.
+ *  - 'stream' is a hipStream_t passed as void* (NULL = default stream). All
+ *    work is enqueued on it asynchronously; the call returns before it runs.
+ *  - The caller owns every buffer; the library allocates no device memory and
+ *    keeps no pointer after it returns. Buffers must stay valid until the
+ *    enqueued work has finished.
+ *  - dtype TSP_BF16: weights, gains, x of tsp_mlp_ring, Q/K/V, O and the MLP
+ *    hidden activations are bf16; the residual stream x/h1/y of the layer is
+ *    fp32; every product accumulates in fp32. In attention the probabilities
+ *    and V enter the P.V product as fp16 (so |V| must stay below 65504).
+ *    dtype TSP_F32: everything is fp32.
+ *  - Errors: all arguments are checked on the host before anything is
+ *    enqueued. On failure nothing is enqueued, the status is returned and
+ *    tsp_last_error() describes the problem (thread-local). TSP_ERR_HIP means
+ *    a launch was rejected by the runtime; faults inside kernels surface at
+ *    the caller's next stream synchronisation.
+ *  - Results are deterministic: identical inputs give identical bits.
+ */
+#ifndef TSP_H
+#define TSP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TSP_OK = 0,
+  TSP_ERR_INVALID_ARG = 1, /* null/misaligned pointer, inconsistent shape, overlap */
+  TSP_ERR_UNSUPPORTED = 2, /* valid but not handled: Dh not 64/128, widths not multiples of 64 */
+  TSP_ERR_WORKSPACE = 3,   /* ws_bytes below tsp_workspace_size() */
+  TSP_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+} tsp_status;
+
+typedef enum { TSP_F32 = 0, TSP_BF16 = 1 } tsp_dtype;
+
+/* Sizes of one layer on the folded axis.
+ *  S  total sequence length (the K/V all-gather covers S rows), S < 2^31
+ *  D  axis size (number of ranks / shards), 1 <= D <= TSP_MAX_D, S % (2D) == 0
+ *  r  this rank, 0 <= r < D
+ *  h  hidden width, h == H*Dh;  H heads (H % D == 0 for the layer);  Dh 64 or 128
+ *  F  MLP width, F % D == 0
+ *  eps   RMSNorm epsilon (>= 0)
+ *  scale softmax scale applied to q.k (finite, >= 0; usually 1/sqrt(Dh))
+ *  dtype tsp_dtype of weights and activations (see conventions)
+ * Local token count N = S/D. Widths used as GEMM dimensions (h, F/D and
+ * 3h/D, h/D) must be multiples of 64. */
+typedef struct {
+  int64_t S;
+  int32_t D, r, h, H, Dh, F;
+  float eps, scale;
+  int32_t dtype;
+} tsp_shape;
+
+#define TSP_MAX_D 64
+
+/* One layer's weights. The four shard arrays are (host) arrays of D device
+ * pointers indexed by SHARD id j (not by delivery step); matrices are stored
+ * (out, in), so every product reads its operands along the contiguous axis.
+ *  g_attn, g_mlp: [h] RMSNorm gains (dtype).
+ *  wqkv[j]: [3h/D][h]  rows: the Q rows of head group j, then its K rows, then
+ *           its V rows, each head-major (head, then feature within the head).
+ *  wo[j]:   [h][h/D]   the columns of W_O that read head group j.
+ *  w1[j]:   [F/D][h]   rows j*F/D.. of W1.
+ *  w2[j]:   [h][F/D]   columns j*F/D.. of W2. */
+typedef struct {
+  const void *g_attn;
+  const void *g_mlp;
+  const void *const *wqkv;
+  const void *const *wo;
+  const void *const *w1;
+  const void *const *w2;
+} tsp_layer_weights;
+
+/* Phases of tsp_layer_fwd, for emulating the K/V all-gather of several ranks
+ * on one GPU: PHASE_KV runs RMSNorm-1 and the QKV shards, writes this rank's
+ * K/V rows into k_full/v_full and keeps Q in the workspace; PHASE_REST runs
+ * attention, the output projection and the MLP ring from that workspace. */
+enum { TSP_PHASE_KV = 1, TSP_PHASE_REST = 2, TSP_PHASE_ALL = 3 };
+
+/* Workspace kinds for tsp_workspace_size. */
+enum { TSP_WS_MLP = 0, TSP_WS_LAYER = 1 };
+
+/* Kernel classes for the optional launch timing. */
+enum {
+  TSP_K_RMSNORM = 0,
+  TSP_K_QKV = 1,
+  TSP_K_ATTN = 2,
+  TSP_K_OUTPROJ = 3,
+  TSP_K_MLP_UP = 4,
+  TSP_K_MLP_DOWN = 5,
+  TSP_K_ZIGZAG = 6,
+  TSP_K_COUNT = 7
+};
+
+/* Static text for a status code. */
+const char *tsp_status_string(int status);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char *tsp_last_error(void);
+
+/* ABI version of this header (bumped on incompatible change). */
+int tsp_abi_version(void);
+
+/* Bytes of scratch the call 'which' (TSP_WS_MLP for tsp_mlp_ring,
+ * TSP_WS_LAYER for tsp_layer_fwd) needs for this shape. */
+tsp_status tsp_workspace_size(const tsp_shape *shape, int which, size_t *bytes);
+
+/* Zigzag token ownership (reading above; the pages name a zigzag partition
+ * for load balance, paragraph 2): pos[t] = global position of local row t,
+ * t < S/D. _host fills a (host) array; the other form launches a kernel that
+ * fills a device int32 array on 'stream'. Both give identical values. */
+tsp_status tsp_zigzag_index_host(int64_t S, int32_t D, int32_t r, int32_t *pos);
+tsp_status tsp_zigzag_index(int64_t S, int32_t D, int32_t r, int32_t *pos, void *stream);
+
+/* Causal attention of rank r's local queries against the gathered K/V
+ * (paragraph 2: K/V are all-gathered, so every rank sees the full sequence).
+ *  q: [S/D][H][Dh] local rows in zigzag order (dtype)
+ *  k, v: [S][H][Dh] all positions in global order (dtype)
+ *  o: [S/D][H][Dh] output (o_dtype: TSP_F32, or TSP_BF16 when dtype is bf16)
+ * o[t][hd] = sum_{u <= pos[t]} softmax_u(scale * q[t][hd].k[u][hd]) v[u][hd].
+ * Uses S, D, r, H, Dh, scale and dtype of the shape. */
+tsp_status tsp_zigzag_attn(const tsp_shape *shape, const void *q, const void *k, const void *v,
+                           void *o, int32_t o_dtype, void *stream);
+
+/* The MLP ring on rank r (paragraph 2: shards circulate on a ring and every
+ * rank sums their contributions itself, with no all-reduce):
+ *   y = residual + sum over steps t = 0..D-1 of GELU(x W1_j^T) W2_j^T,
+ *   j = (r - t) mod D, accumulated into y in fp32 in that order.
+ *  x: [S/D][h] (dtype); w1, w2: (host) arrays of D device pointers, shard
+ *  layout as in tsp_layer_weights; residual: [S/D][h] fp32 or NULL (then
+ *  zero); it may equal y. y: [S/D][h] fp32, fully written.
+ *  ws: device scratch of at least tsp_workspace_size(TSP_WS_MLP) bytes. */
+tsp_status tsp_mlp_ring(const tsp_shape *shape, const void *x, const void *const *w1,
+                        const void *const *w2, const float *residual, float *y, void *ws,
+                        size_t ws_bytes, void *stream);
+
+/* One decoder layer forward on rank r's S/D tokens.
+ *  x: [S/D][h] fp32, local rows in zigzag order.
+ *  k_full, v_full: [S][H][Dh] (dtype). The rows at rank r's own positions are
+ *    written by PHASE_KV; every other row must hold what the all-gather would
+ *    deliver (the other ranks' K/V) before PHASE_REST runs.
+ *  y: [S/D][h] fp32 output, fully written by PHASE_REST.
+ *  phases: TSP_PHASE_KV, TSP_PHASE_REST or TSP_PHASE_ALL; PHASE_REST must use
+ *    the same ws as the PHASE_KV call before it.
+ *  ws: device scratch of at least tsp_workspace_size(TSP_WS_LAYER) bytes.
+ * y must not overlap x, k_full, v_full or ws. */
+tsp_status tsp_layer_fwd(const tsp_shape *shape, const tsp_layer_weights *w, const float *x,
+                         void *k_full, void *v_full, float *y, unsigned phases, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/* Optional launch timing. When enabled, every kernel the library enqueues is
+ * bracketed by HIP events recorded on the same stream; tsp_profile_read
+ * synchronises on the recorded events and returns the summed duration (ms)
+ * and number of launches for one kernel class since the last reset. Not
+ * thread-safe; meant for benchmarks. */
+void tsp_profile_enable(int on);
+void tsp_profile_reset(void);
+tsp_status tsp_profile_read(int kernel_class, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TSP_H */

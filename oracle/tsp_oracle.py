@@ -52,6 +52,8 @@ __all__ = [
     "mlp",
     "mlp_shard",
     "layer_full",
+    "layer_rows",
+    "local_kv",
     "layer_rank",
 ]
 
@@ -206,6 +208,35 @@ def layer_full(x, w: dict, H: int, Dh: int, eps: float, scale: float) -> dict:
     return {"y": y, "h1": h1, "q": q, "k": k, "v": v, "o": o}
 
 
+def layer_rows(x_rows, pos_rows, w: dict, k_all, v_all, H: int, Dh: int, eps: float, scale: float) -> dict:
+    """Layer output for given token rows once the full K/V are gathered (R6).
+
+    x_rows: [m, h] tokens, pos_rows: [m] their global positions, k_all, v_all:
+    [S, H, Dh] the complete gathered K/V (including these tokens' own rows).
+    Every row is independent of the others here: RMSNorm, its query, its
+    causal attention, the output projection, RMSNorm and the MLP.
+    """
+    x_rows = _f64(x_rows)
+    m = x_rows.shape[0]
+    wq, _, _, w_o = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh)
+    a = rms_norm(x_rows, w["g_attn"], eps)
+    q = (a @ wq.T).reshape(m, H, Dh)
+    o = causal_attention(q, k_all, v_all, pos_rows, scale)
+    h1 = x_rows + o.reshape(m, H * Dh) @ w_o.T
+    mm = rms_norm(h1, w["g_mlp"], eps)
+    y = h1 + mlp(mm, w["w1"], w["w2"])
+    return {"y": y, "h1": h1}
+
+
+def local_kv(x_local, w: dict, H: int, Dh: int, eps: float):
+    """K and V [n, H, Dh] of a rank's own tokens (R2, R6)."""
+    x_local = _f64(x_local)
+    n = x_local.shape[0]
+    _, wk, wv, _ = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh)
+    a = rms_norm(x_local, w["g_attn"], eps)
+    return (a @ wk.T).reshape(n, H, Dh), (a @ wv.T).reshape(n, H, Dh)
+
+
 def layer_rank(x_local, w: dict, k_full, v_full, S: int, D: int, r: int,
                H: int, Dh: int, eps: float, scale: float, rows=None) -> dict:
     """Rank r's layer output for its S/D local tokens (reading R6).
@@ -223,17 +254,11 @@ def layer_rank(x_local, w: dict, k_full, v_full, S: int, D: int, r: int,
     if n != pos.shape[0]:
         raise ValueError("x_local must hold S/D rows")
     rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
-    wq, wk, wv, w_o = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh)
-    a = rms_norm(x_local, w["g_attn"], eps)
-    k_loc = (a @ wk.T).reshape(n, H, Dh)
-    v_loc = (a @ wv.T).reshape(n, H, Dh)
+    k_loc, v_loc = local_kv(x_local, w, H, Dh, eps)
     k_all = np.array(k_full, dtype=np.float64, copy=True)
     v_all = np.array(v_full, dtype=np.float64, copy=True)
     k_all[pos] = k_loc
     v_all[pos] = v_loc
-    q = (a[rows] @ wq.T).reshape(len(rows), H, Dh)
-    o = causal_attention(q, k_all, v_all, pos[rows], scale)
-    h1 = x_local[rows] + o.reshape(len(rows), H * Dh) @ w_o.T
-    m = rms_norm(h1, w["g_mlp"], eps)
-    y = h1 + mlp(m, w["w1"], w["w2"])
-    return {"y": y, "h1": h1, "pos": pos[rows]}
+    out = layer_rows(x_local[rows], pos[rows], w, k_all, v_all, H, Dh, eps, scale)
+    out["pos"] = pos[rows]
+    return out

@@ -1,0 +1,147 @@
+"""Host-only checks of the C ABI: the library loads, exports what include/tsp.h
+declares, the host zigzag map matches the oracle bit for bit, and every
+argument error is reported before anything is enqueued (no GPU needed: none
+of these calls reaches a launch)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import tsp_rank_local_amd as tsp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "tsp.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tsp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = tsp.lib()
+    declared = _header_functions()
+    assert declared == sorted(tsp.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.tsp_abi_version() == 1
+
+
+def test_status_strings():
+    L = tsp.lib()
+    assert L.tsp_status_string(0) == b"ok"
+    assert L.tsp_status_string(3) == b"workspace too small"
+    assert L.tsp_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("S,D", [(16, 4), (1024, 4), (64, 1), (96, 3), (131072, 8), (2400, 4)])
+def test_zigzag_host_matches_oracle(S, D):
+    for r in range(D):
+        got = tsp.tsp_zigzag_index_host(S, D, r)
+        assert got.dtype == np.int32
+        assert np.array_equal(got.astype(np.int64), oracle.zigzag_positions(S, D, r))
+
+
+def _shape(**kw):
+    base = dict(S=1024, D=4, r=0, h=256, H=4, Dh=64, F=1024, eps=1e-5, scale=0.125, dtype="f32")
+    base.update(kw)
+    return tsp.make_shape(**base)
+
+
+def test_workspace_sizes():
+    s = _shape(dtype="bf16")
+    N, h, fd = 256, 256, 256
+    assert tsp.workspace_size(s, tsp.TSP_WS_MLP) == N * fd * 2
+    assert tsp.workspace_size(s, tsp.TSP_WS_LAYER) == 2 * N * h * 2 + N * fd * 2
+    s7 = tsp.make_shape(131072, 8, 0, 4096, 32, 128, 16384, dtype="bf16")
+    assert tsp.workspace_size(s7, tsp.TSP_WS_LAYER) == 2 * 16384 * 4096 * 2 + 16384 * 2048 * 2
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=1020), tsp.TSP_ERR_INVALID_ARG),          # S not a multiple of 2D
+    (dict(r=4), tsp.TSP_ERR_INVALID_ARG),             # r out of range
+    (dict(D=0), tsp.TSP_ERR_INVALID_ARG),
+    (dict(D=65, S=130), tsp.TSP_ERR_INVALID_ARG),     # D above the limit
+    (dict(Dh=32, h=128), tsp.TSP_ERR_UNSUPPORTED),
+    (dict(h=512), tsp.TSP_ERR_INVALID_ARG),           # h != H*Dh
+    (dict(H=3, h=192), tsp.TSP_ERR_INVALID_ARG),      # H % D
+    (dict(F=1002), tsp.TSP_ERR_INVALID_ARG),          # F % D
+    (dict(F=4 * 96), tsp.TSP_ERR_UNSUPPORTED),        # F/D not a multiple of 64
+    (dict(dtype=7), tsp.TSP_ERR_INVALID_ARG),
+    (dict(eps=-1.0), tsp.TSP_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), tsp.TSP_ERR_INVALID_ARG),
+])
+def test_shape_errors(kw, code):
+    with pytest.raises(tsp.TspError) as ei:
+        tsp.workspace_size(_shape(**kw), tsp.TSP_WS_LAYER)
+    assert ei.value.status == code
+    assert tsp.lib().tsp_last_error()  # a message explains it
+
+
+FAKE = 1 << 40  # a 16-byte aligned address that is never dereferenced
+
+
+def test_pointer_errors_enqueue_nothing():
+    s = _shape()
+    # null / misaligned pointers on attention
+    for q, code in [(None, tsp.TSP_ERR_INVALID_ARG), (FAKE + 4, tsp.TSP_ERR_INVALID_ARG)]:
+        with pytest.raises(tsp.TspError) as ei:
+            tsp.tsp_zigzag_attn(s, q, FAKE, FAKE + (1 << 30), FAKE + (2 << 30), stream=0)
+        assert ei.value.status == code
+    # output overlapping an input
+    with pytest.raises(tsp.TspError) as ei:
+        tsp.tsp_zigzag_attn(s, FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (1 << 30) + 4096, stream=0)
+    assert ei.value.status == tsp.TSP_ERR_INVALID_ARG and b"overlap" in tsp.lib().tsp_last_error()
+    # fp32 inputs with a bf16 output
+    with pytest.raises(tsp.TspError):
+        tsp.tsp_zigzag_attn(s, FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), tsp.TSP_BF16, stream=0)
+
+
+def test_mlp_errors():
+    s = _shape()
+    w = [FAKE + (i << 24) for i in range(4)]
+    need = tsp.workspace_size(s, tsp.TSP_WS_MLP)
+    with pytest.raises(tsp.TspError) as ei:  # workspace too small
+        tsp.tsp_mlp_ring(s, FAKE + (1 << 32), w, w, None, FAKE + (2 << 32), FAKE + (3 << 32), need - 1, stream=0)
+    assert ei.value.status == tsp.TSP_ERR_WORKSPACE
+    bad = list(w)
+    bad[2] = None
+    with pytest.raises(tsp.TspError) as ei:  # a null shard pointer
+        tsp.tsp_mlp_ring(s, FAKE + (1 << 32), w, bad, None, FAKE + (2 << 32), FAKE + (3 << 32), need, stream=0)
+    assert ei.value.status == tsp.TSP_ERR_INVALID_ARG and b"w2[2]" in tsp.lib().tsp_last_error()
+    with pytest.raises(tsp.TspError):  # x overlaps y
+        tsp.tsp_mlp_ring(s, FAKE, w, w, None, FAKE + 256, FAKE + (3 << 32), need, stream=0)
+
+
+def test_layer_errors():
+    s = _shape()
+    w = dict(g_attn=FAKE, g_mlp=FAKE, wqkv=[FAKE] * 4, wo=[FAKE] * 4, w1=[FAKE] * 4, w2=[FAKE] * 4)
+    need = tsp.workspace_size(s, tsp.TSP_WS_LAYER)
+    args = dict(x=FAKE + (1 << 32), k_full=FAKE + (2 << 32), v_full=FAKE + (3 << 32), y=FAKE + (4 << 32),
+                ws=FAKE + (5 << 32))
+    for phases in (0, 4, 7):
+        with pytest.raises(tsp.TspError):
+            tsp.tsp_layer_fwd(s, w, args["x"], args["k_full"], args["v_full"], args["y"], phases, args["ws"], need, stream=0)
+    with pytest.raises(tsp.TspError) as ei:
+        tsp.tsp_layer_fwd(s, w, args["x"], args["k_full"], args["v_full"], args["y"], 3, args["ws"], need - 256, stream=0)
+    assert ei.value.status == tsp.TSP_ERR_WORKSPACE
+    with pytest.raises(tsp.TspError) as ei:  # y aliases x
+        tsp.tsp_layer_fwd(s, w, args["x"], args["k_full"], args["v_full"], args["x"], 3, args["ws"], need, stream=0)
+    assert b"overlaps" in tsp.lib().tsp_last_error()
+    w_bad = dict(w, wo=[FAKE, FAKE, FAKE + 8, FAKE])
+    with pytest.raises(tsp.TspError) as ei:
+        tsp.tsp_layer_fwd(s, w_bad, args["x"], args["k_full"], args["v_full"], args["y"], 3, args["ws"], need, stream=0)
+    assert b"wo[2]" in tsp.lib().tsp_last_error()
+
+
+def test_zigzag_index_errors():
+    with pytest.raises(tsp.TspError):
+        tsp.tsp_zigzag_index_host(10, 4, 0)
+    with pytest.raises(tsp.TspError):
+        tsp.tsp_zigzag_index(16, 4, 0, None, stream=0)
+    pos = (ctypes.c_int32 * 4)()
+    assert tsp.lib().tsp_zigzag_index_host(16, 4, 1, pos) == 0
+    assert list(pos) == [2, 3, 12, 13]

@@ -1,0 +1,256 @@
+"""GPU parity at sizes the oracle finishes in seconds: every entry point of the
+C ABI against the fp64 oracle on the same seeded inputs, including ragged
+tiles (chunks that are not a multiple of the tile), D = 1, the smallest
+sequence, every rank, both dtypes and both K/V modes of the layer."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import tsp_rank_local_amd as tsp
+from gpu_util import TOL_BF16, TOL_F32, assert_close, down, f64, log, torch_cuda, up
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_cuda()
+    tsp.lib()
+    return t
+
+
+def _sync(torch):
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- zigzag
+@pytest.mark.parametrize("S,D", [(16, 4), (1024, 4), (2400, 4), (131072, 8), (64, 1), (8, 4)])
+def test_zigzag_index_bit_exact(torch, S, D):
+    for r in range(D):
+        pos = torch.full((S // D,), -1, dtype=torch.int32, device="cuda")
+        tsp.tsp_zigzag_index(S, D, r, pos)
+        _sync(torch)
+        assert np.array_equal(pos.cpu().numpy().astype(np.int64), oracle.zigzag_positions(S, D, r))
+
+
+# ---------------------------------------------------------------- attention
+ATTN_CASES = [
+    # S, D, H, Dh, dtype, o_dtype
+    (1024, 4, 4, 64, "f32", "f32"),     # the tiny fp32 layer's attention
+    (1024, 4, 2, 128, "f32", "f32"),
+    (2048, 2, 2, 128, "bf16", "f32"),
+    (1200, 4, 2, 128, "bf16", "f32"),   # C = 150: ragged query and key tiles
+    (600, 3, 3, 64, "bf16", "f32"),     # C = 100, D = 3
+    (512, 1, 3, 64, "bf16", "f32"),     # D = 1: plain causal attention
+    (4096, 4, 2, 128, "bf16", "bf16"),
+    (2048, 4, 4, 64, "bf16", "bf16"),
+    (8, 4, 1, 64, "bf16", "f32"),       # one token per chunk
+]
+
+
+@pytest.mark.parametrize("S,D,H,Dh,dtype,odt", ATTN_CASES)
+def test_zigzag_attention(torch, S, D, H, Dh, dtype, odt):
+    shape = synth.LayerShape(S=S, D=D, h=H * Dh, H=H, Dh=Dh, F=64 * D, dtype=dtype)
+    k, v = synth.remote_kv(shape, seed=11)
+    kd, vd = up(k, dtype), up(v, dtype)
+    k64, v64 = f64(k, dtype), f64(v, dtype)
+    N = S // D
+    for r in range(D):
+        q = synth.normal((N, H, Dh), 11, synth.TID_Q, r, dtype=dtype)
+        o = torch.empty((N, H, Dh), dtype=torch.float32 if odt == "f32" else torch.bfloat16, device="cuda")
+        s = tsp.make_shape(S, D, r, H * Dh, H, Dh, 64 * D, dtype=dtype)
+        log(f"attention S={S} D={D} r={r} H={H} Dh={Dh} {dtype}->{odt}")
+        tsp.tsp_zigzag_attn(s, up(q, dtype), kd, vd, o, tsp.TSP_F32 if odt == "f32" else tsp.TSP_BF16)
+        _sync(torch)
+        want = oracle.causal_attention(f64(q, dtype), k64, v64, oracle.zigzag_positions(S, D, r), shape.scale)
+        got = down(o)
+        if dtype == "f32":
+            assert_close(got, want, TOL_F32, "o")
+        elif odt == "f32":
+            assert_close(got, want, TOL_BF16, "o")
+        else:
+            # a bf16 output adds its own rounding, up to 2^-9 |o| per element
+            rms = float(np.sqrt(np.mean(want ** 2)))
+            excess = np.abs(got - want) - 2.0 ** -8 * np.abs(want)
+            log(f"  o(bf16 out): max excess over rounding = {excess.max():.3e}, rms {rms:.3e}")
+            assert excess.max() <= TOL_BF16 * rms
+
+
+def test_attention_scale_zero_gives_prefix_mean(torch):
+    S, D, H, Dh = 512, 2, 2, 128
+    shape = synth.LayerShape(S=S, D=D, h=H * Dh, H=H, Dh=Dh, F=128, dtype="bf16")
+    k, v = synth.remote_kv(shape, seed=12)
+    q = synth.normal((S // D, H, Dh), 12, synth.TID_Q, 0, dtype="bf16")
+    o = torch.empty((S // D, H, Dh), dtype=torch.float32, device="cuda")
+    tsp.tsp_zigzag_attn(tsp.make_shape(S, D, 1, H * Dh, H, Dh, 128, scale=0.0), up(q, "bf16"), up(k, "bf16"),
+                        up(v, "bf16"), o)
+    _sync(torch)
+    pos = oracle.zigzag_positions(S, D, 1)
+    v64 = f64(v, "bf16")
+    want = (np.cumsum(v64, axis=0) / (np.arange(S) + 1)[:, None, None])[pos]
+    assert_close(down(o), want, TOL_BF16, "prefix mean")
+
+
+# ---------------------------------------------------------------- MLP ring
+MLP_CASES = [
+    # S, D, h, F, dtype, residual
+    (1024, 4, 256, 1024, "f32", False),   # the tiny fp32 layer's MLP
+    (1024, 4, 256, 1024, "f32", True),
+    (2400, 4, 512, 2048, "bf16", True),   # N = 600: ragged row tiles
+    (2048, 2, 256, 512, "bf16", False),
+    (1024, 1, 256, 256, "bf16", False),   # D = 1
+    (4096, 8, 640, 1024, "bf16", True),   # N = 512, h not a multiple of the tile
+]
+
+
+@pytest.mark.parametrize("S,D,h,F,dtype,resid", MLP_CASES)
+def test_mlp_ring(torch, S, D, h, F, dtype, resid):
+    shape = synth.LayerShape(S=S, D=D, h=h, H=h // 64, Dh=64, F=F, dtype=dtype)
+    N = S // D
+    w = synth.layer_weights(shape, seed=21)
+    x = synth.activations(N, h, seed=21, dtype=dtype)
+    res = synth.activations(N, h, seed=22) if resid else None
+    w1d = [up(a, dtype) for a in w["w1"]]
+    w2d = [up(a, dtype) for a in w["w2"]]
+    xd = up(x, dtype)
+    want = oracle.mlp(f64(x, dtype), [f64(a, dtype) for a in w["w1"]], [f64(a, dtype) for a in w["w2"]])
+    if resid:
+        want = want + res.astype(np.float64)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    outs = []
+    for r in sorted({0, D - 1, D // 2}):
+        s = tsp.make_shape(S, D, r, h, h // 64, 64, F, dtype=dtype)
+        ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_MLP), dtype=torch.uint8, device="cuda")
+        y = torch.full((N, h), float("nan"), dtype=torch.float32, device="cuda")
+        log(f"mlp ring S={S} D={D} r={r} h={h} F={F} {dtype} residual={resid}")
+        tsp.tsp_mlp_ring(s, xd, w1d, w2d, up(res, "f32") if resid else None, y, ws)
+        _sync(torch)
+        outs.append(down(y))
+        assert_close(outs[-1], want, tol, "y")
+
+
+def test_mlp_ring_residual_in_place(torch):
+    S, D, h, F = 1024, 4, 256, 1024
+    shape = synth.LayerShape(S=S, D=D, h=h, H=4, Dh=64, F=F, dtype="bf16")
+    w = synth.layer_weights(shape, seed=23)
+    x = synth.activations(S // D, h, seed=23, dtype="bf16")
+    res = synth.activations(S // D, h, seed=24)
+    s = tsp.make_shape(S, D, 2, h, 4, 64, F, dtype="bf16")
+    ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_MLP), dtype=torch.uint8, device="cuda")
+    y = up(res, "f32")
+    tsp.tsp_mlp_ring(s, up(x, "bf16"), [up(a, "bf16") for a in w["w1"]], [up(a, "bf16") for a in w["w2"]], y, y, ws)
+    _sync(torch)
+    want = res + oracle.mlp(f64(x, "bf16"), [f64(a, "bf16") for a in w["w1"]], [f64(a, "bf16") for a in w["w2"]])
+    assert_close(down(y), want, TOL_BF16, "y (residual == y)")
+
+
+# ---------------------------------------------------------------- whole layer
+def _dev_weights(w, dtype):
+    return {k: ([up(a, dtype) for a in w[k]] if isinstance(w[k], list) else up(w[k], dtype))
+            for k in ("wqkv", "wo", "w1", "w2", "g_attn", "g_mlp")}
+
+
+def _w64(w, dtype):
+    return {k: ([f64(a, dtype) for a in w[k]] if isinstance(w[k], list) else f64(w[k], dtype)) for k in w}
+
+
+@pytest.mark.parametrize("gain", ["ones", "random"])
+def test_tiny_layer_every_rank_vs_unsharded(torch, gain):
+    """Tiny fp32 layer (S=1024, D=4, h=256, 4 heads of 64, F=1024): the D ranks
+    each write their K/V rows into one shared buffer (the all-gather), then each
+    runs the rest; every rank's rows must equal the unsharded layer's."""
+    shape = synth.TINY_FP32
+    S, D, h, H, Dh, F = shape.S, shape.D, shape.h, shape.H, shape.Dh, shape.F
+    w = synth.layer_weights(shape, seed=1, gain=gain)
+    x_full = synth.activations(S, h, seed=1)
+    full = oracle.layer_full(x_full, _w64(w, "f32"), H, Dh, shape.eps, shape.scale)
+    wd = _dev_weights(w, "f32")
+    kf = torch.zeros((S, H, Dh), dtype=torch.float32, device="cuda")
+    vf = torch.zeros_like(kf)
+    ranks = []
+    for r in range(D):
+        s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype="f32")
+        pos = oracle.zigzag_positions(S, D, r)
+        ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
+        xd = up(x_full[pos], "f32")
+        y = torch.full((S // D, h), float("nan"), dtype=torch.float32, device="cuda")
+        tsp.tsp_layer_fwd(s, wd, xd, kf, vf, y, tsp.TSP_PHASE_KV, ws)
+        ranks.append((s, pos, ws, xd, y))
+    for s, pos, ws, xd, y in ranks:
+        tsp.tsp_layer_fwd(s, wd, xd, kf, vf, y, tsp.TSP_PHASE_REST, ws)
+    _sync(torch)
+    assert_close(down(kf), full["k"], TOL_F32, "gathered K")
+    assert_close(down(vf), full["v"], TOL_F32, "gathered V")
+    got = np.zeros_like(full["y"])
+    for s, pos, ws, xd, y in ranks:
+        got[pos] = down(y)
+        log(f"rank {s.r}:")
+        assert_close(down(y), full["y"][pos], TOL_F32, "y rows")
+    assert_close(got, full["y"], TOL_F32, "y, all ranks")
+
+
+def test_tiny_layer_rank_mode_given_remote_kv(torch):
+    shape = synth.TINY_FP32
+    S, D, h, H, Dh, F = shape.S, shape.D, shape.h, shape.H, shape.Dh, shape.F
+    w = synth.layer_weights(shape, seed=2, gain="random")
+    w64 = _w64(w, "f32")
+    wd = _dev_weights(w, "f32")
+    k_rem, v_rem = synth.remote_kv(shape, seed=2)
+    for r in range(D):
+        x = synth.activations(S // D, h, seed=2, tid=100 + r)
+        s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype="f32")
+        ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
+        kf, vf = up(k_rem, "f32"), up(v_rem, "f32")
+        y = torch.empty((S // D, h), dtype=torch.float32, device="cuda")
+        tsp.tsp_layer_fwd(s, wd, up(x, "f32"), kf, vf, y, tsp.TSP_PHASE_ALL, ws)
+        _sync(torch)
+        want = oracle.layer_rank(x, w64, k_rem, v_rem, S, D, r, H, Dh, shape.eps, shape.scale)
+        log(f"rank {r}:")
+        assert_close(down(y), want["y"], TOL_F32, "y")
+        assert_close(down(y) - x, want["y"] - x, 10 * TOL_F32, "y - x (both branches)")
+
+
+@pytest.mark.parametrize("S,D,H,Dh,F", [(2048, 4, 4, 128, 2048), (2400, 4, 4, 128, 2048), (1024, 2, 4, 64, 1024)])
+def test_bf16_layer_vs_oracle(torch, S, D, H, Dh, F):
+    h = H * Dh
+    shape = synth.LayerShape(S=S, D=D, h=h, H=H, Dh=Dh, F=F, dtype="bf16")
+    w = synth.layer_weights(shape, seed=3, gain="random")
+    w64 = _w64(w, "bf16")
+    wd = _dev_weights(w, "bf16")
+    k_rem, v_rem = synth.remote_kv(shape, seed=3)
+    k64, v64 = f64(k_rem, "bf16"), f64(v_rem, "bf16")
+    for r in sorted({0, D - 1}):
+        x = synth.activations(S // D, h, seed=3, tid=100 + r)
+        s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype="bf16")
+        ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
+        kf, vf = up(k_rem, "bf16"), up(v_rem, "bf16")
+        y = torch.empty((S // D, h), dtype=torch.float32, device="cuda")
+        log(f"bf16 layer S={S} D={D} r={r} H={H} Dh={Dh} F={F}")
+        tsp.tsp_layer_fwd(s, wd, up(x, "f32"), kf, vf, y, tsp.TSP_PHASE_ALL, ws)
+        _sync(torch)
+        want = oracle.layer_rank(x, w64, k64, v64, S, D, r, H, Dh, shape.eps, shape.scale)
+        assert_close(down(y), want["y"], TOL_BF16, "y")
+        # remote rows of the gathered K/V are left untouched
+        pos = oracle.zigzag_positions(S, D, r)
+        remote = np.setdiff1d(np.arange(S), pos)
+        assert np.array_equal(kf.view(torch.int16).cpu().numpy()[remote], k_rem.view(np.int16)[remote])
+
+
+def test_layer_deterministic(torch):
+    S, D, H, Dh, F = 2048, 4, 4, 128, 2048
+    h = H * Dh
+    shape = synth.LayerShape(S=S, D=D, h=h, H=H, Dh=Dh, F=F, dtype="bf16")
+    w = synth.layer_weights(shape, seed=4)
+    wd = _dev_weights(w, "bf16")
+    k_rem, v_rem = synth.remote_kv(shape, seed=4)
+    x = up(synth.activations(S // D, h, seed=4), "f32")
+    s = tsp.make_shape(S, D, 1, h, H, Dh, F, dtype="bf16")
+    outs = []
+    for _ in range(2):
+        ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
+        y = torch.empty((S // D, h), dtype=torch.float32, device="cuda")
+        tsp.tsp_layer_fwd(s, wd, x, up(k_rem, "bf16"), up(v_rem, "bf16"), y, tsp.TSP_PHASE_ALL, ws)
+        _sync(torch)
+        outs.append(y.cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))

@@ -1,0 +1,380 @@
+// C ABI of the rank-local TSP layer: argument checks, workspace layout and the
+// order of launches. Every check runs on the host before anything is enqueued.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "tsp_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+tsp_status fail(tsp_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+tsp_status ok() {
+  g_err.clear();
+  return TSP_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == TSP_BF16 ? 2 : 4; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  const void *p;
+  size_t bytes;
+  const char *name;
+};
+
+bool overlap(const Range &a, const Range &b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+tsp_status check_ptr(const void *p, const char *name) {
+  if (!p) return fail(TSP_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(TSP_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return TSP_OK;
+}
+
+tsp_status check_ptr_list(const void *const *list, int D, const char *name) {
+  if (!list) return fail(TSP_ERR_INVALID_ARG, "%s (array of shard pointers) is NULL", name);
+  for (int j = 0; j < D; ++j) {
+    if (!list[j]) return fail(TSP_ERR_INVALID_ARG, "%s[%d] is NULL", name, j);
+    if (!aligned16(list[j])) return fail(TSP_ERR_INVALID_ARG, "%s[%d] is not 16-byte aligned", name, j);
+  }
+  return TSP_OK;
+}
+
+// Checks shared by every entry point: the folded axis and the zigzag split.
+tsp_status check_axis(const tsp_shape *s) {
+  if (!s) return fail(TSP_ERR_INVALID_ARG, "shape is NULL");
+  if (s->D < 1 || s->D > TSP_MAX_D) return fail(TSP_ERR_INVALID_ARG, "D=%d outside [1, %d]", s->D, TSP_MAX_D);
+  if (s->S <= 0 || s->S >= (int64_t(1) << 31)) return fail(TSP_ERR_INVALID_ARG, "S=%lld outside [1, 2^31)", (long long)s->S);
+  if (s->S % (2 * s->D) != 0) return fail(TSP_ERR_INVALID_ARG, "S=%lld is not a multiple of 2D=%d", (long long)s->S, 2 * s->D);
+  if (s->r < 0 || s->r >= s->D) return fail(TSP_ERR_INVALID_ARG, "r=%d outside [0, D=%d)", s->r, s->D);
+  if (s->dtype != TSP_F32 && s->dtype != TSP_BF16) return fail(TSP_ERR_INVALID_ARG, "unknown dtype %d", s->dtype);
+  return TSP_OK;
+}
+
+tsp_status check_attn_shape(const tsp_shape *s) {
+  tsp_status st = check_axis(s);
+  if (st) return st;
+  if (s->H < 1) return fail(TSP_ERR_INVALID_ARG, "H=%d must be positive", s->H);
+  if (s->Dh != 64 && s->Dh != 128) return fail(TSP_ERR_UNSUPPORTED, "Dh=%d: only 64 and 128 are supported", s->Dh);
+  if ((int64_t)s->H * s->Dh > (1 << 20)) return fail(TSP_ERR_INVALID_ARG, "H*Dh too large");
+  if (!isfinite(s->scale) || s->scale < 0.f) return fail(TSP_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  return TSP_OK;
+}
+
+tsp_status check_mlp_shape(const tsp_shape *s) {
+  tsp_status st = check_axis(s);
+  if (st) return st;
+  if (s->h < 64 || s->h % 64 != 0) return fail(TSP_ERR_UNSUPPORTED, "h=%d must be a positive multiple of 64", s->h);
+  if (s->F < 1 || s->F % s->D != 0) return fail(TSP_ERR_INVALID_ARG, "F=%d must be a positive multiple of D=%d", s->F, s->D);
+  if ((s->F / s->D) % 64 != 0) return fail(TSP_ERR_UNSUPPORTED, "F/D=%d must be a multiple of 64", s->F / s->D);
+  return TSP_OK;
+}
+
+tsp_status check_layer_shape(const tsp_shape *s) {
+  tsp_status st = check_attn_shape(s);
+  if (st) return st;
+  st = check_mlp_shape(s);
+  if (st) return st;
+  if (s->H % s->D != 0) return fail(TSP_ERR_INVALID_ARG, "H=%d must be a multiple of D=%d", s->H, s->D);
+  if (s->h != s->H * s->Dh) return fail(TSP_ERR_INVALID_ARG, "h=%d != H*Dh=%d", s->h, s->H * s->Dh);
+  if (!isfinite(s->eps) || s->eps < 0.f) return fail(TSP_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  return TSP_OK;
+}
+
+struct LayerWs {
+  size_t q, x2, hid, total;
+};
+
+LayerWs layer_ws(const tsp_shape *s) {
+  const size_t e = elem_bytes(s->dtype);
+  const size_t N = (size_t)(s->S / s->D);
+  LayerWs w;
+  w.q = 0;
+  w.x2 = align256(N * s->h * e);
+  w.hid = w.x2 + align256(N * s->h * e);
+  w.total = w.hid + align256(N * (size_t)(s->F / s->D) * e);
+  return w;
+}
+
+size_t mlp_ws(const tsp_shape *s) {
+  return align256((size_t)(s->S / s->D) * (size_t)(s->F / s->D) * elem_bytes(s->dtype));
+}
+
+tsp_status hip_fail(hipError_t e, const char *what) {
+  return fail(TSP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+tsp::PtrList to_list(const void *const *p, int D) {
+  tsp::PtrList l;
+  memset(&l, 0, sizeof l);
+  for (int j = 0; j < D; ++j) l.p[j] = p[j];
+  return l;
+}
+
+// ---------------------------------------------------------------- profiling
+struct ProfRec {
+  hipEvent_t a, b;
+};
+struct Prof {
+  bool on = false;
+  std::vector<ProfRec> open[TSP_K_COUNT];
+  std::vector<hipEvent_t> pool;
+  double ms[TSP_K_COUNT] = {};
+  int64_t n[TSP_K_COUNT] = {};
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  void drain(int k) {
+    for (ProfRec &r : open[k]) {
+      if (r.a && r.b && hipEventSynchronize(r.b) == hipSuccess) {
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, r.a, r.b) == hipSuccess) {
+          ms[k] += t;
+          n[k] += 1;
+        }
+      }
+      if (r.a) pool.push_back(r.a);
+      if (r.b) pool.push_back(r.b);
+    }
+    open[k].clear();
+  }
+};
+Prof g_prof;
+
+}  // namespace
+
+namespace tsp {
+void prof_begin(int k, hipStream_t s) {
+  if (!g_prof.on) return;
+  ProfRec r{g_prof.get(), nullptr};
+  if (r.a) hipEventRecord(r.a, s);
+  g_prof.open[k].push_back(r);
+}
+void prof_end(int k, hipStream_t s) {
+  if (!g_prof.on || g_prof.open[k].empty()) return;
+  ProfRec &r = g_prof.open[k].back();
+  r.b = g_prof.get();
+  if (r.b) hipEventRecord(r.b, s);
+}
+}  // namespace tsp
+
+#define TSP_LAUNCH(kclass, call, what)                \
+  do {                                                \
+    tsp::prof_begin(kclass, stream);                  \
+    hipError_t e_ = (call);                           \
+    tsp::prof_end(kclass, stream);                    \
+    if (e_ != hipSuccess) return hip_fail(e_, what);  \
+  } while (0)
+
+extern "C" {
+
+const char *tsp_status_string(int status) {
+  switch (status) {
+    case TSP_OK: return "ok";
+    case TSP_ERR_INVALID_ARG: return "invalid argument";
+    case TSP_ERR_UNSUPPORTED: return "unsupported shape";
+    case TSP_ERR_WORKSPACE: return "workspace too small";
+    case TSP_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *tsp_last_error(void) { return g_err.c_str(); }
+
+int tsp_abi_version(void) { return 1; }
+
+tsp_status tsp_workspace_size(const tsp_shape *s, int which, size_t *bytes) {
+  if (!bytes) return fail(TSP_ERR_INVALID_ARG, "bytes is NULL");
+  tsp_status st;
+  if (which == TSP_WS_MLP) {
+    if ((st = check_mlp_shape(s))) return st;
+    *bytes = mlp_ws(s);
+  } else if (which == TSP_WS_LAYER) {
+    if ((st = check_layer_shape(s))) return st;
+    *bytes = layer_ws(s).total;
+  } else {
+    return fail(TSP_ERR_INVALID_ARG, "unknown workspace kind %d", which);
+  }
+  return ok();
+}
+
+tsp_status tsp_zigzag_index_host(int64_t S, int32_t D, int32_t r, int32_t *pos) {
+  tsp_shape s{};
+  s.S = S;
+  s.D = D;
+  s.r = r;
+  s.dtype = TSP_F32;
+  tsp_status st = check_axis(&s);
+  if (st) return st;
+  if (!pos) return fail(TSP_ERR_INVALID_ARG, "pos is NULL");
+  const tsp::ZigzagMap zz = tsp::make_zigzag(S, D, r);
+  const int32_t n = (int32_t)(S / D);
+  for (int32_t t = 0; t < n; ++t) pos[t] = zz.pos(t);
+  return ok();
+}
+
+tsp_status tsp_zigzag_index(int64_t S, int32_t D, int32_t r, int32_t *pos, void *stream_) {
+  tsp_shape s{};
+  s.S = S;
+  s.D = D;
+  s.r = r;
+  s.dtype = TSP_F32;
+  tsp_status st = check_axis(&s);
+  if (st) return st;
+  if ((st = check_ptr(pos, "pos"))) return st;
+  hipStream_t stream = (hipStream_t)stream_;
+  TSP_LAUNCH(TSP_K_ZIGZAG, tsp::launch_zigzag_index(tsp::make_zigzag(S, D, r), (int32_t)(S / D), pos, stream),
+             "zigzag index");
+  return ok();
+}
+
+tsp_status tsp_zigzag_attn(const tsp_shape *s, const void *q, const void *k, const void *v, void *o,
+                           int32_t o_dtype, void *stream_) {
+  tsp_status st = check_attn_shape(s);
+  if (st) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(o, "o")))
+    return st;
+  if (o_dtype != TSP_F32 && o_dtype != TSP_BF16) return fail(TSP_ERR_INVALID_ARG, "unknown o_dtype %d", o_dtype);
+  if (s->dtype == TSP_F32 && o_dtype != TSP_F32) return fail(TSP_ERR_INVALID_ARG, "fp32 inputs need an fp32 output");
+  const size_t e = elem_bytes(s->dtype), row = (size_t)s->H * s->Dh;
+  const size_t N = (size_t)(s->S / s->D);
+  const Range ro{o, N * row * elem_bytes(o_dtype), "o"};
+  const Range ins[] = {{q, N * row * e, "q"}, {k, (size_t)s->S * row * e, "k"}, {v, (size_t)s->S * row * e, "v"}};
+  for (const Range &r : ins)
+    if (overlap(ro, r)) return fail(TSP_ERR_INVALID_ARG, "o overlaps %s", r.name);
+  hipStream_t stream = (hipStream_t)stream_;
+  TSP_LAUNCH(TSP_K_ATTN,
+             tsp::launch_attention(s->dtype, q, k, v, o, o_dtype, s->S, (int32_t)N, s->H, s->Dh, s->scale,
+                                   tsp::make_zigzag(s->S, s->D, s->r), stream),
+             "attention");
+  return ok();
+}
+
+tsp_status tsp_mlp_ring(const tsp_shape *s, const void *x, const void *const *w1, const void *const *w2,
+                        const float *residual, float *y, void *ws, size_t ws_bytes, void *stream_) {
+  tsp_status st = check_mlp_shape(s);
+  if (st) return st;
+  if ((st = check_ptr(x, "x")) || (st = check_ptr(y, "y")) || (st = check_ptr(ws, "ws"))) return st;
+  if (residual && !aligned16(residual)) return fail(TSP_ERR_INVALID_ARG, "residual is not 16-byte aligned");
+  if ((st = check_ptr_list(w1, s->D, "w1")) || (st = check_ptr_list(w2, s->D, "w2"))) return st;
+  const size_t need = mlp_ws(s);
+  if (ws_bytes < need) return fail(TSP_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, need);
+  const int32_t N = (int32_t)(s->S / s->D), h = s->h, fd = s->F / s->D;
+  const Range ry{y, (size_t)N * h * 4, "y"}, rx{x, (size_t)N * h * elem_bytes(s->dtype), "x"}, rw{ws, need, "ws"};
+  if (overlap(ry, rx) || overlap(ry, rw) || overlap(rx, rw))
+    return fail(TSP_ERR_INVALID_ARG, "x, y and ws must not overlap");
+  if (residual && residual != y && overlap(Range{residual, (size_t)N * h * 4, "residual"}, ry))
+    return fail(TSP_ERR_INVALID_ARG, "residual overlaps y without being equal to it");
+  hipStream_t stream = (hipStream_t)stream_;
+  for (int t = 0; t < s->D; ++t) {
+    const int j = ((s->r - t) % s->D + s->D) % s->D;
+    TSP_LAUNCH(TSP_K_MLP_UP, tsp::launch_mlp_up(s->dtype, x, N, h, w1[j], fd, ws, stream), "MLP up");
+    const float *res = t == 0 ? residual : y;
+    TSP_LAUNCH(TSP_K_MLP_DOWN, tsp::launch_mlp_down(s->dtype, ws, N, fd, w2[j], h, res, y, stream), "MLP down");
+  }
+  return ok();
+}
+
+tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const float *x, void *k_full,
+                         void *v_full, float *y, unsigned phases, void *ws_, size_t ws_bytes, void *stream_) {
+  tsp_status st = check_layer_shape(s);
+  if (st) return st;
+  if (!w) return fail(TSP_ERR_INVALID_ARG, "weights is NULL");
+  if (phases == 0 || (phases & ~3u)) return fail(TSP_ERR_INVALID_ARG, "phases=%u must be 1, 2 or 3", phases);
+  if ((st = check_ptr(x, "x")) || (st = check_ptr(k_full, "k_full")) || (st = check_ptr(v_full, "v_full")) ||
+      (st = check_ptr(y, "y")) || (st = check_ptr(ws_, "ws")) || (st = check_ptr(w->g_attn, "g_attn")) ||
+      (st = check_ptr(w->g_mlp, "g_mlp")))
+    return st;
+  if ((st = check_ptr_list(w->wqkv, s->D, "wqkv")) || (st = check_ptr_list(w->wo, s->D, "wo")) ||
+      (st = check_ptr_list(w->w1, s->D, "w1")) || (st = check_ptr_list(w->w2, s->D, "w2")))
+    return st;
+  const LayerWs L = layer_ws(s);
+  if (ws_bytes < L.total) return fail(TSP_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, L.total);
+  const int32_t N = (int32_t)(s->S / s->D), h = s->h, D = s->D, hd = h / D, fd = s->F / D;
+  const size_t e = elem_bytes(s->dtype);
+  const Range rx{x, (size_t)N * h * 4, "x"}, ry{y, (size_t)N * h * 4, "y"}, rws{ws_, L.total, "ws"};
+  const Range rk{k_full, (size_t)s->S * h * e, "k_full"}, rv{v_full, (size_t)s->S * h * e, "v_full"};
+  const Range all[] = {rx, ry, rws, rk, rv};
+  for (int i = 0; i < 5; ++i)
+    for (int j = i + 1; j < 5; ++j)
+      if (overlap(all[i], all[j])) return fail(TSP_ERR_INVALID_ARG, "%s overlaps %s", all[i].name, all[j].name);
+
+  unsigned char *ws = static_cast<unsigned char *>(ws_);
+  void *qbuf = ws + L.q;   // Q, later RMSNorm(h1)
+  void *x2 = ws + L.x2;    // RMSNorm(x), later the attention output O
+  void *hid = ws + L.hid;  // GELU(hn W1_j^T) of the current ring step
+  const tsp::ZigzagMap zz = tsp::make_zigzag(s->S, D, s->r);
+  hipStream_t stream = (hipStream_t)stream_;
+
+  if (phases & TSP_PHASE_KV) {
+    TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(x, w->g_attn, x2, N, h, s->eps, s->dtype, stream), "RMSNorm");
+    TSP_LAUNCH(TSP_K_QKV,
+               tsp::launch_qkv(s->dtype, x2, N, h, to_list(w->wqkv, D), D, hd, qbuf, k_full, v_full, zz, stream),
+               "QKV");
+  }
+  if (phases & TSP_PHASE_REST) {
+    TSP_LAUNCH(TSP_K_ATTN,
+               tsp::launch_attention(s->dtype, qbuf, k_full, v_full, x2, s->dtype, s->S, N, s->H, s->Dh, s->scale,
+                                     zz, stream),
+               "attention");
+    TSP_LAUNCH(TSP_K_OUTPROJ, tsp::launch_outproj(s->dtype, x2, N, h, to_list(w->wo, D), D, hd, x, y, stream),
+               "output projection");
+    TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(y, w->g_mlp, qbuf, N, h, s->eps, s->dtype, stream), "RMSNorm");
+    for (int t = 0; t < D; ++t) {
+      const int j = ((s->r - t) % D + D) % D;
+      TSP_LAUNCH(TSP_K_MLP_UP, tsp::launch_mlp_up(s->dtype, qbuf, N, h, w->w1[j], fd, hid, stream), "MLP up");
+      TSP_LAUNCH(TSP_K_MLP_DOWN, tsp::launch_mlp_down(s->dtype, hid, N, fd, w->w2[j], h, y, y, stream), "MLP down");
+    }
+  }
+  return ok();
+}
+
+void tsp_profile_enable(int on) { g_prof.on = on != 0; }
+
+void tsp_profile_reset(void) {
+  for (int k = 0; k < TSP_K_COUNT; ++k) {
+    g_prof.drain(k);
+    g_prof.ms[k] = 0.0;
+    g_prof.n[k] = 0;
+  }
+}
+
+tsp_status tsp_profile_read(int k, double *total_ms, int64_t *launches) {
+  if (k < 0 || k >= TSP_K_COUNT) return fail(TSP_ERR_INVALID_ARG, "unknown kernel class %d", k);
+  if (!total_ms || !launches) return fail(TSP_ERR_INVALID_ARG, "output pointer is NULL");
+  g_prof.drain(k);
+  *total_ms = g_prof.ms[k];
+  *launches = g_prof.n[k];
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Row-wise kernels: zigzag index map and RMSNorm (fp32 in, bf16/fp32 out).
+#include "device_common.h"
+#include "tsp_internal.h"
+
+namespace tsp {
+
+__global__ void zigzag_index_kernel(ZigzagMap zz, int32_t n, int32_t *pos) {
+  int32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < n) pos[t] = zz.pos(t);
+}
+
+hipError_t launch_zigzag_index(ZigzagMap zz, int32_t n, int32_t *pos, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int threads = 256;
+  int blocks = (n + threads - 1) / threads;
+  hipLaunchKernelGGL(zigzag_index_kernel, dim3(blocks), dim3(threads), 0, s, zz, n, pos);
+  return hipGetLastError();
+}
+
+// One 256-thread block per row; h % 4 == 0. The sum of squares runs in fp32,
+// first per thread, then across the wave with shuffles, then across waves.
+template <typename G, typename O>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ x, const G *__restrict__ g,
+                                                      O *__restrict__ out, int32_t h, float eps) {
+  const int64_t row = blockIdx.x;
+  const float *xr = x + row * h;
+  O *orow = out + row * h;
+  float ss = 0.f;
+  for (int c = threadIdx.x * 4; c < h; c += 1024) {
+    float4 v = *reinterpret_cast<const float4 *>(xr + c);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  __shared__ float part[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) part[wave] = ss;
+  __syncthreads();
+  float tot = part[0] + part[1] + part[2] + part[3];
+  const float rstd = 1.0f / sqrtf(tot / (float)h + eps);
+  for (int c = threadIdx.x * 4; c < h; c += 1024) {
+    float4 v = *reinterpret_cast<const float4 *>(xr + c);
+    float r0 = v.x * rstd * (float)g[c + 0];
+    float r1 = v.y * rstd * (float)g[c + 1];
+    float r2 = v.z * rstd * (float)g[c + 2];
+    float r3 = v.w * rstd * (float)g[c + 3];
+    orow[c + 0] = (O)r0;
+    orow[c + 1] = (O)r1;
+    orow[c + 2] = (O)r2;
+    orow[c + 3] = (O)r3;
+  }
+}
+
+hipError_t launch_rmsnorm(const float *x, const void *g, void *out, int32_t rows, int32_t h, float eps,
+                          int dtype, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (dtype == TSP_BF16) {
+    hipLaunchKernelGGL((rmsnorm_kernel<bf16, bf16>), dim3(rows), dim3(256), 0, s, x, (const bf16 *)g,
+                       (bf16 *)out, h, eps);
+  } else {
+    hipLaunchKernelGGL((rmsnorm_kernel<float, float>), dim3(rows), dim3(256), 0, s, x, (const float *)g,
+                       (float *)out, h, eps);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tsp

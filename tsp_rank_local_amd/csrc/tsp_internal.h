@@ -1,0 +1,69 @@
+// Internal interface between the C-ABI layer (api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tsp.h"
+
+namespace tsp {
+
+// Global position of local row t under the zigzag ownership of rank r:
+// chunk r holds rows [0, C), chunk 2D-1-r holds rows [C, 2C).
+struct ZigzagMap {
+  int32_t C;      // chunk length S/(2D)
+  int32_t base0;  // r*C
+  int32_t base1;  // (2D-1-r)*C
+  __host__ __device__ inline int32_t pos(int32_t t) const {
+    return t < C ? base0 + t : base1 + (t - C);
+  }
+};
+
+inline ZigzagMap make_zigzag(int64_t S, int32_t D, int32_t r) {
+  ZigzagMap z;
+  z.C = (int32_t)(S / (2 * D));
+  z.base0 = r * z.C;
+  z.base1 = (2 * D - 1 - r) * z.C;
+  return z;
+}
+
+// Up to TSP_MAX_D device pointers passed by value as a kernel argument.
+struct PtrList {
+  const void *p[TSP_MAX_D];
+};
+
+// ---------------------------------------------------------------- rows
+hipError_t launch_zigzag_index(ZigzagMap zz, int32_t n, int32_t *pos, hipStream_t s);
+// out[row] = x[row] / sqrt(mean(x[row]^2) + eps) * g, x fp32; g and out in dtype.
+hipError_t launch_rmsnorm(const float *x, const void *g, void *out, int32_t rows, int32_t h, float eps,
+                          int dtype, hipStream_t s);
+
+// ---------------------------------------------------------------- GEMMs
+// All products are C = A B^T with A [M][K] and B [N][K] (both K-contiguous).
+// QKV of every attention shard in one launch: shard z reads w[z] [3hd][h];
+// Q columns go to q [N][h] at column z*hd, K/V rows go to kf/vf [S][h] at row
+// zz.pos(t), column z*hd.
+hipError_t launch_qkv(int dtype, const void *xn, int32_t n, int32_t h, const PtrList &w, int32_t D,
+                      int32_t hd, void *q, void *kf, void *vf, ZigzagMap zz, hipStream_t s);
+// y = x + sum_j o[:, j*hd:(j+1)*hd] wo[j]^T, shards walked j = 0..D-1 inside
+// the reduction loop.
+hipError_t launch_outproj(int dtype, const void *o, int32_t n, int32_t h, const PtrList &wo, int32_t D,
+                          int32_t hd, const float *x, float *y, hipStream_t s);
+// hid = GELU(x w1j^T) stored in dtype, w1j [fd][h].
+hipError_t launch_mlp_up(int dtype, const void *x, int32_t n, int32_t h, const void *w1j, int32_t fd,
+                         void *hid, hipStream_t s);
+// y = (res ? res : 0) + hid w2j^T in fp32, w2j [h][fd]; res may equal y.
+hipError_t launch_mlp_down(int dtype, const void *hid, int32_t n, int32_t fd, const void *w2j, int32_t h,
+                           const float *res, float *y, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+hipError_t launch_attention(int dtype, const void *q, const void *k, const void *v, void *o, int o_dtype,
+                            int64_t S, int32_t n, int32_t H, int32_t Dh, float scale, ZigzagMap zz,
+                            hipStream_t s);
+
+// ---------------------------------------------------------------- timing
+// Bracket a launch with events when profiling is on (api.cpp).
+void prof_begin(int kclass, hipStream_t s);
+void prof_end(int kclass, hipStream_t s);
+
+}  // namespace tsp
