@@ -93,6 +93,9 @@ def main():
     ap.add_argument("--workload", choices=["layer", "mlp", "attn"], default="layer")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=384, help="rows in the CPU oracle sample (0 = skip)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="before warmup, run one plain device-to-device copy of this many MiB (a known-size "
+                         "reference for rocprofv3 HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         sys.exit(f"bench.py: only --gpus 1 is supported; this build measures one rank's share on one GPU "
@@ -156,6 +159,14 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs resident in HBM ({time.perf_counter() - t_gen:.1f} s); warmup {args.warmup}")
 
+    if args.copy_mib > 0:
+        n = args.copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"reference copy: {n} bytes read, {n} bytes written")
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

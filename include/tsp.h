@@ -40,7 +40,9 @@
  *  - dtype TSP_BF16: weights, gains, x of tsp_mlp_ring, Q/K/V, O and the MLP
  *    hidden activations are bf16; the residual stream x/h1/y of the layer is
  *    fp32; every product accumulates in fp32. In attention the probabilities
- *    and V enter the P.V product as fp16 (so |V| must stay below 65504).
+ *    enter the P.V product rounded to bf16, except in query tiles whose
+ *    positions all lie below 1024, where they enter as a bf16 pair hi + lo
+ *    (those rows see few keys, so a single weight can carry most of a row).
  *    dtype TSP_F32: everything is fp32.
  *  - Errors: all arguments are checked on the host before anything is
  *    enqueued. On failure nothing is enqueued, the status is returned and

@@ -3,23 +3,37 @@
 //
 // Work split: the rank's local rows form two chunks (global positions r*C..
 // and (2D-1-r)*C..). They are cut into T = ceil(C/128) query tiles per chunk;
-// block (head, p) takes tile p of the first chunk and the mirrored tile
-// T-1-p of the second, so every block walks about S/64 + 2 key tiles and all
-// blocks carry equal causal work. Key tiles past a tile's last query are never
-// loaded; only tiles that straddle the diagonal apply the mask.
+// block (head, p) takes the mirrored tile T-1-p of the second chunk and then
+// tile p of the first, so every block walks about S/64 + 2 key tiles and all
+// blocks carry equal causal work. The long (second-chunk) tile goes first: the
+// blocks of one head that share an XCD then stream the same key tiles together
+// and each tile comes from HBM about once per head. Key tiles past a tile's
+// last query are never loaded; only tiles that straddle the diagonal apply the
+// mask.
 //
-// Per block: 4 waves x 32 queries. Per 64-key tile the block stages K (bf16,
-// row-major, 16-byte chunks XOR-swizzled by row) and V (converted to fp16 and
-// stored transposed, 8-byte units XOR-swizzled by feature) in LDS, two stages
-// deep, with the next tile's global loads issued before the current tile's
-// math. Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so a
-// lane owns one query and 32 of the tile's keys: the row max needs one
-// exchange between the two half-waves, and the row sum none until the end.
-// Softmax runs in the exp2 domain with the scale folded into one FMA; the
-// probabilities are rounded to fp16 (v_cvt_pk_f16_f32) and summed from those
-// rounded values (v_dot2c_f32_f16), and O^T = V^T P^T runs on
-// v_mfma_f32_32x32x16_f16 with P taken straight from the score registers. The
-// O rescale is skipped when no query of the wave raised its running max.
+// Per block: 4 waves x 32 queries, two blocks per CU. K and V tiles of 64 keys
+// go from HBM straight into LDS (buffer_load ... lds, 16 bytes per lane, no
+// registers on the way), two stages deep: the next tile's copy is issued
+// before the current tile's math. Both stay row-major in LDS with their
+// 16-byte chunks XOR-swizzled by row (the copying lane picks the source
+// chunk), so every fragment read below is free of bank conflicts.
+//
+// Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K rows read
+// with ds_read_b128), so a lane owns one query and 32 of the tile's keys: the
+// row max needs one exchange between the two half-waves and the row sum none
+// until the end. Softmax runs in the exp2 domain with the scale folded into
+// one FMA. The running max is raised only when a score exceeds it by more than
+// 2^8 in probability (a smaller excess stays exact in fp32 and bf16), so the O
+// rescale is rare. P is rounded to bf16 (v_cvt_pk_bf16_f32) and summed from
+// the rounded values (v_dot2c_f32_bf16). O^T = V^T P^T runs on the same MFMA
+// with P taken straight from the score registers; its V^T operand comes from
+// two ds_read_b64_tr_b16 per lane, each a 4x4 transpose of 16-bit elements
+// inside 16 lanes, which hands every lane 4 consecutive keys of one feature in
+// the key order the score registers have.
+//
+// Query tiles whose positions all lie below kSplitPos see so few keys that one
+// probability can carry most of a row; there P is applied as a bf16 pair
+// hi + lo (two MFMAs), which keeps the product accurate to about 2^-16 of |P|.
 //
 // A plain fp32 kernel (one thread per query, exact expf) serves fp32 inputs.
 #include <math.h>
@@ -41,87 +55,201 @@ struct AttnArgs {
 };
 
 constexpr int kBQ = 128, kBKey = 64, kAttnThreads = 256;
+// Query tiles whose last position is below this use the hi + lo split of P.
+[[maybe_unused]] constexpr int kSplitPos = 1024;
+// The running max is raised once a score exceeds it by more than this (log2).
+[[maybe_unused]] constexpr float kRescaleLog2 = 8.0f;
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define TSP_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// Geometry of one K or V tile (64 rows of DH bf16) in LDS.
 template <int DH>
-__device__ __forceinline__ int k_swz(int row, int ch) {  // element offset of chunk ch of K row
-  constexpr int CPR = DH / 8;
-  const int f = CPR == 16 ? (row & 15) : ((row >> 1) & 7);
-  return row * DH + ((ch ^ f) << 3);
+struct KvTile {
+  static constexpr int ROWB = DH * 2;                     // bytes per row
+  static constexpr int CPR = DH / 8;                      // 16-byte chunks per row
+  static constexpr int BYTES = kBKey * ROWB;              // 16 KB (DH 128) or 8 KB (DH 64)
+  static constexpr int ROWS_PER_KB = 1024 / ROWB;         // rows per 1 KB copy window
+  static constexpr int WIN_PER_WAVE = BYTES / 1024 / 4;   // copy windows per wave
+  // Chunk position of logical chunk ch of a K row: the 16 rows that one
+  // 16-lane group reads (same logical chunk) land in 16 distinct bank groups.
+  static __device__ __forceinline__ int k_swz(int row, int ch) {
+    return ch ^ (CPR == 16 ? (row & 15) : ((row >> 1) & 7));
+  }
+  // Chunk position of logical chunk ch of a V row: the 4 rows x 4 chunks that
+  // one transpose read of 32 lanes touches land in 16 distinct bank groups.
+  static __device__ __forceinline__ int v_swz(int row, int ch) {
+    return ch ^ (CPR == 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1));
+  }
+};
+
+// The descriptor type and the LDS-copy builtins exist only for the device
+// target, so the helpers and the kernel body below are compiled in the device
+// pass only (the host pass just needs the kernel's signature for its stub).
+#if defined(__HIP_DEVICE_COMPILE__)
+// Buffer descriptor over rows [k0, min(k0 + 64, S)) of one head of K or V:
+// loads past the last valid row return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16 *head_base, int64_t k0, int64_t S,
+                                                            int64_t rs) {
+  const int64_t rows = min<int64_t>(kBKey, S - k0);
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(head_base + k0 * rs), (short)0, (int)(rows * rs * 2),
+                                           0x00020000);
 }
-__device__ __forceinline__ int v_swz(int d, int unit) {  // element offset of 4-key unit of V^T row d
-  return d * kBKey + ((unit ^ ((d >> 1) & 15)) << 2);
+
+// One 64-key tile for one wave, as two 32-key steps: scores, online softmax,
+// O^T += V^T P^T. MASK: the tile reaches past some query of the wave
+// (diagonal tile). SPLIT: P enters the product as bf16 hi + lo.
+template <int DH, bool MASK, bool SPLIT>
+__device__ __forceinline__ void attn_tile(const unsigned char *__restrict__ Ks, const unsigned char *__restrict__ Vs,
+                                          const bf16x8 (&qf)[DH / 16], f32x16 (&oacc)[DH / 32], float &m_run,
+                                          float &l_part, int kstart, int qpos, float c, int lane) {
+  using G = KvTile<DH>;
+  constexpr int ND = DH / 32;
+  const int g = lane >> 5, l32 = lane & 31;
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  // transpose-read addressing: lane r of each 16-lane group points at key
+  // (base + r/4), features (16*((lane/16)%2) + 4*(r%4)) .. +3 of a 32-feature block
+  const int r16 = lane & 15, dsub = (lane >> 4) & 1;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    // ---- S^T = K Q^T for keys kb*32 .. +31 of the tile
+    f32x16 sacc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+    const int row = kb * 32 + l32;
+#pragma unroll
+    for (int kk = 0; kk < DH / 16; ++kk) {
+      const bf16x8 kf =
+          *reinterpret_cast<const bf16x8 *>(Ks + row * G::ROWB + G::k_swz(row, kk * 2 + g) * 16);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // sacc[v] is the score of key kstart + kb*32 + 8*(v/4) + 4*g + v%4
+    if constexpr (MASK) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = kstart + kb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+        if (key > qpos) sacc[v] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
+    mx = halves_max(mx);
+    // scaled max; -inf stays -inf (c >= 0)
+    const float mxs = mx == -INFINITY ? -INFINITY : mx * c;
+    if (__any(mxs > m_run + kRescaleLog2)) {
+      const float m_new = fmaxf(m_run, mxs);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+    }
+    const float neg_m = -m_run;
+    // ---- probabilities, 16 keys (8 per lane) per step, and O^T += V^T P^T
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int kq = kb * 2 + kh;  // 16-key group within the tile
+      bf16x8 ph, pl;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kh * 8 + e], c, neg_m));
+        float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kh * 8 + e + 1], c, neg_m));
+        if constexpr (MASK) {
+          // masked scores hold -inf, which a zero scale would turn into NaN
+          const int key0 = kstart + kb * 32 + (kh * 2 + (e >> 2)) * 8 + g * 4 + (e & 3);
+          if (key0 > qpos) p0 = 0.f;
+          if (key0 + 1 > qpos) p1 = 0.f;
+        }
+        const bf16x2 h2 = {(bf16)p0, (bf16)p1};
+        ph[e] = h2[0];
+        ph[e + 1] = h2[1];
+        if constexpr (SPLIT) {
+          const bf16x2 l2 = {(bf16)(p0 - (float)h2[0]), (bf16)(p1 - (float)h2[1])};
+          pl[e] = l2[0];
+          pl[e + 1] = l2[1];
+          l_part += p0 + p1;
+        } else {
+          l_part = __builtin_amdgcn_fdot2_f32_bf16(h2, ones, l_part, false);
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const int dstart = db * 32 + dsub * 16 + 4 * (r16 & 3);
+        s16x4 part[2];
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv) {
+          const int key = kq * 16 + hv * 8 + g * 4 + (r16 >> 2);
+          const unsigned char *addr = Vs + key * G::ROWB + G::v_swz(key, dstart >> 3) * 16 + (dstart & 7) * 2;
+          part[hv] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(addr));
+        }
+        const s16x8_t both = {part[0][0], part[0][1], part[0][2], part[0][3],
+                              part[1][0], part[1][1], part[1][2], part[1][3]};
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph, oacc[db], 0, 0, 0);
+        if constexpr (SPLIT) oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl, oacc[db], 0, 0, 0);
+      }
+      // keep each 16-key step's operand reads next to its MFMAs (bounds the
+      // registers in flight; the other wave on the SIMD covers the latency)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
 }
+
+#endif  // __HIP_DEVICE_COMPILE__
 
 template <int DH, bool OUT_F32>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int CPR = DH / 8;                 // 16-byte chunks per K row
-  constexpr int K_LD = (kBKey * CPR) / kAttnThreads;  // K chunks per thread
-  constexpr int V_UNITS = 16 * (DH / 8);      // (4 keys x 8 features) units per tile
-  constexpr int ND = DH / 32;                 // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBKey * DH];
-  __shared__ __attribute__((aligned(16))) _Float16 Vt[2][DH * kBKey];
+#if defined(__HIP_DEVICE_COMPILE__)
+  using G = KvTile<DH>;
+  constexpr int ND = DH / 32;  // 32-row blocks of O^T
+  // [stage][K | V][tile]
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][G::BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int head = L / a.T, p = L - (L / a.T) * a.T;
-  const int64_t rs = (int64_t)a.H * DH;  // row pitch of q, k, v, o
+  const int64_t rs = (int64_t)a.H * DH;  // row pitch of q, k, v, o (elements)
   const bf16 *qg = reinterpret_cast<const bf16 *>(a.q) + head * DH;
   const bf16 *kg = reinterpret_cast<const bf16 *>(a.k) + head * DH;
   const bf16 *vg = reinterpret_cast<const bf16 *>(a.v) + head * DH;
 
-  u32x4 rk[K_LD], rv[4];
-  auto gload = [&](int kt) {
+  // Copy windows of this wave: window w covers rows w*ROWS_PER_KB.. of the
+  // tile; lane -> (row, chunk position); it loads the logical chunk that
+  // belongs at that position.
+  int k_off[G::WIN_PER_WAVE], v_off[G::WIN_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < G::WIN_PER_WAVE; ++i) {
+    const int win = wave * G::WIN_PER_WAVE + i;
+    const int row = win * G::ROWS_PER_KB + lane / G::CPR, pos = lane % G::CPR;
+    k_off[i] = (int)(row * rs * 2) + G::k_swz(row, pos) * 16;
+    v_off[i] = (int)(row * rs * 2) + G::v_swz(row, pos) * 16;
+  }
+  auto copy_tile = [&](int kt, int st) {
     const int64_t k0 = (int64_t)kt * kBKey;
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kg, k0, a.S, rs);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vg, k0, a.S, rs);
 #pragma unroll
-    for (int i = 0; i < K_LD; ++i) {
-      const int c = tid + kAttnThreads * i;
-      const int row = c / CPR, ch = c % CPR;
-      const int64_t key = k0 + row;
-      u32x4 zero = {0u, 0u, 0u, 0u};
-      rk[i] = key < a.S ? *reinterpret_cast<const u32x4 *>(kg + key * rs + ch * 8) : zero;
-    }
-    if (tid < V_UNITS) {
-      const int doct = tid % (DH / 8), kq = tid / (DH / 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t key = k0 + kq * 4 + i;
-        u32x4 zero = {0u, 0u, 0u, 0u};
-        rv[i] = key < a.S ? *reinterpret_cast<const u32x4 *>(vg + key * rs + doct * 8) : zero;
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < K_LD; ++i) {
-      const int c = tid + kAttnThreads * i;
-      const int row = c / CPR, ch = c % CPR;
-      *reinterpret_cast<u32x4 *>(&Ks[buf][k_swz<DH>(row, ch)]) = rk[i];
-    }
-    if (tid < V_UNITS) {
-      const int doct = tid % (DH / 8), kq = tid / (DH / 8);
-      bf16x8 vb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vb[i] = __builtin_bit_cast(bf16x8, rv[i]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        f16x4 u;
-        u[0] = (_Float16)(float)vb[0][e];
-        u[1] = (_Float16)(float)vb[1][e];
-        u[2] = (_Float16)(float)vb[2][e];
-        u[3] = (_Float16)(float)vb[3][e];
-        *reinterpret_cast<f16x4 *>(&Vt[buf][v_swz(doct * 8 + e, kq)]) = u;
-      }
+    for (int i = 0; i < G::WIN_PER_WAVE; ++i) {
+      const int win = wave * G::WIN_PER_WAVE + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, TSP_LDS(&smem[st][0][win * 1024]), 16, k_off[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, TSP_LDS(&smem[st][1][win * 1024]), 16, v_off[i], 0, 0, 0);
     }
   };
 
   for (int half = 0; half < 2; ++half) {
-    const int tile = half == 0 ? p : 2 * a.T - 1 - p;
+    const int tile = half == 0 ? 2 * a.T - 1 - p : p;
     const int ch_half = tile < a.T ? 0 : 1;
     const int row0 = ch_half * a.zz.C + (tile - ch_half * a.T) * kBQ;  // first local row of the tile
     const int nvalid = min(kBQ, (ch_half + 1) * a.zz.C - row0);
     const int pos0 = a.zz.pos(row0);  // positions are consecutive inside a tile
     const int n_kt = (pos0 + nvalid - 1) / kBKey + 1;
+    const bool split = pos0 + nvalid - 1 < kSplitPos;
 
     const int wrow0 = wave * 32;
     const int w_nvalid = max(0, min(32, nvalid - wrow0));
@@ -129,6 +257,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
     const bool my_valid = wrow0 + l32 < nvalid;
     const int qpos = pos0 + min(wrow0 + l32, nvalid - 1);
     const int64_t qrow = row0 + wrow0 + l32;
+
+    copy_tile(0, 0);
 
     bf16x8 qf[DH / 16];
 #pragma unroll
@@ -148,93 +278,28 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
       for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
     float m_run = -INFINITY, l_part = 0.f;
 
-    gload(0);
-    sstore(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
 
     for (int kt = 0; kt < n_kt; ++kt) {
       const int cur = kt & 1;
-      if (kt + 1 < n_kt) gload(kt + 1);
+      if (kt + 1 < n_kt) copy_tile(kt + 1, cur ^ 1);
       const int kstart = kt * kBKey;
       if (w_nvalid > 0 && kstart <= wmax) {
-        // ---- S^T = K Q^T for the 64 keys of this tile
-        f32x16 sacc[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
-#pragma unroll
-          for (int kk = 0; kk < DH / 16; ++kk) {
-            const int row = kb * 32 + l32;
-            const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&Ks[cur][k_swz<DH>(row, kk * 2 + g)]);
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb], 0, 0, 0);
-          }
-        }
-        // sacc[kb][v] is the score of key kstart + kb*32 + 8*(v/4) + 4*g + v%4
-        const bool need_mask = kstart + kBKey - 1 > wmin;
-        if (need_mask) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int key = kstart + kb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-              if (key > qpos) sacc[kb][v] = -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-        mx = halves_max(mx);
-        const float mxs = mx == -INFINITY ? -INFINITY : mx * a.c;
-        const float m_new = fmaxf(m_run, mxs);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        // ---- probabilities (fp16) and their partial row sum
-        f16x8 pf[2][2];
-        float psum = 0.f;
-        const _Float16 one = (_Float16)1.0f;
-        const f16x2 ones = {one, one};
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][hh * 8 + e], a.c, -m_new));
-              float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][hh * 8 + e + 1], a.c, -m_new));
-              if (need_mask) {
-                const int key0 = kstart + kb * 32 + (hh * 2 + (e >> 2)) * 8 + g * 4 + (e & 3);
-                if (key0 > qpos) p0 = 0.f;
-                if (key0 + 1 > qpos) p1 = 0.f;
-              }
-              f16x2 pr = {(_Float16)p0, (_Float16)p1};
-              pf[kb][hh][e] = pr[0];
-              pf[kb][hh][e + 1] = pr[1];
-              psum = __builtin_amdgcn_fdot2(pr, ones, psum, false);
-            }
-        l_part = l_part * alpha + psum;
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-          for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
-        }
-        // ---- O^T += V^T P^T, 16 keys per MFMA
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
-#pragma unroll
-          for (int db = 0; db < ND; ++db) {
-            const int d = db * 32 + l32;
-            const f16x4 lo = *reinterpret_cast<const f16x4 *>(&Vt[cur][v_swz(d, kq * 4 + g)]);
-            const f16x4 hi = *reinterpret_cast<const f16x4 *>(&Vt[cur][v_swz(d, kq * 4 + 2 + g)]);
-            const f16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[kq >> 1][kq & 1], oacc[db], 0, 0, 0);
-          }
-        }
+        const bool mask = kstart + kBKey - 1 > wmin;
+        const unsigned char *Ks = smem[cur][0], *Vs = smem[cur][1];
+        if (!mask && !split)
+          attn_tile<DH, false, false>(Ks, Vs, qf, oacc, m_run, l_part, kstart, qpos, a.c, lane);
+        else if (!split)
+          attn_tile<DH, true, false>(Ks, Vs, qf, oacc, m_run, l_part, kstart, qpos, a.c, lane);
+        else if (!mask)
+          attn_tile<DH, false, true>(Ks, Vs, qf, oacc, m_run, l_part, kstart, qpos, a.c, lane);
+        else
+          attn_tile<DH, true, true>(Ks, Vs, qf, oacc, m_run, l_part, kstart, qpos, a.c, lane);
       }
-      if (kt + 1 < n_kt) sstore(cur ^ 1);
+      // the next tile's copy has landed (this wave's part), and every wave is
+      // done with the current stage before it is overwritten
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
     }
 
@@ -253,14 +318,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
             *reinterpret_cast<float4 *>(og) = make_float4(o0, o1, o2, o3);
           } else {
             bf16 *og = reinterpret_cast<bf16 *>(a.o) + qrow * rs + head * DH + d0;
-            og[0] = (bf16)o0;
-            og[1] = (bf16)o1;
-            og[2] = (bf16)o2;
-            og[3] = (bf16)o3;
+            const bf16x2 w01 = {(bf16)o0, (bf16)o1}, w23 = {(bf16)o2, (bf16)o3};
+            u32x2 u = {__builtin_bit_cast(uint32_t, w01), __builtin_bit_cast(uint32_t, w23)};
+            *reinterpret_cast<u32x2 *>(og) = u;
           }
         }
     }
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 // fp32 inputs: one thread per query row, keys staged 64 at a time in LDS,

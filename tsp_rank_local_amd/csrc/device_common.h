@@ -9,6 +9,7 @@ namespace tsp {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -16,6 +17,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+
+// s_waitcnt immediate that waits for every outstanding vector-memory load
+// (vmcnt = 0) and leaves the export and LDS/scalar counters unconstrained.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 constexpr int kWave = 64;
 
