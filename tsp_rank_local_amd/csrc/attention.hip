@@ -96,109 +96,206 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16 *head_bas
                                            0x00020000);
 }
 
-// One 64-key tile for one wave, as two 32-key steps: scores, online softmax,
-// O^T += V^T P^T. MASK: the tile reaches past some query of the wave
-// (diagonal tile). SPLIT: P enters the product as bf16 hi + lo.
+// One 64-key tile for one wave: scores, online softmax, O^T += V^T P^T.
+// MASK: the tile reaches past some query of the wave (diagonal tile).
+// SPLIT: P enters the product as bf16 hi + lo.
+// Lane-constant LDS byte offsets of the fragment reads, relative to a tile:
+// k[kk]: the 16-byte K chunk (row lane%32, logical chunk 2*kk + lane/32);
+// rows 32.. of the tile are a constant 32*ROWB further (same swizzle).
+// v[db]: the transpose-read address for 32-feature block db and key group 0;
+// key group kq, half hv adds the constant (16*kq + 8*hv)*ROWB (the swizzle
+// depends only on key % 4, which those offsets keep).
+template <int DH>
+struct FragAddr {
+  int k[DH / 16];
+  int v[DH / 32];
+};
+
+template <int DH>
+__device__ __forceinline__ FragAddr<DH> frag_addr(int lane) {
+  using G = KvTile<DH>;
+  FragAddr<DH> fa;
+  const int g = lane >> 5, l32 = lane & 31, r16 = lane & 15, dsub = (lane >> 4) & 1;
+#pragma unroll
+  for (int kk = 0; kk < DH / 16; ++kk) fa.k[kk] = l32 * G::ROWB + G::k_swz(l32, kk * 2 + g) * 16;
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db) {
+    const int key = g * 4 + (r16 >> 2);
+    const int dstart = db * 32 + dsub * 16 + 4 * (r16 & 3);
+    fa.v[db] = key * G::ROWB + G::v_swz(key, dstart >> 3) * 16 + (dstart & 7) * 2;
+  }
+  return fa;
+}
+
 template <int DH, bool MASK, bool SPLIT>
 __device__ __forceinline__ void attn_tile(const unsigned char *__restrict__ Ks, const unsigned char *__restrict__ Vs,
-                                          const bf16x8 (&qf)[DH / 16], f32x16 (&oacc)[DH / 32], float &m_run,
-                                          float &l_part, int kstart, int qpos, float c, int lane) {
+                                          const FragAddr<DH> &fa, const bf16x8 (&qf)[DH / 16],
+                                          f32x16 (&oacc)[DH / 32], float &m_run, float &l_part, int kstart, int qpos,
+                                          float c, int lane) {
   using G = KvTile<DH>;
   constexpr int ND = DH / 32;
-  const int g = lane >> 5, l32 = lane & 31;
-  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-  // transpose-read addressing: lane r of each 16-lane group points at key
-  // (base + r/4), features (16*((lane/16)%2) + 4*(r%4)) .. +3 of a 32-feature block
-  const int r16 = lane & 15, dsub = (lane >> 4) & 1;
+  const int g = lane >> 5;
+  // ---- S^T = K Q^T for the 64 keys: two independent 32-key accumulators
+  // (raised issue priority while this wave feeds the matrix pipe, so the
+  // other wave of the SIMD fills the gaps with its softmax)
+  __builtin_amdgcn_s_setprio(1);
+  f32x16 sacc[2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    // ---- S^T = K Q^T for keys kb*32 .. +31 of the tile
-    f32x16 sacc;
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
-    const int row = kb * 32 + l32;
+    for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < DH / 16; ++kk) {
-      const bf16x8 kf =
-          *reinterpret_cast<const bf16x8 *>(Ks + row * G::ROWB + G::k_swz(row, kk * 2 + g) * 16);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc, 0, 0, 0);
+  for (int kk = 0; kk < DH / 16; ++kk)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + fa.k[kk] + kb * 32 * G::ROWB);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // sacc[v] is the score of key kstart + kb*32 + 8*(v/4) + 4*g + v%4
-    if constexpr (MASK) {
+  __builtin_amdgcn_s_setprio(0);
+  // sacc[kb][v] is the score of key kstart + kb*32 + 8*(v/4) + 4*g + v%4
+  if constexpr (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = kstart + kb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-        if (key > qpos) sacc[v] = -INFINITY;
+        if (key > qpos) sacc[kb][v] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
+  mx = halves_max(mx);
+  // scaled max; only a masked tile can leave a lane with -inf (and -inf * 0
+  // must not become NaN)
+  float mxs = mx * c;
+  if constexpr (MASK) mxs = mx == -INFINITY ? -INFINITY : mxs;
+  if (__any(mxs > m_run + kRescaleLog2)) {
+    const float m_new = fmaxf(m_run, mxs);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_part *= alpha;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+  }
+  const float neg_m = -m_run;
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  // ---- probabilities, 16 keys (8 per lane) per step, and O^T += V^T P^T
+#pragma unroll
+  for (int kq = 0; kq < 4; ++kq) {
+    const int kb = kq >> 1, v0 = (kq & 1) * 8;
+    bf16x8 ph, pl;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v0 + e], c, neg_m));
+      float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v0 + e + 1], c, neg_m));
+      if constexpr (MASK) {
+        // masked scores hold -inf, which a zero scale would turn into NaN
+        const int key0 = kstart + kq * 16 + (e >> 2) * 8 + g * 4 + (e & 3);
+        if (key0 > qpos) p0 = 0.f;
+        if (key0 + 1 > qpos) p1 = 0.f;
+      }
+      const bf16x2 h2 = {(bf16)p0, (bf16)p1};
+      ph[e] = h2[0];
+      ph[e + 1] = h2[1];
+      if constexpr (SPLIT) {
+        const bf16x2 l2 = {(bf16)(p0 - (float)h2[0]), (bf16)(p1 - (float)h2[1])};
+        pl[e] = l2[0];
+        pl[e + 1] = l2[1];
+        l_part += p0 + p1;
+      } else {
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(h2, ones, l_part, false);
       }
     }
-    float mx = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
-    mx = halves_max(mx);
-    // scaled max; -inf stays -inf (c >= 0)
-    const float mxs = mx == -INFINITY ? -INFINITY : mx * c;
-    if (__any(mxs > m_run + kRescaleLog2)) {
-      const float m_new = fmaxf(m_run, mxs);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_part *= alpha;
+    for (int db = 0; db < ND; ++db) {
+      // transpose read: lane r of each 16-lane group points at key
+      // 16*kq + 8*hv + 4*g + r/4 and features 16*((lane/16)%2) + 4*(r%4) .. +3
+      // of block db; it receives 4 consecutive keys of feature r of that group
+      s16x4 part[2];
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
-    }
-    const float neg_m = -m_run;
-    // ---- probabilities, 16 keys (8 per lane) per step, and O^T += V^T P^T
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int kq = kb * 2 + kh;  // 16-key group within the tile
-      bf16x8 ph, pl;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kh * 8 + e], c, neg_m));
-        float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kh * 8 + e + 1], c, neg_m));
-        if constexpr (MASK) {
-          // masked scores hold -inf, which a zero scale would turn into NaN
-          const int key0 = kstart + kb * 32 + (kh * 2 + (e >> 2)) * 8 + g * 4 + (e & 3);
-          if (key0 > qpos) p0 = 0.f;
-          if (key0 + 1 > qpos) p1 = 0.f;
-        }
-        const bf16x2 h2 = {(bf16)p0, (bf16)p1};
-        ph[e] = h2[0];
-        ph[e + 1] = h2[1];
-        if constexpr (SPLIT) {
-          const bf16x2 l2 = {(bf16)(p0 - (float)h2[0]), (bf16)(p1 - (float)h2[1])};
-          pl[e] = l2[0];
-          pl[e + 1] = l2[1];
-          l_part += p0 + p1;
-        } else {
-          l_part = __builtin_amdgcn_fdot2_f32_bf16(h2, ones, l_part, false);
-        }
+      for (int hv = 0; hv < 2; ++hv) {
+        const unsigned char *addr = Vs + fa.v[db] + (kq * 16 + hv * 8) * G::ROWB;
+        part[hv] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(addr));
       }
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const int dstart = db * 32 + dsub * 16 + 4 * (r16 & 3);
-        s16x4 part[2];
-#pragma unroll
-        for (int hv = 0; hv < 2; ++hv) {
-          const int key = kq * 16 + hv * 8 + g * 4 + (r16 >> 2);
-          const unsigned char *addr = Vs + key * G::ROWB + G::v_swz(key, dstart >> 3) * 16 + (dstart & 7) * 2;
-          part[hv] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(addr));
-        }
-        const s16x8_t both = {part[0][0], part[0][1], part[0][2], part[0][3],
-                              part[1][0], part[1][1], part[1][2], part[1][3]};
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph, oacc[db], 0, 0, 0);
-        if constexpr (SPLIT) oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl, oacc[db], 0, 0, 0);
-      }
-      // keep each 16-key step's operand reads next to its MFMAs (bounds the
-      // registers in flight; the other wave on the SIMD covers the latency)
-      __builtin_amdgcn_sched_barrier(0);
+      const s16x8_t both = {part[0][0], part[0][1], part[0][2], part[0][3],
+                            part[1][0], part[1][1], part[1][2], part[1][3]};
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph, oacc[db], 0, 0, 0);
+      if constexpr (SPLIT) oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl, oacc[db], 0, 0, 0);
     }
   }
 }
 
+// What one block needs to copy K/V tiles of its head into LDS.
+template <int DH>
+struct KvCopy {
+  const bf16 *kg, *vg;  // head column of K and V
+  int64_t S, rs;        // rows, row pitch (elements)
+  int wave;
+  int k_off[KvTile<DH>::WIN_PER_WAVE], v_off[KvTile<DH>::WIN_PER_WAVE];
+};
+
+// Copy key tile kt into LDS stage st (this wave's windows).
+template <int DH>
+__device__ __forceinline__ void copy_tile(const KvCopy<DH> &cp, unsigned char (*smem)[2][KvTile<DH>::BYTES], int kt,
+                                          int st) {
+  using G = KvTile<DH>;
+  const int64_t k0 = (int64_t)kt * kBKey;
+  const __amdgpu_buffer_rsrc_t kr = tile_rsrc(cp.kg, k0, cp.S, cp.rs);
+  const __amdgpu_buffer_rsrc_t vr = tile_rsrc(cp.vg, k0, cp.S, cp.rs);
+#pragma unroll
+  for (int i = 0; i < G::WIN_PER_WAVE; ++i) {
+    const int win = cp.wave * G::WIN_PER_WAVE + i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, TSP_LDS(&smem[st][0][win * 1024]), 16, cp.k_off[i], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, TSP_LDS(&smem[st][1][win * 1024]), 16, cp.v_off[i], 0, 0, 0);
+  }
+}
+
+// Key tiles [kt0, kt1) of a walk of n_kt tiles: the tile in stage kt & 1 is
+// already in LDS when tile kt starts; tile kt + 1 is copied meanwhile. Each
+// variant runs its own loop so that the hot one carries no rare-case code.
+template <int DH, bool MASK, bool SPLIT, int CUR>
+__device__ __forceinline__ void attn_step(const KvCopy<DH> &cp, unsigned char (*smem)[2][KvTile<DH>::BYTES], int kt,
+                                          int n_kt, bool active, int wmax, const FragAddr<DH> &fa,
+                                          const bf16x8 (&qf)[DH / 16],
+                                          f32x16 (&oacc)[DH / 32], float &m_run, float &l_part, int qpos, float c,
+                                          int lane) {
+  if (kt + 1 < n_kt) copy_tile<DH>(cp, smem, kt + 1, CUR ^ 1);
+  const int kstart = kt * kBKey;
+  if (active && (!MASK || kstart <= wmax))
+    attn_tile<DH, MASK, SPLIT>(smem[CUR][0], smem[CUR][1], fa, qf, oacc, m_run, l_part, kstart, qpos, c, lane);
+  // the next tile's copy has landed (this wave's part), and every wave is
+  // done with the current stage before it is overwritten
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+}
+
+// Key tiles [kt0, kt1) of a walk of n_kt tiles: tile kt sits in LDS stage
+// kt & 1 when it starts, and tile kt + 1 is copied meanwhile. The loop runs
+// two tiles per trip so that each stage's LDS offsets are constants. Each
+// variant runs its own loop so that the hot one carries no rare-case code.
+template <int DH, bool MASK, bool SPLIT>
+__device__ __forceinline__ void attn_walk(const KvCopy<DH> &cp, unsigned char (*smem)[2][KvTile<DH>::BYTES], int kt0,
+                                          int kt1, int n_kt, bool active, int wmax, const FragAddr<DH> &fa,
+                                          const bf16x8 (&qf)[DH / 16],
+                                          f32x16 (&oacc)[DH / 32], float &m_run, float &l_part, int qpos, float c,
+                                          int lane) {
+  int kt = kt0;
+  if (kt < kt1 && (kt & 1)) {
+    attn_step<DH, MASK, SPLIT, 1>(cp, smem, kt, n_kt, active, wmax, fa, qf, oacc, m_run, l_part, qpos, c, lane);
+    ++kt;
+  }
+  for (; kt + 1 < kt1; kt += 2) {
+    attn_step<DH, MASK, SPLIT, 0>(cp, smem, kt, n_kt, active, wmax, fa, qf, oacc, m_run, l_part, qpos, c, lane);
+    attn_step<DH, MASK, SPLIT, 1>(cp, smem, kt + 1, n_kt, active, wmax, fa, qf, oacc, m_run, l_part, qpos, c, lane);
+  }
+  if (kt < kt1) attn_step<DH, MASK, SPLIT, 0>(cp, smem, kt, n_kt, active, wmax, fa, qf, oacc, m_run, l_part, qpos, c, lane);
+}
 #endif  // __HIP_DEVICE_COMPILE__
 
 template <int DH, bool OUT_F32>
@@ -216,31 +313,25 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
   const int head = L / a.T, p = L - (L / a.T) * a.T;
   const int64_t rs = (int64_t)a.H * DH;  // row pitch of q, k, v, o (elements)
   const bf16 *qg = reinterpret_cast<const bf16 *>(a.q) + head * DH;
-  const bf16 *kg = reinterpret_cast<const bf16 *>(a.k) + head * DH;
-  const bf16 *vg = reinterpret_cast<const bf16 *>(a.v) + head * DH;
 
   // Copy windows of this wave: window w covers rows w*ROWS_PER_KB.. of the
   // tile; lane -> (row, chunk position); it loads the logical chunk that
   // belongs at that position.
-  int k_off[G::WIN_PER_WAVE], v_off[G::WIN_PER_WAVE];
+  KvCopy<DH> cp;
+  cp.kg = reinterpret_cast<const bf16 *>(a.k) + head * DH;
+  cp.vg = reinterpret_cast<const bf16 *>(a.v) + head * DH;
+  cp.S = a.S;
+  cp.rs = rs;
+  cp.wave = wave;
 #pragma unroll
   for (int i = 0; i < G::WIN_PER_WAVE; ++i) {
     const int win = wave * G::WIN_PER_WAVE + i;
     const int row = win * G::ROWS_PER_KB + lane / G::CPR, pos = lane % G::CPR;
-    k_off[i] = (int)(row * rs * 2) + G::k_swz(row, pos) * 16;
-    v_off[i] = (int)(row * rs * 2) + G::v_swz(row, pos) * 16;
+    cp.k_off[i] = (int)(row * rs * 2) + G::k_swz(row, pos) * 16;
+    cp.v_off[i] = (int)(row * rs * 2) + G::v_swz(row, pos) * 16;
   }
-  auto copy_tile = [&](int kt, int st) {
-    const int64_t k0 = (int64_t)kt * kBKey;
-    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kg, k0, a.S, rs);
-    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vg, k0, a.S, rs);
-#pragma unroll
-    for (int i = 0; i < G::WIN_PER_WAVE; ++i) {
-      const int win = wave * G::WIN_PER_WAVE + i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, TSP_LDS(&smem[st][0][win * 1024]), 16, k_off[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, TSP_LDS(&smem[st][1][win * 1024]), 16, v_off[i], 0, 0, 0);
-    }
-  };
+
+  const FragAddr<DH> fa = frag_addr<DH>(lane);
 
   for (int half = 0; half < 2; ++half) {
     const int tile = half == 0 ? 2 * a.T - 1 - p : p;
@@ -249,16 +340,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
     const int nvalid = min(kBQ, (ch_half + 1) * a.zz.C - row0);
     const int pos0 = a.zz.pos(row0);  // positions are consecutive inside a tile
     const int n_kt = (pos0 + nvalid - 1) / kBKey + 1;
+    // key tiles below kt_diag lie wholly at or before every query of the block
+    const int kt_diag = min(n_kt, (pos0 + 1) / kBKey);
     const bool split = pos0 + nvalid - 1 < kSplitPos;
 
     const int wrow0 = wave * 32;
     const int w_nvalid = max(0, min(32, nvalid - wrow0));
-    const int wmin = pos0 + wrow0, wmax = pos0 + wrow0 + w_nvalid - 1;
+    const int wmax = pos0 + wrow0 + w_nvalid - 1;
+    const bool active = w_nvalid > 0;
     const bool my_valid = wrow0 + l32 < nvalid;
     const int qpos = pos0 + min(wrow0 + l32, nvalid - 1);
     const int64_t qrow = row0 + wrow0 + l32;
 
-    copy_tile(0, 0);
+    copy_tile<DH>(cp, smem, 0, 0);
 
     bf16x8 qf[DH / 16];
 #pragma unroll
@@ -281,26 +375,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
 
-    for (int kt = 0; kt < n_kt; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < n_kt) copy_tile(kt + 1, cur ^ 1);
-      const int kstart = kt * kBKey;
-      if (w_nvalid > 0 && kstart <= wmax) {
-        const bool mask = kstart + kBKey - 1 > wmin;
-        const unsigned char *Ks = smem[cur][0], *Vs = smem[cur][1];
-        if (!mask && !split)
-          attn_tile<DH, false, false>(Ks, Vs, qf, oacc, m_run, l_part, kstart, qpos, a.c, lane);
-        else if (!split)
-          attn_tile<DH, true, false>(Ks, Vs, qf, oacc, m_run, l_part, kstart, qpos, a.c, lane);
-        else if (!mask)
-          attn_tile<DH, false, true>(Ks, Vs, qf, oacc, m_run, l_part, kstart, qpos, a.c, lane);
-        else
-          attn_tile<DH, true, true>(Ks, Vs, qf, oacc, m_run, l_part, kstart, qpos, a.c, lane);
-      }
-      // the next tile's copy has landed (this wave's part), and every wave is
-      // done with the current stage before it is overwritten
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
+    if (split) {
+      attn_walk<DH, true, true>(cp, smem, 0, n_kt, n_kt, active, wmax, fa, qf, oacc, m_run, l_part, qpos, a.c, lane);
+    } else {
+      attn_walk<DH, false, false>(cp, smem, 0, kt_diag, n_kt, active, wmax, fa, qf, oacc, m_run, l_part, qpos, a.c,
+                                  lane);
+      attn_walk<DH, true, false>(cp, smem, kt_diag, n_kt, n_kt, active, wmax, fa, qf, oacc, m_run, l_part, qpos, a.c,
+                                 lane);
     }
 
     // ---- normalise and store: oacc[db][v] is O[query][db*32 + 8*(v/4) + 4*g + v%4]
