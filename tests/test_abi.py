@@ -52,12 +52,14 @@ def _shape(**kw):
 
 
 def test_workspace_sizes():
+    # MLP: GELU(x W1_j^T) of every ring step side by side, [N][F] in the dtype;
+    # layer: Q (later RMSNorm(h1)) and RMSNorm(x) (later O), [N][h] each, plus that
     s = _shape(dtype="bf16")
-    N, h, fd = 256, 256, 256
-    assert tsp.workspace_size(s, tsp.TSP_WS_MLP) == N * fd * 2
-    assert tsp.workspace_size(s, tsp.TSP_WS_LAYER) == 2 * N * h * 2 + N * fd * 2
+    N, h, F = 256, 256, 1024
+    assert tsp.workspace_size(s, tsp.TSP_WS_MLP) == N * F * 2
+    assert tsp.workspace_size(s, tsp.TSP_WS_LAYER) == 2 * N * h * 2 + N * F * 2
     s7 = tsp.make_shape(131072, 8, 0, 4096, 32, 128, 16384, dtype="bf16")
-    assert tsp.workspace_size(s7, tsp.TSP_WS_LAYER) == 2 * 16384 * 4096 * 2 + 16384 * 2048 * 2
+    assert tsp.workspace_size(s7, tsp.TSP_WS_LAYER) == 2 * 16384 * 4096 * 2 + 16384 * 16384 * 2
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -114,12 +114,13 @@ LayerWs layer_ws(const tsp_shape *s) {
   w.q = 0;
   w.x2 = align256(N * s->h * e);
   w.hid = w.x2 + align256(N * s->h * e);
-  w.total = w.hid + align256(N * (size_t)(s->F / s->D) * e);
+  w.total = w.hid + align256(N * (size_t)s->F * e);
   return w;
 }
 
+// GELU(x W1_j^T) of every ring step, [N][F] in ring-step column order.
 size_t mlp_ws(const tsp_shape *s) {
-  return align256((size_t)(s->S / s->D) * (size_t)(s->F / s->D) * elem_bytes(s->dtype));
+  return align256((size_t)(s->S / s->D) * (size_t)s->F * elem_bytes(s->dtype));
 }
 
 tsp_status hip_fail(hipError_t e, const char *what) {
@@ -130,6 +131,15 @@ tsp::PtrList to_list(const void *const *p, int D) {
   tsp::PtrList l;
   memset(&l, 0, sizeof l);
   for (int j = 0; j < D; ++j) l.p[j] = p[j];
+  return l;
+}
+
+// Shards in MLP ring order: entry t is the shard that reaches rank r at ring
+// step t, j = (r - t) mod D (it arrives from rank r-1).
+tsp::PtrList ring_list(const void *const *p, int D, int r) {
+  tsp::PtrList l;
+  memset(&l, 0, sizeof l);
+  for (int t = 0; t < D; ++t) l.p[t] = p[((r - t) % D + D) % D];
   return l;
 }
 
@@ -295,12 +305,13 @@ tsp_status tsp_mlp_ring(const tsp_shape *s, const void *x, const void *const *w1
   if (residual && residual != y && overlap(Range{residual, (size_t)N * h * 4, "residual"}, ry))
     return fail(TSP_ERR_INVALID_ARG, "residual overlaps y without being equal to it");
   hipStream_t stream = (hipStream_t)stream_;
-  for (int t = 0; t < s->D; ++t) {
-    const int j = ((s->r - t) % s->D + s->D) % s->D;
-    TSP_LAUNCH(TSP_K_MLP_UP, tsp::launch_mlp_up(s->dtype, x, N, h, w1[j], fd, ws, stream), "MLP up");
-    const float *res = t == 0 ? residual : y;
-    TSP_LAUNCH(TSP_K_MLP_DOWN, tsp::launch_mlp_down(s->dtype, ws, N, fd, w2[j], h, res, y, stream), "MLP down");
-  }
+  // every ring step's GELU(x W1_j^T) side by side, then one reduction over
+  // them and the W2 shards in ring order
+  TSP_LAUNCH(TSP_K_MLP_UP, tsp::launch_mlp_up(s->dtype, x, N, h, ring_list(w1, s->D, s->r), s->D, fd, ws, stream),
+             "MLP up");
+  TSP_LAUNCH(TSP_K_MLP_DOWN,
+             tsp::launch_mlp_down(s->dtype, ws, N, ring_list(w2, s->D, s->r), s->D, fd, h, residual, y, stream),
+             "MLP down");
   return ok();
 }
 
@@ -331,7 +342,7 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
   unsigned char *ws = static_cast<unsigned char *>(ws_);
   void *qbuf = ws + L.q;   // Q, later RMSNorm(h1)
   void *x2 = ws + L.x2;    // RMSNorm(x), later the attention output O
-  void *hid = ws + L.hid;  // GELU(hn W1_j^T) of the current ring step
+  void *hid = ws + L.hid;  // GELU(hn W1_j^T) of every ring step, side by side
   const tsp::ZigzagMap zz = tsp::make_zigzag(s->S, D, s->r);
   hipStream_t stream = (hipStream_t)stream_;
 
@@ -349,11 +360,11 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
     TSP_LAUNCH(TSP_K_OUTPROJ, tsp::launch_outproj(s->dtype, x2, N, h, to_list(w->wo, D), D, hd, x, y, stream),
                "output projection");
     TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(y, w->g_mlp, qbuf, N, h, s->eps, s->dtype, stream), "RMSNorm");
-    for (int t = 0; t < D; ++t) {
-      const int j = ((s->r - t) % D + D) % D;
-      TSP_LAUNCH(TSP_K_MLP_UP, tsp::launch_mlp_up(s->dtype, qbuf, N, h, w->w1[j], fd, hid, stream), "MLP up");
-      TSP_LAUNCH(TSP_K_MLP_DOWN, tsp::launch_mlp_down(s->dtype, hid, N, fd, w->w2[j], h, y, y, stream), "MLP down");
-    }
+    TSP_LAUNCH(TSP_K_MLP_UP,
+               tsp::launch_mlp_up(s->dtype, qbuf, N, h, ring_list(w->w1, D, s->r), D, fd, hid, stream), "MLP up");
+    TSP_LAUNCH(TSP_K_MLP_DOWN,
+               tsp::launch_mlp_down(s->dtype, hid, N, ring_list(w->w2, D, s->r), D, fd, h, y, y, stream),
+               "MLP down");
   }
   return ok();
 }

@@ -48,6 +48,50 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+#if defined(__HIP_DEVICE_COMPILE__)
+// ---------------------------------------------------------------- HBM -> LDS copies
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (N < 16; export and LDS/scalar counters unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Raw buffer descriptor over [base, base + bytes): base, base high with stride
+// 0, size in bytes, raw-buffer format. Loads at offsets >= bytes return zeros.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = (uint32_t)b;
+  r[1] = (uint32_t)(b >> 32) & 0xFFFFu;
+  r[2] = bytes;
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// LDS byte address of a __shared__ object (wave-uniform).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)(p));
+}
+
+// One 16-byte-per-lane copy from a buffer straight into LDS: lane i's 16
+// bytes at voffset + soffset land at lds_base + 16*i (buffer_load ... lds).
+// Issued as plain asm so that the compiler does not treat every later LDS
+// read as a possible reader of this copy (it would then wait for all copies
+// in flight, from HBM, before each read); callers order every copy before
+// its readers themselves (vmcnt waits and block barriers).
+__device__ __forceinline__ void lds_copy16(u32x4 rsrc, int voffset, int soffset, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voffset), "s"(rsrc), "s"(soffset), "s"(lds_base)
+      : "memory", "m0");
+}
+#endif  // __HIP_DEVICE_COMPILE__
+
 // Blocks are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
 // Remap so that consecutive logical tiles land on the same XCD and share its L2.
 __device__ __forceinline__ int xcd_remap(int b, int nblocks) {

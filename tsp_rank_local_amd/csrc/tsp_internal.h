@@ -49,12 +49,16 @@ hipError_t launch_qkv(int dtype, const void *xn, int32_t n, int32_t h, const Ptr
 // the reduction loop.
 hipError_t launch_outproj(int dtype, const void *o, int32_t n, int32_t h, const PtrList &wo, int32_t D,
                           int32_t hd, const float *x, float *y, hipStream_t s);
-// hid = GELU(x w1j^T) stored in dtype, w1j [fd][h].
-hipError_t launch_mlp_up(int dtype, const void *x, int32_t n, int32_t h, const void *w1j, int32_t fd,
+// MLP up over all D ring steps in one launch: hid[:, t*fd:(t+1)*fd] =
+// GELU(x w1[t]^T) in dtype, w1[t] [fd][h] the shard of ring step t; hid
+// [n][D*fd].
+hipError_t launch_mlp_up(int dtype, const void *x, int32_t n, int32_t h, const PtrList &w1, int32_t D, int32_t fd,
                          void *hid, hipStream_t s);
-// y = (res ? res : 0) + hid w2j^T in fp32, w2j [h][fd]; res may equal y.
-hipError_t launch_mlp_down(int dtype, const void *hid, int32_t n, int32_t fd, const void *w2j, int32_t h,
-                           const float *res, float *y, hipStream_t s);
+// y = (res ? res : 0) + sum_t hid[:, t*fd:(t+1)*fd] w2[t]^T in fp32, the
+// reduction walking ring steps t = 0..D-1 in order; w2[t] [h][fd]; res may
+// equal y.
+hipError_t launch_mlp_down(int dtype, const void *hid, int32_t n, const PtrList &w2, int32_t D, int32_t fd,
+                           int32_t h, const float *res, float *y, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 hipError_t launch_attention(int dtype, const void *q, const void *k, const void *v, void *o, int o_dtype,
