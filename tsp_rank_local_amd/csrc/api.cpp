@@ -283,7 +283,7 @@ tsp_status tsp_zigzag_attn(const tsp_shape *s, const void *q, const void *k, con
     if (overlap(ro, r)) return fail(TSP_ERR_INVALID_ARG, "o overlaps %s", r.name);
   hipStream_t stream = (hipStream_t)stream_;
   TSP_LAUNCH(TSP_K_ATTN,
-             tsp::launch_attention(s->dtype, q, k, v, o, o_dtype, s->S, (int32_t)N, s->H, s->Dh, s->scale,
+             tsp::launch_attention(s->dtype, q, k, v, o, o_dtype, false, s->S, (int32_t)N, s->H, s->Dh, s->scale,
                                    tsp::make_zigzag(s->S, s->D, s->r), stream),
              "attention");
   return ok();
@@ -305,12 +305,14 @@ tsp_status tsp_mlp_ring(const tsp_shape *s, const void *x, const void *const *w1
   if (residual && residual != y && overlap(Range{residual, (size_t)N * h * 4, "residual"}, ry))
     return fail(TSP_ERR_INVALID_ARG, "residual overlaps y without being equal to it");
   hipStream_t stream = (hipStream_t)stream_;
-  // every ring step's GELU(x W1_j^T) side by side, then one reduction over
-  // them and the W2 shards in ring order
-  TSP_LAUNCH(TSP_K_MLP_UP, tsp::launch_mlp_up(s->dtype, x, N, h, ring_list(w1, s->D, s->r), s->D, fd, ws, stream),
+  // every ring step's GELU(x W1_j^T) side by side (bf16: in 64-column
+  // panels), then one reduction over them and the W2 shards in ring order
+  const bool pnl = s->dtype == TSP_BF16;
+  TSP_LAUNCH(TSP_K_MLP_UP,
+             tsp::launch_mlp_up(s->dtype, x, false, N, h, ring_list(w1, s->D, s->r), s->D, fd, ws, pnl, stream),
              "MLP up");
   TSP_LAUNCH(TSP_K_MLP_DOWN,
-             tsp::launch_mlp_down(s->dtype, ws, N, ring_list(w2, s->D, s->r), s->D, fd, h, residual, y, stream),
+             tsp::launch_mlp_down(s->dtype, ws, pnl, N, ring_list(w2, s->D, s->r), s->D, fd, h, residual, y, stream),
              "MLP down");
   return ok();
 }
@@ -340,30 +342,36 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
       if (overlap(all[i], all[j])) return fail(TSP_ERR_INVALID_ARG, "%s overlaps %s", all[i].name, all[j].name);
 
   unsigned char *ws = static_cast<unsigned char *>(ws_);
+  // With bf16, every activation that a GEMM reads as its A operand (x2, O,
+  // RMSNorm(h1), H) is kept in 64-column panels; Q stays [N][H][Dh].
   void *qbuf = ws + L.q;   // Q, later RMSNorm(h1)
   void *x2 = ws + L.x2;    // RMSNorm(x), later the attention output O
   void *hid = ws + L.hid;  // GELU(hn W1_j^T) of every ring step, side by side
   const tsp::ZigzagMap zz = tsp::make_zigzag(s->S, D, s->r);
+  const bool pnl = s->dtype == TSP_BF16;
   hipStream_t stream = (hipStream_t)stream_;
 
   if (phases & TSP_PHASE_KV) {
-    TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(x, w->g_attn, x2, N, h, s->eps, s->dtype, stream), "RMSNorm");
+    TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(x, w->g_attn, x2, N, h, s->eps, s->dtype, pnl, stream), "RMSNorm");
     TSP_LAUNCH(TSP_K_QKV,
-               tsp::launch_qkv(s->dtype, x2, N, h, to_list(w->wqkv, D), D, hd, qbuf, k_full, v_full, zz, stream),
+               tsp::launch_qkv(s->dtype, x2, pnl, N, h, to_list(w->wqkv, D), D, hd, qbuf, k_full, v_full, zz, stream),
                "QKV");
   }
   if (phases & TSP_PHASE_REST) {
     TSP_LAUNCH(TSP_K_ATTN,
-               tsp::launch_attention(s->dtype, qbuf, k_full, v_full, x2, s->dtype, s->S, N, s->H, s->Dh, s->scale,
-                                     zz, stream),
+               tsp::launch_attention(s->dtype, qbuf, k_full, v_full, x2, s->dtype, pnl, s->S, N, s->H, s->Dh,
+                                     s->scale, zz, stream),
                "attention");
-    TSP_LAUNCH(TSP_K_OUTPROJ, tsp::launch_outproj(s->dtype, x2, N, h, to_list(w->wo, D), D, hd, x, y, stream),
+    TSP_LAUNCH(TSP_K_OUTPROJ,
+               tsp::launch_outproj(s->dtype, x2, pnl, N, h, to_list(w->wo, D), D, hd, x, y, stream),
                "output projection");
-    TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(y, w->g_mlp, qbuf, N, h, s->eps, s->dtype, stream), "RMSNorm");
+    TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(y, w->g_mlp, qbuf, N, h, s->eps, s->dtype, pnl, stream),
+               "RMSNorm");
     TSP_LAUNCH(TSP_K_MLP_UP,
-               tsp::launch_mlp_up(s->dtype, qbuf, N, h, ring_list(w->w1, D, s->r), D, fd, hid, stream), "MLP up");
+               tsp::launch_mlp_up(s->dtype, qbuf, pnl, N, h, ring_list(w->w1, D, s->r), D, fd, hid, pnl, stream),
+               "MLP up");
     TSP_LAUNCH(TSP_K_MLP_DOWN,
-               tsp::launch_mlp_down(s->dtype, hid, N, ring_list(w->w2, D, s->r), D, fd, h, y, y, stream),
+               tsp::launch_mlp_down(s->dtype, hid, pnl, N, ring_list(w->w2, D, s->r), D, fd, h, y, y, stream),
                "MLP down");
   }
   return ok();

@@ -51,7 +51,8 @@ struct AttnArgs {
   float scale;  // softmax scale
   float c;      // scale * log2(e)
   ZigzagMap zz;
-  int32_t T;  // query tiles per chunk
+  int32_t T;         // query tiles per chunk
+  int64_t o_panel;   // bf16 O: panel stride (64-column panels) or 0 for [n][H][Dh]
 };
 
 constexpr int kBQ = 128, kBKey = 64, kAttnThreads = 256;
@@ -398,7 +399,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
             float *og = reinterpret_cast<float *>(a.o) + qrow * rs + head * DH + d0;
             *reinterpret_cast<float4 *>(og) = make_float4(o0, o1, o2, o3);
           } else {
-            bf16 *og = reinterpret_cast<bf16 *>(a.o) + qrow * rs + head * DH + d0;
+            const int64_t col = head * DH + d0;
+            bf16 *og = reinterpret_cast<bf16 *>(a.o) + (a.o_panel ? panel_index(qrow, col, a.o_panel) : qrow * rs + col);
             const bf16x2 w01 = {(bf16)o0, (bf16)o1}, w23 = {(bf16)o2, (bf16)o3};
             u32x2 u = {__builtin_bit_cast(uint32_t, w01), __builtin_bit_cast(uint32_t, w23)};
             *reinterpret_cast<u32x2 *>(og) = u;
@@ -464,9 +466,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 }
 
 hipError_t launch_attention(int dtype, const void *q, const void *k, const void *v, void *o, int o_dtype,
-                            int64_t S, int32_t n, int32_t H, int32_t Dh, float scale, ZigzagMap zz,
+                            bool o_panel, int64_t S, int32_t n, int32_t H, int32_t Dh, float scale, ZigzagMap zz,
                             hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  if (o_panel && (dtype != TSP_BF16 || o_dtype != TSP_BF16)) return hipErrorInvalidValue;
   AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -479,6 +482,7 @@ hipError_t launch_attention(int dtype, const void *q, const void *k, const void 
   a.c = scale * 1.4426950408889634f;
   a.zz = zz;
   a.T = (zz.C + kBQ - 1) / kBQ;
+  a.o_panel = o_panel ? (int64_t)n * kPanel : 0;
   if (dtype == TSP_BF16) {
     dim3 grid(H * a.T);
     const bool f32out = o_dtype == TSP_F32;

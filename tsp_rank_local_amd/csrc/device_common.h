@@ -51,11 +51,13 @@ __device__ __forceinline__ float halves_sum(float x) {
 #if defined(__HIP_DEVICE_COMPILE__)
 // ---------------------------------------------------------------- HBM -> LDS copies
 // Wait until at most N vector-memory operations of this wave are outstanding
-// (N < 16; export and LDS/scalar counters unconstrained).
+// (N < 64; the count's low 4 bits sit in bits 3:0 of the s_waitcnt immediate
+// and its high 2 bits in bits 15:14; export and LDS/scalar counters are left
+// unconstrained).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Raw buffer descriptor over [base, base + bytes): base, base high with stride
@@ -85,7 +87,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 __device__ __forceinline__ void lds_copy16(u32x4 rsrc, int voffset, int soffset, uint32_t lds_base) {
   asm volatile(
       "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"  // one wait state between an M0 write and an LDS copy
       "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voffset), "s"(rsrc), "s"(soffset), "s"(lds_base)
+      : "memory", "m0");
+}
+
+// Same with 4 bytes per lane (lane i -> lds_base + 4*i). Used to pull lines
+// into L2 ahead of their copies: the data lands in a scratch LDS area nobody
+// reads, so no register has to stay reserved while the load is in flight.
+__device__ __forceinline__ void lds_touch4(u32x4 rsrc, int voffset, int soffset, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %0, %1, %2 offen lds"
       :
       : "v"(voffset), "s"(rsrc), "s"(soffset), "s"(lds_base)
       : "memory", "m0");

@@ -8,17 +8,25 @@
 //   MLP down : the reduction walks H and the D W2 shards in ring order, + h1
 //
 // bf16 operands run on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
-// Block tile 256 (M) x 256 (N), 8 waves as 4 (M) x 2 (N), each wave owning
-// 64 x 128 of the output as 2 x 4 MFMA accumulators of 32 x 32. The MFMAs
-// produce C^T blocks (B rows are the first operand), so a lane holds 4
+// Block tile 256 (M) x 256 (N), 4 waves as 2 (M) x 2 (N), one per SIMD, each
+// owning 128 x 128 of the output as 4 x 4 MFMA accumulators of 32 x 32. The
+// MFMAs produce C^T blocks (B rows are the first operand), so a lane holds 4
 // consecutive output columns of one row and every epilogue access is a 16-
 // (fp32) or 8-byte (bf16) vector.
-// K advances 32 at a time through a ring of 4 LDS stages (A and B tiles of
-// 256 x 32, 32 KB per stage, 128 KB): tiles go from HBM straight into LDS
-// (buffer_load ... lds, 16 bytes per lane) three steps ahead of their use,
-// one block barrier per step. LDS rows are 64 bytes; the 16-byte chunk index
-// is XOR-swizzled by (row/4)%4 (the copying lane picks its source chunk), so
-// the 16 lanes that read one chunk of 16 rows hit 16 distinct bank groups.
+// K advances 64 at a time through 2 LDS stages (A and B tiles of 256 x 64,
+// 64 KB per stage): tiles go from HBM straight into LDS (buffer_load ... lds,
+// 16 bytes per lane), one block barrier per step. The copies of a step are
+// spread over the MFMAs of the last K slice of the step two earlier, and the
+// step after that is prefetched into L2 with one dword load per 128-byte
+// line, so the copies mostly hit L2. Fragment reads of the next K slice are
+// interleaved with the MFMAs of the current one. LDS rows are 128 bytes; the
+// 16-byte chunk index is XOR-swizzled by (row/2)%8 (the copying lane picks
+// its source chunk), so the lanes that read one chunk of 32 rows spread over
+// all bank groups.
+// The A operand may come in the panel layout (64-column panels of [M][64]):
+// then one A tile of a step is 32 KB of contiguous memory, which the copy
+// engine streams at close to its full rate; from row-major A with a long row
+// pitch every copy instruction touches 8 rows far apart and the rate halves.
 // fp32 operands use a plain LDS-tiled FMA kernel (64x64 tiles, 4x4 per thread).
 #include "device_common.h"
 #include "tsp_internal.h"
@@ -26,8 +34,9 @@
 namespace tsp {
 
 struct GemmArgs {
-  const void *A;  // [M][K_total] (lda elements per row)
+  const void *A;  // [M][K_total] (lda elements per row), or panel layout
   int64_t lda;
+  int64_t a_panel;  // bf16 only: panel stride of A in elements (M_alloc * 64), 0 = row-major
   PtrList B;      // B segments: segment s holds columns [s*kseg, (s+1)*kseg) of B
   int64_t ldb;    // row pitch of every B segment
   int32_t kseg;   // reduction length covered by one B pointer
@@ -49,18 +58,21 @@ __device__ __forceinline__ void store4(T *p, float4 v) {
   }
 }
 
-// H[:, z*cols + c] = GELU(acc): problem z is ring step z's shard.
+// H[:, z*cols + c] = GELU(acc): problem z is ring step z's shard. H is
+// row-major with pitch ld, or in panel layout when panel != 0.
 template <typename T>
 struct EpiGelu {
   T *out;
-  int64_t ld;    // row pitch of H
-  int32_t cols;  // columns per shard
-  __device__ __forceinline__ void operator()(int z, int r, int c, float v) const {
-    out[(int64_t)r * ld + (int64_t)z * cols + c] = (T)gelu_erf(v);
+  int64_t ld;     // row pitch of row-major H
+  int64_t panel;  // panel stride of H, or 0
+  int32_t cols;   // columns per shard
+  __device__ __forceinline__ T *at(int z, int r, int c) const {
+    const int64_t col = (int64_t)z * cols + c;
+    return out + (panel ? panel_index(r, col, panel) : (int64_t)r * ld + col);
   }
+  __device__ __forceinline__ void operator()(int z, int r, int c, float v) const { *at(z, r, c) = (T)gelu_erf(v); }
   __device__ __forceinline__ void operator()(int z, int r, int c, float4 v) const {
-    store4(out + (int64_t)r * ld + (int64_t)z * cols + c,
-           make_float4(gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w)));
+    store4(at(z, r, c), make_float4(gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w)));
   }
 };
 
@@ -133,14 +145,25 @@ __device__ __forceinline__ TileCoord tile_of(int L, int tiles_m, int tiles_n) {
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
-constexpr int kBM = 256, kBN = 256, kBK = 32, kGemmThreads = 512, kGemmStages = 4;
-constexpr int kTileBytes = kBM * kBK * 2;                       // one 256 x 32 bf16 tile: 16 KB
+constexpr int kBM = 256, kBN = 256, kBK = 64, kGemmThreads = 256, kGemmStages = 2;
+constexpr int kRowBytes = kBK * 2;                              // 128: one cache line per tile row and step
+constexpr int kTileBytes = kBM * kRowBytes;                     // one 256 x 64 bf16 tile: 32 KB
 constexpr int kGemmStageBytes = 2 * kTileBytes;                 // A tile + B tile
 constexpr size_t kGemmLds = (size_t)kGemmStages * kGemmStageBytes;  // 128 KB
-constexpr int kGemmLoads = 4;  // copy instructions per wave per K step
+constexpr int kGemmWaves = kGemmThreads / 64;
+constexpr int kWinPerWave = kTileBytes / 1024 / kGemmWaves;     // 1 KB copy windows per wave, per tile
+constexpr int kGemmSlices = kBK / 16;                           // 16-wide K slices per step
 
-// Byte offset of logical 16-byte chunk ch (0..3) of row r in a 64-byte-row tile.
-__device__ __forceinline__ int gswz(int r, int ch) { return r * 64 + ((ch ^ ((r >> 2) & 3)) << 4); }
+// Byte offset of logical 16-byte chunk ch (0..7) of row r in a 128-byte-row
+// tile: the 16 rows that 16 lanes read with one logical chunk land in 16
+// distinct bank groups.
+__device__ __forceinline__ int gswz(int r, int ch) { return r * kRowBytes + ((ch ^ ((r >> 1) & 7)) << 4); }
+
+// Fragments of one 16-wide K slice for a wave's 128 x 128 output: 4 A row
+// blocks (M) and 4 B row blocks (N) of 32.
+struct GemmFrags {
+  bf16x8 a[4], b[4];
+};
 
 template <class Epi>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, Epi epi) {
@@ -153,108 +176,202 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;  // wave tile: rows wm*64.., columns wn*128..
+  const int wm = wave >> 1, wn = wave & 1;  // wave tile: rows wm*128.., columns wn*128..
   const int g = lane >> 5, l32 = lane & 31;
 
-  // ---- copy plan: each wave copies A windows 2*wave, 2*wave+1 and the same B
-  // windows of every stage; window w = tile rows 16w..16w+15 (1 KB). Lane ->
-  // (row, chunk position); it loads the logical chunk that belongs there.
+  // ---- copy plan: each wave copies windows kWinPerWave*wave.. of the A and
+  // B tiles of a step; window w = tile rows 8w..8w+7 (1 KB). Lane -> (row,
+  // chunk position); it loads the logical chunk that belongs there.
   const uint32_t lds0 = lds_addr(smem);
-  int a_off[2], b_off[2];
+  const bool a_panel = a.a_panel != 0;
+  const int64_t a_pitch = a_panel ? kPanel : a.lda;  // elements between A rows
+  int a_off[kWinPerWave], b_off[kWinPerWave];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int win = 2 * wave + i, row = win * 16 + lane / 4, pos = lane & 3;
-    const int ch = pos ^ ((row >> 2) & 3);
-    a_off[i] = (int)(row * a.lda * 2) + ch * 16;
+  for (int i = 0; i < kWinPerWave; ++i) {
+    const int win = kWinPerWave * wave + i, row = win * 8 + lane / 8, pos = lane & 7;
+    const int ch = pos ^ ((row >> 1) & 7);
+    a_off[i] = (int)(row * a_pitch * 2) + ch * 16;
     b_off[i] = (int)(row * a.ldb * 2) + ch * 16;
   }
   const int a_rows = min(kBM, a.M - m0), b_rows = min(kBN, a.N - n0);
-  const bf16 *Ab = reinterpret_cast<const bf16 *>(a.A) + (int64_t)m0 * a.lda;
-  const u32x4 ar = buffer_rsrc(Ab, (uint32_t)(a_rows * a.lda * 2));
-  auto copy_step = [&](int kt, int st) {
+  const bf16 *Ab = reinterpret_cast<const bf16 *>(a.A) + (int64_t)m0 * a_pitch;
+
+  // B segment pointers are read from LDS inside the loop: a scalar load
+  // there would turn every wait on the LDS counter into a full wait.
+  __shared__ uint64_t bptr_s[TSP_MAX_D];
+  if (tid < TSP_MAX_D) bptr_s[tid] = (uint64_t)(uintptr_t)a.B.p[tid];
+  auto seg_of = [&](int kt, int &koff) {
     const int k0 = kt * kBK;
-    int seg, koff;
     if (a.nz > 1) {
-      seg = z;
       koff = k0;
-    } else {
-      seg = k0 / a.kseg;
-      koff = k0 - seg * a.kseg;
+      return z;
     }
-    const bf16 *Bb = reinterpret_cast<const bf16 *>(a.B.p[seg]) + (int64_t)n0 * a.ldb;
-    const u32x4 br = buffer_rsrc(Bb, (uint32_t)(b_rows * a.ldb * 2));
+    const int seg = k0 / a.kseg;
+    koff = k0 - seg * a.kseg;
+    return seg;
+  };
+  auto bptr_at = [&](int seg) {
+    const uint64_t v = bptr_s[seg];
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    return reinterpret_cast<const bf16 *>((uintptr_t)(((uint64_t)hi << 32) | lo));
+  };
+  // Where step kt's tiles come from: row-major A keeps one descriptor over
+  // the block's rows and moves along K with soffset; panel A takes one
+  // descriptor per step over the block's rows of that panel.
+  struct StepSrc {
+    u32x4 ar, br;
+    int a_soff, b_soff;
+  };
+  auto step_src = [&](int kt, const bf16 *bseg, int koff) {
+    StepSrc t;
+    t.br = buffer_rsrc(bseg + (int64_t)n0 * a.ldb, (uint32_t)(b_rows * a.ldb * 2));
+    t.b_soff = koff * 2;
+    if (a_panel) {
+      t.ar = buffer_rsrc(Ab + (int64_t)kt * a.a_panel, (uint32_t)(a_rows * kRowBytes));
+      t.a_soff = 0;
+    } else {
+      t.ar = buffer_rsrc(Ab, (uint32_t)(a_rows * a_pitch * 2));
+      t.a_soff = kt * kBK * 2;
+    }
+    return t;
+  };
+  // copies of windows 2q, 2q+1 of the A and B tiles into stage st
+  auto copy_part = [&](const StepSrc &t, int st, int q) {
     const uint32_t base = lds0 + st * kGemmStageBytes;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t win = 2 * wave + i;
-      lds_copy16(ar, a_off[i], k0 * 2, base + win * 1024);
-      lds_copy16(br, b_off[i], koff * 2, base + kTileBytes + win * 1024);
+    for (int i = 2 * q; i < 2 * q + 2; ++i) {
+      const uint32_t win = kWinPerWave * wave + i;
+      lds_copy16(t.ar, a_off[i], t.a_soff, base + win * 1024);
+      lds_copy16(t.br, b_off[i], t.b_soff, base + kTileBytes + win * 1024);
+    }
+  };
+  // L2 prefetch of a step's tiles: each lane touches one 128-byte line of the
+  // A tile and one of the B tile (row wave*64 + lane) with a dword load into
+  // a scratch LDS area that nobody reads.
+  __shared__ uint32_t pf_sink[64];
+  const uint32_t sink = lds_addr(pf_sink);
+  const int pf_va = (wave * 64 + lane) * (int)(a_pitch * 2), pf_vb = (wave * 64 + lane) * (int)(a.ldb * 2);
+  auto prefetch = [&](const StepSrc &t) {
+    lds_touch4(t.ar, pf_va, t.a_soff, sink);
+    lds_touch4(t.br, pf_vb, t.b_soff, sink);
+  };
+
+  // fragment read offsets inside a stage for K slice kk: A rows wm*128 +
+  // j*32 + l32, B rows wn*128 + i*32 + l32, chunk 2*kk + g
+  int fa_a[kGemmSlices][4], fa_b[kGemmSlices][4];
+#pragma unroll
+  for (int kk = 0; kk < kGemmSlices; ++kk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa_a[kk][i] = gswz(wm * 128 + i * 32 + l32, 2 * kk + g);
+      fa_b[kk][i] = kTileBytes + gswz(wn * 128 + i * 32 + l32, 2 * kk + g);
+    }
+  // fragment pair q of K slice kk: q = 0, 1 -> A blocks 2q, 2q+1; q = 2, 3 ->
+  // B blocks 2q-4, 2q-3 (the first MFMA row of a slice needs every A block)
+  auto read_pair = [&](GemmFrags &f, int st, int kk, int q) {
+    const unsigned char *sb = smem + st * kGemmStageBytes;
+    if (q < 2) {
+      f.a[2 * q] = *reinterpret_cast<const bf16x8 *>(sb + fa_a[kk][2 * q]);
+      f.a[2 * q + 1] = *reinterpret_cast<const bf16x8 *>(sb + fa_a[kk][2 * q + 1]);
+    } else {
+      f.b[2 * q - 4] = *reinterpret_cast<const bf16x8 *>(sb + fa_b[kk][2 * q - 4]);
+      f.b[2 * q - 3] = *reinterpret_cast<const bf16x8 *>(sb + fa_b[kk][2 * q - 3]);
     }
   };
 
-  // fragment read offsets inside a stage: A rows wm*64 + j*32 + l32, B rows
-  // wn*128 + i*32 + l32; chunk 2*kk + g of the 32-wide K step
-  int fa_a[2][2], fa_b[4][2];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) fa_a[j][kk] = gswz(wm * 64 + j * 32 + l32, 2 * kk + g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa_b[i][kk] = kTileBytes + gswz(wn * 128 + i * 32 + l32, 2 * kk + g);
-  }
-
-  f32x16 acc[4][2];  // acc[i][j]: C^T block (N block i, M block j)
+  f32x16 acc[4][4];  // acc[i][j]: C^T block (N block i, M block j)
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  auto mfma_row = [&](const GemmFrags &f, int i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[i], f.a[j], acc[i][j], 0, 0, 0);
+  };
 
+  // ---- prologue: steps 0 and 1 into stages 0 and 1, step 2 towards L2.
+  // Past the last step the copies and prefetches repeat step KT-1 into a
+  // stage nobody reads again, which keeps the loop free of branches.
   const int KT = a.K / kBK;
-  // prologue: steps 0..2 in flight; step 0 landed before the first barrier
-  for (int p = 0; p < kGemmStages - 1 && p < KT; ++p) copy_step(p, p);
-  if (KT >= 3)
-    wait_vmcnt<2 * kGemmLoads>();
-  else if (KT == 2)
-    wait_vmcnt<kGemmLoads>();
-  else
-    wait_vmcnt<0>();
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    // stage (kt+3)%4 last held step kt-1, which every wave finished before the
-    // barrier that ended it
-    if (kt + 3 < KT) copy_step(kt + 3, (kt + 3) % kGemmStages);
-    const unsigned char *st = smem + (kt % kGemmStages) * kGemmStageBytes;
+  {
+    int koff;
+    const int s0 = seg_of(0, koff);
+    const StepSrc t0 = step_src(0, reinterpret_cast<const bf16 *>(a.B.p[s0]), koff);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 af[2], bfr[4];
+    for (int q = 0; q < 4; ++q) copy_part(t0, 0, q);
+    const int k1 = min(1, KT - 1);
+    const int s1 = seg_of(k1, koff);
+    const StepSrc t1 = step_src(k1, reinterpret_cast<const bf16 *>(a.B.p[s1]), koff);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) af[j] = *reinterpret_cast<const bf16x8 *>(st + fa_a[j][kk]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bfr[i] = *reinterpret_cast<const bf16x8 *>(st + fa_b[i][kk]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[i], af[j], acc[i][j], 0, 0, 0);
-    }
-    // step kt+1 must have landed (this wave's copies) before the barrier;
-    // the copies of steps kt+2 and kt+3 may stay in flight
-    if (kt + 3 < KT)
-      wait_vmcnt<2 * kGemmLoads>();
-    else if (kt + 2 < KT)
-      wait_vmcnt<kGemmLoads>();
-    else
-      wait_vmcnt<0>();
-    __syncthreads();
+    for (int q = 0; q < 4; ++q) copy_part(t1, 1, q);
   }
+  __syncthreads();  // bptr_s visible
+  {
+    int koff;
+    const int k2 = min(2, KT - 1);
+    prefetch(step_src(k2, bptr_at(seg_of(k2, koff)), koff));
+  }
+  wait_vmcnt<2>();
+  __syncthreads();
+  GemmFrags f0, f1;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) read_pair(f0, 0, 0, q);
+
+  // ---- main loop. Step kt sits in stage kt&1. Each K slice runs as 4
+  // groups of 4 MFMAs, each group also issuing 2 fragment reads of the next
+  // slice. After slice 2 the wave waits for its copies of step kt+1 and the
+  // block synchronises (every wave is done reading stage kt&1); under slice
+  // 3 the wave then reads slice 0 of step kt+1, copies step kt+2 into stage
+  // kt&1 and prefetches step kt+3 into L2. The wait leaves only the 2
+  // prefetch loads issued after those copies in flight.
+  for (int kt = 0; kt < KT; ++kt) {
+    const int st = kt & 1;
+    int koff2, koff3;
+    const int kc = min(kt + 2, KT - 1), kp = min(kt + 3, KT - 1);
+    const bf16 *bseg2 = bptr_at(seg_of(kc, koff2));
+    const bf16 *bseg3 = bptr_at(seg_of(kp, koff3));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      read_pair(f1, st, 1, i);
+      mfma_row(f0, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      read_pair(f0, st, 2, i);
+      mfma_row(f1, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      read_pair(f1, st, 3, i);
+      mfma_row(f0, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmcnt<2>();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    const StepSrc tc = step_src(kc, bseg2, koff2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      read_pair(f0, st ^ 1, 0, i);
+      copy_part(tc, st, i);
+      if (i == 3) prefetch(step_src(kp, bseg3, koff3));
+      mfma_row(f1, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // no copy may still be landing in LDS when the block exits
+  wait_vmcnt<0>();
 
   // accumulator layout (C^T block): lane holds output row (M) l32 of the
   // block and columns (N) 8*(v/4) + 4*g + v%4
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = m0 + wm * 64 + j * 32 + l32;
+  for (int j = 0; j < 4; ++j) {
+    const int row = m0 + wm * 128 + j * 32 + l32;
     if (row >= a.M) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -332,6 +449,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, Epi epi) {
 template <class Epi>
 static hipError_t run_gemm(int dtype, const GemmArgs &a, const Epi &epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.a_panel && dtype != TSP_BF16) return hipErrorInvalidValue;
   if (dtype == TSP_BF16) {
     static bool attr_set = false;  // benign race: every caller sets the same value
     if (!attr_set) {
@@ -349,10 +467,12 @@ static hipError_t run_gemm(int dtype, const GemmArgs &a, const Epi &epi, hipStre
   return hipGetLastError();
 }
 
-static GemmArgs make_args(const void *A, int64_t lda, int32_t M, int32_t N, int32_t K) {
+// a_panel: A in panel layout with M rows (bf16 only).
+static GemmArgs make_args(const void *A, int64_t lda, bool a_panel, int32_t M, int32_t N, int32_t K) {
   GemmArgs a{};
   a.A = A;
   a.lda = lda;
+  a.a_panel = a_panel ? (int64_t)M * kPanel : 0;
   a.M = M;
   a.N = N;
   a.K = K;
@@ -361,9 +481,9 @@ static GemmArgs make_args(const void *A, int64_t lda, int32_t M, int32_t N, int3
   return a;
 }
 
-hipError_t launch_qkv(int dtype, const void *xn, int32_t n, int32_t h, const PtrList &w, int32_t D,
+hipError_t launch_qkv(int dtype, const void *xn, bool a_panel, int32_t n, int32_t h, const PtrList &w, int32_t D,
                       int32_t hd, void *q, void *kf, void *vf, ZigzagMap zz, hipStream_t s) {
-  GemmArgs a = make_args(xn, h, n, 3 * hd, h);
+  GemmArgs a = make_args(xn, h, a_panel, n, 3 * hd, h);
   a.B = w;
   a.ldb = h;
   a.nz = D;
@@ -375,9 +495,9 @@ hipError_t launch_qkv(int dtype, const void *xn, int32_t n, int32_t h, const Ptr
   return run_gemm(dtype, a, e, s);
 }
 
-hipError_t launch_outproj(int dtype, const void *o, int32_t n, int32_t h, const PtrList &wo, int32_t D,
-                          int32_t hd, const float *x, float *y, hipStream_t s) {
-  GemmArgs a = make_args(o, h, n, h, D * hd);
+hipError_t launch_outproj(int dtype, const void *o, bool a_panel, int32_t n, int32_t h, const PtrList &wo,
+                          int32_t D, int32_t hd, const float *x, float *y, hipStream_t s) {
+  GemmArgs a = make_args(o, h, a_panel, n, h, D * hd);
   a.B = wo;
   a.ldb = hd;
   a.kseg = hd;
@@ -385,23 +505,24 @@ hipError_t launch_outproj(int dtype, const void *o, int32_t n, int32_t h, const 
   return run_gemm(dtype, a, e, s);
 }
 
-hipError_t launch_mlp_up(int dtype, const void *x, int32_t n, int32_t h, const PtrList &w1, int32_t D, int32_t fd,
-                         void *hid, hipStream_t s) {
-  GemmArgs a = make_args(x, h, n, fd, h);
+hipError_t launch_mlp_up(int dtype, const void *x, bool a_panel, int32_t n, int32_t h, const PtrList &w1, int32_t D,
+                         int32_t fd, void *hid, bool hid_panel, hipStream_t s) {
+  GemmArgs a = make_args(x, h, a_panel, n, fd, h);
   a.B = w1;
   a.ldb = h;
   a.nz = D;
+  const int64_t hp = hid_panel ? (int64_t)n * kPanel : 0;
   if (dtype == TSP_BF16) {
-    EpiGelu<bf16> e{(bf16 *)hid, (int64_t)D * fd, fd};
+    EpiGelu<bf16> e{(bf16 *)hid, (int64_t)D * fd, hp, fd};
     return run_gemm(dtype, a, e, s);
   }
-  EpiGelu<float> e{(float *)hid, (int64_t)D * fd, fd};
+  EpiGelu<float> e{(float *)hid, (int64_t)D * fd, hp, fd};
   return run_gemm(dtype, a, e, s);
 }
 
-hipError_t launch_mlp_down(int dtype, const void *hid, int32_t n, const PtrList &w2, int32_t D, int32_t fd,
-                           int32_t h, const float *res, float *y, hipStream_t s) {
-  GemmArgs a = make_args(hid, (int64_t)D * fd, n, h, D * fd);
+hipError_t launch_mlp_down(int dtype, const void *hid, bool a_panel, int32_t n, const PtrList &w2, int32_t D,
+                           int32_t fd, int32_t h, const float *res, float *y, hipStream_t s) {
+  GemmArgs a = make_args(hid, (int64_t)D * fd, a_panel, n, h, D * fd);
   a.B = w2;
   a.ldb = fd;
   a.kseg = fd;

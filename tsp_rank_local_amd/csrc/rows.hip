@@ -19,12 +19,12 @@ hipError_t launch_zigzag_index(ZigzagMap zz, int32_t n, int32_t *pos, hipStream_
 
 // One 256-thread block per row; h % 4 == 0. The sum of squares runs in fp32,
 // first per thread, then across the wave with shuffles, then across waves.
+// panel_stride > 0: out in panel layout (64-column panels of [rows][64]).
 template <typename G, typename O>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ x, const G *__restrict__ g,
-                                                      O *__restrict__ out, int32_t h, float eps) {
+                                                      O *__restrict__ out, int32_t h, float eps, int64_t panel_stride) {
   const int64_t row = blockIdx.x;
   const float *xr = x + row * h;
-  O *orow = out + row * h;
   float ss = 0.f;
   for (int c = threadIdx.x * 4; c < h; c += 1024) {
     float4 v = *reinterpret_cast<const float4 *>(xr + c);
@@ -43,22 +43,24 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ 
     float r1 = v.y * rstd * (float)g[c + 1];
     float r2 = v.z * rstd * (float)g[c + 2];
     float r3 = v.w * rstd * (float)g[c + 3];
-    orow[c + 0] = (O)r0;
-    orow[c + 1] = (O)r1;
-    orow[c + 2] = (O)r2;
-    orow[c + 3] = (O)r3;
+    O *o = out + (panel_stride ? panel_index(row, c, panel_stride) : row * h + c);  // 4 elements, one panel
+    o[0] = (O)r0;
+    o[1] = (O)r1;
+    o[2] = (O)r2;
+    o[3] = (O)r3;
   }
 }
 
 hipError_t launch_rmsnorm(const float *x, const void *g, void *out, int32_t rows, int32_t h, float eps,
-                          int dtype, hipStream_t s) {
+                          int dtype, bool out_panel, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  const int64_t ps = out_panel ? (int64_t)rows * kPanel : 0;
   if (dtype == TSP_BF16) {
     hipLaunchKernelGGL((rmsnorm_kernel<bf16, bf16>), dim3(rows), dim3(256), 0, s, x, (const bf16 *)g,
-                       (bf16 *)out, h, eps);
+                       (bf16 *)out, h, eps, ps);
   } else {
     hipLaunchKernelGGL((rmsnorm_kernel<float, float>), dim3(rows), dim3(256), 0, s, x, (const float *)g,
-                       (float *)out, h, eps);
+                       (float *)out, h, eps, ps);
   }
   return hipGetLastError();
 }

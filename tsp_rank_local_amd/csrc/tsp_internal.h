@@ -27,6 +27,16 @@ inline ZigzagMap make_zigzag(int64_t S, int32_t D, int32_t r) {
   return z;
 }
 
+// Panel layout of the bf16 activations that feed a GEMM as its A operand
+// (workspace tensors only): element (r, c) of an [M][K] tensor sits at
+// (c / 64) * (M * 64) + r * 64 + c % 64, i.e. K is cut into panels of 64
+// columns, each [M][64] row-major. A 256 x 64 GEMM tile is then 32 KB of
+// contiguous memory. panel_stride = M * 64 elements; 0 means row-major.
+constexpr int kPanel = 64;
+__host__ __device__ inline int64_t panel_index(int64_t r, int64_t c, int64_t panel_stride) {
+  return (c / kPanel) * panel_stride + r * kPanel + (c % kPanel);
+}
+
 // Up to TSP_MAX_D device pointers passed by value as a kernel argument.
 struct PtrList {
   const void *p[TSP_MAX_D];
@@ -34,35 +44,40 @@ struct PtrList {
 
 // ---------------------------------------------------------------- rows
 hipError_t launch_zigzag_index(ZigzagMap zz, int32_t n, int32_t *pos, hipStream_t s);
-// out[row] = x[row] / sqrt(mean(x[row]^2) + eps) * g, x fp32; g and out in dtype.
+// out[row] = x[row] / sqrt(mean(x[row]^2) + eps) * g, x fp32; g and out in
+// dtype; out in panel layout when out_panel (panel stride rows * 64), else
+// row-major.
 hipError_t launch_rmsnorm(const float *x, const void *g, void *out, int32_t rows, int32_t h, float eps,
-                          int dtype, hipStream_t s);
+                          int dtype, bool out_panel, hipStream_t s);
 
 // ---------------------------------------------------------------- GEMMs
 // All products are C = A B^T with A [M][K] and B [N][K] (both K-contiguous).
+// a_panel: A in panel layout (bf16 only; panel stride M * 64), else row-major.
 // QKV of every attention shard in one launch: shard z reads w[z] [3hd][h];
 // Q columns go to q [N][h] at column z*hd, K/V rows go to kf/vf [S][h] at row
 // zz.pos(t), column z*hd.
-hipError_t launch_qkv(int dtype, const void *xn, int32_t n, int32_t h, const PtrList &w, int32_t D,
+hipError_t launch_qkv(int dtype, const void *xn, bool a_panel, int32_t n, int32_t h, const PtrList &w, int32_t D,
                       int32_t hd, void *q, void *kf, void *vf, ZigzagMap zz, hipStream_t s);
 // y = x + sum_j o[:, j*hd:(j+1)*hd] wo[j]^T, shards walked j = 0..D-1 inside
 // the reduction loop.
-hipError_t launch_outproj(int dtype, const void *o, int32_t n, int32_t h, const PtrList &wo, int32_t D,
-                          int32_t hd, const float *x, float *y, hipStream_t s);
+hipError_t launch_outproj(int dtype, const void *o, bool a_panel, int32_t n, int32_t h, const PtrList &wo,
+                          int32_t D, int32_t hd, const float *x, float *y, hipStream_t s);
 // MLP up over all D ring steps in one launch: hid[:, t*fd:(t+1)*fd] =
 // GELU(x w1[t]^T) in dtype, w1[t] [fd][h] the shard of ring step t; hid
-// [n][D*fd].
-hipError_t launch_mlp_up(int dtype, const void *x, int32_t n, int32_t h, const PtrList &w1, int32_t D, int32_t fd,
-                         void *hid, hipStream_t s);
+// [n][D*fd] (panel layout when hid_panel).
+hipError_t launch_mlp_up(int dtype, const void *x, bool a_panel, int32_t n, int32_t h, const PtrList &w1, int32_t D,
+                         int32_t fd, void *hid, bool hid_panel, hipStream_t s);
 // y = (res ? res : 0) + sum_t hid[:, t*fd:(t+1)*fd] w2[t]^T in fp32, the
 // reduction walking ring steps t = 0..D-1 in order; w2[t] [h][fd]; res may
 // equal y.
-hipError_t launch_mlp_down(int dtype, const void *hid, int32_t n, const PtrList &w2, int32_t D, int32_t fd,
-                           int32_t h, const float *res, float *y, hipStream_t s);
+hipError_t launch_mlp_down(int dtype, const void *hid, bool a_panel, int32_t n, const PtrList &w2, int32_t D,
+                           int32_t fd, int32_t h, const float *res, float *y, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
+// o: [n][H][Dh] in o_dtype, or (bf16 o only) panel layout of [n][H*Dh] when
+// o_panel.
 hipError_t launch_attention(int dtype, const void *q, const void *k, const void *v, void *o, int o_dtype,
-                            int64_t S, int32_t n, int32_t H, int32_t Dh, float scale, ZigzagMap zz,
+                            bool o_panel, int64_t S, int32_t n, int32_t H, int32_t Dh, float scale, ZigzagMap zz,
                             hipStream_t s);
 
 // ---------------------------------------------------------------- timing
