@@ -74,6 +74,67 @@ def traffic_from_profile(kernel_src: str, name: str):
         return None
 
 
+def _counter_per_dispatch(path, counter):
+    """{kernel name: [value per dispatch]} of one counter in a rocprofv3 csv."""
+    import csv
+    out = {}
+    for row in csv.DictReader(open(path)):
+        if row["Counter_Name"] == counter:
+            out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def summarize_counters(fetch_csv, write_csv, copy_mib):
+    """HBM bytes per attention launch from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the plain
+    device copy of copy_mib MiB that --copy-mib runs before warmup."""
+    fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_csv, "WRITE_SIZE")
+    copy_bytes = float(copy_mib) * (1 << 20)
+
+    def one(d, key):
+        names = [k for k in d if key in k]
+        if len(names) != 1:
+            sys.exit(f"summarize-counters: expected one kernel matching {key!r}, found {names}")
+        v = d[names[0]]
+        return names[0], sum(v) / len(v)
+
+    def copy_kib(d):
+        # the largest dispatch of the runtime's copy kernel is the reference copy
+        v = [x for k, vals in d.items() if "copyBuffer" in k for x in vals]
+        if not v:
+            sys.exit("summarize-counters: no copy kernel dispatch found")
+        return max(v)
+
+    name, f_kib = one(fetch, "attn_bf16_kernel<128")
+    _, w_kib = one(write, "attn_bf16_kernel<128")
+    f_scale = copy_bytes / (copy_kib(fetch) * 1024.0)
+    w_scale = copy_bytes / (copy_kib(write) * 1024.0)
+    hbm = f_kib * 1024.0 * f_scale + w_kib * 1024.0 * w_scale
+    src = os.path.join(ROOT, "tsp_rank_local_amd", "csrc", "attention.hip")
+    lines = [
+        "# HBM traffic of one attention launch in the 7B layer (rank 0 of D=8, S=131072), from rocprofv3 counters.",
+        "# Made by:",
+        "#   rocprofv3 --pmc FETCH_SIZE -d <dir1> -o run --output-format csv -- "
+        "python bench.py --steps 1 --warmup 0 --cpu-rows 0 --copy-mib 1024",
+        "#   rocprofv3 --pmc WRITE_SIZE -d <dir2> -o run --output-format csv -- "
+        "python bench.py --steps 1 --warmup 0 --cpu-rows 0 --copy-mib 1024",
+        "#   python bench.py --summarize-counters <dir1>/run_counter_collection.csv <dir2>/run_counter_collection.csv",
+        "# Each counter is scaled by bytes / counter for the 1 GiB device copy run before warmup.",
+        f"kernel: {name}",
+        f"fetch_kib_per_dispatch: {f_kib:.1f}",
+        f"write_kib_per_dispatch: {w_kib:.1f}",
+        f"copy_fetch_scale: {f_scale:.4f}",
+        f"copy_write_scale: {w_scale:.4f}",
+        f"hbm_bytes_per_launch: {hbm:.6g}",
+        f"source_sha256: {hashlib.sha256(open(src, 'rb').read()).hexdigest()}",
+    ]
+    out = os.path.join(ROOT, "profiles", "attention_7b_traffic.txt")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -96,7 +157,13 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warmup, run one plain device-to-device copy of this many MiB (a known-size "
                          "reference for rocprofv3 HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/attention_7b_traffic.txt from two rocprofv3 --pmc counter_collection.csv "
+                         "files (FETCH_SIZE, WRITE_SIZE) of a run with --copy-mib, then exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, copy_mib=args.copy_mib or 1024)
+        return
     if args.gpus != 1:
         sys.exit(f"bench.py: only --gpus 1 is supported; this build measures one rank's share on one GPU "
                  f"(asked for {args.gpus}).")
