@@ -151,7 +151,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["layer", "mlp", "attn"], default="layer")
+    ap.add_argument("--workload", choices=["layer", "mlp", "attn", "layers32"], default="layer")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=384, help="rows in the CPU oracle sample (0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -212,6 +212,45 @@ def main():
             tsp.tsp_mlp_ring(shape, xd, wd["w1"], wd["w2"], None, y, ws)
         step_flops = flops["mlp"]
         workload = "tsp_mlp_ring: 7B MLP ring, 16384x4096 bf16 local X, D=8 shards of 4096x2048"
+    elif args.workload == "layers32":
+        # 32 layers resident in HBM (82 GB of weights and K/V), each with its
+        # own weights and remote K/V, generated on the GPU from a fixed seed:
+        # N(0, 0.02^2) bf16 weights, unit gains, N(0, 1) bf16 K/V and fp32 x
+        n_layers = 32
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(seed)
+
+        def rnd(shape_, std, dtype):
+            return (torch.randn(shape_, generator=gen, device="cuda", dtype=torch.float32) * std).to(dtype)
+
+        hd, fd = sh.h // sh.D, sh.F // sh.D
+        layers = []
+        for _ in range(n_layers):
+            wl = {"g_attn": torch.ones(sh.h, dtype=torch.bfloat16, device="cuda"),
+                  "g_mlp": torch.ones(sh.h, dtype=torch.bfloat16, device="cuda"),
+                  "wqkv": [rnd((3 * hd, sh.h), 0.02, torch.bfloat16) for _ in range(sh.D)],
+                  "wo": [rnd((sh.h, hd), 0.02, torch.bfloat16) for _ in range(sh.D)],
+                  "w1": [rnd((fd, sh.h), 0.02, torch.bfloat16) for _ in range(sh.D)],
+                  "w2": [rnd((sh.h, fd), 0.02, torch.bfloat16) for _ in range(sh.D)]}
+            kl = rnd((sh.S, sh.H, sh.Dh), 1.0, torch.bfloat16)
+            vl = rnd((sh.S, sh.H, sh.Dh), 1.0, torch.bfloat16)
+            layers.append((wl, kl, vl))
+        xbuf = [rnd((N, sh.h), 1.0, torch.float32), torch.empty((N, sh.h), dtype=torch.float32, device="cuda"),
+                torch.empty((N, sh.h), dtype=torch.float32, device="cuda")]
+        ws = torch.empty(tsp.workspace_size(shape, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
+
+        def step():
+            # x0 stays untouched; layer outputs alternate between two buffers
+            src = xbuf[0]
+            for i, (wl, kl, vl) in enumerate(layers):
+                dst = xbuf[1 + (i & 1)]
+                tsp.tsp_layer_fwd(shape, wl, src, kl, vl, dst, tsp.TSP_PHASE_ALL, ws)
+                src = dst
+        step_flops = n_layers * flops["total"]
+        N = N * n_layers  # value = layer-tokens/s, comparable with the one-layer figure
+        workload = (f"32 x tsp_layer_fwd: 32-layer 7B dense forward (each layer h=4096, 32x128 heads, FFN 16384, "
+                    f"bf16, own weights and remote K/V, all resident) on rank {r} of D=8 at S=131072, "
+                    f"16384 local zigzag tokens; value counts layer-tokens (16384 x 32 per step)")
     else:
         q = synth.attn_queries(sh, seed=3)
         k_rem, v_rem = synth.remote_kv(sh, seed=3)
@@ -294,7 +333,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": workload, "S": sh.S, "D": sh.D, "r": r, "h": sh.h, "H": sh.H, "Dh": sh.Dh,
-                   "F": sh.F, "local_tokens": N, "parallelism": "one rank of a D=8 folded TP+SP axis"},
+                   "F": sh.F, "local_tokens": sh.N, "layers": 32 if args.workload == "layers32" else 1,
+                   "parallelism": "one rank of a D=8 folded TP+SP axis"},
         "pct_bf16_mfma_peak": 100.0 * step_flops / (ms_step * 1e-3) / PEAK_BF16,
         "algorithmic_tflop_per_step": step_flops / 1e12,
         "roofline": roofline,

@@ -92,6 +92,36 @@ def test_attention_scale_zero_gives_prefix_mean(torch):
     assert_close(down(o), want, TOL_BF16, "prefix mean")
 
 
+@pytest.mark.parametrize("Dh", [64, 128])
+def test_attention_late_keys_far_above_first_tile(torch, Dh):
+    """Keys 100, 611 and 1500 get scaled log2 scores of about 16, 24 and 24
+    against at most about 5 in any row's first key tile, so the running max
+    must move (the kernels raise it only when a score exceeds it by more than
+    8 in log2 units)."""
+    S, D, H = 2048, 2, 2
+    shape = synth.LayerShape(S=S, D=D, h=H * Dh, H=H, Dh=Dh, F=128, dtype="bf16")
+    k, v = synth.remote_kv(shape, seed=13)
+    kf = synth.bf16_to_f32(k).reshape(S, H, Dh)
+    base = np.ones(Dh, dtype=np.float32) / np.sqrt(Dh)
+    c = 1.0 / np.sqrt(Dh) * np.log2(np.e)
+    for u, lift in ((100, 16.0), (611, 24.0), (1500, 24.0)):
+        kf[u] = base * (lift / c) / np.sqrt(Dh) + 0.01 * kf[u]
+    k = synth.f32_to_bf16(kf)
+    for r in range(D):
+        qf = synth.bf16_to_f32(synth.normal((S // D, H, Dh), 13, synth.TID_Q, r, dtype="bf16"))
+        qf = qf * 0.05 + base * np.sqrt(Dh)
+        q = synth.f32_to_bf16(qf)
+        o = torch.empty((S // D, H, Dh), dtype=torch.float32, device="cuda")
+        s = tsp.make_shape(S, D, r, H * Dh, H, Dh, 128, dtype="bf16")
+        log(f"attention with late large scores Dh={Dh} r={r}")
+        tsp.tsp_zigzag_attn(s, up(q, "bf16"), up(k, "bf16"), up(v, "bf16"), o)
+        _sync(torch)
+        want = oracle.causal_attention(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"),
+                                       oracle.zigzag_positions(S, D, r), shape.scale)
+        assert np.isfinite(down(o)).all()
+        assert_close(down(o), want, TOL_BF16, "o")
+
+
 # ---------------------------------------------------------------- MLP ring
 MLP_CASES = [
     # S, D, h, F, dtype, residual
@@ -254,3 +284,33 @@ def test_layer_deterministic(torch):
         _sync(torch)
         outs.append(y.cpu().numpy())
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype,layers,S,D,H,Dh,F", [("f32", 32, 1024, 4, 4, 64, 1024),
+                                                      ("bf16", 4, 2400, 4, 4, 128, 2048)])
+def test_layer_stack_vs_oracle(torch, dtype, layers, S, D, H, Dh, F):
+    """A stack of layers on one rank's share (the 32-layer 7B forward at small
+    size): layer l reads layer l-1's output and has its own seeded weights
+    and remote K/V. The oracle runs the same stack in fp64 on its own
+    intermediate results."""
+    h = H * Dh
+    shape = synth.LayerShape(S=S, D=D, h=h, H=H, Dh=Dh, F=F, dtype=dtype)
+    r = D - 1
+    s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype=dtype)
+    ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
+    x0 = synth.activations(S // D, h, seed=5, tid=100 + r)
+    bufs = [up(x0, "f32"), torch.empty((S // D, h), dtype=torch.float32, device="cuda")]
+    want = x0.astype(np.float64)
+    keep = []
+    for l in range(layers):
+        w = synth.layer_weights(shape, seed=500 + l, gain="random")
+        k_rem, v_rem = synth.remote_kv(shape, seed=500 + l)
+        kf, vf = up(k_rem, dtype), up(v_rem, dtype)
+        wd = _dev_weights(w, dtype)
+        keep.append((wd, kf, vf))
+        tsp.tsp_layer_fwd(s, wd, bufs[l % 2], kf, vf, bufs[(l + 1) % 2], tsp.TSP_PHASE_ALL, ws)
+        want = oracle.layer_rank(want, _w64(w, dtype), f64(k_rem, dtype), f64(v_rem, dtype), S, D, r, H, Dh,
+                                 shape.eps, shape.scale)["y"]
+    _sync(torch)
+    log(f"{layers}-layer stack S={S} D={D} r={r} {dtype}")
+    assert_close(down(bufs[layers % 2]), want, TOL_F32 if dtype == "f32" else TOL_BF16, "y after the stack")
