@@ -64,6 +64,8 @@ def test_workspace_sizes():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(S=1020), tsp.TSP_ERR_INVALID_ARG),          # S not a multiple of 2D
+    (dict(S=0), tsp.TSP_ERR_INVALID_ARG),             # empty sequence
+    (dict(S=1 << 31), tsp.TSP_ERR_INVALID_ARG),       # positions must fit int32
     (dict(r=4), tsp.TSP_ERR_INVALID_ARG),             # r out of range
     (dict(D=0), tsp.TSP_ERR_INVALID_ARG),
     (dict(D=65, S=130), tsp.TSP_ERR_INVALID_ARG),     # D above the limit
