@@ -74,6 +74,28 @@ struct EpiGelu {
   __device__ __forceinline__ void operator()(int z, int r, int c, float4 v) const {
     store4(at(z, r, c), make_float4(gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w)));
   }
+  // Whole 128-column blocks (see gemm_bf16_kernel): row r, columns c0 + dc
+  // with dc = 32*i + 8*vq + 4*g. In panel layout c0 is a multiple of 64, so
+  // block half i/2 is panel c0/64 + i/2 and the rest is a constant offset.
+  struct Row {
+    T *p[2];
+  };
+  __device__ __forceinline__ bool fast_ok() const { return true; }
+  __device__ __forceinline__ Row row(int z, int r, int c0, int g) const {
+    const int64_t col = (int64_t)z * cols + c0 + 4 * g;
+    Row w;
+    if (panel) {
+      w.p[0] = out + panel_index(r, col, panel);
+      w.p[1] = w.p[0] + panel;
+    } else {
+      w.p[0] = out + (int64_t)r * ld + col;
+      w.p[1] = w.p[0] + 64;
+    }
+    return w;
+  }
+  __device__ __forceinline__ void put(const Row &w, int i, int vq, float4 v) const {
+    store4(w.p[i >> 1] + (i & 1) * 32 + vq * 8, make_float4(gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w)));
+  }
 };
 
 struct EpiStoreF32 {
@@ -82,6 +104,14 @@ struct EpiStoreF32 {
   __device__ __forceinline__ void operator()(int, int r, int c, float v) const { out[(int64_t)r * ld + c] = v; }
   __device__ __forceinline__ void operator()(int, int r, int c, float4 v) const {
     *reinterpret_cast<float4 *>(out + (int64_t)r * ld + c) = v;
+  }
+  struct Row {
+    float *p;
+  };
+  __device__ __forceinline__ bool fast_ok() const { return true; }
+  __device__ __forceinline__ Row row(int, int r, int c0, int g) const { return Row{out + (int64_t)r * ld + c0 + 4 * g}; }
+  __device__ __forceinline__ void put(const Row &w, int i, int vq, float4 v) const {
+    *reinterpret_cast<float4 *>(w.p + i * 32 + vq * 8) = v;
   }
 };
 
@@ -99,6 +129,20 @@ struct EpiAddF32 {
     const int64_t i = (int64_t)r * ld + c;
     const float4 x = *reinterpret_cast<const float4 *>(res + i);
     *reinterpret_cast<float4 *>(out + i) = make_float4(x.x + v.x, x.y + v.y, x.z + v.z, x.w + v.w);
+  }
+  struct Row {
+    const float *x;
+    float *p;
+  };
+  __device__ __forceinline__ bool fast_ok() const { return true; }
+  __device__ __forceinline__ Row row(int, int r, int c0, int g) const {
+    const int64_t i = (int64_t)r * ld + c0 + 4 * g;
+    return Row{res + i, out + i};
+  }
+  __device__ __forceinline__ void put(const Row &w, int i, int vq, float4 v) const {
+    const int d = i * 32 + vq * 8;
+    const float4 x = *reinterpret_cast<const float4 *>(w.x + d);
+    *reinterpret_cast<float4 *>(w.p + d) = make_float4(x.x + v.x, x.y + v.y, x.z + v.z, x.w + v.w);
   }
 };
 
@@ -120,6 +164,15 @@ struct EpiQKV {
   }
   __device__ __forceinline__ void operator()(int z, int r, int c, float val) const { *dst(z, r, c) = (T)val; }
   __device__ __forceinline__ void operator()(int z, int r, int c, float4 val) const { store4(dst(z, r, c), val); }
+  // whole 128-column blocks stay inside one part when hd is a multiple of 128
+  struct Row {
+    T *p;
+  };
+  __device__ __forceinline__ bool fast_ok() const { return (hd & 127) == 0; }
+  __device__ __forceinline__ Row row(int z, int r, int c0, int g) const { return Row{dst(z, r, c0 + 4 * g)}; }
+  __device__ __forceinline__ void put(const Row &w, int i, int vq, float4 v) const {
+    store4(w.p + i * 32 + vq * 8, v);
+  }
 };
 
 // ---------------------------------------------------------------- tile order
@@ -369,19 +422,35 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, 
 
   // accumulator layout (C^T block): lane holds output row (M) l32 of the
   // block and columns (N) 8*(v/4) + 4*g + v%4
+  // When the wave's 128 columns all lie inside N, each row's addresses come
+  // from one per-row base plus constant offsets.
+  const int c0 = n0 + wn * 128;
+  const bool whole = c0 + 128 <= a.N && epi.fast_ok();
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = m0 + wm * 128 + j * 32 + l32;
     if (row >= a.M) continue;
+    if (whole) {
+      const typename Epi::Row rw = epi.row(z, row, c0, g);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int vq = 0; vq < 4; ++vq) {
-        const int col = n0 + wn * 128 + i * 32 + vq * 8 + g * 4;
-        if (col < a.N)
-          epi(z, row, col,
-              make_float4(acc[i][j][vq * 4 + 0], acc[i][j][vq * 4 + 1], acc[i][j][vq * 4 + 2], acc[i][j][vq * 4 + 3]));
-      }
+        for (int vq = 0; vq < 4; ++vq)
+          epi.put(rw, i, vq,
+                  make_float4(acc[i][j][vq * 4 + 0], acc[i][j][vq * 4 + 1], acc[i][j][vq * 4 + 2],
+                              acc[i][j][vq * 4 + 3]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) {
+          const int col = c0 + i * 32 + vq * 8 + g * 4;
+          if (col < a.N)
+            epi(z, row, col,
+                make_float4(acc[i][j][vq * 4 + 0], acc[i][j][vq * 4 + 1], acc[i][j][vq * 4 + 2],
+                            acc[i][j][vq * 4 + 3]));
+        }
+    }
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
