@@ -127,7 +127,8 @@ enum {
   TSP_K_MLP_UP = 4,
   TSP_K_MLP_DOWN = 5,
   TSP_K_ZIGZAG = 6,
-  TSP_K_COUNT = 7
+  TSP_K_LEAD = 7, /* the fp32 recomputation of the leading rows (see tsp_layer_fwd) */
+  TSP_K_COUNT = 8
 };
 
 /* Static text for a status code. */
@@ -181,7 +182,14 @@ tsp_status tsp_mlp_ring(const tsp_shape *shape, const void *x, const void *const
  *  phases: TSP_PHASE_KV, TSP_PHASE_REST or TSP_PHASE_ALL; PHASE_REST must use
  *    the same ws as the PHASE_KV call before it.
  *  ws: device scratch of at least tsp_workspace_size(TSP_WS_LAYER) bytes.
- * y must not overlap x, k_full, v_full or ws. */
+ * y must not overlap x, k_full, v_full or ws.
+ * bf16 rank 0: the queries at positions below min(64, S/(2D)) attend to so
+ * few keys that their output is not averaged down, and the bf16 storage of
+ * the intermediates (normed input, Q/K/V, attention output, MLP input and
+ * hidden layer) alone brings their error close to 2e-2 of the output rms.
+ * PHASE_REST therefore recomputes those rows, which see only each other, with
+ * fp32 intermediates and fp32-accurate products (the bf16 weights are exact),
+ * and writes their y from that; their K/V rows in k_full/v_full stay bf16. */
 tsp_status tsp_layer_fwd(const tsp_shape *shape, const tsp_layer_weights *w, const float *x,
                          void *k_full, void *v_full, float *y, unsigned phases, void *ws,
                          size_t ws_bytes, void *stream);

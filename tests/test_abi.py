@@ -51,15 +51,37 @@ def _shape(**kw):
     return tsp.make_shape(**base)
 
 
+def _a256(n):
+    return (n + 255) // 256 * 256
+
+
+def _lead_bytes(S, D, h, F):
+    """bf16 rank 0 also recomputes its first m = min(64, S/(2D)) rows in fp32:
+    seven [m][h] and one [m][F] fp32 buffers, plus the K-chunk partial sums of
+    the largest of its four products (chunk: 512, 256, 128 or 64 dividing the
+    reduction segment)."""
+    m = min(64, S // (2 * D))
+    hd, fd = h // D, F // D
+    chunk = lambda k: next(c for c in (512, 256, 128, 64) if k % c == 0)
+    part = 4 * max(h // chunk(h) * m * 3 * h, h // chunk(hd) * m * h, h // chunk(h) * m * F, F // chunk(fd) * m * h)
+    return 7 * _a256(m * h * 4) + _a256(m * F * 4) + _a256(part)
+
+
 def test_workspace_sizes():
     # MLP: GELU(x W1_j^T) of every ring step side by side, [N][F] in the dtype;
     # layer: Q (later RMSNorm(h1)) and RMSNorm(x) (later O), [N][h] each, plus that
-    s = _shape(dtype="bf16")
     N, h, F = 256, 256, 1024
-    assert tsp.workspace_size(s, tsp.TSP_WS_MLP) == N * F * 2
-    assert tsp.workspace_size(s, tsp.TSP_WS_LAYER) == 2 * N * h * 2 + N * F * 2
-    s7 = tsp.make_shape(131072, 8, 0, 4096, 32, 128, 16384, dtype="bf16")
-    assert tsp.workspace_size(s7, tsp.TSP_WS_LAYER) == 2 * 16384 * 4096 * 2 + 16384 * 16384 * 2
+    for r in (0, 1):
+        s = _shape(dtype="bf16", r=r)
+        assert tsp.workspace_size(s, tsp.TSP_WS_MLP) == N * F * 2
+        lead = _lead_bytes(1024, 4, h, F) if r == 0 else 0
+        assert tsp.workspace_size(s, tsp.TSP_WS_LAYER) == 2 * N * h * 2 + N * F * 2 + lead
+    s = _shape(dtype="f32")
+    assert tsp.workspace_size(s, tsp.TSP_WS_LAYER) == 2 * N * h * 4 + N * F * 4
+    for r in (0, 3):
+        s7 = tsp.make_shape(131072, 8, r, 4096, 32, 128, 16384, dtype="bf16")
+        lead = _lead_bytes(131072, 8, 4096, 16384) if r == 0 else 0
+        assert tsp.workspace_size(s7, tsp.TSP_WS_LAYER) == 2 * 16384 * 4096 * 2 + 16384 * 16384 * 2 + lead
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -292,6 +292,10 @@ def test_bf16_layer_vs_oracle(torch, S, D, H, Dh, F):
         _sync(torch)
         want = oracle.layer_rank(x, w64, k64, v64, S, D, r, H, Dh, shape.eps, shape.scale)
         assert_close(down(y), want["y"], TOL_BF16, "y")
+        if r == 0:
+            # rank 0's first positions are recomputed with fp32 intermediates
+            m = min(64, S // (2 * D))
+            assert_close(down(y)[:m], want["y"][:m], TOL_F32, f"leading {m} rows")
         # remote rows of the gathered K/V are left untouched
         pos = oracle.zigzag_positions(S, D, r)
         remote = np.setdiff1d(np.arange(S), pos)

@@ -30,7 +30,8 @@ TSP_F32, TSP_BF16 = 0, 1
 TSP_PHASE_KV, TSP_PHASE_REST, TSP_PHASE_ALL = 1, 2, 3
 TSP_WS_MLP, TSP_WS_LAYER = 0, 1
 TSP_MAX_D = 64
-KERNEL_CLASSES = {"rmsnorm": 0, "qkv": 1, "attention": 2, "outproj": 3, "mlp_up": 4, "mlp_down": 5, "zigzag": 6}
+KERNEL_CLASSES = {"rmsnorm": 0, "qkv": 1, "attention": 2, "outproj": 3, "mlp_up": 4, "mlp_down": 5, "zigzag": 6,
+                  "lead": 7}
 
 EXPORTED_SYMBOLS = [
     "tsp_status_string", "tsp_last_error", "tsp_abi_version", "tsp_workspace_size",

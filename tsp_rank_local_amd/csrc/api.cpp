@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -103,8 +104,19 @@ tsp_status check_layer_shape(const tsp_shape *s) {
   return TSP_OK;
 }
 
+// Rows of rank r recomputed in fp32 by the layer (bf16 rank 0 only): the
+// positions below min(kLeadRows, S/(2D)), local rows 0.. of chunk 0.
+int32_t lead_rows(const tsp_shape *s) {
+  if (s->dtype != TSP_BF16 || s->r != 0) return 0;
+  return (int32_t)std::min<int64_t>(tsp::kLeadRows, s->S / (2 * s->D));
+}
+
 struct LayerWs {
-  size_t q, x2, hid, total;
+  size_t q, x2, hid;
+  // leading rows: fp32 [m][h] normed input, q, k, v, attention output, h1,
+  // normed h1; [m][F] hidden layer; partial sums of the products
+  size_t la, lq, lk, lv, lo, lh1, lmm, lhid, lpart;
+  size_t total;
 };
 
 LayerWs layer_ws(const tsp_shape *s) {
@@ -114,7 +126,19 @@ LayerWs layer_ws(const tsp_shape *s) {
   w.q = 0;
   w.x2 = align256(N * s->h * e);
   w.hid = w.x2 + align256(N * s->h * e);
-  w.total = w.hid + align256(N * (size_t)s->F * e);
+  size_t at = w.hid + align256(N * (size_t)s->F * e);
+  const size_t m = (size_t)lead_rows(s);
+  const size_t mh = m ? align256(m * s->h * 4) : 0;
+  w.la = at;
+  w.lq = w.la + mh;
+  w.lk = w.lq + mh;
+  w.lv = w.lk + mh;
+  w.lo = w.lv + mh;
+  w.lh1 = w.lo + mh;
+  w.lmm = w.lh1 + mh;
+  w.lhid = w.lmm + mh;
+  w.lpart = w.lhid + (m ? align256(m * (size_t)s->F * 4) : 0);
+  w.total = w.lpart + (m ? align256(tsp::lead_part_bytes((int32_t)m, s->h, s->F, s->D)) : 0);
   return w;
 }
 
@@ -284,7 +308,7 @@ tsp_status tsp_zigzag_attn(const tsp_shape *s, const void *q, const void *k, con
   hipStream_t stream = (hipStream_t)stream_;
   TSP_LAUNCH(TSP_K_ATTN,
              tsp::launch_attention(s->dtype, q, k, v, o, o_dtype, false, s->S, (int32_t)N, s->H, s->Dh, s->scale,
-                                   tsp::make_zigzag(s->S, s->D, s->r), stream),
+                                   tsp::make_zigzag(s->S, s->D, s->r), false, stream),
              "attention");
   return ok();
 }
@@ -349,18 +373,23 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
   void *hid = ws + L.hid;  // GELU(hn W1_j^T) of every ring step, side by side
   const tsp::ZigzagMap zz = tsp::make_zigzag(s->S, D, s->r);
   const bool pnl = s->dtype == TSP_BF16;
+  // bf16: the QKV epilogue stores Q * scale * log2(e), so attention's scores
+  // come out of the matrix cores in the log2 domain (one rounding of Q, as
+  // without the factor)
+  const float q_scale = pnl ? s->scale * 1.4426950408889634f : 1.0f;
   hipStream_t stream = (hipStream_t)stream_;
 
   if (phases & TSP_PHASE_KV) {
     TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(x, w->g_attn, x2, N, h, s->eps, s->dtype, pnl, stream), "RMSNorm");
     TSP_LAUNCH(TSP_K_QKV,
-               tsp::launch_qkv(s->dtype, x2, pnl, N, h, to_list(w->wqkv, D), D, hd, qbuf, k_full, v_full, zz, stream),
+               tsp::launch_qkv(s->dtype, x2, pnl, N, h, to_list(w->wqkv, D), D, hd, qbuf, k_full, v_full, zz, q_scale,
+                               stream),
                "QKV");
   }
   if (phases & TSP_PHASE_REST) {
     TSP_LAUNCH(TSP_K_ATTN,
                tsp::launch_attention(s->dtype, qbuf, k_full, v_full, x2, s->dtype, pnl, s->S, N, s->H, s->Dh,
-                                     s->scale, zz, stream),
+                                     s->scale, zz, pnl, stream),
                "attention");
     TSP_LAUNCH(TSP_K_OUTPROJ,
                tsp::launch_outproj(s->dtype, x2, pnl, N, h, to_list(w->wo, D), D, hd, x, y, stream),
@@ -373,6 +402,32 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
     TSP_LAUNCH(TSP_K_MLP_DOWN,
                tsp::launch_mlp_down(s->dtype, hid, pnl, N, ring_list(w->w2, D, s->r), D, fd, h, y, y, stream),
                "MLP down");
+    const int32_t m = lead_rows(s);
+    if (m > 0) {
+      // rank 0's first m rows again, fp32 throughout; they attend only to
+      // each other (positions 0..m-1), so their K/V come from the same pass
+      float *la = (float *)(ws + L.la), *lq = (float *)(ws + L.lq), *lk = (float *)(ws + L.lk);
+      float *lv = (float *)(ws + L.lv), *lo = (float *)(ws + L.lo), *lh1 = (float *)(ws + L.lh1);
+      float *lmm = (float *)(ws + L.lmm), *lhid = (float *)(ws + L.lhid), *lpart = (float *)(ws + L.lpart);
+      TSP_LAUNCH(TSP_K_LEAD, tsp::launch_rmsnorm_f32(x, w->g_attn, s->dtype, la, m, h, s->eps, stream),
+                 "leading rows: RMSNorm");
+      TSP_LAUNCH(TSP_K_LEAD,
+                 tsp::launch_lead_qkv(la, m, h, to_list(w->wqkv, D), D, hd, lq, lk, lv, zz, lpart, stream),
+                 "leading rows: QKV");
+      TSP_LAUNCH(TSP_K_LEAD,
+                 tsp::launch_lead_attention(lq, lk, lv, lo, m, s->H, s->Dh, s->scale, stream),
+                 "leading rows: attention");
+      TSP_LAUNCH(TSP_K_LEAD, tsp::launch_lead_outproj(lo, m, h, to_list(w->wo, D), D, hd, x, lh1, lpart, stream),
+                 "leading rows: output projection");
+      TSP_LAUNCH(TSP_K_LEAD, tsp::launch_rmsnorm_f32(lh1, w->g_mlp, s->dtype, lmm, m, h, s->eps, stream),
+                 "leading rows: RMSNorm");
+      TSP_LAUNCH(TSP_K_LEAD,
+                 tsp::launch_lead_mlp_up(lmm, m, h, ring_list(w->w1, D, s->r), D, fd, lhid, lpart, stream),
+                 "leading rows: MLP up");
+      TSP_LAUNCH(TSP_K_LEAD,
+                 tsp::launch_lead_mlp_down(lhid, m, ring_list(w->w2, D, s->r), D, fd, h, lh1, y, lpart, stream),
+                 "leading rows: MLP down");
+    }
   }
   return ok();
 }

@@ -19,17 +19,21 @@
 // chunk), so every fragment read below is free of bank conflicts.
 //
 // Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K rows read
-// with ds_read_b128), so a lane owns one query and 32 of the tile's keys: the
-// row max needs one exchange between the two half-waves and the row sum none
-// until the end. Softmax runs in the exp2 domain with the scale folded into
-// one FMA. The running max is raised only when a score exceeds it by more than
-// 2^8 in probability (a smaller excess stays exact in fp32 and bf16), so the O
-// rescale is rare. P is rounded to bf16 (v_cvt_pk_bf16_f32) and summed from
-// the rounded values (v_dot2c_f32_bf16). O^T = V^T P^T runs on the same MFMA
-// with P taken straight from the score registers; its V^T operand comes from
-// two ds_read_b64_tr_b16 per lane, each a 4x4 transpose of 16-bit elements
-// inside 16 lanes, which hands every lane 4 consecutive keys of one feature in
-// the key order the score registers have.
+// with ds_read_b128), so a lane owns one query and 32 of the tile's keys.
+// Softmax runs in the exp2 domain against a per-row reference max m that is
+// taken on the walk's first key tile and raised only on the rare tile whose
+// probabilities would grow too large; the S^T accumulators start at -m, so
+// with Q pre-multiplied by scale * log2(e) (the layer's QKV epilogue stores it
+// that way) a probability is one exp2 of an accumulator, and otherwise one
+// multiply and an exp2. No per-tile row max is needed: a tile is accepted
+// when each lane's sum of its probabilities stays below a fixed bound, which
+// also bounds every probability; otherwise the tile is redone with m raised
+// to its max and O and l rescaled. P is rounded to bf16 (v_cvt_pk_bf16_f32)
+// and summed from the rounded values (v_dot2c_f32_bf16). O^T = V^T P^T runs on
+// the same MFMA with P taken straight from the score registers; its V^T
+// operand comes from two ds_read_b64_tr_b16 per lane, each a 4x4 transpose of
+// 16-bit elements inside 16 lanes, which hands every lane 4 consecutive keys
+// of one feature in the key order the score registers have.
 //
 // Query tiles whose positions all lie below kSplitPos see so few keys that one
 // probability can carry most of a row; there P is applied as a bf16 pair
@@ -58,8 +62,6 @@ struct AttnArgs {
 constexpr int kBQ = 128, kBKey = 64, kAttnThreads = 256;
 // Query tiles whose last position is below this use the hi + lo split of P.
 [[maybe_unused]] constexpr int kSplitPos = 1024;
-// The running max is raised once a score exceeds it by more than this (log2).
-[[maybe_unused]] constexpr float kRescaleLog2 = 8.0f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define TSP_LDS(p) ((__attribute__((address_space(3))) void *)(p))
@@ -128,29 +130,81 @@ __device__ __forceinline__ FragAddr<DH> frag_addr(int lane) {
   return fa;
 }
 
-template <int DH, bool MASK, bool SPLIT>
+// Probabilities of the 64 scores held by the lane, minus a shift (log2
+// domain): P as bf16 (hi, and lo = p - hi when SPLIT) in MFMA B-operand
+// order, and the lane's sum of them. With Q not pre-scaled, keys past qpos
+// get 0 when MASK (their scores hold -inf, which a zero scale would turn into
+// NaN); pre-scaled, exp2(-inf) is 0 already.
+template <bool SHIFT, bool MASK, bool SPLIT, bool QPRE>
+__device__ __forceinline__ float tile_probs(const f32x16 (&sacc)[2], float shift, float c, int kstart, int qpos, int g,
+                                            bf16x8 (&ph)[4], bf16x8 (&pl)[4]) {
+  const float nsc = -shift * c;
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  float lt = 0.f;
+#pragma unroll
+  for (int kq = 0; kq < 4; ++kq) {
+    const int kb = kq >> 1, v0 = (kq & 1) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float s0 = sacc[kb][v0 + e], s1 = sacc[kb][v0 + e + 1];
+      const float x0 = QPRE ? (SHIFT ? s0 - shift : s0) : (SHIFT ? fmaf(s0, c, nsc) : s0 * c);
+      const float x1 = QPRE ? (SHIFT ? s1 - shift : s1) : (SHIFT ? fmaf(s1, c, nsc) : s1 * c);
+      float p0 = __builtin_amdgcn_exp2f(x0), p1 = __builtin_amdgcn_exp2f(x1);
+      if constexpr (MASK && !QPRE) {
+        const int key0 = kstart + kq * 16 + (e >> 2) * 8 + g * 4 + (e & 3);
+        if (key0 > qpos) p0 = 0.f;
+        if (key0 + 1 > qpos) p1 = 0.f;
+      }
+      const bf16x2 h2 = {(bf16)p0, (bf16)p1};
+      ph[kq][e] = h2[0];
+      ph[kq][e + 1] = h2[1];
+      if constexpr (SPLIT) {
+        const bf16x2 l2 = {(bf16)(p0 - (float)h2[0]), (bf16)(p1 - (float)h2[1])};
+        pl[kq][e] = l2[0];
+        pl[kq][e + 1] = l2[1];
+        lt += p0 + p1;
+      } else {
+        lt = __builtin_amdgcn_fdot2_f32_bf16(h2, ones, lt, false);
+      }
+    }
+  }
+  return lt;
+}
+
+// Largest sum of one lane's 32 probabilities (relative to the row's
+// reference max m) that a tile accepts without raising m: every probability
+// of an accepted tile is at most 2^16, and O and l stay far from fp32
+// overflow over any sequence length the entry points take.
+constexpr float kLaneSumLimit = 65536.0f;
+
+// One 64-key tile for one wave: scores, online softmax, O^T += V^T P^T.
+// Q arrives pre-multiplied by scale * log2(e), so scores are in the log2
+// domain. The accumulators of S^T start at -m (bias, one value per lane), so
+// they hold s - m and the probabilities need only exp2. The reference max m
+// is fixed on the walk's first tile (key 0 is in it and visible to every
+// query) and raised only on a tile whose probabilities would pass
+// kLaneSumLimit (or overflow); that tile is then redone from its scores.
+// MASK: the tile reaches past some query of the wave (diagonal tile).
+// SPLIT: P enters the product as bf16 hi + lo.
+template <int DH, bool MASK, bool SPLIT, bool QPRE>
 __device__ __forceinline__ void attn_tile(const unsigned char *__restrict__ Ks, const unsigned char *__restrict__ Vs,
                                           const FragAddr<DH> &fa, const bf16x8 (&qf)[DH / 16],
-                                          f32x16 (&oacc)[DH / 32], float &m_run, float &l_part, int kstart, int qpos,
-                                          float c, int lane) {
+                                          f32x16 (&oacc)[DH / 32], f32x16 &bias, float &m_run, float &l_part,
+                                          int kstart, int qpos, bool first, float c, int lane) {
   using G = KvTile<DH>;
   constexpr int ND = DH / 32;
   const int g = lane >> 5;
-  // ---- S^T = K Q^T for the 64 keys: two independent 32-key accumulators
-  // (raised issue priority while this wave feeds the matrix pipe, so the
-  // other wave of the SIMD fills the gaps with its softmax)
+  // ---- S^T - m = K Q^T + bias for the 64 keys: two independent 32-key
+  // accumulators (raised issue priority while this wave feeds the matrix
+  // pipe, so the other wave of the SIMD fills the gaps with its softmax)
   __builtin_amdgcn_s_setprio(1);
   f32x16 sacc[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
 #pragma unroll
   for (int kk = 0; kk < DH / 16; ++kk)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + fa.k[kk] + kb * 32 * G::ROWB);
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb], 0, 0, 0);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], kk == 0 ? bias : sacc[kb], 0, 0, 0);
     }
   __builtin_amdgcn_s_setprio(0);
   // sacc[kb][v] is the score of key kstart + kb*32 + 8*(v/4) + 4*g + v%4
@@ -163,55 +217,41 @@ __device__ __forceinline__ void attn_tile(const unsigned char *__restrict__ Ks, 
         if (key > qpos) sacc[kb][v] = -INFINITY;
       }
   }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-  mx = halves_max(mx);
-  // scaled max; only a masked tile can leave a lane with -inf (and -inf * 0
-  // must not become NaN)
-  float mxs = mx * c;
-  if constexpr (MASK) mxs = mx == -INFINITY ? -INFINITY : mxs;
-  if (__any(mxs > m_run + kRescaleLog2)) {
-    const float m_new = fmaxf(m_run, mxs);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_part *= alpha;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+  bf16x8 ph[4], pl[4];
+  float lt = 0.f;
+  bool redo = first;
+  if (!first) {
+    lt = tile_probs<false, MASK, SPLIT, QPRE>(sacc, 0.f, c, kstart, qpos, g, ph, pl);
+    // !(x <= limit) also catches an overflow to inf
+    redo = __any(!(lt <= kLaneSumLimit));
   }
-  const float neg_m = -m_run;
-  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-  // ---- probabilities, 16 keys (8 per lane) per step, and O^T += V^T P^T
+  if (redo) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
+    mx = halves_max(mx);
+    // On the first tile (bias 0) mx is the row's max score, finite; later,
+    // mx is -inf only when every key of the tile is masked for the query.
+    const float delta = first ? mx : fmaxf(mx, 0.f);
+    if (!first) {
+      const float alpha = __builtin_amdgcn_exp2f(QPRE ? -delta : -delta * c);
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+    }
+    m_run += delta;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) bias[v] = -m_run;
+    lt = tile_probs<true, MASK, SPLIT, QPRE>(sacc, delta, c, kstart, qpos, g, ph, pl);
+  }
+  l_part += lt;
+  // ---- O^T += V^T P^T, 16 keys per step
 #pragma unroll
   for (int kq = 0; kq < 4; ++kq) {
-    const int kb = kq >> 1, v0 = (kq & 1) * 8;
-    bf16x8 ph, pl;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v0 + e], c, neg_m));
-      float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v0 + e + 1], c, neg_m));
-      if constexpr (MASK) {
-        // masked scores hold -inf, which a zero scale would turn into NaN
-        const int key0 = kstart + kq * 16 + (e >> 2) * 8 + g * 4 + (e & 3);
-        if (key0 > qpos) p0 = 0.f;
-        if (key0 + 1 > qpos) p1 = 0.f;
-      }
-      const bf16x2 h2 = {(bf16)p0, (bf16)p1};
-      ph[e] = h2[0];
-      ph[e + 1] = h2[1];
-      if constexpr (SPLIT) {
-        const bf16x2 l2 = {(bf16)(p0 - (float)h2[0]), (bf16)(p1 - (float)h2[1])};
-        pl[e] = l2[0];
-        pl[e + 1] = l2[1];
-        l_part += p0 + p1;
-      } else {
-        l_part = __builtin_amdgcn_fdot2_f32_bf16(h2, ones, l_part, false);
-      }
-    }
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
       // transpose read: lane r of each 16-lane group points at key
@@ -226,8 +266,8 @@ __device__ __forceinline__ void attn_tile(const unsigned char *__restrict__ Ks, 
       const s16x8_t both = {part[0][0], part[0][1], part[0][2], part[0][3],
                             part[1][0], part[1][1], part[1][2], part[1][3]};
       const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph, oacc[db], 0, 0, 0);
-      if constexpr (SPLIT) oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl, oacc[db], 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph[kq], oacc[db], 0, 0, 0);
+      if constexpr (SPLIT) oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[kq], oacc[db], 0, 0, 0);
     }
   }
 }
@@ -260,16 +300,17 @@ __device__ __forceinline__ void copy_tile(const KvCopy<DH> &cp, unsigned char (*
 // Key tiles [kt0, kt1) of a walk of n_kt tiles: the tile in stage kt & 1 is
 // already in LDS when tile kt starts; tile kt + 1 is copied meanwhile. Each
 // variant runs its own loop so that the hot one carries no rare-case code.
-template <int DH, bool MASK, bool SPLIT, int CUR>
+template <int DH, bool MASK, bool SPLIT, bool QPRE, int CUR>
 __device__ __forceinline__ void attn_step(const KvCopy<DH> &cp, unsigned char (*smem)[2][KvTile<DH>::BYTES], int kt,
                                           int n_kt, bool active, int wmax, const FragAddr<DH> &fa,
                                           const bf16x8 (&qf)[DH / 16],
-                                          f32x16 (&oacc)[DH / 32], float &m_run, float &l_part, int qpos, float c,
-                                          int lane) {
+                                          f32x16 (&oacc)[DH / 32], f32x16 &bias, float &m_run, float &l_part, int qpos,
+                                          float c, int lane) {
   if (kt + 1 < n_kt) copy_tile<DH>(cp, smem, kt + 1, CUR ^ 1);
   const int kstart = kt * kBKey;
   if (active && (!MASK || kstart <= wmax))
-    attn_tile<DH, MASK, SPLIT>(smem[CUR][0], smem[CUR][1], fa, qf, oacc, m_run, l_part, kstart, qpos, c, lane);
+    attn_tile<DH, MASK, SPLIT, QPRE>(smem[CUR][0], smem[CUR][1], fa, qf, oacc, bias, m_run, l_part, kstart, qpos,
+                                     kt == 0, c, lane);
   // the next tile's copy has landed (this wave's part), and every wave is
   // done with the current stage before it is overwritten
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -280,26 +321,31 @@ __device__ __forceinline__ void attn_step(const KvCopy<DH> &cp, unsigned char (*
 // kt & 1 when it starts, and tile kt + 1 is copied meanwhile. The loop runs
 // two tiles per trip so that each stage's LDS offsets are constants. Each
 // variant runs its own loop so that the hot one carries no rare-case code.
-template <int DH, bool MASK, bool SPLIT>
+template <int DH, bool MASK, bool SPLIT, bool QPRE>
 __device__ __forceinline__ void attn_walk(const KvCopy<DH> &cp, unsigned char (*smem)[2][KvTile<DH>::BYTES], int kt0,
                                           int kt1, int n_kt, bool active, int wmax, const FragAddr<DH> &fa,
                                           const bf16x8 (&qf)[DH / 16],
-                                          f32x16 (&oacc)[DH / 32], float &m_run, float &l_part, int qpos, float c,
-                                          int lane) {
+                                          f32x16 (&oacc)[DH / 32], f32x16 &bias, float &m_run, float &l_part, int qpos,
+                                          float c, int lane) {
   int kt = kt0;
   if (kt < kt1 && (kt & 1)) {
-    attn_step<DH, MASK, SPLIT, 1>(cp, smem, kt, n_kt, active, wmax, fa, qf, oacc, m_run, l_part, qpos, c, lane);
+    attn_step<DH, MASK, SPLIT, QPRE, 1>(cp, smem, kt, n_kt, active, wmax, fa, qf, oacc, bias, m_run, l_part, qpos, c,
+                                        lane);
     ++kt;
   }
   for (; kt + 1 < kt1; kt += 2) {
-    attn_step<DH, MASK, SPLIT, 0>(cp, smem, kt, n_kt, active, wmax, fa, qf, oacc, m_run, l_part, qpos, c, lane);
-    attn_step<DH, MASK, SPLIT, 1>(cp, smem, kt + 1, n_kt, active, wmax, fa, qf, oacc, m_run, l_part, qpos, c, lane);
+    attn_step<DH, MASK, SPLIT, QPRE, 0>(cp, smem, kt, n_kt, active, wmax, fa, qf, oacc, bias, m_run, l_part, qpos, c,
+                                        lane);
+    attn_step<DH, MASK, SPLIT, QPRE, 1>(cp, smem, kt + 1, n_kt, active, wmax, fa, qf, oacc, bias, m_run, l_part, qpos,
+                                        c, lane);
   }
-  if (kt < kt1) attn_step<DH, MASK, SPLIT, 0>(cp, smem, kt, n_kt, active, wmax, fa, qf, oacc, m_run, l_part, qpos, c, lane);
+  if (kt < kt1)
+    attn_step<DH, MASK, SPLIT, QPRE, 0>(cp, smem, kt, n_kt, active, wmax, fa, qf, oacc, bias, m_run, l_part, qpos, c,
+                                        lane);
 }
 #endif  // __HIP_DEVICE_COMPILE__
 
-template <int DH, bool OUT_F32>
+template <int DH, bool OUT_F32, bool QPRE>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using G = KvTile<DH>;
@@ -371,18 +417,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
-    float m_run = -INFINITY, l_part = 0.f;
+    // reference max (log2 domain) and the S^T accumulators' start value -m;
+    // the first key tile sets both
+    float m_run = 0.f, l_part = 0.f;
+    f32x16 bias;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) bias[v] = 0.f;
 
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
 
     if (split) {
-      attn_walk<DH, true, true>(cp, smem, 0, n_kt, n_kt, active, wmax, fa, qf, oacc, m_run, l_part, qpos, a.c, lane);
+      attn_walk<DH, true, true, QPRE>(cp, smem, 0, n_kt, n_kt, active, wmax, fa, qf, oacc, bias, m_run, l_part, qpos,
+                                      a.c, lane);
     } else {
-      attn_walk<DH, false, false>(cp, smem, 0, kt_diag, n_kt, active, wmax, fa, qf, oacc, m_run, l_part, qpos, a.c,
-                                  lane);
-      attn_walk<DH, true, false>(cp, smem, kt_diag, n_kt, n_kt, active, wmax, fa, qf, oacc, m_run, l_part, qpos, a.c,
-                                 lane);
+      attn_walk<DH, false, false, QPRE>(cp, smem, 0, kt_diag, n_kt, active, wmax, fa, qf, oacc, bias, m_run, l_part,
+                                        qpos, a.c, lane);
+      attn_walk<DH, true, false, QPRE>(cp, smem, kt_diag, n_kt, n_kt, active, wmax, fa, qf, oacc, bias, m_run,
+                                       l_part, qpos, a.c, lane);
     }
 
     // ---- normalise and store: oacc[db][v] is O[query][db*32 + 8*(v/4) + 4*g + v%4]
@@ -465,11 +517,103 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
+// Attention of the first m <= 64 positions among themselves in fp32 (the
+// leading rows of rank 0, whose keys are exactly those rows): one block per
+// head, K and V of the m rows staged in LDS, four threads per query, each
+// scoring 16 keys and later producing a quarter of the output features.
+// q, k, v, o: [m][H][DH] fp32.
+template <int DH>
+__global__ __launch_bounds__(256) void lead_attn_kernel(const float *__restrict__ q, const float *__restrict__ k,
+                                                        const float *__restrict__ v, float *__restrict__ o, int m,
+                                                        int H, float scale) {
+  __shared__ __attribute__((aligned(16))) float KP[64 * DH];  // K rows, later P [64][64]
+  __shared__ __attribute__((aligned(16))) float Vs[64 * DH];
+  const int head = blockIdx.x, tid = threadIdx.x;
+  const int64_t rs = (int64_t)H * DH;
+  for (int e = tid * 4; e < 64 * DH; e += 1024) {
+    const int r = e / DH, d = e - r * DH;
+    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+    if (r < m) {
+      kv = *reinterpret_cast<const float4 *>(k + r * rs + head * DH + d);
+      vv = *reinterpret_cast<const float4 *>(v + r * rs + head * DH + d);
+    }
+    *reinterpret_cast<float4 *>(&KP[e]) = kv;
+    *reinterpret_cast<float4 *>(&Vs[e]) = vv;
+  }
+  __syncthreads();
+  const int i = tid >> 2, part = tid & 3;  // query i; keys (then features) of quarter part
+  const float *qi = q + (int64_t)min(i, m - 1) * rs + head * DH;
+  float sc[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) sc[t] = 0.f;
+  for (int d = 0; d < DH; d += 4) {
+    const float4 qv = *reinterpret_cast<const float4 *>(qi + d);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const float4 kv = *reinterpret_cast<const float4 *>(&KP[(16 * part + t) * DH + d]);
+      sc[t] = fmaf(qv.x, kv.x, fmaf(qv.y, kv.y, fmaf(qv.z, kv.z, fmaf(qv.w, kv.w, sc[t]))));
+    }
+  }
+  // causal: key j is visible to query i when j <= i
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+    if (16 * part + t <= i) mx = fmaxf(mx, sc[t] * scale);
+  mx = fmaxf(mx, __shfl_xor(mx, 1));
+  mx = fmaxf(mx, __shfl_xor(mx, 2));
+  float l = 0.f;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    sc[t] = 16 * part + t <= i ? expf(sc[t] * scale - mx) : 0.f;
+    l += sc[t];
+  }
+  l += __shfl_xor(l, 1);
+  l += __shfl_xor(l, 2);
+  __syncthreads();  // every score is taken: K's space now holds P
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) KP[i * 64 + 16 * part + t] = sc[t] * inv;
+  __syncthreads();
+  constexpr int DQ = DH / 4;
+  float acc[DQ];
+#pragma unroll
+  for (int dd = 0; dd < DQ; ++dd) acc[dd] = 0.f;
+  for (int j = 0; j <= i; ++j) {
+    const float pj = KP[i * 64 + j];
+#pragma unroll
+    for (int dd = 0; dd < DQ; dd += 4) {
+      const float4 vv = *reinterpret_cast<const float4 *>(&Vs[j * DH + part * DQ + dd]);
+      acc[dd] = fmaf(pj, vv.x, acc[dd]);
+      acc[dd + 1] = fmaf(pj, vv.y, acc[dd + 1]);
+      acc[dd + 2] = fmaf(pj, vv.z, acc[dd + 2]);
+      acc[dd + 3] = fmaf(pj, vv.w, acc[dd + 3]);
+    }
+  }
+  if (i < m) {
+    float *oi = o + (int64_t)i * rs + head * DH + part * DQ;
+#pragma unroll
+    for (int dd = 0; dd < DQ; dd += 4)
+      *reinterpret_cast<float4 *>(oi + dd) = make_float4(acc[dd], acc[dd + 1], acc[dd + 2], acc[dd + 3]);
+  }
+}
+
+hipError_t launch_lead_attention(const float *q, const float *k, const float *v, float *o, int32_t m, int32_t H,
+                                 int32_t Dh, float scale, hipStream_t s) {
+  if (m <= 0) return hipSuccess;
+  if (m > 64) return hipErrorInvalidValue;
+  if (Dh == 128)
+    hipLaunchKernelGGL((lead_attn_kernel<128>), dim3(H), dim3(256), 0, s, q, k, v, o, m, H, scale);
+  else
+    hipLaunchKernelGGL((lead_attn_kernel<64>), dim3(H), dim3(256), 0, s, q, k, v, o, m, H, scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(int dtype, const void *q, const void *k, const void *v, void *o, int o_dtype,
                             bool o_panel, int64_t S, int32_t n, int32_t H, int32_t Dh, float scale, ZigzagMap zz,
-                            hipStream_t s) {
+                            bool q_prescaled, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (o_panel && (dtype != TSP_BF16 || o_dtype != TSP_BF16)) return hipErrorInvalidValue;
+  if (q_prescaled && (dtype != TSP_BF16 || o_dtype != TSP_BF16)) return hipErrorInvalidValue;
   AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -488,14 +632,18 @@ hipError_t launch_attention(int dtype, const void *q, const void *k, const void 
     const bool f32out = o_dtype == TSP_F32;
     if (Dh == 128) {
       if (f32out)
-        hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, dim3(kAttnThreads), 0, s, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<128, true, false>), grid, dim3(kAttnThreads), 0, s, a);
+      else if (q_prescaled)
+        hipLaunchKernelGGL((attn_bf16_kernel<128, false, true>), grid, dim3(kAttnThreads), 0, s, a);
       else
-        hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, dim3(kAttnThreads), 0, s, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<128, false, false>), grid, dim3(kAttnThreads), 0, s, a);
     } else {
       if (f32out)
-        hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, dim3(kAttnThreads), 0, s, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<64, true, false>), grid, dim3(kAttnThreads), 0, s, a);
+      else if (q_prescaled)
+        hipLaunchKernelGGL((attn_bf16_kernel<64, false, true>), grid, dim3(kAttnThreads), 0, s, a);
       else
-        hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, dim3(kAttnThreads), 0, s, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<64, false, false>), grid, dim3(kAttnThreads), 0, s, a);
     }
   } else {
     dim3 grid((n + 63) / 64, H);

@@ -28,6 +28,8 @@
 // engine streams at close to its full rate; from row-major A with a long row
 // pitch every copy instruction touches 8 rows far apart and the rate halves.
 // fp32 operands use a plain LDS-tiled FMA kernel (64x64 tiles, 4x4 per thread).
+#include <algorithm>
+
 #include "device_common.h"
 #include "tsp_internal.h"
 
@@ -156,22 +158,32 @@ struct EpiQKV {
   int64_t h;
   int32_t hd;
   ZigzagMap zz;
+  float q_scale;  // factor applied to the Q part before rounding
   __device__ __forceinline__ T *dst(int z, int r, int c) const {
     const int part = c / hd;
     const int64_t col = (int64_t)z * hd + (c - part * hd);
     if (part == 0) return q + (int64_t)r * h + col;
     return (part == 1 ? k : v) + (int64_t)zz.pos(r) * h + col;
   }
-  __device__ __forceinline__ void operator()(int z, int r, int c, float val) const { *dst(z, r, c) = (T)val; }
-  __device__ __forceinline__ void operator()(int z, int r, int c, float4 val) const { store4(dst(z, r, c), val); }
+  __device__ __forceinline__ float factor(int c) const { return c < hd ? q_scale : 1.0f; }
+  __device__ __forceinline__ void operator()(int z, int r, int c, float val) const {
+    *dst(z, r, c) = (T)(val * factor(c));
+  }
+  __device__ __forceinline__ void operator()(int z, int r, int c, float4 val) const {
+    const float f = factor(c);
+    store4(dst(z, r, c), make_float4(val.x * f, val.y * f, val.z * f, val.w * f));
+  }
   // whole 128-column blocks stay inside one part when hd is a multiple of 128
   struct Row {
     T *p;
+    float f;
   };
   __device__ __forceinline__ bool fast_ok() const { return (hd & 127) == 0; }
-  __device__ __forceinline__ Row row(int z, int r, int c0, int g) const { return Row{dst(z, r, c0 + 4 * g)}; }
+  __device__ __forceinline__ Row row(int z, int r, int c0, int g) const {
+    return Row{dst(z, r, c0 + 4 * g), factor(c0)};
+  }
   __device__ __forceinline__ void put(const Row &w, int i, int vq, float4 v) const {
-    store4(w.p + i * 32 + vq * 8, v);
+    store4(w.p + i * 32 + vq * 8, make_float4(v.x * w.f, v.y * w.f, v.z * w.f, v.w * w.f));
   }
 };
 
@@ -514,6 +526,189 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, Epi epi) {
     }
 }
 
+// ---------------------------------------------------------------- leading rows
+// C = A B^T for at most kLeadRows rows with fp32 A and bf16 B, accurate to
+// fp32 level: A is split into bf16 hi + lo (A - hi is exact in fp32, and lo
+// keeps it to 2^-9 of itself, so A = hi + lo to about 2^-17 relative), and B
+// is exactly bf16, so hi B^T + lo B^T on the matrix cores, accumulated in
+// fp32, reproduces the fp32 product. The few rows make this a weight stream:
+// each wave owns 32 columns and one K chunk for all rows (two 32-row MFMA
+// blocks), so every weight is read once; the K chunks' partial sums go to
+// part[chunk][row][z*N + column] and a second kernel adds them in chunk order
+// (deterministic) and applies the epilogue.
+// Largest chunk of 512, 256, 128 or 64 that divides the segment length.
+static int lead_chunk(int kseg) {
+  for (int c = 512; c > 64; c >>= 1)
+    if (kseg % c == 0) return c;
+  return 64;
+}
+
+__global__ __launch_bounds__(256) void lead_gemm_kernel(GemmArgs a, int chunk, float *__restrict__ part) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int groups = (a.N + 127) / 128;  // 4 waves x 32 columns per block
+  const int z = blockIdx.x / groups;
+  const int n0 = (blockIdx.x - z * groups) * 128 + wave * 32;
+  if (n0 >= a.N) return;  // wave-uniform
+  const int kc = blockIdx.y, k_begin = kc * chunk;
+  int seg, koff;
+  if (a.nz > 1) {
+    seg = z;
+    koff = k_begin;
+  } else {
+    seg = k_begin / a.kseg;
+    koff = k_begin - seg * a.kseg;
+  }
+  const int l32 = lane & 31, g = lane >> 5;
+  // lane: B row n (column of C), A rows l32 and 32 + l32, K elements 8g..8g+7
+  // of each 16-wide slice. Lanes past N or M read row 0 instead: their
+  // products land only in columns or rows of C that are not stored.
+  const int n = n0 + l32;
+  const bool n_ok = n < a.N;
+  const bf16 *brow = reinterpret_cast<const bf16 *>(a.B.p[seg]) + (int64_t)(n_ok ? n : 0) * a.ldb + koff + 8 * g;
+  const float *A = reinterpret_cast<const float *>(a.A);
+  const float *arow0 = A + (int64_t)(l32 < a.M ? l32 : 0) * a.lda + k_begin + 8 * g;
+  const float *arow1 = A + (int64_t)(32 + l32 < a.M ? 32 + l32 : 0) * a.lda + k_begin + 8 * g;
+  auto split = [](const float4 x0, const float4 x1, bf16x8 &hi, bf16x8 &lo) {
+    const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 h2 = {(bf16)v[e], (bf16)v[e + 1]};
+      const bf16x2 l2 = {(bf16)(v[e] - (float)h2[0]), (bf16)(v[e + 1] - (float)h2[1])};
+      hi[e] = h2[0];
+      hi[e + 1] = h2[1];
+      lo[e] = l2[0];
+      lo[e + 1] = l2[1];
+    }
+  };
+  f32x16 acc0, acc1;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc0[v] = acc1[v] = 0.f;
+  // four 16-wide slices per trip, all loads issued before the first MFMA
+  for (int k = 0; k < chunk; k += 64) {
+    bf16x8 wf[4];
+    float4 x0[4][2], x1[4][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      wf[t] = *reinterpret_cast<const bf16x8 *>(brow + k + 16 * t);
+      x0[t][0] = *reinterpret_cast<const float4 *>(arow0 + k + 16 * t);
+      x0[t][1] = *reinterpret_cast<const float4 *>(arow0 + k + 16 * t + 4);
+      x1[t][0] = *reinterpret_cast<const float4 *>(arow1 + k + 16 * t);
+      x1[t][1] = *reinterpret_cast<const float4 *>(arow1 + k + 16 * t + 4);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      bf16x8 hi, lo;
+      split(x0[t][0], x0[t][1], hi, lo);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, wf[t], acc0, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, wf[t], acc0, 0, 0, 0);
+      split(x1[t][0], x1[t][1], hi, lo);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, wf[t], acc1, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, wf[t], acc1, 0, 0, 0);
+    }
+  }
+  // acc[v] is C[8*(v/4) + 4g + v%4 (+32 for acc1)][n]
+  if (!n_ok) return;
+  const int64_t ntot = (int64_t)a.nz * a.N;
+  float *pc = part + (int64_t)kc * a.M * ntot + (int64_t)z * a.N + n;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int r = 8 * (v >> 2) + 4 * g + (v & 3);
+    if (r < a.M) pc[r * ntot] = acc0[v];
+    if (r + 32 < a.M) pc[(r + 32) * ntot] = acc1[v];
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+template <class Epi>
+__global__ __launch_bounds__(256) void lead_reduce_kernel(int32_t M, int32_t N, int32_t nz, int32_t chunks,
+                                                          const float *__restrict__ part, Epi epi) {
+  const int64_t ntot = (int64_t)nz * N;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * ntot) return;
+  const int r = (int)(i / ntot);
+  const int64_t zc = i - r * ntot;
+  const int z = (int)(zc / N), c = (int)(zc - (int64_t)z * N);
+  float v = 0.f;
+  for (int kc = 0; kc < chunks; ++kc) v += part[((int64_t)kc * M + r) * ntot + zc];
+  epi(z, r, c, v);
+}
+
+template <class Epi>
+static hipError_t run_lead(const GemmArgs &a, const Epi &epi, float *part, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.M > kLeadRows) return hipErrorInvalidValue;
+  const int chunk = lead_chunk(a.kseg);
+  const int chunks = a.K / chunk;
+  dim3 grid(a.nz * ((a.N + 127) / 128), chunks);
+  hipLaunchKernelGGL(lead_gemm_kernel, grid, dim3(256), 0, s, a, chunk, part);
+  const int64_t total = (int64_t)a.M * a.nz * a.N;
+  hipLaunchKernelGGL((lead_reduce_kernel<Epi>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a.M, a.N,
+                     a.nz, chunks, (const float *)part, epi);
+  return hipGetLastError();
+}
+
+static GemmArgs lead_args(const float *A, int64_t lda, int32_t M, int32_t N, int32_t K) {
+  GemmArgs a{};
+  a.A = A;
+  a.lda = lda;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.kseg = K;
+  a.nz = 1;
+  return a;
+}
+
+size_t lead_part_bytes(int32_t m, int32_t h, int32_t F, int32_t D) {
+  const int32_t hd = h / D, fd = F / D;
+  const size_t qkv = (size_t)(h / lead_chunk(h)) * m * 3 * h;
+  const size_t op = (size_t)(h / lead_chunk(hd)) * m * h;
+  const size_t up = (size_t)(h / lead_chunk(h)) * m * F;
+  const size_t dn = (size_t)(F / lead_chunk(fd)) * m * h;
+  return 4 * std::max(std::max(qkv, op), std::max(up, dn));
+}
+
+hipError_t launch_lead_qkv(const float *a, int32_t m, int32_t h, const PtrList &w, int32_t D, int32_t hd, float *q,
+                           float *k, float *v, ZigzagMap zz, float *part, hipStream_t s) {
+  GemmArgs g = lead_args(a, h, m, 3 * hd, h);
+  g.B = w;
+  g.ldb = h;
+  g.nz = D;
+  EpiQKV<float> e{q, k, v, h, hd, zz, 1.0f};
+  return run_lead(g, e, part, s);
+}
+
+hipError_t launch_lead_outproj(const float *o, int32_t m, int32_t h, const PtrList &wo, int32_t D, int32_t hd,
+                               const float *x, float *y, float *part, hipStream_t s) {
+  GemmArgs g = lead_args(o, h, m, h, D * hd);
+  g.B = wo;
+  g.ldb = hd;
+  g.kseg = hd;
+  EpiAddF32 e{x, y, h};
+  return run_lead(g, e, part, s);
+}
+
+hipError_t launch_lead_mlp_up(const float *a, int32_t m, int32_t h, const PtrList &w1, int32_t D, int32_t fd,
+                              float *hid, float *part, hipStream_t s) {
+  GemmArgs g = lead_args(a, h, m, fd, h);
+  g.B = w1;
+  g.ldb = h;
+  g.nz = D;
+  EpiGelu<float> e{hid, (int64_t)D * fd, 0, fd};
+  return run_lead(g, e, part, s);
+}
+
+hipError_t launch_lead_mlp_down(const float *hid, int32_t m, const PtrList &w2, int32_t D, int32_t fd, int32_t h,
+                                const float *res, float *y, float *part, hipStream_t s) {
+  GemmArgs g = lead_args(hid, (int64_t)D * fd, m, h, D * fd);
+  g.B = w2;
+  g.ldb = fd;
+  g.kseg = fd;
+  EpiAddF32 e{res, y, h};
+  return run_lead(g, e, part, s);
+}
+
 // ---------------------------------------------------------------- launchers
 template <class Epi>
 static hipError_t run_gemm(int dtype, const GemmArgs &a, const Epi &epi, hipStream_t s) {
@@ -551,16 +746,16 @@ static GemmArgs make_args(const void *A, int64_t lda, bool a_panel, int32_t M, i
 }
 
 hipError_t launch_qkv(int dtype, const void *xn, bool a_panel, int32_t n, int32_t h, const PtrList &w, int32_t D,
-                      int32_t hd, void *q, void *kf, void *vf, ZigzagMap zz, hipStream_t s) {
+                      int32_t hd, void *q, void *kf, void *vf, ZigzagMap zz, float q_scale, hipStream_t s) {
   GemmArgs a = make_args(xn, h, a_panel, n, 3 * hd, h);
   a.B = w;
   a.ldb = h;
   a.nz = D;
   if (dtype == TSP_BF16) {
-    EpiQKV<bf16> e{(bf16 *)q, (bf16 *)kf, (bf16 *)vf, h, hd, zz};
+    EpiQKV<bf16> e{(bf16 *)q, (bf16 *)kf, (bf16 *)vf, h, hd, zz, q_scale};
     return run_gemm(dtype, a, e, s);
   }
-  EpiQKV<float> e{(float *)q, (float *)kf, (float *)vf, h, hd, zz};
+  EpiQKV<float> e{(float *)q, (float *)kf, (float *)vf, h, hd, zz, q_scale};
   return run_gemm(dtype, a, e, s);
 }
 

@@ -65,4 +65,16 @@ hipError_t launch_rmsnorm(const float *x, const void *g, void *out, int32_t rows
   return hipGetLastError();
 }
 
+hipError_t launch_rmsnorm_f32(const float *x, const void *g, int g_dtype, float *out, int32_t rows, int32_t h,
+                              float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (g_dtype == TSP_BF16)
+    hipLaunchKernelGGL((rmsnorm_kernel<bf16, float>), dim3(rows), dim3(256), 0, s, x, (const bf16 *)g, out, h, eps,
+                       (int64_t)0);
+  else
+    hipLaunchKernelGGL((rmsnorm_kernel<float, float>), dim3(rows), dim3(256), 0, s, x, (const float *)g, out, h, eps,
+                       (int64_t)0);
+  return hipGetLastError();
+}
+
 }  // namespace tsp
