@@ -132,12 +132,11 @@ __device__ __forceinline__ FragAddr<DH> frag_addr(int lane) {
 
 // Probabilities of the 64 scores held by the lane, minus a shift (log2
 // domain): P as bf16 (hi, and lo = p - hi when SPLIT) in MFMA B-operand
-// order, and the lane's sum of them. With Q not pre-scaled, keys past qpos
-// get 0 when MASK (their scores hold -inf, which a zero scale would turn into
-// NaN); pre-scaled, exp2(-inf) is 0 already.
-template <bool SHIFT, bool MASK, bool SPLIT, bool QPRE>
-__device__ __forceinline__ float tile_probs(const f32x16 (&sacc)[2], float shift, float c, int kstart, int qpos, int g,
-                                            bf16x8 (&ph)[4], bf16x8 (&pl)[4]) {
+// order, and the lane's sum of them. Masked keys hold -inf and get 0 (the
+// multiplier c is never 0: see launch_attention).
+template <bool SHIFT, bool SPLIT, bool QPRE>
+__device__ __forceinline__ float tile_probs(const f32x16 (&sacc)[2], float shift, float c, bf16x8 (&ph)[4],
+                                            bf16x8 (&pl)[4]) {
   const float nsc = -shift * c;
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
   float lt = 0.f;
@@ -149,12 +148,7 @@ __device__ __forceinline__ float tile_probs(const f32x16 (&sacc)[2], float shift
       const float s0 = sacc[kb][v0 + e], s1 = sacc[kb][v0 + e + 1];
       const float x0 = QPRE ? (SHIFT ? s0 - shift : s0) : (SHIFT ? fmaf(s0, c, nsc) : s0 * c);
       const float x1 = QPRE ? (SHIFT ? s1 - shift : s1) : (SHIFT ? fmaf(s1, c, nsc) : s1 * c);
-      float p0 = __builtin_amdgcn_exp2f(x0), p1 = __builtin_amdgcn_exp2f(x1);
-      if constexpr (MASK && !QPRE) {
-        const int key0 = kstart + kq * 16 + (e >> 2) * 8 + g * 4 + (e & 3);
-        if (key0 > qpos) p0 = 0.f;
-        if (key0 + 1 > qpos) p1 = 0.f;
-      }
+      const float p0 = __builtin_amdgcn_exp2f(x0), p1 = __builtin_amdgcn_exp2f(x1);
       const bf16x2 h2 = {(bf16)p0, (bf16)p1};
       ph[kq][e] = h2[0];
       ph[kq][e + 1] = h2[1];
@@ -221,7 +215,7 @@ __device__ __forceinline__ void attn_tile(const unsigned char *__restrict__ Ks, 
   float lt = 0.f;
   bool redo = first;
   if (!first) {
-    lt = tile_probs<false, MASK, SPLIT, QPRE>(sacc, 0.f, c, kstart, qpos, g, ph, pl);
+    lt = tile_probs<false, SPLIT, QPRE>(sacc, 0.f, c, ph, pl);
     // !(x <= limit) also catches an overflow to inf
     redo = __any(!(lt <= kLaneSumLimit));
   }
@@ -246,7 +240,7 @@ __device__ __forceinline__ void attn_tile(const unsigned char *__restrict__ Ks, 
     m_run += delta;
 #pragma unroll
     for (int v = 0; v < 16; ++v) bias[v] = -m_run;
-    lt = tile_probs<true, MASK, SPLIT, QPRE>(sacc, delta, c, kstart, qpos, g, ph, pl);
+    lt = tile_probs<true, SPLIT, QPRE>(sacc, delta, c, ph, pl);
   }
   l_part += lt;
   // ---- O^T += V^T P^T, 16 keys per step
@@ -437,22 +431,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
                                        l_part, qpos, a.c, lane);
     }
 
-    // ---- normalise and store: oacc[db][v] is O[query][db*32 + 8*(v/4) + 4*g + v%4]
+    // ---- normalise and store: oacc[db][v] is O[query][db*32 + 8*(v/4) + 4*g + v%4].
+    // Feature d = 32*db + 8*vq + 4*g of the head sits in 64-column panel
+    // head*DH/64 + db/2 at column 32*(db%2) + 8*vq + 4*g, so every store is a
+    // constant offset from one base pointer per lane (a per-column address
+    // would be hoisted out of the key walk and spilled).
     const float inv = 1.0f / halves_sum(l_part);
     if (my_valid) {
 #pragma unroll
       for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int vq = 0; vq < 4; ++vq) {
-          const int d0 = db * 32 + vq * 8 + g * 4;
           const float o0 = oacc[db][vq * 4 + 0] * inv, o1 = oacc[db][vq * 4 + 1] * inv;
           const float o2 = oacc[db][vq * 4 + 2] * inv, o3 = oacc[db][vq * 4 + 3] * inv;
           if constexpr (OUT_F32) {
-            float *og = reinterpret_cast<float *>(a.o) + qrow * rs + head * DH + d0;
-            *reinterpret_cast<float4 *>(og) = make_float4(o0, o1, o2, o3);
+            float *og = reinterpret_cast<float *>(a.o) + qrow * rs + head * DH + g * 4;
+            *reinterpret_cast<float4 *>(og + db * 32 + vq * 8) = make_float4(o0, o1, o2, o3);
           } else {
-            const int64_t col = head * DH + d0;
-            bf16 *og = reinterpret_cast<bf16 *>(a.o) + (a.o_panel ? panel_index(qrow, col, a.o_panel) : qrow * rs + col);
+            bf16 *og = reinterpret_cast<bf16 *>(a.o);
+            og += a.o_panel ? (int64_t)(head * DH / kPanel + (db >> 1)) * a.o_panel + qrow * kPanel + (db & 1) * 32
+                            : qrow * rs + head * DH + db * 32;
+            og += g * 4 + vq * 8;
             const bf16x2 w01 = {(bf16)o0, (bf16)o1}, w23 = {(bf16)o2, (bf16)o3};
             u32x2 u = {__builtin_bit_cast(uint32_t, w01), __builtin_bit_cast(uint32_t, w23)};
             *reinterpret_cast<u32x2 *>(og) = u;
@@ -517,97 +516,6 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-// Attention of the first m <= 64 positions among themselves in fp32 (the
-// leading rows of rank 0, whose keys are exactly those rows): one block per
-// head, K and V of the m rows staged in LDS, four threads per query, each
-// scoring 16 keys and later producing a quarter of the output features.
-// q, k, v, o: [m][H][DH] fp32.
-template <int DH>
-__global__ __launch_bounds__(256) void lead_attn_kernel(const float *__restrict__ q, const float *__restrict__ k,
-                                                        const float *__restrict__ v, float *__restrict__ o, int m,
-                                                        int H, float scale) {
-  __shared__ __attribute__((aligned(16))) float KP[64 * DH];  // K rows, later P [64][64]
-  __shared__ __attribute__((aligned(16))) float Vs[64 * DH];
-  const int head = blockIdx.x, tid = threadIdx.x;
-  const int64_t rs = (int64_t)H * DH;
-  for (int e = tid * 4; e < 64 * DH; e += 1024) {
-    const int r = e / DH, d = e - r * DH;
-    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-    if (r < m) {
-      kv = *reinterpret_cast<const float4 *>(k + r * rs + head * DH + d);
-      vv = *reinterpret_cast<const float4 *>(v + r * rs + head * DH + d);
-    }
-    *reinterpret_cast<float4 *>(&KP[e]) = kv;
-    *reinterpret_cast<float4 *>(&Vs[e]) = vv;
-  }
-  __syncthreads();
-  const int i = tid >> 2, part = tid & 3;  // query i; keys (then features) of quarter part
-  const float *qi = q + (int64_t)min(i, m - 1) * rs + head * DH;
-  float sc[16];
-#pragma unroll
-  for (int t = 0; t < 16; ++t) sc[t] = 0.f;
-  for (int d = 0; d < DH; d += 4) {
-    const float4 qv = *reinterpret_cast<const float4 *>(qi + d);
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const float4 kv = *reinterpret_cast<const float4 *>(&KP[(16 * part + t) * DH + d]);
-      sc[t] = fmaf(qv.x, kv.x, fmaf(qv.y, kv.y, fmaf(qv.z, kv.z, fmaf(qv.w, kv.w, sc[t]))));
-    }
-  }
-  // causal: key j is visible to query i when j <= i
-  float mx = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < 16; ++t)
-    if (16 * part + t <= i) mx = fmaxf(mx, sc[t] * scale);
-  mx = fmaxf(mx, __shfl_xor(mx, 1));
-  mx = fmaxf(mx, __shfl_xor(mx, 2));
-  float l = 0.f;
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    sc[t] = 16 * part + t <= i ? expf(sc[t] * scale - mx) : 0.f;
-    l += sc[t];
-  }
-  l += __shfl_xor(l, 1);
-  l += __shfl_xor(l, 2);
-  __syncthreads();  // every score is taken: K's space now holds P
-  const float inv = 1.0f / l;
-#pragma unroll
-  for (int t = 0; t < 16; ++t) KP[i * 64 + 16 * part + t] = sc[t] * inv;
-  __syncthreads();
-  constexpr int DQ = DH / 4;
-  float acc[DQ];
-#pragma unroll
-  for (int dd = 0; dd < DQ; ++dd) acc[dd] = 0.f;
-  for (int j = 0; j <= i; ++j) {
-    const float pj = KP[i * 64 + j];
-#pragma unroll
-    for (int dd = 0; dd < DQ; dd += 4) {
-      const float4 vv = *reinterpret_cast<const float4 *>(&Vs[j * DH + part * DQ + dd]);
-      acc[dd] = fmaf(pj, vv.x, acc[dd]);
-      acc[dd + 1] = fmaf(pj, vv.y, acc[dd + 1]);
-      acc[dd + 2] = fmaf(pj, vv.z, acc[dd + 2]);
-      acc[dd + 3] = fmaf(pj, vv.w, acc[dd + 3]);
-    }
-  }
-  if (i < m) {
-    float *oi = o + (int64_t)i * rs + head * DH + part * DQ;
-#pragma unroll
-    for (int dd = 0; dd < DQ; dd += 4)
-      *reinterpret_cast<float4 *>(oi + dd) = make_float4(acc[dd], acc[dd + 1], acc[dd + 2], acc[dd + 3]);
-  }
-}
-
-hipError_t launch_lead_attention(const float *q, const float *k, const float *v, float *o, int32_t m, int32_t H,
-                                 int32_t Dh, float scale, hipStream_t s) {
-  if (m <= 0) return hipSuccess;
-  if (m > 64) return hipErrorInvalidValue;
-  if (Dh == 128)
-    hipLaunchKernelGGL((lead_attn_kernel<128>), dim3(H), dim3(256), 0, s, q, k, v, o, m, H, scale);
-  else
-    hipLaunchKernelGGL((lead_attn_kernel<64>), dim3(H), dim3(256), 0, s, q, k, v, o, m, H, scale);
-  return hipGetLastError();
-}
-
 hipError_t launch_attention(int dtype, const void *q, const void *k, const void *v, void *o, int o_dtype,
                             bool o_panel, int64_t S, int32_t n, int32_t H, int32_t Dh, float scale, ZigzagMap zz,
                             bool q_prescaled, hipStream_t s) {
@@ -623,7 +531,10 @@ hipError_t launch_attention(int dtype, const void *q, const void *k, const void 
   a.n = n;
   a.H = H;
   a.scale = scale;
-  a.c = scale * 1.4426950408889634f;
+  // Multiplier of the scores in the exp2 domain. Kept at least the smallest
+  // normal float, so that masked scores (-inf) still give 0 with a zero scale;
+  // the weights then differ from uniform by under |s| * 2^-126.
+  a.c = fmaxf(scale * 1.4426950408889634f, 1.17549435e-38f);
   a.zz = zz;
   a.T = (zz.C + kBQ - 1) / kBQ;
   a.o_panel = o_panel ? (int64_t)n * kPanel : 0;

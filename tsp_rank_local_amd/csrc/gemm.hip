@@ -533,9 +533,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, Epi epi) {
 // is exactly bf16, so hi B^T + lo B^T on the matrix cores, accumulated in
 // fp32, reproduces the fp32 product. The few rows make this a weight stream:
 // each wave owns 32 columns and one K chunk for all rows (two 32-row MFMA
-// blocks), so every weight is read once; the K chunks' partial sums go to
-// part[chunk][row][z*N + column] and a second kernel adds them in chunk order
-// (deterministic) and applies the epilogue.
+// blocks), so every weight is read once, and the block's 4 waves share each
+// 64-wide slab of A (split once) through LDS. The K chunks' partial sums go
+// to part[chunk][row][z*N + column] and a second kernel adds them in chunk
+// order (deterministic) and applies the epilogue.
 // Largest chunk of 512, 256, 128 or 64 that divides the segment length.
 static int lead_chunk(int kseg) {
   for (int c = 512; c > 64; c >>= 1)
@@ -545,11 +546,15 @@ static int lead_chunk(int kseg) {
 
 __global__ __launch_bounds__(256) void lead_gemm_kernel(GemmArgs a, int chunk, float *__restrict__ part) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // one 64-wide K slab of A for all 64 rows, split into bf16 hi and lo and
+  // shared by the block's 4 waves; rows padded by 16 bytes so that the
+  // fragment reads of 32 consecutive rows spread over the banks
+  constexpr int kSlab = 64, kPitch = kSlab + 8;
+  __shared__ __attribute__((aligned(16))) bf16 Ah[kLeadRows * kPitch], Al[kLeadRows * kPitch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int groups = (a.N + 127) / 128;  // 4 waves x 32 columns per block
   const int z = blockIdx.x / groups;
   const int n0 = (blockIdx.x - z * groups) * 128 + wave * 32;
-  if (n0 >= a.N) return;  // wave-uniform
   const int kc = blockIdx.y, k_begin = kc * chunk;
   int seg, koff;
   if (a.nz > 1) {
@@ -561,50 +566,53 @@ __global__ __launch_bounds__(256) void lead_gemm_kernel(GemmArgs a, int chunk, f
   }
   const int l32 = lane & 31, g = lane >> 5;
   // lane: B row n (column of C), A rows l32 and 32 + l32, K elements 8g..8g+7
-  // of each 16-wide slice. Lanes past N or M read row 0 instead: their
-  // products land only in columns or rows of C that are not stored.
+  // of each 16-wide slice. Lanes past N read row 0 instead: their products
+  // land only in columns of C that are not stored (likewise A rows past M).
   const int n = n0 + l32;
   const bool n_ok = n < a.N;
   const bf16 *brow = reinterpret_cast<const bf16 *>(a.B.p[seg]) + (int64_t)(n_ok ? n : 0) * a.ldb + koff + 8 * g;
-  const float *A = reinterpret_cast<const float *>(a.A);
-  const float *arow0 = A + (int64_t)(l32 < a.M ? l32 : 0) * a.lda + k_begin + 8 * g;
-  const float *arow1 = A + (int64_t)(32 + l32 < a.M ? 32 + l32 : 0) * a.lda + k_begin + 8 * g;
-  auto split = [](const float4 x0, const float4 x1, bf16x8 &hi, bf16x8 &lo) {
-    const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const bf16x2 h2 = {(bf16)v[e], (bf16)v[e + 1]};
-      const bf16x2 l2 = {(bf16)(v[e] - (float)h2[0]), (bf16)(v[e + 1] - (float)h2[1])};
-      hi[e] = h2[0];
-      hi[e + 1] = h2[1];
-      lo[e] = l2[0];
-      lo[e + 1] = l2[1];
-    }
-  };
+  // slab staging: thread -> A row tid/4, 16 consecutive K elements
+  const int sr = tid >> 2, sk = (tid & 3) * 16;
+  const float *asrc = reinterpret_cast<const float *>(a.A) + (int64_t)(sr < a.M ? sr : 0) * a.lda + k_begin + sk;
   f32x16 acc0, acc1;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc0[v] = acc1[v] = 0.f;
-  // four 16-wide slices per trip, all loads issued before the first MFMA
-  for (int k = 0; k < chunk; k += 64) {
+  for (int k = 0; k < chunk; k += kSlab) {
     bf16x8 wf[4];
-    float4 x0[4][2], x1[4][2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      wf[t] = *reinterpret_cast<const bf16x8 *>(brow + k + 16 * t);
-      x0[t][0] = *reinterpret_cast<const float4 *>(arow0 + k + 16 * t);
-      x0[t][1] = *reinterpret_cast<const float4 *>(arow0 + k + 16 * t + 4);
-      x1[t][0] = *reinterpret_cast<const float4 *>(arow1 + k + 16 * t);
-      x1[t][1] = *reinterpret_cast<const float4 *>(arow1 + k + 16 * t + 4);
-    }
+    for (int t = 0; t < 4; ++t) wf[t] = *reinterpret_cast<const bf16x8 *>(brow + k + 16 * t);
+    float4 x[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const float4 *>(asrc + k + 4 * i);
+    __syncthreads();  // the previous slab's fragments are read
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+      const float v[8] = {x[i].x, x[i].y, x[i].z, x[i].w, x[i + 1].x, x[i + 1].y, x[i + 1].z, x[i + 1].w};
       bf16x8 hi, lo;
-      split(x0[t][0], x0[t][1], hi, lo);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, wf[t], acc0, 0, 0, 0);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, wf[t], acc0, 0, 0, 0);
-      split(x1[t][0], x1[t][1], hi, lo);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, wf[t], acc1, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, wf[t], acc1, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 h2 = {(bf16)v[e], (bf16)v[e + 1]};
+        const bf16x2 l2 = {(bf16)(v[e] - (float)h2[0]), (bf16)(v[e + 1] - (float)h2[1])};
+        hi[e] = h2[0];
+        hi[e + 1] = h2[1];
+        lo[e] = l2[0];
+        lo[e + 1] = l2[1];
+      }
+      *reinterpret_cast<bf16x8 *>(&Ah[sr * kPitch + sk + 4 * i]) = hi;
+      *reinterpret_cast<bf16x8 *>(&Al[sr * kPitch + sk + 4 * i]) = lo;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = 16 * t + 8 * g;
+      const bf16x8 h0 = *reinterpret_cast<const bf16x8 *>(&Ah[l32 * kPitch + c]);
+      const bf16x8 o0 = *reinterpret_cast<const bf16x8 *>(&Al[l32 * kPitch + c]);
+      const bf16x8 h1 = *reinterpret_cast<const bf16x8 *>(&Ah[(32 + l32) * kPitch + c]);
+      const bf16x8 o1 = *reinterpret_cast<const bf16x8 *>(&Al[(32 + l32) * kPitch + c]);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, wf[t], acc0, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, wf[t], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, wf[t], acc1, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, wf[t], acc1, 0, 0, 0);
     }
   }
   // acc[v] is C[8*(v/4) + 4g + v%4 (+32 for acc1)][n]
