@@ -161,6 +161,18 @@ tsp_status tsp_zigzag_index(int64_t S, int32_t D, int32_t r, int32_t *pos, void 
 tsp_status tsp_zigzag_attn(const tsp_shape *shape, const void *q, const void *k, const void *v,
                            void *o, int32_t o_dtype, void *stream);
 
+/* Flags of tsp_zigzag_attn_ex. */
+enum { TSP_ATTN_Q_LOG2_SCALED = 1 };
+
+/* tsp_zigzag_attn with flags (0 gives tsp_zigzag_attn).
+ *  TSP_ATTN_Q_LOG2_SCALED: q holds q * scale * log2(e), as a caller that folds
+ *    the softmax scale into its Q projection would store it (the layer does
+ *    this); the result is the same attention, with one fewer multiply per
+ *    score. bf16 q and o only (else TSP_ERR_UNSUPPORTED). Unknown flag bits
+ *    are TSP_ERR_INVALID_ARG. */
+tsp_status tsp_zigzag_attn_ex(const tsp_shape *shape, const void *q, const void *k, const void *v,
+                              void *o, int32_t o_dtype, uint32_t flags, void *stream);
+
 /* The MLP ring on rank r (paragraph 2: shards circulate on a ring and every
  * rank sums their contributions itself, with no all-reduce):
  *   y = residual + sum over steps t = 0..D-1 of GELU(x W1_j^T) W2_j^T,

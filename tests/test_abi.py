@@ -124,6 +124,15 @@ def test_pointer_errors_enqueue_nothing():
     # fp32 inputs with a bf16 output
     with pytest.raises(tsp.TspError):
         tsp.tsp_zigzag_attn(s, FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), tsp.TSP_BF16, stream=0)
+    # flags: unknown bits; pre-scaled Q needs bf16 q and o
+    sb = _shape(dtype="bf16")
+    args = (FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30))
+    for shape, odt, flags, code in [(sb, tsp.TSP_BF16, 2, tsp.TSP_ERR_INVALID_ARG),
+                                    (s, tsp.TSP_F32, tsp.TSP_ATTN_Q_LOG2_SCALED, tsp.TSP_ERR_UNSUPPORTED),
+                                    (sb, tsp.TSP_F32, tsp.TSP_ATTN_Q_LOG2_SCALED, tsp.TSP_ERR_UNSUPPORTED)]:
+        with pytest.raises(tsp.TspError) as ei:
+            tsp.tsp_zigzag_attn_ex(shape, *args, odt, flags, stream=0)
+        assert ei.value.status == code
 
 
 def test_mlp_errors():

@@ -92,12 +92,14 @@ def test_attention_scale_zero_gives_prefix_mean(torch):
     assert_close(down(o), want, TOL_BF16, "prefix mean")
 
 
-@pytest.mark.parametrize("Dh", [64, 128])
-def test_attention_late_keys_far_above_first_tile(torch, Dh):
+@pytest.mark.parametrize("Dh,q_log2", [(64, False), (128, False), (64, True), (128, True)])
+def test_attention_late_keys_far_above_first_tile(torch, Dh, q_log2):
     """Keys 100, 611 and 1500 get scaled log2 scores of about 16, 24 and 24
-    against at most about 5 in any row's first key tile, so the running max
-    must move (the kernels raise it only when a score exceeds it by more than
-    8 in log2 units)."""
+    against at most about 5 in any row's first key tile, so the row's
+    reference max must move: the kernel raises it on a tile whose
+    probabilities (relative to it) sum past 2^16 in some lane. q_log2: Q is
+    passed pre-multiplied by scale * log2(e) (TSP_ATTN_Q_LOG2_SCALED, the
+    layer's form); the oracle then takes that Q divided by the factor."""
     S, D, H = 2048, 2, 2
     shape = synth.LayerShape(S=S, D=D, h=H * Dh, H=H, Dh=Dh, F=128, dtype="bf16")
     k, v = synth.remote_kv(shape, seed=13)
@@ -111,13 +113,22 @@ def test_attention_late_keys_far_above_first_tile(torch, Dh):
         qf = synth.bf16_to_f32(synth.normal((S // D, H, Dh), 13, synth.TID_Q, r, dtype="bf16"))
         qf = qf * 0.05 + base * np.sqrt(Dh)
         q = synth.f32_to_bf16(qf)
-        o = torch.empty((S // D, H, Dh), dtype=torch.float32, device="cuda")
         s = tsp.make_shape(S, D, r, H * Dh, H, Dh, 128, dtype="bf16")
-        log(f"attention with late large scores Dh={Dh} r={r}")
-        tsp.tsp_zigzag_attn(s, up(q, "bf16"), up(k, "bf16"), up(v, "bf16"), o)
+        log(f"attention with late large scores Dh={Dh} r={r} q_log2={q_log2}")
+        if q_log2:
+            cf = np.float32(s.scale) * np.float32(np.log2(np.e))
+            q = synth.f32_to_bf16(synth.bf16_to_f32(q) * cf)
+            q64 = f64(q, "bf16") / (float(s.scale) * np.log2(np.e))
+            o = torch.empty((S // D, H, Dh), dtype=torch.bfloat16, device="cuda")
+            tsp.tsp_zigzag_attn_ex(s, up(q, "bf16"), up(k, "bf16"), up(v, "bf16"), o, tsp.TSP_BF16,
+                                   tsp.TSP_ATTN_Q_LOG2_SCALED)
+        else:
+            q64 = f64(q, "bf16")
+            o = torch.empty((S // D, H, Dh), dtype=torch.float32, device="cuda")
+            tsp.tsp_zigzag_attn(s, up(q, "bf16"), up(k, "bf16"), up(v, "bf16"), o)
         _sync(torch)
-        want = oracle.causal_attention(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"),
-                                       oracle.zigzag_positions(S, D, r), shape.scale)
+        want = oracle.causal_attention(q64, f64(k, "bf16"), f64(v, "bf16"), oracle.zigzag_positions(S, D, r),
+                                       shape.scale)
         assert np.isfinite(down(o)).all()
         assert_close(down(o), want, TOL_BF16, "o")
 

@@ -17,9 +17,10 @@ import numpy as np
 
 __all__ = [
     "TspError", "TspShape", "TspLayerWeights", "lib", "make_shape", "workspace_size",
-    "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_mlp_ring", "tsp_layer_fwd",
-    "profile_enable", "profile_reset", "profile_read",
-    "TSP_F32", "TSP_BF16", "TSP_PHASE_KV", "TSP_PHASE_REST", "TSP_PHASE_ALL", "TSP_WS_MLP", "TSP_WS_LAYER",
+    "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_zigzag_attn_ex", "tsp_mlp_ring",
+    "tsp_layer_fwd", "profile_enable", "profile_reset", "profile_read",
+    "TSP_F32", "TSP_BF16", "TSP_ATTN_Q_LOG2_SCALED", "TSP_PHASE_KV", "TSP_PHASE_REST", "TSP_PHASE_ALL",
+    "TSP_WS_MLP", "TSP_WS_LAYER",
     "KERNEL_CLASSES", "EXPORTED_SYMBOLS",
 ]
 
@@ -29,14 +30,15 @@ TSP_OK, TSP_ERR_INVALID_ARG, TSP_ERR_UNSUPPORTED, TSP_ERR_WORKSPACE, TSP_ERR_HIP
 TSP_F32, TSP_BF16 = 0, 1
 TSP_PHASE_KV, TSP_PHASE_REST, TSP_PHASE_ALL = 1, 2, 3
 TSP_WS_MLP, TSP_WS_LAYER = 0, 1
+TSP_ATTN_Q_LOG2_SCALED = 1
 TSP_MAX_D = 64
 KERNEL_CLASSES = {"rmsnorm": 0, "qkv": 1, "attention": 2, "outproj": 3, "mlp_up": 4, "mlp_down": 5, "zigzag": 6,
                   "lead": 7}
 
 EXPORTED_SYMBOLS = [
     "tsp_status_string", "tsp_last_error", "tsp_abi_version", "tsp_workspace_size",
-    "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_mlp_ring", "tsp_layer_fwd",
-    "tsp_profile_enable", "tsp_profile_reset", "tsp_profile_read",
+    "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_zigzag_attn_ex", "tsp_mlp_ring",
+    "tsp_layer_fwd", "tsp_profile_enable", "tsp_profile_reset", "tsp_profile_read",
 ]
 
 
@@ -80,6 +82,7 @@ def lib() -> ctypes.CDLL:
     L.tsp_zigzag_index_host.argtypes = [i64, i32, i32, ctypes.POINTER(i32)]
     L.tsp_zigzag_index.argtypes = [i64, i32, i32, vp, vp]
     L.tsp_zigzag_attn.argtypes = [shp, vp, vp, vp, vp, i32, vp]
+    L.tsp_zigzag_attn_ex.argtypes = [shp, vp, vp, vp, vp, i32, ctypes.c_uint32, vp]
     L.tsp_mlp_ring.argtypes = [shp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, sz, vp]
     L.tsp_layer_fwd.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, ctypes.c_uint, vp, sz, vp]
     L.tsp_profile_enable.argtypes = [ctypes.c_int]
@@ -88,7 +91,7 @@ def lib() -> ctypes.CDLL:
     L.tsp_profile_reset.restype = None
     L.tsp_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     for name in ("tsp_workspace_size", "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn",
-                 "tsp_mlp_ring", "tsp_layer_fwd", "tsp_profile_read"):
+                 "tsp_zigzag_attn_ex", "tsp_mlp_ring", "tsp_layer_fwd", "tsp_profile_read"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -151,6 +154,11 @@ def tsp_zigzag_index(S: int, D: int, r: int, pos, stream=None) -> None:
 def tsp_zigzag_attn(shape: TspShape, q, k, v, o, o_dtype=TSP_F32, stream=None) -> None:
     _check(lib().tsp_zigzag_attn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(o), int(o_dtype),
                                  _stream(stream)))
+
+
+def tsp_zigzag_attn_ex(shape: TspShape, q, k, v, o, o_dtype=TSP_F32, flags=0, stream=None) -> None:
+    _check(lib().tsp_zigzag_attn_ex(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(o), int(o_dtype),
+                                    int(flags), _stream(stream)))
 
 
 def tsp_mlp_ring(shape: TspShape, x, w1, w2, residual, y, ws, ws_bytes=None, stream=None) -> None:

@@ -293,12 +293,21 @@ tsp_status tsp_zigzag_index(int64_t S, int32_t D, int32_t r, int32_t *pos, void 
 
 tsp_status tsp_zigzag_attn(const tsp_shape *s, const void *q, const void *k, const void *v, void *o,
                            int32_t o_dtype, void *stream_) {
+  return tsp_zigzag_attn_ex(s, q, k, v, o, o_dtype, 0u, stream_);
+}
+
+tsp_status tsp_zigzag_attn_ex(const tsp_shape *s, const void *q, const void *k, const void *v, void *o,
+                              int32_t o_dtype, uint32_t flags, void *stream_) {
   tsp_status st = check_attn_shape(s);
   if (st) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(o, "o")))
     return st;
   if (o_dtype != TSP_F32 && o_dtype != TSP_BF16) return fail(TSP_ERR_INVALID_ARG, "unknown o_dtype %d", o_dtype);
   if (s->dtype == TSP_F32 && o_dtype != TSP_F32) return fail(TSP_ERR_INVALID_ARG, "fp32 inputs need an fp32 output");
+  if (flags & ~(uint32_t)TSP_ATTN_Q_LOG2_SCALED) return fail(TSP_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  const bool q_log2 = (flags & TSP_ATTN_Q_LOG2_SCALED) != 0;
+  if (q_log2 && (s->dtype != TSP_BF16 || o_dtype != TSP_BF16))
+    return fail(TSP_ERR_UNSUPPORTED, "TSP_ATTN_Q_LOG2_SCALED needs bf16 q and o");
   const size_t e = elem_bytes(s->dtype), row = (size_t)s->H * s->Dh;
   const size_t N = (size_t)(s->S / s->D);
   const Range ro{o, N * row * elem_bytes(o_dtype), "o"};
@@ -308,7 +317,7 @@ tsp_status tsp_zigzag_attn(const tsp_shape *s, const void *q, const void *k, con
   hipStream_t stream = (hipStream_t)stream_;
   TSP_LAUNCH(TSP_K_ATTN,
              tsp::launch_attention(s->dtype, q, k, v, o, o_dtype, false, s->S, (int32_t)N, s->H, s->Dh, s->scale,
-                                   tsp::make_zigzag(s->S, s->D, s->r), false, stream),
+                                   tsp::make_zigzag(s->S, s->D, s->r), q_log2, stream),
              "attention");
   return ok();
 }
