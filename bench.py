@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -200,6 +201,7 @@ def main():
         def step():
             tsp.tsp_layer_fwd(shape, wd, xd, kf, vf, y, tsp.TSP_PHASE_ALL, ws)
         step_flops = flops["total"]
+        step_exps = sh.H * attn_pairs(sh.S, sh.D, r)
         workload = (f"tsp_layer_fwd: one 7B dense decoder layer (h=4096, 32x128 heads, FFN 16384, bf16) on rank {r} "
                     f"of D=8 at S=131072, 16384 local zigzag tokens")
     elif args.workload == "mlp":
@@ -211,6 +213,7 @@ def main():
         def step():
             tsp.tsp_mlp_ring(shape, xd, wd["w1"], wd["w2"], None, y, ws)
         step_flops = flops["mlp"]
+        step_exps = 0
         workload = "tsp_mlp_ring: 7B MLP ring, 16384x4096 bf16 local X, D=8 shards of 4096x2048"
     elif args.workload == "layers32":
         # 32 layers resident in HBM (82 GB of weights and K/V), each with its
@@ -247,6 +250,7 @@ def main():
                 tsp.tsp_layer_fwd(shape, wl, src, kl, vl, dst, tsp.TSP_PHASE_ALL, ws)
                 src = dst
         step_flops = n_layers * flops["total"]
+        step_exps = n_layers * sh.H * attn_pairs(sh.S, sh.D, r)
         N = N * n_layers  # value = layer-tokens/s, comparable with the one-layer figure
         workload = (f"32 x tsp_layer_fwd: 32-layer 7B dense forward (each layer h=4096, 32x128 heads, FFN 16384, "
                     f"bf16, own weights and remote K/V, all resident) on rank {r} of D=8 at S=131072, "
@@ -261,6 +265,7 @@ def main():
         def step():
             tsp.tsp_zigzag_attn(shape, qd, kf, vf, o, tsp.TSP_F32)
         step_flops = flops["attention"]
+        step_exps = sh.H * attn_pairs(sh.S, sh.D, r)
         workload = f"tsp_zigzag_attn: 32x128 heads, S=131072, 16384 zigzag queries of rank {r} of D=8"
     torch.cuda.synchronize()
     log(f"inputs resident in HBM ({time.perf_counter() - t_gen:.1f} s); warmup {args.warmup}")
@@ -298,6 +303,20 @@ def main():
             kernels[name] = {"ms_per_launch": ms / n, "launches_per_step": n / args.steps}
     log(f"timed: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
 
+    # second pass, outside the timed region above: the same steps, each
+    # bracketed by its own events, for the per-step minimum and median
+    per = []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        per.append((a, b))
+    torch.cuda.synchronize()
+    per_ms = [a.elapsed_time(b) for a, b in per]
+    ms_min, ms_median = min(per_ms), statistics.median(per_ms)
+    log(f"per step: min {ms_min:.3f} ms, median {ms_median:.3f} ms")
+
     tokens_per_s = N / (ms_step * 1e-3)
     # dominant kernel: attention (73% of the layer's algorithmic flops)
     roofline = None
@@ -327,6 +346,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_min": ms_min,
+        "ms_per_step_median": ms_median,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -337,6 +358,7 @@ def main():
                    "parallelism": "one rank of a D=8 folded TP+SP axis"},
         "pct_bf16_mfma_peak": 100.0 * step_flops / (ms_step * 1e-3) / PEAK_BF16,
         "algorithmic_tflop_per_step": step_flops / 1e12,
+        "softmax_exps_per_step": step_exps,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
