@@ -147,6 +147,82 @@ def blas_threads():
     return len(os.sched_getaffinity(0))
 
 
+SQ_PASSES = (
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU_TRANS_F32 "
+    "SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE",
+    "SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_ANY SQ_ACTIVE_INST_ANY SQ_BUSY_CU_CYCLES "
+    "GRBM_GUI_ACTIVE",
+)
+
+
+def summarize_sq(csvs):
+    """Per-kernel shader counters of the default layer step: fractions of the
+    kernel's cycles per SIMD (cycles = GRBM_GUI_ACTIVE / 8 XCDs, 1024 SIMDs),
+    instruction mixes per MFMA. One line per kernel, averaged over dispatches."""
+    import csv
+    per = {}  # (kernel, dispatch) -> {counter: value}
+    for path in csvs:
+        for row in csv.DictReader(open(path)):
+            key = (path, row["Kernel_Name"], row["Dispatch_Id"])
+            per.setdefault(key, {})[row["Counter_Name"]] = float(row["Counter_Value"])
+    kern = {}
+    for (_, name, _), c in per.items():
+        if "GRBM_GUI_ACTIVE" not in c or "copyBuffer" in name:
+            continue
+        simd = 1024.0 * c["GRBM_GUI_ACTIVE"] / 8.0
+        f = {}
+
+        def put(key, num, den=1.0, scale=1.0):
+            if num in c and (den == 1.0 or den in c):
+                f[key] = scale * c[num] / (simd if den == 1.0 else max(c[den], 1.0))
+
+        put("mfma_busy", "SQ_VALU_MFMA_BUSY_CYCLES")
+        put("valu_active", "SQ_ACTIVE_INST_VALU", scale=4.0)
+        put("mfma_valu_coexec", "SQ_VALU_MFMA_COEXEC_CYCLES")
+        put("lds_active", "SQ_ACTIVE_INST_LDS", scale=4.0)
+        put("lds_wait", "SQ_WAIT_INST_LDS")
+        if c.get("SQ_INSTS_MFMA", 0.0) > 0:
+            put("trans_per_mfma", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA")
+        put("bank_conflicts_per_lds_inst", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS")
+        for k, n in (("_mfma", "SQ_INSTS_MFMA"), ("_valu", "SQ_INSTS_VALU"), ("_salu", "SQ_INSTS_SALU"),
+                     ("_lds", "SQ_INSTS_LDS")):
+            if n in c:
+                f[k] = c[n]
+        kern.setdefault(name, []).append(f)
+    lines = ["# Shader counters of the default layer step (7B, rank 0 of D=8, S=131072), per kernel.",
+             "# Made by (one step, two passes, each within one pass's counter limits):"]
+    for i, ctrs in enumerate(SQ_PASSES):
+        lines.append(f"#   rocprofv3 --pmc {ctrs} -d <dir{i + 1}> -o run --output-format csv -- "
+                     "python bench.py --steps 1 --warmup 0 --cpu-rows 0")
+    lines += ["#   python bench.py --summarize-sq <dir1>/run_counter_collection.csv <dir2>/run_counter_collection.csv",
+              "# Fractions are of the kernel's cycles per SIMD (GRBM_GUI_ACTIVE / 8 XCDs, x 1024 SIMDs);",
+              "# SQ_ACTIVE_INST_* count 4-cycle units. Instruction ratios are per MFMA instruction.",
+              "kernel | mfma_busy | valu_active | coexec | lds_active | lds_wait | valu/mfma | salu/mfma | lds/mfma "
+              "| trans/mfma | bank_conflicts/lds"]
+    order = sorted(kern, key=lambda n: -len(kern[n]))
+    for name in order:
+        rows = kern[name]
+
+        def avg(k):
+            v = [r[k] for r in rows if k in r]
+            return sum(v) / len(v) if v else None
+
+        mf, va, sa, ld = avg("_mfma"), avg("_valu"), avg("_salu"), avg("_lds")
+        ratio = (lambda x: f"{x / mf:.2f}" if (x is not None and mf) else "-")
+
+        def fmt(k):
+            v = avg(k)
+            return "-" if v is None else f"{v:.3f}"
+
+        lines.append(f"{name[:80]} | {fmt('mfma_busy')} | {fmt('valu_active')} | {fmt('mfma_valu_coexec')} | "
+                     f"{fmt('lds_active')} | {fmt('lds_wait')} | {ratio(va)} | {ratio(sa)} | {ratio(ld)} | "
+                     f"{fmt('trans_per_mfma')} | {fmt('bank_conflicts_per_lds_inst')}")
+    out = os.path.join(ROOT, "profiles", "layer7b_sq_counters.txt")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,12 +234,17 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warmup, run one plain device-to-device copy of this many MiB (a known-size "
                          "reference for rocprofv3 HBM byte counters)")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="CSV",
+                    help="write profiles/layer7b_sq_counters.txt from rocprofv3 shader-counter csv files")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/attention_7b_traffic.txt from two rocprofv3 --pmc counter_collection.csv "
                          "files (FETCH_SIZE, WRITE_SIZE) of a run with --copy-mib, then exit")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, copy_mib=args.copy_mib or 1024)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq)
         return
     if args.gpus != 1:
         sys.exit(f"bench.py: only --gpus 1 is supported; this build measures one rank's share on one GPU "
