@@ -210,14 +210,20 @@ namespace tsp {
 void prof_begin(int k, hipStream_t s) {
   if (!g_prof.on) return;
   ProfRec r{g_prof.get(), nullptr};
-  if (r.a) hipEventRecord(r.a, s);
+  if (r.a && hipEventRecord(r.a, s) != hipSuccess) {  // not timed, the launch still runs
+    g_prof.pool.push_back(r.a);
+    r.a = nullptr;
+  }
   g_prof.open[k].push_back(r);
 }
 void prof_end(int k, hipStream_t s) {
   if (!g_prof.on || g_prof.open[k].empty()) return;
   ProfRec &r = g_prof.open[k].back();
   r.b = g_prof.get();
-  if (r.b) hipEventRecord(r.b, s);
+  if (r.b && hipEventRecord(r.b, s) != hipSuccess) {
+    g_prof.pool.push_back(r.b);
+    r.b = nullptr;
+  }
 }
 }  // namespace tsp
 

@@ -97,6 +97,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // read as a possible reader of this copy (it would then wait for all copies
 // in flight, from HBM, before each read); callers order every copy before
 // its readers themselves (vmcnt waits and block barriers).
+// M0 holds the LDS address of the copy. The compiler reserves M0 and notes
+// the clobber only as a warning, so these helpers set it on every use and are
+// used only in kernels with no other M0 user (no LDS-DMA builtins there).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_copy16(u32x4 rsrc, int voffset, int soffset, uint32_t lds_base) {
   asm volatile(
       "s_mov_b32 m0, %3\n\t"
@@ -119,6 +124,7 @@ __device__ __forceinline__ void lds_touch4(u32x4 rsrc, int voffset, int soffset,
       : "v"(voffset), "s"(rsrc), "s"(soffset), "s"(lds_base)
       : "memory", "m0");
 }
+#pragma clang diagnostic pop
 #endif  // __HIP_DEVICE_COMPILE__
 
 // Blocks are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).

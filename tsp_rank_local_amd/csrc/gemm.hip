@@ -216,8 +216,9 @@ constexpr int kTileBytes = kBM * kRowBytes;                     // one 256 x 64 
 constexpr int kGemmStageBytes = 2 * kTileBytes;                 // A tile + B tile
 constexpr size_t kGemmLds = (size_t)kGemmStages * kGemmStageBytes;  // 128 KB
 constexpr int kGemmWaves = kGemmThreads / 64;
-constexpr int kWinPerWave = kTileBytes / 1024 / kGemmWaves;     // 1 KB copy windows per wave, per tile
-constexpr int kGemmSlices = kBK / 16;                           // 16-wide K slices per step
+// 1 KB copy windows per wave, per tile; 16-wide K slices per step
+[[maybe_unused]] constexpr int kWinPerWave = kTileBytes / 1024 / kGemmWaves;
+[[maybe_unused]] constexpr int kGemmSlices = kBK / 16;
 
 // Byte offset of logical 16-byte chunk ch (0..7) of row r in a 128-byte-row
 // tile: the 16 rows that 16 lanes read with one logical chunk land in 16
