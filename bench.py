@@ -223,6 +223,65 @@ def summarize_sq(csvs):
     print("\n".join(lines))
 
 
+class ClockSampler:
+    """Mean shader (GFX) clock of the benchmark's GPU while the timed steps
+    run, sampled every few ms from the amdsmi metrics table on a background
+    thread. The device is matched to cuda:0 by PCI bus; anything unavailable
+    gives None."""
+
+    def __init__(self, torch, period_s=0.004):
+        import threading
+        self.period, self.samples, self.handle, self.smi = period_s, [], None, None
+        self.stop_ev = threading.Event()
+        self.thread = None
+        try:
+            import amdsmi
+            props = torch.cuda.get_device_properties(0)
+            amdsmi.amdsmi_init()
+            for h in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                dom, bus = bdf.split(":")[0], bdf.split(":")[1]
+                if int(bus, 16) == props.pci_bus_id and int(dom, 16) == props.pci_domain_id:
+                    self.handle, self.smi = h, amdsmi
+                    break
+        except Exception:
+            self.handle = None
+
+    @staticmethod
+    def _valid(v):
+        return isinstance(v, (int, float)) and 0 < v < 10000
+
+    def _run(self):
+        # the metrics table's current clock of each XCD (the effective clock
+        # under power limits), else its single current or average clock
+        while not self.stop_ev.is_set():
+            try:
+                m = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
+                per_xcd = [v for v in (m.get("current_gfxclks") or []) if self._valid(v)]
+                if per_xcd:
+                    self.samples.append(statistics.mean(per_xcd))
+                elif self._valid(m.get("current_gfxclk")):
+                    self.samples.append(m["current_gfxclk"])
+                elif self._valid(m.get("average_gfxclk_frequency")):
+                    self.samples.append(m["average_gfxclk_frequency"])
+            except Exception:
+                pass
+            self.stop_ev.wait(self.period)
+
+    def start(self):
+        if self.handle is not None:
+            import threading
+            self.thread = threading.Thread(target=self._run, daemon=True)
+            self.thread.start()
+
+    def stop(self):
+        if self.thread is None:
+            return None
+        self.stop_ev.set()
+        self.thread.join()
+        return round(statistics.mean(self.samples), 1) if self.samples else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -366,8 +425,10 @@ def main():
 
     tsp.profile_reset()
     tsp.profile_enable(True)
+    clock = ClockSampler(torch)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    clock.start()
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
@@ -375,6 +436,7 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sclk_mhz = clock.stop()
     tsp.profile_enable(False)
     ms_step = ev0.elapsed_time(ev1) / args.steps
     kernels = {}
@@ -438,6 +500,11 @@ def main():
                    "F": sh.F, "local_tokens": sh.N, "layers": 32 if args.workload == "layers32" else 1,
                    "parallelism": "one rank of a D=8 folded TP+SP axis"},
         "pct_bf16_mfma_peak": 100.0 * step_flops / (ms_step * 1e-3) / PEAK_BF16,
+        # the same against the dense peak scaled to the mean shader clock seen
+        # during the timed steps (the published peak assumes 2.4 GHz)
+        "sclk_mhz_mean": sclk_mhz,
+        "pct_bf16_mfma_peak_at_sclk": (100.0 * step_flops / (ms_step * 1e-3) / (PEAK_BF16 * sclk_mhz / 2400.0)
+                                       if sclk_mhz else None),
         "algorithmic_tflop_per_step": step_flops / 1e12,
         "softmax_exps_per_step": step_exps,
         "roofline": roofline,
@@ -446,6 +513,17 @@ def main():
         "gpu": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)
+
+
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(sh, r, x, w, k_rem, v_rem, m):
@@ -468,7 +546,7 @@ def cpu_baseline(sh, r, x, w, k_rem, v_rem, m):
     oracle.layer_rows(x[rows], pos, w64, k32, v32, sh.H, sh.Dh, sh.eps, sh.scale)
     t = time.perf_counter() - t0
     log(f"cpu baseline: {t:.1f} s")
-    return {"value": m / t, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+    return {"value": m / t, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{m} evenly strided local rows of the same layer (per-row Q/K/V projection, causal attention "
                       f"over the gathered K/V prefix, output projection, MLP) in numpy float64; {t:.1f} s; "
                       f"BLAS threads as cores, exp/erf single-threaded"}
