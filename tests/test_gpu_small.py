@@ -283,7 +283,13 @@ def test_tiny_layer_rank_mode_given_remote_kv(torch):
         assert_close(down(y) - x, want["y"] - x, 10 * TOL_F32, "y - x (both branches)")
 
 
-@pytest.mark.parametrize("S,D,H,Dh,F", [(2048, 4, 4, 128, 2048), (2400, 4, 4, 128, 2048), (1024, 2, 4, 64, 1024)])
+@pytest.mark.parametrize("S,D,H,Dh,F", [
+    (2048, 4, 4, 128, 2048),
+    (2400, 4, 4, 128, 2048),   # N = 600: ragged row tiles
+    (1024, 2, 4, 64, 1024),
+    (96, 3, 6, 64, 576),       # C = 16: rank 0 recomputes 16 leading rows (one 32-row MFMA block)
+    (256, 1, 4, 64, 512),      # D = 1: one shard, the plain layer
+])
 def test_bf16_layer_vs_oracle(torch, S, D, H, Dh, F):
     h = H * Dh
     shape = synth.LayerShape(S=S, D=D, h=h, H=H, Dh=Dh, F=F, dtype="bf16")
