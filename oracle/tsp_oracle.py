@@ -35,6 +35,11 @@ Readings where the pages are silent (each is restated where it is used):
      holds hidden units j*F/D..(j+1)*F/D-1 (rows of W1, columns of W2).
   R6 pre-RMSNorm residual block: h1 = x + Attn(RMSNorm(x)),
      y = h1 + MLP(RMSNorm(h1)); eps = 1e-5; no biases.
+  R7 rotary position embedding (an optional variant; the pages' model has
+     none): with rope_base > 0, Q and K of each token are rotated by its
+     global position p before attention. Feature d and feature d + Dh/2 of a
+     head form a pair (the rotate-half convention); pair i turns by the
+     angle p * rope_base^(-2i/Dh).
 """
 from __future__ import annotations
 
@@ -47,6 +52,7 @@ __all__ = [
     "rms_norm",
     "gelu",
     "causal_attention",
+    "rope",
     "unshard_attention_weights",
     "unshard_mlp_weights",
     "mlp",
@@ -140,6 +146,24 @@ def causal_attention(q, k, v, q_pos, scale: float, row_block: int = 256) -> np.n
     return out
 
 
+def rope(x, pos, base: float) -> np.ndarray:
+    """Rotary position embedding of x [n, H, Dh] at global positions pos [n]
+    (reading R7). base <= 0 leaves x unchanged.
+
+    Pair i (0 <= i < Dh/2) is features (i, i + Dh/2); it turns by the angle
+    pos * base^(-2i/Dh): (a, b) -> (a cos - b sin, b cos + a sin).
+    """
+    x = _f64(x)
+    if base <= 0:
+        return x
+    half = x.shape[-1] // 2
+    inv_freq = float(base) ** (-2.0 * np.arange(half, dtype=np.float64) / x.shape[-1])
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * inv_freq[None, :]  # [n, half]
+    cos, sin = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * cos - b * sin, b * cos + a * sin], axis=-1)
+
+
 # --------------------------------------------------------------------------
 # Shards -> unsharded matrices
 # --------------------------------------------------------------------------
@@ -186,20 +210,21 @@ def mlp_shard(x, w1_j, w2_j) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Whole layer
 # --------------------------------------------------------------------------
-def layer_full(x, w: dict, H: int, Dh: int, eps: float, scale: float) -> dict:
+def layer_full(x, w: dict, H: int, Dh: int, eps: float, scale: float, rope_base: float = 0.0) -> dict:
     """Unsharded pre-norm decoder layer over the whole sequence (reading R6).
 
     x: [S, h] in global order. w: the shard lists wqkv, wo, w1, w2 and gains
     g_attn, g_mlp. TSP rearranges this computation over ranks and shards but
     reaches the same values ([P2] paragraphs 1-2), so this is what every rank
-    must reproduce for its own rows. Returns y and the intermediates h1, k, v.
+    must reproduce for its own rows. rope_base > 0 rotates Q and K (reading
+    R7). Returns y and the intermediates h1, q, k, v, o.
     """
     x = _f64(x)
     S = x.shape[0]
     wq, wk, wv, w_o = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh)
     a = rms_norm(x, w["g_attn"], eps)
-    q = (a @ wq.T).reshape(S, H, Dh)
-    k = (a @ wk.T).reshape(S, H, Dh)
+    q = rope((a @ wq.T).reshape(S, H, Dh), np.arange(S), rope_base)
+    k = rope((a @ wk.T).reshape(S, H, Dh), np.arange(S), rope_base)
     v = (a @ wv.T).reshape(S, H, Dh)
     o = causal_attention(q, k, v, np.arange(S), scale)
     h1 = x + o.reshape(S, H * Dh) @ w_o.T
@@ -208,19 +233,22 @@ def layer_full(x, w: dict, H: int, Dh: int, eps: float, scale: float) -> dict:
     return {"y": y, "h1": h1, "q": q, "k": k, "v": v, "o": o}
 
 
-def layer_rows(x_rows, pos_rows, w: dict, k_all, v_all, H: int, Dh: int, eps: float, scale: float) -> dict:
+def layer_rows(x_rows, pos_rows, w: dict, k_all, v_all, H: int, Dh: int, eps: float, scale: float,
+               rope_base: float = 0.0) -> dict:
     """Layer output for given token rows once the full K/V are gathered (R6).
 
     x_rows: [m, h] tokens, pos_rows: [m] their global positions, k_all, v_all:
     [S, H, Dh] the complete gathered K/V (including these tokens' own rows).
     Every row is independent of the others here: RMSNorm, its query, its
-    causal attention, the output projection, RMSNorm and the MLP.
+    causal attention, the output projection, RMSNorm and the MLP. With
+    rope_base > 0 the query is rotated at its position (k_all holds rotated
+    keys, reading R7).
     """
     x_rows = _f64(x_rows)
     m = x_rows.shape[0]
     wq, _, _, w_o = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh)
     a = rms_norm(x_rows, w["g_attn"], eps)
-    q = (a @ wq.T).reshape(m, H, Dh)
+    q = rope((a @ wq.T).reshape(m, H, Dh), pos_rows, rope_base)
     o = causal_attention(q, k_all, v_all, pos_rows, scale)
     h1 = x_rows + o.reshape(m, H * Dh) @ w_o.T
     mm = rms_norm(h1, w["g_mlp"], eps)
@@ -228,17 +256,21 @@ def layer_rows(x_rows, pos_rows, w: dict, k_all, v_all, H: int, Dh: int, eps: fl
     return {"y": y, "h1": h1}
 
 
-def local_kv(x_local, w: dict, H: int, Dh: int, eps: float):
-    """K and V [n, H, Dh] of a rank's own tokens (R2, R6)."""
+def local_kv(x_local, w: dict, H: int, Dh: int, eps: float, pos=None, rope_base: float = 0.0):
+    """K and V [n, H, Dh] of a rank's own tokens (R2, R6); with rope_base > 0
+    K is rotated at the tokens' global positions pos (R7)."""
     x_local = _f64(x_local)
     n = x_local.shape[0]
     _, wk, wv, _ = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh)
     a = rms_norm(x_local, w["g_attn"], eps)
-    return (a @ wk.T).reshape(n, H, Dh), (a @ wv.T).reshape(n, H, Dh)
+    k = (a @ wk.T).reshape(n, H, Dh)
+    if rope_base > 0:
+        k = rope(k, pos, rope_base)
+    return k, (a @ wv.T).reshape(n, H, Dh)
 
 
 def layer_rank(x_local, w: dict, k_full, v_full, S: int, D: int, r: int,
-               H: int, Dh: int, eps: float, scale: float, rows=None) -> dict:
+               H: int, Dh: int, eps: float, scale: float, rows=None, rope_base: float = 0.0) -> dict:
     """Rank r's layer output for its S/D local tokens (reading R6).
 
     x_local: [S/D, h] rank r's tokens in local zigzag order (R1). k_full,
@@ -246,7 +278,9 @@ def layer_rank(x_local, w: dict, k_full, v_full, S: int, D: int, r: int,
     rows at rank r's own positions are replaced by the K/V this rank computes
     from x_local, the rest are used as given. rows: optional subset of local
     rows whose output is wanted (all local rows still produce K/V, since any
-    later query may attend to them). Returns y [len(rows), h] and h1.
+    later query may attend to them). rope_base > 0 rotates Q and K (R7; the
+    given remote K rows are taken as already rotated). Returns y [len(rows),
+    h] and h1.
     """
     x_local = _f64(x_local)
     n = x_local.shape[0]
@@ -254,11 +288,11 @@ def layer_rank(x_local, w: dict, k_full, v_full, S: int, D: int, r: int,
     if n != pos.shape[0]:
         raise ValueError("x_local must hold S/D rows")
     rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
-    k_loc, v_loc = local_kv(x_local, w, H, Dh, eps)
+    k_loc, v_loc = local_kv(x_local, w, H, Dh, eps, pos, rope_base)
     k_all = np.array(k_full, dtype=np.float64, copy=True)
     v_all = np.array(v_full, dtype=np.float64, copy=True)
     k_all[pos] = k_loc
     v_all[pos] = v_loc
-    out = layer_rows(x_local[rows], pos[rows], w, k_all, v_all, H, Dh, eps, scale)
+    out = layer_rows(x_local[rows], pos[rows], w, k_all, v_all, H, Dh, eps, scale, rope_base)
     out["pos"] = pos[rows]
     return out

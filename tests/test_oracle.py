@@ -194,12 +194,28 @@ def test_mlp_vs_torch_and_shard_sum():
         assert np.allclose(acc, got, atol=1e-13)
 
 
-def _torch_layer(x, wq, wk, wv, wo, W1, W2, g1, g2, H, Dh, eps, scale):
+def _torch_rope(t, base):
+    """Rotary embedding written as complex multiplication: pair i of features
+    (i, i + Dh/2) is the complex number a + ib, multiplied by
+    exp(i * pos * base^(-2i/Dh)). t: [H, S, Dh], positions 0..S-1."""
+    H, S, Dh = t.shape
+    half = Dh // 2
+    z = torch.complex(t[..., :half], t[..., half:])
+    freq = base ** (-torch.arange(0, Dh, 2, dtype=torch.float64) / Dh)
+    rot = torch.polar(torch.ones(S, half, dtype=torch.float64), torch.arange(S, dtype=torch.float64)[:, None] * freq)
+    zr = z * rot[None]
+    return torch.cat([zr.real, zr.imag], dim=-1)
+
+
+def _torch_layer(x, wq, wk, wv, wo, W1, W2, g1, g2, H, Dh, eps, scale, rope_base=0.0):
     tx = torch.from_numpy(x)
     S, h = x.shape
     a = F.rms_norm(tx, (h,), torch.from_numpy(g1), eps=eps)
     heads = lambda m: F.linear(a, torch.from_numpy(m)).reshape(S, H, Dh).permute(1, 0, 2).contiguous()  # noqa: E731
-    o = F.scaled_dot_product_attention(heads(wq), heads(wk), heads(wv), is_causal=True, scale=scale)
+    q, k = heads(wq), heads(wk)
+    if rope_base > 0:
+        q, k = _torch_rope(q, rope_base), _torch_rope(k, rope_base)
+    o = F.scaled_dot_product_attention(q, k, heads(wv), is_causal=True, scale=scale)
     h1 = tx + F.linear(o.permute(1, 0, 2).reshape(S, h), torch.from_numpy(wo))
     m = F.rms_norm(h1, (h,), torch.from_numpy(g2), eps=eps)
     return (h1 + F.linear(F.gelu(F.linear(m, torch.from_numpy(W1))), torch.from_numpy(W2))).numpy()
@@ -256,6 +272,58 @@ def test_layer_rank_d1_is_plain_layer():
     assert np.allclose(out["y"], full["y"], atol=1e-12)
 
 
+# ---------------------------------------------------------------- rotary embedding (R7)
+def test_rope_closed_forms():
+    # one pair (Dh = 2): the angle is the position itself
+    x = np.array([[[1.0, 0.0]], [[1.0, 0.0]], [[0.0, 2.0]]])
+    got = oracle.rope(x, np.array([0, 1, 3]), 10000.0)
+    want = np.array([[[1.0, 0.0]], [[math.cos(1), math.sin(1)]], [[-2 * math.sin(3), 2 * math.cos(3)]]])
+    assert np.allclose(got, want, atol=1e-15)
+    # Dh = 4, base 100: pair 1 turns at 1/10 of the position
+    x = np.array([[[1.0, 0.0, 0.0, 0.0], [0.0, 1.0, 0.0, 0.0]]])
+    got = oracle.rope(x, np.array([5]), 100.0)
+    assert np.allclose(got[0, 0], [math.cos(5), 0.0, math.sin(5), 0.0], atol=1e-15)
+    assert np.allclose(got[0, 1], [0.0, math.cos(0.5), 0.0, math.sin(0.5)], atol=1e-15)
+    # off, and position 0, leave x unchanged
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((3, 2, 8))
+    assert np.array_equal(oracle.rope(x, np.arange(3), 0.0), x)
+    assert np.allclose(oracle.rope(x, np.zeros(3), 500.0), x, atol=0)
+
+
+def test_rope_invariants():
+    rng = np.random.default_rng(22)
+    Dh, base = 16, 10000.0
+    q, k = rng.standard_normal((2, 1, 1, Dh))
+    # every pair keeps its length
+    pos = np.array([12345])
+    qr = oracle.rope(q, pos, base)[0, 0]
+    assert np.allclose(qr[:8] ** 2 + qr[8:] ** 2, q[0, 0, :8] ** 2 + q[0, 0, 8:] ** 2, atol=1e-12)
+    # scores depend on the position difference only
+    for m, n, t in [(7, 3, 100), (0, 0, 131071), (50, 49, 5)]:
+        a = np.dot(oracle.rope(q, [m], base).ravel(), oracle.rope(k, [n], base).ravel())
+        b = np.dot(oracle.rope(q, [m + t], base).ravel(), oracle.rope(k, [n + t], base).ravel())
+        assert abs(a - b) < 1e-10
+
+
+def test_layer_with_rope_vs_torch_and_sharded():
+    H, Dh, eps, base = 4, 8, 1e-5, 50.0
+    scale = 1 / math.sqrt(Dh)
+    S, D = 64, 4
+    x, w, m = _tiny_layer(23, S=S, D=D, H=H, Dh=Dh)
+    full = oracle.layer_full(x, w, H, Dh, eps, scale, rope_base=base)
+    ref = _torch_layer(x, m["wq"], m["wk"], m["wv"], m["wo"], m["W1"], m["W2"], m["g1"], m["g2"], H, Dh, eps, scale,
+                       rope_base=base)
+    assert np.allclose(full["y"], ref, atol=1e-12)
+    # the rank view reproduces its rows; remote K rows are the rotated ones
+    for r in range(D):
+        pos = oracle.zigzag_positions(S, D, r)
+        kr, vr = full["k"].copy(), full["v"].copy()
+        kr[pos], vr[pos] = 1e3, -1e3
+        out = oracle.layer_rank(x[pos], w, kr, vr, S, D, r, H, Dh, eps, scale, rope_base=base)
+        assert np.allclose(out["y"], full["y"][pos], atol=1e-12)
+
+
 # ---------------------------------------------------------------- planted mistakes
 def test_planted_mistakes_are_caught(monkeypatch):
     """Each pin above fails when a plausible slip is planted in the oracle."""
@@ -283,6 +351,18 @@ def test_planted_mistakes_are_caught(monkeypatch):
     w_bad["wqkv"] = [np.concatenate([s[:hd], s[2 * hd:], s[hd:2 * hd]]) for s in w["wqkv"]]
     ref = _torch_layer(x, m["wq"], m["wk"], m["wv"], m["wo"], m["W1"], m["W2"], m["g1"], m["g2"], H2, Dh2, eps, 1 / math.sqrt(Dh2))
     assert not np.allclose(oracle.layer_full(x, w_bad, H2, Dh2, eps, 1 / math.sqrt(Dh2))["y"], ref, atol=1e-6)
+    # rotary slips: interleaved pairs (2i, 2i+1), or the opposite turn, miss
+    # the complex-number form
+    t = rng.standard_normal((2, 5, 8))
+    want = _torch_rope(torch.from_numpy(t), 30.0).numpy()
+    x5 = t.transpose(1, 0, 2)  # [S, H, Dh]
+    interleaved = np.empty_like(x5)
+    perm = np.concatenate([np.arange(0, 8, 2), np.arange(1, 8, 2)])
+    interleaved[..., perm] = oracle.rope(x5[..., perm], np.arange(5), 30.0)
+    assert not np.allclose(interleaved.transpose(1, 0, 2), want, atol=1e-6)
+    flipped = oracle.rope(x5, -np.arange(5), 30.0)
+    assert not np.allclose(flipped.transpose(1, 0, 2), want, atol=1e-6)
+    assert np.allclose(oracle.rope(x5, np.arange(5), 30.0).transpose(1, 0, 2), want, atol=1e-12)
 
 
 # ---------------------------------------------------------------- synth
