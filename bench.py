@@ -232,6 +232,7 @@ class ClockSampler:
     def __init__(self, torch, period_s=0.004):
         import threading
         self.period, self.samples, self.handle, self.smi = period_s, [], None, None
+        self.sources = set()  # metrics fields the samples came from
         self.stop_ev = threading.Event()
         self.thread = None
         try:
@@ -260,10 +261,13 @@ class ClockSampler:
                 per_xcd = [v for v in (m.get("current_gfxclks") or []) if self._valid(v)]
                 if per_xcd:
                     self.samples.append(statistics.mean(per_xcd))
+                    self.sources.add("current_gfxclks")
                 elif self._valid(m.get("current_gfxclk")):
                     self.samples.append(m["current_gfxclk"])
+                    self.sources.add("current_gfxclk")
                 elif self._valid(m.get("average_gfxclk_frequency")):
                     self.samples.append(m["average_gfxclk_frequency"])
+                    self.sources.add("average_gfxclk_frequency")
             except Exception:
                 pass
             self.stop_ev.wait(self.period)
@@ -289,6 +293,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", choices=["layer", "mlp", "attn", "layers32"], default="layer")
     ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--rope-base", type=float, default=0.0,
+                    help="rotary embedding base for the layer workloads (0 = none, the pages' model)")
     ap.add_argument("--cpu-rows", type=int, default=384, help="rows in the CPU oracle sample (0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warmup, run one plain device-to-device copy of this many MiB (a known-size "
@@ -322,7 +328,8 @@ def main():
     seed = 4
     t_gen = time.perf_counter()
     log(f"generating inputs: S={sh.S} D={sh.D} r={r} h={sh.h} H={sh.H} Dh={sh.Dh} F={sh.F}")
-    shape = tsp.make_shape(sh.S, sh.D, r, sh.h, sh.H, sh.Dh, sh.F, eps=sh.eps, dtype="bf16")
+    shape = tsp.make_shape(sh.S, sh.D, r, sh.h, sh.H, sh.Dh, sh.F, eps=sh.eps, dtype="bf16",
+                           rope_base=args.rope_base)
     stream = torch.cuda.current_stream()
     flops = layer_flops(sh, r)
 
@@ -479,7 +486,7 @@ def main():
 
     cpu = None
     if args.cpu_rows > 0 and args.workload == "layer":
-        cpu = cpu_baseline(sh, r, x, w, k_rem, v_rem, args.cpu_rows)
+        cpu = cpu_baseline(sh, r, x, w, k_rem, v_rem, args.cpu_rows, args.rope_base)
 
     out = {
         "metric": METRIC,
@@ -498,11 +505,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload, "S": sh.S, "D": sh.D, "r": r, "h": sh.h, "H": sh.H, "Dh": sh.Dh,
                    "F": sh.F, "local_tokens": sh.N, "layers": 32 if args.workload == "layers32" else 1,
-                   "parallelism": "one rank of a D=8 folded TP+SP axis"},
+                   "parallelism": "one rank of a D=8 folded TP+SP axis", "rope_base": args.rope_base},
         "pct_bf16_mfma_peak": 100.0 * step_flops / (ms_step * 1e-3) / PEAK_BF16,
         # the same against the dense peak scaled to the mean shader clock seen
         # during the timed steps (the published peak assumes 2.4 GHz)
         "sclk_mhz_mean": sclk_mhz,
+        "sclk_source": ("amdsmi gpu metrics: " + ", ".join(sorted(clock.sources))) if sclk_mhz else None,
+        "sclk_samples": len(clock.samples),
         "pct_bf16_mfma_peak_at_sclk": (100.0 * step_flops / (ms_step * 1e-3) / (PEAK_BF16 * sclk_mhz / 2400.0)
                                        if sclk_mhz else None),
         "algorithmic_tflop_per_step": step_flops / 1e12,
@@ -526,7 +535,7 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(sh, r, x, w, k_rem, v_rem, m):
+def cpu_baseline(sh, r, x, w, k_rem, v_rem, m, rope_base=0.0):
     """Time the fp64 oracle on m evenly strided local rows of the same layer:
     each row's RMSNorm, Q/K/V projection, causal attention over its prefix of
     the gathered K/V, output projection, RMSNorm and MLP. The rate scales
@@ -542,8 +551,8 @@ def cpu_baseline(sh, r, x, w, k_rem, v_rem, m):
     rows = np.linspace(0, sh.N - 1, m).round().astype(np.int64)
     pos = oracle.zigzag_positions(sh.S, sh.D, r)[rows]
     t0 = time.perf_counter()
-    oracle.local_kv(x[rows], w64, sh.H, sh.Dh, sh.eps)
-    oracle.layer_rows(x[rows], pos, w64, k32, v32, sh.H, sh.Dh, sh.eps, sh.scale)
+    oracle.local_kv(x[rows], w64, sh.H, sh.Dh, sh.eps, pos, rope_base)
+    oracle.layer_rows(x[rows], pos, w64, k32, v32, sh.H, sh.Dh, sh.eps, sh.scale, rope_base)
     t = time.perf_counter() - t0
     log(f"cpu baseline: {t:.1f} s")
     return {"value": m / t, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle", "cpu_model": cpu_model(),

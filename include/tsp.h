@@ -80,6 +80,12 @@ typedef enum { TSP_F32 = 0, TSP_BF16 = 1 } tsp_dtype;
  *  eps   RMSNorm epsilon (>= 0)
  *  scale softmax scale applied to q.k (finite, >= 0; usually 1/sqrt(Dh))
  *  dtype tsp_dtype of weights and activations (see conventions)
+ *  rope_base rotary position embedding of Q and K in tsp_layer_fwd (an
+ *        optional variant; the pages' model has none): 0 = none; > 0: within
+ *        each head, features i and i + Dh/2 form pair i, which turns by the
+ *        angle pos * rope_base^(-2i/Dh), pos = the token's global position.
+ *        bf16 layers need h/D to be a multiple of 128 for it (else
+ *        TSP_ERR_UNSUPPORTED). tsp_zigzag_attn takes Q and K as given.
  * Local token count N = S/D. Widths used as GEMM dimensions (h, F/D and
  * 3h/D, h/D) must be multiples of 64. */
 typedef struct {
@@ -87,6 +93,7 @@ typedef struct {
   int32_t D, r, h, H, Dh, F;
   float eps, scale;
   int32_t dtype;
+  float rope_base;
 } tsp_shape;
 
 #define TSP_MAX_D 64
@@ -189,7 +196,8 @@ tsp_status tsp_mlp_ring(const tsp_shape *shape, const void *x, const void *const
  *  x: [S/D][h] fp32, local rows in zigzag order.
  *  k_full, v_full: [S][H][Dh] (dtype). The rows at rank r's own positions are
  *    written by PHASE_KV; every other row must hold what the all-gather would
- *    deliver (the other ranks' K/V) before PHASE_REST runs.
+ *    deliver (the other ranks' K/V, K already rotated when rope_base > 0)
+ *    before PHASE_REST runs.
  *  y: [S/D][h] fp32 output, fully written by PHASE_REST.
  *  phases: TSP_PHASE_KV, TSP_PHASE_REST or TSP_PHASE_ALL; PHASE_REST must use
  *    the same ws as the PHASE_KV call before it.

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert declared == sorted(tsp.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.tsp_abi_version() == 1
+    assert L.tsp_abi_version() == 2
 
 
 def test_status_strings():
@@ -99,6 +99,9 @@ def test_workspace_sizes():
     (dict(dtype=7), tsp.TSP_ERR_INVALID_ARG),
     (dict(eps=-1.0), tsp.TSP_ERR_INVALID_ARG),
     (dict(scale=float("nan")), tsp.TSP_ERR_INVALID_ARG),
+    (dict(rope_base=-1.0), tsp.TSP_ERR_INVALID_ARG),
+    (dict(rope_base=float("inf")), tsp.TSP_ERR_INVALID_ARG),
+    (dict(rope_base=1e4, dtype="bf16"), tsp.TSP_ERR_UNSUPPORTED),  # h/D = 64: rotation needs whole 128-column heads
 ])
 def test_shape_errors(kw, code):
     with pytest.raises(tsp.TspError) as ei:

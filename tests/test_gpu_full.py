@@ -96,19 +96,21 @@ def test_zigzag_attention_7b(torch, r):
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("r", [0, 7])
-def test_layer_7b(torch, r):
-    """One full layer, ranks 0 (the benchmark's) and 7, the benchmark's inputs (seed 4)."""
+@pytest.mark.parametrize("r,rope", [(0, 0.0), (7, 0.0), (0, 10000.0)])
+def test_layer_7b(torch, r, rope):
+    """One full layer, ranks 0 (the benchmark's) and 7, the benchmark's inputs
+    (seed 4); and rank 0 with rotary embedding (base 1e4), remote K rows taken
+    as already rotated."""
     N = SH.N
     w = synth.layer_weights(SH, seed=4)
     x = synth.activations(N, SH.h, seed=4)
     k_rem, v_rem = synth.remote_kv(SH, seed=4)
     wd = {k: ([up(a, "bf16") for a in v] if isinstance(v, list) else up(v, "bf16")) for k, v in w.items()}
     kf, vf = up(k_rem, "bf16"), up(v_rem, "bf16")
-    s = _shape(r)
+    s = tsp.make_shape(SH.S, SH.D, r, SH.h, SH.H, SH.Dh, SH.F, eps=SH.eps, dtype="bf16", rope_base=rope)
     ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
     y = torch.full((N, SH.h), float("nan"), dtype=torch.float32, device="cuda")
-    log(f"layer 7B r={r}")
+    log(f"layer 7B r={r} rope={rope}")
     tsp.tsp_layer_fwd(s, wd, up(x, "f32"), kf, vf, y, tsp.TSP_PHASE_ALL, ws)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(y).all())
@@ -116,7 +118,7 @@ def test_layer_7b(torch, r):
     rows = np.concatenate([np.arange(16), np.linspace(16, N - 1, 80).round().astype(np.int64)])
     pos = oracle.zigzag_positions(SH.S, SH.D, r)
     # the K/V rows this rank wrote into the gathered buffers
-    k_loc, v_loc = oracle.local_kv(x[rows], w64, SH.H, SH.Dh, SH.eps)
+    k_loc, v_loc = oracle.local_kv(x[rows], w64, SH.H, SH.Dh, SH.eps, pos[rows], rope)
     idx = torch.from_numpy(pos[rows]).cuda()
     assert_close(down(kf[idx]), k_loc, TOL_BF16, "local K rows")
     assert_close(down(vf[idx]), v_loc, TOL_BF16, "local V rows")
@@ -126,7 +128,7 @@ def test_layer_7b(torch, r):
     assert np.array_equal(kr, k_rem.view(np.int16)[remote.numpy()])
     del kf, vf, kr
     want = oracle.layer_rank(x, w64, synth.as_f32(k_rem, "bf16"), synth.as_f32(v_rem, "bf16"), SH.S, SH.D, r,
-                             SH.H, SH.Dh, SH.eps, SH.scale, rows=rows)
+                             SH.H, SH.Dh, SH.eps, SH.scale, rows=rows, rope_base=rope)
     got = down(y[torch.from_numpy(rows).cuda()])
     assert_close(got, want["y"], TOL_BF16, "y rows")
     if r == 0:

@@ -227,22 +227,23 @@ def _w64(w, dtype):
     return {k: ([f64(a, dtype) for a in w[k]] if isinstance(w[k], list) else f64(w[k], dtype)) for k in w}
 
 
-@pytest.mark.parametrize("gain", ["ones", "random"])
-def test_tiny_layer_every_rank_vs_unsharded(torch, gain):
+@pytest.mark.parametrize("gain,rope", [("ones", 0.0), ("random", 0.0), ("random", 10000.0)])
+def test_tiny_layer_every_rank_vs_unsharded(torch, gain, rope):
     """Tiny fp32 layer (S=1024, D=4, h=256, 4 heads of 64, F=1024): the D ranks
     each write their K/V rows into one shared buffer (the all-gather), then each
-    runs the rest; every rank's rows must equal the unsharded layer's."""
+    runs the rest; every rank's rows must equal the unsharded layer's. rope:
+    rotary base (0 = none)."""
     shape = synth.TINY_FP32
     S, D, h, H, Dh, F = shape.S, shape.D, shape.h, shape.H, shape.Dh, shape.F
     w = synth.layer_weights(shape, seed=1, gain=gain)
     x_full = synth.activations(S, h, seed=1)
-    full = oracle.layer_full(x_full, _w64(w, "f32"), H, Dh, shape.eps, shape.scale)
+    full = oracle.layer_full(x_full, _w64(w, "f32"), H, Dh, shape.eps, shape.scale, rope_base=rope)
     wd = _dev_weights(w, "f32")
     kf = torch.zeros((S, H, Dh), dtype=torch.float32, device="cuda")
     vf = torch.zeros_like(kf)
     ranks = []
     for r in range(D):
-        s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype="f32")
+        s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype="f32", rope_base=rope)
         pos = oracle.zigzag_positions(S, D, r)
         ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
         xd = up(x_full[pos], "f32")
@@ -283,14 +284,17 @@ def test_tiny_layer_rank_mode_given_remote_kv(torch):
         assert_close(down(y) - x, want["y"] - x, 10 * TOL_F32, "y - x (both branches)")
 
 
-@pytest.mark.parametrize("S,D,H,Dh,F", [
-    (2048, 4, 4, 128, 2048),
-    (2400, 4, 4, 128, 2048),   # N = 600: ragged row tiles
-    (1024, 2, 4, 64, 1024),
-    (96, 3, 6, 64, 576),       # C = 16: rank 0 recomputes 16 leading rows (one 32-row MFMA block)
-    (256, 1, 4, 64, 512),      # D = 1: one shard, the plain layer
+@pytest.mark.parametrize("S,D,H,Dh,F,rope", [
+    (2048, 4, 4, 128, 2048, 0.0),
+    (2400, 4, 4, 128, 2048, 0.0),   # N = 600: ragged row tiles
+    (1024, 2, 4, 64, 1024, 0.0),
+    (96, 3, 6, 64, 576, 0.0),       # C = 16: rank 0 recomputes 16 leading rows (one 32-row MFMA block)
+    (256, 1, 4, 64, 512, 0.0),      # D = 1: one shard, the plain layer
+    (2048, 4, 4, 128, 2048, 10000.0),  # rotary embedding, heads of 128
+    (1024, 2, 4, 64, 1024, 500.0),     # rotary embedding, heads of 64 (two per 128-column block)
+    (96, 3, 6, 64, 576, 10000.0),      # rotary embedding on the 16 leading rows too
 ])
-def test_bf16_layer_vs_oracle(torch, S, D, H, Dh, F):
+def test_bf16_layer_vs_oracle(torch, S, D, H, Dh, F, rope):
     h = H * Dh
     shape = synth.LayerShape(S=S, D=D, h=h, H=H, Dh=Dh, F=F, dtype="bf16")
     w = synth.layer_weights(shape, seed=3, gain="random")
@@ -300,15 +304,21 @@ def test_bf16_layer_vs_oracle(torch, S, D, H, Dh, F):
     k64, v64 = f64(k_rem, "bf16"), f64(v_rem, "bf16")
     for r in sorted({0, D - 1}):
         x = synth.activations(S // D, h, seed=3, tid=100 + r)
-        s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype="bf16")
+        s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype="bf16", rope_base=rope)
         ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
         kf, vf = up(k_rem, "bf16"), up(v_rem, "bf16")
         y = torch.empty((S // D, h), dtype=torch.float32, device="cuda")
-        log(f"bf16 layer S={S} D={D} r={r} H={H} Dh={Dh} F={F}")
+        log(f"bf16 layer S={S} D={D} r={r} H={H} Dh={Dh} F={F} rope={rope}")
         tsp.tsp_layer_fwd(s, wd, up(x, "f32"), kf, vf, y, tsp.TSP_PHASE_ALL, ws)
         _sync(torch)
-        want = oracle.layer_rank(x, w64, k64, v64, S, D, r, H, Dh, shape.eps, shape.scale)
-        assert_close(down(y), want["y"], TOL_BF16, "y")
+        want = oracle.layer_rank(x, w64, k64, v64, S, D, r, H, Dh, shape.eps, shape.scale, rope_base=rope)
+        err = assert_close(down(y), want["y"], TOL_BF16, "y")
+        if rope > 0:
+            # the output is much closer to the rotated layer than to the plain one
+            plain = oracle.layer_rank(x, w64, k64, v64, S, D, r, H, Dh, shape.eps, shape.scale)["y"]
+            far = float(np.abs(down(y) - plain).max()) / float(np.sqrt(np.mean(want["y"] ** 2)))
+            log(f"  distance to the layer without rotation: {far:.3e} rms")
+            assert far > 5 * err
         if r == 0:
             # rank 0's first positions are recomputed with fp32 intermediates
             m = min(64, S // (2 * D))

@@ -101,6 +101,10 @@ tsp_status check_layer_shape(const tsp_shape *s) {
   if (s->H % s->D != 0) return fail(TSP_ERR_INVALID_ARG, "H=%d must be a multiple of D=%d", s->H, s->D);
   if (s->h != s->H * s->Dh) return fail(TSP_ERR_INVALID_ARG, "h=%d != H*Dh=%d", s->h, s->H * s->Dh);
   if (!isfinite(s->eps) || s->eps < 0.f) return fail(TSP_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!isfinite(s->rope_base) || s->rope_base < 0.f)
+    return fail(TSP_ERR_INVALID_ARG, "rope_base must be finite and >= 0");
+  if (s->rope_base > 0.f && s->dtype == TSP_BF16 && (s->h / s->D) % 128 != 0)
+    return fail(TSP_ERR_UNSUPPORTED, "rotary embedding in bf16 needs h/D=%d to be a multiple of 128", s->h / s->D);
   return TSP_OK;
 }
 
@@ -113,6 +117,7 @@ int32_t lead_rows(const tsp_shape *s) {
 
 struct LayerWs {
   size_t q, x2, hid;
+  size_t rope;  // rotary table [N][Dh/2] (cos, sin) fp32, when rope_base > 0
   // leading rows: fp32 [m][h] normed input, q, k, v, attention output, h1,
   // normed h1; [m][F] hidden layer; partial sums of the products
   size_t la, lq, lk, lv, lo, lh1, lmm, lhid, lpart;
@@ -127,6 +132,8 @@ LayerWs layer_ws(const tsp_shape *s) {
   w.x2 = align256(N * s->h * e);
   w.hid = w.x2 + align256(N * s->h * e);
   size_t at = w.hid + align256(N * (size_t)s->F * e);
+  w.rope = at;
+  if (s->rope_base > 0.f) at += align256(N * (size_t)(s->Dh / 2) * 8);
   const size_t m = (size_t)lead_rows(s);
   const size_t mh = m ? align256(m * s->h * 4) : 0;
   w.la = at;
@@ -250,7 +257,7 @@ const char *tsp_status_string(int status) {
 
 const char *tsp_last_error(void) { return g_err.c_str(); }
 
-int tsp_abi_version(void) { return 1; }
+int tsp_abi_version(void) { return 2; }
 
 tsp_status tsp_workspace_size(const tsp_shape *s, int which, size_t *bytes) {
   if (!bytes) return fail(TSP_ERR_INVALID_ARG, "bytes is NULL");
@@ -394,12 +401,26 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
   const float q_scale = pnl ? s->scale * 1.4426950408889634f : 1.0f;
   hipStream_t stream = (hipStream_t)stream_;
 
+  // rotary table, written with the QKV of PHASE_KV and read again by the
+  // leading rows in PHASE_REST (same ws)
+  const bool rope = s->rope_base > 0.f;
+  float2 *rtab = rope ? reinterpret_cast<float2 *>(ws + L.rope) : nullptr;
   if (phases & TSP_PHASE_KV) {
     TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(x, w->g_attn, x2, N, h, s->eps, s->dtype, pnl, stream), "RMSNorm");
+    if (rope)
+      TSP_LAUNCH(TSP_K_QKV, tsp::launch_rope_table(zz, N, s->Dh, s->rope_base, rtab, stream), "rotary table");
+    // bf16: Q and K are rotated in the QKV epilogue, before rounding; fp32:
+    // in place afterwards
     TSP_LAUNCH(TSP_K_QKV,
                tsp::launch_qkv(s->dtype, x2, pnl, N, h, to_list(w->wqkv, D), D, hd, qbuf, k_full, v_full, zz, q_scale,
-                               stream),
+                               pnl ? rtab : nullptr, s->Dh, stream),
                "QKV");
+    if (rope && !pnl) {
+      TSP_LAUNCH(TSP_K_QKV, tsp::launch_rope_rows((float *)qbuf, h, N, s->H, s->Dh, zz, false, rtab, stream),
+                 "rotary embedding of Q");
+      TSP_LAUNCH(TSP_K_QKV, tsp::launch_rope_rows((float *)k_full, h, N, s->H, s->Dh, zz, true, rtab, stream),
+                 "rotary embedding of K");
+    }
   }
   if (phases & TSP_PHASE_REST) {
     TSP_LAUNCH(TSP_K_ATTN,
@@ -429,6 +450,12 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
       TSP_LAUNCH(TSP_K_LEAD,
                  tsp::launch_lead_qkv(la, m, h, to_list(w->wqkv, D), D, hd, lq, lk, lv, zz, lpart, stream),
                  "leading rows: QKV");
+      if (rope) {  // rows 0..m-1 sit at positions 0..m-1, table rows 0..m-1
+        TSP_LAUNCH(TSP_K_LEAD, tsp::launch_rope_rows(lq, h, m, s->H, s->Dh, zz, false, rtab, stream),
+                   "leading rows: rotary embedding of Q");
+        TSP_LAUNCH(TSP_K_LEAD, tsp::launch_rope_rows(lk, h, m, s->H, s->Dh, zz, false, rtab, stream),
+                   "leading rows: rotary embedding of K");
+      }
       TSP_LAUNCH(TSP_K_LEAD,
                  tsp::launch_lead_attention(lq, lk, lv, lo, m, s->H, s->Dh, s->scale, stream),
                  "leading rows: attention");

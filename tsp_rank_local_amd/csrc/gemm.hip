@@ -48,7 +48,17 @@ struct GemmArgs {
 
 // ---------------------------------------------------------------- epilogues
 // Each epilogue takes one output element (fp32 kernel) or four consecutive
-// columns of one row (bf16 kernel) of problem z.
+// columns of one row (bf16 kernel) of problem z. On the bf16 kernel's fast
+// path it gets a row's whole 128 columns at once (put_row; v[i][vq] holds
+// columns 32*i + 8*vq + 4*g .. +3 of the wave's block), which most of them
+// store one float4 at a time.
+template <class Epi>
+__device__ __forceinline__ void put_each(const Epi &e, const typename Epi::Row &w, const float4 (&v)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int vq = 0; vq < 4; ++vq) e.put(w, i, vq, v[i][vq]);
+}
 template <typename T>
 __device__ __forceinline__ void store4(T *p, float4 v) {
   if constexpr (sizeof(T) == 4) {
@@ -98,6 +108,7 @@ struct EpiGelu {
   __device__ __forceinline__ void put(const Row &w, int i, int vq, float4 v) const {
     store4(w.p[i >> 1] + (i & 1) * 32 + vq * 8, make_float4(gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w)));
   }
+  __device__ __forceinline__ void put_row(const Row &w, const float4 (&v)[4][4]) const { put_each(*this, w, v); }
 };
 
 struct EpiStoreF32 {
@@ -115,6 +126,7 @@ struct EpiStoreF32 {
   __device__ __forceinline__ void put(const Row &w, int i, int vq, float4 v) const {
     *reinterpret_cast<float4 *>(w.p + i * 32 + vq * 8) = v;
   }
+  __device__ __forceinline__ void put_row(const Row &w, const float4 (&v)[4][4]) const { put_each(*this, w, v); }
 };
 
 // out = res + acc; res may alias out (each element is read then written by
@@ -146,6 +158,7 @@ struct EpiAddF32 {
     const float4 x = *reinterpret_cast<const float4 *>(w.x + d);
     *reinterpret_cast<float4 *>(w.p + d) = make_float4(x.x + v.x, x.y + v.y, x.z + v.z, x.w + v.w);
   }
+  __device__ __forceinline__ void put_row(const Row &w, const float4 (&v)[4][4]) const { put_each(*this, w, v); }
 };
 
 // Shard z of the QKV projection: output column c of the shard falls in part
@@ -158,7 +171,9 @@ struct EpiQKV {
   int64_t h;
   int32_t hd;
   ZigzagMap zz;
-  float q_scale;  // factor applied to the Q part before rounding
+  float q_scale;       // factor applied to the Q part before rounding
+  const float2 *rope;  // rotary table [local row][dh/2] (cos, sin), or null
+  int32_t dh;          // head width (64 or 128) when rope is set
   __device__ __forceinline__ T *dst(int z, int r, int c) const {
     const int part = c / hd;
     const int64_t col = (int64_t)z * hd + (c - part * hd);
@@ -173,17 +188,50 @@ struct EpiQKV {
     const float f = factor(c);
     store4(dst(z, r, c), make_float4(val.x * f, val.y * f, val.z * f, val.w * f));
   }
-  // whole 128-column blocks stay inside one part when hd is a multiple of 128
+  // whole 128-column blocks stay inside one part when hd is a multiple of
+  // 128, and then also hold whole heads
   struct Row {
     T *p;
     float f;
+    const float2 *rot;  // this row's rotary table when the block is Q or K
   };
   __device__ __forceinline__ bool fast_ok() const { return (hd & 127) == 0; }
   __device__ __forceinline__ Row row(int z, int r, int c0, int g) const {
-    return Row{dst(z, r, c0 + 4 * g), factor(c0)};
+    const bool rotate = rope != nullptr && c0 < 2 * hd;
+    return Row{dst(z, r, c0 + 4 * g), factor(c0), rotate ? rope + (int64_t)r * (dh / 2) : nullptr};
   }
   __device__ __forceinline__ void put(const Row &w, int i, int vq, float4 v) const {
     store4(w.p + i * 32 + vq * 8, make_float4(v.x * w.f, v.y * w.f, v.z * w.f, v.w * w.f));
+  }
+  // Rotary embedding on Q and K: feature d of a head pairs with d + dh/2.
+  // The block's column 32*i + 8*vq + 4*g + e is feature (32*i) % dh + ...,
+  // so block i < its partner i + dh/64 (same vq, same lane) whenever block
+  // i holds the first half of a head; the pair's frequency index is
+  // (32*i) % (dh/2) + 8*vq + 4*g + e.
+  __device__ __forceinline__ void put_row(const Row &w, const float4 (&v)[4][4]) const {
+    if (w.rot == nullptr) {
+      put_each(*this, w, v);
+      return;
+    }
+    const int step = dh / 64;
+    const int g = (threadIdx.x >> 5) & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if ((i / step) & 1) continue;  // second half of a head: handled with its partner
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        const int f0 = (32 * i) % (dh / 2) + 8 * vq + 4 * g;
+        const float4 cs01 = *reinterpret_cast<const float4 *>(w.rot + f0);
+        const float4 cs23 = *reinterpret_cast<const float4 *>(w.rot + f0 + 2);
+        const float4 a = v[i][vq], b = v[i + step][vq];
+        put(w, i, vq,
+            make_float4(a.x * cs01.x - b.x * cs01.y, a.y * cs01.z - b.y * cs01.w, a.z * cs23.x - b.z * cs23.y,
+                        a.w * cs23.z - b.w * cs23.w));
+        put(w, i + step, vq,
+            make_float4(b.x * cs01.x + a.x * cs01.y, b.y * cs01.z + a.y * cs01.w, b.z * cs23.x + a.z * cs23.y,
+                        b.w * cs23.z + a.w * cs23.w));
+      }
+    }
   }
 };
 
@@ -445,13 +493,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, 
     if (row >= a.M) continue;
     if (whole) {
       const typename Epi::Row rw = epi.row(z, row, c0, g);
+      float4 vals[4][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int vq = 0; vq < 4; ++vq)
-          epi.put(rw, i, vq,
-                  make_float4(acc[i][j][vq * 4 + 0], acc[i][j][vq * 4 + 1], acc[i][j][vq * 4 + 2],
-                              acc[i][j][vq * 4 + 3]));
+          vals[i][vq] = make_float4(acc[i][j][vq * 4 + 0], acc[i][j][vq * 4 + 1], acc[i][j][vq * 4 + 2],
+                                    acc[i][j][vq * 4 + 3]);
+      epi.put_row(rw, vals);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -684,7 +733,7 @@ hipError_t launch_lead_qkv(const float *a, int32_t m, int32_t h, const PtrList &
   g.B = w;
   g.ldb = h;
   g.nz = D;
-  EpiQKV<float> e{q, k, v, h, hd, zz, 1.0f};
+  EpiQKV<float> e{q, k, v, h, hd, zz, 1.0f, nullptr, 0};
   return run_lead(g, e, part, s);
 }
 
@@ -755,16 +804,18 @@ static GemmArgs make_args(const void *A, int64_t lda, bool a_panel, int32_t M, i
 }
 
 hipError_t launch_qkv(int dtype, const void *xn, bool a_panel, int32_t n, int32_t h, const PtrList &w, int32_t D,
-                      int32_t hd, void *q, void *kf, void *vf, ZigzagMap zz, float q_scale, hipStream_t s) {
+                      int32_t hd, void *q, void *kf, void *vf, ZigzagMap zz, float q_scale, const float2 *rope,
+                      int32_t Dh, hipStream_t s) {
+  if (rope != nullptr && (dtype != TSP_BF16 || (hd & 127) != 0)) return hipErrorInvalidValue;
   GemmArgs a = make_args(xn, h, a_panel, n, 3 * hd, h);
   a.B = w;
   a.ldb = h;
   a.nz = D;
   if (dtype == TSP_BF16) {
-    EpiQKV<bf16> e{(bf16 *)q, (bf16 *)kf, (bf16 *)vf, h, hd, zz, q_scale};
+    EpiQKV<bf16> e{(bf16 *)q, (bf16 *)kf, (bf16 *)vf, h, hd, zz, q_scale, rope, Dh};
     return run_gemm(dtype, a, e, s);
   }
-  EpiQKV<float> e{(float *)q, (float *)kf, (float *)vf, h, hd, zz, q_scale};
+  EpiQKV<float> e{(float *)q, (float *)kf, (float *)vf, h, hd, zz, q_scale, nullptr, 0};
   return run_gemm(dtype, a, e, s);
 }
 

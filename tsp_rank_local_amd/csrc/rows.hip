@@ -65,6 +65,52 @@ hipError_t launch_rmsnorm(const float *x, const void *g, void *out, int32_t rows
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- rotary embedding
+// table[t * half + i] = (cos, sin) of pos(t) * base^(-2i/Dh), in fp64 before
+// rounding to fp32 (the angle reaches S radians for i = 0).
+__global__ __launch_bounds__(256) void rope_table_kernel(ZigzagMap zz, int32_t n, int32_t half, double base,
+                                                         float2 *__restrict__ table) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)n * half) return;
+  const int t = (int)(e / half), i = (int)(e - (int64_t)t * half);
+  const double ang = (double)zz.pos(t) * pow(base, -(double)i / (double)half);
+  table[e] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+// In-place rotation of fp32 rows: row t (at x + (scatter ? pos(t) : t) * ld)
+// holds H heads of Dh; pair i of a head is features (i, i + Dh/2).
+__global__ __launch_bounds__(256) void rope_rows_kernel(float *__restrict__ x, int64_t ld, int32_t n, int32_t H,
+                                                        int32_t half, ZigzagMap zz, int32_t scatter,
+                                                        const float2 *__restrict__ table) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)n * H * half) return;
+  const int t = (int)(e / ((int64_t)H * half));
+  const int rem = (int)(e - (int64_t)t * H * half);
+  const int hh = rem / half, i = rem - hh * half;
+  float *row = x + (int64_t)(scatter ? zz.pos(t) : t) * ld + (int64_t)hh * 2 * half;
+  const float2 cs = table[(int64_t)t * half + i];
+  const float a = row[i], b = row[i + half];
+  row[i] = a * cs.x - b * cs.y;
+  row[i + half] = b * cs.x + a * cs.y;
+}
+
+hipError_t launch_rope_table(ZigzagMap zz, int32_t n, int32_t Dh, float base, float2 *table, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t total = (int64_t)n * (Dh / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, zz, n, Dh / 2,
+                     (double)base, table);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_rows(float *x, int64_t ld, int32_t n, int32_t H, int32_t Dh, ZigzagMap zz, bool scatter,
+                            const float2 *table, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t total = (int64_t)n * H * (Dh / 2);
+  hipLaunchKernelGGL(rope_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, x, ld, n, H, Dh / 2,
+                     zz, scatter ? 1 : 0, table);
+  return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm_f32(const float *x, const void *g, int g_dtype, float *out, int32_t rows, int32_t h,
                               float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;

@@ -54,14 +54,25 @@ hipError_t launch_rmsnorm(const float *x, const void *g, void *out, int32_t rows
 hipError_t launch_rmsnorm_f32(const float *x, const void *g, int g_dtype, float *out, int32_t rows, int32_t h,
                               float eps, hipStream_t s);
 
+// Rotary embedding (optional): table[t][i] = (cos, sin) of pos(t) *
+// base^(-2i/Dh) for local rows t < n, pairs i < Dh/2 (computed in fp64).
+hipError_t launch_rope_table(ZigzagMap zz, int32_t n, int32_t Dh, float base, float2 *table, hipStream_t s);
+// In place on fp32 rows: row t at x + (scatter ? pos(t) : t) * ld holds H
+// heads of Dh; pair i of each head (features i, i + Dh/2) turns by table[t][i].
+hipError_t launch_rope_rows(float *x, int64_t ld, int32_t n, int32_t H, int32_t Dh, ZigzagMap zz, bool scatter,
+                            const float2 *table, hipStream_t s);
+
 // ---------------------------------------------------------------- GEMMs
 // All products are C = A B^T with A [M][K] and B [N][K] (both K-contiguous).
 // a_panel: A in panel layout (bf16 only; panel stride M * 64), else row-major.
 // QKV of every attention shard in one launch: shard z reads w[z] [3hd][h];
 // Q columns go to q [N][h] at column z*hd (multiplied by q_scale before
 // rounding), K/V rows go to kf/vf [S][h] at row zz.pos(t), column z*hd.
+// rope (bf16 only, hd % 128 == 0): when not null, Q and K are rotated with
+// the table of launch_rope_table (heads of Dh) before rounding.
 hipError_t launch_qkv(int dtype, const void *xn, bool a_panel, int32_t n, int32_t h, const PtrList &w, int32_t D,
-                      int32_t hd, void *q, void *kf, void *vf, ZigzagMap zz, float q_scale, hipStream_t s);
+                      int32_t hd, void *q, void *kf, void *vf, ZigzagMap zz, float q_scale, const float2 *rope,
+                      int32_t Dh, hipStream_t s);
 // y = x + sum_j o[:, j*hd:(j+1)*hd] wo[j]^T, shards walked j = 0..D-1 inside
 // the reduction loop.
 hipError_t launch_outproj(int dtype, const void *o, bool a_panel, int32_t n, int32_t h, const PtrList &wo,
