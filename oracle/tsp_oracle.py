@@ -29,8 +29,8 @@ Readings where the pages are silent (each is restated where it is used):
      of W_Q, W_K, W_V (output rows) and of W_O (input columns).
   R3 the gathered K/V are full-sequence, all heads, in global position order.
   R4 causal mask is inclusive (key u is visible to the query at p iff u <= p),
-     softmax scale 1/sqrt(Dh), no bias, no rotary embedding, multi-head (not
-     grouped) attention.
+     softmax scale 1/sqrt(Dh), no bias; rotary embedding and grouped K/V heads
+     only as the optional variants R7 and R8.
   R5 the MLP is two matrices with exact (erf) GELU, width F = 4h; MLP shard j
      holds hidden units j*F/D..(j+1)*F/D-1 (rows of W1, columns of W2).
   R6 pre-RMSNorm residual block: h1 = x + Attn(RMSNorm(x)),
@@ -40,6 +40,10 @@ Readings where the pages are silent (each is restated where it is used):
      global position p before attention. Feature d and feature d + Dh/2 of a
      head form a pair (the rotate-half convention); pair i turns by the
      angle p * rope_base^(-2i/Dh).
+  R8 grouped-query attention (an optional variant; the pages' model is
+     multi-head): Hkv K/V heads, each shared by H/Hkv consecutive query heads
+     (query head i reads K/V head i // (H/Hkv)); shard j then holds query
+     heads j*H/D.. and K/V heads j*Hkv/D.. Hkv = H is multi-head attention.
 """
 from __future__ import annotations
 
@@ -116,17 +120,19 @@ def gelu(z) -> np.ndarray:
 def causal_attention(q, k, v, q_pos, scale: float, row_block: int = 256) -> np.ndarray:
     """Softmax attention of queries at global positions q_pos over K/V.
 
-    q: [n, H, Dh] queries; k, v: [S, H, Dh] full-sequence keys and values in
-    global order (reading R3, the result of the all-gather in [P2] paragraph
-    2); q_pos: [n] global position of each query. For each query t and head,
-    the scores scale * <q, k_u> over keys u <= q_pos[t] (reading R4) go
-    through a softmax that weights the values.
+    q: [n, H, Dh] queries; k, v: [S, Hkv, Dh] full-sequence keys and values
+    in global order (reading R3, the result of the all-gather in [P2]
+    paragraph 2), Hkv dividing H (query head i reads K/V head i // (H/Hkv),
+    reading R8); q_pos: [n] global position of each query. For each query t
+    and head, the scores scale * <q, k_u> over keys u <= q_pos[t] (reading R4)
+    go through a softmax that weights the values.
 
     Rows are taken row_block at a time to bound memory; each row is computed
     independently and in full, with its own softmax over its whole prefix.
     """
     q_pos = np.asarray(q_pos, dtype=np.int64)
     n, H, Dh = q.shape
+    group = H // k.shape[1]
     out = np.empty((n, H, Dh), dtype=np.float64)
     for lo in range(0, n, row_block):
         hi = min(n, lo + row_block)
@@ -135,8 +141,8 @@ def causal_attention(q, k, v, q_pos, scale: float, row_block: int = 256) -> np.n
         visible = np.arange(L)[None, :] <= pos[:, None]
         for hd in range(H):
             qh = _f64(q[lo:hi, hd, :])
-            kh = _f64(k[:L, hd, :])
-            vh = _f64(v[:L, hd, :])
+            kh = _f64(k[:L, hd // group, :])
+            vh = _f64(v[:L, hd // group, :])
             s = scale * (qh @ kh.T)
             s = np.where(visible, s, -np.inf)
             s = s - s.max(axis=1, keepdims=True)
@@ -167,18 +173,21 @@ def rope(x, pos, base: float) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Shards -> unsharded matrices
 # --------------------------------------------------------------------------
-def unshard_attention_weights(wqkv, wo, H: int, Dh: int):
-    """Rebuild W_Q, W_K, W_V [h, h] and W_O [h, h] (out, in) from the D shards.
+def unshard_attention_weights(wqkv, wo, H: int, Dh: int, Hkv: int | None = None):
+    """Rebuild W_Q [H*Dh, h], W_K, W_V [Hkv*Dh, h] and W_O [h, H*Dh] (out, in)
+    from the D shards.
 
     Reading R2: shard j's rows are the Q rows, then K rows, then V rows of its
-    head group, so concatenating shard j's Q rows over j in order gives W_Q,
-    and W_O is the concatenation of the shards' columns.
+    head group (H/D query heads, Hkv/D K/V heads, reading R8), so
+    concatenating shard j's Q rows over j in order gives W_Q, and W_O is the
+    concatenation of the shards' columns.
     """
     D = len(wqkv)
-    hd = (H // D) * Dh
-    wq = np.concatenate([_f64(w)[0:hd] for w in wqkv], axis=0)
-    wk = np.concatenate([_f64(w)[hd:2 * hd] for w in wqkv], axis=0)
-    wv = np.concatenate([_f64(w)[2 * hd:3 * hd] for w in wqkv], axis=0)
+    Hkv = H if Hkv is None else Hkv
+    hq, hkv = (H // D) * Dh, (Hkv // D) * Dh
+    wq = np.concatenate([_f64(w)[0:hq] for w in wqkv], axis=0)
+    wk = np.concatenate([_f64(w)[hq:hq + hkv] for w in wqkv], axis=0)
+    wv = np.concatenate([_f64(w)[hq + hkv:hq + 2 * hkv] for w in wqkv], axis=0)
     w_o = np.concatenate([_f64(w) for w in wo], axis=1)
     return wq, wk, wv, w_o
 
@@ -210,22 +219,25 @@ def mlp_shard(x, w1_j, w2_j) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Whole layer
 # --------------------------------------------------------------------------
-def layer_full(x, w: dict, H: int, Dh: int, eps: float, scale: float, rope_base: float = 0.0) -> dict:
+def layer_full(x, w: dict, H: int, Dh: int, eps: float, scale: float, rope_base: float = 0.0,
+               Hkv: int | None = None) -> dict:
     """Unsharded pre-norm decoder layer over the whole sequence (reading R6).
 
     x: [S, h] in global order. w: the shard lists wqkv, wo, w1, w2 and gains
     g_attn, g_mlp. TSP rearranges this computation over ranks and shards but
     reaches the same values ([P2] paragraphs 1-2), so this is what every rank
     must reproduce for its own rows. rope_base > 0 rotates Q and K (reading
-    R7). Returns y and the intermediates h1, q, k, v, o.
+    R7); Hkv < H groups the K/V heads (R8). Returns y and the intermediates h1,
+    q, k, v, o.
     """
     x = _f64(x)
     S = x.shape[0]
-    wq, wk, wv, w_o = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh)
+    Hkv = H if Hkv is None else Hkv
+    wq, wk, wv, w_o = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh, Hkv)
     a = rms_norm(x, w["g_attn"], eps)
     q = rope((a @ wq.T).reshape(S, H, Dh), np.arange(S), rope_base)
-    k = rope((a @ wk.T).reshape(S, H, Dh), np.arange(S), rope_base)
-    v = (a @ wv.T).reshape(S, H, Dh)
+    k = rope((a @ wk.T).reshape(S, Hkv, Dh), np.arange(S), rope_base)
+    v = (a @ wv.T).reshape(S, Hkv, Dh)
     o = causal_attention(q, k, v, np.arange(S), scale)
     h1 = x + o.reshape(S, H * Dh) @ w_o.T
     m = rms_norm(h1, w["g_mlp"], eps)
@@ -234,7 +246,7 @@ def layer_full(x, w: dict, H: int, Dh: int, eps: float, scale: float, rope_base:
 
 
 def layer_rows(x_rows, pos_rows, w: dict, k_all, v_all, H: int, Dh: int, eps: float, scale: float,
-               rope_base: float = 0.0) -> dict:
+               rope_base: float = 0.0, Hkv: int | None = None) -> dict:
     """Layer output for given token rows once the full K/V are gathered (R6).
 
     x_rows: [m, h] tokens, pos_rows: [m] their global positions, k_all, v_all:
@@ -246,7 +258,7 @@ def layer_rows(x_rows, pos_rows, w: dict, k_all, v_all, H: int, Dh: int, eps: fl
     """
     x_rows = _f64(x_rows)
     m = x_rows.shape[0]
-    wq, _, _, w_o = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh)
+    wq, _, _, w_o = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh, Hkv)
     a = rms_norm(x_rows, w["g_attn"], eps)
     q = rope((a @ wq.T).reshape(m, H, Dh), pos_rows, rope_base)
     o = causal_attention(q, k_all, v_all, pos_rows, scale)
@@ -256,25 +268,28 @@ def layer_rows(x_rows, pos_rows, w: dict, k_all, v_all, H: int, Dh: int, eps: fl
     return {"y": y, "h1": h1}
 
 
-def local_kv(x_local, w: dict, H: int, Dh: int, eps: float, pos=None, rope_base: float = 0.0):
-    """K and V [n, H, Dh] of a rank's own tokens (R2, R6); with rope_base > 0
-    K is rotated at the tokens' global positions pos (R7)."""
+def local_kv(x_local, w: dict, H: int, Dh: int, eps: float, pos=None, rope_base: float = 0.0,
+             Hkv: int | None = None):
+    """K and V [n, Hkv, Dh] of a rank's own tokens (R2, R6, R8); with
+    rope_base > 0 K is rotated at the tokens' global positions pos (R7)."""
     x_local = _f64(x_local)
     n = x_local.shape[0]
-    _, wk, wv, _ = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh)
+    Hkv = H if Hkv is None else Hkv
+    _, wk, wv, _ = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh, Hkv)
     a = rms_norm(x_local, w["g_attn"], eps)
-    k = (a @ wk.T).reshape(n, H, Dh)
+    k = (a @ wk.T).reshape(n, Hkv, Dh)
     if rope_base > 0:
         k = rope(k, pos, rope_base)
-    return k, (a @ wv.T).reshape(n, H, Dh)
+    return k, (a @ wv.T).reshape(n, Hkv, Dh)
 
 
 def layer_rank(x_local, w: dict, k_full, v_full, S: int, D: int, r: int,
-               H: int, Dh: int, eps: float, scale: float, rows=None, rope_base: float = 0.0) -> dict:
+               H: int, Dh: int, eps: float, scale: float, rows=None, rope_base: float = 0.0,
+               Hkv: int | None = None) -> dict:
     """Rank r's layer output for its S/D local tokens (reading R6).
 
     x_local: [S/D, h] rank r's tokens in local zigzag order (R1). k_full,
-    v_full: [S, H, Dh] what the all-gather delivers ([P2] paragraph 2); the
+    v_full: [S, Hkv, Dh] what the all-gather delivers ([P2] paragraph 2); the
     rows at rank r's own positions are replaced by the K/V this rank computes
     from x_local, the rest are used as given. rows: optional subset of local
     rows whose output is wanted (all local rows still produce K/V, since any
@@ -288,11 +303,11 @@ def layer_rank(x_local, w: dict, k_full, v_full, S: int, D: int, r: int,
     if n != pos.shape[0]:
         raise ValueError("x_local must hold S/D rows")
     rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
-    k_loc, v_loc = local_kv(x_local, w, H, Dh, eps, pos, rope_base)
+    k_loc, v_loc = local_kv(x_local, w, H, Dh, eps, pos, rope_base, Hkv)
     k_all = np.array(k_full, dtype=np.float64, copy=True)
     v_all = np.array(v_full, dtype=np.float64, copy=True)
     k_all[pos] = k_loc
     v_all[pos] = v_loc
-    out = layer_rows(x_local[rows], pos[rows], w, k_all, v_all, H, Dh, eps, scale, rope_base)
+    out = layer_rows(x_local[rows], pos[rows], w, k_all, v_all, H, Dh, eps, scale, rope_base, Hkv)
     out["pos"] = pos[rows]
     return out

@@ -160,10 +160,12 @@ def test_attention_vs_torch_sdpa():
 
 
 # ---------------------------------------------------------------- shards
-def _split_attention(wq, wk, wv, wo, D, H, Dh):
-    """Shard layout of the library: head group j's Q, K, V rows; W_O columns."""
-    hd = (H // D) * Dh
-    wqkv = [np.concatenate([wq[j * hd:(j + 1) * hd], wk[j * hd:(j + 1) * hd], wv[j * hd:(j + 1) * hd]]) for j in range(D)]
+def _split_attention(wq, wk, wv, wo, D, H, Dh, Hkv=None):
+    """Shard layout of the library: head group j's Q rows (H/D heads), then
+    its K and V rows (Hkv/D heads each); W_O columns of its query heads."""
+    Hkv = H if Hkv is None else Hkv
+    hd, kd = (H // D) * Dh, (Hkv // D) * Dh
+    wqkv = [np.concatenate([wq[j * hd:(j + 1) * hd], wk[j * kd:(j + 1) * kd], wv[j * kd:(j + 1) * kd]]) for j in range(D)]
     wos = [wo[:, j * hd:(j + 1) * hd] for j in range(D)]
     return wqkv, wos
 
@@ -324,6 +326,59 @@ def test_layer_with_rope_vs_torch_and_sharded():
         assert np.allclose(out["y"], full["y"][pos], atol=1e-12)
 
 
+# ---------------------------------------------------------------- grouped K/V heads (R8)
+def test_gqa_attention_vs_torch():
+    rng = np.random.default_rng(31)
+    S, H, Hkv, Dh = 12, 6, 2, 4
+    q = rng.standard_normal((S, H, Dh))
+    k, v = rng.standard_normal((2, S, Hkv, Dh))
+    got = oracle.causal_attention(q, k, v, np.arange(S), 0.7)
+    t = lambda a: torch.from_numpy(a).permute(1, 0, 2)[None]  # noqa: E731  [1, heads, S, Dh]
+    ref = F.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=True, scale=0.7, enable_gqa=True)
+    assert np.allclose(got, ref[0].permute(1, 0, 2).numpy(), atol=1e-12)
+
+
+def _gqa_layer(seed, S, D, H, Hkv, Dh, Fw=96):
+    rng = np.random.default_rng(seed)
+    h, kvw = H * Dh, Hkv * Dh
+    m = dict(wq=0.2 * rng.standard_normal((h, h)), wk=0.2 * rng.standard_normal((kvw, h)),
+             wv=0.2 * rng.standard_normal((kvw, h)), wo=0.2 * rng.standard_normal((h, h)),
+             W1=0.2 * rng.standard_normal((Fw, h)), W2=0.2 * rng.standard_normal((h, Fw)),
+             g1=1 + 0.1 * rng.standard_normal(h), g2=1 + 0.1 * rng.standard_normal(h))
+    w1, w2 = _split_mlp(m["W1"], m["W2"], D)
+    return rng.standard_normal((S, h)), m, w1, w2
+
+
+def test_gqa_layer_equals_mha_with_repeated_kv_heads():
+    """A grouped layer equals the multi-head layer whose K/V weight rows are
+    repeated for every query head of the group (an independent construction),
+    for the unsharded layer and for every rank's view, with rotation too."""
+    S, D, H, Hkv, Dh, eps, base = 32, 2, 4, 2, 8, 1e-5, 100.0
+    scale = 1 / math.sqrt(Dh)
+    x, m, w1, w2 = _gqa_layer(32, S, D, H, Hkv, Dh)
+    g = H // Hkv
+    rep = lambda wm: np.concatenate([np.repeat(wm[i * Dh:(i + 1) * Dh][None], g, 0).reshape(g * Dh, -1)  # noqa: E731
+                                     for i in range(Hkv)])
+    wqkv, wos = _split_attention(m["wq"], m["wk"], m["wv"], m["wo"], D, H, Dh, Hkv)
+    wqkv_mha, wos_mha = _split_attention(m["wq"], rep(m["wk"]), rep(m["wv"]), m["wo"], D, H, Dh)
+    w = dict(wqkv=wqkv, wo=wos, w1=w1, w2=w2, g_attn=m["g1"], g_mlp=m["g2"])
+    w_mha = dict(wqkv=wqkv_mha, wo=wos_mha, w1=w1, w2=w2, g_attn=m["g1"], g_mlp=m["g2"])
+    for rb in (0.0, base):
+        full = oracle.layer_full(x, w, H, Dh, eps, scale, rope_base=rb, Hkv=Hkv)
+        mha = oracle.layer_full(x, w_mha, H, Dh, eps, scale, rope_base=rb)
+        assert full["k"].shape == (S, Hkv, Dh)
+        assert np.allclose(full["y"], mha["y"], atol=1e-12)
+        ref = _torch_layer(x, m["wq"], rep(m["wk"]), rep(m["wv"]), m["wo"], m["W1"], m["W2"], m["g1"], m["g2"], H, Dh,
+                           eps, scale, rope_base=rb)
+        assert np.allclose(full["y"], ref, atol=1e-12)
+        for r in range(D):
+            pos = oracle.zigzag_positions(S, D, r)
+            kr, vr = full["k"].copy(), full["v"].copy()
+            kr[pos], vr[pos] = 1e3, -1e3
+            out = oracle.layer_rank(x[pos], w, kr, vr, S, D, r, H, Dh, eps, scale, rope_base=rb, Hkv=Hkv)
+            assert np.allclose(out["y"], full["y"][pos], atol=1e-12)
+
+
 # ---------------------------------------------------------------- planted mistakes
 def test_planted_mistakes_are_caught(monkeypatch):
     """Each pin above fails when a plausible slip is planted in the oracle."""
@@ -363,6 +418,15 @@ def test_planted_mistakes_are_caught(monkeypatch):
     flipped = oracle.rope(x5, -np.arange(5), 30.0)
     assert not np.allclose(flipped.transpose(1, 0, 2), want, atol=1e-6)
     assert np.allclose(oracle.rope(x5, np.arange(5), 30.0).transpose(1, 0, 2), want, atol=1e-12)
+    # grouping K/V heads round-robin (head i reads i % Hkv) misses torch's GQA
+    qg = rng.standard_normal((6, 4, 3))
+    kg, vg = rng.standard_normal((2, 6, 2, 3))
+    t = lambda a: torch.from_numpy(a).permute(1, 0, 2)[None]  # noqa: E731
+    ref = F.scaled_dot_product_attention(t(qg), t(kg), t(vg), is_causal=True, scale=0.5, enable_gqa=True)
+    ref = ref[0].permute(1, 0, 2).numpy()
+    rr = oracle.causal_attention(qg, np.tile(kg, (1, 2, 1)), np.tile(vg, (1, 2, 1)), np.arange(6), 0.5)
+    assert not np.allclose(rr, ref, atol=1e-6)
+    assert np.allclose(oracle.causal_attention(qg, kg, vg, np.arange(6), 0.5), ref, atol=1e-12)
 
 
 # ---------------------------------------------------------------- synth
