@@ -17,6 +17,7 @@ timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -48,7 +49,7 @@ def attn_pairs(S, D, r):
 
 def layer_flops(sh, r):
     N = sh.N
-    qkv = 2 * N * sh.h * 3 * sh.h
+    qkv = 2 * N * sh.h * (sh.H + 2 * sh.kv_heads) * sh.Dh
     attn = 4 * sh.Dh * sh.H * attn_pairs(sh.S, sh.D, r)
     outp = 2 * N * sh.h * sh.h
     mlp = 2 * 2 * N * sh.h * sh.F
@@ -295,6 +296,9 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--rope-base", type=float, default=0.0,
                     help="rotary embedding base for the layer workloads (0 = none, the pages' model)")
+    ap.add_argument("--hkv", type=int, default=0,
+                    help="K/V heads for the layer and attention workloads (grouped-query attention; 0 = 32, "
+                         "multi-head as in the pages' model)")
     ap.add_argument("--cpu-rows", type=int, default=384, help="rows in the CPU oracle sample (0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warmup, run one plain device-to-device copy of this many MiB (a known-size "
@@ -322,14 +326,15 @@ def main():
 
     assert torch.cuda.is_available(), "needs a GPU"
     tsp.lib()
-    sh = synth.SEVEN_B
+    sh = dataclasses.replace(synth.SEVEN_B, Hkv=args.hkv)
     r = args.rank
     N = sh.N
     seed = 4
     t_gen = time.perf_counter()
-    log(f"generating inputs: S={sh.S} D={sh.D} r={r} h={sh.h} H={sh.H} Dh={sh.Dh} F={sh.F}")
+    log(f"generating inputs: S={sh.S} D={sh.D} r={r} h={sh.h} H={sh.H} Hkv={sh.kv_heads} Dh={sh.Dh} F={sh.F}")
     shape = tsp.make_shape(sh.S, sh.D, r, sh.h, sh.H, sh.Dh, sh.F, eps=sh.eps, dtype="bf16",
-                           rope_base=args.rope_base)
+                           rope_base=args.rope_base, Hkv=args.hkv)
+    kv_note = f", {sh.kv_heads} K/V heads" if sh.kv_heads != sh.H else ""
     stream = torch.cuda.current_stream()
     flops = layer_flops(sh, r)
 
@@ -349,8 +354,8 @@ def main():
             tsp.tsp_layer_fwd(shape, wd, xd, kf, vf, y, tsp.TSP_PHASE_ALL, ws)
         step_flops = flops["total"]
         step_exps = sh.H * attn_pairs(sh.S, sh.D, r)
-        workload = (f"tsp_layer_fwd: one 7B dense decoder layer (h=4096, 32x128 heads, FFN 16384, bf16) on rank {r} "
-                    f"of D=8 at S=131072, 16384 local zigzag tokens")
+        workload = (f"tsp_layer_fwd: one 7B dense decoder layer (h=4096, 32x128 heads{kv_note}, FFN 16384, bf16) on "
+                    f"rank {r} of D=8 at S=131072, 16384 local zigzag tokens")
     elif args.workload == "mlp":
         x = synth.activations(N, sh.h, seed=2, dtype="bf16")
         xd = tsp.to_device(x, "bf16")
@@ -374,16 +379,17 @@ def main():
             return (torch.randn(shape_, generator=gen, device="cuda", dtype=torch.float32) * std).to(dtype)
 
         hd, fd = sh.h // sh.D, sh.F // sh.D
+        hkd = sh.kv_heads * sh.Dh // sh.D
         layers = []
         for _ in range(n_layers):
             wl = {"g_attn": torch.ones(sh.h, dtype=torch.bfloat16, device="cuda"),
                   "g_mlp": torch.ones(sh.h, dtype=torch.bfloat16, device="cuda"),
-                  "wqkv": [rnd((3 * hd, sh.h), 0.02, torch.bfloat16) for _ in range(sh.D)],
+                  "wqkv": [rnd((hd + 2 * hkd, sh.h), 0.02, torch.bfloat16) for _ in range(sh.D)],
                   "wo": [rnd((sh.h, hd), 0.02, torch.bfloat16) for _ in range(sh.D)],
                   "w1": [rnd((fd, sh.h), 0.02, torch.bfloat16) for _ in range(sh.D)],
                   "w2": [rnd((sh.h, fd), 0.02, torch.bfloat16) for _ in range(sh.D)]}
-            kl = rnd((sh.S, sh.H, sh.Dh), 1.0, torch.bfloat16)
-            vl = rnd((sh.S, sh.H, sh.Dh), 1.0, torch.bfloat16)
+            kl = rnd((sh.S, sh.kv_heads, sh.Dh), 1.0, torch.bfloat16)
+            vl = rnd((sh.S, sh.kv_heads, sh.Dh), 1.0, torch.bfloat16)
             layers.append((wl, kl, vl))
         xbuf = [rnd((N, sh.h), 1.0, torch.float32), torch.empty((N, sh.h), dtype=torch.float32, device="cuda"),
                 torch.empty((N, sh.h), dtype=torch.float32, device="cuda")]
@@ -399,7 +405,7 @@ def main():
         step_flops = n_layers * flops["total"]
         step_exps = n_layers * sh.H * attn_pairs(sh.S, sh.D, r)
         N = N * n_layers  # value = layer-tokens/s, comparable with the one-layer figure
-        workload = (f"32 x tsp_layer_fwd: 32-layer 7B dense forward (each layer h=4096, 32x128 heads, FFN 16384, "
+        workload = (f"32 x tsp_layer_fwd: 32-layer 7B dense forward (each layer h=4096, 32x128 heads{kv_note}, FFN 16384, "
                     f"bf16, own weights and remote K/V, all resident) on rank {r} of D=8 at S=131072, "
                     f"16384 local zigzag tokens; value counts layer-tokens (16384 x 32 per step)")
     else:
@@ -413,7 +419,7 @@ def main():
             tsp.tsp_zigzag_attn(shape, qd, kf, vf, o, tsp.TSP_F32)
         step_flops = flops["attention"]
         step_exps = sh.H * attn_pairs(sh.S, sh.D, r)
-        workload = f"tsp_zigzag_attn: 32x128 heads, S=131072, 16384 zigzag queries of rank {r} of D=8"
+        workload = f"tsp_zigzag_attn: 32x128 heads{kv_note}, S=131072, 16384 zigzag queries of rank {r} of D=8"
     torch.cuda.synchronize()
     log(f"inputs resident in HBM ({time.perf_counter() - t_gen:.1f} s); warmup {args.warmup}")
 
@@ -475,8 +481,9 @@ def main():
         achieved = flops["attention"] / t_attn / 1e12
         roofline = {"kernel": "attn_bf16_kernel<128>", "bound": "mfma", "achieved": achieved,
                     "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_BF16,
-                    "traffic": traffic_from_profile(os.path.join(ROOT, "tsp_rank_local_amd", "csrc", "attention.hip"),
-                                                    "attention_7b")}
+                    # counters were taken on rank 0 with 32 K/V heads
+                    "traffic": (traffic_from_profile(os.path.join(ROOT, "tsp_rank_local_amd", "csrc", "attention.hip"),
+                                                     "attention_7b") if r == 0 and sh.kv_heads == sh.H else None)}
     elif "mlp_up" in kernels:
         t_up = kernels["mlp_up"]["ms_per_launch"] * 1e-3
         f_up = 2 * N * sh.h * (sh.F // sh.D)
@@ -505,7 +512,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload, "S": sh.S, "D": sh.D, "r": r, "h": sh.h, "H": sh.H, "Dh": sh.Dh,
                    "F": sh.F, "local_tokens": sh.N, "layers": 32 if args.workload == "layers32" else 1,
-                   "parallelism": "one rank of a D=8 folded TP+SP axis", "rope_base": args.rope_base},
+                   "parallelism": "one rank of a D=8 folded TP+SP axis", "rope_base": args.rope_base,
+                   "Hkv": sh.kv_heads},
         "pct_bf16_mfma_peak": 100.0 * step_flops / (ms_step * 1e-3) / PEAK_BF16,
         # the same against the dense peak scaled to the mean shader clock seen
         # during the timed steps (the published peak assumes 2.4 GHz)
@@ -551,8 +559,8 @@ def cpu_baseline(sh, r, x, w, k_rem, v_rem, m, rope_base=0.0):
     rows = np.linspace(0, sh.N - 1, m).round().astype(np.int64)
     pos = oracle.zigzag_positions(sh.S, sh.D, r)[rows]
     t0 = time.perf_counter()
-    oracle.local_kv(x[rows], w64, sh.H, sh.Dh, sh.eps, pos, rope_base)
-    oracle.layer_rows(x[rows], pos, w64, k32, v32, sh.H, sh.Dh, sh.eps, sh.scale, rope_base)
+    oracle.local_kv(x[rows], w64, sh.H, sh.Dh, sh.eps, pos, rope_base, Hkv=sh.kv_heads)
+    oracle.layer_rows(x[rows], pos, w64, k32, v32, sh.H, sh.Dh, sh.eps, sh.scale, rope_base, Hkv=sh.kv_heads)
     t = time.perf_counter() - t0
     log(f"cpu baseline: {t:.1f} s")
     return {"value": m / t, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle", "cpu_model": cpu_model(),

@@ -86,14 +86,20 @@ typedef enum { TSP_F32 = 0, TSP_BF16 = 1 } tsp_dtype;
  *        angle pos * rope_base^(-2i/Dh), pos = the token's global position.
  *        bf16 layers need h/D to be a multiple of 128 for it (else
  *        TSP_ERR_UNSUPPORTED). tsp_zigzag_attn takes Q and K as given.
- * Local token count N = S/D. Widths used as GEMM dimensions (h, F/D and
- * 3h/D, h/D) must be multiples of 64. */
+ *  Hkv   K/V heads (grouped-query attention, an optional variant; the
+ *        pages' model is multi-head): 0 = H. Otherwise Hkv divides H and
+ *        query head i reads K/V head i / (H/Hkv); the layer also needs
+ *        Hkv % D == 0, so head group j holds query heads j*H/D.. and K/V
+ *        heads j*Hkv/D.., and bf16 rotation needs Hkv*Dh/D % 128 == 0.
+ * Local token count N = S/D. Widths used as GEMM dimensions (h, F/D, h/D)
+ * must be multiples of 64. */
 typedef struct {
   int64_t S;
   int32_t D, r, h, H, Dh, F;
   float eps, scale;
   int32_t dtype;
   float rope_base;
+  int32_t Hkv;
 } tsp_shape;
 
 #define TSP_MAX_D 64
@@ -102,8 +108,9 @@ typedef struct {
  * pointers indexed by SHARD id j (not by delivery step); matrices are stored
  * (out, in), so every product reads its operands along the contiguous axis.
  *  g_attn, g_mlp: [h] RMSNorm gains (dtype).
- *  wqkv[j]: [3h/D][h]  rows: the Q rows of head group j, then its K rows, then
- *           its V rows, each head-major (head, then feature within the head).
+ *  wqkv[j]: [(H + 2Hkv)Dh/D][h]  rows: the Q rows of head group j (H/D
+ *           heads), then its K rows, then its V rows (Hkv/D heads each),
+ *           each head-major (head, then feature within the head).
  *  wo[j]:   [h][h/D]   the columns of W_O that read head group j.
  *  w1[j]:   [F/D][h]   rows j*F/D.. of W1.
  *  w2[j]:   [h][F/D]   columns j*F/D.. of W2. */
@@ -161,10 +168,11 @@ tsp_status tsp_zigzag_index(int64_t S, int32_t D, int32_t r, int32_t *pos, void 
 /* Causal attention of rank r's local queries against the gathered K/V
  * (paragraph 2: K/V are all-gathered, so every rank sees the full sequence).
  *  q: [S/D][H][Dh] local rows in zigzag order (dtype)
- *  k, v: [S][H][Dh] all positions in global order (dtype)
+ *  k, v: [S][Hkv][Dh] all positions in global order (dtype)
  *  o: [S/D][H][Dh] output (o_dtype: TSP_F32, or TSP_BF16 when dtype is bf16)
- * o[t][hd] = sum_{u <= pos[t]} softmax_u(scale * q[t][hd].k[u][hd]) v[u][hd].
- * Uses S, D, r, H, Dh, scale and dtype of the shape. */
+ * o[t][i] = sum_{u <= pos[t]} softmax_u(scale * q[t][i].k[u][j]) v[u][j],
+ * j = i / (H/Hkv) (j = i when Hkv is 0 or H).
+ * Uses S, D, r, H, Hkv, Dh, scale and dtype of the shape. */
 tsp_status tsp_zigzag_attn(const tsp_shape *shape, const void *q, const void *k, const void *v,
                            void *o, int32_t o_dtype, void *stream);
 
@@ -194,7 +202,7 @@ tsp_status tsp_mlp_ring(const tsp_shape *shape, const void *x, const void *const
 
 /* One decoder layer forward on rank r's S/D tokens.
  *  x: [S/D][h] fp32, local rows in zigzag order.
- *  k_full, v_full: [S][H][Dh] (dtype). The rows at rank r's own positions are
+ *  k_full, v_full: [S][Hkv][Dh] (dtype). The rows at rank r's own positions are
  *    written by PHASE_KV; every other row must hold what the all-gather would
  *    deliver (the other ranks' K/V, K already rotated when rope_base > 0)
  *    before PHASE_REST runs.

@@ -41,7 +41,8 @@ class LayerShape:
 
     S: total sequence, D: axis size, h: hidden, H: heads, Dh: head width,
     F: MLP width, eps: RMSNorm epsilon, dtype: 'f32' or 'bf16' storage type of
-    weights and activations (accumulation is always fp32 on the device).
+    weights and activations (accumulation is always fp32 on the device),
+    Hkv: K/V heads of grouped-query attention (0 means H).
     """
 
     S: int
@@ -52,6 +53,11 @@ class LayerShape:
     F: int
     eps: float = 1e-5
     dtype: str = "bf16"
+    Hkv: int = 0
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     @property
     def C(self) -> int:
@@ -143,9 +149,10 @@ def as_f32(a: np.ndarray, dtype: str) -> np.ndarray:
 def layer_weights(shape: LayerShape, seed: int, gain: str = "ones") -> dict:
     """Per-shard weights of one layer, in storage type.
 
-    Shard j of the attention projections covers heads j*H/D .. (j+1)*H/D-1:
-      wqkv[j]: [3*h/D, h]  rows are that head group's Q rows, then K rows,
-               then V rows, each head-major (head, then feature in head);
+    Shard j of the attention projections covers query heads j*H/D ..
+    (j+1)*H/D-1 and K/V heads j*Hkv/D .. (j+1)*Hkv/D-1:
+      wqkv[j]: [(H + 2*Hkv)*Dh/D, h]  rows are that head group's Q rows, then
+               K rows, then V rows, each head-major (head, then feature);
       wo[j]:   [h, h/D]    the W_O columns that read that head group.
     Shard j of the MLP covers hidden units j*F/D .. (j+1)*F/D-1:
       w1[j]:   [F/D, h]    rows of W1 (out, in);
@@ -154,10 +161,11 @@ def layer_weights(shape: LayerShape, seed: int, gain: str = "ones") -> dict:
     """
     D, h, F = shape.D, shape.h, shape.F
     hd = h // D
+    hkd = shape.kv_heads * shape.Dh // D
     fd = F // D
     dt = shape.dtype
     w = {
-        "wqkv": [normal((3 * hd, h), seed, TID_WQKV, j, WEIGHT_STD, dtype=dt) for j in range(D)],
+        "wqkv": [normal((hd + 2 * hkd, h), seed, TID_WQKV, j, WEIGHT_STD, dtype=dt) for j in range(D)],
         "wo": [normal((h, hd), seed, TID_WO, j, WEIGHT_STD, dtype=dt) for j in range(D)],
         "w1": [normal((fd, h), seed, TID_W1, j, WEIGHT_STD, dtype=dt) for j in range(D)],
         "w2": [normal((h, fd), seed, TID_W2, j, WEIGHT_STD, dtype=dt) for j in range(D)],
@@ -180,10 +188,10 @@ def activations(rows: int, width: int, seed: int, tid: int = TID_X, dtype: str =
 
 
 def remote_kv(shape: LayerShape, seed: int, dtype: str | None = None):
-    """Full-sequence K and V, [S, H, Dh], ~ N(0,1): what the all-gather would deliver."""
+    """Full-sequence K and V, [S, Hkv, Dh], ~ N(0,1): what the all-gather would deliver."""
     dt = dtype or shape.dtype
-    k = normal((shape.S, shape.H, shape.Dh), seed, TID_K_REMOTE, 0, 1.0, dtype=dt)
-    v = normal((shape.S, shape.H, shape.Dh), seed, TID_V_REMOTE, 0, 1.0, dtype=dt)
+    k = normal((shape.S, shape.kv_heads, shape.Dh), seed, TID_K_REMOTE, 0, 1.0, dtype=dt)
+    v = normal((shape.S, shape.kv_heads, shape.Dh), seed, TID_V_REMOTE, 0, 1.0, dtype=dt)
     return k, v
 
 

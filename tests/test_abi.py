@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert declared == sorted(tsp.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.tsp_abi_version() == 2
+    assert L.tsp_abi_version() == 3
 
 
 def test_status_strings():
@@ -84,6 +84,16 @@ def test_workspace_sizes():
         assert tsp.workspace_size(s7, tsp.TSP_WS_LAYER) == 2 * 16384 * 4096 * 2 + 16384 * 16384 * 2 + lead
 
 
+def test_grouped_kv_shapes_accepted():
+    """Grouped K/V heads change no workspace buffer (Q, O and the MLP input
+    keep H heads); Hkv = H is the same as Hkv = 0."""
+    base = tsp.workspace_size(_shape(dtype="bf16", H=8, h=512), tsp.TSP_WS_LAYER)
+    for hkv in (0, 4, 8):
+        assert tsp.workspace_size(_shape(dtype="bf16", H=8, h=512, Hkv=hkv), tsp.TSP_WS_LAYER) == base
+    # rotation with whole 128-column Q and K blocks per shard
+    tsp.workspace_size(_shape(dtype="bf16", H=8, h=512, Hkv=4, D=2, rope_base=1e4), tsp.TSP_WS_LAYER)
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(S=1020), tsp.TSP_ERR_INVALID_ARG),          # S not a multiple of 2D
     (dict(S=0), tsp.TSP_ERR_INVALID_ARG),             # empty sequence
@@ -102,6 +112,12 @@ def test_workspace_sizes():
     (dict(rope_base=-1.0), tsp.TSP_ERR_INVALID_ARG),
     (dict(rope_base=float("inf")), tsp.TSP_ERR_INVALID_ARG),
     (dict(rope_base=1e4, dtype="bf16"), tsp.TSP_ERR_UNSUPPORTED),  # h/D = 64: rotation needs whole 128-column heads
+    (dict(Hkv=-1), tsp.TSP_ERR_INVALID_ARG),
+    (dict(Hkv=3), tsp.TSP_ERR_INVALID_ARG),           # Hkv must divide H
+    (dict(Hkv=8), tsp.TSP_ERR_INVALID_ARG),           # more K/V heads than query heads
+    (dict(Hkv=2), tsp.TSP_ERR_INVALID_ARG),           # Hkv % D: a head group needs whole K/V heads
+    (dict(H=8, h=512, Hkv=4, rope_base=1e4, dtype="bf16"),
+     tsp.TSP_ERR_UNSUPPORTED),                        # h/D = 128 but Hkv*Dh/D = 64: no whole 128-column K block
 ])
 def test_shape_errors(kw, code):
     with pytest.raises(tsp.TspError) as ei:
@@ -124,6 +140,13 @@ def test_pointer_errors_enqueue_nothing():
     with pytest.raises(tsp.TspError) as ei:
         tsp.tsp_zigzag_attn(s, FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (1 << 30) + 4096, stream=0)
     assert ei.value.status == tsp.TSP_ERR_INVALID_ARG and b"overlap" in tsp.lib().tsp_last_error()
+    # grouped K/V heads: k and v hold S*Hkv*Dh elements; an o over the last
+    # bytes of a 1-head k overlaps it
+    s1 = _shape(Hkv=1)
+    kv1 = 1024 * 1 * 64 * 4
+    with pytest.raises(tsp.TspError) as ei:
+        tsp.tsp_zigzag_attn(s1, FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (1 << 30) + kv1 - 256, stream=0)
+    assert b"overlap" in tsp.lib().tsp_last_error()
     # fp32 inputs with a bf16 output
     with pytest.raises(tsp.TspError):
         tsp.tsp_zigzag_attn(s, FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), tsp.TSP_BF16, stream=0)

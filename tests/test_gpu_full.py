@@ -4,6 +4,8 @@ oracle computes sampled output rows one by one; where output power is
 concentrated in a few rows (attention of rank 0, whose first queries see few
 keys) the rms in the tolerance is a stratified estimate: a dense block of
 those rows plus a strided sample of the rest, weighted by the stride."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -14,7 +16,7 @@ from gpu_util import TOL_BF16, TOL_F32, assert_close, down, f64, log, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
-SH = synth.SEVEN_B
+SH = SH7 = synth.SEVEN_B
 
 
 @pytest.fixture(scope="module")
@@ -96,21 +98,23 @@ def test_zigzag_attention_7b(torch, r):
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("r,rope", [(0, 0.0), (7, 0.0), (0, 10000.0)])
-def test_layer_7b(torch, r, rope):
+@pytest.mark.parametrize("r,rope,hkv", [(0, 0.0, 0), (7, 0.0, 0), (0, 10000.0, 0), (3, 10000.0, 8)])
+def test_layer_7b(torch, r, rope, hkv):
     """One full layer, ranks 0 (the benchmark's) and 7, the benchmark's inputs
-    (seed 4); and rank 0 with rotary embedding (base 1e4), remote K rows taken
-    as already rotated."""
+    (seed 4); rank 0 with rotary embedding (base 1e4), remote K rows taken as
+    already rotated; and rank 3 with rotation and 8 K/V heads shared by the 32
+    query heads (grouped-query attention)."""
+    SH = dataclasses.replace(SH7, Hkv=hkv)
     N = SH.N
     w = synth.layer_weights(SH, seed=4)
     x = synth.activations(N, SH.h, seed=4)
     k_rem, v_rem = synth.remote_kv(SH, seed=4)
     wd = {k: ([up(a, "bf16") for a in v] if isinstance(v, list) else up(v, "bf16")) for k, v in w.items()}
     kf, vf = up(k_rem, "bf16"), up(v_rem, "bf16")
-    s = tsp.make_shape(SH.S, SH.D, r, SH.h, SH.H, SH.Dh, SH.F, eps=SH.eps, dtype="bf16", rope_base=rope)
+    s = tsp.make_shape(SH.S, SH.D, r, SH.h, SH.H, SH.Dh, SH.F, eps=SH.eps, dtype="bf16", rope_base=rope, Hkv=hkv)
     ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
     y = torch.full((N, SH.h), float("nan"), dtype=torch.float32, device="cuda")
-    log(f"layer 7B r={r} rope={rope}")
+    log(f"layer 7B r={r} rope={rope} Hkv={hkv}")
     tsp.tsp_layer_fwd(s, wd, up(x, "f32"), kf, vf, y, tsp.TSP_PHASE_ALL, ws)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(y).all())
@@ -118,7 +122,7 @@ def test_layer_7b(torch, r, rope):
     rows = np.concatenate([np.arange(16), np.linspace(16, N - 1, 80).round().astype(np.int64)])
     pos = oracle.zigzag_positions(SH.S, SH.D, r)
     # the K/V rows this rank wrote into the gathered buffers
-    k_loc, v_loc = oracle.local_kv(x[rows], w64, SH.H, SH.Dh, SH.eps, pos[rows], rope)
+    k_loc, v_loc = oracle.local_kv(x[rows], w64, SH.H, SH.Dh, SH.eps, pos[rows], rope, Hkv=SH.kv_heads)
     idx = torch.from_numpy(pos[rows]).cuda()
     assert_close(down(kf[idx]), k_loc, TOL_BF16, "local K rows")
     assert_close(down(vf[idx]), v_loc, TOL_BF16, "local V rows")
@@ -128,7 +132,7 @@ def test_layer_7b(torch, r, rope):
     assert np.array_equal(kr, k_rem.view(np.int16)[remote.numpy()])
     del kf, vf, kr
     want = oracle.layer_rank(x, w64, synth.as_f32(k_rem, "bf16"), synth.as_f32(v_rem, "bf16"), SH.S, SH.D, r,
-                             SH.H, SH.Dh, SH.eps, SH.scale, rows=rows, rope_base=rope)
+                             SH.H, SH.Dh, SH.eps, SH.scale, rows=rows, rope_base=rope, Hkv=SH.kv_heads)
     got = down(y[torch.from_numpy(rows).cuda()])
     assert_close(got, want["y"], TOL_BF16, "y rows")
     if r == 0:

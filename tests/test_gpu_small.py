@@ -77,6 +77,52 @@ def test_zigzag_attention(torch, S, D, H, Dh, dtype, odt):
             assert excess.max() <= TOL_BF16 * rms
 
 
+GQA_CASES = [
+    # S, D, H, Hkv, Dh, dtype, o_dtype, q pre-scaled
+    (2048, 4, 8, 2, 128, "bf16", "f32", False),   # groups of 4 query heads
+    (1200, 4, 4, 1, 64, "bf16", "f32", False),    # one K/V head for all (C = 150: ragged tiles)
+    (4096, 2, 8, 4, 128, "bf16", "bf16", True),   # the layer's form: Q * scale * log2(e), bf16 O
+    (1024, 4, 6, 3, 64, "f32", "f32", False),     # fp32 kernel
+]
+
+
+@pytest.mark.parametrize("S,D,H,Hkv,Dh,dtype,odt,q_log2", GQA_CASES)
+def test_grouped_attention(torch, S, D, H, Hkv, Dh, dtype, odt, q_log2):
+    """Grouped K/V heads (query head i reads K/V head i // (H/Hkv)) against
+    the oracle; every rank."""
+    shape = synth.LayerShape(S=S, D=D, h=H * Dh, H=H, Dh=Dh, F=64 * D, dtype=dtype, Hkv=Hkv)
+    k, v = synth.remote_kv(shape, seed=17)
+    assert k.shape == (S, Hkv, Dh)
+    kd, vd = up(k, dtype), up(v, dtype)
+    k64, v64 = f64(k, dtype), f64(v, dtype)
+    N = S // D
+    for r in range(D):
+        q = synth.normal((N, H, Dh), 17, synth.TID_Q, r, dtype=dtype)
+        s = tsp.make_shape(S, D, r, H * Dh, H, Dh, 64 * D, dtype=dtype, Hkv=Hkv)
+        o = torch.empty((N, H, Dh), dtype=torch.float32 if odt == "f32" else torch.bfloat16, device="cuda")
+        log(f"grouped attention S={S} D={D} r={r} H={H} Hkv={Hkv} Dh={Dh} {dtype}->{odt} q_log2={q_log2}")
+        if q_log2:
+            cf = np.float32(s.scale) * np.float32(np.log2(np.e))
+            q = synth.f32_to_bf16(synth.bf16_to_f32(q) * cf)
+            q64 = f64(q, dtype) / (float(s.scale) * np.log2(np.e))
+            tsp.tsp_zigzag_attn_ex(s, up(q, dtype), kd, vd, o, tsp.TSP_BF16, tsp.TSP_ATTN_Q_LOG2_SCALED)
+        else:
+            q64 = f64(q, dtype)
+            tsp.tsp_zigzag_attn(s, up(q, dtype), kd, vd, o, tsp.TSP_F32 if odt == "f32" else tsp.TSP_BF16)
+        _sync(torch)
+        want = oracle.causal_attention(q64, k64, v64, oracle.zigzag_positions(S, D, r), shape.scale)
+        got = down(o)
+        if dtype == "f32":
+            assert_close(got, want, TOL_F32, "o")
+        elif odt == "f32":
+            assert_close(got, want, TOL_BF16, "o")
+        else:
+            rms = float(np.sqrt(np.mean(want ** 2)))
+            excess = np.abs(got - want) - 2.0 ** -8 * np.abs(want)
+            log(f"  o(bf16 out): max excess over rounding = {excess.max():.3e}, rms {rms:.3e}")
+            assert excess.max() <= TOL_BF16 * rms
+
+
 def test_attention_scale_zero_gives_prefix_mean(torch):
     S, D, H, Dh = 512, 2, 2, 128
     shape = synth.LayerShape(S=S, D=D, h=H * Dh, H=H, Dh=Dh, F=128, dtype="bf16")
@@ -263,6 +309,42 @@ def test_tiny_layer_every_rank_vs_unsharded(torch, gain, rope):
     assert_close(got, full["y"], TOL_F32, "y, all ranks")
 
 
+@pytest.mark.parametrize("rope", [0.0, 10000.0])
+def test_fp32_grouped_layer_every_rank_vs_unsharded(torch, rope):
+    """fp32 layer with 8 query heads sharing 2 K/V heads (S=1024, D=2, h=512,
+    Dh=64, F=1024): the ranks write their K/V rows into one gathered buffer of
+    2 heads, then each runs the rest; every rank's rows must equal the
+    unsharded grouped layer's."""
+    S, D, H, Hkv, Dh, F = 1024, 2, 8, 2, 64, 1024
+    h = H * Dh
+    shape = synth.LayerShape(S=S, D=D, h=h, H=H, Dh=Dh, F=F, dtype="f32", Hkv=Hkv)
+    w = synth.layer_weights(shape, seed=5, gain="random")
+    assert w["wqkv"][0].shape == ((H + 2 * Hkv) * Dh // D, h)
+    x_full = synth.activations(S, h, seed=5)
+    full = oracle.layer_full(x_full, _w64(w, "f32"), H, Dh, shape.eps, shape.scale, rope_base=rope, Hkv=Hkv)
+    wd = _dev_weights(w, "f32")
+    kf = torch.zeros((S, Hkv, Dh), dtype=torch.float32, device="cuda")
+    vf = torch.zeros_like(kf)
+    ranks = []
+    for r in range(D):
+        s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype="f32", rope_base=rope, Hkv=Hkv)
+        pos = oracle.zigzag_positions(S, D, r)
+        ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
+        xd = up(x_full[pos], "f32")
+        y = torch.full((S // D, h), float("nan"), dtype=torch.float32, device="cuda")
+        log(f"fp32 grouped layer r={r} rope={rope}: K/V phase")
+        tsp.tsp_layer_fwd(s, wd, xd, kf, vf, y, tsp.TSP_PHASE_KV, ws)
+        ranks.append((s, pos, ws, xd, y))
+    for s, pos, ws, xd, y in ranks:
+        tsp.tsp_layer_fwd(s, wd, xd, kf, vf, y, tsp.TSP_PHASE_REST, ws)
+    _sync(torch)
+    assert_close(down(kf), full["k"], TOL_F32, "gathered K")
+    assert_close(down(vf), full["v"], TOL_F32, "gathered V")
+    for s, pos, ws, xd, y in ranks:
+        log(f"rank {s.r}:")
+        assert_close(down(y), full["y"][pos], TOL_F32, "y rows")
+
+
 def test_tiny_layer_rank_mode_given_remote_kv(torch):
     shape = synth.TINY_FP32
     S, D, h, H, Dh, F = shape.S, shape.D, shape.h, shape.H, shape.Dh, shape.F
@@ -284,19 +366,24 @@ def test_tiny_layer_rank_mode_given_remote_kv(torch):
         assert_close(down(y) - x, want["y"] - x, 10 * TOL_F32, "y - x (both branches)")
 
 
-@pytest.mark.parametrize("S,D,H,Dh,F,rope", [
-    (2048, 4, 4, 128, 2048, 0.0),
-    (2400, 4, 4, 128, 2048, 0.0),   # N = 600: ragged row tiles
-    (1024, 2, 4, 64, 1024, 0.0),
-    (96, 3, 6, 64, 576, 0.0),       # C = 16: rank 0 recomputes 16 leading rows (one 32-row MFMA block)
-    (256, 1, 4, 64, 512, 0.0),      # D = 1: one shard, the plain layer
-    (2048, 4, 4, 128, 2048, 10000.0),  # rotary embedding, heads of 128
-    (1024, 2, 4, 64, 1024, 500.0),     # rotary embedding, heads of 64 (two per 128-column block)
-    (96, 3, 6, 64, 576, 10000.0),      # rotary embedding on the 16 leading rows too
+@pytest.mark.parametrize("S,D,H,Dh,F,rope,Hkv", [
+    (2048, 4, 4, 128, 2048, 0.0, 0),
+    (2400, 4, 4, 128, 2048, 0.0, 0),   # N = 600: ragged row tiles
+    (1024, 2, 4, 64, 1024, 0.0, 0),
+    (96, 3, 6, 64, 576, 0.0, 0),       # C = 16: rank 0 recomputes 16 leading rows (one 32-row MFMA block)
+    (256, 1, 4, 64, 512, 0.0, 0),      # D = 1: one shard, the plain layer
+    (2048, 4, 4, 128, 2048, 10000.0, 0),  # rotary embedding, heads of 128
+    (1024, 2, 4, 64, 1024, 500.0, 0),     # rotary embedding, heads of 64 (two per 128-column block)
+    (96, 3, 6, 64, 576, 10000.0, 0),      # rotary embedding on the 16 leading rows too
+    (2048, 4, 8, 128, 2048, 0.0, 4),      # grouped K/V: 2 query heads per K/V head, 128-column blocks
+    (2048, 4, 8, 128, 2048, 10000.0, 4),  # grouped K/V with rotation in the epilogue
+    (1024, 2, 4, 64, 1024, 0.0, 2),       # grouped K/V, 64-column K/V parts (element-wise epilogue)
+    (96, 3, 6, 64, 576, 0.0, 3),          # grouped K/V on the 16 leading rows
+    (96, 3, 6, 128, 576, 10000.0, 3),     # grouped K/V and rotation on the 16 leading rows, heads of 128
 ])
-def test_bf16_layer_vs_oracle(torch, S, D, H, Dh, F, rope):
+def test_bf16_layer_vs_oracle(torch, S, D, H, Dh, F, rope, Hkv):
     h = H * Dh
-    shape = synth.LayerShape(S=S, D=D, h=h, H=H, Dh=Dh, F=F, dtype="bf16")
+    shape = synth.LayerShape(S=S, D=D, h=h, H=H, Dh=Dh, F=F, dtype="bf16", Hkv=Hkv)
     w = synth.layer_weights(shape, seed=3, gain="random")
     w64 = _w64(w, "bf16")
     wd = _dev_weights(w, "bf16")
@@ -304,18 +391,19 @@ def test_bf16_layer_vs_oracle(torch, S, D, H, Dh, F, rope):
     k64, v64 = f64(k_rem, "bf16"), f64(v_rem, "bf16")
     for r in sorted({0, D - 1}):
         x = synth.activations(S // D, h, seed=3, tid=100 + r)
-        s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype="bf16", rope_base=rope)
+        s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype="bf16", rope_base=rope, Hkv=Hkv)
         ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
         kf, vf = up(k_rem, "bf16"), up(v_rem, "bf16")
         y = torch.empty((S // D, h), dtype=torch.float32, device="cuda")
-        log(f"bf16 layer S={S} D={D} r={r} H={H} Dh={Dh} F={F} rope={rope}")
+        log(f"bf16 layer S={S} D={D} r={r} H={H} Hkv={Hkv} Dh={Dh} F={F} rope={rope}")
         tsp.tsp_layer_fwd(s, wd, up(x, "f32"), kf, vf, y, tsp.TSP_PHASE_ALL, ws)
         _sync(torch)
-        want = oracle.layer_rank(x, w64, k64, v64, S, D, r, H, Dh, shape.eps, shape.scale, rope_base=rope)
+        want = oracle.layer_rank(x, w64, k64, v64, S, D, r, H, Dh, shape.eps, shape.scale, rope_base=rope,
+                                 Hkv=Hkv or None)
         err = assert_close(down(y), want["y"], TOL_BF16, "y")
         if rope > 0:
             # the output is much closer to the rotated layer than to the plain one
-            plain = oracle.layer_rank(x, w64, k64, v64, S, D, r, H, Dh, shape.eps, shape.scale)["y"]
+            plain = oracle.layer_rank(x, w64, k64, v64, S, D, r, H, Dh, shape.eps, shape.scale, Hkv=Hkv or None)["y"]
             far = float(np.abs(down(y) - plain).max()) / float(np.sqrt(np.mean(want["y"] ** 2)))
             log(f"  distance to the layer without rotation: {far:.3e} rms")
             assert far > 5 * err

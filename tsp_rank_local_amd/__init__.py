@@ -51,7 +51,8 @@ class TspError(RuntimeError):
 class TspShape(ctypes.Structure):
     _fields_ = [("S", ctypes.c_int64), ("D", ctypes.c_int32), ("r", ctypes.c_int32), ("h", ctypes.c_int32),
                 ("H", ctypes.c_int32), ("Dh", ctypes.c_int32), ("F", ctypes.c_int32), ("eps", ctypes.c_float),
-                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("rope_base", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("rope_base", ctypes.c_float),
+                ("Hkv", ctypes.c_int32)]
 
 
 class TspLayerWeights(ctypes.Structure):
@@ -126,14 +127,14 @@ def _stream(stream) -> int | None:
     return torch.cuda.current_stream().cuda_stream
 
 
-def make_shape(S, D, r, h, H, Dh, F, eps=1e-5, scale=None, dtype="bf16", rope_base=0.0) -> TspShape:
+def make_shape(S, D, r, h, H, Dh, F, eps=1e-5, scale=None, dtype="bf16", rope_base=0.0, Hkv=0) -> TspShape:
     """A tsp_shape; dtype 'bf16' or 'f32'; scale defaults to 1/sqrt(Dh);
-    rope_base 0 means no rotary embedding."""
+    rope_base 0 means no rotary embedding; Hkv 0 means Hkv = H (multi-head)."""
     if scale is None:
         scale = 1.0 / float(np.sqrt(Dh))
     dt = {"bf16": TSP_BF16, "f32": TSP_F32}[dtype] if isinstance(dtype, str) else int(dtype)
     return TspShape(int(S), int(D), int(r), int(h), int(H), int(Dh), int(F), float(eps), float(scale), dt,
-                    float(rope_base))
+                    float(rope_base), int(Hkv))
 
 
 def workspace_size(shape: TspShape, which: int) -> int:

@@ -74,10 +74,15 @@ tsp_status check_axis(const tsp_shape *s) {
   return TSP_OK;
 }
 
+// K/V heads of the shape (Hkv = 0 stands for H).
+int32_t kv_heads(const tsp_shape *s) { return s->Hkv ? s->Hkv : s->H; }
+
 tsp_status check_attn_shape(const tsp_shape *s) {
   tsp_status st = check_axis(s);
   if (st) return st;
   if (s->H < 1) return fail(TSP_ERR_INVALID_ARG, "H=%d must be positive", s->H);
+  if (s->Hkv < 0 || kv_heads(s) > s->H || s->H % kv_heads(s) != 0)
+    return fail(TSP_ERR_INVALID_ARG, "Hkv=%d must divide H=%d (0 for Hkv = H)", s->Hkv, s->H);
   if (s->Dh != 64 && s->Dh != 128) return fail(TSP_ERR_UNSUPPORTED, "Dh=%d: only 64 and 128 are supported", s->Dh);
   if ((int64_t)s->H * s->Dh > (1 << 20)) return fail(TSP_ERR_INVALID_ARG, "H*Dh too large");
   if (!isfinite(s->scale) || s->scale < 0.f) return fail(TSP_ERR_INVALID_ARG, "scale must be finite and >= 0");
@@ -99,12 +104,16 @@ tsp_status check_layer_shape(const tsp_shape *s) {
   st = check_mlp_shape(s);
   if (st) return st;
   if (s->H % s->D != 0) return fail(TSP_ERR_INVALID_ARG, "H=%d must be a multiple of D=%d", s->H, s->D);
+  if (kv_heads(s) % s->D != 0)
+    return fail(TSP_ERR_INVALID_ARG, "Hkv=%d must be a multiple of D=%d", kv_heads(s), s->D);
   if (s->h != s->H * s->Dh) return fail(TSP_ERR_INVALID_ARG, "h=%d != H*Dh=%d", s->h, s->H * s->Dh);
   if (!isfinite(s->eps) || s->eps < 0.f) return fail(TSP_ERR_INVALID_ARG, "eps must be finite and >= 0");
   if (!isfinite(s->rope_base) || s->rope_base < 0.f)
     return fail(TSP_ERR_INVALID_ARG, "rope_base must be finite and >= 0");
-  if (s->rope_base > 0.f && s->dtype == TSP_BF16 && (s->h / s->D) % 128 != 0)
-    return fail(TSP_ERR_UNSUPPORTED, "rotary embedding in bf16 needs h/D=%d to be a multiple of 128", s->h / s->D);
+  if (s->rope_base > 0.f && s->dtype == TSP_BF16 &&
+      ((s->h / s->D) % 128 != 0 || (kv_heads(s) / s->D * s->Dh) % 128 != 0))
+    return fail(TSP_ERR_UNSUPPORTED, "rotary embedding in bf16 needs h/D=%d and Hkv*Dh/D=%d to be multiples of 128",
+                s->h / s->D, kv_heads(s) / s->D * s->Dh);
   return TSP_OK;
 }
 
@@ -257,7 +266,7 @@ const char *tsp_status_string(int status) {
 
 const char *tsp_last_error(void) { return g_err.c_str(); }
 
-int tsp_abi_version(void) { return 2; }
+int tsp_abi_version(void) { return 3; }
 
 tsp_status tsp_workspace_size(const tsp_shape *s, int which, size_t *bytes) {
   if (!bytes) return fail(TSP_ERR_INVALID_ARG, "bytes is NULL");
@@ -321,16 +330,17 @@ tsp_status tsp_zigzag_attn_ex(const tsp_shape *s, const void *q, const void *k, 
   const bool q_log2 = (flags & TSP_ATTN_Q_LOG2_SCALED) != 0;
   if (q_log2 && (s->dtype != TSP_BF16 || o_dtype != TSP_BF16))
     return fail(TSP_ERR_UNSUPPORTED, "TSP_ATTN_Q_LOG2_SCALED needs bf16 q and o");
-  const size_t e = elem_bytes(s->dtype), row = (size_t)s->H * s->Dh;
+  const size_t e = elem_bytes(s->dtype), row = (size_t)s->H * s->Dh, kvrow = (size_t)kv_heads(s) * s->Dh;
   const size_t N = (size_t)(s->S / s->D);
   const Range ro{o, N * row * elem_bytes(o_dtype), "o"};
-  const Range ins[] = {{q, N * row * e, "q"}, {k, (size_t)s->S * row * e, "k"}, {v, (size_t)s->S * row * e, "v"}};
+  const Range ins[] = {
+      {q, N * row * e, "q"}, {k, (size_t)s->S * kvrow * e, "k"}, {v, (size_t)s->S * kvrow * e, "v"}};
   for (const Range &r : ins)
     if (overlap(ro, r)) return fail(TSP_ERR_INVALID_ARG, "o overlaps %s", r.name);
   hipStream_t stream = (hipStream_t)stream_;
   TSP_LAUNCH(TSP_K_ATTN,
-             tsp::launch_attention(s->dtype, q, k, v, o, o_dtype, false, s->S, (int32_t)N, s->H, s->Dh, s->scale,
-                                   tsp::make_zigzag(s->S, s->D, s->r), q_log2, stream),
+             tsp::launch_attention(s->dtype, q, k, v, o, o_dtype, false, s->S, (int32_t)N, s->H, kv_heads(s), s->Dh,
+                                   s->scale, tsp::make_zigzag(s->S, s->D, s->r), q_log2, stream),
              "attention");
   return ok();
 }
@@ -379,9 +389,11 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
   const LayerWs L = layer_ws(s);
   if (ws_bytes < L.total) return fail(TSP_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, L.total);
   const int32_t N = (int32_t)(s->S / s->D), h = s->h, D = s->D, hd = h / D, fd = s->F / D;
+  // K/V: Hkv heads, hk = Hkv*Dh/D columns per shard, rows of hkv = Hkv*Dh
+  const int32_t Hkv = kv_heads(s), hkv = Hkv * s->Dh, hk = hkv / D;
   const size_t e = elem_bytes(s->dtype);
   const Range rx{x, (size_t)N * h * 4, "x"}, ry{y, (size_t)N * h * 4, "y"}, rws{ws_, L.total, "ws"};
-  const Range rk{k_full, (size_t)s->S * h * e, "k_full"}, rv{v_full, (size_t)s->S * h * e, "v_full"};
+  const Range rk{k_full, (size_t)s->S * hkv * e, "k_full"}, rv{v_full, (size_t)s->S * hkv * e, "v_full"};
   const Range all[] = {rx, ry, rws, rk, rv};
   for (int i = 0; i < 5; ++i)
     for (int j = i + 1; j < 5; ++j)
@@ -412,19 +424,19 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
     // bf16: Q and K are rotated in the QKV epilogue, before rounding; fp32:
     // in place afterwards
     TSP_LAUNCH(TSP_K_QKV,
-               tsp::launch_qkv(s->dtype, x2, pnl, N, h, to_list(w->wqkv, D), D, hd, qbuf, k_full, v_full, zz, q_scale,
-                               pnl ? rtab : nullptr, s->Dh, stream),
+               tsp::launch_qkv(s->dtype, x2, pnl, N, h, to_list(w->wqkv, D), D, hd, hk, qbuf, k_full, v_full, zz,
+                               q_scale, pnl ? rtab : nullptr, s->Dh, stream),
                "QKV");
     if (rope && !pnl) {
       TSP_LAUNCH(TSP_K_QKV, tsp::launch_rope_rows((float *)qbuf, h, N, s->H, s->Dh, zz, false, rtab, stream),
                  "rotary embedding of Q");
-      TSP_LAUNCH(TSP_K_QKV, tsp::launch_rope_rows((float *)k_full, h, N, s->H, s->Dh, zz, true, rtab, stream),
+      TSP_LAUNCH(TSP_K_QKV, tsp::launch_rope_rows((float *)k_full, hkv, N, Hkv, s->Dh, zz, true, rtab, stream),
                  "rotary embedding of K");
     }
   }
   if (phases & TSP_PHASE_REST) {
     TSP_LAUNCH(TSP_K_ATTN,
-               tsp::launch_attention(s->dtype, qbuf, k_full, v_full, x2, s->dtype, pnl, s->S, N, s->H, s->Dh,
+               tsp::launch_attention(s->dtype, qbuf, k_full, v_full, x2, s->dtype, pnl, s->S, N, s->H, Hkv, s->Dh,
                                      s->scale, zz, pnl, stream),
                "attention");
     TSP_LAUNCH(TSP_K_OUTPROJ,
@@ -448,16 +460,16 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
       TSP_LAUNCH(TSP_K_LEAD, tsp::launch_rmsnorm_f32(x, w->g_attn, s->dtype, la, m, h, s->eps, stream),
                  "leading rows: RMSNorm");
       TSP_LAUNCH(TSP_K_LEAD,
-                 tsp::launch_lead_qkv(la, m, h, to_list(w->wqkv, D), D, hd, lq, lk, lv, zz, lpart, stream),
+                 tsp::launch_lead_qkv(la, m, h, to_list(w->wqkv, D), D, hd, hk, lq, lk, lv, zz, lpart, stream),
                  "leading rows: QKV");
       if (rope) {  // rows 0..m-1 sit at positions 0..m-1, table rows 0..m-1
         TSP_LAUNCH(TSP_K_LEAD, tsp::launch_rope_rows(lq, h, m, s->H, s->Dh, zz, false, rtab, stream),
                    "leading rows: rotary embedding of Q");
-        TSP_LAUNCH(TSP_K_LEAD, tsp::launch_rope_rows(lk, h, m, s->H, s->Dh, zz, false, rtab, stream),
+        TSP_LAUNCH(TSP_K_LEAD, tsp::launch_rope_rows(lk, hkv, m, Hkv, s->Dh, zz, false, rtab, stream),
                    "leading rows: rotary embedding of K");
       }
       TSP_LAUNCH(TSP_K_LEAD,
-                 tsp::launch_lead_attention(lq, lk, lv, lo, m, s->H, s->Dh, s->scale, stream),
+                 tsp::launch_lead_attention(lq, lk, lv, lo, m, s->H, Hkv, s->Dh, s->scale, stream),
                  "leading rows: attention");
       TSP_LAUNCH(TSP_K_LEAD, tsp::launch_lead_outproj(lo, m, h, to_list(w->wo, D), D, hd, x, lh1, lpart, stream),
                  "leading rows: output projection");

@@ -52,6 +52,7 @@ struct AttnArgs {
   void *o;
   int64_t S;
   int32_t n, H;
+  int32_t Hkv, grp;  // K/V heads; query head i reads K/V head i / grp, grp = H / Hkv
   float scale;  // softmax scale
   float c;      // scale * log2(e)
   ZigzagMap zz;
@@ -352,24 +353,25 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
   const int g = lane >> 5, l32 = lane & 31;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int head = L / a.T, p = L - (L / a.T) * a.T;
-  const int64_t rs = (int64_t)a.H * DH;  // row pitch of q, k, v, o (elements)
+  const int64_t rs = (int64_t)a.H * DH;  // row pitch of q and o (elements)
+  const int kvh = head / a.grp;
   const bf16 *qg = reinterpret_cast<const bf16 *>(a.q) + head * DH;
 
   // Copy windows of this wave: window w covers rows w*ROWS_PER_KB.. of the
   // tile; lane -> (row, chunk position); it loads the logical chunk that
   // belongs at that position.
   KvCopy<DH> cp;
-  cp.kg = reinterpret_cast<const bf16 *>(a.k) + head * DH;
-  cp.vg = reinterpret_cast<const bf16 *>(a.v) + head * DH;
+  cp.kg = reinterpret_cast<const bf16 *>(a.k) + kvh * DH;
+  cp.vg = reinterpret_cast<const bf16 *>(a.v) + kvh * DH;
   cp.S = a.S;
-  cp.rs = rs;
+  cp.rs = (int64_t)a.Hkv * DH;
   cp.wave = wave;
 #pragma unroll
   for (int i = 0; i < G::WIN_PER_WAVE; ++i) {
     const int win = wave * G::WIN_PER_WAVE + i;
     const int row = win * G::ROWS_PER_KB + lane / G::CPR, pos = lane % G::CPR;
-    cp.k_off[i] = (int)(row * rs * 2) + G::k_swz(row, pos) * 16;
-    cp.v_off[i] = (int)(row * rs * 2) + G::v_swz(row, pos) * 16;
+    cp.k_off[i] = (int)(row * cp.rs * 2) + G::k_swz(row, pos) * 16;
+    cp.v_off[i] = (int)(row * cp.rs * 2) + G::v_swz(row, pos) * 16;
   }
 
   const FragAddr<DH> fa = frag_addr<DH>(lane);
@@ -474,10 +476,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   const int last_row = min(a.n - 1, (int)blockIdx.x * 64 + 63);
   const int max_pos = a.zz.pos(last_row);  // positions grow with the local row
   const int qpos = a.zz.pos(valid ? row : last_row);
-  const int64_t rs = (int64_t)a.H * DH;
+  const int64_t rs = (int64_t)a.H * DH, kvs = (int64_t)a.Hkv * DH;  // row pitches: q and o, k and v
   const float *q = reinterpret_cast<const float *>(a.q) + head * DH;
-  const float *k = reinterpret_cast<const float *>(a.k) + head * DH;
-  const float *v = reinterpret_cast<const float *>(a.v) + head * DH;
+  const float *k = reinterpret_cast<const float *>(a.k) + (head / a.grp) * DH;
+  const float *v = reinterpret_cast<const float *>(a.v) + (head / a.grp) * DH;
   float qv[DH], ov[DH];
 #pragma unroll
   for (int d = 0; d < DH; ++d) {
@@ -488,8 +490,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   for (int k0 = 0; k0 <= max_pos; k0 += 64) {
     const int64_t key = k0 + tid;
     for (int d = 0; d < DH; ++d) {
-      Ks[tid][d] = key < a.S ? k[key * rs + d] : 0.f;
-      Vs[tid][d] = key < a.S ? v[key * rs + d] : 0.f;
+      Ks[tid][d] = key < a.S ? k[key * kvs + d] : 0.f;
+      Vs[tid][d] = key < a.S ? v[key * kvs + d] : 0.f;
     }
     __syncthreads();
     const int nk = min(64, qpos - k0 + 1);
@@ -517,9 +519,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 }
 
 hipError_t launch_attention(int dtype, const void *q, const void *k, const void *v, void *o, int o_dtype,
-                            bool o_panel, int64_t S, int32_t n, int32_t H, int32_t Dh, float scale, ZigzagMap zz,
-                            bool q_prescaled, hipStream_t s) {
+                            bool o_panel, int64_t S, int32_t n, int32_t H, int32_t Hkv, int32_t Dh, float scale,
+                            ZigzagMap zz, bool q_prescaled, hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  if (Hkv < 1 || H % Hkv != 0) return hipErrorInvalidValue;
   if (o_panel && (dtype != TSP_BF16 || o_dtype != TSP_BF16)) return hipErrorInvalidValue;
   if (q_prescaled && (dtype != TSP_BF16 || o_dtype != TSP_BF16)) return hipErrorInvalidValue;
   AttnArgs a{};
@@ -530,6 +533,8 @@ hipError_t launch_attention(int dtype, const void *q, const void *k, const void 
   a.S = S;
   a.n = n;
   a.H = H;
+  a.Hkv = Hkv;
+  a.grp = H / Hkv;
   a.scale = scale;
   // Multiplier of the scores in the exp2 domain. Kept at least the smallest
   // normal float, so that masked scores (-inf) still give 0 with a zero scale;

@@ -161,26 +161,26 @@ struct EpiAddF32 {
   __device__ __forceinline__ void put_row(const Row &w, const float4 (&v)[4][4]) const { put_each(*this, w, v); }
 };
 
-// Shard z of the QKV projection: output column c of the shard falls in part
-// c / hd (0 = Q, 1 = K, 2 = V), head-group feature c % hd, i.e. global feature
-// z*hd + c % hd. Q stays in local row order; K and V go to the global row of
-// the token. (Four consecutive columns never straddle parts: hd % 4 == 0.)
+// Shard z of the QKV projection: its output columns are hq Q columns (H/D
+// heads), then hk K and hk V columns (Hkv/D heads). Q column c is global
+// feature z*hq + c of q [n][ldq], in local row order; K/V column c is feature
+// z*hk + c of kf/vf [S][ldkv] at the token's global row. (Four consecutive
+// columns never straddle parts: hq and hk are multiples of 4.)
 template <typename T>
 struct EpiQKV {
   T *q, *k, *v;
-  int64_t h;
-  int32_t hd;
+  int64_t ldq, ldkv;
+  int32_t hq, hk;
   ZigzagMap zz;
   float q_scale;       // factor applied to the Q part before rounding
   const float2 *rope;  // rotary table [local row][dh/2] (cos, sin), or null
   int32_t dh;          // head width (64 or 128) when rope is set
   __device__ __forceinline__ T *dst(int z, int r, int c) const {
-    const int part = c / hd;
-    const int64_t col = (int64_t)z * hd + (c - part * hd);
-    if (part == 0) return q + (int64_t)r * h + col;
-    return (part == 1 ? k : v) + (int64_t)zz.pos(r) * h + col;
+    if (c < hq) return q + (int64_t)r * ldq + (int64_t)z * hq + c;
+    const int kc = c - hq, part = kc >= hk;
+    return (part ? v : k) + (int64_t)zz.pos(r) * ldkv + (int64_t)z * hk + (kc - part * hk);
   }
-  __device__ __forceinline__ float factor(int c) const { return c < hd ? q_scale : 1.0f; }
+  __device__ __forceinline__ float factor(int c) const { return c < hq ? q_scale : 1.0f; }
   __device__ __forceinline__ void operator()(int z, int r, int c, float val) const {
     *dst(z, r, c) = (T)(val * factor(c));
   }
@@ -188,16 +188,16 @@ struct EpiQKV {
     const float f = factor(c);
     store4(dst(z, r, c), make_float4(val.x * f, val.y * f, val.z * f, val.w * f));
   }
-  // whole 128-column blocks stay inside one part when hd is a multiple of
-  // 128, and then also hold whole heads
+  // whole 128-column blocks stay inside one part when hq and hk are
+  // multiples of 128, and then also hold whole heads
   struct Row {
     T *p;
     float f;
     const float2 *rot;  // this row's rotary table when the block is Q or K
   };
-  __device__ __forceinline__ bool fast_ok() const { return (hd & 127) == 0; }
+  __device__ __forceinline__ bool fast_ok() const { return ((hq | hk) & 127) == 0; }
   __device__ __forceinline__ Row row(int z, int r, int c0, int g) const {
-    const bool rotate = rope != nullptr && c0 < 2 * hd;
+    const bool rotate = rope != nullptr && c0 < hq + hk;
     return Row{dst(z, r, c0 + 4 * g), factor(c0), rotate ? rope + (int64_t)r * (dh / 2) : nullptr};
   }
   __device__ __forceinline__ void put(const Row &w, int i, int vq, float4 v) const {
@@ -727,13 +727,13 @@ size_t lead_part_bytes(int32_t m, int32_t h, int32_t F, int32_t D) {
   return 4 * std::max(std::max(qkv, op), std::max(up, dn));
 }
 
-hipError_t launch_lead_qkv(const float *a, int32_t m, int32_t h, const PtrList &w, int32_t D, int32_t hd, float *q,
-                           float *k, float *v, ZigzagMap zz, float *part, hipStream_t s) {
-  GemmArgs g = lead_args(a, h, m, 3 * hd, h);
+hipError_t launch_lead_qkv(const float *a, int32_t m, int32_t h, const PtrList &w, int32_t D, int32_t hq, int32_t hk,
+                           float *q, float *k, float *v, ZigzagMap zz, float *part, hipStream_t s) {
+  GemmArgs g = lead_args(a, h, m, hq + 2 * hk, h);
   g.B = w;
   g.ldb = h;
   g.nz = D;
-  EpiQKV<float> e{q, k, v, h, hd, zz, 1.0f, nullptr, 0};
+  EpiQKV<float> e{q, k, v, (int64_t)D * hq, (int64_t)D * hk, hq, hk, zz, 1.0f, nullptr, 0};
   return run_lead(g, e, part, s);
 }
 
@@ -804,18 +804,19 @@ static GemmArgs make_args(const void *A, int64_t lda, bool a_panel, int32_t M, i
 }
 
 hipError_t launch_qkv(int dtype, const void *xn, bool a_panel, int32_t n, int32_t h, const PtrList &w, int32_t D,
-                      int32_t hd, void *q, void *kf, void *vf, ZigzagMap zz, float q_scale, const float2 *rope,
-                      int32_t Dh, hipStream_t s) {
-  if (rope != nullptr && (dtype != TSP_BF16 || (hd & 127) != 0)) return hipErrorInvalidValue;
-  GemmArgs a = make_args(xn, h, a_panel, n, 3 * hd, h);
+                      int32_t hq, int32_t hk, void *q, void *kf, void *vf, ZigzagMap zz, float q_scale,
+                      const float2 *rope, int32_t Dh, hipStream_t s) {
+  if (rope != nullptr && (dtype != TSP_BF16 || ((hq | hk) & 127) != 0)) return hipErrorInvalidValue;
+  GemmArgs a = make_args(xn, h, a_panel, n, hq + 2 * hk, h);
   a.B = w;
   a.ldb = h;
   a.nz = D;
+  const int64_t ldq = (int64_t)D * hq, ldkv = (int64_t)D * hk;
   if (dtype == TSP_BF16) {
-    EpiQKV<bf16> e{(bf16 *)q, (bf16 *)kf, (bf16 *)vf, h, hd, zz, q_scale, rope, Dh};
+    EpiQKV<bf16> e{(bf16 *)q, (bf16 *)kf, (bf16 *)vf, ldq, ldkv, hq, hk, zz, q_scale, rope, Dh};
     return run_gemm(dtype, a, e, s);
   }
-  EpiQKV<float> e{(float *)q, (float *)kf, (float *)vf, h, hd, zz, q_scale, nullptr, 0};
+  EpiQKV<float> e{(float *)q, (float *)kf, (float *)vf, ldq, ldkv, hq, hk, zz, q_scale, nullptr, 0};
   return run_gemm(dtype, a, e, s);
 }
 

@@ -13,21 +13,23 @@ namespace tsp {
 // leading rows of rank 0, whose keys are exactly those rows): one block per
 // head, K and V of the m rows staged in LDS, four threads per query, each
 // scoring 16 keys and later producing a quarter of the output features.
-// q, k, v, o: [m][H][DH] fp32.
+// q, o: [m][H][DH] fp32; k, v: [m][Hkv][DH] fp32, query head i reading K/V
+// head i / (H / Hkv).
 template <int DH>
 __global__ __launch_bounds__(256) void lead_attn_kernel(const float *__restrict__ q, const float *__restrict__ k,
                                                         const float *__restrict__ v, float *__restrict__ o, int m,
-                                                        int H, float scale) {
+                                                        int H, int Hkv, float scale) {
   __shared__ __attribute__((aligned(16))) float KP[64 * DH];  // K rows, later P [64][64]
   __shared__ __attribute__((aligned(16))) float Vs[64 * DH];
   const int head = blockIdx.x, tid = threadIdx.x;
-  const int64_t rs = (int64_t)H * DH;
+  const int kvh = head / (H / Hkv);
+  const int64_t rs = (int64_t)H * DH, kvs = (int64_t)Hkv * DH;
   for (int e = tid * 4; e < 64 * DH; e += 1024) {
     const int r = e / DH, d = e - r * DH;
     float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
     if (r < m) {
-      kv = *reinterpret_cast<const float4 *>(k + r * rs + head * DH + d);
-      vv = *reinterpret_cast<const float4 *>(v + r * rs + head * DH + d);
+      kv = *reinterpret_cast<const float4 *>(k + r * kvs + kvh * DH + d);
+      vv = *reinterpret_cast<const float4 *>(v + r * kvs + kvh * DH + d);
     }
     *reinterpret_cast<float4 *>(&KP[e]) = kv;
     *reinterpret_cast<float4 *>(&Vs[e]) = vv;
@@ -90,13 +92,13 @@ __global__ __launch_bounds__(256) void lead_attn_kernel(const float *__restrict_
 }
 
 hipError_t launch_lead_attention(const float *q, const float *k, const float *v, float *o, int32_t m, int32_t H,
-                                 int32_t Dh, float scale, hipStream_t s) {
+                                 int32_t Hkv, int32_t Dh, float scale, hipStream_t s) {
   if (m <= 0) return hipSuccess;
-  if (m > 64) return hipErrorInvalidValue;
+  if (m > 64 || Hkv < 1 || H % Hkv != 0) return hipErrorInvalidValue;
   if (Dh == 128)
-    hipLaunchKernelGGL((lead_attn_kernel<128>), dim3(H), dim3(256), 0, s, q, k, v, o, m, H, scale);
+    hipLaunchKernelGGL((lead_attn_kernel<128>), dim3(H), dim3(256), 0, s, q, k, v, o, m, H, Hkv, scale);
   else
-    hipLaunchKernelGGL((lead_attn_kernel<64>), dim3(H), dim3(256), 0, s, q, k, v, o, m, H, scale);
+    hipLaunchKernelGGL((lead_attn_kernel<64>), dim3(H), dim3(256), 0, s, q, k, v, o, m, H, Hkv, scale);
   return hipGetLastError();
 }
 

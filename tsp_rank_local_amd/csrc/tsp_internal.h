@@ -65,14 +65,15 @@ hipError_t launch_rope_rows(float *x, int64_t ld, int32_t n, int32_t H, int32_t 
 // ---------------------------------------------------------------- GEMMs
 // All products are C = A B^T with A [M][K] and B [N][K] (both K-contiguous).
 // a_panel: A in panel layout (bf16 only; panel stride M * 64), else row-major.
-// QKV of every attention shard in one launch: shard z reads w[z] [3hd][h];
-// Q columns go to q [N][h] at column z*hd (multiplied by q_scale before
-// rounding), K/V rows go to kf/vf [S][h] at row zz.pos(t), column z*hd.
-// rope (bf16 only, hd % 128 == 0): when not null, Q and K are rotated with
-// the table of launch_rope_table (heads of Dh) before rounding.
+// QKV of every attention shard in one launch: shard z reads w[z]
+// [hq + 2hk][h] (hq Q rows, hk K rows, hk V rows); Q columns go to q
+// [n][D*hq] at column z*hq (multiplied by q_scale before rounding), K/V rows
+// go to kf/vf [S][D*hk] at row zz.pos(t), column z*hk.
+// rope (bf16 only, hq and hk multiples of 128): when not null, Q and K are
+// rotated with the table of launch_rope_table (heads of Dh) before rounding.
 hipError_t launch_qkv(int dtype, const void *xn, bool a_panel, int32_t n, int32_t h, const PtrList &w, int32_t D,
-                      int32_t hd, void *q, void *kf, void *vf, ZigzagMap zz, float q_scale, const float2 *rope,
-                      int32_t Dh, hipStream_t s);
+                      int32_t hq, int32_t hk, void *q, void *kf, void *vf, ZigzagMap zz, float q_scale,
+                      const float2 *rope, int32_t Dh, hipStream_t s);
 // y = x + sum_j o[:, j*hd:(j+1)*hd] wo[j]^T, shards walked j = 0..D-1 inside
 // the reduction loop.
 hipError_t launch_outproj(int dtype, const void *o, bool a_panel, int32_t n, int32_t h, const PtrList &wo,
@@ -90,12 +91,13 @@ hipError_t launch_mlp_down(int dtype, const void *hid, bool a_panel, int32_t n, 
 
 // Leading rows in fp32: the same products for m <= kLeadRows rows with fp32
 // activations (row-major) and the bf16 weights, computed to fp32 accuracy.
-// part: scratch of lead_part_bytes(m, h, F, D) bytes. QKV writes fp32 q
-// [m][h] and k/v rows zz.pos(t) of [*][h] buffers (no Q factor).
+// part: scratch of lead_part_bytes(m, h, F, D) bytes (enough for any
+// hk <= hq). QKV writes fp32 q [m][D*hq] and k/v rows zz.pos(t) of
+// [*][D*hk] buffers (no Q factor).
 constexpr int32_t kLeadRows = 64;
 size_t lead_part_bytes(int32_t m, int32_t h, int32_t F, int32_t D);
-hipError_t launch_lead_qkv(const float *a, int32_t m, int32_t h, const PtrList &w, int32_t D, int32_t hd, float *q,
-                           float *k, float *v, ZigzagMap zz, float *part, hipStream_t s);
+hipError_t launch_lead_qkv(const float *a, int32_t m, int32_t h, const PtrList &w, int32_t D, int32_t hq, int32_t hk,
+                           float *q, float *k, float *v, ZigzagMap zz, float *part, hipStream_t s);
 hipError_t launch_lead_outproj(const float *o, int32_t m, int32_t h, const PtrList &wo, int32_t D, int32_t hd,
                                const float *x, float *y, float *part, hipStream_t s);
 hipError_t launch_lead_mlp_up(const float *a, int32_t m, int32_t h, const PtrList &w1, int32_t D, int32_t fd,
@@ -104,17 +106,19 @@ hipError_t launch_lead_mlp_down(const float *hid, int32_t m, const PtrList &w2, 
                                 const float *res, float *y, float *part, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
-// o: [n][H][Dh] in o_dtype, or (bf16 o only) panel layout of [n][H*Dh] when
-// o_panel. q_prescaled (bf16 q and o only): q already holds
-// q * scale * log2(e), as launch_qkv writes it with that q_scale.
+// q: [n][H][Dh]; k, v: [S][Hkv][Dh], query head i reading K/V head
+// i / (H / Hkv) (H % Hkv == 0). o: [n][H][Dh] in o_dtype, or (bf16 o only)
+// panel layout of [n][H*Dh] when o_panel. q_prescaled (bf16 q and o only): q
+// already holds q * scale * log2(e), as launch_qkv writes it with that
+// q_scale.
 hipError_t launch_attention(int dtype, const void *q, const void *k, const void *v, void *o, int o_dtype,
-                            bool o_panel, int64_t S, int32_t n, int32_t H, int32_t Dh, float scale, ZigzagMap zz,
-                            bool q_prescaled, hipStream_t s);
+                            bool o_panel, int64_t S, int32_t n, int32_t H, int32_t Hkv, int32_t Dh, float scale,
+                            ZigzagMap zz, bool q_prescaled, hipStream_t s);
 // fp32 attention of the first m <= 64 positions among themselves (the
-// leading rows of rank 0): q, k, v, o [m][H][Dh] fp32, key j visible to query
-// i when j <= i.
+// leading rows of rank 0): q, o [m][H][Dh], k, v [m][Hkv][Dh] fp32, key j
+// visible to query i when j <= i.
 hipError_t launch_lead_attention(const float *q, const float *k, const float *v, float *o, int32_t m, int32_t H,
-                                 int32_t Dh, float scale, hipStream_t s);
+                                 int32_t Hkv, int32_t Dh, float scale, hipStream_t s);
 
 // ---------------------------------------------------------------- timing
 // Bracket a launch with events when profiling is on (api.cpp).
