@@ -44,17 +44,24 @@ Readings where the pages are silent (each is restated where it is used):
      multi-head): Hkv K/V heads, each shared by H/Hkv consecutive query heads
      (query head i reads K/V head i // (H/Hkv)); shard j then holds query
      heads j*H/D.. and K/V heads j*Hkv/D.. Hkv = H is multi-head attention.
+  R9 gated MLP (an optional variant; the pages' MLP is R5): the hidden layer
+     is SiLU(x W_g^T) * (x W_u^T), elementwise, with SiLU(z) = z / (1 + e^-z)
+     (the SwiGLU form of common 7B models), then W_2 as in R5. Shard j holds
+     hidden units j*F/D..(j+1)*F/D-1: its first matrix stacks the W_g rows of
+     those units on the W_u rows of the same units, [2F/D, h].
 """
 from __future__ import annotations
 
 import numpy as np
 from scipy.special import erf as _erf
+from scipy.special import expit as _expit
 
 __all__ = [
     "zigzag_positions",
     "zigzag_owner",
     "rms_norm",
     "gelu",
+    "silu",
     "causal_attention",
     "rope",
     "unshard_attention_weights",
@@ -115,6 +122,13 @@ def gelu(z) -> np.ndarray:
     """Exact GELU, z * Phi(z) = z * (1 + erf(z / sqrt 2)) / 2 (reading R5)."""
     z = _f64(z)
     return 0.5 * z * (1.0 + _erf(z / np.sqrt(2.0)))
+
+
+def silu(z) -> np.ndarray:
+    """SiLU, z * sigma(z) = z / (1 + e^-z) (reading R9); sigma from scipy's
+    expit, which does not overflow for large |z|."""
+    z = _f64(z)
+    return z * _expit(z)
 
 
 def causal_attention(q, k, v, q_pos, scale: float, row_block: int = 256) -> np.ndarray:
@@ -192,43 +206,59 @@ def unshard_attention_weights(wqkv, wo, H: int, Dh: int, Hkv: int | None = None)
     return wq, wk, wv, w_o
 
 
-def unshard_mlp_weights(w1, w2):
-    """Rebuild W1 [F, h] and W2 [h, F] (out, in) from the D shards (reading R5)."""
-    return np.concatenate([_f64(w) for w in w1], axis=0), np.concatenate([_f64(w) for w in w2], axis=1)
+def unshard_mlp_weights(w1, w2, gated: bool = False):
+    """Rebuild W1 [F, h] and W2 [h, F] (out, in) from the D shards (reading
+    R5). gated: returns W_g, W_u [F, h] and W2 instead (reading R9: shard j's
+    first matrix is its W_g rows above its W_u rows)."""
+    W2 = np.concatenate([_f64(w) for w in w2], axis=1)
+    if not gated:
+        return np.concatenate([_f64(w) for w in w1], axis=0), W2
+    halves = [np.split(_f64(w), 2, axis=0) for w in w1]
+    return np.concatenate([g for g, _ in halves], axis=0), np.concatenate([u for _, u in halves], axis=0), W2
 
 
 # --------------------------------------------------------------------------
 # MLP
 # --------------------------------------------------------------------------
-def mlp(x, w1, w2) -> np.ndarray:
-    """Unsharded MLP branch GELU(x W1^T) W2^T from lists of shards (reading R5).
+def mlp(x, w1, w2, gated: bool = False) -> np.ndarray:
+    """Unsharded MLP branch GELU(x W1^T) W2^T from lists of shards (reading
+    R5), or with gated, (SiLU(x W_g^T) * (x W_u^T)) W2^T (reading R9).
 
     [P2] paragraphs 2 and 4: the ring applies each shard to the local tokens
     and sums the contributions without an all-reduce; this is the unsharded
     quantity that sum must equal.
     """
+    x = _f64(x)
+    if gated:
+        Wg, Wu, W2 = unshard_mlp_weights(w1, w2, gated=True)
+        return (silu(x @ Wg.T) * (x @ Wu.T)) @ W2.T
     W1, W2 = unshard_mlp_weights(w1, w2)
-    return gelu(_f64(x) @ W1.T) @ W2.T
+    return gelu(x @ W1.T) @ W2.T
 
 
-def mlp_shard(x, w1_j, w2_j) -> np.ndarray:
-    """One shard's contribution GELU(x W1_j^T) W2_j^T (reading R5)."""
-    return gelu(_f64(x) @ _f64(w1_j).T) @ _f64(w2_j).T
+def mlp_shard(x, w1_j, w2_j, gated: bool = False) -> np.ndarray:
+    """One shard's contribution GELU(x W1_j^T) W2_j^T (reading R5), or the
+    gated form of reading R9."""
+    x = _f64(x)
+    if gated:
+        wg, wu = np.split(_f64(w1_j), 2, axis=0)
+        return (silu(x @ wg.T) * (x @ wu.T)) @ _f64(w2_j).T
+    return gelu(x @ _f64(w1_j).T) @ _f64(w2_j).T
 
 
 # --------------------------------------------------------------------------
 # Whole layer
 # --------------------------------------------------------------------------
 def layer_full(x, w: dict, H: int, Dh: int, eps: float, scale: float, rope_base: float = 0.0,
-               Hkv: int | None = None) -> dict:
+               Hkv: int | None = None, gated: bool = False) -> dict:
     """Unsharded pre-norm decoder layer over the whole sequence (reading R6).
 
     x: [S, h] in global order. w: the shard lists wqkv, wo, w1, w2 and gains
     g_attn, g_mlp. TSP rearranges this computation over ranks and shards but
     reaches the same values ([P2] paragraphs 1-2), so this is what every rank
     must reproduce for its own rows. rope_base > 0 rotates Q and K (reading
-    R7); Hkv < H groups the K/V heads (R8). Returns y and the intermediates h1,
-    q, k, v, o.
+    R7); Hkv < H groups the K/V heads (R8); gated selects the gated MLP (R9).
+    Returns y and the intermediates h1, q, k, v, o.
     """
     x = _f64(x)
     S = x.shape[0]
@@ -241,12 +271,12 @@ def layer_full(x, w: dict, H: int, Dh: int, eps: float, scale: float, rope_base:
     o = causal_attention(q, k, v, np.arange(S), scale)
     h1 = x + o.reshape(S, H * Dh) @ w_o.T
     m = rms_norm(h1, w["g_mlp"], eps)
-    y = h1 + mlp(m, w["w1"], w["w2"])
+    y = h1 + mlp(m, w["w1"], w["w2"], gated)
     return {"y": y, "h1": h1, "q": q, "k": k, "v": v, "o": o}
 
 
 def layer_rows(x_rows, pos_rows, w: dict, k_all, v_all, H: int, Dh: int, eps: float, scale: float,
-               rope_base: float = 0.0, Hkv: int | None = None) -> dict:
+               rope_base: float = 0.0, Hkv: int | None = None, gated: bool = False) -> dict:
     """Layer output for given token rows once the full K/V are gathered (R6).
 
     x_rows: [m, h] tokens, pos_rows: [m] their global positions, k_all, v_all:
@@ -254,7 +284,7 @@ def layer_rows(x_rows, pos_rows, w: dict, k_all, v_all, H: int, Dh: int, eps: fl
     Every row is independent of the others here: RMSNorm, its query, its
     causal attention, the output projection, RMSNorm and the MLP. With
     rope_base > 0 the query is rotated at its position (k_all holds rotated
-    keys, reading R7).
+    keys, reading R7); gated selects the gated MLP (R9).
     """
     x_rows = _f64(x_rows)
     m = x_rows.shape[0]
@@ -264,7 +294,7 @@ def layer_rows(x_rows, pos_rows, w: dict, k_all, v_all, H: int, Dh: int, eps: fl
     o = causal_attention(q, k_all, v_all, pos_rows, scale)
     h1 = x_rows + o.reshape(m, H * Dh) @ w_o.T
     mm = rms_norm(h1, w["g_mlp"], eps)
-    y = h1 + mlp(mm, w["w1"], w["w2"])
+    y = h1 + mlp(mm, w["w1"], w["w2"], gated)
     return {"y": y, "h1": h1}
 
 
@@ -285,7 +315,7 @@ def local_kv(x_local, w: dict, H: int, Dh: int, eps: float, pos=None, rope_base:
 
 def layer_rank(x_local, w: dict, k_full, v_full, S: int, D: int, r: int,
                H: int, Dh: int, eps: float, scale: float, rows=None, rope_base: float = 0.0,
-               Hkv: int | None = None) -> dict:
+               Hkv: int | None = None, gated: bool = False) -> dict:
     """Rank r's layer output for its S/D local tokens (reading R6).
 
     x_local: [S/D, h] rank r's tokens in local zigzag order (R1). k_full,
@@ -294,8 +324,8 @@ def layer_rank(x_local, w: dict, k_full, v_full, S: int, D: int, r: int,
     from x_local, the rest are used as given. rows: optional subset of local
     rows whose output is wanted (all local rows still produce K/V, since any
     later query may attend to them). rope_base > 0 rotates Q and K (R7; the
-    given remote K rows are taken as already rotated). Returns y [len(rows),
-    h] and h1.
+    given remote K rows are taken as already rotated); gated selects the gated
+    MLP (R9). Returns y [len(rows), h] and h1.
     """
     x_local = _f64(x_local)
     n = x_local.shape[0]
@@ -308,6 +338,6 @@ def layer_rank(x_local, w: dict, k_full, v_full, S: int, D: int, r: int,
     v_all = np.array(v_full, dtype=np.float64, copy=True)
     k_all[pos] = k_loc
     v_all[pos] = v_loc
-    out = layer_rows(x_local[rows], pos[rows], w, k_all, v_all, H, Dh, eps, scale, rope_base, Hkv)
+    out = layer_rows(x_local[rows], pos[rows], w, k_all, v_all, H, Dh, eps, scale, rope_base, Hkv, gated)
     out["pos"] = pos[rows]
     return out

@@ -209,7 +209,8 @@ def _torch_rope(t, base):
     return torch.cat([zr.real, zr.imag], dim=-1)
 
 
-def _torch_layer(x, wq, wk, wv, wo, W1, W2, g1, g2, H, Dh, eps, scale, rope_base=0.0):
+def _torch_layer(x, wq, wk, wv, wo, W1, W2, g1, g2, H, Dh, eps, scale, rope_base=0.0, Wu=None):
+    """torch fp64 layer; with Wu given, W1 is the gate matrix of a SwiGLU MLP."""
     tx = torch.from_numpy(x)
     S, h = x.shape
     a = F.rms_norm(tx, (h,), torch.from_numpy(g1), eps=eps)
@@ -220,7 +221,11 @@ def _torch_layer(x, wq, wk, wv, wo, W1, W2, g1, g2, H, Dh, eps, scale, rope_base
     o = F.scaled_dot_product_attention(q, k, heads(wv), is_causal=True, scale=scale)
     h1 = tx + F.linear(o.permute(1, 0, 2).reshape(S, h), torch.from_numpy(wo))
     m = F.rms_norm(h1, (h,), torch.from_numpy(g2), eps=eps)
-    return (h1 + F.linear(F.gelu(F.linear(m, torch.from_numpy(W1))), torch.from_numpy(W2))).numpy()
+    if Wu is not None:
+        hid = F.silu(F.linear(m, torch.from_numpy(W1))) * F.linear(m, torch.from_numpy(Wu))
+    else:
+        hid = F.gelu(F.linear(m, torch.from_numpy(W1)))
+    return (h1 + F.linear(hid, torch.from_numpy(W2))).numpy()
 
 
 def _tiny_layer(seed, S=64, D=4, H=4, Dh=8, Fw=128):
@@ -380,6 +385,86 @@ def test_gqa_layer_equals_mha_with_repeated_kv_heads():
 
 
 # ---------------------------------------------------------------- planted mistakes
+# ---------------------------------------------------------------- gated MLP (R9)
+def test_silu_closed_forms_and_identities():
+    # sigma(ln 3) = 1 / (1 + 1/3) = 3/4 and sigma(-ln 3) = 1/4, so SiLU there
+    # is (3/4) ln 3 and -(1/4) ln 3; sigma(0) = 1/2 gives SiLU(0) = 0
+    l3 = math.log(3.0)
+    got = oracle.silu(np.array([0.0, l3, -l3]))
+    assert np.allclose(got, [0.0, 0.75 * l3, -0.25 * l3], rtol=0, atol=1e-15)
+    z = np.linspace(-30, 30, 241)
+    # SiLU(z) - SiLU(-z) = z (sigma(z) + sigma(-z) = 1)
+    assert np.allclose(oracle.silu(z) - oracle.silu(-z), z, atol=1e-13)
+    # far tails: z and 0, without overflow
+    with np.errstate(all="raise"):
+        big = oracle.silu(np.array([-800.0, 800.0]))
+    assert big[0] == 0.0 and big[1] == 800.0
+    assert np.allclose(oracle.silu(z), F.silu(torch.from_numpy(z)).numpy(), atol=1e-14)
+
+
+def _split_gated(Wg, Wu, W2, D):
+    """Shard j of a gated MLP: its W_g rows above its W_u rows (reading R9)."""
+    f = Wg.shape[0] // D
+    w1 = [np.concatenate([Wg[j * f:(j + 1) * f], Wu[j * f:(j + 1) * f]]) for j in range(D)]
+    return w1, [W2[:, j * f:(j + 1) * f] for j in range(D)]
+
+
+def test_gated_mlp_vs_torch_and_shard_sum():
+    rng = np.random.default_rng(41)
+    n, h, Fw, D = 9, 16, 64, 4
+    x = rng.standard_normal((n, h))
+    Wg, Wu = 0.3 * rng.standard_normal((2, Fw, h))
+    W2 = 0.3 * rng.standard_normal((h, Fw))
+    w1, w2 = _split_gated(Wg, Wu, W2, D)
+    got = oracle.mlp(x, w1, w2, gated=True)
+    tx = torch.from_numpy(x)
+    ref = F.linear(F.silu(F.linear(tx, torch.from_numpy(Wg))) * F.linear(tx, torch.from_numpy(Wu)),
+                   torch.from_numpy(W2)).numpy()
+    assert np.allclose(got, ref, atol=1e-13)
+    for r in range(D):
+        acc = np.zeros_like(got)
+        for t in range(D):
+            j = (r - t) % D
+            acc += oracle.mlp_shard(x, w1[j], w2[j], gated=True)
+        assert np.allclose(acc, got, atol=1e-13)
+    # the plain MLP on the same numbers is something else
+    assert not np.allclose(oracle.mlp(x, [a[:Fw // D] for a in w1], w2), got, atol=1e-3)
+
+
+def test_gated_layer_vs_torch_and_rank_views():
+    """The gated layer against a torch fp64 layer at D = 1, and every rank's
+    view against the unsharded layer, with rotation and grouped K/V too."""
+    S, D, H, Dh, eps, Fw = 64, 4, 4, 8, 1e-5, 128
+    scale = 1 / math.sqrt(Dh)
+    x, w, m = _tiny_layer(43, S=S, D=D, H=H, Dh=Dh, Fw=Fw)
+    rng = np.random.default_rng(44)
+    Wu = 0.2 * rng.standard_normal((Fw, H * Dh))
+    w1, _ = _split_gated(m["W1"], Wu, m["W2"], D)
+    wg = dict(w, w1=w1)
+    ref = _torch_layer(x, m["wq"], m["wk"], m["wv"], m["wo"], m["W1"], m["W2"], m["g1"], m["g2"], H, Dh, eps, scale,
+                       Wu=Wu)
+    full = oracle.layer_full(x, wg, H, Dh, eps, scale, gated=True)
+    assert np.allclose(full["y"], ref, atol=1e-12)
+    for r in range(D):
+        pos = oracle.zigzag_positions(S, D, r)
+        out = oracle.layer_rank(x[pos], wg, full["k"], full["v"], S, D, r, H, Dh, eps, scale, gated=True)
+        assert np.allclose(out["y"], full["y"][pos], atol=1e-12)
+    # composed with rotation and 2 K/V heads (D = 2)
+    D2, Hkv = 2, 2
+    x2, m2, _, _ = _gqa_layer(45, S, D2, H, Hkv, Dh)
+    Wg2, Wu2 = 0.2 * rng.standard_normal((2, 96, H * Dh))
+    W22 = 0.2 * rng.standard_normal((H * Dh, 96))
+    g1, g2 = _split_gated(Wg2, Wu2, W22, D2)
+    wqkv, wos = _split_attention(m2["wq"], m2["wk"], m2["wv"], m2["wo"], D2, H, Dh, Hkv)
+    wc = dict(wqkv=wqkv, wo=wos, w1=g1, w2=g2, g_attn=m2["g1"], g_mlp=m2["g2"])
+    fc = oracle.layer_full(x2, wc, H, Dh, eps, scale, rope_base=50.0, Hkv=Hkv, gated=True)
+    for r in range(D2):
+        pos = oracle.zigzag_positions(S, D2, r)
+        out = oracle.layer_rank(x2[pos], wc, fc["k"], fc["v"], S, D2, r, H, Dh, eps, scale, rope_base=50.0, Hkv=Hkv,
+                                gated=True)
+        assert np.allclose(out["y"], fc["y"][pos], atol=1e-12)
+
+
 def test_planted_mistakes_are_caught(monkeypatch):
     """Each pin above fails when a plausible slip is planted in the oracle."""
     rng = np.random.default_rng(9)
@@ -427,6 +512,19 @@ def test_planted_mistakes_are_caught(monkeypatch):
     rr = oracle.causal_attention(qg, np.tile(kg, (1, 2, 1)), np.tile(vg, (1, 2, 1)), np.arange(6), 0.5)
     assert not np.allclose(rr, ref, atol=1e-6)
     assert np.allclose(oracle.causal_attention(qg, kg, vg, np.arange(6), 0.5), ref, atol=1e-12)
+    # gated MLP slips: gate and up halves swapped inside a shard, or a plain
+    # sigmoid gate, miss torch's SwiGLU
+    xs = rng.standard_normal((5, 8))
+    Wg, Wu = rng.standard_normal((2, 16, 8))
+    W2 = rng.standard_normal((8, 16))
+    w1, w2 = _split_gated(Wg, Wu, W2, 2)
+    tx = torch.from_numpy(xs)
+    ref = F.linear(F.silu(F.linear(tx, torch.from_numpy(Wg))) * F.linear(tx, torch.from_numpy(Wu)),
+                   torch.from_numpy(W2)).numpy()
+    swapped = [np.concatenate([a[8:], a[:8]]) for a in w1]
+    assert not np.allclose(oracle.mlp(xs, swapped, w2, gated=True), ref, atol=1e-6)
+    monkeypatch.setattr(oracle.tsp_oracle, "silu", lambda z: 1 / (1 + np.exp(-np.asarray(z, dtype=np.float64))))
+    assert not np.allclose(oracle.mlp(xs, w1, w2, gated=True), ref, atol=1e-6)
 
 
 # ---------------------------------------------------------------- synth
