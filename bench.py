@@ -52,7 +52,7 @@ def layer_flops(sh, r):
     qkv = 2 * N * sh.h * (sh.H + 2 * sh.kv_heads) * sh.Dh
     attn = 4 * sh.Dh * sh.H * attn_pairs(sh.S, sh.D, r)
     outp = 2 * N * sh.h * sh.h
-    mlp = 2 * 2 * N * sh.h * sh.F
+    mlp = (3 if sh.mlp == "swiglu" else 2) * 2 * N * sh.h * sh.F  # gated: gate, up and down products
     return {"qkv": qkv, "attention": attn, "outproj": outp, "mlp": mlp, "total": qkv + attn + outp + mlp}
 
 
@@ -299,6 +299,8 @@ def main():
     ap.add_argument("--hkv", type=int, default=0,
                     help="K/V heads for the layer and attention workloads (grouped-query attention; 0 = 32, "
                          "multi-head as in the pages' model)")
+    ap.add_argument("--mlp", choices=["gelu", "swiglu"], default="gelu",
+                    help="MLP form for the layer and MLP workloads (gelu: the pages' two-matrix MLP)")
     ap.add_argument("--cpu-rows", type=int, default=384, help="rows in the CPU oracle sample (0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warmup, run one plain device-to-device copy of this many MiB (a known-size "
@@ -326,15 +328,16 @@ def main():
 
     assert torch.cuda.is_available(), "needs a GPU"
     tsp.lib()
-    sh = dataclasses.replace(synth.SEVEN_B, Hkv=args.hkv)
+    sh = dataclasses.replace(synth.SEVEN_B, Hkv=args.hkv, mlp=args.mlp)
     r = args.rank
     N = sh.N
     seed = 4
     t_gen = time.perf_counter()
     log(f"generating inputs: S={sh.S} D={sh.D} r={r} h={sh.h} H={sh.H} Hkv={sh.kv_heads} Dh={sh.Dh} F={sh.F}")
     shape = tsp.make_shape(sh.S, sh.D, r, sh.h, sh.H, sh.Dh, sh.F, eps=sh.eps, dtype="bf16",
-                           rope_base=args.rope_base, Hkv=args.hkv)
+                           rope_base=args.rope_base, Hkv=args.hkv, mlp=args.mlp)
     kv_note = f", {sh.kv_heads} K/V heads" if sh.kv_heads != sh.H else ""
+    mlp_note = "SwiGLU FFN" if sh.mlp == "swiglu" else "FFN"
     stream = torch.cuda.current_stream()
     flops = layer_flops(sh, r)
 
@@ -354,7 +357,7 @@ def main():
             tsp.tsp_layer_fwd(shape, wd, xd, kf, vf, y, tsp.TSP_PHASE_ALL, ws)
         step_flops = flops["total"]
         step_exps = sh.H * attn_pairs(sh.S, sh.D, r)
-        workload = (f"tsp_layer_fwd: one 7B dense decoder layer (h=4096, 32x128 heads{kv_note}, FFN 16384, bf16) on "
+        workload = (f"tsp_layer_fwd: one 7B dense decoder layer (h=4096, 32x128 heads{kv_note}, {mlp_note} 16384, bf16) on "
                     f"rank {r} of D=8 at S=131072, 16384 local zigzag tokens")
     elif args.workload == "mlp":
         x = synth.activations(N, sh.h, seed=2, dtype="bf16")
@@ -366,7 +369,8 @@ def main():
             tsp.tsp_mlp_ring(shape, xd, wd["w1"], wd["w2"], None, y, ws)
         step_flops = flops["mlp"]
         step_exps = 0
-        workload = "tsp_mlp_ring: 7B MLP ring, 16384x4096 bf16 local X, D=8 shards of 4096x2048"
+        workload = (f"tsp_mlp_ring: 7B MLP ring ({mlp_note}), 16384x4096 bf16 local X, D=8 shards of "
+                    f"{2 if sh.mlp == 'swiglu' else 1}x2048x4096 and 4096x2048")
     elif args.workload == "layers32":
         # 32 layers resident in HBM (82 GB of weights and K/V), each with its
         # own weights and remote K/V, generated on the GPU from a fixed seed:
@@ -380,13 +384,14 @@ def main():
 
         hd, fd = sh.h // sh.D, sh.F // sh.D
         hkd = sh.kv_heads * sh.Dh // sh.D
+        f1 = (2 if sh.mlp == "swiglu" else 1) * fd
         layers = []
         for _ in range(n_layers):
             wl = {"g_attn": torch.ones(sh.h, dtype=torch.bfloat16, device="cuda"),
                   "g_mlp": torch.ones(sh.h, dtype=torch.bfloat16, device="cuda"),
                   "wqkv": [rnd((hd + 2 * hkd, sh.h), 0.02, torch.bfloat16) for _ in range(sh.D)],
                   "wo": [rnd((sh.h, hd), 0.02, torch.bfloat16) for _ in range(sh.D)],
-                  "w1": [rnd((fd, sh.h), 0.02, torch.bfloat16) for _ in range(sh.D)],
+                  "w1": [rnd((f1, sh.h), 0.02, torch.bfloat16) for _ in range(sh.D)],
                   "w2": [rnd((sh.h, fd), 0.02, torch.bfloat16) for _ in range(sh.D)]}
             kl = rnd((sh.S, sh.kv_heads, sh.Dh), 1.0, torch.bfloat16)
             vl = rnd((sh.S, sh.kv_heads, sh.Dh), 1.0, torch.bfloat16)
@@ -405,7 +410,7 @@ def main():
         step_flops = n_layers * flops["total"]
         step_exps = n_layers * sh.H * attn_pairs(sh.S, sh.D, r)
         N = N * n_layers  # value = layer-tokens/s, comparable with the one-layer figure
-        workload = (f"32 x tsp_layer_fwd: 32-layer 7B dense forward (each layer h=4096, 32x128 heads{kv_note}, FFN 16384, "
+        workload = (f"32 x tsp_layer_fwd: 32-layer 7B dense forward (each layer h=4096, 32x128 heads{kv_note}, {mlp_note} 16384, "
                     f"bf16, own weights and remote K/V, all resident) on rank {r} of D=8 at S=131072, "
                     f"16384 local zigzag tokens; value counts layer-tokens (16384 x 32 per step)")
     else:
@@ -485,10 +490,12 @@ def main():
                     "traffic": (traffic_from_profile(os.path.join(ROOT, "tsp_rank_local_amd", "csrc", "attention.hip"),
                                                      "attention_7b") if r == 0 and sh.kv_heads == sh.H else None)}
     elif "mlp_up" in kernels:
+        # one launch covers the up products of all D ring steps
         t_up = kernels["mlp_up"]["ms_per_launch"] * 1e-3
-        f_up = 2 * N * sh.h * (sh.F // sh.D)
+        f_up = (2 if sh.mlp == "swiglu" else 1) * 2 * N * sh.h * sh.F
         achieved = f_up / t_up / 1e12
-        roofline = {"kernel": "gemm_bf16_kernel<EpiGelu>", "bound": "mfma", "achieved": achieved,
+        roofline = {"kernel": "gemm_bf16_kernel<EpiSwiGLU>" if sh.mlp == "swiglu" else "gemm_bf16_kernel<EpiGelu>",
+                    "bound": "mfma", "achieved": achieved,
                     "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_BF16, "traffic": None}
 
     cpu = None
@@ -513,7 +520,7 @@ def main():
         "config": {"workload": workload, "S": sh.S, "D": sh.D, "r": r, "h": sh.h, "H": sh.H, "Dh": sh.Dh,
                    "F": sh.F, "local_tokens": sh.N, "layers": 32 if args.workload == "layers32" else 1,
                    "parallelism": "one rank of a D=8 folded TP+SP axis", "rope_base": args.rope_base,
-                   "Hkv": sh.kv_heads},
+                   "Hkv": sh.kv_heads, "mlp": sh.mlp},
         "pct_bf16_mfma_peak": 100.0 * step_flops / (ms_step * 1e-3) / PEAK_BF16,
         # the same against the dense peak scaled to the mean shader clock seen
         # during the timed steps (the published peak assumes 2.4 GHz)
@@ -560,7 +567,8 @@ def cpu_baseline(sh, r, x, w, k_rem, v_rem, m, rope_base=0.0):
     pos = oracle.zigzag_positions(sh.S, sh.D, r)[rows]
     t0 = time.perf_counter()
     oracle.local_kv(x[rows], w64, sh.H, sh.Dh, sh.eps, pos, rope_base, Hkv=sh.kv_heads)
-    oracle.layer_rows(x[rows], pos, w64, k32, v32, sh.H, sh.Dh, sh.eps, sh.scale, rope_base, Hkv=sh.kv_heads)
+    oracle.layer_rows(x[rows], pos, w64, k32, v32, sh.H, sh.Dh, sh.eps, sh.scale, rope_base, Hkv=sh.kv_heads,
+                      gated=sh.mlp == "swiglu")
     t = time.perf_counter() - t0
     log(f"cpu baseline: {t:.1f} s")
     return {"value": m / t, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle", "cpu_model": cpu_model(),

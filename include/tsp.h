@@ -71,6 +71,15 @@ typedef enum {
 
 typedef enum { TSP_F32 = 0, TSP_BF16 = 1 } tsp_dtype;
 
+/* MLP form (tsp_shape.mlp).
+ *  TSP_MLP_GELU:   GELU(x W1^T) W2^T, exact erf GELU (the pages' "FFN x4"
+ *                  model, [P2] paragraph 1).
+ *  TSP_MLP_SWIGLU: (SiLU(x Wg^T) * (x Wu^T)) W2^T, SiLU(z) = z / (1 + e^-z)
+ *                  (an optional variant, the gated MLP of common 7B models;
+ *                  not on the pages). Shard j's first matrix stacks its F/D
+ *                  Wg rows on the Wu rows of the same hidden units. */
+typedef enum { TSP_MLP_GELU = 0, TSP_MLP_SWIGLU = 1 } tsp_mlp_kind;
+
 /* Sizes of one layer on the folded axis.
  *  S  total sequence length (the K/V all-gather covers S rows), S < 2^31
  *  D  axis size (number of ranks / shards), 1 <= D <= TSP_MAX_D, S % (2D) == 0
@@ -91,6 +100,8 @@ typedef enum { TSP_F32 = 0, TSP_BF16 = 1 } tsp_dtype;
  *        query head i reads K/V head i / (H/Hkv); the layer also needs
  *        Hkv % D == 0, so head group j holds query heads j*H/D.. and K/V
  *        heads j*Hkv/D.., and bf16 rotation needs Hkv*Dh/D % 128 == 0.
+ *  mlp   tsp_mlp_kind of tsp_mlp_ring and tsp_layer_fwd (0 = GELU, the
+ *        pages' model). F is the number of hidden units either way.
  * Local token count N = S/D. Widths used as GEMM dimensions (h, F/D, h/D)
  * must be multiples of 64. */
 typedef struct {
@@ -100,6 +111,7 @@ typedef struct {
   int32_t dtype;
   float rope_base;
   int32_t Hkv;
+  int32_t mlp;
 } tsp_shape;
 
 #define TSP_MAX_D 64
@@ -112,7 +124,8 @@ typedef struct {
  *           heads), then its K rows, then its V rows (Hkv/D heads each),
  *           each head-major (head, then feature within the head).
  *  wo[j]:   [h][h/D]   the columns of W_O that read head group j.
- *  w1[j]:   [F/D][h]   rows j*F/D.. of W1.
+ *  w1[j]:   [F/D][h]   rows j*F/D.. of W1; TSP_MLP_SWIGLU: [2F/D][h], rows
+ *           j*F/D.. of Wg, then the same rows of Wu.
  *  w2[j]:   [h][F/D]   columns j*F/D.. of W2. */
 typedef struct {
   const void *g_attn;
@@ -191,7 +204,8 @@ tsp_status tsp_zigzag_attn_ex(const tsp_shape *shape, const void *q, const void 
 /* The MLP ring on rank r (paragraph 2: shards circulate on a ring and every
  * rank sums their contributions itself, with no all-reduce):
  *   y = residual + sum over steps t = 0..D-1 of GELU(x W1_j^T) W2_j^T,
- *   j = (r - t) mod D, accumulated into y in fp32 in that order.
+ *   j = (r - t) mod D, accumulated into y in fp32 in that order (with
+ *   TSP_MLP_SWIGLU the hidden layer is SiLU(x Wg_j^T) * (x Wu_j^T)).
  *  x: [S/D][h] (dtype); w1, w2: (host) arrays of D device pointers, shard
  *  layout as in tsp_layer_weights; residual: [S/D][h] fp32 or NULL (then
  *  zero); it may equal y. y: [S/D][h] fp32, fully written.

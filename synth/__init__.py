@@ -42,7 +42,8 @@ class LayerShape:
     S: total sequence, D: axis size, h: hidden, H: heads, Dh: head width,
     F: MLP width, eps: RMSNorm epsilon, dtype: 'f32' or 'bf16' storage type of
     weights and activations (accumulation is always fp32 on the device),
-    Hkv: K/V heads of grouped-query attention (0 means H).
+    Hkv: K/V heads of grouped-query attention (0 means H), mlp: 'gelu' (two
+    matrices) or 'swiglu' (gated: the first matrix holds gate and up rows).
     """
 
     S: int
@@ -54,6 +55,7 @@ class LayerShape:
     eps: float = 1e-5
     dtype: str = "bf16"
     Hkv: int = 0
+    mlp: str = "gelu"
 
     @property
     def kv_heads(self) -> int:
@@ -155,7 +157,8 @@ def layer_weights(shape: LayerShape, seed: int, gain: str = "ones") -> dict:
                K rows, then V rows, each head-major (head, then feature);
       wo[j]:   [h, h/D]    the W_O columns that read that head group.
     Shard j of the MLP covers hidden units j*F/D .. (j+1)*F/D-1:
-      w1[j]:   [F/D, h]    rows of W1 (out, in);
+      w1[j]:   [F/D, h]    rows of W1 (out, in); with mlp 'swiglu' [2F/D, h],
+               the gate rows of those units, then their up rows;
       w2[j]:   [h, F/D]    columns of W2 (out, in).
     Gains g_attn, g_mlp: [h]; 'ones' or 'random' (1 + 0.1*N(0,1)).
     """
@@ -167,7 +170,8 @@ def layer_weights(shape: LayerShape, seed: int, gain: str = "ones") -> dict:
     w = {
         "wqkv": [normal((hd + 2 * hkd, h), seed, TID_WQKV, j, WEIGHT_STD, dtype=dt) for j in range(D)],
         "wo": [normal((h, hd), seed, TID_WO, j, WEIGHT_STD, dtype=dt) for j in range(D)],
-        "w1": [normal((fd, h), seed, TID_W1, j, WEIGHT_STD, dtype=dt) for j in range(D)],
+        "w1": [normal(((2 if shape.mlp == "swiglu" else 1) * fd, h), seed, TID_W1, j, WEIGHT_STD, dtype=dt)
+               for j in range(D)],
         "w2": [normal((h, fd), seed, TID_W2, j, WEIGHT_STD, dtype=dt) for j in range(D)],
     }
     if gain == "ones":

@@ -55,15 +55,16 @@ def _a256(n):
     return (n + 255) // 256 * 256
 
 
-def _lead_bytes(S, D, h, F):
+def _lead_bytes(S, D, h, F, gated=False):
     """bf16 rank 0 also recomputes its first m = min(64, S/(2D)) rows in fp32:
     seven [m][h] and one [m][F] fp32 buffers, plus the K-chunk partial sums of
     the largest of its four products (chunk: 512, 256, 128 or 64 dividing the
-    reduction segment)."""
+    reduction segment; a gated MLP up has 2F product columns)."""
     m = min(64, S // (2 * D))
     hd, fd = h // D, F // D
     chunk = lambda k: next(c for c in (512, 256, 128, 64) if k % c == 0)
-    part = 4 * max(h // chunk(h) * m * 3 * h, h // chunk(hd) * m * h, h // chunk(h) * m * F, F // chunk(fd) * m * h)
+    up = h // chunk(h) * m * (2 * F if gated else F)
+    part = 4 * max(h // chunk(h) * m * 3 * h, h // chunk(hd) * m * h, up, F // chunk(fd) * m * h)
     return 7 * _a256(m * h * 4) + _a256(m * F * 4) + _a256(part)
 
 
@@ -82,6 +83,12 @@ def test_workspace_sizes():
         s7 = tsp.make_shape(131072, 8, r, 4096, 32, 128, 16384, dtype="bf16")
         lead = _lead_bytes(131072, 8, 4096, 16384) if r == 0 else 0
         assert tsp.workspace_size(s7, tsp.TSP_WS_LAYER) == 2 * 16384 * 4096 * 2 + 16384 * 16384 * 2 + lead
+    # gated MLP: the hidden layer is still [N][F]; only the leading rows'
+    # partial sums of the up product double
+    s7g = tsp.make_shape(131072, 8, 0, 4096, 32, 128, 16384, dtype="bf16", mlp="swiglu")
+    assert tsp.workspace_size(s7g, tsp.TSP_WS_MLP) == 16384 * 16384 * 2
+    assert tsp.workspace_size(s7g, tsp.TSP_WS_LAYER) == (2 * 16384 * 4096 * 2 + 16384 * 16384 * 2 +
+                                                         _lead_bytes(131072, 8, 4096, 16384, gated=True))
 
 
 def test_grouped_kv_shapes_accepted():
@@ -112,6 +119,8 @@ def test_grouped_kv_shapes_accepted():
     (dict(rope_base=-1.0), tsp.TSP_ERR_INVALID_ARG),
     (dict(rope_base=float("inf")), tsp.TSP_ERR_INVALID_ARG),
     (dict(rope_base=1e4, dtype="bf16"), tsp.TSP_ERR_UNSUPPORTED),  # h/D = 64: rotation needs whole 128-column heads
+    (dict(mlp=2), tsp.TSP_ERR_INVALID_ARG),           # unknown MLP kind
+    (dict(mlp=-1), tsp.TSP_ERR_INVALID_ARG),
     (dict(Hkv=-1), tsp.TSP_ERR_INVALID_ARG),
     (dict(Hkv=3), tsp.TSP_ERR_INVALID_ARG),           # Hkv must divide H
     (dict(Hkv=8), tsp.TSP_ERR_INVALID_ARG),           # more K/V heads than query heads

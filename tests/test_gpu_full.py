@@ -98,23 +98,26 @@ def test_zigzag_attention_7b(torch, r):
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("r,rope,hkv", [(0, 0.0, 0), (7, 0.0, 0), (0, 10000.0, 0), (3, 10000.0, 8)])
-def test_layer_7b(torch, r, rope, hkv):
+@pytest.mark.parametrize("r,rope,hkv,mlp", [(0, 0.0, 0, "gelu"), (7, 0.0, 0, "gelu"), (0, 10000.0, 0, "gelu"),
+                                            (3, 10000.0, 8, "gelu"), (0, 10000.0, 8, "swiglu")])
+def test_layer_7b(torch, r, rope, hkv, mlp):
     """One full layer, ranks 0 (the benchmark's) and 7, the benchmark's inputs
     (seed 4); rank 0 with rotary embedding (base 1e4), remote K rows taken as
-    already rotated; and rank 3 with rotation and 8 K/V heads shared by the 32
-    query heads (grouped-query attention)."""
-    SH = dataclasses.replace(SH7, Hkv=hkv)
+    already rotated; rank 3 with rotation and 8 K/V heads shared by the 32
+    query heads (grouped-query attention); and rank 0 with all three variants
+    (rotation, 8 K/V heads, gated MLP)."""
+    SH = dataclasses.replace(SH7, Hkv=hkv, mlp=mlp)
     N = SH.N
     w = synth.layer_weights(SH, seed=4)
     x = synth.activations(N, SH.h, seed=4)
     k_rem, v_rem = synth.remote_kv(SH, seed=4)
     wd = {k: ([up(a, "bf16") for a in v] if isinstance(v, list) else up(v, "bf16")) for k, v in w.items()}
     kf, vf = up(k_rem, "bf16"), up(v_rem, "bf16")
-    s = tsp.make_shape(SH.S, SH.D, r, SH.h, SH.H, SH.Dh, SH.F, eps=SH.eps, dtype="bf16", rope_base=rope, Hkv=hkv)
+    s = tsp.make_shape(SH.S, SH.D, r, SH.h, SH.H, SH.Dh, SH.F, eps=SH.eps, dtype="bf16", rope_base=rope, Hkv=hkv,
+                       mlp=mlp)
     ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
     y = torch.full((N, SH.h), float("nan"), dtype=torch.float32, device="cuda")
-    log(f"layer 7B r={r} rope={rope} Hkv={hkv}")
+    log(f"layer 7B r={r} rope={rope} Hkv={hkv} {mlp}")
     tsp.tsp_layer_fwd(s, wd, up(x, "f32"), kf, vf, y, tsp.TSP_PHASE_ALL, ws)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(y).all())
@@ -132,7 +135,8 @@ def test_layer_7b(torch, r, rope, hkv):
     assert np.array_equal(kr, k_rem.view(np.int16)[remote.numpy()])
     del kf, vf, kr
     want = oracle.layer_rank(x, w64, synth.as_f32(k_rem, "bf16"), synth.as_f32(v_rem, "bf16"), SH.S, SH.D, r,
-                             SH.H, SH.Dh, SH.eps, SH.scale, rows=rows, rope_base=rope, Hkv=SH.kv_heads)
+                             SH.H, SH.Dh, SH.eps, SH.scale, rows=rows, rope_base=rope, Hkv=SH.kv_heads,
+                             gated=mlp == "swiglu")
     got = down(y[torch.from_numpy(rows).cuda()])
     assert_close(got, want["y"], TOL_BF16, "y rows")
     if r == 0:

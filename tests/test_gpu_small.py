@@ -181,19 +181,23 @@ def test_attention_late_keys_far_above_first_tile(torch, Dh, q_log2):
 
 # ---------------------------------------------------------------- MLP ring
 MLP_CASES = [
-    # S, D, h, F, dtype, residual
-    (1024, 4, 256, 1024, "f32", False),   # the tiny fp32 layer's MLP
-    (1024, 4, 256, 1024, "f32", True),
-    (2400, 4, 512, 2048, "bf16", True),   # N = 600: ragged row tiles
-    (2048, 2, 256, 512, "bf16", False),
-    (1024, 1, 256, 256, "bf16", False),   # D = 1
-    (4096, 8, 640, 1024, "bf16", True),   # N = 512, h not a multiple of the tile
+    # S, D, h, F, dtype, residual, MLP form
+    (1024, 4, 256, 1024, "f32", False, "gelu"),   # the tiny fp32 layer's MLP
+    (1024, 4, 256, 1024, "f32", True, "gelu"),
+    (2400, 4, 512, 2048, "bf16", True, "gelu"),   # N = 600: ragged row tiles
+    (2048, 2, 256, 512, "bf16", False, "gelu"),
+    (1024, 1, 256, 256, "bf16", False, "gelu"),   # D = 1
+    (4096, 8, 640, 1024, "bf16", True, "gelu"),   # N = 512, h not a multiple of the tile
+    (1024, 4, 256, 1024, "f32", True, "swiglu"),  # gated: (gate, up) column pairs
+    (2400, 4, 512, 2048, "bf16", True, "swiglu"),  # gated: 64 gate + 64 up columns per 128, ragged rows
+    (1024, 2, 256, 128, "bf16", False, "swiglu"),  # gated, F/D = 64: 128 product columns, half a tile
+    (4096, 8, 640, 1024, "bf16", True, "swiglu"),
 ]
 
 
-@pytest.mark.parametrize("S,D,h,F,dtype,resid", MLP_CASES)
-def test_mlp_ring(torch, S, D, h, F, dtype, resid):
-    shape = synth.LayerShape(S=S, D=D, h=h, H=h // 64, Dh=64, F=F, dtype=dtype)
+@pytest.mark.parametrize("S,D,h,F,dtype,resid,mlp", MLP_CASES)
+def test_mlp_ring(torch, S, D, h, F, dtype, resid, mlp):
+    shape = synth.LayerShape(S=S, D=D, h=h, H=h // 64, Dh=64, F=F, dtype=dtype, mlp=mlp)
     N = S // D
     w = synth.layer_weights(shape, seed=21)
     x = synth.activations(N, h, seed=21, dtype=dtype)
@@ -201,16 +205,17 @@ def test_mlp_ring(torch, S, D, h, F, dtype, resid):
     w1d = [up(a, dtype) for a in w["w1"]]
     w2d = [up(a, dtype) for a in w["w2"]]
     xd = up(x, dtype)
-    want = oracle.mlp(f64(x, dtype), [f64(a, dtype) for a in w["w1"]], [f64(a, dtype) for a in w["w2"]])
+    want = oracle.mlp(f64(x, dtype), [f64(a, dtype) for a in w["w1"]], [f64(a, dtype) for a in w["w2"]],
+                      gated=mlp == "swiglu")
     if resid:
         want = want + res.astype(np.float64)
     tol = TOL_F32 if dtype == "f32" else TOL_BF16
     outs = []
     for r in sorted({0, D - 1, D // 2}):
-        s = tsp.make_shape(S, D, r, h, h // 64, 64, F, dtype=dtype)
+        s = tsp.make_shape(S, D, r, h, h // 64, 64, F, dtype=dtype, mlp=mlp)
         ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_MLP), dtype=torch.uint8, device="cuda")
         y = torch.full((N, h), float("nan"), dtype=torch.float32, device="cuda")
-        log(f"mlp ring S={S} D={D} r={r} h={h} F={F} {dtype} residual={resid}")
+        log(f"mlp ring S={S} D={D} r={r} h={h} F={F} {dtype} residual={resid} {mlp}")
         tsp.tsp_mlp_ring(s, xd, w1d, w2d, up(res, "f32") if resid else None, y, ws)
         _sync(torch)
         outs.append(down(y))
@@ -309,30 +314,31 @@ def test_tiny_layer_every_rank_vs_unsharded(torch, gain, rope):
     assert_close(got, full["y"], TOL_F32, "y, all ranks")
 
 
-@pytest.mark.parametrize("rope", [0.0, 10000.0])
-def test_fp32_grouped_layer_every_rank_vs_unsharded(torch, rope):
+@pytest.mark.parametrize("rope,mlp", [(0.0, "gelu"), (10000.0, "gelu"), (10000.0, "swiglu")])
+def test_fp32_grouped_layer_every_rank_vs_unsharded(torch, rope, mlp):
     """fp32 layer with 8 query heads sharing 2 K/V heads (S=1024, D=2, h=512,
     Dh=64, F=1024): the ranks write their K/V rows into one gathered buffer of
     2 heads, then each runs the rest; every rank's rows must equal the
-    unsharded grouped layer's."""
+    unsharded grouped layer's. Also with rotation, and with the gated MLP."""
     S, D, H, Hkv, Dh, F = 1024, 2, 8, 2, 64, 1024
     h = H * Dh
-    shape = synth.LayerShape(S=S, D=D, h=h, H=H, Dh=Dh, F=F, dtype="f32", Hkv=Hkv)
+    shape = synth.LayerShape(S=S, D=D, h=h, H=H, Dh=Dh, F=F, dtype="f32", Hkv=Hkv, mlp=mlp)
     w = synth.layer_weights(shape, seed=5, gain="random")
     assert w["wqkv"][0].shape == ((H + 2 * Hkv) * Dh // D, h)
     x_full = synth.activations(S, h, seed=5)
-    full = oracle.layer_full(x_full, _w64(w, "f32"), H, Dh, shape.eps, shape.scale, rope_base=rope, Hkv=Hkv)
+    full = oracle.layer_full(x_full, _w64(w, "f32"), H, Dh, shape.eps, shape.scale, rope_base=rope, Hkv=Hkv,
+                             gated=mlp == "swiglu")
     wd = _dev_weights(w, "f32")
     kf = torch.zeros((S, Hkv, Dh), dtype=torch.float32, device="cuda")
     vf = torch.zeros_like(kf)
     ranks = []
     for r in range(D):
-        s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype="f32", rope_base=rope, Hkv=Hkv)
+        s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype="f32", rope_base=rope, Hkv=Hkv, mlp=mlp)
         pos = oracle.zigzag_positions(S, D, r)
         ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
         xd = up(x_full[pos], "f32")
         y = torch.full((S // D, h), float("nan"), dtype=torch.float32, device="cuda")
-        log(f"fp32 grouped layer r={r} rope={rope}: K/V phase")
+        log(f"fp32 grouped layer r={r} rope={rope} {mlp}: K/V phase")
         tsp.tsp_layer_fwd(s, wd, xd, kf, vf, y, tsp.TSP_PHASE_KV, ws)
         ranks.append((s, pos, ws, xd, y))
     for s, pos, ws, xd, y in ranks:
@@ -366,24 +372,28 @@ def test_tiny_layer_rank_mode_given_remote_kv(torch):
         assert_close(down(y) - x, want["y"] - x, 10 * TOL_F32, "y - x (both branches)")
 
 
-@pytest.mark.parametrize("S,D,H,Dh,F,rope,Hkv", [
-    (2048, 4, 4, 128, 2048, 0.0, 0),
-    (2400, 4, 4, 128, 2048, 0.0, 0),   # N = 600: ragged row tiles
-    (1024, 2, 4, 64, 1024, 0.0, 0),
-    (96, 3, 6, 64, 576, 0.0, 0),       # C = 16: rank 0 recomputes 16 leading rows (one 32-row MFMA block)
-    (256, 1, 4, 64, 512, 0.0, 0),      # D = 1: one shard, the plain layer
-    (2048, 4, 4, 128, 2048, 10000.0, 0),  # rotary embedding, heads of 128
-    (1024, 2, 4, 64, 1024, 500.0, 0),     # rotary embedding, heads of 64 (two per 128-column block)
-    (96, 3, 6, 64, 576, 10000.0, 0),      # rotary embedding on the 16 leading rows too
-    (2048, 4, 8, 128, 2048, 0.0, 4),      # grouped K/V: 2 query heads per K/V head, 128-column blocks
-    (2048, 4, 8, 128, 2048, 10000.0, 4),  # grouped K/V with rotation in the epilogue
-    (1024, 2, 4, 64, 1024, 0.0, 2),       # grouped K/V, 64-column K/V parts (element-wise epilogue)
-    (96, 3, 6, 64, 576, 0.0, 3),          # grouped K/V on the 16 leading rows
-    (96, 3, 6, 128, 576, 10000.0, 3),     # grouped K/V and rotation on the 16 leading rows, heads of 128
+@pytest.mark.parametrize("S,D,H,Dh,F,rope,Hkv,mlp", [
+    (2048, 4, 4, 128, 2048, 0.0, 0, "gelu"),
+    (2400, 4, 4, 128, 2048, 0.0, 0, "gelu"),   # N = 600: ragged row tiles
+    (1024, 2, 4, 64, 1024, 0.0, 0, "gelu"),
+    (96, 3, 6, 64, 576, 0.0, 0, "gelu"),       # C = 16: rank 0 recomputes 16 leading rows (one 32-row MFMA block)
+    (256, 1, 4, 64, 512, 0.0, 0, "gelu"),      # D = 1: one shard, the plain layer
+    (2048, 4, 4, 128, 2048, 10000.0, 0, "gelu"),  # rotary embedding, heads of 128
+    (1024, 2, 4, 64, 1024, 500.0, 0, "gelu"),     # rotary embedding, heads of 64 (two per 128-column block)
+    (96, 3, 6, 64, 576, 10000.0, 0, "gelu"),      # rotary embedding on the 16 leading rows too
+    (2048, 4, 8, 128, 2048, 0.0, 4, "gelu"),      # grouped K/V: 2 query heads per K/V head, 128-column blocks
+    (2048, 4, 8, 128, 2048, 10000.0, 4, "gelu"),  # grouped K/V with rotation in the epilogue
+    (1024, 2, 4, 64, 1024, 0.0, 2, "gelu"),       # grouped K/V, 64-column K/V parts (element-wise epilogue)
+    (96, 3, 6, 64, 576, 0.0, 3, "gelu"),          # grouped K/V on the 16 leading rows
+    (96, 3, 6, 128, 576, 10000.0, 3, "gelu"),     # grouped K/V and rotation on the 16 leading rows, heads of 128
+    (2048, 4, 4, 128, 2048, 0.0, 0, "swiglu"),      # gated MLP
+    (96, 3, 6, 64, 576, 0.0, 0, "swiglu"),          # gated MLP on the 16 leading rows
+    (2048, 4, 8, 128, 2048, 10000.0, 4, "swiglu"),  # rotation, grouped K/V and the gated MLP together
 ])
-def test_bf16_layer_vs_oracle(torch, S, D, H, Dh, F, rope, Hkv):
+def test_bf16_layer_vs_oracle(torch, S, D, H, Dh, F, rope, Hkv, mlp):
     h = H * Dh
-    shape = synth.LayerShape(S=S, D=D, h=h, H=H, Dh=Dh, F=F, dtype="bf16", Hkv=Hkv)
+    shape = synth.LayerShape(S=S, D=D, h=h, H=H, Dh=Dh, F=F, dtype="bf16", Hkv=Hkv, mlp=mlp)
+    gated = mlp == "swiglu"
     w = synth.layer_weights(shape, seed=3, gain="random")
     w64 = _w64(w, "bf16")
     wd = _dev_weights(w, "bf16")
@@ -391,19 +401,20 @@ def test_bf16_layer_vs_oracle(torch, S, D, H, Dh, F, rope, Hkv):
     k64, v64 = f64(k_rem, "bf16"), f64(v_rem, "bf16")
     for r in sorted({0, D - 1}):
         x = synth.activations(S // D, h, seed=3, tid=100 + r)
-        s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype="bf16", rope_base=rope, Hkv=Hkv)
+        s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype="bf16", rope_base=rope, Hkv=Hkv, mlp=mlp)
         ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
         kf, vf = up(k_rem, "bf16"), up(v_rem, "bf16")
         y = torch.empty((S // D, h), dtype=torch.float32, device="cuda")
-        log(f"bf16 layer S={S} D={D} r={r} H={H} Hkv={Hkv} Dh={Dh} F={F} rope={rope}")
+        log(f"bf16 layer S={S} D={D} r={r} H={H} Hkv={Hkv} Dh={Dh} F={F} rope={rope} {mlp}")
         tsp.tsp_layer_fwd(s, wd, up(x, "f32"), kf, vf, y, tsp.TSP_PHASE_ALL, ws)
         _sync(torch)
         want = oracle.layer_rank(x, w64, k64, v64, S, D, r, H, Dh, shape.eps, shape.scale, rope_base=rope,
-                                 Hkv=Hkv or None)
+                                 Hkv=Hkv or None, gated=gated)
         err = assert_close(down(y), want["y"], TOL_BF16, "y")
         if rope > 0:
             # the output is much closer to the rotated layer than to the plain one
-            plain = oracle.layer_rank(x, w64, k64, v64, S, D, r, H, Dh, shape.eps, shape.scale, Hkv=Hkv or None)["y"]
+            plain = oracle.layer_rank(x, w64, k64, v64, S, D, r, H, Dh, shape.eps, shape.scale, Hkv=Hkv or None,
+                                      gated=gated)["y"]
             far = float(np.abs(down(y) - plain).max()) / float(np.sqrt(np.mean(want["y"] ** 2)))
             log(f"  distance to the layer without rotation: {far:.3e} rms")
             assert far > 5 * err

@@ -20,7 +20,7 @@ __all__ = [
     "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_zigzag_attn_ex", "tsp_mlp_ring",
     "tsp_layer_fwd", "profile_enable", "profile_reset", "profile_read",
     "TSP_F32", "TSP_BF16", "TSP_ATTN_Q_LOG2_SCALED", "TSP_PHASE_KV", "TSP_PHASE_REST", "TSP_PHASE_ALL",
-    "TSP_WS_MLP", "TSP_WS_LAYER",
+    "TSP_WS_MLP", "TSP_WS_LAYER", "TSP_MLP_GELU", "TSP_MLP_SWIGLU", "MLP_KINDS",
     "KERNEL_CLASSES", "EXPORTED_SYMBOLS",
 ]
 
@@ -31,6 +31,8 @@ TSP_F32, TSP_BF16 = 0, 1
 TSP_PHASE_KV, TSP_PHASE_REST, TSP_PHASE_ALL = 1, 2, 3
 TSP_WS_MLP, TSP_WS_LAYER = 0, 1
 TSP_ATTN_Q_LOG2_SCALED = 1
+TSP_MLP_GELU, TSP_MLP_SWIGLU = 0, 1
+MLP_KINDS = {"gelu": TSP_MLP_GELU, "swiglu": TSP_MLP_SWIGLU}
 TSP_MAX_D = 64
 KERNEL_CLASSES = {"rmsnorm": 0, "qkv": 1, "attention": 2, "outproj": 3, "mlp_up": 4, "mlp_down": 5, "zigzag": 6,
                   "lead": 7}
@@ -52,7 +54,7 @@ class TspShape(ctypes.Structure):
     _fields_ = [("S", ctypes.c_int64), ("D", ctypes.c_int32), ("r", ctypes.c_int32), ("h", ctypes.c_int32),
                 ("H", ctypes.c_int32), ("Dh", ctypes.c_int32), ("F", ctypes.c_int32), ("eps", ctypes.c_float),
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("rope_base", ctypes.c_float),
-                ("Hkv", ctypes.c_int32)]
+                ("Hkv", ctypes.c_int32), ("mlp", ctypes.c_int32)]
 
 
 class TspLayerWeights(ctypes.Structure):
@@ -127,14 +129,16 @@ def _stream(stream) -> int | None:
     return torch.cuda.current_stream().cuda_stream
 
 
-def make_shape(S, D, r, h, H, Dh, F, eps=1e-5, scale=None, dtype="bf16", rope_base=0.0, Hkv=0) -> TspShape:
+def make_shape(S, D, r, h, H, Dh, F, eps=1e-5, scale=None, dtype="bf16", rope_base=0.0, Hkv=0,
+               mlp="gelu") -> TspShape:
     """A tsp_shape; dtype 'bf16' or 'f32'; scale defaults to 1/sqrt(Dh);
-    rope_base 0 means no rotary embedding; Hkv 0 means Hkv = H (multi-head)."""
+    rope_base 0 means no rotary embedding; Hkv 0 means Hkv = H (multi-head);
+    mlp 'gelu' or 'swiglu' (or a TSP_MLP_* value)."""
     if scale is None:
         scale = 1.0 / float(np.sqrt(Dh))
     dt = {"bf16": TSP_BF16, "f32": TSP_F32}[dtype] if isinstance(dtype, str) else int(dtype)
     return TspShape(int(S), int(D), int(r), int(h), int(H), int(Dh), int(F), float(eps), float(scale), dt,
-                    float(rope_base), int(Hkv))
+                    float(rope_base), int(Hkv), MLP_KINDS[mlp] if isinstance(mlp, str) else int(mlp))
 
 
 def workspace_size(shape: TspShape, which: int) -> int:

@@ -95,6 +95,9 @@ tsp_status check_mlp_shape(const tsp_shape *s) {
   if (s->h < 64 || s->h % 64 != 0) return fail(TSP_ERR_UNSUPPORTED, "h=%d must be a positive multiple of 64", s->h);
   if (s->F < 1 || s->F % s->D != 0) return fail(TSP_ERR_INVALID_ARG, "F=%d must be a positive multiple of D=%d", s->F, s->D);
   if ((s->F / s->D) % 64 != 0) return fail(TSP_ERR_UNSUPPORTED, "F/D=%d must be a multiple of 64", s->F / s->D);
+  if (s->mlp != TSP_MLP_GELU && s->mlp != TSP_MLP_SWIGLU) return fail(TSP_ERR_INVALID_ARG, "unknown mlp kind %d", s->mlp);
+  if (s->mlp == TSP_MLP_SWIGLU && (int64_t)(2 * (s->F / s->D) + 256) * s->h * 2 >= ((int64_t)1 << 31))
+    return fail(TSP_ERR_UNSUPPORTED, "gated MLP shard of %d x %d rows is too large", 2 * (s->F / s->D), s->h);
   return TSP_OK;
 }
 
@@ -154,7 +157,7 @@ LayerWs layer_ws(const tsp_shape *s) {
   w.lmm = w.lh1 + mh;
   w.lhid = w.lmm + mh;
   w.lpart = w.lhid + (m ? align256(m * (size_t)s->F * 4) : 0);
-  w.total = w.lpart + (m ? align256(tsp::lead_part_bytes((int32_t)m, s->h, s->F, s->D)) : 0);
+  w.total = w.lpart + (m ? align256(tsp::lead_part_bytes((int32_t)m, s->h, s->F, s->D, s->mlp == TSP_MLP_SWIGLU)) : 0);
   return w;
 }
 
@@ -365,7 +368,8 @@ tsp_status tsp_mlp_ring(const tsp_shape *s, const void *x, const void *const *w1
   // panels), then one reduction over them and the W2 shards in ring order
   const bool pnl = s->dtype == TSP_BF16;
   TSP_LAUNCH(TSP_K_MLP_UP,
-             tsp::launch_mlp_up(s->dtype, x, false, N, h, ring_list(w1, s->D, s->r), s->D, fd, ws, pnl, stream),
+             tsp::launch_mlp_up(s->dtype, x, false, N, h, ring_list(w1, s->D, s->r), s->D, fd, s->mlp == TSP_MLP_SWIGLU,
+                                ws, pnl, stream),
              "MLP up");
   TSP_LAUNCH(TSP_K_MLP_DOWN,
              tsp::launch_mlp_down(s->dtype, ws, pnl, N, ring_list(w2, s->D, s->r), s->D, fd, h, residual, y, stream),
@@ -391,6 +395,7 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
   const int32_t N = (int32_t)(s->S / s->D), h = s->h, D = s->D, hd = h / D, fd = s->F / D;
   // K/V: Hkv heads, hk = Hkv*Dh/D columns per shard, rows of hkv = Hkv*Dh
   const int32_t Hkv = kv_heads(s), hkv = Hkv * s->Dh, hk = hkv / D;
+  const bool gated = s->mlp == TSP_MLP_SWIGLU;
   const size_t e = elem_bytes(s->dtype);
   const Range rx{x, (size_t)N * h * 4, "x"}, ry{y, (size_t)N * h * 4, "y"}, rws{ws_, L.total, "ws"};
   const Range rk{k_full, (size_t)s->S * hkv * e, "k_full"}, rv{v_full, (size_t)s->S * hkv * e, "v_full"};
@@ -445,7 +450,7 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
     TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(y, w->g_mlp, qbuf, N, h, s->eps, s->dtype, pnl, stream),
                "RMSNorm");
     TSP_LAUNCH(TSP_K_MLP_UP,
-               tsp::launch_mlp_up(s->dtype, qbuf, pnl, N, h, ring_list(w->w1, D, s->r), D, fd, hid, pnl, stream),
+               tsp::launch_mlp_up(s->dtype, qbuf, pnl, N, h, ring_list(w->w1, D, s->r), D, fd, gated, hid, pnl, stream),
                "MLP up");
     TSP_LAUNCH(TSP_K_MLP_DOWN,
                tsp::launch_mlp_down(s->dtype, hid, pnl, N, ring_list(w->w2, D, s->r), D, fd, h, y, y, stream),
@@ -476,7 +481,7 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
       TSP_LAUNCH(TSP_K_LEAD, tsp::launch_rmsnorm_f32(lh1, w->g_mlp, s->dtype, lmm, m, h, s->eps, stream),
                  "leading rows: RMSNorm");
       TSP_LAUNCH(TSP_K_LEAD,
-                 tsp::launch_lead_mlp_up(lmm, m, h, ring_list(w->w1, D, s->r), D, fd, lhid, lpart, stream),
+                 tsp::launch_lead_mlp_up(lmm, m, h, ring_list(w->w1, D, s->r), D, fd, gated, lhid, lpart, stream),
                  "leading rows: MLP up");
       TSP_LAUNCH(TSP_K_LEAD,
                  tsp::launch_lead_mlp_down(lhid, m, ring_list(w->w2, D, s->r), D, fd, h, lh1, y, lpart, stream),

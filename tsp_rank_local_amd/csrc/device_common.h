@@ -47,6 +47,13 @@ __device__ __forceinline__ float gelu_erf(float z) {
   return z * (z >= 0.0f ? 1.0f - q : q);
 }
 
+// SiLU z * sigma(z) = z / (1 + e^-z) in fp32, e^-z as exp2(-z log2 e): for
+// z -> -inf, e^-z overflows to inf and the result goes to -0; for z -> +inf
+// it goes to z.
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+
 // For a value held by every lane, combine it with the value of lane l^32.
 // v_permlane32_swap exchanges the upper half of one register with the lower
 // half of another; fed the same value twice, the two results hold, in every

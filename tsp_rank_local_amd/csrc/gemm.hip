@@ -29,6 +29,7 @@
 // pitch every copy instruction touches 8 rows far apart and the rate halves.
 // fp32 operands use a plain LDS-tiled FMA kernel (64x64 tiles, 4x4 per thread).
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "tsp_internal.h"
@@ -44,7 +45,18 @@ struct GemmArgs {
   int32_t kseg;   // reduction length covered by one B pointer
   int32_t M, N, K;
   int32_t nz;     // independent problems; problem z uses B.p[z] and K == kseg
+  // Gated MLP up (epilogue EpiSwiGLU): each B segment holds gate_rows gate
+  // rows, then the same units' up rows; the product's N = 2*gate_rows
+  // columns interleave them (gemm_bf16_kernel: 64 gate then 64 up columns
+  // per 128; the other kernels: gate, up column pairs). 0 otherwise.
+  int32_t gate_rows;
 };
+
+// B row behind product column v of a gated product (see GemmArgs).
+__device__ __forceinline__ int gated_row_blocks(int v, int gate_rows) {
+  return ((v >> 7) << 6) + (v & 63) + ((v >> 6) & 1) * gate_rows;
+}
+__device__ __forceinline__ int gated_row_pairs(int v, int gate_rows) { return (v >> 1) + (v & 1) * gate_rows; }
 
 // ---------------------------------------------------------------- epilogues
 // Each epilogue takes one output element (fp32 kernel) or four consecutive
@@ -111,6 +123,53 @@ struct EpiGelu {
   __device__ __forceinline__ void put_row(const Row &w, const float4 (&v)[4][4]) const { put_each(*this, w, v); }
 };
 
+// H[:, z*cols + u] = SiLU(gate_u) * up_u for hidden unit u of ring step z's
+// shard (gated MLP). The fp32 kernel and the leading-rows reduction hand it
+// (gate, up) pairs; the bf16 kernel's fast path hands it 128 columns, of
+// which blocks i = 0, 1 are the gates and i + 2 the ups of 64 units (B rows
+// remapped by gated_row_blocks), all in one lane. 2*cols is a multiple of
+// 128, so that path covers every column.
+template <typename T>
+struct EpiSwiGLU {
+  static constexpr bool kGated = true;
+  T *out;
+  int64_t ld;     // row pitch of row-major H
+  int64_t panel;  // panel stride of H, or 0
+  int32_t cols;   // hidden units per shard
+  __device__ __forceinline__ static float act(float gate, float up) { return silu(gate) * up; }
+  __device__ __forceinline__ void pair(int z, int r, int u, float gate, float up) const {
+    const int64_t col = (int64_t)z * cols + u;
+    out[panel ? panel_index(r, col, panel) : (int64_t)r * ld + col] = (T)act(gate, up);
+  }
+  struct Row {
+    T *p;
+  };
+  __device__ __forceinline__ bool fast_ok() const { return true; }
+  __device__ __forceinline__ Row row(int z, int r, int c0, int g) const {
+    const int64_t col = (int64_t)z * cols + (c0 >> 7) * 64;  // first unit of the block, a multiple of 64
+    return Row{out + (panel ? panel_index(r, col, panel) : (int64_t)r * ld + col) + 4 * g};
+  }
+  __device__ __forceinline__ void put_row(const Row &w, const float4 (&v)[4][4]) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        const float4 a = v[i][vq], b = v[i + 2][vq];
+        store4(w.p + i * 32 + vq * 8, make_float4(act(a.x, b.x), act(a.y, b.y), act(a.z, b.z), act(a.w, b.w)));
+      }
+  }
+};
+
+// Whether an epilogue takes gated (gate, up) pairs.
+template <class Epi, class = void>
+struct is_gated {
+  static constexpr bool value = false;
+};
+template <class Epi>
+struct is_gated<Epi, std::void_t<decltype(Epi::kGated)>> {
+  static constexpr bool value = Epi::kGated;
+};
+
 struct EpiStoreF32 {
   float *out;
   int64_t ld;
@@ -165,8 +224,10 @@ struct EpiAddF32 {
 // heads), then hk K and hk V columns (Hkv/D heads). Q column c is global
 // feature z*hq + c of q [n][ldq], in local row order; K/V column c is feature
 // z*hk + c of kf/vf [S][ldkv] at the token's global row. (Four consecutive
-// columns never straddle parts: hq and hk are multiples of 4.)
-template <typename T>
+// columns never straddle parts: hq and hk are multiples of 4.) ROPE: the
+// bf16 fast path rotates Q and K with the table (a separate instance, so that
+// the plain one carries no rotation state).
+template <typename T, bool ROPE = false>
 struct EpiQKV {
   T *q, *k, *v;
   int64_t ldq, ldkv;
@@ -197,7 +258,7 @@ struct EpiQKV {
   };
   __device__ __forceinline__ bool fast_ok() const { return ((hq | hk) & 127) == 0; }
   __device__ __forceinline__ Row row(int z, int r, int c0, int g) const {
-    const bool rotate = rope != nullptr && c0 < hq + hk;
+    const bool rotate = ROPE && c0 < hq + hk;
     return Row{dst(z, r, c0 + 4 * g), factor(c0), rotate ? rope + (int64_t)r * (dh / 2) : nullptr};
   }
   __device__ __forceinline__ void put(const Row &w, int i, int vq, float4 v) const {
@@ -209,7 +270,7 @@ struct EpiQKV {
   // i holds the first half of a head; the pair's frequency index is
   // (32*i) % (dh/2) + 8*vq + 4*g + e.
   __device__ __forceinline__ void put_row(const Row &w, const float4 (&v)[4][4]) const {
-    if (w.rot == nullptr) {
+    if (!ROPE || w.rot == nullptr) {
       put_each(*this, w, v);
       return;
     }
@@ -283,6 +344,7 @@ template <class Epi>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, Epi epi) {
 #if defined(__HIP_DEVICE_COMPILE__)
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  constexpr bool kGatedB = is_gated<Epi>::value;
 
   const int tiles_m = (a.M + kBM - 1) / kBM, tiles_n = (a.N + kBN - 1) / kBN;
   const TileCoord tc = tile_of(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n);
@@ -305,7 +367,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, 
     const int win = kWinPerWave * wave + i, row = win * 8 + lane / 8, pos = lane & 7;
     const int ch = pos ^ ((row >> 1) & 7);
     a_off[i] = (int)(row * a_pitch * 2) + ch * 16;
-    b_off[i] = (int)(row * a.ldb * 2) + ch * 16;
+    if constexpr (kGatedB)  // offset from the segment start (descriptor below)
+      b_off[i] = (int)(gated_row_blocks(n0 + row, a.gate_rows) * a.ldb * 2) + ch * 16;
+    else
+      b_off[i] = (int)(row * a.ldb * 2) + ch * 16;
   }
   const int a_rows = min(kBM, a.M - m0), b_rows = min(kBN, a.N - n0);
   const bf16 *Ab = reinterpret_cast<const bf16 *>(a.A) + (int64_t)m0 * a_pitch;
@@ -339,7 +404,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, 
   };
   auto step_src = [&](int kt, const bf16 *bseg, int koff) {
     StepSrc t;
-    t.br = buffer_rsrc(bseg + (int64_t)n0 * a.ldb, (uint32_t)(b_rows * a.ldb * 2));
+    if constexpr (kGatedB)  // the tile's rows are spread over the gate and up halves
+      t.br = buffer_rsrc(bseg, (uint32_t)(2 * a.gate_rows * a.ldb * 2));
+    else
+      t.br = buffer_rsrc(bseg + (int64_t)n0 * a.ldb, (uint32_t)(b_rows * a.ldb * 2));
     t.b_soff = koff * 2;
     if (a_panel) {
       t.ar = buffer_rsrc(Ab + (int64_t)kt * a.a_panel, (uint32_t)(a_rows * kRowBytes));
@@ -365,7 +433,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, 
   // a scratch LDS area that nobody reads.
   __shared__ uint32_t pf_sink[64];
   const uint32_t sink = lds_addr(pf_sink);
-  const int pf_va = (wave * 64 + lane) * (int)(a_pitch * 2), pf_vb = (wave * 64 + lane) * (int)(a.ldb * 2);
+  const int pf_va = (wave * 64 + lane) * (int)(a_pitch * 2);
+  const int pf_vb = (kGatedB ? gated_row_blocks(n0 + wave * 64 + lane, a.gate_rows) : wave * 64 + lane) *
+                    (int)(a.ldb * 2);
   auto prefetch = [&](const StepSrc &t) {
     lds_touch4(t.ar, pf_va, t.a_soff, sink);
     lds_touch4(t.br, pf_vb, t.b_soff, sink);
@@ -501,7 +571,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, 
           vals[i][vq] = make_float4(acc[i][j][vq * 4 + 0], acc[i][j][vq * 4 + 1], acc[i][j][vq * 4 + 2],
                                     acc[i][j][vq * 4 + 3]);
       epi.put_row(rw, vals);
-    } else {
+    } else if constexpr (!kGatedB) {  // gated: every wave's 128 columns are whole or past N
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -542,7 +612,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, Epi epi) {
     const float *B = reinterpret_cast<const float *>(a.B.p[seg]);
     float4 av = make_float4(0.f, 0.f, 0.f, 0.f), bv = av;
     if (m0 + lrow < a.M) av = *reinterpret_cast<const float4 *>(A + (int64_t)(m0 + lrow) * a.lda + k0 + lk);
-    if (n0 + lrow < a.N) bv = *reinterpret_cast<const float4 *>(B + (int64_t)(n0 + lrow) * a.ldb + koff + lk);
+    if (n0 + lrow < a.N) {
+      const int brow = is_gated<Epi>::value ? gated_row_pairs(n0 + lrow, a.gate_rows) : n0 + lrow;
+      bv = *reinterpret_cast<const float4 *>(B + (int64_t)brow * a.ldb + koff + lk);
+    }
     As[lk + 0][lrow] = av.x;
     As[lk + 1][lrow] = av.y;
     As[lk + 2][lrow] = av.z;
@@ -567,13 +640,24 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, Epi epi) {
     }
     __syncthreads();
   }
+  if constexpr (is_gated<Epi>::value) {
+    // columns 2u, 2u+1 are the gate and up of unit u (N is even)
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = m0 + ty * 4 + i, c = n0 + tx * 4 + j;
-      if (r < a.M && c < a.N) epi(z, r, c, acc[i][j]);
-    }
+      for (int j = 0; j < 4; j += 2) {
+        const int r = m0 + ty * 4 + i, c = n0 + tx * 4 + j;
+        if (r < a.M && c < a.N) epi.pair(z, r, c >> 1, acc[i][j], acc[i][j + 1]);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = m0 + ty * 4 + i, c = n0 + tx * 4 + j;
+        if (r < a.M && c < a.N) epi(z, r, c, acc[i][j]);
+      }
+  }
 }
 
 // ---------------------------------------------------------------- leading rows
@@ -620,7 +704,8 @@ __global__ __launch_bounds__(256) void lead_gemm_kernel(GemmArgs a, int chunk, f
   // land only in columns of C that are not stored (likewise A rows past M).
   const int n = n0 + l32;
   const bool n_ok = n < a.N;
-  const bf16 *brow = reinterpret_cast<const bf16 *>(a.B.p[seg]) + (int64_t)(n_ok ? n : 0) * a.ldb + koff + 8 * g;
+  const int nrow = !n_ok ? 0 : a.gate_rows ? gated_row_pairs(n, a.gate_rows) : n;
+  const bf16 *brow = reinterpret_cast<const bf16 *>(a.B.p[seg]) + (int64_t)nrow * a.ldb + koff + 8 * g;
   // slab staging: thread -> A row tid/4, 16 consecutive K elements
   const int sr = tid >> 2, sk = (tid & 3) * 16;
   const float *asrc = reinterpret_cast<const float *>(a.A) + (int64_t)(sr < a.M ? sr : 0) * a.lda + k_begin + sk;
@@ -683,13 +768,26 @@ __global__ __launch_bounds__(256) void lead_reduce_kernel(int32_t M, int32_t N, 
                                                           const float *__restrict__ part, Epi epi) {
   const int64_t ntot = (int64_t)nz * N;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= M * ntot) return;
-  const int r = (int)(i / ntot);
-  const int64_t zc = i - r * ntot;
-  const int z = (int)(zc / N), c = (int)(zc - (int64_t)z * N);
-  float v = 0.f;
-  for (int kc = 0; kc < chunks; ++kc) v += part[((int64_t)kc * M + r) * ntot + zc];
-  epi(z, r, c, v);
+  if constexpr (is_gated<Epi>::value) {  // one thread per (row, unit): columns 2u, 2u+1
+    if (i >= M * (ntot >> 1)) return;
+    const int r = (int)(i / (ntot >> 1));
+    const int64_t zc = 2 * (i - r * (ntot >> 1));
+    const int z = (int)(zc / N), c = (int)(zc - (int64_t)z * N);
+    float gate = 0.f, up = 0.f;
+    for (int kc = 0; kc < chunks; ++kc) {
+      gate += part[((int64_t)kc * M + r) * ntot + zc];
+      up += part[((int64_t)kc * M + r) * ntot + zc + 1];
+    }
+    epi.pair(z, r, c >> 1, gate, up);
+  } else {
+    if (i >= M * ntot) return;
+    const int r = (int)(i / ntot);
+    const int64_t zc = i - r * ntot;
+    const int z = (int)(zc / N), c = (int)(zc - (int64_t)z * N);
+    float v = 0.f;
+    for (int kc = 0; kc < chunks; ++kc) v += part[((int64_t)kc * M + r) * ntot + zc];
+    epi(z, r, c, v);
+  }
 }
 
 template <class Epi>
@@ -718,11 +816,11 @@ static GemmArgs lead_args(const float *A, int64_t lda, int32_t M, int32_t N, int
   return a;
 }
 
-size_t lead_part_bytes(int32_t m, int32_t h, int32_t F, int32_t D) {
+size_t lead_part_bytes(int32_t m, int32_t h, int32_t F, int32_t D, bool gated) {
   const int32_t hd = h / D, fd = F / D;
   const size_t qkv = (size_t)(h / lead_chunk(h)) * m * 3 * h;
   const size_t op = (size_t)(h / lead_chunk(hd)) * m * h;
-  const size_t up = (size_t)(h / lead_chunk(h)) * m * F;
+  const size_t up = (size_t)(h / lead_chunk(h)) * m * (gated ? 2 * F : F);
   const size_t dn = (size_t)(F / lead_chunk(fd)) * m * h;
   return 4 * std::max(std::max(qkv, op), std::max(up, dn));
 }
@@ -748,11 +846,16 @@ hipError_t launch_lead_outproj(const float *o, int32_t m, int32_t h, const PtrLi
 }
 
 hipError_t launch_lead_mlp_up(const float *a, int32_t m, int32_t h, const PtrList &w1, int32_t D, int32_t fd,
-                              float *hid, float *part, hipStream_t s) {
-  GemmArgs g = lead_args(a, h, m, fd, h);
+                              bool gated, float *hid, float *part, hipStream_t s) {
+  GemmArgs g = lead_args(a, h, m, gated ? 2 * fd : fd, h);
   g.B = w1;
   g.ldb = h;
   g.nz = D;
+  if (gated) {
+    g.gate_rows = fd;
+    EpiSwiGLU<float> e{hid, (int64_t)D * fd, 0, fd};
+    return run_lead(g, e, part, s);
+  }
   EpiGelu<float> e{hid, (int64_t)D * fd, 0, fd};
   return run_lead(g, e, part, s);
 }
@@ -813,7 +916,11 @@ hipError_t launch_qkv(int dtype, const void *xn, bool a_panel, int32_t n, int32_
   a.nz = D;
   const int64_t ldq = (int64_t)D * hq, ldkv = (int64_t)D * hk;
   if (dtype == TSP_BF16) {
-    EpiQKV<bf16> e{(bf16 *)q, (bf16 *)kf, (bf16 *)vf, ldq, ldkv, hq, hk, zz, q_scale, rope, Dh};
+    if (rope != nullptr) {
+      EpiQKV<bf16, true> e{(bf16 *)q, (bf16 *)kf, (bf16 *)vf, ldq, ldkv, hq, hk, zz, q_scale, rope, Dh};
+      return run_gemm(dtype, a, e, s);
+    }
+    EpiQKV<bf16> e{(bf16 *)q, (bf16 *)kf, (bf16 *)vf, ldq, ldkv, hq, hk, zz, q_scale, nullptr, 0};
     return run_gemm(dtype, a, e, s);
   }
   EpiQKV<float> e{(float *)q, (float *)kf, (float *)vf, ldq, ldkv, hq, hk, zz, q_scale, nullptr, 0};
@@ -831,12 +938,23 @@ hipError_t launch_outproj(int dtype, const void *o, bool a_panel, int32_t n, int
 }
 
 hipError_t launch_mlp_up(int dtype, const void *x, bool a_panel, int32_t n, int32_t h, const PtrList &w1, int32_t D,
-                         int32_t fd, void *hid, bool hid_panel, hipStream_t s) {
-  GemmArgs a = make_args(x, h, a_panel, n, fd, h);
+                         int32_t fd, bool gated, void *hid, bool hid_panel, hipStream_t s) {
+  GemmArgs a = make_args(x, h, a_panel, n, gated ? 2 * fd : fd, h);
   a.B = w1;
   a.ldb = h;
   a.nz = D;
   const int64_t hp = hid_panel ? (int64_t)n * kPanel : 0;
+  if (gated) {
+    // the gated bf16 path needs whole 128-column blocks and 32-bit B offsets
+    if ((fd & 63) != 0 || (int64_t)(2 * fd + 256) * h * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    a.gate_rows = fd;
+    if (dtype == TSP_BF16) {
+      EpiSwiGLU<bf16> e{(bf16 *)hid, (int64_t)D * fd, hp, fd};
+      return run_gemm(dtype, a, e, s);
+    }
+    EpiSwiGLU<float> e{(float *)hid, (int64_t)D * fd, hp, fd};
+    return run_gemm(dtype, a, e, s);
+  }
   if (dtype == TSP_BF16) {
     EpiGelu<bf16> e{(bf16 *)hid, (int64_t)D * fd, hp, fd};
     return run_gemm(dtype, a, e, s);

@@ -80,9 +80,10 @@ hipError_t launch_outproj(int dtype, const void *o, bool a_panel, int32_t n, int
                           int32_t D, int32_t hd, const float *x, float *y, hipStream_t s);
 // MLP up over all D ring steps in one launch: hid[:, t*fd:(t+1)*fd] =
 // GELU(x w1[t]^T) in dtype, w1[t] [fd][h] the shard of ring step t; hid
-// [n][D*fd] (panel layout when hid_panel).
+// [n][D*fd] (panel layout when hid_panel). gated: w1[t] is [2fd][h] (gate
+// rows, then up rows) and hid = SiLU(x W_g^T) * (x W_u^T).
 hipError_t launch_mlp_up(int dtype, const void *x, bool a_panel, int32_t n, int32_t h, const PtrList &w1, int32_t D,
-                         int32_t fd, void *hid, bool hid_panel, hipStream_t s);
+                         int32_t fd, bool gated, void *hid, bool hid_panel, hipStream_t s);
 // y = (res ? res : 0) + sum_t hid[:, t*fd:(t+1)*fd] w2[t]^T in fp32, the
 // reduction walking ring steps t = 0..D-1 in order; w2[t] [h][fd]; res may
 // equal y.
@@ -95,13 +96,13 @@ hipError_t launch_mlp_down(int dtype, const void *hid, bool a_panel, int32_t n, 
 // hk <= hq). QKV writes fp32 q [m][D*hq] and k/v rows zz.pos(t) of
 // [*][D*hk] buffers (no Q factor).
 constexpr int32_t kLeadRows = 64;
-size_t lead_part_bytes(int32_t m, int32_t h, int32_t F, int32_t D);
+size_t lead_part_bytes(int32_t m, int32_t h, int32_t F, int32_t D, bool gated);
 hipError_t launch_lead_qkv(const float *a, int32_t m, int32_t h, const PtrList &w, int32_t D, int32_t hq, int32_t hk,
                            float *q, float *k, float *v, ZigzagMap zz, float *part, hipStream_t s);
 hipError_t launch_lead_outproj(const float *o, int32_t m, int32_t h, const PtrList &wo, int32_t D, int32_t hd,
                                const float *x, float *y, float *part, hipStream_t s);
 hipError_t launch_lead_mlp_up(const float *a, int32_t m, int32_t h, const PtrList &w1, int32_t D, int32_t fd,
-                              float *hid, float *part, hipStream_t s);
+                              bool gated, float *hid, float *part, hipStream_t s);
 hipError_t launch_lead_mlp_down(const float *hid, int32_t m, const PtrList &w2, int32_t D, int32_t fd, int32_t h,
                                 const float *res, float *y, float *part, hipStream_t s);
 
