@@ -49,6 +49,14 @@ Readings where the pages are silent (each is restated where it is used):
      (the SwiGLU form of common 7B models), then W_2 as in R5. Shard j holds
      hidden units j*F/D..(j+1)*F/D-1: its first matrix stacks the W_g rows of
      those units on the W_u rows of the same units, [2F/D, h].
+  R10 backward of the MLP ring (an optional extension; the pages give the
+     2.6x figure for training but describe only how shards move): the
+     gradients are those of the unsharded branch y = GELU(x W1^T) W2^T by the
+     chain rule. A rank's input gradient is summed over the shards it
+     receives, again with no all-reduce; its weight gradients are its own
+     tokens' contribution to each shard's gradient, and the D ranks'
+     contributions add up to the gradient over the whole sequence (the sum a
+     ring would carry back to the shard's owner).
 """
 from __future__ import annotations
 
@@ -68,6 +76,8 @@ __all__ = [
     "unshard_mlp_weights",
     "mlp",
     "mlp_shard",
+    "gelu_grad",
+    "mlp_backward",
     "layer_full",
     "layer_rows",
     "local_kv",
@@ -244,6 +254,44 @@ def mlp_shard(x, w1_j, w2_j, gated: bool = False) -> np.ndarray:
         wg, wu = np.split(_f64(w1_j), 2, axis=0)
         return (silu(x @ wg.T) * (x @ wu.T)) @ _f64(w2_j).T
     return gelu(x @ _f64(w1_j).T) @ _f64(w2_j).T
+
+
+# --------------------------------------------------------------------------
+# MLP backward (reading R10)
+# --------------------------------------------------------------------------
+def gelu_grad(z) -> np.ndarray:
+    """Derivative of the exact GELU (reading R5): Phi(z) + z * phi(z), with
+    phi(z) = exp(-z^2/2) / sqrt(2 pi) the standard normal density."""
+    z = _f64(z)
+    cdf = 0.5 * (1.0 + _erf(z / np.sqrt(2.0)))
+    pdf = np.exp(-0.5 * z * z) / np.sqrt(2.0 * np.pi)
+    return cdf + z * pdf
+
+
+def mlp_backward(x, w1, w2, dy) -> dict:
+    """Gradients of the MLP branch y = GELU(x W1^T) W2^T (readings R5, R10).
+
+    x: [n, h] branch input (the normalised tokens), w1/w2: the D shards
+    ([F/D, h] rows of W1, [h, F/D] columns of W2), dy: [n, h] gradient of the
+    branch output. With Z = x W1^T and H = GELU(Z), the chain rule gives
+    dH = dy W2, dZ = dH * GELU'(Z), dx = dZ W1, dW1 = dZ^T x, dW2 = dy^T H.
+    Returns dx [n, h] and the shard slices of dW1 and dW2 as lists indexed by
+    shard (the same split as the weights). Evaluated on a rank's own tokens
+    this is that rank's contribution to each shard's gradient.
+    """
+    x, dy = _f64(x), _f64(dy)
+    W1, W2 = unshard_mlp_weights(w1, w2)
+    Z = x @ W1.T
+    H = gelu(Z)
+    dZ = (dy @ W2) * gelu_grad(Z)
+    dW1 = dZ.T @ x
+    dW2 = dy.T @ H
+    fd = W1.shape[0] // len(w1)
+    return {
+        "dx": dZ @ W1,
+        "dw1": [dW1[j * fd:(j + 1) * fd] for j in range(len(w1))],
+        "dw2": [dW2[:, j * fd:(j + 1) * fd] for j in range(len(w2))],
+    }
 
 
 # --------------------------------------------------------------------------

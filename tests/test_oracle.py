@@ -527,6 +527,120 @@ def test_planted_mistakes_are_caught(monkeypatch):
     assert not np.allclose(oracle.mlp(xs, w1, w2, gated=True), ref, atol=1e-6)
 
 
+# ---------------------------------------------------------------- MLP backward
+def test_gelu_grad_closed_forms_and_identities():
+    # GELU'(0) = Phi(0) = 1/2; GELU(z) - GELU(-z) = z gives GELU'(z) + GELU'(-z) = 1
+    assert oracle.gelu_grad(0.0) == pytest.approx(0.5, abs=1e-15)
+    z = np.linspace(-6, 6, 241)
+    assert np.allclose(oracle.gelu_grad(z) + oracle.gelu_grad(-z), 1.0, atol=1e-14)
+    # GELU'(1) = Phi(1) + phi(1), from the textbook values Phi(1) = 0.841344746...
+    # and phi(1) = exp(-1/2)/sqrt(2 pi) = 0.241970724...
+    assert oracle.gelu_grad(1.0) == pytest.approx(0.8413447460685429 + 0.24197072451914337, abs=1e-14)
+    # tails: 1 far right, 0 far left
+    assert oracle.gelu_grad(40.0) == pytest.approx(1.0, abs=1e-15)
+    assert abs(oracle.gelu_grad(-40.0)) < 1e-15
+    # central differences of math.erf's GELU, and torch autograd fp64
+    gelu = lambda t: 0.5 * t * (1 + math.erf(t / math.sqrt(2)))  # noqa: E731
+    e = 1e-6
+    for t in (-3.1, -0.7, 0.2, 1.3, 4.0):
+        assert oracle.gelu_grad(t) == pytest.approx((gelu(t + e) - gelu(t - e)) / (2 * e), abs=1e-8)
+    tz = torch.from_numpy(z.copy()).requires_grad_(True)
+    F.gelu(tz).sum().backward()
+    assert np.allclose(oracle.gelu_grad(z), tz.grad.numpy(), atol=1e-14)
+
+
+def _torch_mlp_grads(x, W1, W2, dy):
+    tx = torch.from_numpy(x).requires_grad_(True)
+    t1 = torch.from_numpy(W1).requires_grad_(True)
+    t2 = torch.from_numpy(W2).requires_grad_(True)
+    y = F.linear(F.gelu(F.linear(tx, t1)), t2)
+    (y * torch.from_numpy(dy)).sum().backward()
+    return tx.grad.numpy(), t1.grad.numpy(), t2.grad.numpy()
+
+
+def test_mlp_backward_vs_torch_autograd():
+    rng = np.random.default_rng(11)
+    n, h, Fw, D = 13, 16, 64, 4
+    x = rng.standard_normal((n, h))
+    W1, W2 = 0.3 * rng.standard_normal((Fw, h)), 0.3 * rng.standard_normal((h, Fw))
+    dy = rng.standard_normal((n, h))
+    w1, w2 = _split_mlp(W1, W2, D)
+    got = oracle.mlp_backward(x, w1, w2, dy)
+    gx, g1, g2 = _torch_mlp_grads(x, W1, W2, dy)
+    assert np.allclose(got["dx"], gx, atol=1e-13)
+    assert np.allclose(np.concatenate(got["dw1"], axis=0), g1, atol=1e-13)
+    assert np.allclose(np.concatenate(got["dw2"], axis=1), g2, atol=1e-13)
+
+
+def test_mlp_backward_finite_differences():
+    """Central differences of L = sum(dy * y) with y from oracle.mlp (the
+    forward, pinned on its own) in chosen entries of x, W1 and W2."""
+    rng = np.random.default_rng(12)
+    n, h, Fw, D = 5, 6, 8, 2
+    x = rng.standard_normal((n, h))
+    W1, W2 = 0.5 * rng.standard_normal((Fw, h)), 0.5 * rng.standard_normal((h, Fw))
+    dy = rng.standard_normal((n, h))
+    got = oracle.mlp_backward(x, *_split_mlp(W1, W2, D), dy)
+    dW1, dW2 = np.concatenate(got["dw1"], axis=0), np.concatenate(got["dw2"], axis=1)
+    loss = lambda x_, a, b: float((dy * oracle.mlp(x_, *_split_mlp(a, b, D))).sum())  # noqa: E731
+    e = 1e-6
+    for (i, j) in [(0, 0), (2, 5), (4, 3)]:
+        xp, xm = x.copy(), x.copy()
+        xp[i, j] += e
+        xm[i, j] -= e
+        assert got["dx"][i, j] == pytest.approx((loss(xp, W1, W2) - loss(xm, W1, W2)) / (2 * e), abs=1e-7)
+    for (i, j) in [(0, 1), (5, 4), (7, 0)]:
+        ap, am = W1.copy(), W1.copy()
+        ap[i, j] += e
+        am[i, j] -= e
+        assert dW1[i, j] == pytest.approx((loss(x, ap, W2) - loss(x, am, W2)) / (2 * e), abs=1e-7)
+    for (i, j) in [(0, 7), (3, 2), (5, 5)]:
+        bp, bm = W2.copy(), W2.copy()
+        bp[i, j] += e
+        bm[i, j] -= e
+        assert dW2[i, j] == pytest.approx((loss(x, W1, bp) - loss(x, W1, bm)) / (2 * e), abs=1e-7)
+
+
+def test_mlp_backward_rank_contributions_sum_to_full_gradient():
+    """Reading R10: every rank's rows of dx are the full-sequence dx at its
+    positions, and the D ranks' weight-gradient contributions add up to the
+    gradient over the whole sequence."""
+    rng = np.random.default_rng(13)
+    S, D, h, Fw = 32, 4, 8, 32
+    x, dy = rng.standard_normal((2, S, h))
+    W1, W2 = 0.3 * rng.standard_normal((Fw, h)), 0.3 * rng.standard_normal((h, Fw))
+    w1, w2 = _split_mlp(W1, W2, D)
+    full = oracle.mlp_backward(x, w1, w2, dy)
+    acc1 = [np.zeros_like(a) for a in full["dw1"]]
+    acc2 = [np.zeros_like(a) for a in full["dw2"]]
+    for r in range(D):
+        pos = oracle.zigzag_positions(S, D, r)
+        part = oracle.mlp_backward(x[pos], w1, w2, dy[pos])
+        assert np.allclose(part["dx"], full["dx"][pos], atol=1e-13)
+        for j in range(D):
+            acc1[j] += part["dw1"][j]
+            acc2[j] += part["dw2"][j]
+    for j in range(D):
+        assert np.allclose(acc1[j], full["dw1"][j], atol=1e-12)
+        assert np.allclose(acc2[j], full["dw2"][j], atol=1e-12)
+
+
+def test_mlp_backward_planted_mistakes_are_caught(monkeypatch):
+    """GELU' without its z*phi(z) term, or the tanh form's derivative, misses
+    torch's gradients."""
+    rng = np.random.default_rng(14)
+    n, h, Fw, D = 7, 8, 16, 2
+    x = rng.standard_normal((n, h))
+    W1, W2 = 0.5 * rng.standard_normal((Fw, h)), 0.5 * rng.standard_normal((h, Fw))
+    dy = rng.standard_normal((n, h))
+    gx, g1, _ = _torch_mlp_grads(x, W1, W2, dy)
+    phi_only = lambda z: 0.5 * (1 + np.vectorize(math.erf)(np.asarray(z, dtype=np.float64) / math.sqrt(2)))  # noqa: E731
+    monkeypatch.setattr(oracle.tsp_oracle, "gelu_grad", phi_only)
+    bad = oracle.mlp_backward(x, *_split_mlp(W1, W2, D), dy)
+    assert not np.allclose(bad["dx"], gx, atol=1e-6)
+    assert not np.allclose(np.concatenate(bad["dw1"], axis=0), g1, atol=1e-6)
+
+
 # ---------------------------------------------------------------- synth
 def test_synth_deterministic_and_bf16_rounding():
     a = synth.normal((3, 5), 1, 7)
