@@ -284,6 +284,9 @@ class ClockSampler:
             return None
         self.stop_ev.set()
         self.thread.join()
+        # readings below 500 MHz are idle-state values left in the metrics
+        # table from before the load started (a loaded part runs far above)
+        self.samples = [v for v in self.samples if v >= 500]
         return round(statistics.mean(self.samples), 1) if self.samples else None
 
 
@@ -292,7 +295,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["layer", "mlp", "attn", "layers32"], default="layer")
+    ap.add_argument("--workload", choices=["layer", "mlp", "attn", "layers32", "mlp_bwd"], default="layer")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--rope-base", type=float, default=0.0,
                     help="rotary embedding base for the layer workloads (0 = none, the pages' model)")
@@ -341,7 +344,7 @@ def main():
     stream = torch.cuda.current_stream()
     flops = layer_flops(sh, r)
 
-    if args.workload in ("layer", "mlp"):
+    if args.workload in ("layer", "mlp", "mlp_bwd"):
         w = synth.layer_weights(sh, seed=seed)
         wd = {k: ([tsp.to_device(a, "bf16") for a in v] if isinstance(v, list) else tsp.to_device(v, "bf16"))
               for k, v in w.items()}
@@ -371,6 +374,24 @@ def main():
         step_exps = 0
         workload = (f"tsp_mlp_ring: 7B MLP ring ({mlp_note}), 16384x4096 bf16 local X, D=8 shards of "
                     f"{2 if sh.mlp == 'swiglu' else 1}x2048x4096 and 4096x2048")
+    elif args.workload == "mlp_bwd":
+        x = synth.activations(N, sh.h, seed=2, dtype="bf16")
+        dy = synth.activations(N, sh.h, seed=2, tid=synth.TID_DY, dtype="bf16")
+        xd, dyd = tsp.to_device(x, "bf16"), tsp.to_device(dy, "bf16")
+        fd = sh.F // sh.D
+        dx = torch.empty((N, sh.h), dtype=torch.float32, device="cuda")
+        dw1 = [torch.empty((fd, sh.h), dtype=torch.float32, device="cuda") for _ in range(sh.D)]
+        dw2 = [torch.empty((sh.h, fd), dtype=torch.float32, device="cuda") for _ in range(sh.D)]
+        ws = torch.empty(tsp.workspace_size(shape, tsp.TSP_WS_MLP_BWD), dtype=torch.uint8, device="cuda")
+
+        def step():
+            tsp.tsp_mlp_ring_bwd(shape, xd, wd["w1"], wd["w2"], dyd, None, dx, dw1, dw2, ws)
+        # algorithmic: the four products of the chain rule (dy W2, dZ W1, dZ^T x,
+        # dy^T GELU(Z)); the recomputation of Z = x W1^T is extra work, not counted
+        step_flops = 4 * 2.0 * N * sh.h * sh.F
+        step_exps = 0
+        workload = ("tsp_mlp_ring_bwd: backward of the 7B MLP ring (FFN), 16384x4096 bf16 local x and dy, D=8 shards "
+                    "of 2048x4096 and 4096x2048; dx, dW1, dW2 in fp32 (Z recomputed)")
     elif args.workload == "layers32":
         # 32 layers resident in HBM (82 GB of weights and K/V), each with its
         # own weights and remote K/V, generated on the GPU from a fixed seed:
@@ -489,6 +510,12 @@ def main():
                     # counters were taken on rank 0 with 32 K/V heads
                     "traffic": (traffic_from_profile(os.path.join(ROOT, "tsp_rank_local_amd", "csrc", "attention.hip"),
                                                      "attention_7b") if r == 0 and sh.kv_heads == sh.H else None)}
+    elif "bwd_gemm" in kernels:
+        # five launches of one product size each (Z recomputation, dZ, dW1, dW2, dx)
+        t_g = kernels["bwd_gemm"]["ms_per_launch"] * 1e-3
+        achieved = 2.0 * N * sh.h * sh.F / t_g / 1e12
+        roofline = {"kernel": "gemm_bf16_kernel (MLP backward products)", "bound": "mfma", "achieved": achieved,
+                    "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_BF16, "traffic": None}
     elif "mlp_up" in kernels:
         # one launch covers the up products of all D ring steps
         t_up = kernels["mlp_up"]["ms_per_launch"] * 1e-3

@@ -143,7 +143,7 @@ typedef struct {
 enum { TSP_PHASE_KV = 1, TSP_PHASE_REST = 2, TSP_PHASE_ALL = 3 };
 
 /* Workspace kinds for tsp_workspace_size. */
-enum { TSP_WS_MLP = 0, TSP_WS_LAYER = 1 };
+enum { TSP_WS_MLP = 0, TSP_WS_LAYER = 1, TSP_WS_MLP_BWD = 2 };
 
 /* Kernel classes for the optional launch timing. */
 enum {
@@ -155,7 +155,9 @@ enum {
   TSP_K_MLP_DOWN = 5,
   TSP_K_ZIGZAG = 6,
   TSP_K_LEAD = 7, /* the fp32 recomputation of the leading rows (see tsp_layer_fwd) */
-  TSP_K_COUNT = 8
+  TSP_K_BWD_GEMM = 8,  /* the products of tsp_mlp_ring_bwd */
+  TSP_K_TRANSPOSE = 9, /* the layout changes of tsp_mlp_ring_bwd */
+  TSP_K_COUNT = 10
 };
 
 /* Static text for a status code. */
@@ -168,7 +170,8 @@ const char *tsp_last_error(void);
 int tsp_abi_version(void);
 
 /* Bytes of scratch the call 'which' (TSP_WS_MLP for tsp_mlp_ring,
- * TSP_WS_LAYER for tsp_layer_fwd) needs for this shape. */
+ * TSP_WS_LAYER for tsp_layer_fwd, TSP_WS_MLP_BWD for tsp_mlp_ring_bwd)
+ * needs for this shape. */
 tsp_status tsp_workspace_size(const tsp_shape *shape, int which, size_t *bytes);
 
 /* Zigzag token ownership (reading above; the pages name a zigzag partition
@@ -213,6 +216,33 @@ tsp_status tsp_zigzag_attn_ex(const tsp_shape *shape, const void *q, const void 
 tsp_status tsp_mlp_ring(const tsp_shape *shape, const void *x, const void *const *w1,
                         const void *const *w2, const float *residual, float *y, void *ws,
                         size_t ws_bytes, void *stream);
+
+/* Backward of the MLP ring on rank r (an optional extension: the pages quote
+ * their 2.6x for training, [P2] paragraph 1, but describe only how the
+ * shards move, paragraph 2). With Z = x W1^T and y = GELU(Z) W2^T summed over
+ * the shards, and dy the gradient of y:
+ *   dx     = dx_residual + sum over ring steps t of (dy W2_j * GELU'(Z_j)) W1_j,
+ *            j = (r - t) mod D, reduced in fp32 in that order (again with no
+ *            all-reduce: every rank sums the shards it receives itself);
+ *   dw1[j] = dZ_j^T x   [F/D][h],  dZ_j = (dy W2_j) * GELU'(Z_j);
+ *   dw2[j] = dy^T GELU(Z_j)   [h][F/D];
+ * the weight gradients being this rank's own tokens' contribution (the D
+ * ranks' contributions add up to the shard's gradient over the sequence, the
+ * sum a ring would carry back to the shard's owner). GELU MLP only
+ * (tsp_shape.mlp = TSP_MLP_GELU, else TSP_ERR_UNSUPPORTED); S/D must be a
+ * multiple of 64.
+ *  x, dy: [S/D][h] (dtype), the branch input of tsp_mlp_ring and the gradient
+ *  of its output; w1, w2: (host) arrays of D device pointers, shard layout as
+ *  in tsp_layer_weights. dx_residual: [S/D][h] fp32 or NULL (then zero); it
+ *  may equal dx. dx: [S/D][h] fp32, dw1/dw2: (host) arrays of D device
+ *  pointers to fp32 buffers, all fully written. Z is recomputed (Z and
+ *  GELU(Z) rounded to dtype once, as the forward stores GELU(Z)); dZ is
+ *  rounded to dtype once; every product accumulates in fp32.
+ *  ws: device scratch of at least tsp_workspace_size(TSP_WS_MLP_BWD) bytes. */
+tsp_status tsp_mlp_ring_bwd(const tsp_shape *shape, const void *x, const void *const *w1,
+                            const void *const *w2, const void *dy, const float *dx_residual,
+                            float *dx, float *const *dw1, float *const *dw2, void *ws,
+                            size_t ws_bytes, void *stream);
 
 /* One decoder layer forward on rank r's S/D tokens.
  *  x: [S/D][h] fp32, local rows in zigzag order.

@@ -33,6 +33,7 @@ TID_W2 = 13
 TID_K_REMOTE = 20
 TID_V_REMOTE = 21
 TID_Q = 22
+TID_DY = 30  # gradient arriving at a branch output (backward tests)
 
 
 @dataclasses.dataclass(frozen=True)

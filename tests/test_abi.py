@@ -186,6 +186,43 @@ def test_mlp_errors():
         tsp.tsp_mlp_ring(s, FAKE, w, w, None, FAKE + 256, FAKE + (3 << 32), need, stream=0)
 
 
+def test_mlp_bwd_workspace_and_errors():
+    # W1 stacked, W1^T, W2^T ([F][h] each), x^T and dy^T ([h][N]), Z^T and
+    # GELU(Z)^T ([F][N]), all in the dtype
+    for dtype, e in (("f32", 4), ("bf16", 2)):
+        s = _shape(dtype=dtype)
+        N, h, F = 256, 256, 1024
+        assert tsp.workspace_size(s, tsp.TSP_WS_MLP_BWD) == (3 * F * h + 2 * h * N + 2 * F * N) * e
+    s7 = tsp.make_shape(131072, 8, 3, 4096, 32, 128, 16384, dtype="bf16")
+    assert tsp.workspace_size(s7, tsp.TSP_WS_MLP_BWD) == (3 * 16384 * 4096 + 2 * 4096 * 16384 + 2 * 16384 ** 2) * 2
+    s = _shape(dtype="bf16")
+    need = tsp.workspace_size(s, tsp.TSP_WS_MLP_BWD)
+    w = [FAKE + (i << 24) for i in range(4)]
+    g = [FAKE + (1 << 36) + (i << 24) for i in range(4)]
+    x, dy, dx, ws = FAKE + (1 << 32), FAKE + (2 << 32), FAKE + (3 << 32), FAKE + (4 << 32)
+
+    def call(shape=s, x=x, dy=dy, dx=dx, dw1=g, dw2=g, ws=ws, nbytes=need, res=None):
+        with pytest.raises(tsp.TspError) as ei:
+            tsp.tsp_mlp_ring_bwd(shape, x, w, w, dy, res, dx, dw1, dw2, ws, nbytes, stream=0)
+        return ei.value.status, tsp.lib().tsp_last_error()
+
+    assert call(nbytes=need - 1)[0] == tsp.TSP_ERR_WORKSPACE
+    bad = list(g)
+    bad[1] = None
+    st, msg = call(dw2=bad)
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"dw2[1]" in msg
+    assert call(dx=x + 512)[0] == tsp.TSP_ERR_INVALID_ARG                       # dx overlaps x
+    assert call(dw1=[ws + 256] + g[1:])[0] == tsp.TSP_ERR_INVALID_ARG           # dW1 inside the workspace
+    assert call(res=dx + 64)[0] == tsp.TSP_ERR_INVALID_ARG                      # residual partly over dx
+    assert call(dy=dy + 8)[0] == tsp.TSP_ERR_INVALID_ARG                        # misaligned
+    assert call(shape=_shape(dtype="bf16", mlp="swiglu"))[0] == tsp.TSP_ERR_UNSUPPORTED
+    # S/D = 96 tokens: not a multiple of 64 (K of the weight-gradient products)
+    st = call(shape=tsp.make_shape(384, 4, 0, 256, 4, 64, 1024, dtype="bf16"), nbytes=1 << 40)[0]
+    assert st == tsp.TSP_ERR_UNSUPPORTED
+    with pytest.raises(tsp.TspError):
+        tsp.workspace_size(_shape(dtype="bf16", mlp="swiglu"), tsp.TSP_WS_MLP_BWD)
+
+
 def test_layer_errors():
     s = _shape()
     w = dict(g_attn=FAKE, g_mlp=FAKE, wqkv=[FAKE] * 4, wo=[FAKE] * 4, w1=[FAKE] * 4, w2=[FAKE] * 4)

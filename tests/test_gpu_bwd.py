@@ -1,0 +1,160 @@
+"""GPU parity of the MLP ring backward (tsp_mlp_ring_bwd) against the fp64
+oracle's chain-rule gradients: small shapes in both dtypes on every rank
+(ragged tiles, shards narrower than a tile, the residual in place), the D
+ranks' weight-gradient contributions summed against the gradient over the
+whole sequence, and the 7B shape with sampled rows of dx and sampled hidden
+units of dW1 and dW2."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import tsp_rank_local_amd as tsp
+from gpu_util import TOL_BF16, TOL_F32, assert_close, down, f64, log, torch_cuda, up
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_cuda()
+    tsp.lib()
+    return t
+
+
+def _run(torch, s, x, w1, w2, dy, res=None, in_place=False):
+    """Calls tsp_mlp_ring_bwd; returns dx, dw1, dw2 as float64 numpy (dw lists by shard)."""
+    D, N, h, fd = s.D, s.S // s.D, s.h, s.F // s.D
+    ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_MLP_BWD), dtype=torch.uint8, device="cuda")
+    if in_place:
+        dx = res.clone()
+        resd = dx
+    else:
+        dx = torch.full((N, h), float("nan"), dtype=torch.float32, device="cuda")
+        resd = res
+    dw1 = [torch.full((fd, h), float("nan"), dtype=torch.float32, device="cuda") for _ in range(D)]
+    dw2 = [torch.full((h, fd), float("nan"), dtype=torch.float32, device="cuda") for _ in range(D)]
+    tsp.tsp_mlp_ring_bwd(s, x, w1, w2, dy, resd, dx, dw1, dw2, ws)
+    torch.cuda.synchronize()
+    return down(dx), [down(a) for a in dw1], [down(a) for a in dw2]
+
+
+def _check(got, want, tol, tag):
+    dx, dw1, dw2 = got
+    assert_close(dx, want["dx"], tol, f"dx {tag}")
+    assert_close(np.concatenate(dw1, axis=0), np.concatenate(want["dw1"], axis=0), tol, f"dW1 {tag}")
+    assert_close(np.concatenate(dw2, axis=1), np.concatenate(want["dw2"], axis=1), tol, f"dW2 {tag}")
+
+
+BWD_CASES = [
+    # S, D, h, F, dtype
+    (1024, 4, 256, 1024, "f32"),   # the tiny fp32 layer's MLP
+    (2048, 4, 256, 1024, "bf16"),  # 512 tokens: two token tiles
+    (640, 2, 320, 384, "bf16"),    # 320 tokens, h = 320, F/D = 192: ragged tiles, shard not a multiple of 128
+    (1024, 8, 192, 512, "bf16"),   # F/D = 64: half a tile of hidden units per shard
+    (128, 1, 64, 64, "bf16"),      # D = 1, one tile everywhere
+]
+
+
+@pytest.mark.parametrize("S,D,h,F,dtype", BWD_CASES)
+def test_mlp_ring_bwd_every_rank(torch, S, D, h, F, dtype):
+    shape = synth.LayerShape(S=S, D=D, h=h, H=h // 64, Dh=64, F=F, dtype=dtype)
+    N = S // D
+    w = synth.layer_weights(shape, seed=41)
+    x = synth.activations(N, h, seed=41, dtype=dtype)
+    dy = synth.activations(N, h, seed=41, tid=synth.TID_DY, dtype=dtype)
+    w1d, w2d = [up(a, dtype) for a in w["w1"]], [up(a, dtype) for a in w["w2"]]
+    want = oracle.mlp_backward(f64(x, dtype), [f64(a, dtype) for a in w["w1"]], [f64(a, dtype) for a in w["w2"]],
+                               f64(dy, dtype))
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    for r in range(D):
+        s = tsp.make_shape(S, D, r, h, h // 64, 64, F, dtype=dtype)
+        log(f"mlp ring bwd S={S} D={D} r={r} h={h} F={F} {dtype}")
+        _check(_run(torch, s, up(x, dtype), w1d, w2d, up(dy, dtype)), want, tol, f"r={r}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mlp_ring_bwd_residual_in_place(torch, dtype):
+    S, D, h, F = 1024, 4, 256, 1024
+    shape = synth.LayerShape(S=S, D=D, h=h, H=4, Dh=64, F=F, dtype=dtype)
+    N = S // D
+    w = synth.layer_weights(shape, seed=42)
+    x = synth.activations(N, h, seed=42, dtype=dtype)
+    dy = synth.activations(N, h, seed=42, tid=synth.TID_DY, dtype=dtype)
+    res = synth.activations(N, h, seed=43)
+    want = oracle.mlp_backward(f64(x, dtype), [f64(a, dtype) for a in w["w1"]], [f64(a, dtype) for a in w["w2"]],
+                               f64(dy, dtype))
+    want["dx"] = want["dx"] + res.astype(np.float64)
+    s = tsp.make_shape(S, D, 1, h, 4, 64, F, dtype=dtype)
+    log(f"mlp ring bwd residual == dx, {dtype}")
+    got = _run(torch, s, up(x, dtype), [up(a, dtype) for a in w["w1"]], [up(a, dtype) for a in w["w2"]],
+               up(dy, dtype), up(res, "f32"), in_place=True)
+    _check(got, want, TOL_F32 if dtype == "f32" else TOL_BF16, "residual")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mlp_ring_bwd_rank_contributions_sum(torch, dtype):
+    """D emulated ranks, each on its own zigzag tokens of one sequence: every
+    rank's dx rows are the full-sequence dx at its positions, and the ranks'
+    weight-gradient contributions add up to the whole sequence's gradient."""
+    S, D, h, F = 2048, 4, 256, 512
+    shape = synth.LayerShape(S=S, D=D, h=h, H=4, Dh=64, F=F, dtype=dtype)
+    w = synth.layer_weights(shape, seed=44)
+    x = synth.activations(S, h, seed=44, dtype=dtype)
+    dy = synth.activations(S, h, seed=44, tid=synth.TID_DY, dtype=dtype)
+    w1_64, w2_64 = [f64(a, dtype) for a in w["w1"]], [f64(a, dtype) for a in w["w2"]]
+    full = oracle.mlp_backward(f64(x, dtype), w1_64, w2_64, f64(dy, dtype))
+    w1d, w2d = [up(a, dtype) for a in w["w1"]], [up(a, dtype) for a in w["w2"]]
+    acc1 = [np.zeros_like(a) for a in full["dw1"]]
+    acc2 = [np.zeros_like(a) for a in full["dw2"]]
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    for r in range(D):
+        pos = oracle.zigzag_positions(S, D, r)
+        s = tsp.make_shape(S, D, r, h, 4, 64, F, dtype=dtype)
+        log(f"mlp ring bwd, emulated rank {r} of {D}, {dtype}")
+        dx, dw1, dw2 = _run(torch, s, up(x[pos], dtype), w1d, w2d, up(dy[pos], dtype))
+        assert_close(dx, full["dx"][pos], tol, f"dx rows of rank {r}")
+        for j in range(D):
+            acc1[j] += dw1[j]
+            acc2[j] += dw2[j]
+    assert_close(np.concatenate(acc1, axis=0), np.concatenate(full["dw1"], axis=0), tol, "sum of dW1 contributions")
+    assert_close(np.concatenate(acc2, axis=1), np.concatenate(full["dw2"], axis=1), tol, "sum of dW2 contributions")
+
+
+@pytest.mark.timeout(900)
+def test_mlp_ring_bwd_7b(torch):
+    """7B shape (16384 tokens, h 4096, F 16384, D 8), ring starts r = 0 and 5:
+    dx on 64 strided rows (each needs its whole hidden row), dW1 rows and dW2
+    columns of 48 strided hidden units (each needs that unit's pre-activation
+    over all tokens), against the oracle's chain rule on those slices."""
+    SH = synth.SEVEN_B
+    N, h, F, D = SH.N, SH.h, SH.F, SH.D
+    fd = F // D
+    w = synth.layer_weights(SH, seed=45)
+    x = synth.activations(N, h, seed=45, dtype="bf16")
+    dy = synth.activations(N, h, seed=45, tid=synth.TID_DY, dtype="bf16")
+    x64, dy64 = f64(x, "bf16"), f64(dy, "bf16")
+    W1 = np.concatenate([f64(a, "bf16") for a in w["w1"]], axis=0)
+    W2 = np.concatenate([f64(a, "bf16") for a in w["w2"]], axis=1)
+    rows = np.linspace(0, N - 1, 64).round().astype(np.int64)
+    units = np.linspace(0, F - 1, 48).round().astype(np.int64)
+    # dx rows: the oracle on those tokens alone (each token's dx depends only on its own x and dy)
+    want_dx = oracle.mlp_backward(x64[rows], [f64(a, "bf16") for a in w["w1"]],
+                                  [f64(a, "bf16") for a in w["w2"]], dy64[rows])["dx"]
+    # hidden units: Z[:, f], GELU and GELU' over all tokens, written from the chain rule
+    Zu = x64 @ W1[units].T
+    dZu = (dy64 @ W2[:, units]) * oracle.gelu_grad(Zu)
+    want_dw1 = dZu.T @ x64             # [units, h]
+    want_dw2 = dy64.T @ oracle.gelu(Zu)  # [h, units]
+    xd, dyd = up(x, "bf16"), up(dy, "bf16")
+    w1d, w2d = [up(a, "bf16") for a in w["w1"]], [up(a, "bf16") for a in w["w2"]]
+    for r in (0, 5):
+        s = tsp.make_shape(SH.S, D, r, h, SH.H, SH.Dh, F, dtype="bf16")
+        log(f"mlp ring bwd 7B, ring start r={r}")
+        dx, dw1, dw2 = _run(torch, s, xd, w1d, w2d, dyd)
+        assert_close(dx[rows], want_dx, TOL_BF16, f"dx rows (r={r})")
+        g1 = np.stack([dw1[u // fd][u % fd] for u in units])
+        g2 = np.stack([dw2[u // fd][:, u % fd] for u in units], axis=1)
+        assert_close(g1, want_dw1, TOL_BF16, f"dW1 rows of sampled units (r={r})")
+        assert_close(g2, want_dw2, TOL_BF16, f"dW2 columns of sampled units (r={r})")
+        assert all(np.isfinite(a).all() for a in dw1 + dw2) and np.isfinite(dx).all()

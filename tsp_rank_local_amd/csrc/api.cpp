@@ -166,6 +166,38 @@ size_t mlp_ws(const tsp_shape *s) {
   return align256((size_t)(s->S / s->D) * (size_t)s->F * elem_bytes(s->dtype));
 }
 
+// MLP backward scratch: the weights rearranged for the products (W1 stacked
+// in ring order [F][h], its transpose [h][F], W2 transposed [F][h]), x^T and
+// dy^T [h][N], Z^T (later dZ^T) and GELU(Z)^T [F][N]; the last also holds dZ
+// [N][F] once GELU(Z)^T has been used.
+struct MlpBwdWs {
+  size_t w1cat, w1t, w2t, xt, dyt, zt, ht, total;
+};
+
+MlpBwdWs mlp_bwd_ws(const tsp_shape *s) {
+  const size_t e = elem_bytes(s->dtype), N = (size_t)(s->S / s->D), h = (size_t)s->h, F = (size_t)s->F;
+  MlpBwdWs w;
+  w.w1cat = 0;
+  w.w1t = w.w1cat + align256(F * h * e);
+  w.w2t = w.w1t + align256(F * h * e);
+  w.xt = w.w2t + align256(F * h * e);
+  w.dyt = w.xt + align256(h * N * e);
+  w.zt = w.dyt + align256(h * N * e);
+  w.ht = w.zt + align256(F * N * e);
+  w.total = w.ht + align256(F * N * e);
+  return w;
+}
+
+tsp_status check_mlp_bwd_shape(const tsp_shape *s) {
+  tsp_status st = check_mlp_shape(s);
+  if (st) return st;
+  if (s->mlp != TSP_MLP_GELU) return fail(TSP_ERR_UNSUPPORTED, "the MLP backward covers the GELU MLP only");
+  if ((s->S / s->D) % 64 != 0) return fail(TSP_ERR_UNSUPPORTED, "S/D=%lld must be a multiple of 64", (long long)(s->S / s->D));
+  if ((int64_t)s->F * s->h >= (int64_t(1) << 31) / 2)
+    return fail(TSP_ERR_UNSUPPORTED, "F*h=%lld is too large", (long long)s->F * s->h);
+  return TSP_OK;
+}
+
 tsp_status hip_fail(hipError_t e, const char *what) {
   return fail(TSP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -280,6 +312,9 @@ tsp_status tsp_workspace_size(const tsp_shape *s, int which, size_t *bytes) {
   } else if (which == TSP_WS_LAYER) {
     if ((st = check_layer_shape(s))) return st;
     *bytes = layer_ws(s).total;
+  } else if (which == TSP_WS_MLP_BWD) {
+    if ((st = check_mlp_bwd_shape(s))) return st;
+    *bytes = mlp_bwd_ws(s).total;
   } else {
     return fail(TSP_ERR_INVALID_ARG, "unknown workspace kind %d", which);
   }
@@ -374,6 +409,82 @@ tsp_status tsp_mlp_ring(const tsp_shape *s, const void *x, const void *const *w1
   TSP_LAUNCH(TSP_K_MLP_DOWN,
              tsp::launch_mlp_down(s->dtype, ws, pnl, N, ring_list(w2, s->D, s->r), s->D, fd, h, residual, y, stream),
              "MLP down");
+  return ok();
+}
+
+tsp_status tsp_mlp_ring_bwd(const tsp_shape *s, const void *x, const void *const *w1, const void *const *w2,
+                            const void *dy, const float *dx_residual, float *dx, float *const *dw1, float *const *dw2,
+                            void *ws, size_t ws_bytes, void *stream_) {
+  tsp_status st = check_mlp_bwd_shape(s);
+  if (st) return st;
+  if ((st = check_ptr(x, "x")) || (st = check_ptr(dy, "dy")) || (st = check_ptr(dx, "dx")) ||
+      (st = check_ptr(ws, "ws")))
+    return st;
+  if (dx_residual && !aligned16(dx_residual)) return fail(TSP_ERR_INVALID_ARG, "dx_residual is not 16-byte aligned");
+  if ((st = check_ptr_list(w1, s->D, "w1")) || (st = check_ptr_list(w2, s->D, "w2")) ||
+      (st = check_ptr_list((const void *const *)dw1, s->D, "dw1")) ||
+      (st = check_ptr_list((const void *const *)dw2, s->D, "dw2")))
+    return st;
+  const MlpBwdWs L = mlp_bwd_ws(s);
+  if (ws_bytes < L.total) return fail(TSP_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, L.total);
+  const int32_t N = (int32_t)(s->S / s->D), h = s->h, F = s->F, D = s->D, fd = F / D;
+  const size_t e = elem_bytes(s->dtype);
+  const Range rdx{dx, (size_t)N * h * 4, "dx"}, rx{x, (size_t)N * h * e, "x"}, rdy{dy, (size_t)N * h * e, "dy"},
+      rw{ws, L.total, "ws"};
+  if (overlap(rdx, rx) || overlap(rdx, rdy) || overlap(rdx, rw) || overlap(rx, rw) || overlap(rdy, rw))
+    return fail(TSP_ERR_INVALID_ARG, "x, dy, dx and ws must not overlap");
+  if (dx_residual && dx_residual != dx && overlap(Range{dx_residual, (size_t)N * h * 4, "dx_residual"}, rdx))
+    return fail(TSP_ERR_INVALID_ARG, "dx_residual overlaps dx without being equal to it");
+  for (int j = 0; j < D; ++j) {
+    const Range r1{dw1[j], (size_t)fd * h * 4, "dw1"}, r2{dw2[j], (size_t)h * fd * 4, "dw2"};
+    if (overlap(r1, rw) || overlap(r2, rw) || overlap(r1, rdx) || overlap(r2, rdx))
+      return fail(TSP_ERR_INVALID_ARG, "dw1[%d]/dw2[%d] overlap dx or ws", j, j);
+  }
+  hipStream_t stream = (hipStream_t)stream_;
+  unsigned char *base = (unsigned char *)ws;
+  void *w1cat = base + L.w1cat, *w1t = base + L.w1t, *w2t = base + L.w2t, *xt = base + L.xt, *dyt = base + L.dyt,
+       *zt = base + L.zt, *ht = base + L.ht;
+  const bool bf = s->dtype == TSP_BF16;
+  const tsp::PtrList r1 = ring_list(w1, D, s->r), r2 = ring_list(w2, D, s->r);
+  // weights in ring-step order: W1 rows stacked, W1^T and W2^T
+  for (int t = 0; t < D; ++t) {
+    hipError_t err = hipMemcpyAsync(base + L.w1cat + (size_t)t * fd * h * e, r1.p[t], (size_t)fd * h * e,
+                                    hipMemcpyDeviceToDevice, stream);
+    if (err != hipSuccess) return hip_fail(err, "W1 copy");
+  }
+  TSP_LAUNCH(TSP_K_TRANSPOSE, tsp::launch_transpose(s->dtype, r1, D, h, 0, fd, h, w1t, F, 0, fd, stream), "W1 transpose");
+  TSP_LAUNCH(TSP_K_TRANSPOSE,
+             tsp::launch_transpose(s->dtype, r2, D, fd, 0, h, fd, w2t, h, 0, (int64_t)fd * h, stream), "W2 transpose");
+  // activations with the token axis innermost (K of the weight gradients)
+  tsp::PtrList lx{}, ldy{};
+  lx.p[0] = x;
+  ldy.p[0] = dy;
+  TSP_LAUNCH(TSP_K_TRANSPOSE, tsp::launch_transpose(s->dtype, lx, 1, h, 0, N, h, xt, N, 0, 0, stream), "x transpose");
+  TSP_LAUNCH(TSP_K_TRANSPOSE,
+             tsp::launch_transpose(s->dtype, ldy, 1, h, 0, N, h, dyt, N, bf ? (int64_t)h * 64 : 0, 0, stream),
+             "dy transpose");
+  // Z^T and GELU(Z)^T, then dZ^T = (W2^T dy^T) * GELU'(Z^T) in place
+  TSP_LAUNCH(TSP_K_BWD_GEMM, tsp::launch_mlp_bwd_recompute(s->dtype, w1cat, F, h, x, N, zt, bf, ht, stream),
+             "MLP backward Z");
+  TSP_LAUNCH(TSP_K_BWD_GEMM, tsp::launch_mlp_bwd_dz(s->dtype, w2t, F, h, dy, N, zt, bf, stream), "MLP backward dZ");
+  // weight gradients of every ring step's shard: dW1 = dZ^T x, dW2 = dy^T GELU(Z)
+  TSP_LAUNCH(TSP_K_BWD_GEMM,
+             tsp::launch_wgrad(s->dtype, zt, bf, F, xt, h, N, ring_list((const void *const *)dw1, D, s->r), fd, true,
+                               stream),
+             "MLP backward dW1");
+  TSP_LAUNCH(TSP_K_BWD_GEMM,
+             tsp::launch_wgrad(s->dtype, dyt, bf, h, ht, F, N, ring_list((const void *const *)dw2, D, s->r), fd, false,
+                               stream),
+             "MLP backward dW2");
+  // dZ [N][F] over the GELU(Z)^T buffer, then dx = dZ W1 reduced in ring order
+  tsp::PtrList lz{};
+  lz.p[0] = zt;
+  TSP_LAUNCH(TSP_K_TRANSPOSE,
+             tsp::launch_transpose(s->dtype, lz, 1, N, bf ? (int64_t)F * 64 : 0, F, N, ht, F, bf ? (int64_t)N * 64 : 0,
+                                   0, stream),
+             "dZ transpose");
+  TSP_LAUNCH(TSP_K_BWD_GEMM, tsp::launch_mlp_bwd_dx(s->dtype, ht, bf, N, F, w1t, h, dx_residual, dx, stream),
+             "MLP backward dx");
   return ok();
 }
 

@@ -47,6 +47,20 @@ __device__ __forceinline__ float gelu_erf(float z) {
   return z * (z >= 0.0f ? 1.0f - q : q);
 }
 
+// GELU'(z) = Phi(z) + z phi(z) in fp32, phi(z) = exp(-z^2/2) / sqrt(2 pi):
+// Phi from the same erf approximation as gelu_erf, and exp(-z^2/2) is the
+// factor that approximation already needs.
+__device__ __forceinline__ float gelu_erf_grad(float z) {
+  constexpr float p = 0.3275911f, a1 = 0.254829592f, a2 = -0.284496736f, a3 = 1.421413741f,
+                  a4 = -1.453152027f, a5 = 1.061405429f;
+  const float x = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(p, x, 1.0f));
+  const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
+  const float e = __builtin_amdgcn_exp2f(z * z * -0.72134752044448170f);
+  const float q = 0.5f * poly * e;
+  return fmaf(z * 0.39894228040143268f, e, z >= 0.0f ? 1.0f - q : q);
+}
+
 // SiLU z * sigma(z) = z / (1 + e^-z) in fp32, e^-z as exp2(-z log2 e): for
 // z -> -inf, e^-z overflows to inf and the result goes to -0; for z -> +inf
 // it goes to z.

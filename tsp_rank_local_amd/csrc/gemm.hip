@@ -297,6 +297,132 @@ struct EpiQKV {
 };
 
 // ---------------------------------------------------------------- tile order
+// ---------------------------------------------------------------- backward epilogues
+template <typename T>
+__device__ __forceinline__ float4 load4(const T *p) {
+  if constexpr (sizeof(T) == 4) {
+    return *reinterpret_cast<const float4 *>(p);
+  } else {
+    // a bf16 is the upper half of the fp32 with the same value
+    const u32x2 u = *reinterpret_cast<const u32x2 *>(p);
+    return make_float4(__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
+                       __uint_as_float(u[1] & 0xffff0000u));
+  }
+}
+__device__ __forceinline__ float4 gelu4(float4 v) {
+  return make_float4(gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w));
+}
+
+// Z^T of the MLP backward: rows are hidden units, columns tokens. zt = Z^T
+// (row-major with pitch ld, or panel layout when panel != 0) and ht = GELU(Z^T)
+// (row-major, pitch ld), both rounded once from the fp32 product.
+template <typename T>
+struct EpiZH {
+  T *zt, *ht;
+  int64_t ld, panel;
+  __device__ __forceinline__ T *zat(int r, int c) const {
+    return zt + (panel ? panel_index(r, c, panel) : (int64_t)r * ld + c);
+  }
+  __device__ __forceinline__ void operator()(int, int r, int c, float v) const {
+    *zat(r, c) = (T)v;
+    ht[(int64_t)r * ld + c] = (T)gelu_erf(v);
+  }
+  __device__ __forceinline__ void operator()(int, int r, int c, float4 v) const {
+    store4(zat(r, c), v);
+    store4(ht + (int64_t)r * ld + c, gelu4(v));
+  }
+  struct Row {
+    T *z[2];
+    T *h;
+  };
+  __device__ __forceinline__ bool fast_ok() const { return true; }
+  __device__ __forceinline__ Row row(int, int r, int c0, int g) const {
+    Row w;
+    w.z[0] = zat(r, c0 + 4 * g);
+    w.z[1] = panel ? w.z[0] + panel : w.z[0] + 64;
+    w.h = ht + (int64_t)r * ld + c0 + 4 * g;
+    return w;
+  }
+  __device__ __forceinline__ void put_row(const Row &w, const float4 (&v)[4][4]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        store4(w.z[i >> 1] + (i & 1) * 32 + vq * 8, v[i][vq]);
+        store4(w.h + i * 32 + vq * 8, gelu4(v[i][vq]));
+      }
+  }
+};
+
+// dZ^T = acc * GELU'(Z^T), in place over the Z^T buffer of EpiZH (each
+// element is read and then written by the same lane).
+template <typename T>
+struct EpiDZ {
+  T *zt;
+  int64_t ld, panel;
+  __device__ __forceinline__ T *zat(int r, int c) const {
+    return zt + (panel ? panel_index(r, c, panel) : (int64_t)r * ld + c);
+  }
+  __device__ __forceinline__ static float4 dz4(float4 v, float4 z) {
+    return make_float4(v.x * gelu_erf_grad(z.x), v.y * gelu_erf_grad(z.y), v.z * gelu_erf_grad(z.z),
+                       v.w * gelu_erf_grad(z.w));
+  }
+  __device__ __forceinline__ void operator()(int, int r, int c, float v) const {
+    T *p = zat(r, c);
+    *p = (T)(v * gelu_erf_grad((float)*p));
+  }
+  __device__ __forceinline__ void operator()(int, int r, int c, float4 v) const {
+    T *p = zat(r, c);
+    store4(p, dz4(v, load4(p)));
+  }
+  struct Row {
+    T *z[2];
+  };
+  __device__ __forceinline__ bool fast_ok() const { return true; }
+  __device__ __forceinline__ Row row(int, int r, int c0, int g) const {
+    Row w;
+    w.z[0] = zat(r, c0 + 4 * g);
+    w.z[1] = panel ? w.z[0] + panel : w.z[0] + 64;
+    return w;
+  }
+  __device__ __forceinline__ void put_row(const Row &w, const float4 (&v)[4][4]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        T *p = w.z[i >> 1] + (i & 1) * 32 + vq * 8;
+        store4(p, dz4(v[i][vq], load4(p)));
+      }
+  }
+};
+
+// fp32 weight gradient split over shards: by rows (row m -> shard m / split,
+// pitch ld) or by columns (column c -> shard c / split, pitch split).
+struct EpiShardF32 {
+  PtrList out;
+  int32_t split;
+  int64_t ld;
+  bool by_rows;
+  __device__ __forceinline__ float *at(int r, int c) const {
+    if (by_rows) return (float *)out.p[r / split] + (int64_t)(r % split) * ld + c;
+    return (float *)out.p[c / split] + (int64_t)r * split + (c % split);
+  }
+  __device__ __forceinline__ void operator()(int, int r, int c, float v) const { *at(r, c) = v; }
+  __device__ __forceinline__ void operator()(int, int r, int c, float4 v) const {
+    *reinterpret_cast<float4 *>(at(r, c)) = v;  // split % 4 == 0: never straddles shards
+  }
+  struct Row {
+    float *p;
+  };
+  // a wave's 128 columns (c0 a multiple of 128) stay in one shard
+  __device__ __forceinline__ bool fast_ok() const { return by_rows || (split & 127) == 0; }
+  __device__ __forceinline__ Row row(int, int r, int c0, int g) const { return Row{at(r, c0 + 4 * g)}; }
+  __device__ __forceinline__ void put(const Row &w, int i, int vq, float4 v) const {
+    *reinterpret_cast<float4 *>(w.p + i * 32 + vq * 8) = v;
+  }
+  __device__ __forceinline__ void put_row(const Row &w, const float4 (&v)[4][4]) const { put_each(*this, w, v); }
+};
+
 // Logical tile L -> (z, tm, tn): problems outermost, then groups of GM tile
 // rows walked column-major, so the blocks that run together on one XCD share
 // A row panels and B column panels in its L2.
@@ -974,6 +1100,58 @@ hipError_t launch_mlp_down(int dtype, const void *hid, bool a_panel, int32_t n, 
     return run_gemm(dtype, a, e, s);
   }
   EpiStoreF32 e{y, h};
+  return run_gemm(dtype, a, e, s);
+}
+
+// ---------------------------------------------------------------- MLP backward
+hipError_t launch_mlp_bwd_recompute(int dtype, const void *w1cat, int32_t F, int32_t h, const void *x, int32_t n,
+                                    void *zt, bool zt_panel, void *ht, hipStream_t s) {
+  GemmArgs a = make_args(w1cat, h, false, F, n, h);
+  a.B.p[0] = x;
+  a.ldb = h;
+  const int64_t pnl = zt_panel ? (int64_t)F * kPanel : 0;
+  if (dtype == TSP_BF16) {
+    EpiZH<bf16> e{(bf16 *)zt, (bf16 *)ht, n, pnl};
+    return run_gemm(dtype, a, e, s);
+  }
+  EpiZH<float> e{(float *)zt, (float *)ht, n, pnl};
+  return run_gemm(dtype, a, e, s);
+}
+
+hipError_t launch_mlp_bwd_dz(int dtype, const void *w2t, int32_t F, int32_t h, const void *dy, int32_t n, void *zt,
+                             bool zt_panel, hipStream_t s) {
+  GemmArgs a = make_args(w2t, h, false, F, n, h);
+  a.B.p[0] = dy;
+  a.ldb = h;
+  const int64_t pnl = zt_panel ? (int64_t)F * kPanel : 0;
+  if (dtype == TSP_BF16) {
+    EpiDZ<bf16> e{(bf16 *)zt, n, pnl};
+    return run_gemm(dtype, a, e, s);
+  }
+  EpiDZ<float> e{(float *)zt, n, pnl};
+  return run_gemm(dtype, a, e, s);
+}
+
+hipError_t launch_wgrad(int dtype, const void *A, bool a_panel, int32_t M, const void *b, int32_t N, int32_t n,
+                        const PtrList &out, int32_t split, bool by_rows, hipStream_t s) {
+  if (split <= 0 || (split & 3) != 0) return hipErrorInvalidValue;
+  GemmArgs a = make_args(A, n, a_panel, M, N, n);
+  a.B.p[0] = b;
+  a.ldb = n;
+  EpiShardF32 e{out, split, N, by_rows};
+  return run_gemm(dtype, a, e, s);
+}
+
+hipError_t launch_mlp_bwd_dx(int dtype, const void *dz, bool a_panel, int32_t n, int32_t F, const void *w1t,
+                             int32_t h, const float *res, float *dx, hipStream_t s) {
+  GemmArgs a = make_args(dz, F, a_panel, n, h, F);
+  a.B.p[0] = w1t;
+  a.ldb = F;
+  if (res) {
+    EpiAddF32 e{res, dx, h};
+    return run_gemm(dtype, a, e, s);
+  }
+  EpiStoreF32 e{dx, h};
   return run_gemm(dtype, a, e, s);
 }
 

@@ -123,4 +123,50 @@ hipError_t launch_rmsnorm_f32(const float *x, const void *g, int g_dtype, float 
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------- transpose
+// One 256-thread block per 64 x 64 tile of one matrix (blockIdx.z). The tile
+// goes through LDS as fp32 (bf16 widens exactly), read along input rows and
+// written along output rows, so both sides are contiguous runs of 64
+// elements (a panel layout keeps 64 aligned columns contiguous too). The
+// padded LDS row keeps the column reads conflict-free.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(PtrList in, int64_t in_ld, int64_t in_panel, int32_t R,
+                                                        int32_t C, T *__restrict__ out, int64_t out_ld,
+                                                        int64_t out_panel, int64_t out_zoff) {
+  __shared__ float tile[64][65];
+  const T *src = reinterpret_cast<const T *>(in.p[blockIdx.z]);
+  T *dst = out + (int64_t)blockIdx.z * out_zoff;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + ty + 4 * i, c = c0 + tx;
+    float v = 0.f;
+    if (r < R && c < C) v = (float)src[in_panel ? panel_index(r, c, in_panel) : (int64_t)r * in_ld + c];
+    tile[ty + 4 * i][tx] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = c0 + ty + 4 * i, r = r0 + tx;  // output row c, column r
+    if (r < R && c < C) dst[out_panel ? panel_index(c, r, out_panel) : (int64_t)c * out_ld + r] = (T)tile[tx][ty + 4 * i];
+  }
+}
+
+hipError_t launch_transpose(int dtype, const PtrList &in, int32_t nz, int64_t in_ld, int64_t in_panel, int32_t R,
+                            int32_t C, void *out, int64_t out_ld, int64_t out_panel, int64_t out_zoff, hipStream_t s) {
+  if (R <= 0 || C <= 0 || nz <= 0) return hipSuccess;
+  if ((in_panel || out_panel) && dtype != TSP_BF16) return hipErrorInvalidValue;
+  if (nz > TSP_MAX_D || (R + 63) / 64 > 65535) return hipErrorInvalidValue;
+  const dim3 grid((C + 63) / 64, (R + 63) / 64, nz);
+  if (dtype == TSP_BF16)
+    hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, s, in, in_ld, in_panel, R, C,
+                       reinterpret_cast<bf16 *>(out), out_ld, out_panel, out_zoff);
+  else
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s, in, in_ld, in_panel, R, C,
+                       reinterpret_cast<float *>(out), out_ld, out_panel, out_zoff);
+  return hipGetLastError();
+}
+
 }  // namespace tsp

@@ -62,6 +62,13 @@ hipError_t launch_rope_table(ZigzagMap zz, int32_t n, int32_t Dh, float base, fl
 hipError_t launch_rope_rows(float *x, int64_t ld, int32_t n, int32_t H, int32_t Dh, ZigzagMap zz, bool scatter,
                             const float2 *table, hipStream_t s);
 
+// out(c, r) = in(r, c) for nz R x C matrices: matrix z is in.p[z] (row
+// pitch in_ld, or panel layout with panel stride in_panel) and lands at
+// out + z * out_zoff (row pitch out_ld, or panel layout with panel stride
+// out_panel). Panel layouts are bf16 only.
+hipError_t launch_transpose(int dtype, const PtrList &in, int32_t nz, int64_t in_ld, int64_t in_panel, int32_t R,
+                            int32_t C, void *out, int64_t out_ld, int64_t out_panel, int64_t out_zoff, hipStream_t s);
+
 // ---------------------------------------------------------------- GEMMs
 // All products are C = A B^T with A [M][K] and B [N][K] (both K-contiguous).
 // a_panel: A in panel layout (bf16 only; panel stride M * 64), else row-major.
@@ -89,6 +96,27 @@ hipError_t launch_mlp_up(int dtype, const void *x, bool a_panel, int32_t n, int3
 // equal y.
 hipError_t launch_mlp_down(int dtype, const void *hid, bool a_panel, int32_t n, const PtrList &w2, int32_t D,
                            int32_t fd, int32_t h, const float *res, float *y, hipStream_t s);
+
+// MLP backward products (the MLP ring's gradients on one rank). The
+// hidden-unit axis F is in ring-step order throughout (ring step t owns
+// units t*fd..(t+1)*fd-1). zt_panel: Z^T / dZ^T [F][n] in panel layout
+// (bf16 only, panel stride F * 64), else row-major with pitch n.
+// Z^T = w1cat x^T (w1cat [F][h], x [n][h]): zt = Z^T, ht [F][n] row-major =
+// GELU(Z^T), both in dtype.
+hipError_t launch_mlp_bwd_recompute(int dtype, const void *w1cat, int32_t F, int32_t h, const void *x, int32_t n,
+                                    void *zt, bool zt_panel, void *ht, hipStream_t s);
+// dZ^T = (w2t dy^T) * GELU'(Z^T) (w2t [F][h], dy [n][h]), written over zt.
+hipError_t launch_mlp_bwd_dz(int dtype, const void *w2t, int32_t F, int32_t h, const void *dy, int32_t n, void *zt,
+                             bool zt_panel, hipStream_t s);
+// Weight gradients over K = n tokens: C [M][N] = A [M][n] B [N][n]^T in
+// fp32, A in panel layout when a_panel (bf16). by_rows: row m goes to
+// out.p[m / split] row m % split (pitch N); else column c goes to
+// out.p[c / split] column c % split (pitch split).
+hipError_t launch_wgrad(int dtype, const void *a, bool a_panel, int32_t M, const void *b, int32_t N, int32_t n,
+                        const PtrList &out, int32_t split, bool by_rows, hipStream_t s);
+// dx = (res ? res : 0) + dz w1t^T: dz [n][F] (panel when a_panel), w1t [h][F].
+hipError_t launch_mlp_bwd_dx(int dtype, const void *dz, bool a_panel, int32_t n, int32_t F, const void *w1t,
+                             int32_t h, const float *res, float *dx, hipStream_t s);
 
 // Leading rows in fp32: the same products for m <= kLeadRows rows with fp32
 // activations (row-major) and the bf16 weights, computed to fp32 accuracy.
