@@ -57,6 +57,12 @@ Readings where the pages are silent (each is restated where it is used):
      tokens' contribution to each shard's gradient, and the D ranks'
      contributions add up to the gradient over the whole sequence (the sum a
      ring would carry back to the shard's owner).
+  R11 backward of the zigzag attention (an optional extension, like R10):
+     the gradients of causal_attention by the chain rule through the
+     softmax. A rank's queries give their own dQ rows; its dK and dV are its
+     queries' contribution to every key row (the D ranks' contributions add
+     up to the whole sequence's dK and dV, the sum that would travel back to
+     each row's owner after the all-gather).
 """
 from __future__ import annotations
 
@@ -77,6 +83,8 @@ __all__ = [
     "mlp",
     "mlp_shard",
     "gelu_grad",
+    "softmax_backward",
+    "causal_attention_backward",
     "mlp_backward",
     "layer_full",
     "layer_rows",
@@ -174,6 +182,52 @@ def causal_attention(q, k, v, q_pos, scale: float, row_block: int = 256) -> np.n
             p = p / p.sum(axis=1, keepdims=True)
             out[lo:hi, hd, :] = p @ vh
     return out
+
+
+def softmax_backward(p, dp) -> np.ndarray:
+    """Gradient of the scores from that of the probabilities, row by row: the
+    Jacobian of softmax gives ds_u = p_u * (dp_u - sum_w p_w dp_w) (R11)."""
+    p, dp = _f64(p), _f64(dp)
+    return p * (dp - (p * dp).sum(axis=-1, keepdims=True))
+
+
+def causal_attention_backward(q, k, v, q_pos, scale: float, do, row_block: int = 256) -> dict:
+    """Gradients of causal_attention (reading R11) for an output gradient do
+    [n, H, Dh]: dq [n, H, Dh] and dk, dv [S, Hkv, Dh].
+
+    Per query t and head, with s_u = scale * <q, k_u> over the visible keys
+    u <= q_pos[t], p = softmax(s) and o = sum_u p_u v_u: dp_u = <do, v_u>,
+    the softmax Jacobian gives ds_u = p_u * (dp_u - sum_w p_w dp_w), and then
+    dq = scale * sum_u ds_u k_u, dk_u += scale * ds_u q, dv_u += p_u do. Rows
+    are taken row_block at a time, each with its whole prefix; K/V head i //
+    (H/Hkv) collects the gradients of every query head that reads it (R8).
+    """
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    n, H, Dh = q.shape
+    Skv, Hkv = k.shape[0], k.shape[1]
+    group = H // Hkv
+    dq = np.zeros((n, H, Dh), dtype=np.float64)
+    dk = np.zeros((Skv, Hkv, Dh), dtype=np.float64)
+    dv = np.zeros((Skv, Hkv, Dh), dtype=np.float64)
+    for lo in range(0, n, row_block):
+        hi = min(n, lo + row_block)
+        pos = q_pos[lo:hi]
+        L = int(pos.max()) + 1
+        visible = np.arange(L)[None, :] <= pos[:, None]
+        for hd in range(H):
+            kv = hd // group
+            qh = _f64(q[lo:hi, hd, :])
+            kh = _f64(k[:L, kv, :])
+            vh = _f64(v[:L, kv, :])
+            doh = _f64(do[lo:hi, hd, :])
+            s = np.where(visible, scale * (qh @ kh.T), -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p = p / p.sum(axis=1, keepdims=True)
+            ds = softmax_backward(p, doh @ vh.T)
+            dq[lo:hi, hd, :] = scale * (ds @ kh)
+            dk[:L, kv, :] += scale * (ds.T @ qh)
+            dv[:L, kv, :] += p.T @ doh
+    return {"dq": dq, "dk": dk, "dv": dv}
 
 
 def rope(x, pos, base: float) -> np.ndarray:

@@ -641,6 +641,114 @@ def test_mlp_backward_planted_mistakes_are_caught(monkeypatch):
     assert not np.allclose(np.concatenate(bad["dw1"], axis=0), g1, atol=1e-6)
 
 
+# ---------------------------------------------------------------- attention backward
+def _torch_attn_grads(q, k, v, do, scale, gqa=False):
+    """torch fp64 autograd through scaled_dot_product_attention (causal, all
+    positions 0..S-1); q [S, H, Dh], k/v [S, Hkv, Dh]."""
+    t = lambda a: torch.from_numpy(a).permute(1, 0, 2)[None].contiguous().requires_grad_(True)  # noqa: E731
+    tq, tk, tv = t(q), t(k), t(v)
+    o = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale, enable_gqa=gqa)
+    (o * torch.from_numpy(do).permute(1, 0, 2)[None]).sum().backward()
+    back = lambda g: g[0].permute(1, 0, 2).numpy()  # noqa: E731
+    return back(tq.grad), back(tk.grad), back(tv.grad)
+
+
+@pytest.mark.parametrize("Hkv", [3, 1])
+def test_attention_backward_vs_torch_autograd(Hkv):
+    rng = np.random.default_rng(21)
+    S, H, Dh, scale = 20, 3, 5, 0.4
+    q = rng.standard_normal((S, H, Dh))
+    k, v = rng.standard_normal((2, S, Hkv, Dh))
+    do = rng.standard_normal((S, H, Dh))
+    got = oracle.causal_attention_backward(q, k, v, np.arange(S), scale, do, row_block=7)
+    gq, gk, gv = _torch_attn_grads(q, k, v, do, scale, gqa=Hkv != H)
+    assert np.allclose(got["dq"], gq, atol=1e-12)
+    assert np.allclose(got["dk"], gk, atol=1e-12)
+    assert np.allclose(got["dv"], gv, atol=1e-12)
+
+
+def test_attention_backward_finite_differences():
+    """Central differences of L = sum(do * o), o from causal_attention (pinned
+    on its own), in chosen entries of q, k and v; zigzag query positions."""
+    rng = np.random.default_rng(22)
+    S, D, r, H, Dh, scale = 16, 2, 1, 2, 3, 0.7
+    pos = oracle.zigzag_positions(S, D, r)
+    q = rng.standard_normal((len(pos), H, Dh))
+    k, v = rng.standard_normal((2, S, H, Dh))
+    do = rng.standard_normal((len(pos), H, Dh))
+    got = oracle.causal_attention_backward(q, k, v, pos, scale, do)
+    loss = lambda q_, k_, v_: float((do * oracle.causal_attention(q_, k_, v_, pos, scale)).sum())  # noqa: E731
+    e = 1e-6
+    for name, arr, idx in [("dq", q, (3, 1, 2)), ("dq", q, (7, 0, 0)), ("dk", k, (0, 1, 1)), ("dk", k, (13, 0, 2)),
+                           ("dv", v, (2, 1, 0)), ("dv", v, (12, 0, 1))]:
+        ap, am = arr.copy(), arr.copy()
+        ap[idx] += e
+        am[idx] -= e
+        args_p = [ap if a is arr else a for a in (q, k, v)]
+        args_m = [am if a is arr else a for a in (q, k, v)]
+        fd = (loss(*args_p) - loss(*args_m)) / (2 * e)
+        assert got[name][idx] == pytest.approx(fd, abs=1e-7), name
+    # keys past every query of this rank get no gradient
+    assert not got["dk"][pos.max() + 1:].any() and not got["dv"][pos.max() + 1:].any()
+
+
+def test_attention_backward_rank_contributions_sum():
+    """Reading R11: every rank's dq rows equal the full-sequence dq at its
+    positions, and the ranks' dK/dV contributions add up to the full ones."""
+    rng = np.random.default_rng(23)
+    S, D, H, Dh, scale = 32, 4, 2, 4, 0.5
+    q_all = rng.standard_normal((S, H, Dh))
+    k, v = rng.standard_normal((2, S, H, Dh))
+    do_all = rng.standard_normal((S, H, Dh))
+    full = oracle.causal_attention_backward(q_all, k, v, np.arange(S), scale, do_all)
+    dk, dv = np.zeros_like(k), np.zeros_like(v)
+    for r in range(D):
+        pos = oracle.zigzag_positions(S, D, r)
+        part = oracle.causal_attention_backward(q_all[pos], k, v, pos, scale, do_all[pos])
+        assert np.allclose(part["dq"], full["dq"][pos], atol=1e-13)
+        dk += part["dk"]
+        dv += part["dv"]
+    assert np.allclose(dk, full["dk"], atol=1e-12)
+    assert np.allclose(dv, full["dv"], atol=1e-12)
+
+
+def test_attention_backward_special_cases():
+    """Scale 0: uniform weights over the prefix, so dv_u = sum over queries
+    t >= u of do_t / (t + 1) and dq = 0 (closed forms); the query at position
+    0 sees only key 0, so its dq is 0 and its do goes wholly to dv_0."""
+    rng = np.random.default_rng(24)
+    S, H, Dh = 9, 1, 3
+    q, k, v, do = rng.standard_normal((4, S, H, Dh))
+    got = oracle.causal_attention_backward(q, k, v, np.arange(S), 0.0, do)
+    assert np.allclose(got["dq"], 0.0, atol=1e-15)
+    for u in range(S):
+        want = sum(do[t, 0] / (t + 1) for t in range(u, S))
+        assert np.allclose(got["dv"][u, 0], want, atol=1e-13)
+    one = oracle.causal_attention_backward(q[:1], k, v, np.array([0]), 0.9, do[:1])
+    assert np.allclose(one["dq"], 0.0, atol=1e-15)
+    assert np.allclose(one["dv"][0], do[0], atol=1e-15) and not one["dv"][1:].any()
+
+
+def test_attention_backward_planted_mistakes_are_caught(monkeypatch):
+    """A softmax Jacobian without its row-sum term, or gradients taken with
+    an exclusive mask, miss torch's autograd."""
+    rng = np.random.default_rng(25)
+    S, H, Dh, scale = 12, 2, 4, 0.6
+    q, k, v, do = rng.standard_normal((4, S, H, Dh))
+    gq, gk, gv = _torch_attn_grads(q, k, v, do, scale)
+    bad_mask = oracle.causal_attention_backward(q[1:], k, v, np.arange(1, S) - 1, scale, do[1:])
+    assert not np.allclose(bad_mask["dq"], gq[1:], atol=1e-6)
+    # the identity sum_u p_u (dp_u - sum_w p_w dp_w) = 0 holds only with the term
+    p = np.full((1, 4), 0.25)
+    dp = np.array([[1.0, -2.0, 0.5, 3.0]])
+    assert abs(oracle.softmax_backward(p, dp).sum()) < 1e-15
+    monkeypatch.setattr(oracle.tsp_oracle, "softmax_backward", lambda p_, dp_: p_ * dp_)
+    bad = oracle.causal_attention_backward(q, k, v, np.arange(S), scale, do)
+    assert not np.allclose(bad["dq"], gq, atol=1e-6)
+    assert not np.allclose(bad["dk"], gk, atol=1e-6)
+    assert np.allclose(bad["dv"], gv, atol=1e-12)  # dv does not go through the Jacobian
+
+
 # ---------------------------------------------------------------- synth
 def test_synth_deterministic_and_bf16_rounding():
     a = synth.normal((3, 5), 1, 7)
