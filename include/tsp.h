@@ -143,7 +143,7 @@ typedef struct {
 enum { TSP_PHASE_KV = 1, TSP_PHASE_REST = 2, TSP_PHASE_ALL = 3 };
 
 /* Workspace kinds for tsp_workspace_size. */
-enum { TSP_WS_MLP = 0, TSP_WS_LAYER = 1, TSP_WS_MLP_BWD = 2 };
+enum { TSP_WS_MLP = 0, TSP_WS_LAYER = 1, TSP_WS_MLP_BWD = 2, TSP_WS_ATTN_BWD = 3 };
 
 /* Kernel classes for the optional launch timing. */
 enum {
@@ -157,7 +157,8 @@ enum {
   TSP_K_LEAD = 7, /* the fp32 recomputation of the leading rows (see tsp_layer_fwd) */
   TSP_K_BWD_GEMM = 8,  /* the products of tsp_mlp_ring_bwd */
   TSP_K_TRANSPOSE = 9, /* the layout changes of tsp_mlp_ring_bwd */
-  TSP_K_COUNT = 10
+  TSP_K_ATTN_BWD = 10, /* the launches of tsp_zigzag_attn_bwd */
+  TSP_K_COUNT = 11
 };
 
 /* Static text for a status code. */
@@ -170,8 +171,8 @@ const char *tsp_last_error(void);
 int tsp_abi_version(void);
 
 /* Bytes of scratch the call 'which' (TSP_WS_MLP for tsp_mlp_ring,
- * TSP_WS_LAYER for tsp_layer_fwd, TSP_WS_MLP_BWD for tsp_mlp_ring_bwd)
- * needs for this shape. */
+ * TSP_WS_LAYER for tsp_layer_fwd, TSP_WS_MLP_BWD for tsp_mlp_ring_bwd,
+ * TSP_WS_ATTN_BWD for tsp_zigzag_attn_bwd) needs for this shape. */
 tsp_status tsp_workspace_size(const tsp_shape *shape, int which, size_t *bytes);
 
 /* Zigzag token ownership (reading above; the pages name a zigzag partition
@@ -216,6 +217,28 @@ tsp_status tsp_zigzag_attn_ex(const tsp_shape *shape, const void *q, const void 
 tsp_status tsp_mlp_ring(const tsp_shape *shape, const void *x, const void *const *w1,
                         const void *const *w2, const float *residual, float *y, void *ws,
                         size_t ws_bytes, void *stream);
+
+/* Backward of the zigzag causal attention on rank r (an optional extension,
+ * like tsp_mlp_ring_bwd: the pages give no backward). For the forward of
+ * tsp_zigzag_attn, o = softmax(scale q k^T, causal) v over the gathered K/V,
+ * and an output gradient dout, with p the probabilities, dp = dout v^T and
+ * ds = p * (dp - sum over the row's keys of p dp) (the softmax Jacobian; the
+ * sum equals rowsum(dout * o) and is formed from the fp32 probabilities, so
+ * the forward's output is not needed):
+ *   dq = scale ds k           [S/D][H][Dh]  this rank's queries;
+ *   dk = scale ds^T q,  dv = p^T dout   [S][Hkv][Dh]  this rank's queries'
+ *   contribution to every key and value row (zero past the rank's last
+ *   position; the D ranks' contributions add up to the gradients over the
+ *   whole sequence, which would travel back to each row's owner).
+ *  q, dout: [S/D][H][Dh] (dtype), local rows in zigzag order, q unscaled;
+ *  k, v: [S][Hkv][Dh] (dtype), global order. dq, dk, dv: fp32, fully
+ *  written. Rounding (bf16): p enters p^T dout and ds enters ds k and ds^T q
+ *  as a bf16 pair hi + lo (exact to about 2^-16 of their size); row
+ *  statistics, dp, ds and all accumulation are fp32.
+ *  ws: device scratch of at least tsp_workspace_size(TSP_WS_ATTN_BWD) bytes. */
+tsp_status tsp_zigzag_attn_bwd(const tsp_shape *shape, const void *q, const void *k, const void *v,
+                               const void *dout, float *dq, float *dk, float *dv, void *ws,
+                               size_t ws_bytes, void *stream);
 
 /* Backward of the MLP ring on rank r (an optional extension: the pages quote
  * their 2.6x for training, [P2] paragraph 1, but describe only how the

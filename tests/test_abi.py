@@ -223,6 +223,35 @@ def test_mlp_bwd_workspace_and_errors():
         tsp.workspace_size(_shape(dtype="bf16", mlp="swiglu"), tsp.TSP_WS_MLP_BWD)
 
 
+def test_attn_bwd_workspace_and_errors():
+    # log-sum-exp and Delta of every (head, local row), fp32
+    s = _shape(dtype="bf16")
+    assert tsp.workspace_size(s, tsp.TSP_WS_ATTN_BWD) == 2 * 4 * 256 * 4
+    s7 = tsp.make_shape(131072, 8, 0, 4096, 32, 128, 16384, dtype="bf16")
+    assert tsp.workspace_size(s7, tsp.TSP_WS_ATTN_BWD) == 2 * 32 * 16384 * 4
+    need = tsp.workspace_size(s, tsp.TSP_WS_ATTN_BWD)
+    q, k, v, do = (FAKE + (i << 32) for i in range(4))
+    dq, dk, dv, ws = (FAKE + ((5 + i) << 32) for i in range(4))
+
+    def call(shape=s, nbytes=need, **kw):
+        a = dict(q=q, k=k, v=v, do=do, dq=dq, dk=dk, dv=dv, ws=ws)
+        a.update(kw)
+        with pytest.raises(tsp.TspError) as ei:
+            tsp.tsp_zigzag_attn_bwd(shape, a["q"], a["k"], a["v"], a["do"], a["dq"], a["dk"], a["dv"],
+                                    a["ws"], nbytes, stream=0)
+        return ei.value.status, tsp.lib().tsp_last_error()
+
+    assert call(nbytes=need - 1)[0] == tsp.TSP_ERR_WORKSPACE
+    st, msg = call(do=None)
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"dout is NULL" in msg
+    st, msg = call(dk=k + 4096)  # an output over an input
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"overlap" in msg
+    st, msg = call(dv=dk + 256)  # two outputs over each other
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"overlap" in msg
+    assert call(dq=dq + 4)[0] == tsp.TSP_ERR_INVALID_ARG
+    assert call(shape=_shape(dtype="bf16", Dh=32, H=8))[0] == tsp.TSP_ERR_UNSUPPORTED
+
+
 def test_layer_errors():
     s = _shape()
     w = dict(g_attn=FAKE, g_mlp=FAKE, wqkv=[FAKE] * 4, wo=[FAKE] * 4, w1=[FAKE] * 4, w2=[FAKE] * 4)

@@ -158,3 +158,111 @@ def test_mlp_ring_bwd_7b(torch):
         assert_close(g1, want_dw1, TOL_BF16, f"dW1 rows of sampled units (r={r})")
         assert_close(g2, want_dw2, TOL_BF16, f"dW2 columns of sampled units (r={r})")
         assert all(np.isfinite(a).all() for a in dw1 + dw2) and np.isfinite(dx).all()
+
+
+# ---------------------------------------------------------------- attention backward
+def _attn_bwd_run(torch, s, q, k, v, do, dtype):
+    """tsp_zigzag_attn_bwd; returns dq, dk, dv (float64)."""
+    N, H, Dh = q.shape
+    S, Hkv = k.shape[0], k.shape[1]
+    qd, kd, vd, dod = up(q, dtype), up(k, dtype), up(v, dtype), up(do, dtype)
+    ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_ATTN_BWD), dtype=torch.uint8, device="cuda")
+    dq = torch.full((N, H, Dh), float("nan"), dtype=torch.float32, device="cuda")
+    dk = torch.full((S, Hkv, Dh), float("nan"), dtype=torch.float32, device="cuda")
+    dv = torch.full((S, Hkv, Dh), float("nan"), dtype=torch.float32, device="cuda")
+    tsp.tsp_zigzag_attn_bwd(s, qd, kd, vd, dod, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    return down(dq), down(dk), down(dv)
+
+
+ATTN_BWD_CASES = [
+    # S, D, H, Hkv, Dh, dtype
+    (1024, 4, 4, 4, 64, "f32"),    # the tiny fp32 layer's attention
+    (2048, 4, 4, 4, 128, "bf16"),  # chunks of 256: two query tiles, eight 32-row steps each
+    (640, 2, 2, 2, 64, "bf16"),    # chunks of 160: a ragged query tile and step
+    (1024, 2, 4, 2, 128, "bf16"),  # two query heads per K/V head
+    (256, 1, 2, 2, 128, "bf16"),   # D = 1: plain causal attention
+]
+
+
+@pytest.mark.parametrize("S,D,H,Hkv,Dh,dtype", ATTN_BWD_CASES)
+def test_attn_bwd_every_rank(torch, S, D, H, Hkv, Dh, dtype):
+    shape = synth.LayerShape(S=S, D=D, h=H * Dh, H=H, Dh=Dh, F=64 * D, dtype=dtype, Hkv=Hkv)
+    N = S // D
+    k, v = synth.remote_kv(shape, seed=51)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    for r in range(D):
+        q = synth.normal((N, H, Dh), 51, synth.TID_Q, r, dtype=dtype)
+        do = synth.normal((N, H, Dh), 51, synth.TID_DY, r, dtype=dtype)
+        pos = oracle.zigzag_positions(S, D, r)
+        want = oracle.causal_attention_backward(f64(q, dtype), f64(k, dtype), f64(v, dtype), pos, shape.scale,
+                                                f64(do, dtype))
+        s = tsp.make_shape(S, D, r, H * Dh, H, Dh, 64 * D, dtype=dtype, Hkv=Hkv)
+        log(f"attention backward S={S} D={D} r={r} H={H} Hkv={Hkv} Dh={Dh} {dtype}")
+        dq, dk, dv = _attn_bwd_run(torch, s, q, k, v, do, dtype)
+        assert_close(dq, want["dq"], tol, f"dq r={r}")
+        assert_close(dk, want["dk"], tol, f"dk r={r}")
+        assert_close(dv, want["dv"], tol, f"dv r={r}")
+        assert not dk[pos.max() + 1:].any() and not dv[pos.max() + 1:].any()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_attn_bwd_rank_contributions_sum(torch, dtype):
+    """D emulated ranks over one sequence: each rank's dq rows are the
+    full-sequence dq at its positions; the ranks' dK and dV add up to the
+    full-sequence gradients."""
+    S, D, H, Dh = 1024, 4, 2, 128 if dtype == "bf16" else 64
+    shape = synth.LayerShape(S=S, D=D, h=H * Dh, H=H, Dh=Dh, F=256, dtype=dtype)
+    k, v = synth.remote_kv(shape, seed=52)
+    q_all = synth.normal((S, H, Dh), 52, synth.TID_Q, 0, dtype=dtype)
+    do_all = synth.normal((S, H, Dh), 52, synth.TID_DY, 0, dtype=dtype)
+    full = oracle.causal_attention_backward(f64(q_all, dtype), f64(k, dtype), f64(v, dtype), np.arange(S),
+                                            shape.scale, f64(do_all, dtype))
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    dk_sum, dv_sum = np.zeros_like(full["dk"]), np.zeros_like(full["dv"])
+    for r in range(D):
+        pos = oracle.zigzag_positions(S, D, r)
+        s = tsp.make_shape(S, D, r, H * Dh, H, Dh, 256, dtype=dtype)
+        log(f"attention backward, emulated rank {r} of {D}, {dtype}")
+        dq, dk, dv = _attn_bwd_run(torch, s, q_all[pos], k, v, do_all[pos], dtype)
+        assert_close(dq, full["dq"][pos], tol, f"dq rows of rank {r}")
+        dk_sum += dk
+        dv_sum += dv
+    assert_close(dk_sum, full["dk"], tol, "sum of dK contributions")
+    assert_close(dv_sum, full["dv"], tol, "sum of dV contributions")
+
+
+@pytest.mark.timeout(900)
+def test_attn_bwd_7b(torch):
+    """7B attention (32 heads x 128, S = 131072, D = 8), rank 0: dq of the
+    first 64 and the last 64 local rows (positions 0.. and 131008..), and dK,
+    dV of the last 64 keys, which only those last rows see, against the
+    oracle; over the whole sequence, sum_u dV_u = sum_t dO_t and sum_u dK_u =
+    0 for every head and feature (the softmax weights sum to one, the score
+    gradients of a row to zero), and keys past the rank are untouched by it."""
+    SH = synth.SEVEN_B
+    N, S, H, Dh = SH.N, SH.S, SH.H, SH.Dh
+    r = 0
+    q = synth.attn_queries(SH, seed=53)
+    k, v = synth.remote_kv(SH, seed=53)
+    do = synth.normal((N, H, Dh), 53, synth.TID_DY, 0, dtype="bf16")
+    s = tsp.make_shape(S, SH.D, r, SH.h, H, Dh, SH.F, dtype="bf16")
+    log("attention backward 7B, rank 0")
+    dq, dk, dv = _attn_bwd_run(torch, s, q, k, v, do, "bf16")
+    assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
+    pos = oracle.zigzag_positions(S, SH.D, r)
+    k64, v64 = f64(k, "bf16"), f64(v, "bf16")
+    for rows, what in ((np.arange(64), "first"), (np.arange(N - 64, N), "last")):
+        want = oracle.causal_attention_backward(f64(q[rows], "bf16"), k64, v64, pos[rows], SH.scale,
+                                                f64(do[rows], "bf16"))
+        assert_close(dq[rows], want["dq"], TOL_BF16, f"dq of the {what} 64 rows")
+        if what == "last":
+            assert_close(dk[S - 64:], want["dk"][S - 64:], TOL_BF16, "dK of the last 64 keys")
+            assert_close(dv[S - 64:], want["dv"][S - 64:], TOL_BF16, "dV of the last 64 keys")
+    do64 = f64(do, "bf16")
+    assert_close(dv.sum(axis=0), do64.sum(axis=0), TOL_BF16, "sum over keys of dV vs sum over rows of dO")
+    # sum_u dK_u = 0: held against the scale of one key row's gradient
+    rms_row = float(np.sqrt(np.mean(dk ** 2)))
+    err = float(np.abs(dk.sum(axis=0)).max())
+    log(f"  sum over keys of dK: max {err:.3e} (dK rms {rms_row:.3e})")
+    assert err <= TOL_BF16 * rms_row * np.sqrt(S)

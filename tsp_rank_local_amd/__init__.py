@@ -18,9 +18,9 @@ import numpy as np
 __all__ = [
     "TspError", "TspShape", "TspLayerWeights", "lib", "make_shape", "workspace_size",
     "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_zigzag_attn_ex", "tsp_mlp_ring",
-    "tsp_mlp_ring_bwd", "tsp_layer_fwd", "profile_enable", "profile_reset", "profile_read",
+    "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_layer_fwd", "profile_enable", "profile_reset", "profile_read",
     "TSP_F32", "TSP_BF16", "TSP_ATTN_Q_LOG2_SCALED", "TSP_PHASE_KV", "TSP_PHASE_REST", "TSP_PHASE_ALL",
-    "TSP_WS_MLP", "TSP_WS_LAYER", "TSP_WS_MLP_BWD", "TSP_MLP_GELU", "TSP_MLP_SWIGLU", "MLP_KINDS",
+    "TSP_WS_MLP", "TSP_WS_LAYER", "TSP_WS_MLP_BWD", "TSP_WS_ATTN_BWD", "TSP_MLP_GELU", "TSP_MLP_SWIGLU", "MLP_KINDS",
     "KERNEL_CLASSES", "EXPORTED_SYMBOLS",
 ]
 
@@ -29,18 +29,19 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsp.so")
 TSP_OK, TSP_ERR_INVALID_ARG, TSP_ERR_UNSUPPORTED, TSP_ERR_WORKSPACE, TSP_ERR_HIP = range(5)
 TSP_F32, TSP_BF16 = 0, 1
 TSP_PHASE_KV, TSP_PHASE_REST, TSP_PHASE_ALL = 1, 2, 3
-TSP_WS_MLP, TSP_WS_LAYER, TSP_WS_MLP_BWD = 0, 1, 2
+TSP_WS_MLP, TSP_WS_LAYER, TSP_WS_MLP_BWD, TSP_WS_ATTN_BWD = 0, 1, 2, 3
 TSP_ATTN_Q_LOG2_SCALED = 1
 TSP_MLP_GELU, TSP_MLP_SWIGLU = 0, 1
 MLP_KINDS = {"gelu": TSP_MLP_GELU, "swiglu": TSP_MLP_SWIGLU}
 TSP_MAX_D = 64
 KERNEL_CLASSES = {"rmsnorm": 0, "qkv": 1, "attention": 2, "outproj": 3, "mlp_up": 4, "mlp_down": 5, "zigzag": 6,
-                  "lead": 7, "bwd_gemm": 8, "transpose": 9}
+                  "lead": 7, "bwd_gemm": 8, "transpose": 9,
+                  "attn_bwd": 10}
 
 EXPORTED_SYMBOLS = [
     "tsp_status_string", "tsp_last_error", "tsp_abi_version", "tsp_workspace_size",
     "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_zigzag_attn_ex", "tsp_mlp_ring",
-    "tsp_mlp_ring_bwd", "tsp_layer_fwd", "tsp_profile_enable", "tsp_profile_reset", "tsp_profile_read",
+    "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_layer_fwd", "tsp_profile_enable", "tsp_profile_reset", "tsp_profile_read",
 ]
 
 
@@ -89,6 +90,7 @@ def lib() -> ctypes.CDLL:
     L.tsp_mlp_ring.argtypes = [shp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, sz, vp]
     L.tsp_mlp_ring_bwd.argtypes = [shp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, ctypes.POINTER(vp),
                                    ctypes.POINTER(vp), vp, sz, vp]
+    L.tsp_zigzag_attn_bwd.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.tsp_layer_fwd.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, ctypes.c_uint, vp, sz, vp]
     L.tsp_profile_enable.argtypes = [ctypes.c_int]
     L.tsp_profile_enable.restype = None
@@ -96,7 +98,8 @@ def lib() -> ctypes.CDLL:
     L.tsp_profile_reset.restype = None
     L.tsp_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     for name in ("tsp_workspace_size", "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn",
-                 "tsp_zigzag_attn_ex", "tsp_mlp_ring", "tsp_mlp_ring_bwd", "tsp_layer_fwd", "tsp_profile_read"):
+                 "tsp_zigzag_attn_ex", "tsp_mlp_ring", "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_layer_fwd",
+                 "tsp_profile_read"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -176,6 +179,13 @@ def tsp_mlp_ring(shape: TspShape, x, w1, w2, residual, y, ws, ws_bytes=None, str
     a1, a2 = _ptr_array(w1), _ptr_array(w2)
     _check(lib().tsp_mlp_ring(ctypes.byref(shape), _ptr(x), a1, a2, _ptr(residual), _ptr(y), _ptr(ws),
                               int(ws_bytes), _stream(stream)))
+
+
+def tsp_zigzag_attn_bwd(shape: TspShape, q, k, v, dout, dq, dk, dv, ws, ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().tsp_zigzag_attn_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq),
+                                     _ptr(dk), _ptr(dv), _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
 def tsp_mlp_ring_bwd(shape: TspShape, x, w1, w2, dy, dx_residual, dx, dw1, dw2, ws, ws_bytes=None,

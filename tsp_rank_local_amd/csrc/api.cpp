@@ -188,6 +188,9 @@ MlpBwdWs mlp_bwd_ws(const tsp_shape *s) {
   return w;
 }
 
+// Attention backward scratch: log-sum-exp and Delta (sum of P dP) of every (head, row), fp32.
+size_t attn_bwd_ws(const tsp_shape *s) { return 2 * align256((size_t)s->H * (size_t)(s->S / s->D) * 4); }
+
 tsp_status check_mlp_bwd_shape(const tsp_shape *s) {
   tsp_status st = check_mlp_shape(s);
   if (st) return st;
@@ -315,6 +318,9 @@ tsp_status tsp_workspace_size(const tsp_shape *s, int which, size_t *bytes) {
   } else if (which == TSP_WS_MLP_BWD) {
     if ((st = check_mlp_bwd_shape(s))) return st;
     *bytes = mlp_bwd_ws(s).total;
+  } else if (which == TSP_WS_ATTN_BWD) {
+    if ((st = check_attn_shape(s))) return st;
+    *bytes = attn_bwd_ws(s);
   } else {
     return fail(TSP_ERR_INVALID_ARG, "unknown workspace kind %d", which);
   }
@@ -409,6 +415,35 @@ tsp_status tsp_mlp_ring(const tsp_shape *s, const void *x, const void *const *w1
   TSP_LAUNCH(TSP_K_MLP_DOWN,
              tsp::launch_mlp_down(s->dtype, ws, pnl, N, ring_list(w2, s->D, s->r), s->D, fd, h, residual, y, stream),
              "MLP down");
+  return ok();
+}
+
+tsp_status tsp_zigzag_attn_bwd(const tsp_shape *s, const void *q, const void *k, const void *v, const void *dout, float *dq, float *dk, float *dv, void *ws, size_t ws_bytes,
+                               void *stream_) {
+  tsp_status st = check_attn_shape(s);
+  if (st) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(dout, "dout")) || (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) ||
+      (st = check_ptr(dv, "dv")) || (st = check_ptr(ws, "ws")))
+    return st;
+  const size_t need = attn_bwd_ws(s);
+  if (ws_bytes < need) return fail(TSP_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, need);
+  const int64_t N = s->S / s->D;
+  const size_t e = elem_bytes(s->dtype);
+  const size_t qb = (size_t)N * s->H * s->Dh, kb = (size_t)s->S * kv_heads(s) * s->Dh;
+  const Range ins[] = {{q, qb * e, "q"}, {k, kb * e, "k"}, {v, kb * e, "v"}, {dout, qb * e, "dout"}};
+  const Range outs[] = {{dq, qb * 4, "dq"}, {dk, kb * 4, "dk"}, {dv, kb * 4, "dv"}, {ws, need, "ws"}};
+  for (const Range &ro : outs) {
+    for (const Range &ri : ins)
+      if (overlap(ro, ri)) return fail(TSP_ERR_INVALID_ARG, "%s overlaps %s", ro.name, ri.name);
+    for (const Range &r2 : outs)
+      if (&r2 != &ro && overlap(ro, r2)) return fail(TSP_ERR_INVALID_ARG, "%s overlaps %s", ro.name, r2.name);
+  }
+  hipStream_t stream = (hipStream_t)stream_;
+  float *lse = (float *)ws, *delta = (float *)((unsigned char *)ws + need / 2);
+  TSP_LAUNCH(TSP_K_ATTN_BWD,
+             tsp::launch_attention_bwd(s->dtype, q, k, v, dout, dq, dk, dv, lse, delta, s->S, (int32_t)N, s->H,
+                                       kv_heads(s), s->Dh, s->scale, tsp::make_zigzag(s->S, s->D, s->r), stream),
+             "attention backward");
   return ok();
 }
 

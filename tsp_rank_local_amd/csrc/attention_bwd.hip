@@ -1,0 +1,539 @@
+// Backward of the zigzag causal attention on one rank: the gradients of the
+// rank's queries (dQ) and the rank's contribution to the gradients of every
+// key and value row of the gathered sequence (dK, dV), from the output
+// gradient dO. With P = softmax(scale * Q K^T) over the visible keys and
+// dP = dO V^T, the softmax Jacobian gives dS = P * (dP - Delta), Delta the row
+// sum of dO * O; then dQ = scale * dS K, dK = scale * dS^T Q, dV = P^T dO.
+//
+// Two launches:
+//  1. dQ, query-major (like the forward): block = 4 waves x 32 queries of one
+//     head. A first walk over the key tiles takes each row's log-sum-exp and
+//     Delta = sum_u P_u dP_u (S^T = K Q^T and dP^T = V dO^T, a lane owning one
+//     query and 32 of a tile's keys; both kept for launch 2). Delta is formed
+//     from the fp32 probabilities rather than from a stored bf16 O, whose
+//     rounding would pass into every dS of rows that see few keys. A second
+//     walk recomputes S^T and dP^T, forms dS^T and accumulates dQ^T += K^T
+//     dS^T. The K^T operand comes from transpose reads of a second copy of the
+//     K tile, laid out for them.
+//  2. dK and dV, key-major: block = 4 waves x 32 keys of one K/V head. It walks
+//     the rank's query rows that can see its keys, 32 at a time, over every
+//     query head that reads the K/V head: S = Q K^T and dP = dO V^T with the
+//     keys on the lanes, P and dS from the row statistics of launch 2, then
+//     dV^T += dO^T P and dK^T += Q^T dS, whose dO^T and Q^T operands are
+//     transpose reads of the query tiles.
+// The operands of the second products are the score registers themselves,
+// rounded to bf16, in the order the MFMA takes them; the transpose reads hand
+// each lane 4 consecutive rows of one feature in that order. Every product
+// runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation. P and dS enter
+// their products as a bf16 pair hi + lo (two MFMAs each), exact to about
+// 2^-16 of their size: a plain bf16 rounding (2^-9) of them leaves errors of
+// 2-4% of the rms gradient on ranks whose rows see thousands of keys, not
+// only on the first rows of the sequence as in the forward.
+//
+// fp32 inputs run plain per-row kernels with exact expf.
+#include <math.h>
+
+#include "device_common.h"
+#include "tsp_internal.h"
+
+namespace tsp {
+
+struct BwdArgs {
+  const void *q, *k, *v, *dout;
+  float *dq, *dk, *dv;
+  float *lse;    // [H][n]: log2 of each row's softmax denominator (scores in the log2 domain)
+  float *delta;  // [H][n]: sum over the row's keys of P dP
+  int64_t S;
+  int32_t n, H, Hkv, grp;
+  float scale, c;  // c = scale * log2(e)
+  ZigzagMap zz;
+  int32_t Tq;  // 128-row query tiles per chunk (launch 1)
+  int32_t Tk;  // 128-key tiles over the sequence (launch 2)
+};
+
+typedef short s16x4_b __attribute__((ext_vector_type(4)));
+
+// Geometry of an R x DH bf16 tile in LDS: row-major, 16-byte chunks XOR-
+// swizzled by row. ROW layout: for ds_read_b128 row fragments; TR layout: for
+// the 4 x 4 transpose reads.
+template <int DH>
+struct BTile {
+  static constexpr int ROWB = DH * 2;
+  static constexpr int CPR = DH / 8;
+  static __device__ __forceinline__ int row_swz(int row, int ch) {
+    return ch ^ (CPR == 16 ? (row & 15) : ((row >> 1) & 7));
+  }
+  static __device__ __forceinline__ int tr_swz(int row, int ch) {
+    return ch ^ (CPR == 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1));
+  }
+};
+
+// Rows [r0, r0 + R) of a bf16 [*][pitch] tensor (DH columns from src) into
+// LDS in ROW (TR = false) or TR layout; rows at or past rmax read as zero.
+template <int DH, int R, bool TR>
+__device__ __forceinline__ void stage_tile(unsigned char *dst, const bf16 *src, int64_t pitch, int64_t r0,
+                                           int64_t rmax) {
+  using G = BTile<DH>;
+  constexpr int CH = R * G::CPR;
+  for (int c = threadIdx.x; c < CH; c += 256) {
+    const int row = c / G::CPR, ch = c % G::CPR;
+    const int64_t gr = r0 + row;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (gr < rmax) val = *reinterpret_cast<const u32x4 *>(src + gr * pitch + ch * 8);
+    const int pos = TR ? G::tr_swz(row, ch) : G::row_swz(row, ch);
+    *reinterpret_cast<u32x4 *>(dst + row * G::ROWB + pos * 16) = val;
+  }
+}
+
+// Row fragment: 8 bf16 of row `row`, logical chunk ch (ROW layout).
+template <int DH>
+__device__ __forceinline__ bf16x8 row_frag(const unsigned char *t, int row, int ch) {
+  return *reinterpret_cast<const bf16x8 *>(t + row * BTile<DH>::ROWB + BTile<DH>::row_swz(row, ch) * 16);
+}
+
+// Transpose fragment (TR layout) for feature block db and row group mu (16
+// rows): lane l receives, for feature 32*db + l%32, rows 16*mu + 4*(l/32) +
+// {0..3} and 16*mu + 8 + 4*(l/32) + {0..3}: the A operand whose k index runs
+// over those rows in the order of the score registers.
+template <int DH>
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char *t, int db, int mu, int lane) {
+  using G = BTile<DH>;
+  const int g = lane >> 5, r16 = lane & 15, dsub = (lane >> 4) & 1;
+  const int dstart = db * 32 + dsub * 16 + 4 * (r16 & 3);
+  s16x4_b part[2];
+#pragma unroll
+  for (int hv = 0; hv < 2; ++hv) {
+    const int row = mu * 16 + hv * 8 + g * 4 + (r16 >> 2);
+    const unsigned char *addr = t + row * G::ROWB + G::tr_swz(row, dstart >> 3) * 16 + (dstart & 7) * 2;
+    part[hv] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_b *)(addr));
+  }
+  const s16x8_t both = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+// ---------------------------------------------------------------- dQ (bf16)
+constexpr int kBwdKey = 64;  // keys per tile of the dQ walk
+
+// v as bf16 at element e of hi, and the remainder v - hi (exact in fp32) as
+// bf16 at element e of lo.
+__device__ __forceinline__ void put_split(bf16x8 &hi, bf16x8 &lo, int e, float v) {
+  const bf16 h = (bf16)v;
+  hi[e] = h;
+  lo[e] = (bf16)(v - (float)h);
+}
+
+template <int DH>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using G = BTile<DH>;
+  constexpr int ND = DH / 32, NK = DH / 16;
+  constexpr int TB = kBwdKey * G::ROWB;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[3][TB];  // K (ROW), K (TR), V (ROW)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int head = blockIdx.x / (2 * a.Tq), tile = blockIdx.x % (2 * a.Tq);
+  const int kvh = head / a.grp;
+  const int ch_half = tile < a.Tq ? 0 : 1;
+  const int row0 = ch_half * a.zz.C + (tile - ch_half * a.Tq) * 128;
+  const int nvalid = min(128, (ch_half + 1) * a.zz.C - row0);
+  if (nvalid <= 0) return;
+  const int pos0 = a.zz.pos(row0);
+  const int n_kt = (pos0 + nvalid - 1) / kBwdKey + 1;
+  const int wrow0 = wave * 32;
+  const bool active = wrow0 < nvalid;
+  const bool my_valid = wrow0 + l32 < nvalid;
+  const int qpos = pos0 + min(wrow0 + l32, nvalid - 1);
+  const int64_t qrow = row0 + wrow0 + l32;
+  const int64_t rs = (int64_t)a.H * DH, kvs = (int64_t)a.Hkv * DH;
+  const bf16 *kg = reinterpret_cast<const bf16 *>(a.k) + kvh * DH;
+  const bf16 *vg = reinterpret_cast<const bf16 *>(a.v) + kvh * DH;
+
+  bf16x8 qf[NK], df[NK];
+  {
+    const bf16 *qg = reinterpret_cast<const bf16 *>(a.q) + qrow * rs + head * DH;
+    const bf16 *dg = reinterpret_cast<const bf16 *>(a.dout) + qrow * rs + head * DH;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      if (my_valid) {
+        qf[kk] = *reinterpret_cast<const bf16x8 *>(qg + kk * 16 + g * 8);
+        df[kk] = *reinterpret_cast<const bf16x8 *>(dg + kk * 16 + g * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[kk][e] = df[kk][e] = (bf16)0.f;
+      }
+    }
+  }
+  // scores of the 64 keys of a tile held by this lane (log2 domain), masked
+  auto scores = [&](const unsigned char *Ks, const bf16x8 (&bf)[NK], int k0, f32x16 (&acc)[2], bool mask) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[kb][v] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<DH>(Ks, kb * 32 + l32, 2 * kk + g), bf[kk],
+                                                          acc[kb], 0, 0, 0);
+    if (mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = k0 + kb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+          acc[kb][v] = key > qpos ? -INFINITY : acc[kb][v] * a.c;
+        }
+    }
+  };
+
+  // ---- walk 1: row max, sum and Delta (log2 domain)
+  float m = -INFINITY, l = 0.f, dsum = 0.f;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * kBwdKey;
+    __syncthreads();
+    stage_tile<DH, kBwdKey, false>(smem[0], kg, kvs, k0, a.S);
+    stage_tile<DH, kBwdKey, false>(smem[2], vg, kvs, k0, a.S);
+    __syncthreads();
+    if (!active) continue;
+    f32x16 sacc[2], pacc[2];
+    scores(smem[0], qf, k0, sacc, true);
+    scores(smem[2], df, k0, pacc, false);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
+    mx = halves_max(mx);
+    const float m_new = fmaxf(m, mx);  // finite from the first tile on (key 0 is visible)
+    float part = 0.f, dpart = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float e = __builtin_amdgcn_exp2f(sacc[kb][v] - m_new);
+        part += e;
+        dpart = fmaf(e, pacc[kb][v], dpart);
+      }
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    l = l * alpha + part;
+    dsum = dsum * alpha + dpart;
+    m = m_new;
+  }
+  l = halves_sum(l);
+  dsum = halves_sum(dsum);
+  const float lse = m + __log2f(l);
+  const float dlt = dsum / l;
+  if (my_valid && g == 0) {
+    a.lse[(int64_t)head * a.n + qrow] = lse;
+    a.delta[(int64_t)head * a.n + qrow] = dlt;
+  }
+
+  // ---- walk 2: dQ^T += K^T dS^T
+  f32x16 qacc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) qacc[db][v] = 0.f;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * kBwdKey;
+    __syncthreads();
+    stage_tile<DH, kBwdKey, false>(smem[0], kg, kvs, k0, a.S);
+    stage_tile<DH, kBwdKey, true>(smem[1], kg, kvs, k0, a.S);
+    stage_tile<DH, kBwdKey, false>(smem[2], vg, kvs, k0, a.S);
+    __syncthreads();
+    if (!active) continue;
+    f32x16 sacc[2], pacc[2];
+    scores(smem[0], qf, k0, sacc, true);
+    scores(smem[2], df, k0, pacc, false);  // dP^T = V dO^T (unscaled, unmasked)
+    bf16x8 ds[4], dsl[4];
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      const int kb = kq >> 1, v0 = (kq & 1) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(sacc[kb][v0 + e] - lse);
+        put_split(ds[kq], dsl[kq], e, p * (pacc[kb][v0 + e] - dlt));
+      }
+    }
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const bf16x8 kt_frag = tr_frag<DH>(smem[1], db, kq, lane);
+        qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_frag, ds[kq], qacc[db], 0, 0, 0);
+        qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_frag, dsl[kq], qacc[db], 0, 0, 0);
+      }
+  }
+  // qacc[db][v] is dQ[query][32*db + 8*(v/4) + 4*g + v%4] / scale
+  if (my_valid) {
+    float *dq = a.dq + qrow * rs + head * DH + g * 4;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq)
+        *reinterpret_cast<float4 *>(dq + db * 32 + vq * 8) =
+            make_float4(qacc[db][vq * 4] * a.scale, qacc[db][vq * 4 + 1] * a.scale, qacc[db][vq * 4 + 2] * a.scale,
+                        qacc[db][vq * 4 + 3] * a.scale);
+  }
+#endif
+}
+
+// ---------------------------------------------------------------- dK, dV (bf16)
+constexpr int kBwdQ = 32;  // query rows per step of the dK/dV walk
+
+template <int DH>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using G = BTile<DH>;
+  constexpr int ND = DH / 32, NK = DH / 16;
+  constexpr int TB = kBwdQ * G::ROWB;
+  // Q (ROW), Q (TR), dO (ROW), dO (TR), then the rows' statistics and positions
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4][TB];
+  __shared__ float lse_s[kBwdQ], dlt_s[kBwdQ];
+  __shared__ int pos_s[kBwdQ];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int kvh = blockIdx.x / a.Tk;
+  const int64_t kb0 = (int64_t)(blockIdx.x % a.Tk) * 128;
+  const int64_t key = kb0 + wave * 32 + l32;
+  const int64_t rs = (int64_t)a.H * DH, kvs = (int64_t)a.Hkv * DH;
+
+  bf16x8 kf[NK], vf[NK];
+  {
+    const bf16 *kg = reinterpret_cast<const bf16 *>(a.k) + key * kvs + kvh * DH;
+    const bf16 *vg = reinterpret_cast<const bf16 *>(a.v) + key * kvs + kvh * DH;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      if (key < a.S) {
+        kf[kk] = *reinterpret_cast<const bf16x8 *>(kg + kk * 16 + g * 8);
+        vf[kk] = *reinterpret_cast<const bf16x8 *>(vg + kk * 16 + g * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kf[kk][e] = vf[kk][e] = (bf16)0.f;
+      }
+    }
+  }
+  f32x16 kacc[ND], vacc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) kacc[db][v] = vacc[db][v] = 0.f;
+  const int wkey0 = (int)kb0 + wave * 32;  // first key of this wave
+
+  for (int hi = 0; hi < a.grp; ++hi) {
+    const int head = kvh * a.grp + hi;
+    const bf16 *qg = reinterpret_cast<const bf16 *>(a.q) + head * DH;
+    const bf16 *dg = reinterpret_cast<const bf16 *>(a.dout) + head * DH;
+    for (int chh = 0; chh < 2; ++chh) {
+      const int base = chh == 0 ? a.zz.base0 : a.zz.base1;  // position of the chunk's first row
+      const int t_end = (chh + 1) * a.zz.C;
+      const int t_lo = chh * a.zz.C + (int)max<int64_t>(0, kb0 - base);  // first row that sees a key of the block
+      for (int t0 = t_lo; t0 < t_end; t0 += kBwdQ) {
+        __syncthreads();
+        stage_tile<DH, kBwdQ, false>(smem[0], qg, rs, t0, t_end);
+        stage_tile<DH, kBwdQ, true>(smem[1], qg, rs, t0, t_end);
+        stage_tile<DH, kBwdQ, false>(smem[2], dg, rs, t0, t_end);
+        stage_tile<DH, kBwdQ, true>(smem[3], dg, rs, t0, t_end);
+        if (threadIdx.x < kBwdQ) {
+          const int t = t0 + threadIdx.x;
+          const bool ok = t < t_end;
+          lse_s[threadIdx.x] = ok ? a.lse[(int64_t)head * a.n + t] : 0.f;
+          dlt_s[threadIdx.x] = ok ? a.delta[(int64_t)head * a.n + t] : 0.f;
+          pos_s[threadIdx.x] = ok ? base + (t - chh * a.zz.C) : -1;
+        }
+        __syncthreads();
+        const int tmax = min(t_end, t0 + kBwdQ) - 1;
+        const int pmax = base + (tmax - chh * a.zz.C);  // last position of the step
+        if (wkey0 > pmax) continue;                     // every key of the wave is past every row
+        f32x16 sacc, pacc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<DH>(smem[0], l32, 2 * kk + g), kf[kk], sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<DH>(smem[2], l32, 2 * kk + g), vf[kk], pacc, 0, 0, 0);
+        }
+        // sacc[v]: S[row 8*(v/4) + 4*g + v%4][key]; P and dS in the B-operand order
+        bf16x8 ph[2], dh[2], p_lo[2], ds_lo[2];
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+          const int r = m4 * 8 + g * 4;
+          const float4 ls = *reinterpret_cast<const float4 *>(&lse_s[r]);
+          const float4 dl = *reinterpret_cast<const float4 *>(&dlt_s[r]);
+          const int4 ps = *reinterpret_cast<const int4 *>(&pos_s[r]);
+          const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, dlv[4] = {dl.x, dl.y, dl.z, dl.w};
+          const int psv[4] = {ps.x, ps.y, ps.z, ps.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = m4 * 4 + e;
+            const float p = key > psv[e] ? 0.f : __builtin_amdgcn_exp2f(fmaf(sacc[v], a.c, -lsv[e]));
+            put_split(ph[v >> 3], p_lo[v >> 3], v & 7, p);
+            put_split(dh[v >> 3], ds_lo[v >> 3], v & 7, p * (pacc[v] - dlv[e]));
+          }
+        }
+#pragma unroll
+        for (int mu = 0; mu < 2; ++mu)
+#pragma unroll
+          for (int db = 0; db < ND; ++db) {
+            const bf16x8 dot = tr_frag<DH>(smem[3], db, mu, lane), qt = tr_frag<DH>(smem[1], db, mu, lane);
+            vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, ph[mu], vacc[db], 0, 0, 0);
+            kacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dh[mu], kacc[db], 0, 0, 0);
+            vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, p_lo[mu], vacc[db], 0, 0, 0);
+            kacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, ds_lo[mu], kacc[db], 0, 0, 0);
+          }
+      }
+    }
+  }
+  // kacc/vacc[db][v]: feature 32*db + 8*(v/4) + 4*g + v%4 of this lane's key
+  if (key < a.S) {
+    float *dk = a.dk + key * kvs + kvh * DH + g * 4;
+    float *dv = a.dv + key * kvs + kvh * DH + g * 4;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        *reinterpret_cast<float4 *>(dk + db * 32 + vq * 8) =
+            make_float4(kacc[db][vq * 4] * a.scale, kacc[db][vq * 4 + 1] * a.scale, kacc[db][vq * 4 + 2] * a.scale,
+                        kacc[db][vq * 4 + 3] * a.scale);
+        *reinterpret_cast<float4 *>(dv + db * 32 + vq * 8) =
+            make_float4(vacc[db][vq * 4], vacc[db][vq * 4 + 1], vacc[db][vq * 4 + 2], vacc[db][vq * 4 + 3]);
+      }
+  }
+#endif
+}
+
+// ---------------------------------------------------------------- fp32
+// Row statistics and dQ: one thread per (query row, head), exact expf; the
+// log-sum-exp is kept in the log2 domain like the bf16 path.
+template <int DH>
+__global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(BwdArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  const int head = blockIdx.y;
+  if (row >= a.n) return;
+  const int qpos = a.zz.pos((int32_t)row);
+  const int64_t rs = (int64_t)a.H * DH, kvs = (int64_t)a.Hkv * DH;
+  const float *q = reinterpret_cast<const float *>(a.q) + row * rs + head * DH;
+  const float *dout = reinterpret_cast<const float *>(a.dout) + row * rs + head * DH;
+  const float *k = reinterpret_cast<const float *>(a.k) + (head / a.grp) * DH;
+  const float *v = reinterpret_cast<const float *>(a.v) + (head / a.grp) * DH;
+  float m = -INFINITY, l = 0.f, dsum = 0.f;
+  for (int u = 0; u <= qpos; ++u) {
+    float s = 0.f, dp = 0.f;
+    for (int d = 0; d < DH; ++d) {
+      s = fmaf(q[d], k[(int64_t)u * kvs + d], s);
+      dp = fmaf(dout[d], v[(int64_t)u * kvs + d], dp);
+    }
+    s *= a.scale;
+    const float m_new = fmaxf(m, s);
+    const float alpha = expf(m - m_new), e = expf(s - m_new);
+    l = l * alpha + e;
+    dsum = dsum * alpha + e * dp;
+    m = m_new;
+  }
+  const float lse_nat = m + logf(l);
+  const float dlt = dsum / l;
+  a.lse[(int64_t)head * a.n + row] = lse_nat * 1.4426950408889634f;
+  a.delta[(int64_t)head * a.n + row] = dlt;
+  float acc[DH];
+  for (int d = 0; d < DH; ++d) acc[d] = 0.f;
+  for (int u = 0; u <= qpos; ++u) {
+    float s = 0.f, dp = 0.f;
+    for (int d = 0; d < DH; ++d) {
+      s = fmaf(q[d], k[(int64_t)u * kvs + d], s);
+      dp = fmaf(dout[d], v[(int64_t)u * kvs + d], dp);
+    }
+    const float ds = expf(s * a.scale - lse_nat) * (dp - dlt);
+    for (int d = 0; d < DH; ++d) acc[d] = fmaf(ds, k[(int64_t)u * kvs + d], acc[d]);
+  }
+  float *dq = a.dq + row * rs + head * DH;
+  for (int d = 0; d < DH; ++d) dq[d] = acc[d] * a.scale;
+}
+
+// dK, dV: one thread per (key, K/V head) over every query row that sees the
+// key, in every query head of the group.
+template <int DH>
+__global__ __launch_bounds__(64) void attn_bwd_dkv_f32_kernel(BwdArgs a) {
+  const int64_t key = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  const int kvh = blockIdx.y;
+  if (key >= a.S) return;
+  const int64_t rs = (int64_t)a.H * DH, kvs = (int64_t)a.Hkv * DH;
+  const float *k = reinterpret_cast<const float *>(a.k) + key * kvs + kvh * DH;
+  const float *v = reinterpret_cast<const float *>(a.v) + key * kvs + kvh * DH;
+  float gk[DH], gv[DH];
+  for (int d = 0; d < DH; ++d) gk[d] = gv[d] = 0.f;
+  for (int hi = 0; hi < a.grp; ++hi) {
+    const int head = kvh * a.grp + hi;
+    for (int t = 0; t < a.n; ++t) {
+      if (a.zz.pos(t) < key) continue;
+      const float *q = reinterpret_cast<const float *>(a.q) + (int64_t)t * rs + head * DH;
+      const float *dout = reinterpret_cast<const float *>(a.dout) + (int64_t)t * rs + head * DH;
+      float s = 0.f, dp = 0.f;
+      for (int d = 0; d < DH; ++d) {
+        s = fmaf(q[d], k[d], s);
+        dp = fmaf(dout[d], v[d], dp);
+      }
+      const float lse_nat = a.lse[(int64_t)head * a.n + t] * 0.69314718055994531f;
+      const float p = expf(s * a.scale - lse_nat);
+      const float ds = p * (dp - a.delta[(int64_t)head * a.n + t]);
+      for (int d = 0; d < DH; ++d) {
+        gk[d] = fmaf(ds, q[d], gk[d]);
+        gv[d] = fmaf(p, dout[d], gv[d]);
+      }
+    }
+  }
+  float *dk = a.dk + key * kvs + kvh * DH;
+  float *dv = a.dv + key * kvs + kvh * DH;
+  for (int d = 0; d < DH; ++d) {
+    dk[d] = gk[d] * a.scale;
+    dv[d] = gv[d];
+  }
+}
+
+hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout, float *dq, float *dk, float *dv, float *lse, float *delta, int64_t S,
+                                int32_t n, int32_t H, int32_t Hkv, int32_t Dh, float scale, ZigzagMap zz,
+                                hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (Hkv < 1 || H % Hkv != 0 || (Dh != 64 && Dh != 128)) return hipErrorInvalidValue;
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.lse = lse;
+  a.delta = delta;
+  a.S = S;
+  a.n = n;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.grp = H / Hkv;
+  a.scale = scale;
+  a.c = scale * 1.4426950408889634f;
+  a.zz = zz;
+  a.Tq = (zz.C + 127) / 128;
+  a.Tk = (int32_t)((S + 127) / 128);
+  if (dtype == TSP_BF16) {
+    const dim3 qgrid(H * 2 * a.Tq), kgrid(Hkv * a.Tk);
+    if (Dh == 128) {
+      hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, qgrid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(attn_bwd_dkv_kernel<128>, kgrid, dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, qgrid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(attn_bwd_dkv_kernel<64>, kgrid, dim3(256), 0, s, a);
+    }
+  } else {
+    const dim3 qgrid((n + 63) / 64, H), kgrid((unsigned)((S + 63) / 64), Hkv);
+    if (Dh == 128) {
+      hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<128>, qgrid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL(attn_bwd_dkv_f32_kernel<128>, kgrid, dim3(64), 0, s, a);
+    } else {
+      hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<64>, qgrid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL(attn_bwd_dkv_f32_kernel<64>, kgrid, dim3(64), 0, s, a);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tsp

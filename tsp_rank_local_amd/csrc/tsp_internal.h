@@ -149,6 +149,15 @@ hipError_t launch_attention(int dtype, const void *q, const void *k, const void 
 hipError_t launch_lead_attention(const float *q, const float *k, const float *v, float *o, int32_t m, int32_t H,
                                  int32_t Hkv, int32_t Dh, float scale, hipStream_t s);
 
+// Backward of launch_attention (bf16 or fp32 inputs, no pre-scaled Q): q,
+// dout [n][H][Dh] and k, v [S][Hkv][Dh] in dtype; dq [n][H][Dh] and the
+// rank's contributions dk, dv [S][Hkv][Dh] in fp32 (every row written). lse,
+// delta: scratch [H][n] fp32 each (log2-domain log-sum-exp of each row, and
+// sum over its keys of P dP).
+hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout, float *dq, float *dk, float *dv, float *lse, float *delta, int64_t S,
+                                int32_t n, int32_t H, int32_t Hkv, int32_t Dh, float scale, ZigzagMap zz,
+                                hipStream_t s);
+
 // ---------------------------------------------------------------- timing
 // Bracket a launch with events when profiling is on (api.cpp).
 void prof_begin(int kclass, hipStream_t s);
