@@ -295,7 +295,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["layer", "mlp", "attn", "layers32", "mlp_bwd"], default="layer")
+    ap.add_argument("--workload", choices=["layer", "mlp", "attn", "layers32", "mlp_bwd", "attn_bwd"], default="layer")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--rope-base", type=float, default=0.0,
                     help="rotary embedding base for the layer workloads (0 = none, the pages' model)")
@@ -392,6 +392,25 @@ def main():
         step_exps = 0
         workload = ("tsp_mlp_ring_bwd: backward of the 7B MLP ring (FFN), 16384x4096 bf16 local x and dy, D=8 shards "
                     "of 2048x4096 and 4096x2048; dx, dW1, dW2 in fp32 (Z recomputed)")
+    elif args.workload == "attn_bwd":
+        q = synth.attn_queries(sh, seed=3)
+        k_rem, v_rem = synth.remote_kv(sh, seed=3)
+        dout = synth.normal((N, sh.H, sh.Dh), 3, synth.TID_DY, 0, dtype="bf16")
+        qd, dod = tsp.to_device(q, "bf16"), tsp.to_device(dout, "bf16")
+        kf, vf = tsp.to_device(k_rem, "bf16"), tsp.to_device(v_rem, "bf16")
+        dq = torch.empty((N, sh.H, sh.Dh), dtype=torch.float32, device="cuda")
+        dk = torch.empty((sh.S, sh.kv_heads, sh.Dh), dtype=torch.float32, device="cuda")
+        dv = torch.empty_like(dk)
+        ws = torch.empty(tsp.workspace_size(shape, tsp.TSP_WS_ATTN_BWD), dtype=torch.uint8, device="cuda")
+
+        def step():
+            tsp.tsp_zigzag_attn_bwd(shape, qd, kf, vf, dod, dq, dk, dv, ws)
+        # algorithmic: 2.5 x the forward's 4*Dh flops per unmasked (query, key)
+        # pair and head (S recomputed, dP, dV, dK, dQ)
+        step_flops = 2.5 * flops["attention"]
+        step_exps = sh.H * attn_pairs(sh.S, sh.D, r)
+        workload = (f"tsp_zigzag_attn_bwd: 32x128 heads{kv_note}, S=131072, 16384 zigzag queries of rank {r} of D=8; "
+                    f"dq, dk, dv in fp32")
     elif args.workload == "layers32":
         # 32 layers resident in HBM (82 GB of weights and K/V), each with its
         # own weights and remote K/V, generated on the GPU from a fixed seed:
@@ -510,6 +529,11 @@ def main():
                     # counters were taken on rank 0 with 32 K/V heads
                     "traffic": (traffic_from_profile(os.path.join(ROOT, "tsp_rank_local_amd", "csrc", "attention.hip"),
                                                      "attention_7b") if r == 0 and sh.kv_heads == sh.H else None)}
+    elif "attn_bwd" in kernels:
+        t_b = kernels["attn_bwd"]["ms_per_launch"] * 1e-3
+        achieved = 2.5 * flops["attention"] / t_b / 1e12
+        roofline = {"kernel": "attn_bwd_dq_kernel + attn_bwd_dkv_kernel<128>", "bound": "mfma", "achieved": achieved,
+                    "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_BF16, "traffic": None}
     elif "bwd_gemm" in kernels:
         # five launches of one product size each (Z recomputation, dZ, dW1, dW2, dx)
         t_g = kernels["bwd_gemm"]["ms_per_launch"] * 1e-3

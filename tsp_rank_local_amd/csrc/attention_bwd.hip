@@ -68,20 +68,38 @@ struct BTile {
   }
 };
 
-// Rows [r0, r0 + R) of a bf16 [*][pitch] tensor (DH columns from src) into
-// LDS in ROW (TR = false) or TR layout; rows at or past rmax read as zero.
-template <int DH, int R, bool TR>
-__device__ __forceinline__ void stage_tile(unsigned char *dst, const bf16 *src, int64_t pitch, int64_t r0,
-                                           int64_t rmax) {
+// Rows [r0, r0 + R) of a bf16 [*][pitch] tensor (DH columns from src) go to
+// LDS in ROW or TR layout, rows at or past rmax as zeros, in two halves, so
+// that the global loads of the next tile can be issued before the current
+// tile's math and land in registers meanwhile: load_tile fills this thread's
+// chunks, store_tile writes them to LDS.
+template <int DH, int R>
+struct TileRegs {
+  static constexpr int N = R * BTile<DH>::CPR / 256;  // 16-byte chunks per thread
+  u32x4 v[N];
+};
+template <int DH, int R>
+__device__ __forceinline__ void load_tile(TileRegs<DH, R> &t, const bf16 *src, int64_t pitch, int64_t r0,
+                                          int64_t rmax) {
   using G = BTile<DH>;
-  constexpr int CH = R * G::CPR;
-  for (int c = threadIdx.x; c < CH; c += 256) {
+#pragma unroll
+  for (int i = 0; i < TileRegs<DH, R>::N; ++i) {
+    const int c = threadIdx.x + 256 * i;
     const int row = c / G::CPR, ch = c % G::CPR;
     const int64_t gr = r0 + row;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (gr < rmax) val = *reinterpret_cast<const u32x4 *>(src + gr * pitch + ch * 8);
+    t.v[i] = u32x4{0u, 0u, 0u, 0u};
+    if (gr < rmax) t.v[i] = *reinterpret_cast<const u32x4 *>(src + gr * pitch + ch * 8);
+  }
+}
+template <int DH, int R, bool TR>
+__device__ __forceinline__ void store_tile(unsigned char *dst, const TileRegs<DH, R> &t) {
+  using G = BTile<DH>;
+#pragma unroll
+  for (int i = 0; i < TileRegs<DH, R>::N; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const int row = c / G::CPR, ch = c % G::CPR;
     const int pos = TR ? G::tr_swz(row, ch) : G::row_swz(row, ch);
-    *reinterpret_cast<u32x4 *>(dst + row * G::ROWB + pos * 16) = val;
+    *reinterpret_cast<u32x4 *>(dst + row * G::ROWB + pos * 16) = t.v[i];
   }
 }
 
@@ -188,12 +206,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 
   // ---- walk 1: row max, sum and Delta (log2 domain)
   float m = -INFINITY, l = 0.f, dsum = 0.f;
+  TileRegs<DH, kBwdKey> kr, vr;
+  load_tile<DH, kBwdKey>(kr, kg, kvs, 0, a.S);
+  load_tile<DH, kBwdKey>(vr, vg, kvs, 0, a.S);
   for (int kt = 0; kt < n_kt; ++kt) {
     const int k0 = kt * kBwdKey;
     __syncthreads();
-    stage_tile<DH, kBwdKey, false>(smem[0], kg, kvs, k0, a.S);
-    stage_tile<DH, kBwdKey, false>(smem[2], vg, kvs, k0, a.S);
+    store_tile<DH, kBwdKey, false>(smem[0], kr);
+    store_tile<DH, kBwdKey, false>(smem[2], vr);
     __syncthreads();
+    if (kt + 1 < n_kt) {  // next tile on its way during this one's math
+      load_tile<DH, kBwdKey>(kr, kg, kvs, k0 + kBwdKey, a.S);
+      load_tile<DH, kBwdKey>(vr, vg, kvs, k0 + kBwdKey, a.S);
+    }
     if (!active) continue;
     f32x16 sacc[2], pacc[2];
     scores(smem[0], qf, k0, sacc, true);
@@ -234,13 +259,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   for (int db = 0; db < ND; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) qacc[db][v] = 0.f;
+  load_tile<DH, kBwdKey>(kr, kg, kvs, 0, a.S);
+  load_tile<DH, kBwdKey>(vr, vg, kvs, 0, a.S);
   for (int kt = 0; kt < n_kt; ++kt) {
     const int k0 = kt * kBwdKey;
     __syncthreads();
-    stage_tile<DH, kBwdKey, false>(smem[0], kg, kvs, k0, a.S);
-    stage_tile<DH, kBwdKey, true>(smem[1], kg, kvs, k0, a.S);
-    stage_tile<DH, kBwdKey, false>(smem[2], vg, kvs, k0, a.S);
+    store_tile<DH, kBwdKey, false>(smem[0], kr);
+    store_tile<DH, kBwdKey, true>(smem[1], kr);
+    store_tile<DH, kBwdKey, false>(smem[2], vr);
     __syncthreads();
+    if (kt + 1 < n_kt) {
+      load_tile<DH, kBwdKey>(kr, kg, kvs, k0 + kBwdKey, a.S);
+      load_tile<DH, kBwdKey>(vr, vg, kvs, k0 + kBwdKey, a.S);
+    }
     if (!active) continue;
     f32x16 sacc[2], pacc[2];
     scores(smem[0], qf, k0, sacc, true);
@@ -328,20 +359,33 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       const int base = chh == 0 ? a.zz.base0 : a.zz.base1;  // position of the chunk's first row
       const int t_end = (chh + 1) * a.zz.C;
       const int t_lo = chh * a.zz.C + (int)max<int64_t>(0, kb0 - base);  // first row that sees a key of the block
+      TileRegs<DH, kBwdQ> qr, dr;
+      float st_lse = 0.f, st_dlt = 0.f;
+      auto fetch = [&](int t0) {  // the step's rows into registers (statistics: threads < 32)
+        load_tile<DH, kBwdQ>(qr, qg, rs, t0, t_end);
+        load_tile<DH, kBwdQ>(dr, dg, rs, t0, t_end);
+        const int t = t0 + (int)threadIdx.x;
+        if (threadIdx.x < kBwdQ && t < t_end) {
+          st_lse = a.lse[(int64_t)head * a.n + t];
+          st_dlt = a.delta[(int64_t)head * a.n + t];
+        }
+      };
+      if (t_lo < t_end) fetch(t_lo);
       for (int t0 = t_lo; t0 < t_end; t0 += kBwdQ) {
         __syncthreads();
-        stage_tile<DH, kBwdQ, false>(smem[0], qg, rs, t0, t_end);
-        stage_tile<DH, kBwdQ, true>(smem[1], qg, rs, t0, t_end);
-        stage_tile<DH, kBwdQ, false>(smem[2], dg, rs, t0, t_end);
-        stage_tile<DH, kBwdQ, true>(smem[3], dg, rs, t0, t_end);
+        store_tile<DH, kBwdQ, false>(smem[0], qr);
+        store_tile<DH, kBwdQ, true>(smem[1], qr);
+        store_tile<DH, kBwdQ, false>(smem[2], dr);
+        store_tile<DH, kBwdQ, true>(smem[3], dr);
         if (threadIdx.x < kBwdQ) {
           const int t = t0 + threadIdx.x;
           const bool ok = t < t_end;
-          lse_s[threadIdx.x] = ok ? a.lse[(int64_t)head * a.n + t] : 0.f;
-          dlt_s[threadIdx.x] = ok ? a.delta[(int64_t)head * a.n + t] : 0.f;
+          lse_s[threadIdx.x] = ok ? st_lse : 0.f;
+          dlt_s[threadIdx.x] = ok ? st_dlt : 0.f;
           pos_s[threadIdx.x] = ok ? base + (t - chh * a.zz.C) : -1;
         }
         __syncthreads();
+        if (t0 + kBwdQ < t_end) fetch(t0 + kBwdQ);
         const int tmax = min(t_end, t0 + kBwdQ) - 1;
         const int pmax = base + (tmax - chh * a.zz.C);  // last position of the step
         if (wkey0 > pmax) continue;                     // every key of the wave is past every row
