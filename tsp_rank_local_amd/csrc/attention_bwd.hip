@@ -389,13 +389,24 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
         const int tmax = min(t_end, t0 + kBwdQ) - 1;
         const int pmax = base + (tmax - chh * a.zz.C);  // last position of the step
         if (wkey0 > pmax) continue;                     // every key of the wave is past every row
-        f32x16 sacc, pacc;
+        // two accumulators per product (even and odd K slices), so that four
+        // independent MFMA chains interleave
+        f32x16 sacc, pacc, sacc1, pacc1;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = 0.f;
+        for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = sacc1[v] = pacc1[v] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
+        for (int kk = 0; kk < NK; kk += 2) {
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<DH>(smem[0], l32, 2 * kk + g), kf[kk], sacc, 0, 0, 0);
           pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<DH>(smem[2], l32, 2 * kk + g), vf[kk], pacc, 0, 0, 0);
+          sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<DH>(smem[0], l32, 2 * kk + 2 + g), kf[kk + 1], sacc1,
+                                                          0, 0, 0);
+          pacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<DH>(smem[2], l32, 2 * kk + 2 + g), vf[kk + 1], pacc1,
+                                                          0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          sacc[v] += sacc1[v];
+          pacc[v] += pacc1[v];
         }
         // sacc[v]: S[row 8*(v/4) + 4*g + v%4][key]; P and dS in the B-operand order
         bf16x8 ph[2], dh[2], p_lo[2], ds_lo[2];
