@@ -156,10 +156,22 @@ SQ_PASSES = (
 )
 
 
-def summarize_sq(csvs):
-    """Per-kernel shader counters of the default layer step: fractions of the
+# workload -> (title, summary file, the bench arguments of the counter runs)
+SQ_WORKLOADS = {
+    "layer": ("the default layer step (7B, rank 0 of D=8, S=131072)", "layer7b_sq_counters.txt",
+              "--steps 1 --warmup 0 --cpu-rows 0"),
+    "attn_bwd": ("the 7B zigzag attention backward (rank 0 of D=8, S=131072)", "attn_bwd_7b_sq_counters.txt",
+                 "--workload attn_bwd --steps 1 --warmup 0"),
+    "mlp_bwd": ("the 7B MLP ring backward (16384 tokens, D=8)", "mlp_bwd_7b_sq_counters.txt",
+                "--workload mlp_bwd --steps 1 --warmup 0"),
+}
+
+
+def summarize_sq(csvs, workload="layer"):
+    """Per-kernel shader counters of one workload's step: fractions of the
     kernel's cycles per SIMD (cycles = GRBM_GUI_ACTIVE / 8 XCDs, 1024 SIMDs),
     instruction mixes per MFMA. One line per kernel, averaged over dispatches."""
+    title, fname, bench_args = SQ_WORKLOADS[workload]
     import csv
     per = {}  # (kernel, dispatch) -> {counter: value}
     for path in csvs:
@@ -190,12 +202,13 @@ def summarize_sq(csvs):
             if n in c:
                 f[k] = c[n]
         kern.setdefault(name, []).append(f)
-    lines = ["# Shader counters of the default layer step (7B, rank 0 of D=8, S=131072), per kernel.",
+    lines = [f"# Shader counters of {title}, per kernel.",
              "# Made by (one step, two passes, each within one pass's counter limits):"]
     for i, ctrs in enumerate(SQ_PASSES):
         lines.append(f"#   rocprofv3 --pmc {ctrs} -d <dir{i + 1}> -o run --output-format csv -- "
-                     "python bench.py --steps 1 --warmup 0 --cpu-rows 0")
-    lines += ["#   python bench.py --summarize-sq <dir1>/run_counter_collection.csv <dir2>/run_counter_collection.csv",
+                     f"python bench.py {bench_args}")
+    wl = "" if workload == "layer" else f" --workload {workload}"
+    lines += [f"#   python bench.py --summarize-sq <dir1>/run_counter_collection.csv <dir2>/run_counter_collection.csv{wl}",
               "# Fractions are of the kernel's cycles per SIMD (GRBM_GUI_ACTIVE / 8 XCDs, x 1024 SIMDs);",
               "# SQ_ACTIVE_INST_* count 4-cycle units. Instruction ratios are per MFMA instruction.",
               "kernel | mfma_busy | valu_active | coexec | lds_active | lds_wait | valu/mfma | salu/mfma | lds/mfma "
@@ -218,7 +231,7 @@ def summarize_sq(csvs):
         lines.append(f"{name[:80]} | {fmt('mfma_busy')} | {fmt('valu_active')} | {fmt('mfma_valu_coexec')} | "
                      f"{fmt('lds_active')} | {fmt('lds_wait')} | {ratio(va)} | {ratio(sa)} | {ratio(ld)} | "
                      f"{fmt('trans_per_mfma')} | {fmt('bank_conflicts_per_lds_inst')}")
-    out = os.path.join(ROOT, "profiles", "layer7b_sq_counters.txt")
+    out = os.path.join(ROOT, "profiles", fname)
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -318,7 +331,7 @@ def main():
         summarize_counters(*args.summarize_counters, copy_mib=args.copy_mib or 1024)
         return
     if args.summarize_sq:
-        summarize_sq(args.summarize_sq)
+        summarize_sq(args.summarize_sq, args.workload)
         return
     if args.gpus != 1:
         sys.exit(f"bench.py: only --gpus 1 is supported; this build measures one rank's share on one GPU "

@@ -33,6 +33,8 @@
 // fp32 inputs run plain per-row kernels with exact expf.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "tsp_internal.h"
 
@@ -45,7 +47,7 @@ struct BwdArgs {
   float *delta;  // [H][n]: sum over the row's keys of P dP
   int64_t S;
   int32_t n, H, Hkv, grp;
-  float scale, c;  // c = scale * log2(e)
+  float scale, c;  // c = scale * log2(e) (at least the smallest normal float)
   ZigzagMap zz;
   int32_t Tq;  // 128-row query tiles per chunk (launch 1)
   int32_t Tk;  // 128-key tiles over the sequence (launch 2)
@@ -132,12 +134,15 @@ __device__ __forceinline__ bf16x8 tr_frag(const unsigned char *t, int db, int mu
 // ---------------------------------------------------------------- dQ (bf16)
 constexpr int kBwdKey = 64;  // keys per tile of the dQ walk
 
-// v as bf16 at element e of hi, and the remainder v - hi (exact in fp32) as
-// bf16 at element e of lo.
-__device__ __forceinline__ void put_split(bf16x8 &hi, bf16x8 &lo, int e, float v) {
-  const bf16 h = (bf16)v;
-  hi[e] = h;
-  lo[e] = (bf16)(v - (float)h);
+// v0, v1 as bf16 at elements e, e + 1 of hi (one packed conversion), and
+// the remainders v - hi (exact in fp32) as bf16 at the same elements of lo.
+__device__ __forceinline__ void put_split2(bf16x8 &hi, bf16x8 &lo, int e, float v0, float v1) {
+  const bf16x2 h = {(bf16)v0, (bf16)v1};
+  hi[e] = h[0];
+  hi[e + 1] = h[1];
+  const bf16x2 l = {(bf16)(v0 - (float)h[0]), (bf16)(v1 - (float)h[1])};
+  lo[e] = l[0];
+  lo[e + 1] = l[1];
 }
 
 template <int DH>
@@ -181,8 +186,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
       }
     }
   }
-  // scores of the 64 keys of a tile held by this lane (log2 domain), masked
-  auto scores = [&](const unsigned char *Ks, const bf16x8 (&bf)[NK], int k0, f32x16 (&acc)[2], bool mask) {
+  // raw products of the 64 keys of a tile held by this lane: acc[kb][v] is
+  // key k0 + kb*32 + 8*(v/4) + 4*g + v%4
+  auto scores = [&](const unsigned char *Ks, const bf16x8 (&bf)[NK], f32x16 (&acc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -193,15 +199,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
         acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<DH>(Ks, kb * 32 + l32, 2 * kk + g), bf[kk],
                                                           acc[kb], 0, 0, 0);
-    if (mask) {
+  };
+  // keys past the lane's query get -inf; only tiles that reach past the
+  // wave's first query need it (c > 0, so -inf stays -inf after scaling)
+  const int wmin = pos0 + wrow0;
+  auto mask = [&](f32x16 (&acc)[2], int k0) {
+    if (k0 + kBwdKey - 1 <= wmin) return;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = k0 + kb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-          acc[kb][v] = key > qpos ? -INFINITY : acc[kb][v] * a.c;
-        }
-    }
+      for (int v = 0; v < 16; ++v) {
+        const int key = k0 + kb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+        if (key > qpos) acc[kb][v] = -INFINITY;
+      }
   };
 
   // ---- walk 1: row max, sum and Delta (log2 domain)
@@ -221,21 +231,22 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     }
     if (!active) continue;
     f32x16 sacc[2], pacc[2];
-    scores(smem[0], qf, k0, sacc, true);
-    scores(smem[2], df, k0, pacc, false);
+    scores(smem[0], qf, sacc);
+    scores(smem[2], df, pacc);
+    mask(sacc, k0);
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-    mx = halves_max(mx);
+    mx = halves_max(mx) * a.c;
     const float m_new = fmaxf(m, mx);  // finite from the first tile on (key 0 is visible)
     float part = 0.f, dpart = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float e = __builtin_amdgcn_exp2f(sacc[kb][v] - m_new);
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v], a.c, -m_new));
         part += e;
         dpart = fmaf(e, pacc[kb][v], dpart);
       }
@@ -274,16 +285,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     }
     if (!active) continue;
     f32x16 sacc[2], pacc[2];
-    scores(smem[0], qf, k0, sacc, true);
-    scores(smem[2], df, k0, pacc, false);  // dP^T = V dO^T (unscaled, unmasked)
+    scores(smem[0], qf, sacc);
+    scores(smem[2], df, pacc);  // dP^T = V dO^T
+    mask(sacc, k0);
     bf16x8 ds[4], dsl[4];
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) {
       const int kb = kq >> 1, v0 = (kq & 1) * 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(sacc[kb][v0 + e] - lse);
-        put_split(ds[kq], dsl[kq], e, p * (pacc[kb][v0 + e] - dlt));
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v0 + e], a.c, -lse));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v0 + e + 1], a.c, -lse));
+        put_split2(ds[kq], dsl[kq], e, p0 * (pacc[kb][v0 + e] - dlt), p1 * (pacc[kb][v0 + e + 1] - dlt));
       }
     }
 #pragma unroll
@@ -408,24 +421,41 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
           sacc[v] += sacc1[v];
           pacc[v] += pacc1[v];
         }
-        // sacc[v]: S[row 8*(v/4) + 4*g + v%4][key]; P and dS in the B-operand order
+        // sacc[v]: S[row 8*(v/4) + 4*g + v%4][key]; P and dS in the B-operand
+        // order. Rows past the chunk, or before some key of the wave, need
+        // the mask; the rest of the walk does not.
+        const bool need_mask = t0 + kBwdQ > t_end || base + (t0 - chh * a.zz.C) < wkey0 + 31;
         bf16x8 ph[2], dh[2], p_lo[2], ds_lo[2];
+        auto probs = [&](auto masked) {
 #pragma unroll
-        for (int m4 = 0; m4 < 4; ++m4) {
-          const int r = m4 * 8 + g * 4;
-          const float4 ls = *reinterpret_cast<const float4 *>(&lse_s[r]);
-          const float4 dl = *reinterpret_cast<const float4 *>(&dlt_s[r]);
-          const int4 ps = *reinterpret_cast<const int4 *>(&pos_s[r]);
-          const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, dlv[4] = {dl.x, dl.y, dl.z, dl.w};
-          const int psv[4] = {ps.x, ps.y, ps.z, ps.w};
+          for (int m4 = 0; m4 < 4; ++m4) {
+            const int r = m4 * 8 + g * 4;
+            const float4 ls = *reinterpret_cast<const float4 *>(&lse_s[r]);
+            const float4 dl = *reinterpret_cast<const float4 *>(&dlt_s[r]);
+            const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, dlv[4] = {dl.x, dl.y, dl.z, dl.w};
+            float pv[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int v = m4 * 4 + e;
-            const float p = key > psv[e] ? 0.f : __builtin_amdgcn_exp2f(fmaf(sacc[v], a.c, -lsv[e]));
-            put_split(ph[v >> 3], p_lo[v >> 3], v & 7, p);
-            put_split(dh[v >> 3], ds_lo[v >> 3], v & 7, p * (pacc[v] - dlv[e]));
+            for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[m4 * 4 + e], a.c, -lsv[e]));
+            if constexpr (decltype(masked)::value) {
+              const int4 ps = *reinterpret_cast<const int4 *>(&pos_s[r]);
+              const int psv[4] = {ps.x, ps.y, ps.z, ps.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (key > psv[e]) pv[e] = 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+              const int v = m4 * 4 + e;  // v, v + 1 share the fragment (v is even)
+              put_split2(ph[v >> 3], p_lo[v >> 3], v & 7, pv[e], pv[e + 1]);
+              put_split2(dh[v >> 3], ds_lo[v >> 3], v & 7, pv[e] * (pacc[v] - dlv[e]),
+                         pv[e + 1] * (pacc[v + 1] - dlv[e + 1]));
+            }
           }
-        }
+        };
+        if (need_mask)
+          probs(std::true_type{});
+        else
+          probs(std::false_type{});
 #pragma unroll
         for (int mu = 0; mu < 2; ++mu)
 #pragma unroll
@@ -565,7 +595,9 @@ hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const v
   a.Hkv = Hkv;
   a.grp = H / Hkv;
   a.scale = scale;
-  a.c = scale * 1.4426950408889634f;
+  // multiplier of the scores in the exp2 domain, kept at least the smallest
+  // normal float so that masked scores (-inf) stay -inf with a zero scale
+  a.c = fmaxf(scale * 1.4426950408889634f, 1.17549435e-38f);
   a.zz = zz;
   a.Tq = (zz.C + 127) / 128;
   a.Tk = (int32_t)((S + 127) / 128);
