@@ -105,28 +105,50 @@ __device__ __forceinline__ void store_tile(unsigned char *dst, const TileRegs<DH
   }
 }
 
-// Row fragment: 8 bf16 of row `row`, logical chunk ch (ROW layout).
+// Lane-constant LDS byte offsets of the fragment reads of a tile, computed
+// once per kernel. row[kk]: the ROW-layout chunk of row lane%32, logical
+// chunk 2*kk + lane/32; rows 32.. are 32*ROWB further (same swizzle, which
+// depends on the row modulo 16, or on (row/2) modulo 8). tr[db]: the
+// transpose read for feature block db, row group 0, half 0; row group mu and
+// half hv are (16*mu + 8*hv)*ROWB further (the TR swizzle depends on the row
+// modulo 4 only).
 template <int DH>
-__device__ __forceinline__ bf16x8 row_frag(const unsigned char *t, int row, int ch) {
-  return *reinterpret_cast<const bf16x8 *>(t + row * BTile<DH>::ROWB + BTile<DH>::row_swz(row, ch) * 16);
+struct FragOff {
+  int row[DH / 16];
+  int tr[DH / 32];
+};
+template <int DH>
+__device__ __forceinline__ FragOff<DH> frag_off(int lane) {
+  using G = BTile<DH>;
+  FragOff<DH> f;
+  const int g = lane >> 5, l32 = lane & 31, r16 = lane & 15, dsub = (lane >> 4) & 1;
+#pragma unroll
+  for (int kk = 0; kk < DH / 16; ++kk) f.row[kk] = l32 * G::ROWB + G::row_swz(l32, 2 * kk + g) * 16;
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db) {
+    const int row = g * 4 + (r16 >> 2);
+    const int dstart = db * 32 + dsub * 16 + 4 * (r16 & 3);
+    f.tr[db] = row * G::ROWB + G::tr_swz(row, dstart >> 3) * 16 + (dstart & 7) * 2;
+  }
+  return f;
 }
 
-// Transpose fragment (TR layout) for feature block db and row group mu (16
-// rows): lane l receives, for feature 32*db + l%32, rows 16*mu + 4*(l/32) +
-// {0..3} and 16*mu + 8 + 4*(l/32) + {0..3}: the A operand whose k index runs
-// over those rows in the order of the score registers.
+// Row fragment (ROW layout) at a precomputed offset.
+__device__ __forceinline__ bf16x8 row_frag(const unsigned char *t, int off) {
+  return *reinterpret_cast<const bf16x8 *>(t + off);
+}
+
+// Transpose fragment (TR layout) at precomputed offset off (row group and
+// half included): lane l receives, for feature 32*db + l%32, rows 16*mu +
+// 4*(l/32) + {0..3} and 16*mu + 8 + 4*(l/32) + {0..3}: the A operand whose k
+// index runs over those rows in the order of the score registers.
 template <int DH>
-__device__ __forceinline__ bf16x8 tr_frag(const unsigned char *t, int db, int mu, int lane) {
-  using G = BTile<DH>;
-  const int g = lane >> 5, r16 = lane & 15, dsub = (lane >> 4) & 1;
-  const int dstart = db * 32 + dsub * 16 + 4 * (r16 & 3);
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char *t, int off) {
   s16x4_b part[2];
 #pragma unroll
-  for (int hv = 0; hv < 2; ++hv) {
-    const int row = mu * 16 + hv * 8 + g * 4 + (r16 >> 2);
-    const unsigned char *addr = t + row * G::ROWB + G::tr_swz(row, dstart >> 3) * 16 + (dstart & 7) * 2;
-    part[hv] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_b *)(addr));
-  }
+  for (int hv = 0; hv < 2; ++hv)
+    part[hv] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_b *)(t + off + hv * 8 * BTile<DH>::ROWB));
   const s16x8_t both = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
   return __builtin_bit_cast(bf16x8, both);
 }
@@ -154,6 +176,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[3][TB];  // K (ROW), K (TR), V (ROW)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
+  const FragOff<DH> fo = frag_off<DH>(lane);
   const int head = blockIdx.x / (2 * a.Tq), tile = blockIdx.x % (2 * a.Tq);
   const int kvh = head / a.grp;
   const int ch_half = tile < a.Tq ? 0 : 1;
@@ -189,16 +212,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   // raw products of the 64 keys of a tile held by this lane: acc[kb][v] is
   // key k0 + kb*32 + 8*(v/4) + 4*g + v%4
   auto scores = [&](const unsigned char *Ks, const bf16x8 (&bf)[NK], f32x16 (&acc)[2]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[kb][v] = 0.f;
+    const f32x16 zero = {};
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<DH>(Ks, kb * 32 + l32, 2 * kk + g), bf[kk],
-                                                          acc[kb], 0, 0, 0);
+        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Ks, fo.row[kk] + kb * 32 * G::ROWB), bf[kk],
+                                                          kk == 0 ? zero : acc[kb], 0, 0, 0);
   };
   // keys past the lane's query get -inf; only tiles that reach past the
   // wave's first query need it (c > 0, so -inf stays -inf after scaling)
@@ -303,7 +323,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
-        const bf16x8 kt_frag = tr_frag<DH>(smem[1], db, kq, lane);
+        const bf16x8 kt_frag = tr_frag<DH>(smem[1], fo.tr[db] + kq * 16 * G::ROWB);
         qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_frag, ds[kq], qacc[db], 0, 0, 0);
         qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_frag, dsl[kq], qacc[db], 0, 0, 0);
       }
@@ -337,6 +357,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   __shared__ int pos_s[kBwdQ];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
+  const FragOff<DH> fo = frag_off<DH>(lane);
   const int kvh = blockIdx.x / a.Tk;
   const int64_t kb0 = (int64_t)(blockIdx.x % a.Tk) * 128;
   const int64_t key = kb0 + wave * 32 + l32;
@@ -404,17 +425,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
         if (wkey0 > pmax) continue;                     // every key of the wave is past every row
         // two accumulators per product (even and odd K slices), so that four
         // independent MFMA chains interleave
-        f32x16 sacc, pacc, sacc1, pacc1;
+        // each chain starts from a zero constant (no accumulator to clear)
+        const f32x16 zero = {};
+        f32x16 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[0], fo.row[0]), kf[0], zero, 0, 0, 0);
+        f32x16 pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[2], fo.row[0]), vf[0], zero, 0, 0, 0);
+        f32x16 sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[0], fo.row[1]), kf[1], zero, 0, 0, 0);
+        f32x16 pacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[2], fo.row[1]), vf[1], zero, 0, 0, 0);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = sacc1[v] = pacc1[v] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < NK; kk += 2) {
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<DH>(smem[0], l32, 2 * kk + g), kf[kk], sacc, 0, 0, 0);
-          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<DH>(smem[2], l32, 2 * kk + g), vf[kk], pacc, 0, 0, 0);
-          sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<DH>(smem[0], l32, 2 * kk + 2 + g), kf[kk + 1], sacc1,
-                                                          0, 0, 0);
-          pacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<DH>(smem[2], l32, 2 * kk + 2 + g), vf[kk + 1], pacc1,
-                                                          0, 0, 0);
+        for (int kk = 2; kk < NK; kk += 2) {
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[0], fo.row[kk]), kf[kk], sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[2], fo.row[kk]), vf[kk], pacc, 0, 0, 0);
+          sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[0], fo.row[kk + 1]), kf[kk + 1], sacc1, 0, 0, 0);
+          pacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[2], fo.row[kk + 1]), vf[kk + 1], pacc1, 0, 0, 0);
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -460,7 +482,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
         for (int mu = 0; mu < 2; ++mu)
 #pragma unroll
           for (int db = 0; db < ND; ++db) {
-            const bf16x8 dot = tr_frag<DH>(smem[3], db, mu, lane), qt = tr_frag<DH>(smem[1], db, mu, lane);
+            const int off = fo.tr[db] + mu * 16 * G::ROWB;
+            const bf16x8 dot = tr_frag<DH>(smem[3], off), qt = tr_frag<DH>(smem[1], off);
             vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, ph[mu], vacc[db], 0, 0, 0);
             kacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dh[mu], kacc[db], 0, 0, 0);
             vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, p_lo[mu], vacc[db], 0, 0, 0);
