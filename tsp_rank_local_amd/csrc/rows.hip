@@ -154,13 +154,49 @@ __global__ __launch_bounds__(256) void transpose_kernel(PtrList in, int64_t in_l
   }
 }
 
+// bf16 with R and C multiples of 8: each thread moves 16-byte runs (8
+// elements) both ways, through a 64 x 64 tile with rows padded by 16 bytes.
+__global__ __launch_bounds__(256) void transpose_bf16x8_kernel(PtrList in, int64_t in_ld, int64_t in_panel, int32_t R,
+                                                               int32_t C, bf16 *__restrict__ out, int64_t out_ld,
+                                                               int64_t out_panel, int64_t out_zoff) {
+  __shared__ __attribute__((aligned(16))) bf16 tile[64][72];
+  const bf16 *src = reinterpret_cast<const bf16 *>(in.p[blockIdx.z]);
+  bf16 *dst = out + (int64_t)blockIdx.z * out_zoff;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int chunk = threadIdx.x + 256 * i, row = chunk >> 3, cc = (chunk & 7) * 8;
+    const int r = r0 + row, c = c0 + cc;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < R && c < C) v = *reinterpret_cast<const u32x4 *>(src + (in_panel ? panel_index(r, c, in_panel) : (int64_t)r * in_ld + c));
+    *reinterpret_cast<u32x4 *>(&tile[row][cc]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int chunk = threadIdx.x + 256 * i, orow = chunk >> 3, oc = (chunk & 7) * 8;  // output row c0 + orow
+    const int c = c0 + orow, r = r0 + oc;
+    if (c < C && r < R) {
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = tile[oc + e][orow];
+      *reinterpret_cast<bf16x8 *>(dst + (out_panel ? panel_index(c, r, out_panel) : (int64_t)c * out_ld + r)) = v;
+    }
+  }
+}
+
 hipError_t launch_transpose(int dtype, const PtrList &in, int32_t nz, int64_t in_ld, int64_t in_panel, int32_t R,
                             int32_t C, void *out, int64_t out_ld, int64_t out_panel, int64_t out_zoff, hipStream_t s) {
   if (R <= 0 || C <= 0 || nz <= 0) return hipSuccess;
   if ((in_panel || out_panel) && dtype != TSP_BF16) return hipErrorInvalidValue;
   if (nz > TSP_MAX_D || (R + 63) / 64 > 65535) return hipErrorInvalidValue;
   const dim3 grid((C + 63) / 64, (R + 63) / 64, nz);
-  if (dtype == TSP_BF16)
+  // 16-byte runs need 8-element alignment of both extents, pitches and offsets
+  const bool x8 = ((R | C) & 7) == 0 && (in_ld & 7) == 0 && (out_ld & 7) == 0 && (out_zoff & 7) == 0;
+  if (dtype == TSP_BF16 && x8)
+    hipLaunchKernelGGL(transpose_bf16x8_kernel, grid, dim3(256), 0, s, in, in_ld, in_panel, R, C,
+                       reinterpret_cast<bf16 *>(out), out_ld, out_panel, out_zoff);
+  else if (dtype == TSP_BF16)
     hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, s, in, in_ld, in_panel, R, C,
                        reinterpret_cast<bf16 *>(out), out_ld, out_panel, out_zoff);
   else
