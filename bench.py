@@ -308,7 +308,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["layer", "mlp", "attn", "layers32", "mlp_bwd", "attn_bwd"], default="layer")
+    ap.add_argument("--workload", choices=["layer", "mlp", "attn", "layers32", "mlp_bwd", "attn_bwd", "attn_bwd_lse"], default="layer")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--rope-base", type=float, default=0.0,
                     help="rotary embedding base for the layer workloads (0 = none, the pages' model)")
@@ -405,7 +405,7 @@ def main():
         step_exps = 0
         workload = ("tsp_mlp_ring_bwd: backward of the 7B MLP ring (FFN), 16384x4096 bf16 local x and dy, D=8 shards "
                     "of 2048x4096 and 4096x2048; dx, dW1, dW2 in fp32 (Z recomputed)")
-    elif args.workload == "attn_bwd":
+    elif args.workload in ("attn_bwd", "attn_bwd_lse"):
         q = synth.attn_queries(sh, seed=3)
         k_rem, v_rem = synth.remote_kv(sh, seed=3)
         dout = synth.normal((N, sh.H, sh.Dh), 3, synth.TID_DY, 0, dtype="bf16")
@@ -416,14 +416,24 @@ def main():
         dv = torch.empty_like(dk)
         ws = torch.empty(tsp.workspace_size(shape, tsp.TSP_WS_ATTN_BWD), dtype=torch.uint8, device="cuda")
 
-        def step():
-            tsp.tsp_zigzag_attn_bwd(shape, qd, kf, vf, dod, dq, dk, dv, ws)
+        if args.workload == "attn_bwd_lse":
+            # the forward's fp32 O and row log-sum-exp, made once before timing
+            o_f = torch.empty((N, sh.H, sh.Dh), dtype=torch.float32, device="cuda")
+            lse_f = torch.empty((sh.H, N), dtype=torch.float32, device="cuda")
+            tsp.tsp_zigzag_attn_lse(shape, qd, kf, vf, o_f, lse_f)
+
+            def step():
+                tsp.tsp_zigzag_attn_bwd_lse(shape, qd, kf, vf, o_f, lse_f, dod, dq, dk, dv, ws)
+        else:
+            def step():
+                tsp.tsp_zigzag_attn_bwd(shape, qd, kf, vf, dod, dq, dk, dv, ws)
         # algorithmic: 2.5 x the forward's 4*Dh flops per unmasked (query, key)
         # pair and head (S recomputed, dP, dV, dK, dQ)
         step_flops = 2.5 * flops["attention"]
         step_exps = sh.H * attn_pairs(sh.S, sh.D, r)
-        workload = (f"tsp_zigzag_attn_bwd: 32x128 heads{kv_note}, S=131072, 16384 zigzag queries of rank {r} of D=8; "
-                    f"dq, dk, dv in fp32")
+        workload = (f"{'tsp_zigzag_attn_bwd_lse' if args.workload == 'attn_bwd_lse' else 'tsp_zigzag_attn_bwd'}: "
+                    f"32x128 heads{kv_note}, S=131072, 16384 zigzag queries of rank {r} of D=8; dq, dk, dv in fp32"
+                    + ("; the forward's fp32 O and log-sum-exp given" if args.workload == "attn_bwd_lse" else ""))
     elif args.workload == "layers32":
         # 32 layers resident in HBM (82 GB of weights and K/V), each with its
         # own weights and remote K/V, generated on the GPU from a fixed seed:

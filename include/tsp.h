@@ -240,6 +240,24 @@ tsp_status tsp_zigzag_attn_bwd(const tsp_shape *shape, const void *q, const void
                                const void *dout, float *dq, float *dk, float *dv, void *ws,
                                size_t ws_bytes, void *stream);
 
+/* tsp_zigzag_attn for the backward's use: bf16 inputs (else
+ * TSP_ERR_UNSUPPORTED), plain q, o in fp32 [S/D][H][Dh], and also lse
+ * [H][S/D] fp32, the natural log of each row's softmax denominator,
+ * log sum_u exp(scale q.k_u) over its visible keys. Errors as for
+ * tsp_zigzag_attn; o and lse must not overlap the inputs or each other. */
+tsp_status tsp_zigzag_attn_lse(const tsp_shape *shape, const void *q, const void *k, const void *v,
+                               float *o, float *lse, void *stream);
+
+/* tsp_zigzag_attn_bwd with the row statistics of the forward (bf16 inputs,
+ * else TSP_ERR_UNSUPPORTED): o and lse are the outputs of
+ * tsp_zigzag_attn_lse for the same q, k, v. Each row's sum over its keys of
+ * p dp is then taken as rowsum(dout * o) from the fp32 o, and p from lse,
+ * which saves the kernels one pass over the keys; everything else is as in
+ * tsp_zigzag_attn_bwd (same workspace). */
+tsp_status tsp_zigzag_attn_bwd_lse(const tsp_shape *shape, const void *q, const void *k, const void *v,
+                                   const float *o, const float *lse, const void *dout, float *dq,
+                                   float *dk, float *dv, void *ws, size_t ws_bytes, void *stream);
+
 /* Backward of the MLP ring on rank r (an optional extension: the pages quote
  * their 2.6x for training, [P2] paragraph 1, but describe only how the
  * shards move, paragraph 2). With Z = x W1^T and y = GELU(Z) W2^T summed over

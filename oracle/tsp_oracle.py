@@ -84,6 +84,7 @@ __all__ = [
     "mlp_shard",
     "gelu_grad",
     "softmax_backward",
+    "causal_attention_lse",
     "causal_attention_backward",
     "mlp_backward",
     "layer_full",
@@ -181,6 +182,27 @@ def causal_attention(q, k, v, q_pos, scale: float, row_block: int = 256) -> np.n
             p = np.exp(s)
             p = p / p.sum(axis=1, keepdims=True)
             out[lo:hi, hd, :] = p @ vh
+    return out
+
+
+def causal_attention_lse(q, k, q_pos, scale: float, row_block: int = 256) -> np.ndarray:
+    """Natural log of each row's softmax denominator in causal_attention,
+    log sum_{u <= q_pos[t]} exp(scale * <q, k_u>), as [H, n] (reading R11:
+    the row statistic a backward can take from its forward). Evaluated as
+    max + log(sum(exp(s - max))), which is the same number without overflow."""
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    n, H, _ = q.shape
+    group = H // k.shape[1]
+    out = np.empty((H, n), dtype=np.float64)
+    for lo in range(0, n, row_block):
+        hi = min(n, lo + row_block)
+        pos = q_pos[lo:hi]
+        L = int(pos.max()) + 1
+        visible = np.arange(L)[None, :] <= pos[:, None]
+        for hd in range(H):
+            s = np.where(visible, scale * (_f64(q[lo:hi, hd, :]) @ _f64(k[:L, hd // group, :]).T), -np.inf)
+            mx = s.max(axis=1)
+            out[hd, lo:hi] = mx + np.log(np.exp(s - mx[:, None]).sum(axis=1))
     return out
 
 

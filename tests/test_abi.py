@@ -252,6 +252,28 @@ def test_attn_bwd_workspace_and_errors():
     assert call(shape=_shape(dtype="bf16", Dh=32, H=8))[0] == tsp.TSP_ERR_UNSUPPORTED
 
 
+def test_attn_lse_entry_points_errors():
+    sb, sf = _shape(dtype="bf16"), _shape(dtype="f32")
+    q, k, v, o, lse, do = (FAKE + (i << 32) for i in range(6))
+    dq, dk, dv, ws = (FAKE + ((7 + i) << 32) for i in range(4))
+    need = tsp.workspace_size(sb, tsp.TSP_WS_ATTN_BWD)
+    with pytest.raises(tsp.TspError) as ei:  # bf16 inputs only
+        tsp.tsp_zigzag_attn_lse(sf, q, k, v, o, lse, stream=0)
+    assert ei.value.status == tsp.TSP_ERR_UNSUPPORTED
+    with pytest.raises(tsp.TspError) as ei:  # lse over o
+        tsp.tsp_zigzag_attn_lse(sb, q, k, v, o, o + 256, stream=0)
+    assert ei.value.status == tsp.TSP_ERR_INVALID_ARG and b"overlap" in tsp.lib().tsp_last_error()
+    with pytest.raises(tsp.TspError) as ei:  # the statistics are required
+        tsp.tsp_zigzag_attn_bwd_lse(sb, q, k, v, o, None, do, dq, dk, dv, ws, need, stream=0)
+    assert ei.value.status == tsp.TSP_ERR_INVALID_ARG and b"lse is NULL" in tsp.lib().tsp_last_error()
+    with pytest.raises(tsp.TspError) as ei:
+        tsp.tsp_zigzag_attn_bwd_lse(sf, q, k, v, o, lse, do, dq, dk, dv, ws, need, stream=0)
+    assert ei.value.status == tsp.TSP_ERR_UNSUPPORTED
+    with pytest.raises(tsp.TspError) as ei:  # dq over the given o
+        tsp.tsp_zigzag_attn_bwd_lse(sb, q, k, v, o, lse, do, o + 4096, dk, dv, ws, need, stream=0)
+    assert ei.value.status == tsp.TSP_ERR_INVALID_ARG and b"overlap" in tsp.lib().tsp_last_error()
+
+
 def test_layer_errors():
     s = _shape()
     w = dict(g_attn=FAKE, g_mlp=FAKE, wqkv=[FAKE] * 4, wo=[FAKE] * 4, w1=[FAKE] * 4, w2=[FAKE] * 4)

@@ -161,16 +161,24 @@ def test_mlp_ring_bwd_7b(torch):
 
 
 # ---------------------------------------------------------------- attention backward
-def _attn_bwd_run(torch, s, q, k, v, do, dtype):
-    """tsp_zigzag_attn_bwd; returns dq, dk, dv (float64)."""
+def _attn_bwd_run(torch, s, q, k, v, do, dtype, from_fwd=False):
+    """tsp_zigzag_attn_bwd, or (from_fwd) tsp_zigzag_attn_lse followed by
+    tsp_zigzag_attn_bwd_lse; returns dq, dk, dv (float64)."""
     N, H, Dh = q.shape
     S, Hkv = k.shape[0], k.shape[1]
     qd, kd, vd, dod = up(q, dtype), up(k, dtype), up(v, dtype), up(do, dtype)
+    if from_fwd:
+        o = torch.empty((N, H, Dh), dtype=torch.float32, device="cuda")
+        lse = torch.empty((H, N), dtype=torch.float32, device="cuda")
+        tsp.tsp_zigzag_attn_lse(s, qd, kd, vd, o, lse)
     ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_ATTN_BWD), dtype=torch.uint8, device="cuda")
     dq = torch.full((N, H, Dh), float("nan"), dtype=torch.float32, device="cuda")
     dk = torch.full((S, Hkv, Dh), float("nan"), dtype=torch.float32, device="cuda")
     dv = torch.full((S, Hkv, Dh), float("nan"), dtype=torch.float32, device="cuda")
-    tsp.tsp_zigzag_attn_bwd(s, qd, kd, vd, dod, dq, dk, dv, ws)
+    if from_fwd:
+        tsp.tsp_zigzag_attn_bwd_lse(s, qd, kd, vd, o, lse, dod, dq, dk, dv, ws)
+    else:
+        tsp.tsp_zigzag_attn_bwd(s, qd, kd, vd, dod, dq, dk, dv, ws)
     torch.cuda.synchronize()
     return down(dq), down(dk), down(dv)
 
@@ -206,6 +214,36 @@ def test_attn_bwd_every_rank(torch, S, D, H, Hkv, Dh, dtype):
         assert not dk[pos.max() + 1:].any() and not dv[pos.max() + 1:].any()
 
 
+@pytest.mark.parametrize("S,D,H,Hkv,Dh,dtype", [c for c in ATTN_BWD_CASES if c[-1] == "bf16"])
+def test_attn_lse_and_bwd_from_forward_every_rank(torch, S, D, H, Hkv, Dh, dtype):
+    """tsp_zigzag_attn_lse (fp32 O and the row log-sum-exp) and the backward
+    that takes them, on every rank, against the oracle."""
+    shape = synth.LayerShape(S=S, D=D, h=H * Dh, H=H, Dh=Dh, F=64 * D, dtype=dtype, Hkv=Hkv)
+    N = S // D
+    k, v = synth.remote_kv(shape, seed=51)
+    k64, v64 = f64(k, dtype), f64(v, dtype)
+    for r in range(D):
+        q = synth.normal((N, H, Dh), 51, synth.TID_Q, r, dtype=dtype)
+        do = synth.normal((N, H, Dh), 51, synth.TID_DY, r, dtype=dtype)
+        pos = oracle.zigzag_positions(S, D, r)
+        s = tsp.make_shape(S, D, r, H * Dh, H, Dh, 64 * D, dtype=dtype, Hkv=Hkv)
+        log(f"attention with log-sum-exp, then backward from it: S={S} D={D} r={r} H={H} Hkv={Hkv} Dh={Dh}")
+        o = torch.empty((N, H, Dh), dtype=torch.float32, device="cuda")
+        lse = torch.full((H, N), float("nan"), dtype=torch.float32, device="cuda")
+        tsp.tsp_zigzag_attn_lse(s, up(q, dtype), up(k, dtype), up(v, dtype), o, lse)
+        torch.cuda.synchronize()
+        want_lse = oracle.causal_attention_lse(f64(q, dtype), k64, pos, shape.scale)
+        err = float(np.abs(down(lse) - want_lse).max())
+        log(f"  lse: max|err| = {err:.3e}")
+        assert err <= 1e-4 * max(1.0, float(np.abs(want_lse).max()))
+        assert_close(down(o), oracle.causal_attention(f64(q, dtype), k64, v64, pos, shape.scale), TOL_BF16, "o")
+        want = oracle.causal_attention_backward(f64(q, dtype), k64, v64, pos, shape.scale, f64(do, dtype))
+        dq, dk, dv = _attn_bwd_run(torch, s, q, k, v, do, dtype, from_fwd=True)
+        assert_close(dq, want["dq"], TOL_BF16, f"dq r={r}")
+        assert_close(dk, want["dk"], TOL_BF16, f"dk r={r}")
+        assert_close(dv, want["dv"], TOL_BF16, f"dv r={r}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_attn_bwd_rank_contributions_sum(torch, dtype):
     """D emulated ranks over one sequence: each rank's dq rows are the
@@ -233,7 +271,8 @@ def test_attn_bwd_rank_contributions_sum(torch, dtype):
 
 
 @pytest.mark.timeout(900)
-def test_attn_bwd_7b(torch):
+@pytest.mark.parametrize("from_fwd", [False, True])
+def test_attn_bwd_7b(torch, from_fwd):
     """7B attention (32 heads x 128, S = 131072, D = 8), rank 0: dq of the
     first 64 and the last 64 local rows (positions 0.. and 131008..), and dK,
     dV of the last 64 keys, which only those last rows see, against the
@@ -247,8 +286,8 @@ def test_attn_bwd_7b(torch):
     k, v = synth.remote_kv(SH, seed=53)
     do = synth.normal((N, H, Dh), 53, synth.TID_DY, 0, dtype="bf16")
     s = tsp.make_shape(S, SH.D, r, SH.h, H, Dh, SH.F, dtype="bf16")
-    log("attention backward 7B, rank 0")
-    dq, dk, dv = _attn_bwd_run(torch, s, q, k, v, do, "bf16")
+    log(f"attention backward 7B, rank 0, statistics from the forward: {from_fwd}")
+    dq, dk, dv = _attn_bwd_run(torch, s, q, k, v, do, "bf16", from_fwd)
     assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
     pos = oracle.zigzag_positions(S, SH.D, r)
     k64, v64 = f64(k, "bf16"), f64(v, "bf16")

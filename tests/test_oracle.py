@@ -729,6 +729,26 @@ def test_attention_backward_special_cases():
     assert np.allclose(one["dv"][0], do[0], atol=1e-15) and not one["dv"][1:].any()
 
 
+def test_attention_lse_closed_forms_and_scipy():
+    rng = np.random.default_rng(26)
+    S, H, Dh = 11, 2, 3
+    q, k = rng.standard_normal((2, S, H, Dh))
+    # scale 0: every visible score is 0, so the log-sum-exp is log(pos + 1)
+    got0 = oracle.causal_attention_lse(q, k, np.arange(S), 0.0)
+    assert np.allclose(got0, np.log(np.arange(1, S + 1))[None, :], atol=1e-14)
+    # scipy's logsumexp over each visible prefix; large scores do not overflow
+    from scipy.special import logsumexp
+    got = oracle.causal_attention_lse(q, k, np.arange(S), 40.0, row_block=4)
+    for hd in range(H):
+        for t in range(S):
+            want = logsumexp(40.0 * (k[:t + 1, hd] @ q[t, hd]))
+            assert got[hd, t] == pytest.approx(want, abs=1e-11)
+    assert np.isfinite(got).all()
+    # the forward's probabilities are exp(s - lse): each row sums to one
+    p_row = np.exp(0.5 * (k[:6, 1] @ q[5, 1]) - oracle.causal_attention_lse(q, k, np.arange(S), 0.5)[1, 5])
+    assert p_row.sum() == pytest.approx(1.0, abs=1e-14)
+
+
 def test_attention_backward_planted_mistakes_are_caught(monkeypatch):
     """A softmax Jacobian without its row-sum term, or gradients taken with
     an exclusive mask, miss torch's autograd."""

@@ -418,19 +418,49 @@ tsp_status tsp_mlp_ring(const tsp_shape *s, const void *x, const void *const *w1
   return ok();
 }
 
-tsp_status tsp_zigzag_attn_bwd(const tsp_shape *s, const void *q, const void *k, const void *v, const void *dout, float *dq, float *dk, float *dv, void *ws, size_t ws_bytes,
+tsp_status tsp_zigzag_attn_lse(const tsp_shape *s, const void *q, const void *k, const void *v, float *o, float *lse,
                                void *stream_) {
   tsp_status st = check_attn_shape(s);
   if (st) return st;
-  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(dout, "dout")) || (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) ||
-      (st = check_ptr(dv, "dv")) || (st = check_ptr(ws, "ws")))
+  if (s->dtype != TSP_BF16) return fail(TSP_ERR_UNSUPPORTED, "tsp_zigzag_attn_lse takes bf16 inputs");
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(o, "o")) ||
+      (st = check_ptr(lse, "lse")))
     return st;
+  const size_t row = (size_t)s->H * s->Dh, kvrow = (size_t)kv_heads(s) * s->Dh, N = (size_t)(s->S / s->D);
+  const Range outs[] = {{o, N * row * 4, "o"}, {lse, N * s->H * 4, "lse"}};
+  const Range ins[] = {{q, N * row * 2, "q"}, {k, (size_t)s->S * kvrow * 2, "k"}, {v, (size_t)s->S * kvrow * 2, "v"}};
+  for (const Range &ro : outs)
+    for (const Range &ri : ins)
+      if (overlap(ro, ri)) return fail(TSP_ERR_INVALID_ARG, "%s overlaps %s", ro.name, ri.name);
+  if (overlap(outs[0], outs[1])) return fail(TSP_ERR_INVALID_ARG, "o overlaps lse");
+  hipStream_t stream = (hipStream_t)stream_;
+  TSP_LAUNCH(TSP_K_ATTN,
+             tsp::launch_attention(s->dtype, q, k, v, o, TSP_F32, false, s->S, (int32_t)N, s->H, kv_heads(s), s->Dh,
+                                   s->scale, tsp::make_zigzag(s->S, s->D, s->r), false, stream, lse),
+             "attention");
+  return ok();
+}
+
+static tsp_status attn_bwd(const tsp_shape *s, const void *q, const void *k, const void *v, const float *o, const float *lse,
+                    const void *dout, float *dq, float *dk, float *dv, void *ws, size_t ws_bytes, void *stream_) {
+  tsp_status st = check_attn_shape(s);
+  if (st) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(dout, "dout")) ||
+      (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")) ||
+      (st = check_ptr(ws, "ws")))
+    return st;
+  const bool given = o != nullptr || lse != nullptr;
+  if (given) {
+    if ((st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse"))) return st;
+    if (s->dtype != TSP_BF16) return fail(TSP_ERR_UNSUPPORTED, "the forward's statistics are taken with bf16 inputs");
+  }
   const size_t need = attn_bwd_ws(s);
   if (ws_bytes < need) return fail(TSP_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, need);
   const int64_t N = s->S / s->D;
   const size_t e = elem_bytes(s->dtype);
   const size_t qb = (size_t)N * s->H * s->Dh, kb = (size_t)s->S * kv_heads(s) * s->Dh;
-  const Range ins[] = {{q, qb * e, "q"}, {k, kb * e, "k"}, {v, kb * e, "v"}, {dout, qb * e, "dout"}};
+  const Range ins[] = {{q, qb * e, "q"},       {k, kb * e, "k"},   {v, kb * e, "v"},
+                       {dout, qb * e, "dout"}, {o, qb * 4, "o"},   {lse, (size_t)N * s->H * 4, "lse"}};
   const Range outs[] = {{dq, qb * 4, "dq"}, {dk, kb * 4, "dk"}, {dv, kb * 4, "dv"}, {ws, need, "ws"}};
   for (const Range &ro : outs) {
     for (const Range &ri : ins)
@@ -439,12 +469,25 @@ tsp_status tsp_zigzag_attn_bwd(const tsp_shape *s, const void *q, const void *k,
       if (&r2 != &ro && overlap(ro, r2)) return fail(TSP_ERR_INVALID_ARG, "%s overlaps %s", ro.name, r2.name);
   }
   hipStream_t stream = (hipStream_t)stream_;
-  float *lse = (float *)ws, *delta = (float *)((unsigned char *)ws + need / 2);
+  float *lse_ws = (float *)ws, *delta = (float *)((unsigned char *)ws + need / 2);
   TSP_LAUNCH(TSP_K_ATTN_BWD,
-             tsp::launch_attention_bwd(s->dtype, q, k, v, dout, dq, dk, dv, lse, delta, s->S, (int32_t)N, s->H,
-                                       kv_heads(s), s->Dh, s->scale, tsp::make_zigzag(s->S, s->D, s->r), stream),
+             tsp::launch_attention_bwd(s->dtype, q, k, v, dout, dq, dk, dv, lse_ws, delta, s->S, (int32_t)N, s->H,
+                                       kv_heads(s), s->Dh, s->scale, tsp::make_zigzag(s->S, s->D, s->r), stream, o,
+                                       lse),
              "attention backward");
   return ok();
+}
+
+tsp_status tsp_zigzag_attn_bwd(const tsp_shape *s, const void *q, const void *k, const void *v, const void *dout,
+                               float *dq, float *dk, float *dv, void *ws, size_t ws_bytes, void *stream) {
+  return attn_bwd(s, q, k, v, nullptr, nullptr, dout, dq, dk, dv, ws, ws_bytes, stream);
+}
+
+tsp_status tsp_zigzag_attn_bwd_lse(const tsp_shape *s, const void *q, const void *k, const void *v, const float *o,
+                                   const float *lse, const void *dout, float *dq, float *dk, float *dv, void *ws,
+                                   size_t ws_bytes, void *stream) {
+  if (!o || !lse) return fail(TSP_ERR_INVALID_ARG, "%s is NULL", o ? "lse" : "o");
+  return attn_bwd(s, q, k, v, o, lse, dout, dq, dk, dv, ws, ws_bytes, stream);
 }
 
 tsp_status tsp_mlp_ring_bwd(const tsp_shape *s, const void *x, const void *const *w1, const void *const *w2,

@@ -58,6 +58,7 @@ struct AttnArgs {
   ZigzagMap zz;
   int32_t T;         // query tiles per chunk
   int64_t o_panel;   // bf16 O: panel stride (64-column panels) or 0 for [n][H][Dh]
+  float *lse;        // [H][n] natural log-sum-exp of each row's scaled scores (LSE variant only)
 };
 
 constexpr int kBQ = 128, kBKey = 64, kAttnThreads = 256;
@@ -340,7 +341,7 @@ __device__ __forceinline__ void attn_walk(const KvCopy<DH> &cp, unsigned char (*
 }
 #endif  // __HIP_DEVICE_COMPILE__
 
-template <int DH, bool OUT_F32, bool QPRE>
+template <int DH, bool OUT_F32, bool QPRE, bool LSE = false>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using G = KvTile<DH>;
@@ -438,7 +439,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
     // head*DH/64 + db/2 at column 32*(db%2) + 8*vq + 4*g, so every store is a
     // constant offset from one base pointer per lane (a per-column address
     // would be hoisted out of the key walk and spilled).
-    const float inv = 1.0f / halves_sum(l_part);
+    const float lsum = halves_sum(l_part);
+    const float inv = 1.0f / lsum;
+    if constexpr (LSE) {
+      // l sums exp2 of the scores (times c unless Q came pre-multiplied) minus
+      // the reference max m, which is in the same units as the accumulators
+      if (my_valid && g == 0)
+        a.lse[(int64_t)head * a.n + qrow] = 0.69314718055994531f * ((QPRE ? m_run : m_run * a.c) + __log2f(lsum));
+    }
     if (my_valid) {
 #pragma unroll
       for (int db = 0; db < ND; ++db)
@@ -520,11 +528,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 
 hipError_t launch_attention(int dtype, const void *q, const void *k, const void *v, void *o, int o_dtype,
                             bool o_panel, int64_t S, int32_t n, int32_t H, int32_t Hkv, int32_t Dh, float scale,
-                            ZigzagMap zz, bool q_prescaled, hipStream_t s) {
+                            ZigzagMap zz, bool q_prescaled, hipStream_t s, float *lse) {
   if (n <= 0) return hipSuccess;
   if (Hkv < 1 || H % Hkv != 0) return hipErrorInvalidValue;
   if (o_panel && (dtype != TSP_BF16 || o_dtype != TSP_BF16)) return hipErrorInvalidValue;
   if (q_prescaled && (dtype != TSP_BF16 || o_dtype != TSP_BF16)) return hipErrorInvalidValue;
+  if (lse && (dtype != TSP_BF16 || o_dtype != TSP_F32 || q_prescaled)) return hipErrorInvalidValue;
   AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -543,10 +552,16 @@ hipError_t launch_attention(int dtype, const void *q, const void *k, const void 
   a.zz = zz;
   a.T = (zz.C + kBQ - 1) / kBQ;
   a.o_panel = o_panel ? (int64_t)n * kPanel : 0;
+  a.lse = lse;
   if (dtype == TSP_BF16) {
     dim3 grid(H * a.T);
     const bool f32out = o_dtype == TSP_F32;
-    if (Dh == 128) {
+    if (lse) {
+      if (Dh == 128)
+        hipLaunchKernelGGL((attn_bf16_kernel<128, true, false, true>), grid, dim3(kAttnThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_bf16_kernel<64, true, false, true>), grid, dim3(kAttnThreads), 0, s, a);
+    } else if (Dh == 128) {
       if (f32out)
         hipLaunchKernelGGL((attn_bf16_kernel<128, true, false>), grid, dim3(kAttnThreads), 0, s, a);
       else if (q_prescaled)

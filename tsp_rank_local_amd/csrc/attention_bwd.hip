@@ -42,6 +42,7 @@ namespace tsp {
 
 struct BwdArgs {
   const void *q, *k, *v, *dout;
+  const float *o_f32, *lse_in;  // the forward's fp32 O and natural log-sum-exp, or null
   float *dq, *dk, *dv;
   float *lse;    // [H][n]: log2 of each row's softmax denominator (scores in the log2 domain)
   float *delta;  // [H][n]: sum over the row's keys of P dP
@@ -167,7 +168,30 @@ __device__ __forceinline__ void put_split2(bf16x8 &hi, bf16x8 &lo, int e, float 
   lo[e + 1] = l[1];
 }
 
-template <int DH>
+// Row statistics from the forward: Delta = sum over features of dO * O
+// (fp32 O) and the log-sum-exp in the log2 domain, one thread per (row,
+// head), head fastest.
+__global__ __launch_bounds__(256) void attn_bwd_stats_kernel(BwdArgs a, int DH) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.n * a.H) return;
+  const int64_t row = i / a.H;
+  const int head = (int)(i - row * a.H);
+  const float4 *o = reinterpret_cast<const float4 *>(a.o_f32 + i * DH);
+  const bf16 *d = reinterpret_cast<const bf16 *>(a.dout) + i * DH;
+  float acc = 0.f;
+  for (int e = 0; e < DH / 4; ++e) {
+    const float4 ov = o[e];
+    acc = fmaf(ov.x, (float)d[4 * e], acc);
+    acc = fmaf(ov.y, (float)d[4 * e + 1], acc);
+    acc = fmaf(ov.z, (float)d[4 * e + 2], acc);
+    acc = fmaf(ov.w, (float)d[4 * e + 3], acc);
+  }
+  const int64_t at = (int64_t)head * a.n + row;
+  a.delta[at] = acc;
+  a.lse[at] = a.lse_in[at] * 1.4426950408889634f;
+}
+
+template <int DH, bool GIVEN>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using G = BTile<DH>;
@@ -234,54 +258,60 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
       }
   };
 
-  // ---- walk 1: row max, sum and Delta (log2 domain)
-  float m = -INFINITY, l = 0.f, dsum = 0.f;
   TileRegs<DH, kBwdKey> kr, vr;
-  load_tile<DH, kBwdKey>(kr, kg, kvs, 0, a.S);
-  load_tile<DH, kBwdKey>(vr, vg, kvs, 0, a.S);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int k0 = kt * kBwdKey;
-    __syncthreads();
-    store_tile<DH, kBwdKey, false>(smem[0], kr);
-    store_tile<DH, kBwdKey, false>(smem[2], vr);
-    __syncthreads();
-    if (kt + 1 < n_kt) {  // next tile on its way during this one's math
-      load_tile<DH, kBwdKey>(kr, kg, kvs, k0 + kBwdKey, a.S);
-      load_tile<DH, kBwdKey>(vr, vg, kvs, k0 + kBwdKey, a.S);
-    }
-    if (!active) continue;
-    f32x16 sacc[2], pacc[2];
-    scores(smem[0], qf, sacc);
-    scores(smem[2], df, pacc);
-    mask(sacc, k0);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-    mx = halves_max(mx) * a.c;
-    const float m_new = fmaxf(m, mx);  // finite from the first tile on (key 0 is visible)
-    float part = 0.f, dpart = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v], a.c, -m_new));
-        part += e;
-        dpart = fmaf(e, pacc[kb][v], dpart);
+  float lse, dlt;
+  if constexpr (GIVEN) {  // statistics from the forward (attn_bwd_stats_kernel)
+    lse = my_valid ? a.lse[(int64_t)head * a.n + qrow] : 0.f;
+    dlt = my_valid ? a.delta[(int64_t)head * a.n + qrow] : 0.f;
+  } else {
+    // ---- walk 1: row max, sum and Delta (log2 domain)
+    float m = -INFINITY, l = 0.f, dsum = 0.f;
+    load_tile<DH, kBwdKey>(kr, kg, kvs, 0, a.S);
+    load_tile<DH, kBwdKey>(vr, vg, kvs, 0, a.S);
+    for (int kt = 0; kt < n_kt; ++kt) {
+      const int k0 = kt * kBwdKey;
+      __syncthreads();
+      store_tile<DH, kBwdKey, false>(smem[0], kr);
+      store_tile<DH, kBwdKey, false>(smem[2], vr);
+      __syncthreads();
+      if (kt + 1 < n_kt) {  // next tile on its way during this one's math
+        load_tile<DH, kBwdKey>(kr, kg, kvs, k0 + kBwdKey, a.S);
+        load_tile<DH, kBwdKey>(vr, vg, kvs, k0 + kBwdKey, a.S);
       }
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    l = l * alpha + part;
-    dsum = dsum * alpha + dpart;
-    m = m_new;
-  }
-  l = halves_sum(l);
-  dsum = halves_sum(dsum);
-  const float lse = m + __log2f(l);
-  const float dlt = dsum / l;
-  if (my_valid && g == 0) {
-    a.lse[(int64_t)head * a.n + qrow] = lse;
-    a.delta[(int64_t)head * a.n + qrow] = dlt;
+      if (!active) continue;
+      f32x16 sacc[2], pacc[2];
+      scores(smem[0], qf, sacc);
+      scores(smem[2], df, pacc);
+      mask(sacc, k0);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
+      mx = halves_max(mx) * a.c;
+      const float m_new = fmaxf(m, mx);  // finite from the first tile on (key 0 is visible)
+      float part = 0.f, dpart = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v], a.c, -m_new));
+          part += e;
+          dpart = fmaf(e, pacc[kb][v], dpart);
+        }
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      l = l * alpha + part;
+      dsum = dsum * alpha + dpart;
+      m = m_new;
+    }
+    l = halves_sum(l);
+    dsum = halves_sum(dsum);
+    lse = m + __log2f(l);
+    dlt = dsum / l;
+    if (my_valid && g == 0) {
+      a.lse[(int64_t)head * a.n + qrow] = lse;
+      a.delta[(int64_t)head * a.n + qrow] = dlt;
+    }
   }
 
   // ---- walk 2: dQ^T += K^T dS^T
@@ -597,16 +627,21 @@ __global__ __launch_bounds__(64) void attn_bwd_dkv_f32_kernel(BwdArgs a) {
   }
 }
 
-hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout, float *dq, float *dk, float *dv, float *lse, float *delta, int64_t S,
-                                int32_t n, int32_t H, int32_t Hkv, int32_t Dh, float scale, ZigzagMap zz,
-                                hipStream_t s) {
+hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout, float *dq,
+                                float *dk, float *dv, float *lse, float *delta, int64_t S, int32_t n, int32_t H,
+                                int32_t Hkv, int32_t Dh, float scale, ZigzagMap zz, hipStream_t s,
+                                const float *o_f32, const float *lse_in) {
   if (n <= 0) return hipSuccess;
   if (Hkv < 1 || H % Hkv != 0 || (Dh != 64 && Dh != 128)) return hipErrorInvalidValue;
+  const bool given = o_f32 != nullptr && lse_in != nullptr;
+  if (given && dtype != TSP_BF16) return hipErrorInvalidValue;
   BwdArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
   a.dout = dout;
+  a.o_f32 = o_f32;
+  a.lse_in = lse_in;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -626,13 +661,23 @@ hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const v
   a.Tk = (int32_t)((S + 127) / 128);
   if (dtype == TSP_BF16) {
     const dim3 qgrid(H * 2 * a.Tq), kgrid(Hkv * a.Tk);
-    if (Dh == 128) {
-      hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, qgrid, dim3(256), 0, s, a);
-      hipLaunchKernelGGL(attn_bwd_dkv_kernel<128>, kgrid, dim3(256), 0, s, a);
+    if (given) {  // statistics from the forward, then dQ without its first walk
+      const int64_t rows = (int64_t)n * H;
+      hipLaunchKernelGGL(attn_bwd_stats_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a, (int)Dh);
+      if (Dh == 128)
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<128, true>), qgrid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<64, true>), qgrid, dim3(256), 0, s, a);
     } else {
-      hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, qgrid, dim3(256), 0, s, a);
-      hipLaunchKernelGGL(attn_bwd_dkv_kernel<64>, kgrid, dim3(256), 0, s, a);
+      if (Dh == 128)
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<128, false>), qgrid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<64, false>), qgrid, dim3(256), 0, s, a);
     }
+    if (Dh == 128)
+      hipLaunchKernelGGL(attn_bwd_dkv_kernel<128>, kgrid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(attn_bwd_dkv_kernel<64>, kgrid, dim3(256), 0, s, a);
   } else {
     const dim3 qgrid((n + 63) / 64, H), kgrid((unsigned)((S + 63) / 64), Hkv);
     if (Dh == 128) {

@@ -140,9 +140,11 @@ hipError_t launch_lead_mlp_down(const float *hid, int32_t m, const PtrList &w2, 
 // panel layout of [n][H*Dh] when o_panel. q_prescaled (bf16 q and o only): q
 // already holds q * scale * log2(e), as launch_qkv writes it with that
 // q_scale.
+// lse (bf16 inputs, fp32 o, plain q only; else null): also write each row's
+// natural log-sum-exp of its scaled scores, [H][n] fp32.
 hipError_t launch_attention(int dtype, const void *q, const void *k, const void *v, void *o, int o_dtype,
                             bool o_panel, int64_t S, int32_t n, int32_t H, int32_t Hkv, int32_t Dh, float scale,
-                            ZigzagMap zz, bool q_prescaled, hipStream_t s);
+                            ZigzagMap zz, bool q_prescaled, hipStream_t s, float *lse = nullptr);
 // fp32 attention of the first m <= 64 positions among themselves (the
 // leading rows of rank 0): q, o [m][H][Dh], k, v [m][Hkv][Dh] fp32, key j
 // visible to query i when j <= i.
@@ -154,9 +156,13 @@ hipError_t launch_lead_attention(const float *q, const float *k, const float *v,
 // rank's contributions dk, dv [S][Hkv][Dh] in fp32 (every row written). lse,
 // delta: scratch [H][n] fp32 each (log2-domain log-sum-exp of each row, and
 // sum over its keys of P dP).
-hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout, float *dq, float *dk, float *dv, float *lse, float *delta, int64_t S,
-                                int32_t n, int32_t H, int32_t Hkv, int32_t Dh, float scale, ZigzagMap zz,
-                                hipStream_t s);
+// With o_f32 and lse_in given (bf16 inputs; the forward's fp32 output and
+// natural log-sum-exp [H][n] of launch_attention), Delta is the row sum of
+// dout * o and the statistics walk of the dQ kernel is skipped.
+hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout, float *dq,
+                                float *dk, float *dv, float *lse, float *delta, int64_t S, int32_t n, int32_t H,
+                                int32_t Hkv, int32_t Dh, float scale, ZigzagMap zz, hipStream_t s,
+                                const float *o_f32 = nullptr, const float *lse_in = nullptr);
 
 // ---------------------------------------------------------------- timing
 // Bracket a launch with events when profiling is on (api.cpp).
