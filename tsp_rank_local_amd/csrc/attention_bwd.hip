@@ -18,9 +18,12 @@
 //  2. dK and dV, key-major: block = 4 waves x 32 keys of one K/V head. It walks
 //     the rank's query rows that can see its keys, 32 at a time, over every
 //     query head that reads the K/V head: S = Q K^T and dP = dO V^T with the
-//     keys on the lanes, P and dS from the row statistics of launch 2, then
+//     keys on the lanes, P and dS from the row statistics of launch 1, then
 //     dV^T += dO^T P and dK^T += Q^T dS, whose dO^T and Q^T operands are
 //     transpose reads of the query tiles.
+// When the forward's fp32 O and log-sum-exp are given, a small kernel forms
+// Delta = rowsum(dO * O) and the log2-domain statistics instead, and the dQ
+// kernel skips its first walk.
 // The operands of the second products are the score registers themselves,
 // rounded to bf16, in the order the MFMA takes them; the transpose reads hand
 // each lane 4 consecutive rows of one feature in that order. Every product
@@ -50,8 +53,8 @@ struct BwdArgs {
   int32_t n, H, Hkv, grp;
   float scale, c;  // c = scale * log2(e) (at least the smallest normal float)
   ZigzagMap zz;
-  int32_t Tq;  // 128-row query tiles per chunk (launch 1)
-  int32_t Tk;  // 128-key tiles over the sequence (launch 2)
+  int32_t Tq;  // 128-row query tiles per chunk (dQ kernel)
+  int32_t Tk;  // 128-key tiles over the sequence (dK/dV kernel)
 };
 
 typedef short s16x4_b __attribute__((ext_vector_type(4)));
