@@ -308,7 +308,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["layer", "mlp", "attn", "layers32", "mlp_bwd", "attn_bwd", "attn_bwd_lse"], default="layer")
+    ap.add_argument("--workload", choices=["layer", "mlp", "attn", "layers32", "mlp_bwd", "mlp_bwd_z", "attn_bwd", "attn_bwd_lse"], default="layer")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--rope-base", type=float, default=0.0,
                     help="rotary embedding base for the layer workloads (0 = none, the pages' model)")
@@ -357,7 +357,7 @@ def main():
     stream = torch.cuda.current_stream()
     flops = layer_flops(sh, r)
 
-    if args.workload in ("layer", "mlp", "mlp_bwd"):
+    if args.workload in ("layer", "mlp", "mlp_bwd", "mlp_bwd_z"):
         w = synth.layer_weights(sh, seed=seed)
         wd = {k: ([tsp.to_device(a, "bf16") for a in v] if isinstance(v, list) else tsp.to_device(v, "bf16"))
               for k, v in w.items()}
@@ -387,7 +387,7 @@ def main():
         step_exps = 0
         workload = (f"tsp_mlp_ring: 7B MLP ring ({mlp_note}), 16384x4096 bf16 local X, D=8 shards of "
                     f"{2 if sh.mlp == 'swiglu' else 1}x2048x4096 and 4096x2048")
-    elif args.workload == "mlp_bwd":
+    elif args.workload in ("mlp_bwd", "mlp_bwd_z"):
         x = synth.activations(N, sh.h, seed=2, dtype="bf16")
         dy = synth.activations(N, sh.h, seed=2, tid=synth.TID_DY, dtype="bf16")
         xd, dyd = tsp.to_device(x, "bf16"), tsp.to_device(dy, "bf16")
@@ -397,14 +397,24 @@ def main():
         dw2 = [torch.empty((sh.h, fd), dtype=torch.float32, device="cuda") for _ in range(sh.D)]
         ws = torch.empty(tsp.workspace_size(shape, tsp.TSP_WS_MLP_BWD), dtype=torch.uint8, device="cuda")
 
-        def step():
-            tsp.tsp_mlp_ring_bwd(shape, xd, wd["w1"], wd["w2"], dyd, None, dx, dw1, dw2, ws)
+        if args.workload == "mlp_bwd_z":
+            # the forward's pre-activation, made once before timing
+            z_f = torch.empty((N, sh.F), dtype=torch.bfloat16, device="cuda")
+            ws_f = torch.empty(tsp.workspace_size(shape, tsp.TSP_WS_MLP), dtype=torch.uint8, device="cuda")
+            tsp.tsp_mlp_ring_z(shape, xd, wd["w1"], wd["w2"], None, dx, z_f, ws_f)
+
+            def step():
+                tsp.tsp_mlp_ring_bwd_z(shape, xd, z_f, wd["w1"], wd["w2"], dyd, None, dx, dw1, dw2, ws)
+        else:
+            def step():
+                tsp.tsp_mlp_ring_bwd(shape, xd, wd["w1"], wd["w2"], dyd, None, dx, dw1, dw2, ws)
         # algorithmic: the four products of the chain rule (dy W2, dZ W1, dZ^T x,
         # dy^T GELU(Z)); the recomputation of Z = x W1^T is extra work, not counted
         step_flops = 4 * 2.0 * N * sh.h * sh.F
         step_exps = 0
-        workload = ("tsp_mlp_ring_bwd: backward of the 7B MLP ring (FFN), 16384x4096 bf16 local x and dy, D=8 shards "
-                    "of 2048x4096 and 4096x2048; dx, dW1, dW2 in fp32 (Z recomputed)")
+        workload = (f"{'tsp_mlp_ring_bwd_z' if args.workload == 'mlp_bwd_z' else 'tsp_mlp_ring_bwd'}: backward of the "
+                    "7B MLP ring (FFN), 16384x4096 bf16 local x and dy, D=8 shards of 2048x4096 and 4096x2048; dx, dW1, "
+                    "dW2 in fp32 " + ("(Z from the forward)" if args.workload == "mlp_bwd_z" else "(Z recomputed)"))
     elif args.workload in ("attn_bwd", "attn_bwd_lse"):
         q = synth.attn_queries(sh, seed=3)
         k_rem, v_rem = synth.remote_kv(sh, seed=3)
@@ -558,7 +568,7 @@ def main():
         roofline = {"kernel": "attn_bwd_dq_kernel + attn_bwd_dkv_kernel<128>", "bound": "mfma", "achieved": achieved,
                     "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_BF16, "traffic": None}
     elif "bwd_gemm" in kernels:
-        # five launches of one product size each (Z recomputation, dZ, dW1, dW2, dx)
+        # launches of one product size each (Z recomputation unless Z is given, dZ, dW1, dW2, dx)
         t_g = kernels["bwd_gemm"]["ms_per_launch"] * 1e-3
         achieved = 2.0 * N * sh.h * sh.F / t_g / 1e12
         roofline = {"kernel": "gemm_bf16_kernel (MLP backward products)", "bound": "mfma", "achieved": achieved,

@@ -285,6 +285,23 @@ tsp_status tsp_mlp_ring_bwd(const tsp_shape *shape, const void *x, const void *c
                             float *dx, float *const *dw1, float *const *dw2, void *ws,
                             size_t ws_bytes, void *stream);
 
+/* tsp_mlp_ring that also keeps the pre-activation for the backward (bf16,
+ * GELU MLP only, else TSP_ERR_UNSUPPORTED): z [S/D][F] bf16 receives
+ * Z = x W1_j^T of every ring step t in columns t*F/D.., rounded once from the
+ * fp32 product; z must not overlap x, y, residual or ws. */
+tsp_status tsp_mlp_ring_z(const tsp_shape *shape, const void *x, const void *const *w1,
+                          const void *const *w2, const float *residual, float *y, void *z, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* tsp_mlp_ring_bwd with the pre-activation given (bf16 only): z is the z of
+ * tsp_mlp_ring_z for the same shape (same r, so the same column order) and
+ * x. Z is then not recomputed; GELU(Z) for dW2 is taken from the bf16 Z.
+ * Everything else is as in tsp_mlp_ring_bwd (same workspace). */
+tsp_status tsp_mlp_ring_bwd_z(const tsp_shape *shape, const void *x, const void *z,
+                              const void *const *w1, const void *const *w2, const void *dy,
+                              const float *dx_residual, float *dx, float *const *dw1,
+                              float *const *dw2, void *ws, size_t ws_bytes, void *stream);
+
 /* One decoder layer forward on rank r's S/D tokens.
  *  x: [S/D][h] fp32, local rows in zigzag order.
  *  k_full, v_full: [S][Hkv][Dh] (dtype). The rows at rank r's own positions are

@@ -274,6 +274,30 @@ def test_attn_lse_entry_points_errors():
     assert ei.value.status == tsp.TSP_ERR_INVALID_ARG and b"overlap" in tsp.lib().tsp_last_error()
 
 
+def test_mlp_z_entry_points_errors():
+    sb, sf = _shape(dtype="bf16"), _shape(dtype="f32")
+    w = [FAKE + (i << 24) for i in range(4)]
+    g = [FAKE + (1 << 36) + (i << 24) for i in range(4)]
+    x, y, z, ws, dy, dx = (FAKE + (i << 32) for i in range(1, 7))
+    need = tsp.workspace_size(sb, tsp.TSP_WS_MLP)
+    with pytest.raises(tsp.TspError) as ei:  # bf16 only
+        tsp.tsp_mlp_ring_z(sf, x, w, w, None, y, z, ws, need, stream=0)
+    assert ei.value.status == tsp.TSP_ERR_UNSUPPORTED
+    with pytest.raises(tsp.TspError) as ei:  # z over y
+        tsp.tsp_mlp_ring_z(sb, x, w, w, None, y, y + 256, ws, need, stream=0)
+    assert ei.value.status == tsp.TSP_ERR_INVALID_ARG and b"z overlaps" in tsp.lib().tsp_last_error()
+    with pytest.raises(tsp.TspError) as ei:
+        tsp.tsp_mlp_ring_z(sb, x, w, w, None, y, None, ws, need, stream=0)
+    assert ei.value.status == tsp.TSP_ERR_INVALID_ARG and b"z is NULL" in tsp.lib().tsp_last_error()
+    nb = tsp.workspace_size(sb, tsp.TSP_WS_MLP_BWD)
+    with pytest.raises(tsp.TspError) as ei:
+        tsp.tsp_mlp_ring_bwd_z(sf, x, z, w, w, dy, None, dx, g, g, ws, nb, stream=0)
+    assert ei.value.status == tsp.TSP_ERR_UNSUPPORTED
+    with pytest.raises(tsp.TspError) as ei:  # z inside the workspace
+        tsp.tsp_mlp_ring_bwd_z(sb, x, ws + 1024, w, w, dy, None, dx, g, g, ws, nb, stream=0)
+    assert ei.value.status == tsp.TSP_ERR_INVALID_ARG and b"z overlaps" in tsp.lib().tsp_last_error()
+
+
 def test_layer_errors():
     s = _shape()
     w = dict(g_attn=FAKE, g_mlp=FAKE, wqkv=[FAKE] * 4, wo=[FAKE] * 4, w1=[FAKE] * 4, w2=[FAKE] * 4)

@@ -73,6 +73,42 @@ def test_mlp_ring_bwd_every_rank(torch, S, D, h, F, dtype):
         _check(_run(torch, s, up(x, dtype), w1d, w2d, up(dy, dtype)), want, tol, f"r={r}")
 
 
+@pytest.mark.parametrize("S,D,h,F", [(2048, 4, 256, 1024), (640, 2, 320, 384), (128, 1, 64, 64)])
+def test_mlp_ring_z_and_bwd_from_forward(torch, S, D, h, F):
+    """tsp_mlp_ring_z (y and the pre-activation Z in ring-step columns) and
+    tsp_mlp_ring_bwd_z taking that Z, every rank, bf16, against the oracle."""
+    shape = synth.LayerShape(S=S, D=D, h=h, H=h // 64, Dh=64, F=F, dtype="bf16")
+    N, fd = S // D, F // D
+    w = synth.layer_weights(shape, seed=46)
+    x = synth.activations(N, h, seed=46, dtype="bf16")
+    dy = synth.activations(N, h, seed=46, tid=synth.TID_DY, dtype="bf16")
+    w1_64, w2_64 = [f64(a, "bf16") for a in w["w1"]], [f64(a, "bf16") for a in w["w2"]]
+    x64 = f64(x, "bf16")
+    want_y = oracle.mlp(x64, w1_64, w2_64)
+    want = oracle.mlp_backward(x64, w1_64, w2_64, f64(dy, "bf16"))
+    xd, dyd = up(x, "bf16"), up(dy, "bf16")
+    w1d, w2d = [up(a, "bf16") for a in w["w1"]], [up(a, "bf16") for a in w["w2"]]
+    for r in range(D):
+        s = tsp.make_shape(S, D, r, h, h // 64, 64, F, dtype="bf16")
+        log(f"mlp ring with Z, then backward from it: S={S} D={D} r={r} h={h} F={F}")
+        ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_MLP), dtype=torch.uint8, device="cuda")
+        y = torch.empty((N, h), dtype=torch.float32, device="cuda")
+        z = torch.empty((N, F), dtype=torch.bfloat16, device="cuda")
+        tsp.tsp_mlp_ring_z(s, xd, w1d, w2d, None, y, z, ws)
+        torch.cuda.synchronize()
+        assert_close(down(y), want_y, TOL_BF16, f"y r={r}")
+        # ring step t holds shard (r - t) mod D in columns t*fd..
+        want_z = np.concatenate([x64 @ w1_64[(r - t) % D].T for t in range(D)], axis=1)
+        assert_close(down(z), want_z, TOL_BF16, f"Z r={r}")
+        wsb = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_MLP_BWD), dtype=torch.uint8, device="cuda")
+        dx = torch.full((N, h), float("nan"), dtype=torch.float32, device="cuda")
+        dw1 = [torch.full((fd, h), float("nan"), dtype=torch.float32, device="cuda") for _ in range(D)]
+        dw2 = [torch.full((h, fd), float("nan"), dtype=torch.float32, device="cuda") for _ in range(D)]
+        tsp.tsp_mlp_ring_bwd_z(s, xd, z, w1d, w2d, dyd, None, dx, dw1, dw2, wsb)
+        torch.cuda.synchronize()
+        _check((down(dx), [down(a) for a in dw1], [down(a) for a in dw2]), want, TOL_BF16, f"from Z, r={r}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_mlp_ring_bwd_residual_in_place(torch, dtype):
     S, D, h, F = 1024, 4, 256, 1024

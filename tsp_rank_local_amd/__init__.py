@@ -19,7 +19,7 @@ __all__ = [
     "TspError", "TspShape", "TspLayerWeights", "lib", "make_shape", "workspace_size",
     "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_zigzag_attn_ex", "tsp_mlp_ring",
     "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_zigzag_attn_lse", "tsp_zigzag_attn_bwd_lse", "tsp_layer_fwd",
-    "profile_enable", "profile_reset", "profile_read",
+    "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z", "profile_enable", "profile_reset", "profile_read",
     "TSP_F32", "TSP_BF16", "TSP_ATTN_Q_LOG2_SCALED", "TSP_PHASE_KV", "TSP_PHASE_REST", "TSP_PHASE_ALL",
     "TSP_WS_MLP", "TSP_WS_LAYER", "TSP_WS_MLP_BWD", "TSP_WS_ATTN_BWD", "TSP_MLP_GELU", "TSP_MLP_SWIGLU", "MLP_KINDS",
     "KERNEL_CLASSES", "EXPORTED_SYMBOLS",
@@ -43,7 +43,7 @@ EXPORTED_SYMBOLS = [
     "tsp_status_string", "tsp_last_error", "tsp_abi_version", "tsp_workspace_size",
     "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_zigzag_attn_ex", "tsp_mlp_ring",
     "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_zigzag_attn_lse", "tsp_zigzag_attn_bwd_lse", "tsp_layer_fwd",
-    "tsp_profile_enable", "tsp_profile_reset", "tsp_profile_read",
+    "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z", "tsp_profile_enable", "tsp_profile_reset", "tsp_profile_read",
 ]
 
 
@@ -94,6 +94,9 @@ def lib() -> ctypes.CDLL:
                                    ctypes.POINTER(vp), vp, sz, vp]
     L.tsp_zigzag_attn_bwd.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.tsp_zigzag_attn_lse.argtypes = [shp, vp, vp, vp, vp, vp, vp]
+    L.tsp_mlp_ring_z.argtypes = [shp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp, sz, vp]
+    L.tsp_mlp_ring_bwd_z.argtypes = [shp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp,
+                                     ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp]
     L.tsp_zigzag_attn_bwd_lse.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.tsp_layer_fwd.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, ctypes.c_uint, vp, sz, vp]
     L.tsp_profile_enable.argtypes = [ctypes.c_int]
@@ -103,7 +106,8 @@ def lib() -> ctypes.CDLL:
     L.tsp_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     for name in ("tsp_workspace_size", "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn",
                  "tsp_zigzag_attn_ex", "tsp_mlp_ring", "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_layer_fwd",
-                 "tsp_zigzag_attn_lse", "tsp_zigzag_attn_bwd_lse", "tsp_profile_read"):
+                 "tsp_zigzag_attn_lse", "tsp_zigzag_attn_bwd_lse", "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z",
+                 "tsp_profile_read"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -190,6 +194,22 @@ def tsp_zigzag_attn_bwd(shape: TspShape, q, k, v, dout, dq, dk, dv, ws, ws_bytes
         ws_bytes = ws.numel() * ws.element_size()
     _check(lib().tsp_zigzag_attn_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq),
                                      _ptr(dk), _ptr(dv), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def tsp_mlp_ring_z(shape: TspShape, x, w1, w2, residual, y, z, ws, ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().tsp_mlp_ring_z(ctypes.byref(shape), _ptr(x), _ptr_array(w1), _ptr_array(w2), _ptr(residual), _ptr(y),
+                                _ptr(z), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def tsp_mlp_ring_bwd_z(shape: TspShape, x, z, w1, w2, dy, dx_residual, dx, dw1, dw2, ws, ws_bytes=None,
+                       stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().tsp_mlp_ring_bwd_z(ctypes.byref(shape), _ptr(x), _ptr(z), _ptr_array(w1), _ptr_array(w2), _ptr(dy),
+                                    _ptr(dx_residual), _ptr(dx), _ptr_array(dw1), _ptr_array(dw2), _ptr(ws),
+                                    int(ws_bytes), _stream(stream)))
 
 
 def tsp_zigzag_attn_lse(shape: TspShape, q, k, v, o, lse, stream=None) -> None:

@@ -389,12 +389,17 @@ tsp_status tsp_zigzag_attn_ex(const tsp_shape *s, const void *q, const void *k, 
   return ok();
 }
 
-tsp_status tsp_mlp_ring(const tsp_shape *s, const void *x, const void *const *w1, const void *const *w2,
-                        const float *residual, float *y, void *ws, size_t ws_bytes, void *stream_) {
+static tsp_status mlp_ring(const tsp_shape *s, const void *x, const void *const *w1, const void *const *w2,
+                           const float *residual, float *y, void *z, void *ws, size_t ws_bytes, void *stream_) {
   tsp_status st = check_mlp_shape(s);
   if (st) return st;
   if ((st = check_ptr(x, "x")) || (st = check_ptr(y, "y")) || (st = check_ptr(ws, "ws"))) return st;
   if (residual && !aligned16(residual)) return fail(TSP_ERR_INVALID_ARG, "residual is not 16-byte aligned");
+  if (z) {
+    if ((st = check_ptr(z, "z"))) return st;
+    if (s->dtype != TSP_BF16 || s->mlp != TSP_MLP_GELU)
+      return fail(TSP_ERR_UNSUPPORTED, "the pre-activation output covers the bf16 GELU MLP only");
+  }
   if ((st = check_ptr_list(w1, s->D, "w1")) || (st = check_ptr_list(w2, s->D, "w2"))) return st;
   const size_t need = mlp_ws(s);
   if (ws_bytes < need) return fail(TSP_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, need);
@@ -404,13 +409,17 @@ tsp_status tsp_mlp_ring(const tsp_shape *s, const void *x, const void *const *w1
     return fail(TSP_ERR_INVALID_ARG, "x, y and ws must not overlap");
   if (residual && residual != y && overlap(Range{residual, (size_t)N * h * 4, "residual"}, ry))
     return fail(TSP_ERR_INVALID_ARG, "residual overlaps y without being equal to it");
+  const Range rz{z, (size_t)N * s->F * 2, "z"};
+  if (overlap(rz, rx) || overlap(rz, ry) || overlap(rz, rw) ||
+      (residual && overlap(rz, Range{residual, (size_t)N * h * 4, "residual"})))
+    return fail(TSP_ERR_INVALID_ARG, "z overlaps x, y, residual or ws");
   hipStream_t stream = (hipStream_t)stream_;
   // every ring step's GELU(x W1_j^T) side by side (bf16: in 64-column
   // panels), then one reduction over them and the W2 shards in ring order
   const bool pnl = s->dtype == TSP_BF16;
   TSP_LAUNCH(TSP_K_MLP_UP,
              tsp::launch_mlp_up(s->dtype, x, false, N, h, ring_list(w1, s->D, s->r), s->D, fd, s->mlp == TSP_MLP_SWIGLU,
-                                ws, pnl, stream),
+                                ws, pnl, stream, z),
              "MLP up");
   TSP_LAUNCH(TSP_K_MLP_DOWN,
              tsp::launch_mlp_down(s->dtype, ws, pnl, N, ring_list(w2, s->D, s->r), s->D, fd, h, residual, y, stream),
@@ -490,15 +499,19 @@ tsp_status tsp_zigzag_attn_bwd_lse(const tsp_shape *s, const void *q, const void
   return attn_bwd(s, q, k, v, o, lse, dout, dq, dk, dv, ws, ws_bytes, stream);
 }
 
-tsp_status tsp_mlp_ring_bwd(const tsp_shape *s, const void *x, const void *const *w1, const void *const *w2,
-                            const void *dy, const float *dx_residual, float *dx, float *const *dw1, float *const *dw2,
-                            void *ws, size_t ws_bytes, void *stream_) {
+static tsp_status mlp_ring_bwd(const tsp_shape *s, const void *x, const void *zin, const void *const *w1,
+                               const void *const *w2, const void *dy, const float *dx_residual, float *dx,
+                               float *const *dw1, float *const *dw2, void *ws, size_t ws_bytes, void *stream_) {
   tsp_status st = check_mlp_bwd_shape(s);
   if (st) return st;
   if ((st = check_ptr(x, "x")) || (st = check_ptr(dy, "dy")) || (st = check_ptr(dx, "dx")) ||
       (st = check_ptr(ws, "ws")))
     return st;
   if (dx_residual && !aligned16(dx_residual)) return fail(TSP_ERR_INVALID_ARG, "dx_residual is not 16-byte aligned");
+  if (zin) {
+    if ((st = check_ptr(zin, "z"))) return st;
+    if (s->dtype != TSP_BF16) return fail(TSP_ERR_UNSUPPORTED, "a given pre-activation needs bf16");
+  }
   if ((st = check_ptr_list(w1, s->D, "w1")) || (st = check_ptr_list(w2, s->D, "w2")) ||
       (st = check_ptr_list((const void *const *)dw1, s->D, "dw1")) ||
       (st = check_ptr_list((const void *const *)dw2, s->D, "dw2")))
@@ -511,6 +524,8 @@ tsp_status tsp_mlp_ring_bwd(const tsp_shape *s, const void *x, const void *const
       rw{ws, L.total, "ws"};
   if (overlap(rdx, rx) || overlap(rdx, rdy) || overlap(rdx, rw) || overlap(rx, rw) || overlap(rdy, rw))
     return fail(TSP_ERR_INVALID_ARG, "x, dy, dx and ws must not overlap");
+  const Range rz{zin, (size_t)N * F * 2, "z"};
+  if (overlap(rz, rdx) || overlap(rz, rw)) return fail(TSP_ERR_INVALID_ARG, "z overlaps dx or ws");
   if (dx_residual && dx_residual != dx && overlap(Range{dx_residual, (size_t)N * h * 4, "dx_residual"}, rdx))
     return fail(TSP_ERR_INVALID_ARG, "dx_residual overlaps dx without being equal to it");
   for (int j = 0; j < D; ++j) {
@@ -524,8 +539,9 @@ tsp_status tsp_mlp_ring_bwd(const tsp_shape *s, const void *x, const void *const
        *zt = base + L.zt, *ht = base + L.ht;
   const bool bf = s->dtype == TSP_BF16;
   const tsp::PtrList r1 = ring_list(w1, D, s->r), r2 = ring_list(w2, D, s->r);
-  // weights in ring-step order: W1 rows stacked, W1^T and W2^T
-  for (int t = 0; t < D; ++t) {
+  // weights in ring-step order: W1 rows stacked (for the recomputation of Z),
+  // W1^T and W2^T
+  for (int t = 0; t < D && !zin; ++t) {
     hipError_t err = hipMemcpyAsync(base + L.w1cat + (size_t)t * fd * h * e, r1.p[t], (size_t)fd * h * e,
                                     hipMemcpyDeviceToDevice, stream);
     if (err != hipSuccess) return hip_fail(err, "W1 copy");
@@ -541,9 +557,13 @@ tsp_status tsp_mlp_ring_bwd(const tsp_shape *s, const void *x, const void *const
   TSP_LAUNCH(TSP_K_TRANSPOSE,
              tsp::launch_transpose(s->dtype, ldy, 1, h, 0, N, h, dyt, N, bf ? (int64_t)h * 64 : 0, 0, stream),
              "dy transpose");
-  // Z^T and GELU(Z)^T, then dZ^T = (W2^T dy^T) * GELU'(Z^T) in place
-  TSP_LAUNCH(TSP_K_BWD_GEMM, tsp::launch_mlp_bwd_recompute(s->dtype, w1cat, F, h, x, N, zt, bf, ht, stream),
-             "MLP backward Z");
+  // Z^T and GELU(Z)^T (recomputed, or from the given Z), then
+  // dZ^T = (W2^T dy^T) * GELU'(Z^T) in place
+  if (zin)
+    TSP_LAUNCH(TSP_K_TRANSPOSE, tsp::launch_transpose_gelu(zin, N, F, zt, ht, stream), "Z transpose");
+  else
+    TSP_LAUNCH(TSP_K_BWD_GEMM, tsp::launch_mlp_bwd_recompute(s->dtype, w1cat, F, h, x, N, zt, bf, ht, stream),
+               "MLP backward Z");
   TSP_LAUNCH(TSP_K_BWD_GEMM, tsp::launch_mlp_bwd_dz(s->dtype, w2t, F, h, dy, N, zt, bf, stream), "MLP backward dZ");
   // weight gradients of every ring step's shard: dW1 = dZ^T x, dW2 = dy^T GELU(Z)
   TSP_LAUNCH(TSP_K_BWD_GEMM,
@@ -564,6 +584,30 @@ tsp_status tsp_mlp_ring_bwd(const tsp_shape *s, const void *x, const void *const
   TSP_LAUNCH(TSP_K_BWD_GEMM, tsp::launch_mlp_bwd_dx(s->dtype, ht, bf, N, F, w1t, h, dx_residual, dx, stream),
              "MLP backward dx");
   return ok();
+}
+
+tsp_status tsp_mlp_ring(const tsp_shape *s, const void *x, const void *const *w1, const void *const *w2,
+                        const float *residual, float *y, void *ws, size_t ws_bytes, void *stream) {
+  return mlp_ring(s, x, w1, w2, residual, y, nullptr, ws, ws_bytes, stream);
+}
+
+tsp_status tsp_mlp_ring_z(const tsp_shape *s, const void *x, const void *const *w1, const void *const *w2,
+                          const float *residual, float *y, void *z, void *ws, size_t ws_bytes, void *stream) {
+  if (!z) return fail(TSP_ERR_INVALID_ARG, "z is NULL");
+  return mlp_ring(s, x, w1, w2, residual, y, z, ws, ws_bytes, stream);
+}
+
+tsp_status tsp_mlp_ring_bwd(const tsp_shape *s, const void *x, const void *const *w1, const void *const *w2,
+                            const void *dy, const float *dx_residual, float *dx, float *const *dw1, float *const *dw2,
+                            void *ws, size_t ws_bytes, void *stream) {
+  return mlp_ring_bwd(s, x, nullptr, w1, w2, dy, dx_residual, dx, dw1, dw2, ws, ws_bytes, stream);
+}
+
+tsp_status tsp_mlp_ring_bwd_z(const tsp_shape *s, const void *x, const void *z, const void *const *w1,
+                              const void *const *w2, const void *dy, const float *dx_residual, float *dx,
+                              float *const *dw1, float *const *dw2, void *ws, size_t ws_bytes, void *stream) {
+  if (!z) return fail(TSP_ERR_INVALID_ARG, "z is NULL");
+  return mlp_ring_bwd(s, x, z, w1, w2, dy, dx_residual, dx, dw1, dw2, ws, ws_bytes, stream);
 }
 
 tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const float *x, void *k_full,

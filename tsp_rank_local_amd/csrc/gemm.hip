@@ -123,6 +123,38 @@ struct EpiGelu {
   __device__ __forceinline__ void put_row(const Row &w, const float4 (&v)[4][4]) const { put_each(*this, w, v); }
 };
 
+// EpiGelu that also keeps the pre-activation: Z[:, z*cols + c] = acc in bf16,
+// row-major with pitch ldz, for a backward that takes Z from the forward.
+struct EpiGeluZ {
+  EpiGelu<bf16> h;
+  bf16 *zo;
+  int64_t ldz;
+  __device__ __forceinline__ bf16 *zat(int z, int r, int c) const { return zo + (int64_t)r * ldz + (int64_t)z * h.cols + c; }
+  __device__ __forceinline__ void operator()(int z, int r, int c, float v) const {
+    h(z, r, c, v);
+    *zat(z, r, c) = (bf16)v;
+  }
+  __device__ __forceinline__ void operator()(int z, int r, int c, float4 v) const {
+    h(z, r, c, v);
+    store4(zat(z, r, c), v);
+  }
+  struct Row {
+    EpiGelu<bf16>::Row hr;
+    bf16 *zp;
+  };
+  __device__ __forceinline__ bool fast_ok() const { return true; }
+  __device__ __forceinline__ Row row(int z, int r, int c0, int g) const { return Row{h.row(z, r, c0, g), zat(z, r, c0 + 4 * g)}; }
+  __device__ __forceinline__ void put_row(const Row &w, const float4 (&v)[4][4]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        h.put(w.hr, i, vq, v[i][vq]);
+        store4(w.zp + i * 32 + vq * 8, v[i][vq]);
+      }
+  }
+};
+
 // H[:, z*cols + u] = SiLU(gate_u) * up_u for hidden unit u of ring step z's
 // shard (gated MLP). The fp32 kernel and the leading-rows reduction hand it
 // (gate, up) pairs; the bf16 kernel's fast path hands it 128 columns, of
@@ -1064,7 +1096,7 @@ hipError_t launch_outproj(int dtype, const void *o, bool a_panel, int32_t n, int
 }
 
 hipError_t launch_mlp_up(int dtype, const void *x, bool a_panel, int32_t n, int32_t h, const PtrList &w1, int32_t D,
-                         int32_t fd, bool gated, void *hid, bool hid_panel, hipStream_t s) {
+                         int32_t fd, bool gated, void *hid, bool hid_panel, hipStream_t s, void *z_out) {
   GemmArgs a = make_args(x, h, a_panel, n, gated ? 2 * fd : fd, h);
   a.B = w1;
   a.ldb = h;
@@ -1079,6 +1111,11 @@ hipError_t launch_mlp_up(int dtype, const void *x, bool a_panel, int32_t n, int3
       return run_gemm(dtype, a, e, s);
     }
     EpiSwiGLU<float> e{(float *)hid, (int64_t)D * fd, hp, fd};
+    return run_gemm(dtype, a, e, s);
+  }
+  if (z_out != nullptr) {
+    if (dtype != TSP_BF16) return hipErrorInvalidValue;
+    EpiGeluZ e{EpiGelu<bf16>{(bf16 *)hid, (int64_t)D * fd, hp, fd}, (bf16 *)z_out, (int64_t)D * fd};
     return run_gemm(dtype, a, e, s);
   }
   if (dtype == TSP_BF16) {

@@ -185,6 +185,48 @@ __global__ __launch_bounds__(256) void transpose_bf16x8_kernel(PtrList in, int64
   }
 }
 
+// Z [R = n][C = F] to Z^T (panels of [F][n]) and GELU(Z)^T ([F][n] row-major),
+// 16-byte runs through a padded 64 x 64 tile as in transpose_bf16x8_kernel.
+__global__ __launch_bounds__(256) void transpose_gelu_kernel(const bf16 *__restrict__ z, int32_t R, int32_t C,
+                                                             bf16 *__restrict__ zt, bf16 *__restrict__ ht) {
+  __shared__ __attribute__((aligned(16))) bf16 tile[64][72];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int64_t zt_panel = (int64_t)C * 64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int chunk = threadIdx.x + 256 * i, row = chunk >> 3, cc = (chunk & 7) * 8;
+    const int r = r0 + row, c = c0 + cc;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < R && c < C) v = *reinterpret_cast<const u32x4 *>(z + (int64_t)r * C + c);
+    *reinterpret_cast<u32x4 *>(&tile[row][cc]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int chunk = threadIdx.x + 256 * i, orow = chunk >> 3, oc = (chunk & 7) * 8;
+    const int c = c0 + orow, r = r0 + oc;
+    if (c < C && r < R) {
+      bf16x8 v, gv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] = tile[oc + e][orow];
+        gv[e] = (bf16)gelu_erf((float)v[e]);
+      }
+      *reinterpret_cast<bf16x8 *>(zt + panel_index(c, r, zt_panel)) = v;
+      *reinterpret_cast<bf16x8 *>(ht + (int64_t)c * R + r) = gv;
+    }
+  }
+}
+
+hipError_t launch_transpose_gelu(const void *z, int32_t n, int32_t F, void *zt_panel, void *ht, hipStream_t s) {
+  if (n <= 0 || F <= 0) return hipSuccess;
+  if (((n | F) & 7) != 0 || (n + 63) / 64 > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_gelu_kernel, dim3((F + 63) / 64, (n + 63) / 64), dim3(256), 0, s,
+                     reinterpret_cast<const bf16 *>(z), n, F, reinterpret_cast<bf16 *>(zt_panel),
+                     reinterpret_cast<bf16 *>(ht));
+  return hipGetLastError();
+}
+
 hipError_t launch_transpose(int dtype, const PtrList &in, int32_t nz, int64_t in_ld, int64_t in_panel, int32_t R,
                             int32_t C, void *out, int64_t out_ld, int64_t out_panel, int64_t out_zoff, hipStream_t s) {
   if (R <= 0 || C <= 0 || nz <= 0) return hipSuccess;

@@ -69,6 +69,10 @@ hipError_t launch_rope_rows(float *x, int64_t ld, int32_t n, int32_t H, int32_t 
 hipError_t launch_transpose(int dtype, const PtrList &in, int32_t nz, int64_t in_ld, int64_t in_panel, int32_t R,
                             int32_t C, void *out, int64_t out_ld, int64_t out_panel, int64_t out_zoff, hipStream_t s);
 
+// Z [n][F] bf16 (row-major) to Z^T in panel layout (panel stride F * 64) and
+// GELU(Z)^T [F][n] row-major, in one pass (n and F multiples of 8).
+hipError_t launch_transpose_gelu(const void *z, int32_t n, int32_t F, void *zt_panel, void *ht, hipStream_t s);
+
 // ---------------------------------------------------------------- GEMMs
 // All products are C = A B^T with A [M][K] and B [N][K] (both K-contiguous).
 // a_panel: A in panel layout (bf16 only; panel stride M * 64), else row-major.
@@ -89,8 +93,10 @@ hipError_t launch_outproj(int dtype, const void *o, bool a_panel, int32_t n, int
 // GELU(x w1[t]^T) in dtype, w1[t] [fd][h] the shard of ring step t; hid
 // [n][D*fd] (panel layout when hid_panel). gated: w1[t] is [2fd][h] (gate
 // rows, then up rows) and hid = SiLU(x W_g^T) * (x W_u^T).
+// z_out (bf16, GELU MLP only; else null): also write Z = x w1[t]^T before
+// the GELU, [n][D*fd] row-major in the same column order as hid.
 hipError_t launch_mlp_up(int dtype, const void *x, bool a_panel, int32_t n, int32_t h, const PtrList &w1, int32_t D,
-                         int32_t fd, bool gated, void *hid, bool hid_panel, hipStream_t s);
+                         int32_t fd, bool gated, void *hid, bool hid_panel, hipStream_t s, void *z_out = nullptr);
 // y = (res ? res : 0) + sum_t hid[:, t*fd:(t+1)*fd] w2[t]^T in fp32, the
 // reduction walking ring steps t = 0..D-1 in order; w2[t] [h][fd]; res may
 // equal y.
