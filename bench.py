@@ -56,82 +56,185 @@ def layer_flops(sh, r):
     return {"qkv": qkv, "attention": attn, "outproj": outp, "mlp": mlp, "total": qkv + attn + outp + mlp}
 
 
-def traffic_from_profile(kernel_src: str, name: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if the
-    kernel source is unchanged since the counters were taken; else None."""
-    path = os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
-    if not os.path.exists(path):
-        return None
-    fields = {}
-    for line in open(path):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            fields[k.strip()] = v.strip()
-    src = open(kernel_src, "rb").read()
-    if fields.get("source_sha256") != hashlib.sha256(src).hexdigest():
-        return None
-    try:
-        return float(fields["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+# Kernel classes of the layer step whose HBM bytes the traffic summary
+# records: (class, substring of the kernel name, which dispatch of that name
+# within a step when one name serves two classes, source file).
+# Names appear demangled or mangled in the counter files, so a class is
+# matched by substrings that must all be present.
+TRAFFIC_KERNELS = (
+    ("attention", ("attn_bf16_kernel<128, false, true",), None, "attention.hip"),
+    ("qkv", ("gemm_bf16_kernel", "EpiQKV"), None, "gemm.hip"),
+    ("outproj", ("gemm_bf16_kernel", "EpiAddF32"), 0, "gemm.hip"),
+    ("mlp_down", ("gemm_bf16_kernel", "EpiAddF32"), 1, "gemm.hip"),
+    ("mlp_up", ("gemm_bf16_kernel", "EpiGelu"), None, "gemm.hip"),
+    ("rmsnorm", ("rmsnorm_kernelIDF16bDF16b",), None, "rows.hip"),
+)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer7b_hbm_traffic.txt")
+TRAFFIC_PASSES = (
+    "TCC_BUBBLE_sum TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_DRAM_32B_sum GRBM_GUI_ACTIVE",
+    "TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum TCC_EA0_WRREQ_WRITE_DRAM_32B_sum GRBM_GUI_ACTIVE",
+)
 
 
-def _counter_per_dispatch(path, counter):
-    """{kernel name: [value per dispatch]} of one counter in a rocprofv3 csv."""
+def _src_sha(name):
+    return hashlib.sha256(open(os.path.join(ROOT, "tsp_rank_local_amd", "csrc", name), "rb").read()).hexdigest()
+
+
+def traffic_from_profile():
+    """{kernel class: HBM bytes per launch} from the committed counter
+    summary, for the classes whose kernel source is unchanged since the
+    counters were taken (the others are left out)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    out, sha = {}, {}
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("source_sha256 "):
+            _, name, h = line.split()
+            sha[name] = h
+        elif line.startswith("hbm_bytes "):
+            _, cls, v = line.split()
+            out[cls] = float(v)
+    srcs = {cls: src for cls, _, _, src in TRAFFIC_KERNELS}
+    return {cls: v for cls, v in out.items() if cls in srcs and sha.get(srcs[cls]) == _src_sha(srcs[cls])}
+
+
+def summarize_traffic(csvs, copy_mib):
+    """HBM bytes per launch of the layer step's kernels from the L2-to-memory
+    request counters of rocprofv3 (two passes, TRAFFIC_PASSES).
+
+    Reads: the requests the L2 sends to the data fabric, by size, give
+    FETCH_SIZE (128-byte requests x 128 + 64-byte x 64 + 32-byte x 32); the
+    requests due to DRAM, counted in 32-byte units whatever their size, give
+    the DRAM read bytes. Writes: WRITE_SIZE (64-byte requests x 64, the rest
+    x 32) and the DRAM write requests in 32-byte units. The plain device copy
+    of copy_mib MiB that --copy-mib runs before warmup calibrates each: its
+    known bytes divided by what the counter reads. The bytes recorded per
+    kernel are the DRAM counts times their copy factors."""
     import csv
-    out = {}
-    for row in csv.DictReader(open(path)):
-        if row["Counter_Name"] == counter:
-            out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
-    return out
+    per = {}  # (kernel, dispatch) -> {counter: value}
+    order = {}
+    for path in csvs:
+        for row in csv.DictReader(open(path)):
+            key = (row["Kernel_Name"], int(row["Dispatch_Id"]))
+            per.setdefault(key, {})[row["Counter_Name"]] = float(row["Counter_Value"])
+    for name, disp in sorted(per, key=lambda k: k[1]):
+        order.setdefault(name, []).append(disp)
 
+    def derived(c):
+        d = {}
+        if "TCC_EA0_RDREQ_sum" in c:
+            b, rq, r32 = c.get("TCC_BUBBLE_sum", 0.0), c["TCC_EA0_RDREQ_sum"], c.get("TCC_EA0_RDREQ_32B_sum", 0.0)
+            d["fetch"] = b * 128 + (rq - b - r32) * 64 + r32 * 32
+            d["req128"], d["req32"], d["req"] = b, r32, rq
+        if "FETCH_SIZE" in c:  # the derived counter itself (KiB)
+            d.setdefault("fetch", 1024 * c["FETCH_SIZE"])
+        if "WRITE_SIZE" in c:
+            d.setdefault("write", 1024 * c["WRITE_SIZE"])
+        if "TCC_EA0_RDREQ_DRAM_32B_sum" in c:
+            d["dram_rd"] = 32 * c["TCC_EA0_RDREQ_DRAM_32B_sum"]
+        if "TCC_EA0_WRREQ_sum" in c:
+            w, w64 = c["TCC_EA0_WRREQ_sum"], c.get("TCC_EA0_WRREQ_64B_sum", 0.0)
+            d["write"] = (w - w64) * 32 + w64 * 64
+        if "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum" in c:
+            d["dram_wr"] = 32 * c["TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"]
+        return d
 
-def summarize_counters(fetch_csv, write_csv, copy_mib):
-    """HBM bytes per attention launch from FETCH_SIZE and WRITE_SIZE (KiB per
-    dispatch), each scaled by what the same counter reads for the plain
-    device copy of copy_mib MiB that --copy-mib runs before warmup."""
-    fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE")
-    write = _counter_per_dispatch(write_csv, "WRITE_SIZE")
-    copy_bytes = float(copy_mib) * (1 << 20)
+    # the copy: the largest dispatch of the runtime's copy kernel in each pass
+    copy = {}
+    for (name, disp), c in per.items():
+        if "copyBuffer" not in name:
+            continue
+        for k, v in derived(c).items():
+            copy[k] = max(copy.get(k, 0.0), v)
+    nbytes = float(copy_mib) * (1 << 20)
+    scale = {k: nbytes / copy[k] for k in ("fetch", "dram_rd", "write", "dram_wr") if copy.get(k)}
 
-    def one(d, key):
-        names = [k for k in d if key in k]
-        if len(names) != 1:
-            sys.exit(f"summarize-counters: expected one kernel matching {key!r}, found {names}")
-        v = d[names[0]]
-        return names[0], sum(v) / len(v)
+    def avg(dicts, k):
+        v = [d[k] for d in dicts if k in d]
+        return sum(v) / len(v) if v else None
 
-    def copy_kib(d):
-        # the largest dispatch of the runtime's copy kernel is the reference copy
-        v = [x for k, vals in d.items() if "copyBuffer" in k for x in vals]
-        if not v:
-            sys.exit("summarize-counters: no copy kernel dispatch found")
-        return max(v)
-
-    name, f_kib = one(fetch, "attn_bf16_kernel<128")
-    _, w_kib = one(write, "attn_bf16_kernel<128")
-    f_scale = copy_bytes / (copy_kib(fetch) * 1024.0)
-    w_scale = copy_bytes / (copy_kib(write) * 1024.0)
-    hbm = f_kib * 1024.0 * f_scale + w_kib * 1024.0 * w_scale
-    src = os.path.join(ROOT, "tsp_rank_local_amd", "csrc", "attention.hip")
     lines = [
-        "# HBM traffic of one attention launch in the 7B layer (rank 0 of D=8, S=131072), from rocprofv3 counters.",
-        "# Made by:",
-        "#   rocprofv3 --pmc FETCH_SIZE -d <dir1> -o run --output-format csv -- "
-        "python bench.py --steps 1 --warmup 0 --cpu-rows 0 --copy-mib 1024",
-        "#   rocprofv3 --pmc WRITE_SIZE -d <dir2> -o run --output-format csv -- "
-        "python bench.py --steps 1 --warmup 0 --cpu-rows 0 --copy-mib 1024",
-        "#   python bench.py --summarize-counters <dir1>/run_counter_collection.csv <dir2>/run_counter_collection.csv",
-        "# Each counter is scaled by bytes / counter for the 1 GiB device copy run before warmup.",
-        f"kernel: {name}",
-        f"fetch_kib_per_dispatch: {f_kib:.1f}",
-        f"write_kib_per_dispatch: {w_kib:.1f}",
-        f"copy_fetch_scale: {f_scale:.4f}",
-        f"copy_write_scale: {w_scale:.4f}",
-        f"hbm_bytes_per_launch: {hbm:.6g}",
-        f"source_sha256: {hashlib.sha256(open(src, 'rb').read()).hexdigest()}",
+        "# HBM traffic per launch of the 7B layer step's kernels (rank 0 of D=8, S=131072), from rocprofv3 counters.",
+        "# Made by (one step each; the 1 GiB device copy run before warmup calibrates the counters):",
     ]
-    out = os.path.join(ROOT, "profiles", "attention_7b_traffic.txt")
+    for i, ctrs in enumerate(TRAFFIC_PASSES):
+        lines.append(f"#   rocprofv3 --pmc {ctrs} -d <dir{i + 1}> -o run --output-format csv -- "
+                     "python bench.py --steps 1 --warmup 0 --cpu-rows 0 --copy-mib 1024")
+    lines += [
+        "#   python bench.py --summarize-traffic <dir1>/run_counter_collection.csv <dir2>/run_counter_collection.csv",
+        "# fetch: L2->fabric read requests by size (128/64/32 B); dram_rd, dram_wr: DRAM requests in 32-byte units;",
+        "# write: write requests (64 B or 32 B). Copy factor = copy bytes / counter bytes for the 1 GiB copy.",
+        "# hbm_bytes <class> = dram_rd x its copy factor + dram_wr x its copy factor (per launch).",
+    ]
+    for k in ("fetch", "dram_rd", "write", "dram_wr"):
+        if k in copy:
+            lines.append(f"copy {k}: {copy[k]:.6g} bytes for {nbytes:.6g}; factor {scale.get(k, float('nan')):.4f}")
+    for cls, key, which, src in TRAFFIC_KERNELS:
+        names = [n for n in order if all(k in n for k in key)]
+        if len(names) != 1:
+            continue
+        disps = order[names[0]]
+        if which is not None:  # dispatch `which` of every step (dispatches alternate between the classes)
+            disps = disps[which::2]
+        rows = [derived(per[(names[0], d)]) for d in disps]
+        f, dr, w, dw = avg(rows, "fetch"), avg(rows, "dram_rd"), avg(rows, "write"), avg(rows, "dram_wr")
+        r128, r32, rq = avg(rows, "req128"), avg(rows, "req32"), avg(rows, "req")
+        split = (f"{100 * r128 / rq:.1f}/{100 * (rq - r128 - r32) / rq:.1f}/{100 * r32 / rq:.1f}"
+                 if rq else "-")
+        lines.append(f"kernel {cls}: {names[0][:90]}")
+        g = (lambda x: "-" if x is None else f"{x:.6g}")  # noqa: E731
+        lines.append(f"  fetch {g(f)}  dram_rd {g(dr)}  write {g(w)}  dram_wr {g(dw)}  "
+                     f"read requests 128/64/32 B (%) {split}")
+        if dr is not None and dw is not None and "dram_rd" in scale and "dram_wr" in scale:
+            lines.append(f"hbm_bytes {cls} {dr * scale['dram_rd'] + dw * scale['dram_wr']:.6g}")
+    for src in sorted({t[3] for t in TRAFFIC_KERNELS}):
+        lines.append(f"source_sha256 {src} {_src_sha(src)}")
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+KTRACE_WORKLOADS = {
+    # workload -> (title, summary file, bench arguments)
+    "layer": ("one 7B TSP layer forward (rank 0 of D=8, S=131072, 16384 local tokens, bf16)",
+              "attn_layer7b_kernel_stats.md", ""),
+}
+
+
+def summarize_ktrace(stats_csv, bench_json, workload="layer"):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of the
+    benchmark: per-kernel launches and durations from the profiler, beside
+    the same run's own HIP-event figures (its JSON line)."""
+    import csv
+    title, fname, bench_args = KTRACE_WORKLOADS[workload]
+    rows = list(csv.DictReader(open(stats_csv)))
+    b = json.loads([ln for ln in open(bench_json).read().splitlines() if ln.startswith("{")][-1])
+    cmd = ("rocprofv3 --kernel-trace --stats -d <dir> -o run --output-format csv -- python bench.py" +
+           (f" {bench_args}" if bench_args else ""))
+    lines = [f"# Kernel time, {title}", "", "Command (run from the repository root on one MI355X):", "",
+             f"    {cmd}", "",
+             f"`run_kernel_stats.csv` ({b['warmup']} warmup + {b['steps']} timed + {b['steps']} per-step steps):", "",
+             "| kernel | calls | avg ms | min ms | max ms | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['Name'][:110]} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
+                     f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} | {float(r['Percentage']):.1f}% |")
+    k = b.get("kernels", {})
+    lines += ["", "Same run, bench.py's HIP events on the launching stream:", ""]
+    lines.append(f"- step: {b['ms_per_step']:.3f} ms, {b['value']:,.0f} local tokens/s, "
+                 f"{b['pct_bf16_mfma_peak']:.1f}% of the 2.5 PF bf16 peak over the layer")
+    for name, v in k.items():
+        extra = f", {v['hbm_gb_s']:.0f} GB/s of HBM traffic" if "hbm_gb_s" in v else ""
+        lines.append(f"- {name}: {v['ms_per_launch']:.3f} ms per launch, {v['launches_per_step']:g} per step{extra}")
+    rf = b.get("roofline") or {}
+    if rf:
+        lines.append(f"- roofline ({rf['kernel']}): {rf['achieved']:.0f} {rf['unit']} of {rf['peak']:.0f}, "
+                     f"frac {rf['frac']:.3f}; traffic {rf['traffic']}")
+    att = [r for r in rows if "attn_bf16_kernel" in r["Name"]]
+    if att and "attention" in k:
+        a_ms = float(att[0]["AverageNs"]) / 1e6
+        lines.append(f"- attention: profiler average {a_ms:.3f} ms vs HIP events {k['attention']['ms_per_launch']:.3f} "
+                     f"ms ({100 * (k['attention']['ms_per_launch'] / a_ms - 1):+.1f}%)")
+    out = os.path.join(ROOT, "profiles", fname)
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -178,6 +281,7 @@ def summarize_sq(csvs, workload="layer"):
         for row in csv.DictReader(open(path)):
             key = (path, row["Kernel_Name"], row["Dispatch_Id"])
             per.setdefault(key, {})[row["Counter_Name"]] = float(row["Counter_Value"])
+            per[key]["_ns"] = float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
     kern = {}
     for (_, name, _), c in per.items():
         if "GRBM_GUI_ACTIVE" not in c or "copyBuffer" in name:
@@ -189,6 +293,9 @@ def summarize_sq(csvs, workload="layer"):
             if num in c and (den == 1.0 or den in c):
                 f[key] = scale * c[num] / (simd if den == 1.0 else max(c[den], 1.0))
 
+        # effective shader clock: the kernel's cycles (per XCD) over its duration
+        if c.get("_ns", 0.0) > 0:
+            f["sclk_ghz"] = c["GRBM_GUI_ACTIVE"] / 8.0 / c["_ns"]
         put("mfma_busy", "SQ_VALU_MFMA_BUSY_CYCLES")
         put("valu_active", "SQ_ACTIVE_INST_VALU", scale=4.0)
         put("mfma_valu_coexec", "SQ_VALU_MFMA_COEXEC_CYCLES")
@@ -211,8 +318,10 @@ def summarize_sq(csvs, workload="layer"):
     lines += [f"#   python bench.py --summarize-sq <dir1>/run_counter_collection.csv <dir2>/run_counter_collection.csv{wl}",
               "# Fractions are of the kernel's cycles per SIMD (GRBM_GUI_ACTIVE / 8 XCDs, x 1024 SIMDs);",
               "# SQ_ACTIVE_INST_* count 4-cycle units. Instruction ratios are per MFMA instruction.",
-              "kernel | mfma_busy | valu_active | coexec | lds_active | lds_wait | valu/mfma | salu/mfma | lds/mfma "
-              "| trans/mfma | bank_conflicts/lds"]
+              "# sclk: effective shader clock, GRBM_GUI_ACTIVE / 8 XCDs / the dispatch's duration (GHz);",
+              "# mfma_tflops: mfma_busy x sclk x 256 CUs x 4096 flop per CU-cycle (dense bf16 rate at that busy share).",
+              "kernel | sclk | mfma_busy | mfma_tflops | valu_active | coexec | lds_active | lds_wait | valu/mfma | "
+              "salu/mfma | lds/mfma | trans/mfma | bank_conflicts/lds"]
     order = sorted(kern, key=lambda n: -len(kern[n]))
     for name in order:
         rows = kern[name]
@@ -228,7 +337,10 @@ def summarize_sq(csvs, workload="layer"):
             v = avg(k)
             return "-" if v is None else f"{v:.3f}"
 
-        lines.append(f"{name[:80]} | {fmt('mfma_busy')} | {fmt('valu_active')} | {fmt('mfma_valu_coexec')} | "
+        mb, ck = avg("mfma_busy"), avg("sclk_ghz")
+        tf = f"{mb * ck * 1e9 * 256 * 4096 / 1e12:.0f}" if (mb is not None and ck is not None) else "-"
+        lines.append(f"{name[:80]} | {fmt('sclk_ghz')} | {fmt('mfma_busy')} | {tf} | {fmt('valu_active')} | "
+                     f"{fmt('mfma_valu_coexec')} | "
                      f"{fmt('lds_active')} | {fmt('lds_wait')} | {ratio(va)} | {ratio(sa)} | {ratio(ld)} | "
                      f"{fmt('trans_per_mfma')} | {fmt('bank_conflicts_per_lds_inst')}")
     out = os.path.join(ROOT, "profiles", fname)
@@ -321,14 +433,20 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warmup, run one plain device-to-device copy of this many MiB (a known-size "
                          "reference for rocprofv3 HBM byte counters)")
+    ap.add_argument("--summarize-ktrace", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"),
+                    help="write the kernel-time summary of the workload under profiles/ from a rocprofv3 "
+                         "--kernel-trace --stats run of bench.py (its run_kernel_stats.csv and JSON line)")
     ap.add_argument("--summarize-sq", nargs="+", metavar="CSV",
                     help="write profiles/layer7b_sq_counters.txt from rocprofv3 shader-counter csv files")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/attention_7b_traffic.txt from two rocprofv3 --pmc counter_collection.csv "
-                         "files (FETCH_SIZE, WRITE_SIZE) of a run with --copy-mib, then exit")
+    ap.add_argument("--summarize-traffic", nargs="+", metavar="CSV",
+                    help="write profiles/layer7b_hbm_traffic.txt from the rocprofv3 counter_collection.csv files of "
+                         "the two traffic passes of a run with --copy-mib, then exit")
     args = ap.parse_args()
-    if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, copy_mib=args.copy_mib or 1024)
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic, copy_mib=args.copy_mib or 1024)
+        return
+    if args.summarize_ktrace:
+        summarize_ktrace(*args.summarize_ktrace, args.workload)
         return
     if args.summarize_sq:
         summarize_sq(args.summarize_sq, args.workload)
@@ -344,6 +462,7 @@ def main():
 
     assert torch.cuda.is_available(), "needs a GPU"
     tsp.lib()
+    mem0 = torch.cuda.memory_allocated()
     sh = dataclasses.replace(synth.SEVEN_B, Hkv=args.hkv, mlp=args.mlp)
     r = args.rank
     N = sh.N
@@ -499,7 +618,9 @@ def main():
         step_exps = sh.H * attn_pairs(sh.S, sh.D, r)
         workload = f"tsp_zigzag_attn: 32x128 heads{kv_note}, S=131072, 16384 zigzag queries of rank {r} of D=8"
     torch.cuda.synchronize()
-    log(f"inputs resident in HBM ({time.perf_counter() - t_gen:.1f} s); warmup {args.warmup}")
+    mem_inputs = torch.cuda.memory_allocated() - mem0
+    log(f"inputs resident in HBM ({time.perf_counter() - t_gen:.1f} s, {mem_inputs / 1e9:.3f} GB); "
+        f"warmup {args.warmup}")
 
     if args.copy_mib > 0:
         n = args.copy_mib << 20
@@ -553,15 +674,23 @@ def main():
 
     tokens_per_s = N / (ms_step * 1e-3)
     # dominant kernel: attention (73% of the layer's algorithmic flops)
+    # HBM bytes per launch from the committed counter summary (taken on the
+    # default layer: rank 0, 32 K/V heads, GELU MLP, no rotation), and the
+    # bandwidth they give at this run's launch times
+    default_layer = (args.workload == "layer" and r == 0 and sh.kv_heads == sh.H and sh.mlp == "gelu"
+                     and args.rope_base == 0.0)
+    hbm = traffic_from_profile() if default_layer else {}
+    for cls, nbytes in hbm.items():
+        if cls in kernels:
+            kernels[cls]["hbm_bytes"] = nbytes
+            kernels[cls]["hbm_gb_s"] = nbytes / (kernels[cls]["ms_per_launch"] * 1e-3) / 1e9
     roofline = None
     if "attention" in kernels:
         t_attn = kernels["attention"]["ms_per_launch"] * 1e-3
         achieved = flops["attention"] / t_attn / 1e12
         roofline = {"kernel": "attn_bf16_kernel<128>", "bound": "mfma", "achieved": achieved,
                     "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_BF16,
-                    # counters were taken on rank 0 with 32 K/V heads
-                    "traffic": (traffic_from_profile(os.path.join(ROOT, "tsp_rank_local_amd", "csrc", "attention.hip"),
-                                                     "attention_7b") if r == 0 and sh.kv_heads == sh.H else None)}
+                    "traffic": hbm.get("attention")}
     elif "attn_bwd" in kernels:
         t_b = kernels["attn_bwd"]["ms_per_launch"] * 1e-3
         achieved = 2.5 * flops["attention"] / t_b / 1e12
@@ -581,6 +710,10 @@ def main():
         roofline = {"kernel": "gemm_bf16_kernel<EpiSwiGLU>" if sh.mlp == "swiglu" else "gemm_bf16_kernel<EpiGelu>",
                     "bound": "mfma", "achieved": achieved,
                     "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_BF16, "traffic": None}
+
+    memory = None
+    if args.workload in ("layer", "layers32"):
+        memory = memory_report(sh, r, args, mem_inputs)
 
     cpu = None
     if args.cpu_rows > 0 and args.workload == "layer":
@@ -617,10 +750,31 @@ def main():
         "softmax_exps_per_step": step_exps,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "memory": memory,
         "kernels": kernels,
         "gpu": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)
+
+
+def memory_report(sh, r, args, allocated):
+    """Device bytes the workload's inputs, outputs and workspace took (the
+    allocator's count) beside the analytic model of the same allocations,
+    and the model's per-rank footprint of the distributed 32-layer forward
+    (and of training under its stated assumptions) at this shape; the pages'
+    38.8 GB per GPU (8 x MI300X, 128K tokens) is context, not a target."""
+    from tsp_rank_local_amd import memory as mm
+
+    layers = 32 if args.workload == "layers32" else 1
+    m = mm.Model(S=sh.S, D=sh.D, r=r, h=sh.h, H=sh.H, Dh=sh.Dh, F=sh.F, layers=layers, Hkv=sh.Hkv, mlp=sh.mlp,
+                 rope_base=args.rope_base)
+    model = mm.single_gpu_bytes(m, "layer" if layers == 1 else "layers")
+    m32 = dataclasses.replace(m, layers=32)
+    fwd, trn = mm.rank_memory(m32), mm.rank_memory(m32, train=True)
+    return {"allocated_bytes": allocated, "model_bytes": model, "model_vs_allocated": model / allocated,
+            "rank_forward_32_layers_gb": {k: round(v / 1e9, 3) for k, v in fwd.items()},
+            "rank_train_32_layers_gb": round(trn["total"] / 1e9, 3),
+            "pages_tsp_gb_per_gpu": 38.8}
 
 
 def cpu_model():

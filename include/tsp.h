@@ -302,7 +302,14 @@ tsp_status tsp_mlp_ring_bwd_z(const tsp_shape *shape, const void *x, const void 
                               const float *dx_residual, float *dx, float *const *dw1,
                               float *const *dw2, void *ws, size_t ws_bytes, void *stream);
 
-/* One decoder layer forward on rank r's S/D tokens.
+/* One decoder layer forward on rank r's S/D tokens: the whole folded-axis
+ * schedule of the zubnet.ai news item "Zyphra TSP folds TP+SP onto one GPU
+ * axis" on one rank. Paragraph 1: the rank holds 1/D of the tokens and 1/D
+ * of every weight matrix. Paragraph 2: the attention weight shards arrive by
+ * broadcast, one after another, and the rank applies each to its own tokens
+ * (QKV, then the output projection); K and V are all-gathered under the
+ * zigzag partition before attention; the MLP shards arrive round a ring and
+ * the rank sums their contributions itself, with no all-reduce.
  *  x: [S/D][h] fp32, local rows in zigzag order.
  *  k_full, v_full: [S][Hkv][Dh] (dtype). The rows at rank r's own positions are
  *    written by PHASE_KV; every other row must hold what the all-gather would

@@ -219,6 +219,13 @@ def test_mlp_bwd_workspace_and_errors():
     # S/D = 96 tokens: not a multiple of 64 (K of the weight-gradient products)
     st = call(shape=tsp.make_shape(384, 4, 0, 256, 4, 64, 1024, dtype="bf16"), nbytes=1 << 40)[0]
     assert st == tsp.TSP_ERR_UNSUPPORTED
+    # S/D = 4194304 tokens: past the 65535 x 64 rows of a layout pass and the
+    # 32-bit offsets of the token-K products; rejected before anything runs
+    # (the stream argument 0 would be the default stream: nothing may reach it)
+    st, msg = call(shape=tsp.make_shape(2 * 4194304, 2, 0, 64, 1, 64, 128, dtype="bf16"), nbytes=1 << 60)
+    assert st == tsp.TSP_ERR_UNSUPPORTED and b"S/D" in msg
+    with pytest.raises(tsp.TspError):
+        tsp.workspace_size(tsp.make_shape(2 * 4194304, 2, 0, 64, 1, 64, 128, dtype="bf16"), tsp.TSP_WS_MLP_BWD)
     with pytest.raises(tsp.TspError):
         tsp.workspace_size(_shape(dtype="bf16", mlp="swiglu"), tsp.TSP_WS_MLP_BWD)
 

@@ -309,12 +309,13 @@ def test_attn_bwd_rank_contributions_sum(torch, dtype):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("from_fwd", [False, True])
 def test_attn_bwd_7b(torch, from_fwd):
-    """7B attention (32 heads x 128, S = 131072, D = 8), rank 0: dq of the
-    first 64 and the last 64 local rows (positions 0.. and 131008..), and dK,
-    dV of the last 64 keys, which only those last rows see, against the
-    oracle; over the whole sequence, sum_u dV_u = sum_t dO_t and sum_u dK_u =
-    0 for every head and feature (the softmax weights sum to one, the score
-    gradients of a row to zero), and keys past the rank are untouched by it."""
+    """7B attention (32 heads x 128, S = 131072, D = 8), rank 0: for one
+    whole head, dq of every local row and dK, dV of every key row of the
+    sequence (the rank's contribution, which covers the key blocks on both
+    sides of the chunk boundaries and the keys past the rank's last position)
+    against the oracle, which works per head; over all heads, sum_u dV_u =
+    sum_t dO_t and sum_u dK_u = 0 for every head and feature (the softmax
+    weights sum to one, the score gradients of a row to zero)."""
     SH = synth.SEVEN_B
     N, S, H, Dh = SH.N, SH.S, SH.H, SH.Dh
     r = 0
@@ -326,14 +327,13 @@ def test_attn_bwd_7b(torch, from_fwd):
     dq, dk, dv = _attn_bwd_run(torch, s, q, k, v, do, "bf16", from_fwd)
     assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
     pos = oracle.zigzag_positions(S, SH.D, r)
-    k64, v64 = f64(k, "bf16"), f64(v, "bf16")
-    for rows, what in ((np.arange(64), "first"), (np.arange(N - 64, N), "last")):
-        want = oracle.causal_attention_backward(f64(q[rows], "bf16"), k64, v64, pos[rows], SH.scale,
-                                                f64(do[rows], "bf16"))
-        assert_close(dq[rows], want["dq"], TOL_BF16, f"dq of the {what} 64 rows")
-        if what == "last":
-            assert_close(dk[S - 64:], want["dk"][S - 64:], TOL_BF16, "dK of the last 64 keys")
-            assert_close(dv[S - 64:], want["dv"][S - 64:], TOL_BF16, "dV of the last 64 keys")
+    hd = 5
+    sl = slice(hd, hd + 1)
+    want = oracle.causal_attention_backward(f64(q[:, sl], "bf16"), f64(k[:, sl], "bf16"), f64(v[:, sl], "bf16"),
+                                            pos, SH.scale, f64(do[:, sl], "bf16"))
+    assert_close(dq[:, sl], want["dq"], TOL_BF16, f"dq of head {hd}, all {N} rows")
+    assert_close(dk[:, sl], want["dk"], TOL_BF16, f"dK of head {hd}, all {S} keys")
+    assert_close(dv[:, sl], want["dv"], TOL_BF16, f"dV of head {hd}, all {S} keys")
     do64 = f64(do, "bf16")
     assert_close(dv.sum(axis=0), do64.sum(axis=0), TOL_BF16, "sum over keys of dV vs sum over rows of dO")
     # sum_u dK_u = 0: held against the scale of one key row's gradient

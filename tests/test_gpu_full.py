@@ -1,9 +1,10 @@
 """GPU parity at the full 7B sizes (hidden 4096, 32 heads of 128, MLP 16384,
-S = 131072, D = 8), in the launch configuration the benchmark times. The
-oracle computes sampled output rows one by one; where output power is
-concentrated in a few rows (attention of rank 0, whose first queries see few
-keys) the rms in the tolerance is a stratified estimate: a dense block of
-those rows plus a strided sample of the rest, weighted by the stride."""
+S = 131072, D = 8), in the launch configuration the benchmark times. Where the
+oracle cannot take the whole output in seconds it computes a sample: whole
+heads of the attention output (every row), whole 128-row query tiles of the
+layer plus rows at a stride prime to the 32 rows of a wave, and evenly
+spread rows of the MLP ring; the tolerance's rms is over the compared
+oracle values."""
 import dataclasses
 
 import numpy as np
@@ -63,17 +64,14 @@ def test_mlp_ring_7b(torch):
     assert d <= 1e-4 * rms
 
 
-def _stratified_rows(N, C, dense, stride):
-    """Rows 0..dense-1 of the first chunk, plus every stride-th row after."""
-    rows_dense = np.arange(dense)
-    rows_sparse = np.arange(dense, N, stride)
-    return rows_dense, rows_sparse
-
-
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("r", [0, 7])
 def test_zigzag_attention_7b(torch, r):
-    """Attention alone: 32 heads x 128, 16384 zigzag queries of rank r."""
+    """Attention alone: 32 heads x 128, 16384 zigzag queries of rank r. Two
+    whole heads (the first and the last) are compared element by element on
+    every local row, so every lane, wave, query tile and key walk of the
+    launch is checked; the oracle works per head, so q, k and v are sliced to
+    the head. Every head's output is checked to be finite."""
     N = SH.N
     q = synth.attn_queries(SH, seed=3)
     k, v = synth.remote_kv(SH, seed=3)
@@ -85,16 +83,11 @@ def test_zigzag_attention_7b(torch, r):
     assert bool(torch.isfinite(o).all())
     del kd, vd
     pos = oracle.zigzag_positions(SH.S, SH.D, r)
-    stride = 64
-    rd, rsp = _stratified_rows(N, SH.C, 256, stride)
-    rows = np.concatenate([rd, rsp])
-    k32, v32 = synth.as_f32(k, "bf16"), synth.as_f32(v, "bf16")
-    want = oracle.causal_attention(f64(q[rows], "bf16"), k32, v32, pos[rows], SH.scale)
-    # stratified estimate of mean(o^2) over all N rows
-    nd = len(rd)
-    sq = (want ** 2).sum(axis=(1, 2))
-    est = (sq[:nd].sum() + stride * sq[nd:].sum()) / (N * SH.H * SH.Dh)
-    assert_close(down(o[torch.from_numpy(rows).cuda()]), want, TOL_BF16, f"O rows (r={r})", rms=float(np.sqrt(est)))
+    for hd in (0, SH.H - 1):
+        sl = slice(hd, hd + 1)
+        want = oracle.causal_attention(f64(q[:, sl], "bf16"), synth.as_f32(k[:, sl], "bf16"),
+                                       synth.as_f32(v[:, sl], "bf16"), pos, SH.scale)
+        assert_close(down(o[:, sl]), want, TOL_BF16, f"O of head {hd}, all {N} rows (r={r})")
 
 
 @pytest.mark.timeout(1200)
@@ -122,7 +115,12 @@ def test_layer_7b(torch, r, rope, hkv, mlp):
     torch.cuda.synchronize()
     assert bool(torch.isfinite(y).all())
     w64 = _w64(w)
-    rows = np.concatenate([np.arange(16), np.linspace(16, N - 1, 80).round().astype(np.int64)])
+    # one whole 128-row query tile of each chunk (the first tile of chunk 0,
+    # which holds rank 0's recomputed leading rows, and a tile in the middle of
+    # the second chunk's long key walk) and rows at a stride of 61, which is
+    # prime to the 32 rows of a wave, across both chunks
+    C = SH.C
+    rows = np.unique(np.concatenate([np.arange(128), C + C // 2 + np.arange(128), np.arange(128, N, 61)]))
     pos = oracle.zigzag_positions(SH.S, SH.D, r)
     # the K/V rows this rank wrote into the gathered buffers
     k_loc, v_loc = oracle.local_kv(x[rows], w64, SH.H, SH.Dh, SH.eps, pos[rows], rope, Hkv=SH.kv_heads)

@@ -198,6 +198,15 @@ tsp_status check_mlp_bwd_shape(const tsp_shape *s) {
   if ((s->S / s->D) % 64 != 0) return fail(TSP_ERR_UNSUPPORTED, "S/D=%lld must be a multiple of 64", (long long)(s->S / s->D));
   if ((int64_t)s->F * s->h >= (int64_t(1) << 31) / 2)
     return fail(TSP_ERR_UNSUPPORTED, "F*h=%lld is too large", (long long)s->F * s->h);
+  // The layout passes put 64 rows of a matrix in one grid row (at most 65535
+  // grid rows), and the products over K = tokens address 256 rows of N
+  // tokens with 32-bit byte offsets: N, F and h are bounded here, before
+  // anything is enqueued.
+  const int64_t N = s->S / s->D, kMaxRows = int64_t(65535) * 64;
+  if (N > kMaxRows || 256 * N * 2 >= (int64_t(1) << 31))
+    return fail(TSP_ERR_UNSUPPORTED, "S/D=%lld is too large for the MLP backward", (long long)N);
+  if (s->F > kMaxRows || s->h > kMaxRows)
+    return fail(TSP_ERR_UNSUPPORTED, "F=%d or h=%d is too large for the MLP backward", s->F, s->h);
   return TSP_OK;
 }
 

@@ -388,8 +388,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   constexpr int TB = kBwdQ * G::ROWB;
   // Q (ROW), Q (TR), dO (ROW), dO (TR), then the rows' statistics and positions
   __shared__ __attribute__((aligned(1024))) unsigned char smem[4][TB];
-  __shared__ float lse_s[kBwdQ], dlt_s[kBwdQ];
-  __shared__ int pos_s[kBwdQ];
+  // read as float4 / int4 below, so 16-byte alignment is part of the layout
+  __shared__ __attribute__((aligned(16))) float lse_s[kBwdQ];
+  __shared__ __attribute__((aligned(16))) float dlt_s[kBwdQ];
+  __shared__ __attribute__((aligned(16))) int pos_s[kBwdQ];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const FragOff<DH> fo = frag_off<DH>(lane);
