@@ -35,8 +35,10 @@
  *  - 'stream' is a hipStream_t passed as void* (NULL = default stream). All
  *    work is enqueued on it asynchronously; the call returns before it runs.
  *  - The caller owns every buffer; the library allocates no device memory and
- *    keeps no pointer after it returns. Buffers must stay valid until the
- *    enqueued work has finished.
+ *    keeps no pointer after it returns (its only device memory of its own is
+ *    the static scratch array of tsp_zigzag_attn_bwd_noalloc, 8 MiB per GPU,
+ *    part of the loaded library). Buffers must stay valid until the enqueued
+ *    work has finished.
  *  - dtype TSP_BF16: weights, gains, x of tsp_mlp_ring, Q/K/V, O and the MLP
  *    hidden activations are bf16; the residual stream x/h1/y of the layer is
  *    fp32; every product accumulates in fp32. In attention the probabilities
@@ -239,6 +241,21 @@ tsp_status tsp_mlp_ring(const tsp_shape *shape, const void *x, const void *const
 tsp_status tsp_zigzag_attn_bwd(const tsp_shape *shape, const void *q, const void *k, const void *v,
                                const void *dout, float *dq, float *dk, float *dv, void *ws,
                                size_t ws_bytes, void *stream);
+
+/* tsp_zigzag_attn_bwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation, arguments and errors, but the row
+ * statistics live in a static device array of the library (8 MiB per GPU,
+ * reserved from the library's load until the process ends) instead of a
+ * caller's workspace; it allocates nothing. Limit: H * S/D <= 1048576 (the
+ * 7B shape at 128K tokens and D = 8 uses half); larger shapes return
+ * TSP_ERR_UNSUPPORTED with nothing enqueued. The stream's device must be
+ * the current device (else TSP_ERR_INVALID_ARG). All calls on one GPU share
+ * its array, and each call writes every entry it later reads, so nothing
+ * carries over between calls; calls that overlap in time on one GPU (two
+ * streams, two threads) race on it and must be serialised by the caller. */
+tsp_status tsp_zigzag_attn_bwd_noalloc(const tsp_shape *shape, const void *q, const void *k, const void *v,
+                                       const void *dout, float *dq, float *dk, float *dv, void *stream);
 
 /* tsp_zigzag_attn for the backward's use: bf16 inputs (else
  * TSP_ERR_UNSUPPORTED), plain q, o in fp32 [S/D][H][Dh], and also lse

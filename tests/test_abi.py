@@ -259,6 +259,34 @@ def test_attn_bwd_workspace_and_errors():
     assert call(shape=_shape(dtype="bf16", Dh=32, H=8))[0] == tsp.TSP_ERR_UNSUPPORTED
 
 
+def test_attn_bwd_noalloc_errors():
+    """The entry point without a workspace checks every argument, and the size
+    of its static scratch, before it looks the scratch up or enqueues
+    anything (so these run without a GPU)."""
+    s = _shape(dtype="bf16")
+    q, k, v, do = (FAKE + (i << 32) for i in range(4))
+    dq, dk, dv = (FAKE + ((5 + i) << 32) for i in range(3))
+
+    def call(shape=s, **kw):
+        a = dict(q=q, k=k, v=v, do=do, dq=dq, dk=dk, dv=dv)
+        a.update(kw)
+        with pytest.raises(tsp.TspError) as ei:
+            tsp.tsp_zigzag_attn_bwd_noalloc(shape, a["q"], a["k"], a["v"], a["do"], a["dq"], a["dk"], a["dv"],
+                                            stream=0)
+        return ei.value.status, tsp.lib().tsp_last_error()
+
+    st, msg = call(do=None)
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"dout is NULL" in msg
+    st, msg = call(dk=k + 4096)
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"overlap" in msg
+    # H * S/D above 1048576 statistics: the 8 MiB array cannot hold them
+    big = tsp.make_shape(524288, 8, 0, 4096, 32, 128, 16384, dtype="bf16")
+    st, msg = call(shape=big, q=FAKE, k=FAKE + (1 << 40), v=FAKE + (2 << 40), do=FAKE + (3 << 40),
+                   dq=FAKE + (4 << 40), dk=FAKE + (5 << 40), dv=FAKE + (6 << 40))
+    assert st == tsp.TSP_ERR_UNSUPPORTED and b"static" in msg
+    assert call(shape=_shape(dtype="bf16", Dh=32, H=8))[0] == tsp.TSP_ERR_UNSUPPORTED
+
+
 def test_attn_lse_entry_points_errors():
     sb, sf = _shape(dtype="bf16"), _shape(dtype="f32")
     q, k, v, o, lse, do = (FAKE + (i << 32) for i in range(6))

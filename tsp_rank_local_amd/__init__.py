@@ -18,8 +18,8 @@ import numpy as np
 __all__ = [
     "TspError", "TspShape", "TspLayerWeights", "lib", "make_shape", "workspace_size",
     "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_zigzag_attn_ex", "tsp_mlp_ring",
-    "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_zigzag_attn_lse", "tsp_zigzag_attn_bwd_lse", "tsp_layer_fwd",
-    "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z", "profile_enable", "profile_reset", "profile_read",
+    "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_zigzag_attn_bwd_noalloc", "tsp_zigzag_attn_lse",
+    "tsp_zigzag_attn_bwd_lse", "tsp_layer_fwd", "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z", "profile_enable", "profile_reset", "profile_read",
     "TSP_F32", "TSP_BF16", "TSP_ATTN_Q_LOG2_SCALED", "TSP_PHASE_KV", "TSP_PHASE_REST", "TSP_PHASE_ALL",
     "TSP_WS_MLP", "TSP_WS_LAYER", "TSP_WS_MLP_BWD", "TSP_WS_ATTN_BWD", "TSP_MLP_GELU", "TSP_MLP_SWIGLU", "MLP_KINDS",
     "KERNEL_CLASSES", "EXPORTED_SYMBOLS",
@@ -42,8 +42,8 @@ KERNEL_CLASSES = {"rmsnorm": 0, "qkv": 1, "attention": 2, "outproj": 3, "mlp_up"
 EXPORTED_SYMBOLS = [
     "tsp_status_string", "tsp_last_error", "tsp_abi_version", "tsp_workspace_size",
     "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_zigzag_attn_ex", "tsp_mlp_ring",
-    "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_zigzag_attn_lse", "tsp_zigzag_attn_bwd_lse", "tsp_layer_fwd",
-    "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z", "tsp_profile_enable", "tsp_profile_reset", "tsp_profile_read",
+    "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_zigzag_attn_bwd_noalloc", "tsp_zigzag_attn_lse",
+    "tsp_zigzag_attn_bwd_lse", "tsp_layer_fwd", "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z", "tsp_profile_enable", "tsp_profile_reset", "tsp_profile_read",
 ]
 
 
@@ -93,6 +93,7 @@ def lib() -> ctypes.CDLL:
     L.tsp_mlp_ring_bwd.argtypes = [shp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, ctypes.POINTER(vp),
                                    ctypes.POINTER(vp), vp, sz, vp]
     L.tsp_zigzag_attn_bwd.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.tsp_zigzag_attn_bwd_noalloc.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.tsp_zigzag_attn_lse.argtypes = [shp, vp, vp, vp, vp, vp, vp]
     L.tsp_mlp_ring_z.argtypes = [shp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp, sz, vp]
     L.tsp_mlp_ring_bwd_z.argtypes = [shp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp,
@@ -105,7 +106,8 @@ def lib() -> ctypes.CDLL:
     L.tsp_profile_reset.restype = None
     L.tsp_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     for name in ("tsp_workspace_size", "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn",
-                 "tsp_zigzag_attn_ex", "tsp_mlp_ring", "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_layer_fwd",
+                 "tsp_zigzag_attn_ex", "tsp_mlp_ring", "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd",
+                 "tsp_zigzag_attn_bwd_noalloc", "tsp_layer_fwd",
                  "tsp_zigzag_attn_lse", "tsp_zigzag_attn_bwd_lse", "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z",
                  "tsp_profile_read"):
         getattr(L, name).restype = ctypes.c_int
@@ -194,6 +196,11 @@ def tsp_zigzag_attn_bwd(shape: TspShape, q, k, v, dout, dq, dk, dv, ws, ws_bytes
         ws_bytes = ws.numel() * ws.element_size()
     _check(lib().tsp_zigzag_attn_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq),
                                      _ptr(dk), _ptr(dv), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def tsp_zigzag_attn_bwd_noalloc(shape: TspShape, q, k, v, dout, dq, dk, dv, stream=None) -> None:
+    _check(lib().tsp_zigzag_attn_bwd_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq),
+                                             _ptr(dk), _ptr(dv), _stream(stream)))
 
 
 def tsp_mlp_ring_z(shape: TspShape, x, w1, w2, residual, y, z, ws, ws_bytes=None, stream=None) -> None:

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libtsp.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "rows.hip", "gemm.hip", "attention.hip", "attention_bwd.hip", "lead.hip"]
+SOURCES = ["api.cpp", "rows.hip", "gemm.hip", "attention.hip", "attention_bwd.hip", "lead.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -459,13 +459,16 @@ tsp_status tsp_zigzag_attn_lse(const tsp_shape *s, const void *q, const void *k,
   return ok();
 }
 
+// ws == nullptr with static_ws: the scratch is the library's static device
+// array (tsp_zigzag_attn_bwd_noalloc), looked up after every argument check.
 static tsp_status attn_bwd(const tsp_shape *s, const void *q, const void *k, const void *v, const float *o, const float *lse,
-                    const void *dout, float *dq, float *dk, float *dv, void *ws, size_t ws_bytes, void *stream_) {
+                    const void *dout, float *dq, float *dk, float *dv, void *ws, size_t ws_bytes, void *stream_,
+                    bool static_ws = false) {
   tsp_status st = check_attn_shape(s);
   if (st) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(dout, "dout")) ||
       (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")) ||
-      (st = check_ptr(ws, "ws")))
+      (!static_ws && (st = check_ptr(ws, "ws"))))
     return st;
   const bool given = o != nullptr || lse != nullptr;
   if (given) {
@@ -473,13 +476,18 @@ static tsp_status attn_bwd(const tsp_shape *s, const void *q, const void *k, con
     if (s->dtype != TSP_BF16) return fail(TSP_ERR_UNSUPPORTED, "the forward's statistics are taken with bf16 inputs");
   }
   const size_t need = attn_bwd_ws(s);
-  if (ws_bytes < need) return fail(TSP_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, need);
+  if (static_ws && need > tsp::kNoallocScratchBytes)
+    return fail(TSP_ERR_UNSUPPORTED,
+                "H*S/D=%lld rows of statistics need %zu bytes of scratch, more than the static %zu (H*S/D <= %zu)",
+                (long long)s->H * (s->S / s->D), need, tsp::kNoallocScratchBytes, tsp::kNoallocScratchBytes / 8);
+  if (!static_ws && ws_bytes < need) return fail(TSP_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, need);
   const int64_t N = s->S / s->D;
   const size_t e = elem_bytes(s->dtype);
   const size_t qb = (size_t)N * s->H * s->Dh, kb = (size_t)s->S * kv_heads(s) * s->Dh;
   const Range ins[] = {{q, qb * e, "q"},       {k, kb * e, "k"},   {v, kb * e, "v"},
                        {dout, qb * e, "dout"}, {o, qb * 4, "o"},   {lse, (size_t)N * s->H * 4, "lse"}};
-  const Range outs[] = {{dq, qb * 4, "dq"}, {dk, kb * 4, "dk"}, {dv, kb * 4, "dv"}, {ws, need, "ws"}};
+  const Range outs[] = {{dq, qb * 4, "dq"}, {dk, kb * 4, "dk"}, {dv, kb * 4, "dv"},
+                        {static_ws ? nullptr : ws, need, "ws"}};
   for (const Range &ro : outs) {
     for (const Range &ri : ins)
       if (overlap(ro, ri)) return fail(TSP_ERR_INVALID_ARG, "%s overlaps %s", ro.name, ri.name);
@@ -487,6 +495,12 @@ static tsp_status attn_bwd(const tsp_shape *s, const void *q, const void *k, con
       if (&r2 != &ro && overlap(ro, r2)) return fail(TSP_ERR_INVALID_ARG, "%s overlaps %s", ro.name, r2.name);
   }
   hipStream_t stream = (hipStream_t)stream_;
+  if (static_ws) {
+    const hipError_t e_ = tsp::noalloc_scratch(stream, &ws);
+    if (e_ == hipErrorInvalidDevice)
+      return fail(TSP_ERR_INVALID_ARG, "the stream's device is not the current device (or above 64)");
+    if (e_ != hipSuccess) return hip_fail(e_, "static scratch lookup");
+  }
   float *lse_ws = (float *)ws, *delta = (float *)((unsigned char *)ws + need / 2);
   TSP_LAUNCH(TSP_K_ATTN_BWD,
              tsp::launch_attention_bwd(s->dtype, q, k, v, dout, dq, dk, dv, lse_ws, delta, s->S, (int32_t)N, s->H,
@@ -499,6 +513,11 @@ static tsp_status attn_bwd(const tsp_shape *s, const void *q, const void *k, con
 tsp_status tsp_zigzag_attn_bwd(const tsp_shape *s, const void *q, const void *k, const void *v, const void *dout,
                                float *dq, float *dk, float *dv, void *ws, size_t ws_bytes, void *stream) {
   return attn_bwd(s, q, k, v, nullptr, nullptr, dout, dq, dk, dv, ws, ws_bytes, stream);
+}
+
+tsp_status tsp_zigzag_attn_bwd_noalloc(const tsp_shape *s, const void *q, const void *k, const void *v, const void *dout,
+                                       float *dq, float *dk, float *dv, void *stream) {
+  return attn_bwd(s, q, k, v, nullptr, nullptr, dout, dq, dk, dv, nullptr, 0, stream, true);
 }
 
 tsp_status tsp_zigzag_attn_bwd_lse(const tsp_shape *s, const void *q, const void *k, const void *v, const float *o,

@@ -170,6 +170,14 @@ hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const v
                                 int32_t Hkv, int32_t Dh, float scale, ZigzagMap zz, hipStream_t s,
                                 const float *o_f32 = nullptr, const float *lse_in = nullptr);
 
+// ---------------------------------------------------------------- static scratch
+// Size of the device array that tsp_zigzag_attn_bwd_noalloc uses in place of
+// a caller's workspace (one array per GPU, shared by every such call on it).
+constexpr size_t kNoallocScratchBytes = size_t(8) << 20;
+// Device address of that array on the stream's device (which must be the
+// current device); looked up once per device and kept.
+hipError_t noalloc_scratch(hipStream_t stream, void **addr);
+
 // ---------------------------------------------------------------- timing
 // Bracket a launch with events when profiling is on (api.cpp).
 void prof_begin(int kclass, hipStream_t s);
