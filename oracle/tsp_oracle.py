@@ -57,6 +57,18 @@ Readings where the pages are silent (each is restated where it is used):
      tokens' contribution to each shard's gradient, and the D ranks'
      contributions add up to the gradient over the whole sequence (the sum a
      ring would carry back to the shard's owner).
+  R12 backward of the whole layer (an optional extension, like R10): the
+     gradients of the pre-norm layer (R6) by the chain rule, on one rank in
+     two halves around the exchange that returns key/value gradients to
+     their owners. First half: the rank recomputes its own forward from x,
+     then takes the MLP ring backward (R10), the second RMSNorm's backward,
+     the output projection's backward and the attention backward (R11); its
+     K/V gradients cover every key row. Second half, once the rank holds the
+     summed gradients of its own K/V rows: the QKV projection's backward and
+     the first RMSNorm's backward. Weight and gain gradients are the rank's
+     own tokens' contribution (the D ranks' contributions add up to the
+     gradient over the whole sequence). No rotation, grouped K/V heads as in
+     R8, the pages' GELU MLP only.
   R11 backward of the zigzag attention (an optional extension, like R10):
      the gradients of causal_attention by the chain rule through the
      softmax. A rank's queries give their own dQ rows; its dK and dV are its
@@ -87,6 +99,10 @@ __all__ = [
     "causal_attention_lse",
     "causal_attention_backward",
     "mlp_backward",
+    "rms_norm_backward",
+    "layer_bwd_attn_part",
+    "layer_bwd_qkv_part",
+    "layer_backward_full",
     "layer_full",
     "layer_rows",
     "local_kv",
@@ -368,6 +384,101 @@ def mlp_backward(x, w1, w2, dy) -> dict:
         "dw1": [dW1[j * fd:(j + 1) * fd] for j in range(len(w1))],
         "dw2": [dW2[:, j * fd:(j + 1) * fd] for j in range(len(w2))],
     }
+
+
+# --------------------------------------------------------------------------
+# Layer backward (reading R12)
+# --------------------------------------------------------------------------
+def rms_norm_backward(x, g, eps: float, dout):
+    """Gradients of rms_norm (R6) for an output gradient dout, row by row.
+    With r = (mean(x^2) + eps)^(-1/2) and y_i = g_i x_i r, the derivative of
+    r is -r^3 x_k / h, so dx_k = r g_k dout_k - (r^3 x_k / h) sum_i dout_i
+    g_i x_i, and dg_i = sum over rows of dout_i x_i r. Returns (dx, dg)."""
+    x, g, dout = _f64(x), _f64(g), _f64(dout)
+    h = x.shape[-1]
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    dx = r * g * dout - (r ** 3) * x * np.sum(dout * g * x, axis=-1, keepdims=True) / h
+    dg = np.sum(dout * x * r, axis=0)
+    return dx, dg
+
+
+def layer_bwd_attn_part(x_local, pos, w: dict, k_full, v_full, dy, H: int, Dh: int, eps: float, scale: float,
+                        Hkv: int | None = None) -> dict:
+    """First half of a rank's layer backward (reading R12).
+
+    x_local: [n, h] the rank's tokens, pos: [n] their global positions,
+    k_full, v_full: [S, Hkv, Dh] the gathered K/V (the rank's own rows
+    included), dy: [n, h] gradient of the layer output. The rank's forward is
+    recomputed (xn, q, o, h1, hn); then, in reverse: the MLP branch
+    (mlp_backward on hn), the second RMSNorm (dh1 = dy + its backward), the
+    output projection (do = dh1 W_O, dW_O = dh1^T o), the attention
+    (causal_attention_backward). Returns dh1, dq [n, H, Dh], dk, dv
+    [S, Hkv, Dh] (this rank's contribution to every key row), dwo, dw1, dw2
+    (shard lists, this rank's contribution), dg_mlp, and the recomputed xn.
+    """
+    x = _f64(x_local)
+    n, h = x.shape
+    Hkv = H if Hkv is None else Hkv
+    wq, _, _, w_o = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh, Hkv)
+    xn = rms_norm(x, w["g_attn"], eps)
+    q = (xn @ wq.T).reshape(n, H, Dh)
+    o = causal_attention(q, k_full, v_full, pos, scale)
+    o2 = o.reshape(n, H * Dh)
+    h1 = x + o2 @ w_o.T
+    hn = rms_norm(h1, w["g_mlp"], eps)
+    mb = mlp_backward(hn, w["w1"], w["w2"], dy)
+    dhn_h1, dg_mlp = rms_norm_backward(h1, w["g_mlp"], eps, mb["dx"])
+    dh1 = _f64(dy) + dhn_h1
+    do = dh1 @ w_o
+    dWo = dh1.T @ o2
+    hd = w_o.shape[1] // len(w["wo"])
+    ab = causal_attention_backward(q, k_full, v_full, pos, scale, do.reshape(n, H, Dh))
+    return {"dh1": dh1, "dq": ab["dq"], "dk": ab["dk"], "dv": ab["dv"],
+            "dwo": [dWo[:, j * hd:(j + 1) * hd] for j in range(len(w["wo"]))],
+            "dw1": mb["dw1"], "dw2": mb["dw2"], "dg_mlp": dg_mlp, "xn": xn, "h1": h1}
+
+
+def layer_bwd_qkv_part(x_local, w: dict, dh1, dq, dk_loc, dv_loc, H: int, Dh: int, eps: float,
+                       Hkv: int | None = None) -> dict:
+    """Second half of a rank's layer backward (reading R12), once the rank
+    holds the summed gradients dk_loc, dv_loc [n, Hkv, Dh] of its own K/V
+    rows. With xn = RMSNorm(x) recomputed: dxn = dq W_Q + dk W_K + dv W_V,
+    each shard's gradient dW_QKV,j = [dq_j | dk_j | dv_j]^T xn (its Q, K and V
+    rows, as in the weights' layout), and dx = dh1 + the first RMSNorm's
+    backward of dxn. Returns dx [n, h], dwqkv (shard list, this rank's
+    contribution) and dg_attn."""
+    x = _f64(x_local)
+    n, h = x.shape
+    Hkv = H if Hkv is None else Hkv
+    D = len(w["wqkv"])
+    wq, wk, wv, _ = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh, Hkv)
+    xn = rms_norm(x, w["g_attn"], eps)
+    dq2, dk2, dv2 = _f64(dq).reshape(n, H * Dh), _f64(dk_loc).reshape(n, Hkv * Dh), _f64(dv_loc).reshape(n, Hkv * Dh)
+    dxn = dq2 @ wq + dk2 @ wk + dv2 @ wv
+    hq, hk = (H // D) * Dh, (Hkv // D) * Dh
+    dwqkv = [np.concatenate([dq2[:, j * hq:(j + 1) * hq].T @ xn, dk2[:, j * hk:(j + 1) * hk].T @ xn,
+                             dv2[:, j * hk:(j + 1) * hk].T @ xn], axis=0) for j in range(D)]
+    dx_n, dg_attn = rms_norm_backward(x, w["g_attn"], eps, dxn)
+    return {"dx": _f64(dh1) + dx_n, "dwqkv": dwqkv, "dg_attn": dg_attn}
+
+
+def layer_backward_full(x, w: dict, dy, H: int, Dh: int, eps: float, scale: float, Hkv: int | None = None) -> dict:
+    """Backward of the unsharded layer over the whole sequence (reading R12
+    with one rank: its K/V rows are all the rows, so the first half's K/V
+    gradients are already the full ones). x, dy: [S, h] in global order.
+    Returns dx, dwqkv, dwo, dw1, dw2 (shard lists) and dg_attn, dg_mlp."""
+    x = _f64(x)
+    S, h = x.shape
+    Hkv = H if Hkv is None else Hkv
+    _, wk, wv, _ = unshard_attention_weights(w["wqkv"], w["wo"], H, Dh, Hkv)
+    pos = np.arange(S)
+    xn = rms_norm(x, w["g_attn"], eps)
+    k = (xn @ wk.T).reshape(S, Hkv, Dh)
+    v = (xn @ wv.T).reshape(S, Hkv, Dh)
+    a = layer_bwd_attn_part(x, pos, w, k, v, dy, H, Dh, eps, scale, Hkv)
+    b = layer_bwd_qkv_part(x, w, a["dh1"], a["dq"], a["dk"], a["dv"], H, Dh, eps, Hkv)
+    return {"dx": b["dx"], "dwqkv": b["dwqkv"], "dwo": a["dwo"], "dw1": a["dw1"], "dw2": a["dw2"],
+            "dg_attn": b["dg_attn"], "dg_mlp": a["dg_mlp"]}
 
 
 # --------------------------------------------------------------------------

@@ -783,3 +783,165 @@ def test_synth_deterministic_and_bf16_rounding():
     big = synth.normal(((1 << 23) + 5,), 3, 1)  # several chunks
     assert np.array_equal(big[: 1 << 22], synth.normal((1 << 22,), 3, 1))  # chunked streams
     assert abs(float(big.mean())) < 2e-3 and abs(float(big.std()) - 1) < 2e-3
+
+
+# ---------------------------------------------------------------- layer backward (R12)
+def test_rms_norm_backward_vs_torch_autograd():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((6, 24))
+    g = 1 + 0.2 * rng.standard_normal(24)
+    dout = rng.standard_normal((6, 24))
+    tx, tg = torch.from_numpy(x).requires_grad_(True), torch.from_numpy(g).requires_grad_(True)
+    (F.rms_norm(tx, (24,), tg, eps=1e-5) * torch.from_numpy(dout)).sum().backward()
+    dx, dg = oracle.rms_norm_backward(x, g, 1e-5, dout)
+    assert np.allclose(dx, tx.grad.numpy(), atol=1e-13)
+    assert np.allclose(dg, tg.grad.numpy(), atol=1e-13)
+    # a constant row is a fixed point of the norm's direction: the gradient
+    # along x itself vanishes when eps = 0 (scale invariance)
+    xc = rng.standard_normal((1, 24))
+    dxc, _ = oracle.rms_norm_backward(xc, np.ones(24), 0.0, xc)
+    assert abs(float((dxc * xc).sum())) < 1e-12
+
+
+def _torch_layer_grads(x, m, dy, H, Dh, eps, scale, Hkv):
+    """torch fp64 autograd of the layer (grouped K/V heads as repeated heads
+    inside scaled_dot_product_attention's enable_gqa)."""
+    t = {k: torch.from_numpy(v).requires_grad_(True) for k, v in m.items()}
+    tx = torch.from_numpy(x).requires_grad_(True)
+    S, h = x.shape
+    a = F.rms_norm(tx, (h,), t["g1"], eps=eps)
+    heads = lambda w, nh: F.linear(a, w).reshape(S, nh, Dh).permute(1, 0, 2).contiguous()  # noqa: E731
+    o = F.scaled_dot_product_attention(heads(t["wq"], H), heads(t["wk"], Hkv), heads(t["wv"], Hkv), is_causal=True,
+                                       scale=scale, enable_gqa=Hkv != H)
+    h1 = tx + F.linear(o.permute(1, 0, 2).reshape(S, h), t["wo"])
+    mm = F.rms_norm(h1, (h,), t["g2"], eps=eps)
+    y = h1 + F.linear(F.gelu(F.linear(mm, t["W1"])), t["W2"])
+    (y * torch.from_numpy(dy)).sum().backward()
+    return tx.grad.numpy(), {k: v.grad.numpy() for k, v in t.items()}
+
+
+def _layer_bwd_case(seed, S=24, D=2, H=4, Hkv=4, Dh=4, Fw=32):
+    rng = np.random.default_rng(seed)
+    h = H * Dh
+    m = dict(wq=0.3 * rng.standard_normal((h, h)), wk=0.3 * rng.standard_normal((Hkv * Dh, h)),
+             wv=0.3 * rng.standard_normal((Hkv * Dh, h)), wo=0.3 * rng.standard_normal((h, h)),
+             W1=0.3 * rng.standard_normal((Fw, h)), W2=0.3 * rng.standard_normal((h, Fw)),
+             g1=1 + 0.1 * rng.standard_normal(h), g2=1 + 0.1 * rng.standard_normal(h))
+    hq, hk = (H // D) * Dh, (Hkv // D) * Dh
+    wqkv = [np.concatenate([m["wq"][j * hq:(j + 1) * hq], m["wk"][j * hk:(j + 1) * hk],
+                            m["wv"][j * hk:(j + 1) * hk]], axis=0) for j in range(D)]
+    wo = [m["wo"][:, j * hq:(j + 1) * hq] for j in range(D)]
+    w1, w2 = _split_mlp(m["W1"], m["W2"], D)
+    w = dict(wqkv=wqkv, wo=wo, w1=w1, w2=w2, g_attn=m["g1"], g_mlp=m["g2"])
+    return rng.standard_normal((S, h)), rng.standard_normal((S, h)), w, m
+
+
+@pytest.mark.parametrize("Hkv", [4, 2])
+def test_layer_backward_vs_torch_autograd(Hkv):
+    H, Dh, eps, scale = 4, 4, 1e-5, 0.5
+    x, dy, w, m = _layer_bwd_case(32, Hkv=Hkv)
+    got = oracle.layer_backward_full(x, w, dy, H, Dh, eps, scale, Hkv)
+    gx, gm = _torch_layer_grads(x, m, dy, H, Dh, eps, scale, Hkv)
+    assert np.allclose(got["dx"], gx, atol=1e-12)
+    hq, hk = 2 * Dh, Hkv // 2 * Dh
+    dwq = np.concatenate([d[:hq] for d in got["dwqkv"]], axis=0)
+    dwk = np.concatenate([d[hq:hq + hk] for d in got["dwqkv"]], axis=0)
+    dwv = np.concatenate([d[hq + hk:] for d in got["dwqkv"]], axis=0)
+    for name, a in (("wq", dwq), ("wk", dwk), ("wv", dwv), ("wo", np.concatenate(got["dwo"], axis=1)),
+                    ("W1", np.concatenate(got["dw1"], axis=0)), ("W2", np.concatenate(got["dw2"], axis=1)),
+                    ("g1", got["dg_attn"]), ("g2", got["dg_mlp"])):
+        assert np.allclose(a, gm[name], atol=1e-12), name
+
+
+def test_layer_backward_finite_differences():
+    """Central differences of L = sum(dy * y), y from oracle.layer_full (the
+    forward, pinned on its own), in entries of x, the QKV and out-proj shards,
+    W1 and both gains."""
+    H, Dh, eps, scale = 4, 4, 1e-5, 0.5
+    x, dy, w, _ = _layer_bwd_case(33, S=12)
+    got = oracle.layer_backward_full(x, w, dy, H, Dh, eps, scale)
+
+    def loss(x_, w_):
+        return float((dy * oracle.layer_full(x_, w_, H, Dh, eps, scale)["y"]).sum())
+
+    e = 1e-6
+
+    def fd(path, idx):
+        wp = {k: ([a.copy() for a in v] if isinstance(v, list) else v.copy()) for k, v in w.items()}
+        wm = {k: ([a.copy() for a in v] if isinstance(v, list) else v.copy()) for k, v in w.items()}
+        if path == "x":
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += e
+            xm[idx] -= e
+            return (loss(xp, w) - loss(xm, w)) / (2 * e)
+        key, j = path
+        tp = wp[key][j] if j is not None else wp[key]
+        tm = wm[key][j] if j is not None else wm[key]
+        tp[idx] += e
+        tm[idx] -= e
+        return (loss(x, wp) - loss(x, wm)) / (2 * e)
+
+    for idx in [(0, 0), (5, 7), (11, 15)]:
+        assert got["dx"][idx] == pytest.approx(fd("x", idx), abs=1e-7)
+    for j, idx in [(0, (0, 3)), (1, (9, 2)), (1, (23, 14))]:  # Q, K and V rows of the shards
+        assert got["dwqkv"][j][idx] == pytest.approx(fd(("wqkv", j), idx), abs=1e-7)
+    assert got["dwo"][1][(4, 5)] == pytest.approx(fd(("wo", 1), (4, 5)), abs=1e-7)
+    assert got["dw1"][0][(3, 9)] == pytest.approx(fd(("w1", 0), (3, 9)), abs=1e-7)
+    assert got["dg_attn"][6] == pytest.approx(fd(("g_attn", None), (6,)), abs=1e-7)
+    assert got["dg_mlp"][10] == pytest.approx(fd(("g_mlp", None), (10,)), abs=1e-7)
+
+
+@pytest.mark.parametrize("D,Hkv", [(4, 4), (2, 2)])
+def test_layer_backward_rank_halves_compose(D, Hkv):
+    """Reading R12 on D ranks: every rank runs the first half on its own rows
+    (the gathered K/V of the full forward), the ranks' K/V gradients are
+    summed and each rank takes the rows of its own positions into the second
+    half. Every rank's dx rows are the full backward's at its positions, and
+    the ranks' weight and gain contributions add up to the full gradients."""
+    S, H, Dh, eps, scale = 32, 4, 4, 1e-5, 0.5
+    x, dy, w, _ = _layer_bwd_case(34, S=S, D=D, Hkv=Hkv)
+    full = oracle.layer_backward_full(x, w, dy, H, Dh, eps, scale, Hkv)
+    fwd = oracle.layer_full(x, w, H, Dh, eps, scale, Hkv=Hkv)
+    parts = [oracle.layer_bwd_attn_part(x[p], p, w, fwd["k"], fwd["v"], dy[p], H, Dh, eps, scale, Hkv)
+             for p in (oracle.zigzag_positions(S, D, r) for r in range(D))]
+    dk = sum(a["dk"] for a in parts)
+    dv = sum(a["dv"] for a in parts)
+    acc = {k: [np.zeros_like(t) for t in full[k]] for k in ("dwqkv", "dwo", "dw1", "dw2")}
+    dg1, dg2 = np.zeros_like(full["dg_attn"]), np.zeros_like(full["dg_mlp"])
+    for r, a in enumerate(parts):
+        pos = oracle.zigzag_positions(S, D, r)
+        b = oracle.layer_bwd_qkv_part(x[pos], w, a["dh1"], a["dq"], dk[pos], dv[pos], H, Dh, eps, Hkv)
+        assert np.allclose(b["dx"], full["dx"][pos], atol=1e-12)
+        for k, src in (("dwqkv", b), ("dwo", a), ("dw1", a), ("dw2", a)):
+            for j in range(D):
+                acc[k][j] += src[k][j]
+        dg1 += b["dg_attn"]
+        dg2 += a["dg_mlp"]
+    for k in acc:
+        for j in range(D):
+            assert np.allclose(acc[k][j], full[k][j], atol=1e-12), k
+    assert np.allclose(dg1, full["dg_attn"], atol=1e-12)
+    assert np.allclose(dg2, full["dg_mlp"], atol=1e-12)
+
+
+def test_layer_backward_planted_mistakes_are_caught(monkeypatch):
+    """An RMSNorm backward without its mean term, or K and V gradients swapped
+    in the QKV half, miss torch's gradients."""
+    H, Dh, eps, scale = 4, 4, 1e-5, 0.5
+    x, dy, w, m = _layer_bwd_case(35)
+    gx, gm = _torch_layer_grads(x, m, dy, H, Dh, eps, scale, 4)
+    good = oracle.rms_norm_backward
+
+    def no_mean(x_, g_, eps_, dout):
+        dx_, dg_ = good(x_, g_, eps_, dout)
+        r = 1.0 / np.sqrt(np.mean(np.asarray(x_) ** 2, axis=-1, keepdims=True) + eps_)
+        return r * np.asarray(g_) * np.asarray(dout), dg_
+
+    monkeypatch.setattr(oracle.tsp_oracle, "rms_norm_backward", no_mean)
+    assert not np.allclose(oracle.layer_backward_full(x, w, dy, H, Dh, eps, scale)["dx"], gx, atol=1e-6)
+    monkeypatch.setattr(oracle.tsp_oracle, "rms_norm_backward", good)
+    part = oracle.tsp_oracle.layer_bwd_qkv_part
+    swapped = lambda x_, w_, dh1, dq, dk, dv, *a, **k: part(x_, w_, dh1, dq, dv, dk, *a, **k)  # noqa: E731
+    monkeypatch.setattr(oracle.tsp_oracle, "layer_bwd_qkv_part", swapped)
+    bad = oracle.tsp_oracle.layer_backward_full(x, w, dy, H, Dh, eps, scale)
+    assert not np.allclose(bad["dx"], gx, atol=1e-6)
