@@ -198,6 +198,8 @@ KTRACE_WORKLOADS = {
     # workload -> (title, summary file, bench arguments)
     "layer": ("one 7B TSP layer forward (rank 0 of D=8, S=131072, 16384 local tokens, bf16)",
               "attn_layer7b_kernel_stats.md", ""),
+    "layer_bwd": ("one 7B TSP layer backward, both halves (rank 0 of D=8, S=131072, 16384 local tokens, bf16)",
+                  "layer_bwd_7b_kernel_stats.md", "--workload layer_bwd --steps 5 --warmup 1"),
 }
 
 
@@ -221,7 +223,7 @@ def summarize_ktrace(stats_csv, bench_json, workload="layer"):
     k = b.get("kernels", {})
     lines += ["", "Same run, bench.py's HIP events on the launching stream:", ""]
     lines.append(f"- step: {b['ms_per_step']:.3f} ms, {b['value']:,.0f} local tokens/s, "
-                 f"{b['pct_bf16_mfma_peak']:.1f}% of the 2.5 PF bf16 peak over the layer")
+                 f"{b['pct_bf16_mfma_peak']:.1f}% of the 2.5 PF bf16 peak over the step")
     for name, v in k.items():
         extra = f", {v['hbm_gb_s']:.0f} GB/s of HBM traffic" if "hbm_gb_s" in v else ""
         lines.append(f"- {name}: {v['ms_per_launch']:.3f} ms per launch, {v['launches_per_step']:g} per step{extra}")
@@ -267,6 +269,8 @@ SQ_WORKLOADS = {
                  "--workload attn_bwd --steps 1 --warmup 0"),
     "mlp_bwd": ("the 7B MLP ring backward (16384 tokens, D=8)", "mlp_bwd_7b_sq_counters.txt",
                 "--workload mlp_bwd --steps 1 --warmup 0"),
+    "layer_bwd": ("the 7B layer backward, both halves (rank 0 of D=8, S=131072)", "layer_bwd_7b_sq_counters.txt",
+                  "--workload layer_bwd --steps 1 --warmup 0"),
 }
 
 
@@ -420,7 +424,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["layer", "mlp", "attn", "layers32", "mlp_bwd", "mlp_bwd_z", "attn_bwd", "attn_bwd_lse"], default="layer")
+    ap.add_argument("--workload", choices=["layer", "mlp", "attn", "layers32", "mlp_bwd", "mlp_bwd_z", "attn_bwd",
+                                           "attn_bwd_lse", "layer_bwd"], default="layer")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--rope-base", type=float, default=0.0,
                     help="rotary embedding base for the layer workloads (0 = none, the pages' model)")
@@ -476,7 +481,7 @@ def main():
     stream = torch.cuda.current_stream()
     flops = layer_flops(sh, r)
 
-    if args.workload in ("layer", "mlp", "mlp_bwd", "mlp_bwd_z"):
+    if args.workload in ("layer", "mlp", "mlp_bwd", "mlp_bwd_z", "layer_bwd"):
         w = synth.layer_weights(sh, seed=seed)
         wd = {k: ([tsp.to_device(a, "bf16") for a in v] if isinstance(v, list) else tsp.to_device(v, "bf16"))
               for k, v in w.items()}
@@ -494,6 +499,40 @@ def main():
         step_exps = sh.H * attn_pairs(sh.S, sh.D, r)
         workload = (f"tsp_layer_fwd: one 7B dense decoder layer (h=4096, 32x128 heads{kv_note}, {mlp_note} 16384, bf16) on "
                     f"rank {r} of D=8 at S=131072, 16384 local zigzag tokens")
+    elif args.workload == "layer_bwd":
+        # both halves of one rank's layer backward; the summed K/V-row
+        # gradients the second half takes are seeded values (the
+        # reduce-scatter that would deliver them is not on one GPU)
+        x = synth.activations(N, sh.h, seed=seed)
+        dy = synth.activations(N, sh.h, seed=seed, tid=synth.TID_DY)
+        k_rem, v_rem = synth.remote_kv(sh, seed=seed)
+        dkl = synth.normal((N, sh.kv_heads, sh.Dh), seed, synth.TID_DK_LOC, std=0.05)
+        dvl = synth.normal((N, sh.kv_heads, sh.Dh), seed, synth.TID_DV_LOC, std=0.05)
+        xd, dyd = tsp.to_device(x, "f32"), tsp.to_device(dy, "f32")
+        kf, vf = tsp.to_device(k_rem, "bf16"), tsp.to_device(v_rem, "bf16")
+        dkld, dvld = tsp.to_device(dkl, "f32"), tsp.to_device(dvl, "f32")
+        dkf = torch.empty((sh.S, sh.kv_heads, sh.Dh), dtype=torch.float32, device="cuda")
+        dvf = torch.empty_like(dkf)
+        dx = torch.empty((N, sh.h), dtype=torch.float32, device="cuda")
+        grads = {k: [torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in wd[k]]
+                 for k in ("wqkv", "wo", "w1", "w2")}
+        grads.update(g_attn=torch.empty(sh.h, dtype=torch.float32, device="cuda"),
+                     g_mlp=torch.empty(sh.h, dtype=torch.float32, device="cuda"))
+        ws = torch.empty(tsp.workspace_size(shape, tsp.TSP_WS_LAYER_BWD), dtype=torch.uint8, device="cuda")
+
+        def step():
+            tsp.tsp_layer_bwd(shape, wd, xd, kf, vf, dyd, dkf, dvf, None, None, None, grads, tsp.TSP_BWD_ATTN, ws)
+            tsp.tsp_layer_bwd(shape, wd, xd, None, None, None, None, None, dkld, dvld, dx, grads, tsp.TSP_BWD_QKV,
+                              ws)
+        # algorithmic: the chain rule's products only, twice each forward GEMM
+        # (input and weight gradient) and 2.5x the attention; the forward
+        # recomputation (RMSNorms, Q, attention with its statistics, output
+        # projection, the MLP's Z) is extra work, not counted
+        step_flops = 2.0 * (flops["qkv"] + flops["outproj"] + flops["mlp"]) + 2.5 * flops["attention"]
+        step_exps = 2 * sh.H * attn_pairs(sh.S, sh.D, r)
+        workload = (f"tsp_layer_bwd: backward of one 7B dense decoder layer (h=4096, 32x128 heads{kv_note}, FFN 16384, "
+                    f"bf16) on rank {r} of D=8 at S=131072, 16384 local zigzag tokens, both halves (forward "
+                    f"recomputed from x; dx, dK/dV of every key row and all weight and gain gradients in fp32)")
     elif args.workload == "mlp":
         x = synth.activations(N, sh.h, seed=2, dtype="bf16")
         xd = tsp.to_device(x, "bf16")
@@ -685,7 +724,14 @@ def main():
             kernels[cls]["hbm_bytes"] = nbytes
             kernels[cls]["hbm_gb_s"] = nbytes / (kernels[cls]["ms_per_launch"] * 1e-3) / 1e9
     roofline = None
-    if "attention" in kernels:
+    if args.workload == "layer_bwd" and "attn_bwd" in kernels:
+        # the attention backward: 4.40e13 of the step's 5.72e13 algorithmic flops
+        t_b = kernels["attn_bwd"]["ms_per_launch"] * 1e-3
+        achieved = 2.5 * flops["attention"] / t_b / 1e12
+        roofline = {"kernel": "attn_bwd_stats_kernel + attn_bwd_dq_kernel + attn_bwd_dkv_kernel<128>",
+                    "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                    "frac": achieved * 1e12 / PEAK_BF16, "traffic": None}
+    elif "attention" in kernels:
         t_attn = kernels["attention"]["ms_per_launch"] * 1e-3
         achieved = flops["attention"] / t_attn / 1e12
         roofline = {"kernel": "attn_bf16_kernel<128>", "bound": "mfma", "achieved": achieved,

@@ -145,7 +145,24 @@ typedef struct {
 enum { TSP_PHASE_KV = 1, TSP_PHASE_REST = 2, TSP_PHASE_ALL = 3 };
 
 /* Workspace kinds for tsp_workspace_size. */
-enum { TSP_WS_MLP = 0, TSP_WS_LAYER = 1, TSP_WS_MLP_BWD = 2, TSP_WS_ATTN_BWD = 3 };
+enum { TSP_WS_MLP = 0, TSP_WS_LAYER = 1, TSP_WS_MLP_BWD = 2, TSP_WS_ATTN_BWD = 3, TSP_WS_LAYER_BWD = 4 };
+
+/* Phases of tsp_layer_bwd: the two halves of a rank's layer backward on
+ * either side of the exchange that returns key/value gradients to the ranks
+ * that own those rows. */
+enum { TSP_BWD_ATTN = 1, TSP_BWD_QKV = 2, TSP_BWD_ALL = 3 };
+
+/* Gradients of one layer's weights, laid out as tsp_layer_weights, fp32:
+ * g_attn, g_mlp [h]; wqkv, wo, w1, w2 (host) arrays of D device pointers with
+ * the shard shapes of tsp_layer_weights. */
+typedef struct {
+  float *g_attn;
+  float *g_mlp;
+  float *const *wqkv;
+  float *const *wo;
+  float *const *w1;
+  float *const *w2;
+} tsp_layer_grads;
 
 /* Kernel classes for the optional launch timing. */
 enum {
@@ -160,7 +177,8 @@ enum {
   TSP_K_BWD_GEMM = 8,  /* the products of tsp_mlp_ring_bwd */
   TSP_K_TRANSPOSE = 9, /* the layout changes of tsp_mlp_ring_bwd */
   TSP_K_ATTN_BWD = 10, /* the launches of tsp_zigzag_attn_bwd */
-  TSP_K_COUNT = 11
+  TSP_K_ROWS_BWD = 11, /* the RMSNorm backward and column packing of tsp_layer_bwd */
+  TSP_K_COUNT = 12
 };
 
 /* Static text for a status code. */
@@ -174,7 +192,8 @@ int tsp_abi_version(void);
 
 /* Bytes of scratch the call 'which' (TSP_WS_MLP for tsp_mlp_ring,
  * TSP_WS_LAYER for tsp_layer_fwd, TSP_WS_MLP_BWD for tsp_mlp_ring_bwd,
- * TSP_WS_ATTN_BWD for tsp_zigzag_attn_bwd) needs for this shape. */
+ * TSP_WS_ATTN_BWD for tsp_zigzag_attn_bwd, TSP_WS_LAYER_BWD for
+ * tsp_layer_bwd) needs for this shape. */
 tsp_status tsp_workspace_size(const tsp_shape *shape, int which, size_t *bytes);
 
 /* Zigzag token ownership (reading above; the pages name a zigzag partition
@@ -347,6 +366,54 @@ tsp_status tsp_mlp_ring_bwd_z(const tsp_shape *shape, const void *x, const void 
 tsp_status tsp_layer_fwd(const tsp_shape *shape, const tsp_layer_weights *w, const float *x,
                          void *k_full, void *v_full, float *y, unsigned phases, void *ws,
                          size_t ws_bytes, void *stream);
+
+/* Backward of tsp_layer_fwd on rank r (an optional extension, like
+ * tsp_mlp_ring_bwd: the pages report training throughput, the ageofai.tools
+ * review "Zyphra TSP: 2.6x Faster AI Training Review", key features and
+ * benefits, but describe no backward). It keeps the forward's schedule (the
+ * zubnet.ai news item, paragraph 2): the rank applies the weight shards it
+ * receives to its own tokens and sums the MLP ring's contributions itself;
+ * the only new exchange is the reverse of the K/V all-gather, a
+ * reduce-scatter that returns each key/value row's gradient to its owner,
+ * between the two phases. Chain rule on the pre-norm layer, forward
+ * recomputed from x:
+ *  TSP_BWD_ATTN: xn = RMSNorm(x) g_attn, Q, attention (o, and its row
+ *    statistics), h1 = x + o W_O^T, hn = RMSNorm(h1) g_mlp; then the MLP
+ *    ring backward of tsp_mlp_ring_bwd on hn and dy, the second RMSNorm's
+ *    backward, dh1 = dy + that; do = dh1 W_O, dW_O = dh1^T o; the attention
+ *    backward of tsp_zigzag_attn_bwd_lse, giving dq (kept in ws) and this
+ *    rank's contribution dk_full, dv_full to every key/value row.
+ *  TSP_BWD_QKV, once dk_loc, dv_loc hold the summed gradients of the rank's
+ *    own K/V rows: dxn = [dq | dk | dv] W_QKV over the shards,
+ *    dW_QKV,j = [dq_j | dk_j | dv_j]^T xn, and dx = dh1 + the first
+ *    RMSNorm's backward of dxn.
+ * Weight and gain gradients are this rank's tokens' contribution (the D
+ * ranks' contributions add up to the gradient over the whole sequence).
+ * Supported: GELU MLP, no rotary embedding, S/D a multiple of 64, h <= 8192
+ * (else TSP_ERR_UNSUPPORTED, nothing enqueued).
+ *  x, dy: [S/D][h] fp32, local rows in zigzag order (dy: gradient of y).
+ *  k_full, v_full: [S][Hkv][Dh] (dtype), the gathered K/V of the forward.
+ *  dk_full, dv_full: [S][Hkv][Dh] fp32, fully written by TSP_BWD_ATTN.
+ *  dk_loc, dv_loc: [S/D][Hkv][Dh] fp32, read by TSP_BWD_QKV: row t is the
+ *    gradient of the K/V row at the rank's position pos(t), summed over the
+ *    D ranks. With D = 1 they may be dk_full and dv_full themselves, and
+ *    TSP_BWD_ALL runs both phases in one call (D = 1 only).
+ *  dx: [S/D][h] fp32, written by TSP_BWD_QKV.
+ *  grads: written: wo, w1, w2, g_mlp by TSP_BWD_ATTN; wqkv, g_attn by
+ *    TSP_BWD_QKV. Pointers a phase does not touch may be NULL.
+ *  ws: device scratch of at least tsp_workspace_size(TSP_WS_LAYER_BWD)
+ *    bytes; TSP_BWD_QKV reads what TSP_BWD_ATTN left there (dh1 and dq),
+ *    so both phases use the same ws.
+ * Rounding (bf16): xn, Q, o (for the products), hn, dy (for the MLP
+ * products), dh1 (for its products), do, and dq/dk/dv (for the QKV products)
+ * are rounded once to bf16; RMSNorm statistics, the residual-stream
+ * gradients dh1 and dx and all accumulation are fp32. Outputs must not
+ * overlap inputs or each other. */
+tsp_status tsp_layer_bwd(const tsp_shape *shape, const tsp_layer_weights *w, const float *x,
+                         const void *k_full, const void *v_full, const float *dy, float *dk_full,
+                         float *dv_full, const float *dk_loc, const float *dv_loc, float *dx,
+                         const tsp_layer_grads *grads, unsigned phases, void *ws, size_t ws_bytes,
+                         void *stream);
 
 /* Optional launch timing. When enabled, every kernel the library enqueues is
  * bracketed by HIP events recorded on the same stream; tsp_profile_read

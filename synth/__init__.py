@@ -34,6 +34,8 @@ TID_K_REMOTE = 20
 TID_V_REMOTE = 21
 TID_Q = 22
 TID_DY = 30  # gradient arriving at a branch output (backward tests)
+TID_DK_LOC = 31  # summed K/V-row gradients handed to a layer backward's second half
+TID_DV_LOC = 32
 
 
 @dataclasses.dataclass(frozen=True)

@@ -362,3 +362,73 @@ def test_zigzag_index_errors():
     pos = (ctypes.c_int32 * 4)()
     assert tsp.lib().tsp_zigzag_index_host(16, 4, 1, pos) == 0
     assert list(pos) == [2, 3, 12, 13]
+
+
+def test_layer_bwd_workspace_and_errors():
+    # dh1, dq fp32 [N][h]; then the larger phase: nine [N][h] in dtype, three
+    # fp32 [N][h], W_O^T, the forward's lse [H][N], the attention backward's
+    # statistics, the gain partials and the MLP backward's scratch; or xn, xn^T,
+    # [dq|dk|dv] and its transpose, W_QKV^T, dxn, the gain partials
+    for dtype, e in (("f32", 4), ("bf16", 2)):
+        s = _shape(dtype=dtype)
+        N, h, H, F, k3 = 256, 256, 4, 1024, 3 * 256
+        part = (N // 16) * h * 4
+        mlp = (3 * F * h + 2 * h * N + 2 * F * N) * e
+        first = 9 * N * h * e + 3 * N * h * 4 + h * h * e + H * N * 4 + 2 * H * N * 4 + part + mlp
+        second = 2 * N * h * e + 2 * N * k3 * e + h * k3 * e + N * h * 4 + part
+        assert tsp.workspace_size(s, tsp.TSP_WS_LAYER_BWD) == 2 * N * h * 4 + max(first, second)
+    s = _shape(dtype="bf16")
+    need = tsp.workspace_size(s, tsp.TSP_WS_LAYER_BWD)
+    w = dict(g_attn=FAKE, g_mlp=FAKE, wqkv=[FAKE] * 4, wo=[FAKE] * 4, w1=[FAKE] * 4, w2=[FAKE] * 4)
+
+    def gl(base):
+        return [FAKE + (base << 32) + (i << 28) for i in range(4)]
+
+    grads = dict(g_attn=FAKE + (20 << 32), g_mlp=FAKE + (21 << 32), wqkv=gl(22), wo=gl(23), w1=gl(24), w2=gl(25))
+    a = dict(x=FAKE + (1 << 32), k_full=FAKE + (2 << 32), v_full=FAKE + (3 << 32), dy=FAKE + (4 << 32),
+             dk_full=FAKE + (5 << 32), dv_full=FAKE + (6 << 32), dk_loc=FAKE + (7 << 32), dv_loc=FAKE + (8 << 32),
+             dx=FAKE + (9 << 32), ws=FAKE + (10 << 32))
+
+    def call(shape=s, phases=tsp.TSP_BWD_ATTN, nbytes=need, g=grads, wt=w, **kw):
+        b = dict(a)
+        b.update(kw)
+        with pytest.raises(tsp.TspError) as ei:
+            tsp.tsp_layer_bwd(shape, wt, b["x"], b["k_full"], b["v_full"], b["dy"], b["dk_full"], b["dv_full"],
+                              b["dk_loc"], b["dv_loc"], b["dx"], g, phases, b["ws"], nbytes, stream=0)
+        return ei.value.status, tsp.lib().tsp_last_error()
+
+    for phases in (0, 4, 7):
+        assert call(phases=phases)[0] == tsp.TSP_ERR_INVALID_ARG
+    st, msg = call(phases=tsp.TSP_BWD_ALL)  # both halves in one call: D = 1 only
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"D=1" in msg
+    assert call(nbytes=need - 1)[0] == tsp.TSP_ERR_WORKSPACE
+    st, msg = call(dy=None)
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"dy is NULL" in msg
+    st, msg = call(g=dict(grads, wo=grads["wo"][:2] + [None] + grads["wo"][3:]))
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"grads->wo[2]" in msg
+    # a phase checks only what it uses: the QKV half needs no dy, no K/V and
+    # no MLP gradients, but its own dk_loc and dx
+    st, msg = call(phases=tsp.TSP_BWD_QKV, dy=None, k_full=None, g=dict(grads, w1=None, g_mlp=None), dk_loc=None)
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"dk_loc is NULL" in msg
+    st, msg = call(phases=tsp.TSP_BWD_QKV, dx=a["x"] + 1024)  # dx over x
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"overlaps" in msg
+    st, msg = call(dv_full=a["dk_full"] + 4096)  # two outputs over each other
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"overlaps" in msg
+    st, msg = call(g=dict(grads, w2=[a["ws"] + 256] + grads["w2"][1:]))  # a gradient inside the workspace
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"overlaps" in msg
+    st, msg = call(g=dict(grads, g_mlp=a["v_full"]))  # a gradient over an input
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"overlaps" in msg
+    assert call(dk_full=a["dk_full"] + 8)[0] == tsp.TSP_ERR_INVALID_ARG  # misaligned
+    # what the backward does not cover
+    assert call(shape=_shape(dtype="bf16", mlp="swiglu"), nbytes=1 << 40)[0] == tsp.TSP_ERR_UNSUPPORTED
+    assert call(shape=_shape(dtype="bf16", rope_base=1e4), nbytes=1 << 40)[0] == tsp.TSP_ERR_UNSUPPORTED
+    st = call(shape=tsp.make_shape(384, 4, 0, 256, 4, 64, 1024, dtype="bf16"), nbytes=1 << 40)[0]
+    assert st == tsp.TSP_ERR_UNSUPPORTED  # S/D = 96
+    st, msg = call(shape=tsp.make_shape(1024, 1, 0, 8320, 65, 128, 1024, dtype="bf16"), nbytes=1 << 40)
+    assert st == tsp.TSP_ERR_UNSUPPORTED and b"h=8320" in msg
+    for bad in (_shape(dtype="bf16", mlp="swiglu"), _shape(dtype="bf16", rope_base=1e4)):
+        with pytest.raises(tsp.TspError):
+            tsp.workspace_size(bad, tsp.TSP_WS_LAYER_BWD)
+    # 7B: a few GB of scratch for one rank's layer backward
+    s7 = tsp.make_shape(131072, 8, 0, 4096, 32, 128, 16384, dtype="bf16")
+    assert 3e9 < tsp.workspace_size(s7, tsp.TSP_WS_LAYER_BWD) < 5e9

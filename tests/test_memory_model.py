@@ -10,7 +10,7 @@ import pytest
 import tsp_rank_local_amd as tsp
 from tsp_rank_local_amd import memory as mm
 
-KINDS = (tsp.TSP_WS_MLP, tsp.TSP_WS_LAYER, tsp.TSP_WS_MLP_BWD, tsp.TSP_WS_ATTN_BWD)
+KINDS = (tsp.TSP_WS_MLP, tsp.TSP_WS_LAYER, tsp.TSP_WS_MLP_BWD, tsp.TSP_WS_ATTN_BWD, tsp.TSP_WS_LAYER_BWD)
 
 
 def _lib_ws(m, kind):
@@ -37,6 +37,8 @@ def test_workspace_matches_library(shape):
         for kind in KINDS:
             if kind == tsp.TSP_WS_MLP_BWD and (m.mlp != "gelu" or m.N % 64 != 0):
                 continue  # the MLP backward covers the GELU MLP with S/D a multiple of 64
+            if kind == tsp.TSP_WS_LAYER_BWD and (m.mlp != "gelu" or m.N % 64 != 0 or m.rope_base > 0):
+                continue  # so does the layer backward, without rotation
             assert mm.workspace_bytes(m, kind) == _lib_ws(m, kind), (shape, r, kind)
 
 
@@ -84,6 +86,12 @@ def test_training_terms():
         if k != "total":
             assert trn[k] == fwd[k]
     assert trn["total"] > fwd["total"]
+    # one layer's backward: dK/dV over the sequence plus the rank's summed
+    # rows, the library's layer-backward workspace, dy and dx, and the
+    # received shards' weight gradients
+    kvw = 2 * m.kv_heads * m.Dh
+    assert trn["backward_peak"] == ((m.S + m.N) * kvw * 4 + _lib_ws(m, tsp.TSP_WS_LAYER_BWD) + 2 * m.N * m.h * 4
+                                    + W * 4 * 7 // 8)
 
 
 def test_single_gpu_bytes():

@@ -19,9 +19,11 @@ __all__ = [
     "TspError", "TspShape", "TspLayerWeights", "lib", "make_shape", "workspace_size",
     "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_zigzag_attn_ex", "tsp_mlp_ring",
     "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_zigzag_attn_bwd_noalloc", "tsp_zigzag_attn_lse",
-    "tsp_zigzag_attn_bwd_lse", "tsp_layer_fwd", "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z", "profile_enable", "profile_reset", "profile_read",
+    "tsp_zigzag_attn_bwd_lse", "tsp_layer_fwd", "tsp_layer_bwd", "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z", "profile_enable",
+    "profile_reset", "profile_read", "TspLayerGrads",
     "TSP_F32", "TSP_BF16", "TSP_ATTN_Q_LOG2_SCALED", "TSP_PHASE_KV", "TSP_PHASE_REST", "TSP_PHASE_ALL",
-    "TSP_WS_MLP", "TSP_WS_LAYER", "TSP_WS_MLP_BWD", "TSP_WS_ATTN_BWD", "TSP_MLP_GELU", "TSP_MLP_SWIGLU", "MLP_KINDS",
+    "TSP_WS_MLP", "TSP_WS_LAYER", "TSP_WS_MLP_BWD", "TSP_WS_ATTN_BWD", "TSP_WS_LAYER_BWD", "TSP_BWD_ATTN", "TSP_BWD_QKV",
+    "TSP_BWD_ALL", "TSP_MLP_GELU", "TSP_MLP_SWIGLU", "MLP_KINDS",
     "KERNEL_CLASSES", "EXPORTED_SYMBOLS",
 ]
 
@@ -30,20 +32,22 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsp.so")
 TSP_OK, TSP_ERR_INVALID_ARG, TSP_ERR_UNSUPPORTED, TSP_ERR_WORKSPACE, TSP_ERR_HIP = range(5)
 TSP_F32, TSP_BF16 = 0, 1
 TSP_PHASE_KV, TSP_PHASE_REST, TSP_PHASE_ALL = 1, 2, 3
-TSP_WS_MLP, TSP_WS_LAYER, TSP_WS_MLP_BWD, TSP_WS_ATTN_BWD = 0, 1, 2, 3
+TSP_WS_MLP, TSP_WS_LAYER, TSP_WS_MLP_BWD, TSP_WS_ATTN_BWD, TSP_WS_LAYER_BWD = 0, 1, 2, 3, 4
+TSP_BWD_ATTN, TSP_BWD_QKV, TSP_BWD_ALL = 1, 2, 3
 TSP_ATTN_Q_LOG2_SCALED = 1
 TSP_MLP_GELU, TSP_MLP_SWIGLU = 0, 1
 MLP_KINDS = {"gelu": TSP_MLP_GELU, "swiglu": TSP_MLP_SWIGLU}
 TSP_MAX_D = 64
 KERNEL_CLASSES = {"rmsnorm": 0, "qkv": 1, "attention": 2, "outproj": 3, "mlp_up": 4, "mlp_down": 5, "zigzag": 6,
                   "lead": 7, "bwd_gemm": 8, "transpose": 9,
-                  "attn_bwd": 10}
+                  "attn_bwd": 10, "rows_bwd": 11}
 
 EXPORTED_SYMBOLS = [
     "tsp_status_string", "tsp_last_error", "tsp_abi_version", "tsp_workspace_size",
     "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_zigzag_attn_ex", "tsp_mlp_ring",
     "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_zigzag_attn_bwd_noalloc", "tsp_zigzag_attn_lse",
-    "tsp_zigzag_attn_bwd_lse", "tsp_layer_fwd", "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z", "tsp_profile_enable", "tsp_profile_reset", "tsp_profile_read",
+    "tsp_zigzag_attn_bwd_lse", "tsp_layer_fwd", "tsp_layer_bwd", "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z", "tsp_profile_enable",
+    "tsp_profile_reset", "tsp_profile_read",
 ]
 
 
@@ -61,6 +65,12 @@ class TspShape(ctypes.Structure):
 
 
 class TspLayerWeights(ctypes.Structure):
+    _fields_ = [("g_attn", ctypes.c_void_p), ("g_mlp", ctypes.c_void_p),
+                ("wqkv", ctypes.POINTER(ctypes.c_void_p)), ("wo", ctypes.POINTER(ctypes.c_void_p)),
+                ("w1", ctypes.POINTER(ctypes.c_void_p)), ("w2", ctypes.POINTER(ctypes.c_void_p))]
+
+
+class TspLayerGrads(ctypes.Structure):
     _fields_ = [("g_attn", ctypes.c_void_p), ("g_mlp", ctypes.c_void_p),
                 ("wqkv", ctypes.POINTER(ctypes.c_void_p)), ("wo", ctypes.POINTER(ctypes.c_void_p)),
                 ("w1", ctypes.POINTER(ctypes.c_void_p)), ("w2", ctypes.POINTER(ctypes.c_void_p))]
@@ -100,6 +110,8 @@ def lib() -> ctypes.CDLL:
                                      ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp]
     L.tsp_zigzag_attn_bwd_lse.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.tsp_layer_fwd.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, ctypes.c_uint, vp, sz, vp]
+    L.tsp_layer_bwd.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                ctypes.POINTER(TspLayerGrads), ctypes.c_uint, vp, sz, vp]
     L.tsp_profile_enable.argtypes = [ctypes.c_int]
     L.tsp_profile_enable.restype = None
     L.tsp_profile_reset.argtypes = []
@@ -107,7 +119,7 @@ def lib() -> ctypes.CDLL:
     L.tsp_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     for name in ("tsp_workspace_size", "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn",
                  "tsp_zigzag_attn_ex", "tsp_mlp_ring", "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd",
-                 "tsp_zigzag_attn_bwd_noalloc", "tsp_layer_fwd",
+                 "tsp_zigzag_attn_bwd_noalloc", "tsp_layer_fwd", "tsp_layer_bwd",
                  "tsp_zigzag_attn_lse", "tsp_zigzag_attn_bwd_lse", "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z",
                  "tsp_profile_read"):
         getattr(L, name).restype = ctypes.c_int
@@ -251,6 +263,30 @@ def tsp_layer_fwd(shape: TspShape, w: dict, x, k_full, v_full, y, phases, ws, ws
     cw = TspLayerWeights(_ptr(w["g_attn"]), _ptr(w["g_mlp"]), arrs["wqkv"], arrs["wo"], arrs["w1"], arrs["w2"])
     _check(lib().tsp_layer_fwd(ctypes.byref(shape), ctypes.byref(cw), _ptr(x), _ptr(k_full), _ptr(v_full), _ptr(y),
                                int(phases), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def _weights(w: dict) -> tuple:
+    """A TspLayerWeights for a dict of g_attn, g_mlp and shard lists, plus the
+    pointer arrays it refers to (kept alive by the caller)."""
+    arrs = {k: _ptr_array(w[k]) for k in ("wqkv", "wo", "w1", "w2")}
+    return TspLayerWeights(_ptr(w["g_attn"]), _ptr(w["g_mlp"]), arrs["wqkv"], arrs["wo"], arrs["w1"], arrs["w2"]), arrs
+
+
+def tsp_layer_bwd(shape: TspShape, w: dict, x, k_full, v_full, dy, dk_full, dv_full, dk_loc, dv_loc, dx,
+                  grads: dict, phases, ws, ws_bytes=None, stream=None) -> None:
+    """w: as for tsp_layer_fwd; grads: dict with fp32 g_attn, g_mlp and lists
+    wqkv, wo, w1, w2 of D fp32 device tensors (entries a phase does not
+    write may be None)."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    cw, keep_w = _weights(w)
+    garr = {k: (_ptr_array(grads[k]) if grads.get(k) is not None else None) for k in ("wqkv", "wo", "w1", "w2")}
+    cg = TspLayerGrads(_ptr(grads.get("g_attn")), _ptr(grads.get("g_mlp")), garr["wqkv"], garr["wo"], garr["w1"],
+                       garr["w2"])
+    _check(lib().tsp_layer_bwd(ctypes.byref(shape), ctypes.byref(cw), _ptr(x), _ptr(k_full), _ptr(v_full), _ptr(dy),
+                               _ptr(dk_full), _ptr(dv_full), _ptr(dk_loc), _ptr(dv_loc), _ptr(dx), ctypes.byref(cg),
+                               int(phases), _ptr(ws), int(ws_bytes), _stream(stream)))
+    del keep_w
 
 
 def profile_enable(on: bool = True) -> None:

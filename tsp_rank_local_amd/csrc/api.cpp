@@ -210,6 +210,75 @@ tsp_status check_mlp_bwd_shape(const tsp_shape *s) {
   return TSP_OK;
 }
 
+// Layer backward scratch: dh1 and dq (fp32) carried from TSP_BWD_ATTN to
+// TSP_BWD_QKV, then one region that each phase lays out for itself.
+//  ATTN: xn, Q, o (fp32) and o in dtype (panel), o^T, h1 (fp32), hn, dy in
+//  dtype, dhn (fp32), dh1 in dtype (panel) and dh1^T (panel), W_O^T, do,
+//  the forward's log-sum-exp, the attention backward's statistics, the gain
+//  gradient partials and the MLP backward's own scratch.
+//  QKV: xn, xn^T, [dq|dk|dv] (panel) and its transpose (panel), W_QKV^T,
+//  dxn (fp32), the gain gradient partials.
+struct LayerBwdWs {
+  size_t dh1, dq;
+  size_t xn, q, o, olo, ot, h1, hn, dylo, dhn, dh1lo, dh1t, wot, dout, lse, stat, part, mlp, mlp_bytes;
+  size_t xr, xnt, dqkv, dqkvt, wqkvt, dxn, part2;
+  size_t total;
+};
+
+LayerBwdWs layer_bwd_ws(const tsp_shape *s) {
+  const size_t e = elem_bytes(s->dtype), N = (size_t)(s->S / s->D), h = (size_t)s->h;
+  const size_t K3 = h + 2 * (size_t)kv_heads(s) * s->Dh;
+  const size_t nh = align256(N * h * e), nh4 = align256(N * h * 4), part = align256(tsp::rmsnorm_bwd_part_bytes((int32_t)N, s->h));
+  LayerBwdWs w;
+  w.dh1 = 0;
+  w.dq = nh4;
+  const size_t region = 2 * nh4;
+  size_t at = region;
+  auto take = [&](size_t bytes) {
+    const size_t o = at;
+    at += bytes;
+    return o;
+  };
+  w.xn = take(nh);
+  w.q = take(nh);
+  w.o = take(nh4);
+  w.olo = take(nh);
+  w.ot = take(nh);
+  w.h1 = take(nh4);
+  w.hn = take(nh);
+  w.dylo = take(nh);
+  w.dhn = take(nh4);
+  w.dh1lo = take(nh);
+  w.dh1t = take(nh);
+  w.wot = take(align256(h * h * e));
+  w.dout = take(nh);
+  w.lse = take(align256((size_t)s->H * N * 4));
+  w.stat = take(attn_bwd_ws(s));
+  w.part = take(part);
+  w.mlp_bytes = mlp_bwd_ws(s).total;
+  w.mlp = take(w.mlp_bytes);
+  const size_t attn_end = at;
+  at = region;
+  w.xr = take(nh);
+  w.xnt = take(nh);
+  w.dqkv = take(align256(N * K3 * e));
+  w.dqkvt = take(align256(N * K3 * e));
+  w.wqkvt = take(align256(h * K3 * e));
+  w.dxn = take(nh4);
+  w.part2 = take(part);
+  w.total = std::max(attn_end, at);
+  return w;
+}
+
+tsp_status check_layer_bwd_shape(const tsp_shape *s) {
+  tsp_status st = check_layer_shape(s);
+  if (st) return st;
+  if ((st = check_mlp_bwd_shape(s))) return st;
+  if (s->rope_base != 0.f) return fail(TSP_ERR_UNSUPPORTED, "the layer backward covers the layer without rotation");
+  if (s->h > 8192) return fail(TSP_ERR_UNSUPPORTED, "h=%d: the RMSNorm backward takes h <= 8192", s->h);
+  return TSP_OK;
+}
+
 tsp_status hip_fail(hipError_t e, const char *what) {
   return fail(TSP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -330,6 +399,9 @@ tsp_status tsp_workspace_size(const tsp_shape *s, int which, size_t *bytes) {
   } else if (which == TSP_WS_ATTN_BWD) {
     if ((st = check_attn_shape(s))) return st;
     *bytes = attn_bwd_ws(s);
+  } else if (which == TSP_WS_LAYER_BWD) {
+    if ((st = check_layer_bwd_shape(s))) return st;
+    *bytes = layer_bwd_ws(s).total;
   } else {
     return fail(TSP_ERR_INVALID_ARG, "unknown workspace kind %d", which);
   }
@@ -748,6 +820,180 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
                  tsp::launch_lead_mlp_down(lhid, m, ring_list(w->w2, D, s->r), D, fd, h, lh1, y, lpart, stream),
                  "leading rows: MLP down");
     }
+  }
+  return ok();
+}
+
+tsp_status tsp_layer_bwd(const tsp_shape *s, const tsp_layer_weights *w, const float *x, const void *k_full,
+                         const void *v_full, const float *dy, float *dk_full, float *dv_full, const float *dk_loc,
+                         const float *dv_loc, float *dx, const tsp_layer_grads *gr, unsigned phases, void *ws_,
+                         size_t ws_bytes, void *stream_) {
+  tsp_status st = check_layer_bwd_shape(s);
+  if (st) return st;
+  if (!w) return fail(TSP_ERR_INVALID_ARG, "weights is NULL");
+  if (!gr) return fail(TSP_ERR_INVALID_ARG, "grads is NULL");
+  if (phases == 0 || (phases & ~3u)) return fail(TSP_ERR_INVALID_ARG, "phases=%u must be 1, 2 or 3", phases);
+  if (phases == TSP_BWD_ALL && s->D != 1)
+    return fail(TSP_ERR_INVALID_ARG, "TSP_BWD_ALL needs D=1 (D=%d ranks exchange K/V gradients between the phases)",
+                s->D);
+  const bool pa = (phases & TSP_BWD_ATTN) != 0, pq = (phases & TSP_BWD_QKV) != 0;
+  const int32_t N = (int32_t)(s->S / s->D), h = s->h, D = s->D, hd = h / D, fd = s->F / D;
+  const int32_t Hkv = kv_heads(s), hkv = Hkv * s->Dh, hq = h / D, hk = hkv / D, K3 = h + 2 * hkv;
+  if ((st = check_ptr(x, "x")) || (st = check_ptr(ws_, "ws")) || (st = check_ptr(w->g_attn, "g_attn")) ||
+      (st = check_ptr_list(w->wqkv, D, "wqkv")))
+    return st;
+  if (pa && ((st = check_ptr(k_full, "k_full")) || (st = check_ptr(v_full, "v_full")) || (st = check_ptr(dy, "dy")) ||
+             (st = check_ptr(dk_full, "dk_full")) || (st = check_ptr(dv_full, "dv_full")) ||
+             (st = check_ptr(w->g_mlp, "g_mlp")) || (st = check_ptr_list(w->wo, D, "wo")) ||
+             (st = check_ptr_list(w->w1, D, "w1")) || (st = check_ptr_list(w->w2, D, "w2")) ||
+             (st = check_ptr(gr->g_mlp, "grads->g_mlp")) ||
+             (st = check_ptr_list((const void *const *)gr->wo, D, "grads->wo")) ||
+             (st = check_ptr_list((const void *const *)gr->w1, D, "grads->w1")) ||
+             (st = check_ptr_list((const void *const *)gr->w2, D, "grads->w2"))))
+    return st;
+  if (pq && ((st = check_ptr(dk_loc, "dk_loc")) || (st = check_ptr(dv_loc, "dv_loc")) || (st = check_ptr(dx, "dx")) ||
+             (st = check_ptr(gr->g_attn, "grads->g_attn")) ||
+             (st = check_ptr_list((const void *const *)gr->wqkv, D, "grads->wqkv"))))
+    return st;
+  const LayerBwdWs L = layer_bwd_ws(s);
+  if (ws_bytes < L.total) return fail(TSP_ERR_WORKSPACE, "ws_bytes=%zu < %zu", ws_bytes, L.total);
+  const size_t e = elem_bytes(s->dtype), nh4 = (size_t)N * h * 4, kvf = (size_t)s->S * hkv;
+  // what the requested phases read and write; dk_loc/dv_loc may be
+  // dk_full/dv_full themselves when both phases run (D = 1)
+  std::vector<Range> in, out;
+  in.push_back({x, nh4, "x"});
+  in.push_back({w->g_attn, (size_t)h * e, "g_attn"});
+  for (int j = 0; j < D; ++j) in.push_back({w->wqkv[j], (size_t)(hq + 2 * hk) * h * e, "wqkv"});
+  out.push_back({ws_, L.total, "ws"});
+  if (pa) {
+    in.push_back({k_full, kvf * e, "k_full"});
+    in.push_back({v_full, kvf * e, "v_full"});
+    in.push_back({dy, nh4, "dy"});
+    in.push_back({w->g_mlp, (size_t)h * e, "g_mlp"});
+    out.push_back({dk_full, kvf * 4, "dk_full"});
+    out.push_back({dv_full, kvf * 4, "dv_full"});
+    out.push_back({gr->g_mlp, (size_t)h * 4, "grads->g_mlp"});
+    for (int j = 0; j < D; ++j) {
+      in.push_back({w->wo[j], (size_t)h * hd * e, "wo"});
+      in.push_back({w->w1[j], (size_t)fd * h * e, "w1"});
+      in.push_back({w->w2[j], (size_t)h * fd * e, "w2"});
+      out.push_back({gr->wo[j], (size_t)h * hd * 4, "grads->wo"});
+      out.push_back({gr->w1[j], (size_t)fd * h * 4, "grads->w1"});
+      out.push_back({gr->w2[j], (size_t)h * fd * 4, "grads->w2"});
+    }
+  }
+  if (pq) {
+    const bool same_k = pa && (const void *)dk_loc == (const void *)dk_full;
+    const bool same_v = pa && (const void *)dv_loc == (const void *)dv_full;
+    if (!same_k) in.push_back({dk_loc, (size_t)N * hkv * 4, "dk_loc"});
+    if (!same_v) in.push_back({dv_loc, (size_t)N * hkv * 4, "dv_loc"});
+    out.push_back({dx, nh4, "dx"});
+    out.push_back({gr->g_attn, (size_t)h * 4, "grads->g_attn"});
+    for (int j = 0; j < D; ++j) out.push_back({gr->wqkv[j], (size_t)(hq + 2 * hk) * h * 4, "grads->wqkv"});
+  }
+  for (size_t i = 0; i < out.size(); ++i) {
+    for (const Range &ri : in)
+      if (overlap(out[i], ri)) return fail(TSP_ERR_INVALID_ARG, "%s overlaps %s", out[i].name, ri.name);
+    for (size_t j = i + 1; j < out.size(); ++j)
+      if (overlap(out[i], out[j])) return fail(TSP_ERR_INVALID_ARG, "%s overlaps %s", out[i].name, out[j].name);
+  }
+
+  unsigned char *ws = static_cast<unsigned char *>(ws_);
+  float *dh1 = (float *)(ws + L.dh1), *dq = (float *)(ws + L.dq);
+  const tsp::ZigzagMap zz = tsp::make_zigzag(s->S, D, s->r);
+  const int dt = s->dtype;
+  const bool pnl = dt == TSP_BF16;  // bf16 A operands in panel layout
+  const int64_t np = pnl ? (int64_t)N * tsp::kPanel : 0;
+  hipStream_t stream = (hipStream_t)stream_;
+  auto one = [](const void *p) {
+    tsp::PtrList l;
+    memset(&l, 0, sizeof l);
+    l.p[0] = p;
+    return l;
+  };
+  if (pa) {
+    void *xn = ws + L.xn, *q = ws + L.q, *olo = ws + L.olo, *ot = ws + L.ot, *hn = ws + L.hn, *dylo = ws + L.dylo;
+    void *dh1lo = ws + L.dh1lo, *dh1t = ws + L.dh1t, *wot = ws + L.wot, *dout = ws + L.dout;
+    float *o = (float *)(ws + L.o), *h1 = (float *)(ws + L.h1), *dhn = (float *)(ws + L.dhn);
+    float *lse = (float *)(ws + L.lse), *part = (float *)(ws + L.part);
+    float *stat_lse = (float *)(ws + L.stat), *stat_delta = (float *)(ws + L.stat + attn_bwd_ws(s) / 2);
+    // the rank's forward again: xn, Q (no pre-scaling), o with its row
+    // statistics, h1, hn
+    TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(x, w->g_attn, xn, N, h, s->eps, dt, pnl, stream), "RMSNorm");
+    TSP_LAUNCH(TSP_K_QKV,
+               tsp::launch_qkv(dt, xn, pnl, N, h, to_list(w->wqkv, D), D, hq, 0, q, nullptr, nullptr, zz, 1.0f,
+                               nullptr, s->Dh, stream),
+               "Q");
+    TSP_LAUNCH(TSP_K_ATTN,
+               tsp::launch_attention(dt, q, k_full, v_full, o, TSP_F32, false, s->S, N, s->H, Hkv, s->Dh, s->scale, zz,
+                                     false, stream, pnl ? lse : nullptr),
+               "attention");
+    TSP_LAUNCH(TSP_K_ROWS_BWD, tsp::launch_pack_cols(dt, o, nullptr, nullptr, N, 1, h, 0, olo, pnl, stream),
+               "o conversion");
+    TSP_LAUNCH(TSP_K_OUTPROJ, tsp::launch_outproj(dt, olo, pnl, N, h, to_list(w->wo, D), D, hd, x, h1, stream),
+               "output projection");
+    TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(h1, w->g_mlp, hn, N, h, s->eps, dt, false, stream), "RMSNorm");
+    // MLP branch: dhn, and the ring shards' dW1, dW2
+    TSP_LAUNCH(TSP_K_ROWS_BWD, tsp::launch_pack_cols(dt, dy, nullptr, nullptr, N, 1, h, 0, dylo, false, stream),
+               "dy conversion");
+    if ((st = mlp_ring_bwd(s, hn, nullptr, w->w1, w->w2, dylo, nullptr, dhn, gr->w1, gr->w2, ws + L.mlp,
+                           L.mlp_bytes, stream_)))
+      return st;
+    // dh1 = dy + the second RMSNorm's backward of dhn
+    TSP_LAUNCH(TSP_K_ROWS_BWD,
+               tsp::launch_rmsnorm_bwd(h1, w->g_mlp, dhn, dy, dh1, dh1lo, pnl, N, h, s->eps, dt, part, gr->g_mlp,
+                                       stream),
+               "RMSNorm backward");
+    // output projection: do = dh1 W_O (W_O^T stacked by shard), dW_O,j =
+    // dh1^T o[:, head group j]
+    TSP_LAUNCH(TSP_K_TRANSPOSE,
+               tsp::launch_transpose(dt, to_list(w->wo, D), D, hd, 0, h, hd, wot, h, 0, (int64_t)hd * h, stream),
+               "W_O transpose");
+    TSP_LAUNCH(TSP_K_BWD_GEMM, tsp::launch_gemm_nt(dt, dh1lo, pnl, N, h, wot, h, dout, dt, stream), "do");
+    TSP_LAUNCH(TSP_K_TRANSPOSE,
+               tsp::launch_transpose(dt, one(dh1lo), 1, h, np, N, h, dh1t, N, pnl ? (int64_t)h * tsp::kPanel : 0, 0,
+                                     stream),
+               "dh1 transpose");
+    TSP_LAUNCH(TSP_K_TRANSPOSE, tsp::launch_transpose(dt, one(olo), 1, h, np, N, h, ot, N, 0, 0, stream),
+               "o transpose");
+    TSP_LAUNCH(TSP_K_BWD_GEMM,
+               tsp::launch_wgrad(dt, dh1t, pnl, h, ot, h, N, to_list((const void *const *)gr->wo, D), hd, false,
+                                 stream),
+               "dW_O");
+    // attention: dq (kept for the second phase) and this rank's share of
+    // every key/value row's gradient
+    TSP_LAUNCH(TSP_K_ATTN_BWD,
+               tsp::launch_attention_bwd(dt, q, k_full, v_full, dout, dq, dk_full, dv_full, stat_lse, stat_delta, s->S,
+                                         N, s->H, Hkv, s->Dh, s->scale, zz, stream, pnl ? o : nullptr,
+                                         pnl ? lse : nullptr),
+               "attention backward");
+  }
+  if (pq) {
+    void *xr = ws + L.xr, *xnt = ws + L.xnt, *dqkv = ws + L.dqkv, *dqkvt = ws + L.dqkvt, *wqkvt = ws + L.wqkvt;
+    float *dxn = (float *)(ws + L.dxn), *part = (float *)(ws + L.part2);
+    TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(x, w->g_attn, xr, N, h, s->eps, dt, false, stream), "RMSNorm");
+    TSP_LAUNCH(TSP_K_TRANSPOSE, tsp::launch_transpose(dt, one(xr), 1, h, 0, N, h, xnt, N, 0, 0, stream),
+               "xn transpose");
+    // [dq_j | dk_j | dv_j] side by side in shard order, as the rows of W_QKV,j
+    TSP_LAUNCH(TSP_K_ROWS_BWD, tsp::launch_pack_cols(dt, dq, dk_loc, dv_loc, N, D, hq, hk, dqkv, pnl, stream),
+               "dQKV packing");
+    TSP_LAUNCH(TSP_K_TRANSPOSE,
+               tsp::launch_transpose(dt, one(dqkv), 1, K3, np, N, K3, dqkvt, N, pnl ? (int64_t)K3 * tsp::kPanel : 0, 0,
+                                     stream),
+               "dQKV transpose");
+    TSP_LAUNCH(TSP_K_TRANSPOSE,
+               tsp::launch_transpose(dt, to_list(w->wqkv, D), D, h, 0, hq + 2 * hk, h, wqkvt, K3, 0, hq + 2 * hk,
+                                     stream),
+               "W_QKV transpose");
+    TSP_LAUNCH(TSP_K_BWD_GEMM, tsp::launch_gemm_nt(dt, dqkv, pnl, N, K3, wqkvt, h, dxn, TSP_F32, stream), "dxn");
+    TSP_LAUNCH(TSP_K_BWD_GEMM,
+               tsp::launch_wgrad(dt, dqkvt, pnl, K3, xnt, h, N, to_list((const void *const *)gr->wqkv, D), hq + 2 * hk,
+                                 true, stream),
+               "dW_QKV");
+    TSP_LAUNCH(TSP_K_ROWS_BWD,
+               tsp::launch_rmsnorm_bwd(x, w->g_attn, dxn, dh1, dx, nullptr, false, N, h, s->eps, dt, part, gr->g_attn,
+                                       stream),
+               "RMSNorm backward");
   }
   return ok();
 }

@@ -220,6 +220,21 @@ struct EpiStoreF32 {
   __device__ __forceinline__ void put_row(const Row &w, const float4 (&v)[4][4]) const { put_each(*this, w, v); }
 };
 
+// out [M][N] row-major in bf16, rounded once from the fp32 sums.
+struct EpiStoreBf16 {
+  bf16 *out;
+  int64_t ld;
+  __device__ __forceinline__ void operator()(int, int r, int c, float v) const { out[(int64_t)r * ld + c] = (bf16)v; }
+  __device__ __forceinline__ void operator()(int, int r, int c, float4 v) const { store4(out + (int64_t)r * ld + c, v); }
+  struct Row {
+    bf16 *p;
+  };
+  __device__ __forceinline__ bool fast_ok() const { return true; }
+  __device__ __forceinline__ Row row(int, int r, int c0, int g) const { return Row{out + (int64_t)r * ld + c0 + 4 * g}; }
+  __device__ __forceinline__ void put(const Row &w, int i, int vq, float4 v) const { store4(w.p + i * 32 + vq * 8, v); }
+  __device__ __forceinline__ void put_row(const Row &w, const float4 (&v)[4][4]) const { put_each(*this, w, v); }
+};
+
 // out = res + acc; res may alias out (each element is read then written by
 // the same lane).
 struct EpiAddF32 {
@@ -1189,6 +1204,20 @@ hipError_t launch_mlp_bwd_dx(int dtype, const void *dz, bool a_panel, int32_t n,
     return run_gemm(dtype, a, e, s);
   }
   EpiStoreF32 e{dx, h};
+  return run_gemm(dtype, a, e, s);
+}
+
+hipError_t launch_gemm_nt(int dtype, const void *A, bool a_panel, int32_t M, int32_t K, const void *B, int32_t N,
+                          void *out, int out_dtype, hipStream_t s) {
+  GemmArgs a = make_args(A, K, a_panel, M, N, K);
+  a.B.p[0] = B;
+  a.ldb = K;
+  if (out_dtype == TSP_BF16) {
+    if (dtype != TSP_BF16) return hipErrorInvalidValue;
+    EpiStoreBf16 e{(bf16 *)out, N};
+    return run_gemm(dtype, a, e, s);
+  }
+  EpiStoreF32 e{(float *)out, N};
   return run_gemm(dtype, a, e, s);
 }
 

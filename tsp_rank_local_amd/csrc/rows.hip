@@ -65,6 +65,182 @@ hipError_t launch_rmsnorm(const float *x, const void *g, void *out, int32_t rows
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- RMSNorm backward
+// Backward of rmsnorm_kernel. With r = (mean(x^2) + eps)^(-1/2) and output
+// x_k g_k r, the gradient of row x for output gradient d is
+//   dx_k = r g_k d_k - x_k r^3 / h * sum_i d_i g_i x_i,
+// and the gain receives sum over rows of d_k x_k r. A block takes
+// kNormBwdRows consecutive rows; each thread keeps its float4 columns
+// (c = 4 * thread + 1024 * i) of x and d in registers between the two row
+// sums and the output, and adds d x r into per-column partial sums that the
+// block writes to part[block][h]. rmsnorm_bwd_dg_kernel adds those rows in
+// block order, so the gain gradient does not depend on scheduling.
+constexpr int kNormBwdRows = 16, kNormBwdChunks = 8;  // h <= 4 * 256 * 8
+
+template <typename G, typename L>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float *__restrict__ x, const G *__restrict__ g,
+                                                          const float *__restrict__ d, const float *__restrict__ res,
+                                                          float *__restrict__ dx, L *__restrict__ lo, int64_t lo_panel,
+                                                          int32_t rows, int32_t h, float eps,
+                                                          float *__restrict__ part) {
+  float4 gg[kNormBwdChunks], acc[kNormBwdChunks];
+#pragma unroll
+  for (int i = 0; i < kNormBwdChunks; ++i) {
+    const int c = threadIdx.x * 4 + 1024 * i;
+    gg[i] = c < h ? make_float4((float)g[c], (float)g[c + 1], (float)g[c + 2], (float)g[c + 3])
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __shared__ float2 red[2][4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int rr = 0; rr < kNormBwdRows; ++rr) {
+    const int64_t row = (int64_t)blockIdx.x * kNormBwdRows + rr;
+    if (row >= rows) break;  // the same for the whole block
+    const float *xr = x + row * h, *dr = d + row * h;
+    float4 xv[kNormBwdChunks], dv[kNormBwdChunks];
+    float ss = 0.f, sdgx = 0.f;
+#pragma unroll
+    for (int i = 0; i < kNormBwdChunks; ++i) {
+      const int c = threadIdx.x * 4 + 1024 * i;
+      xv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      dv[i] = xv[i];
+      if (c < h) {
+        xv[i] = *reinterpret_cast<const float4 *>(xr + c);
+        dv[i] = *reinterpret_cast<const float4 *>(dr + c);
+      }
+      ss += xv[i].x * xv[i].x + xv[i].y * xv[i].y + xv[i].z * xv[i].z + xv[i].w * xv[i].w;
+      sdgx += dv[i].x * gg[i].x * xv[i].x + dv[i].y * gg[i].y * xv[i].y + dv[i].z * gg[i].z * xv[i].z +
+              dv[i].w * gg[i].w * xv[i].w;
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      ss += __shfl_xor(ss, off);
+      sdgx += __shfl_xor(sdgx, off);
+    }
+    // two slots: a wave that runs ahead into the next row writes the other
+    // one, and cannot reach this slot again before every wave has passed
+    // the next row's barrier (after its reads here)
+    if (lane == 0) red[rr & 1][wave] = make_float2(ss, sdgx);
+    __syncthreads();
+    const float2 t0 = red[rr & 1][0], t1 = red[rr & 1][1], t2 = red[rr & 1][2], t3 = red[rr & 1][3];
+    const float tss = t0.x + t1.x + t2.x + t3.x, tsd = t0.y + t1.y + t2.y + t3.y;
+    const float r = 1.0f / sqrtf(tss / (float)h + eps);
+    const float k = r * r * r * tsd / (float)h;
+#pragma unroll
+    for (int i = 0; i < kNormBwdChunks; ++i) {
+      const int c = threadIdx.x * 4 + 1024 * i;
+      if (c >= h) continue;
+      float4 o = make_float4(r * gg[i].x * dv[i].x - k * xv[i].x, r * gg[i].y * dv[i].y - k * xv[i].y,
+                             r * gg[i].z * dv[i].z - k * xv[i].z, r * gg[i].w * dv[i].w - k * xv[i].w);
+      if (res) {
+        const float4 a = *reinterpret_cast<const float4 *>(res + row * h + c);
+        o = make_float4(o.x + a.x, o.y + a.y, o.z + a.z, o.w + a.w);
+      }
+      *reinterpret_cast<float4 *>(dx + row * h + c) = o;
+      if (lo) {
+        L *p = lo + (lo_panel ? panel_index(row, c, lo_panel) : row * h + c);  // 4 elements, one panel
+        p[0] = (L)o.x;
+        p[1] = (L)o.y;
+        p[2] = (L)o.z;
+        p[3] = (L)o.w;
+      }
+      acc[i].x += dv[i].x * xv[i].x * r;
+      acc[i].y += dv[i].y * xv[i].y * r;
+      acc[i].z += dv[i].z * xv[i].z * r;
+      acc[i].w += dv[i].w * xv[i].w * r;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kNormBwdChunks; ++i) {
+    const int c = threadIdx.x * 4 + 1024 * i;
+    if (c < h) *reinterpret_cast<float4 *>(part + (int64_t)blockIdx.x * h + c) = acc[i];
+  }
+}
+
+// dg[c] = sum over b < nb of part[b][c]: 64 columns per block, four slices
+// of b (b = s, s + 4, ...) summed in order and then added slice by slice.
+__global__ __launch_bounds__(256) void rmsnorm_bwd_dg_kernel(const float *__restrict__ part, int32_t nb, int32_t h,
+                                                             float *__restrict__ dg) {
+  __shared__ float sl[4][64];
+  const int col = blockIdx.x * 64 + (threadIdx.x & 63), s = threadIdx.x >> 6;
+  float a = 0.f;
+  if (col < h)
+    for (int b = s; b < nb; b += 4) a += part[(int64_t)b * h + col];
+  sl[s][threadIdx.x & 63] = a;
+  __syncthreads();
+  if (s == 0 && col < h) dg[col] = ((sl[0][threadIdx.x] + sl[1][threadIdx.x]) + sl[2][threadIdx.x]) + sl[3][threadIdx.x];
+}
+
+size_t rmsnorm_bwd_part_bytes(int32_t rows, int32_t h) {
+  return (size_t)((rows + kNormBwdRows - 1) / kNormBwdRows) * (size_t)h * 4;
+}
+
+hipError_t launch_rmsnorm_bwd(const float *x, const void *g, const float *d, const float *res, float *dx, void *lo,
+                              bool lo_panel, int32_t rows, int32_t h, float eps, int dtype, float *part, float *dg,
+                              hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if ((h & 3) != 0 || h > 4 * 256 * kNormBwdChunks || (h + 63) / 64 > 65535) return hipErrorInvalidValue;
+  const int nb = (rows + kNormBwdRows - 1) / kNormBwdRows;
+  const int64_t ps = lo_panel ? (int64_t)rows * kPanel : 0;
+  if (dtype == TSP_BF16)
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<bf16, bf16>), dim3(nb), dim3(256), 0, s, x, (const bf16 *)g, d, res, dx,
+                       (bf16 *)lo, ps, rows, h, eps, part);
+  else
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<float, float>), dim3(nb), dim3(256), 0, s, x, (const float *)g, d, res,
+                       dx, (float *)lo, (int64_t)0, rows, h, eps, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rmsnorm_bwd_dg_kernel, dim3((h + 63) / 64), dim3(256), 0, s, part, nb, h, dg);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- column packing
+// out[t][j * (wa + 2 wb) + c] = a[t][j * wa + c] (c < wa), then b[t][j * wb +
+// c - wa], then cc[t][j * wb + c - wa - wb], for j < D: fp32 sources
+// interleaved by shard into one dtype matrix [n][D (wa + 2 wb)], row-major
+// or (bf16) in panel layout. Four consecutive columns never straddle
+// sources (wa and wb are multiples of 4). With D = 1 and wb = 0 it is a
+// plain conversion of a.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_cols_kernel(const float *__restrict__ a, const float *__restrict__ b,
+                                                        const float *__restrict__ cc, int32_t n, int32_t D,
+                                                        int32_t wa, int32_t wb, T *__restrict__ out,
+                                                        int64_t out_panel) {
+  const int32_t ws = wa + 2 * wb, W = D * ws, W4 = W / 4;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)n * W4) return;
+  const int64_t t = e / W4;
+  const int32_t col = (int32_t)(e - t * W4) * 4, j = col / ws, c = col - j * ws;
+  const float *src;
+  if (c < wa)
+    src = a + t * ((int64_t)D * wa) + (int64_t)j * wa + c;
+  else if (c < wa + wb)
+    src = b + t * ((int64_t)D * wb) + (int64_t)j * wb + (c - wa);
+  else
+    src = cc + t * ((int64_t)D * wb) + (int64_t)j * wb + (c - wa - wb);
+  const float4 v = *reinterpret_cast<const float4 *>(src);
+  T *o = out + (out_panel ? panel_index(t, col, out_panel) : t * W + col);
+  o[0] = (T)v.x;
+  o[1] = (T)v.y;
+  o[2] = (T)v.z;
+  o[3] = (T)v.w;
+}
+
+hipError_t launch_pack_cols(int dtype, const float *a, const float *b, const float *c, int32_t n, int32_t D,
+                            int32_t wa, int32_t wb, void *out, bool out_panel, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (((wa | wb) & 3) != 0 || (out_panel && dtype != TSP_BF16)) return hipErrorInvalidValue;
+  const int64_t total = (int64_t)n * D * (wa + 2 * wb) / 4;
+  if ((total + 255) / 256 > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (dtype == TSP_BF16)
+    hipLaunchKernelGGL(pack_cols_kernel<bf16>, grid, dim3(256), 0, s, a, b, c, n, D, wa, wb, (bf16 *)out,
+                       out_panel ? (int64_t)n * kPanel : (int64_t)0);
+  else
+    hipLaunchKernelGGL(pack_cols_kernel<float>, grid, dim3(256), 0, s, a, b, c, n, D, wa, wb, (float *)out,
+                       (int64_t)0);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- rotary embedding
 // table[t * half + i] = (cos, sin) of pos(t) * base^(-2i/Dh), in fp64 before
 // rounding to fp32 (the angle reaches S radians for i = 0).

@@ -54,6 +54,23 @@ hipError_t launch_rmsnorm(const float *x, const void *g, void *out, int32_t rows
 hipError_t launch_rmsnorm_f32(const float *x, const void *g, int g_dtype, float *out, int32_t rows, int32_t h,
                               float eps, hipStream_t s);
 
+// Backward of launch_rmsnorm for rows of x [rows][h] fp32 (h a multiple of 4,
+// at most 8192) and output gradient d [rows][h] fp32: dx = (res ? res : 0) +
+// the RMSNorm input gradient, fp32 [rows][h]; lo (optional) receives dx in
+// dtype as well, in panel layout when lo_panel (bf16). dg [h] fp32 receives
+// the gain gradient summed over the rows, through part (rmsnorm_bwd_part_bytes
+// of scratch) in a fixed order. g in dtype.
+size_t rmsnorm_bwd_part_bytes(int32_t rows, int32_t h);
+hipError_t launch_rmsnorm_bwd(const float *x, const void *g, const float *d, const float *res, float *dx, void *lo,
+                              bool lo_panel, int32_t rows, int32_t h, float eps, int dtype, float *part, float *dg,
+                              hipStream_t s);
+// out [n][D (wa + 2 wb)] in dtype (bf16 panel layout when out_panel): shard
+// j's columns are a's columns j*wa.., then b's j*wb.., then c's j*wb.. (fp32
+// sources [n][D wa] and [n][D wb]); wa, wb multiples of 4. D = 1, wb = 0
+// converts a alone.
+hipError_t launch_pack_cols(int dtype, const float *a, const float *b, const float *c, int32_t n, int32_t D,
+                            int32_t wa, int32_t wb, void *out, bool out_panel, hipStream_t s);
+
 // Rotary embedding (optional): table[t][i] = (cos, sin) of pos(t) *
 // base^(-2i/Dh) for local rows t < n, pairs i < Dh/2 (computed in fp64).
 hipError_t launch_rope_table(ZigzagMap zz, int32_t n, int32_t Dh, float base, float2 *table, hipStream_t s);
@@ -123,6 +140,11 @@ hipError_t launch_wgrad(int dtype, const void *a, bool a_panel, int32_t M, const
 // dx = (res ? res : 0) + dz w1t^T: dz [n][F] (panel when a_panel), w1t [h][F].
 hipError_t launch_mlp_bwd_dx(int dtype, const void *dz, bool a_panel, int32_t n, int32_t F, const void *w1t,
                              int32_t h, const float *res, float *dx, hipStream_t s);
+
+// Plain product out [M][N] = A [M][K] B [N][K]^T (A in panel layout when
+// a_panel), out row-major in out_dtype (bf16 only with bf16 operands).
+hipError_t launch_gemm_nt(int dtype, const void *A, bool a_panel, int32_t M, int32_t K, const void *B, int32_t N,
+                          void *out, int out_dtype, hipStream_t s);
 
 // Leading rows in fp32: the same products for m <= kLeadRows rows with fp32
 // activations (row-major) and the bf16 weights, computed to fp32 accuracy.

@@ -31,7 +31,8 @@ from __future__ import annotations
 import dataclasses
 
 # workspace kinds, as in the C header
-WS_MLP, WS_LAYER, WS_MLP_BWD, WS_ATTN_BWD = 0, 1, 2, 3
+WS_MLP, WS_LAYER, WS_MLP_BWD, WS_ATTN_BWD, WS_LAYER_BWD = 0, 1, 2, 3, 4
+NORM_BWD_ROWS = 16  # rows per block of the RMSNorm backward (one gain partial each)
 
 LEAD_ROWS = 64  # rank 0's leading positions that the bf16 layer recomputes in fp32
 
@@ -117,6 +118,16 @@ def workspace_bytes(m: Model, kind: int) -> int:
     WS_MLP_BWD: W1 stacked in ring order, W1^T and W2^T ([F][h] each), x^T
       and dy^T ([h][N]), Z^T and GELU(Z)^T ([F][N]), all in dtype.
     WS_ATTN_BWD: log-sum-exp and Delta of every (head, local row), fp32.
+    WS_LAYER_BWD: dh1 and dq, fp32 [N][h] each, kept between the two
+      phases; then the larger of the phases' own buffers. First phase: nine
+      [N][h] in dtype (normed input, Q, attention output and its transpose,
+      normed h1, dy, dh1 and its transpose, do), three fp32 [N][h] (attention
+      output, h1, MLP input gradient), W_O^T [h][h], the forward's
+      log-sum-exp [H][N] fp32, WS_ATTN_BWD, the gain partials (one fp32 row
+      of h per 16 tokens) and WS_MLP_BWD. Second phase: normed input and its
+      transpose, [dq|dk|dv] and its transpose ([N][h + 2 Hkv Dh] each), its
+      weights transposed [h][h + 2 Hkv Dh] (all in dtype), dxn fp32 [N][h],
+      the gain partials.
     Each buffer starts on a 256-byte boundary."""
     e, N, h, F = _elem(m.dtype), m.N, m.h, m.F
     if kind == WS_MLP:
@@ -125,6 +136,14 @@ def workspace_bytes(m: Model, kind: int) -> int:
         return 2 * _align256(m.H * N * 4)
     if kind == WS_MLP_BWD:
         return 3 * _align256(F * h * e) + 2 * _align256(h * N * e) + 2 * _align256(F * N * e)
+    if kind == WS_LAYER_BWD:
+        nh, nh4 = _align256(N * h * e), _align256(N * h * 4)
+        k3 = h + 2 * m.kv_heads * m.Dh
+        part = _align256(-(-N // NORM_BWD_ROWS) * h * 4)
+        first = (9 * nh + 3 * nh4 + _align256(h * h * e) + _align256(m.H * N * 4) + workspace_bytes(m, WS_ATTN_BWD)
+                 + part + workspace_bytes(m, WS_MLP_BWD))
+        second = 2 * nh + 2 * _align256(N * k3 * e) + _align256(h * k3 * e) + nh4 + part
+        return 2 * nh4 + max(first, second)
     if kind != WS_LAYER:
         raise ValueError(f"unknown workspace kind {kind}")
     total = 2 * _align256(N * h * e) + _align256(N * F * e)
@@ -172,8 +191,10 @@ def rank_memory(m: Model, train: bool = False) -> dict:
     dtype copy); each layer's fp32 input kept for its backward, which
     recomputes the rest of the layer; and the peak of one layer's backward:
     its fp32 dK/dV over the whole gathered sequence (the rank's contribution
-    before the reduce-scatter that returns each row to its owner), the two
-    backward workspaces and the fp32 weight gradients of the received shards."""
+    before the reduce-scatter that returns each row to its owner) and the
+    summed rows the rank gets back, the layer backward's workspace
+    (WS_LAYER_BWD), the fp32 output gradient and input gradient [N][h], and
+    the fp32 weight gradients of the received shards."""
     e = _elem(m.dtype)
     W = layer_weight_elems(m)
     kvw = 2 * m.kv_heads * m.Dh  # K and V elements per token
@@ -189,8 +210,8 @@ def rank_memory(m: Model, train: bool = False) -> dict:
         out["grads_owned"] = m.layers * W * 4 // m.D
         out["optimizer_owned"] = m.layers * W * 12 // m.D
         out["saved_layer_inputs"] = m.layers * m.N * m.h * 4
-        bwd_ws = workspace_bytes(m, WS_MLP_BWD) + workspace_bytes(m, WS_ATTN_BWD)
-        out["backward_peak"] = m.S * kvw * 4 + bwd_ws + (W * 4 - W * 4 // m.D)
+        out["backward_peak"] = ((m.S + m.N) * kvw * 4 + workspace_bytes(m, WS_LAYER_BWD) + 2 * m.N * m.h * 4
+                                + (W * 4 - W * 4 // m.D))
     out["total"] = sum(out.values())
     return out
 
