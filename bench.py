@@ -98,6 +98,35 @@ def traffic_from_profile():
     return {cls: v for cls, v in out.items() if cls in srcs and sha.get(srcs[cls]) == _src_sha(srcs[cls])}
 
 
+SQ_FILE = os.path.join(ROOT, "profiles", "layer7b_sq_counters.txt")
+
+
+def sq_from_profile():
+    """{kernel class: {"sclk_ghz", "mfma_busy"}} from the committed shader
+    counter summary of the layer step, for the classes of TRAFFIC_KERNELS
+    whose source is unchanged since the counters were taken. The output
+    projection and the MLP down product share one kernel name there, so
+    they get the average of the two."""
+    if not os.path.exists(SQ_FILE):
+        return {}
+    sha, rows = {}, []
+    for line in open(SQ_FILE):
+        if line.startswith("source_sha256 "):
+            _, name, h = line.split()
+            sha[name] = h
+        elif " | " in line and not line.startswith(("#", "kernel |")):
+            rows.append([c.strip() for c in line.split(" | ")])
+    out = {}
+    for cls, subs, _, src in TRAFFIC_KERNELS:
+        if sha.get(src) != _src_sha(src):
+            continue
+        for r in rows:
+            if all(x in r[0] for x in subs) and r[1] != "-" and r[2] != "-":
+                out[cls] = {"sclk_ghz": float(r[1]), "mfma_busy": float(r[2])}
+                break
+    return out
+
+
 def summarize_traffic(csvs, copy_mib):
     """HBM bytes per launch of the layer step's kernels from the L2-to-memory
     request counters of rocprofv3 (two passes, TRAFFIC_PASSES).
@@ -347,76 +376,14 @@ def summarize_sq(csvs, workload="layer"):
                      f"{fmt('mfma_valu_coexec')} | "
                      f"{fmt('lds_active')} | {fmt('lds_wait')} | {ratio(va)} | {ratio(sa)} | {ratio(ld)} | "
                      f"{fmt('trans_per_mfma')} | {fmt('bank_conflicts_per_lds_inst')}")
+    # the kernel sources the counters were taken on (bench.py reads a
+    # kernel's clock from here only while its source is unchanged)
+    for src in ("attention.hip", "attention_bwd.hip", "gemm.hip", "lead.hip", "rows.hip"):
+        lines.append(f"source_sha256 {src} {_src_sha(src)}")
     out = os.path.join(ROOT, "profiles", fname)
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
-
-
-class ClockSampler:
-    """Mean shader (GFX) clock of the benchmark's GPU while the timed steps
-    run, sampled every few ms from the amdsmi metrics table on a background
-    thread. The device is matched to cuda:0 by PCI bus; anything unavailable
-    gives None."""
-
-    def __init__(self, torch, period_s=0.004):
-        import threading
-        self.period, self.samples, self.handle, self.smi = period_s, [], None, None
-        self.sources = set()  # metrics fields the samples came from
-        self.stop_ev = threading.Event()
-        self.thread = None
-        try:
-            import amdsmi
-            props = torch.cuda.get_device_properties(0)
-            amdsmi.amdsmi_init()
-            for h in amdsmi.amdsmi_get_processor_handles():
-                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
-                dom, bus = bdf.split(":")[0], bdf.split(":")[1]
-                if int(bus, 16) == props.pci_bus_id and int(dom, 16) == props.pci_domain_id:
-                    self.handle, self.smi = h, amdsmi
-                    break
-        except Exception:
-            self.handle = None
-
-    @staticmethod
-    def _valid(v):
-        return isinstance(v, (int, float)) and 0 < v < 10000
-
-    def _run(self):
-        # the metrics table's current clock of each XCD (the effective clock
-        # under power limits), else its single current or average clock
-        while not self.stop_ev.is_set():
-            try:
-                m = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
-                per_xcd = [v for v in (m.get("current_gfxclks") or []) if self._valid(v)]
-                if per_xcd:
-                    self.samples.append(statistics.mean(per_xcd))
-                    self.sources.add("current_gfxclks")
-                elif self._valid(m.get("current_gfxclk")):
-                    self.samples.append(m["current_gfxclk"])
-                    self.sources.add("current_gfxclk")
-                elif self._valid(m.get("average_gfxclk_frequency")):
-                    self.samples.append(m["average_gfxclk_frequency"])
-                    self.sources.add("average_gfxclk_frequency")
-            except Exception:
-                pass
-            self.stop_ev.wait(self.period)
-
-    def start(self):
-        if self.handle is not None:
-            import threading
-            self.thread = threading.Thread(target=self._run, daemon=True)
-            self.thread.start()
-
-    def stop(self):
-        if self.thread is None:
-            return None
-        self.stop_ev.set()
-        self.thread.join()
-        # readings below 500 MHz are idle-state values left in the metrics
-        # table from before the load started (a loaded part runs far above)
-        self.samples = [v for v in self.samples if v >= 500]
-        return round(statistics.mean(self.samples), 1) if self.samples else None
 
 
 def main():
@@ -434,6 +401,9 @@ def main():
                          "multi-head as in the pages' model)")
     ap.add_argument("--mlp", choices=["gelu", "swiglu"], default="gelu",
                     help="MLP form for the layer and MLP workloads (gelu: the pages' two-matrix MLP)")
+    ap.add_argument("--plain-pds", action="store_true",
+                    help="attention backward workloads: P and dS rounded once to bf16 (TSP_ATTN_BWD_PLAIN_PDS) "
+                         "instead of the hi + lo pair")
     ap.add_argument("--cpu-rows", type=int, default=384, help="rows in the CPU oracle sample (0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warmup, run one plain device-to-device copy of this many MiB (a known-size "
@@ -591,17 +561,26 @@ def main():
             tsp.tsp_zigzag_attn_lse(shape, qd, kf, vf, o_f, lse_f)
 
             def step():
-                tsp.tsp_zigzag_attn_bwd_lse(shape, qd, kf, vf, o_f, lse_f, dod, dq, dk, dv, ws)
+                if args.plain_pds:
+                    tsp.tsp_zigzag_attn_bwd_ex(shape, qd, kf, vf, o_f, lse_f, dod, dq, dk, dv,
+                                               tsp.TSP_ATTN_BWD_PLAIN_PDS, ws)
+                else:
+                    tsp.tsp_zigzag_attn_bwd_lse(shape, qd, kf, vf, o_f, lse_f, dod, dq, dk, dv, ws)
         else:
             def step():
-                tsp.tsp_zigzag_attn_bwd(shape, qd, kf, vf, dod, dq, dk, dv, ws)
+                if args.plain_pds:
+                    tsp.tsp_zigzag_attn_bwd_ex(shape, qd, kf, vf, None, None, dod, dq, dk, dv,
+                                               tsp.TSP_ATTN_BWD_PLAIN_PDS, ws)
+                else:
+                    tsp.tsp_zigzag_attn_bwd(shape, qd, kf, vf, dod, dq, dk, dv, ws)
         # algorithmic: 2.5 x the forward's 4*Dh flops per unmasked (query, key)
         # pair and head (S recomputed, dP, dV, dK, dQ)
         step_flops = 2.5 * flops["attention"]
         step_exps = sh.H * attn_pairs(sh.S, sh.D, r)
         workload = (f"{'tsp_zigzag_attn_bwd_lse' if args.workload == 'attn_bwd_lse' else 'tsp_zigzag_attn_bwd'}: "
                     f"32x128 heads{kv_note}, S=131072, 16384 zigzag queries of rank {r} of D=8; dq, dk, dv in fp32"
-                    + ("; the forward's fp32 O and log-sum-exp given" if args.workload == "attn_bwd_lse" else ""))
+                    + ("; the forward's fp32 O and log-sum-exp given" if args.workload == "attn_bwd_lse" else "")
+                    + ("; P and dS rounded once to bf16" if args.plain_pds else "; P and dS as bf16 hi + lo"))
     elif args.workload == "layers32":
         # 32 layers resident in HBM (82 GB of weights and K/V), each with its
         # own weights and remote K/V, generated on the GPU from a fixed seed:
@@ -676,10 +655,8 @@ def main():
 
     tsp.profile_reset()
     tsp.profile_enable(True)
-    clock = ClockSampler(torch)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    clock.start()
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
@@ -687,7 +664,6 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sclk_mhz = clock.stop()
     tsp.profile_enable(False)
     ms_step = ev0.elapsed_time(ev1) / args.steps
     kernels = {}
@@ -723,6 +699,12 @@ def main():
         if cls in kernels:
             kernels[cls]["hbm_bytes"] = nbytes
             kernels[cls]["hbm_gb_s"] = nbytes / (kernels[cls]["ms_per_launch"] * 1e-3) / 1e9
+    # effective shader clock and MFMA-busy share per kernel from the committed
+    # shader-counter summary of the same step (when the source is unchanged)
+    sq = sq_from_profile() if default_layer else {}
+    for cls, v in sq.items():
+        if cls in kernels:
+            kernels[cls].update(v)
     roofline = None
     if args.workload == "layer_bwd" and "attn_bwd" in kernels:
         # the attention backward: 4.40e13 of the step's 5.72e13 algorithmic flops
@@ -737,6 +719,11 @@ def main():
         roofline = {"kernel": "attn_bf16_kernel<128>", "bound": "mfma", "achieved": achieved,
                     "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_BF16,
                     "traffic": hbm.get("attention")}
+        if "attention" in sq:
+            # the published peak is at 2.4 GHz; the counters give the clock the
+            # kernel actually ran at
+            roofline["sclk_ghz"] = sq["attention"]["sclk_ghz"]
+            roofline["frac_of_peak_at_sclk"] = roofline["frac"] * 2.4 / sq["attention"]["sclk_ghz"]
     elif "attn_bwd" in kernels:
         t_b = kernels["attn_bwd"]["ms_per_launch"] * 1e-3
         achieved = 2.5 * flops["attention"] / t_b / 1e12
@@ -785,13 +772,6 @@ def main():
                    "parallelism": "one rank of a D=8 folded TP+SP axis", "rope_base": args.rope_base,
                    "Hkv": sh.kv_heads, "mlp": sh.mlp},
         "pct_bf16_mfma_peak": 100.0 * step_flops / (ms_step * 1e-3) / PEAK_BF16,
-        # the same against the dense peak scaled to the mean shader clock seen
-        # during the timed steps (the published peak assumes 2.4 GHz)
-        "sclk_mhz_mean": sclk_mhz,
-        "sclk_source": ("amdsmi gpu metrics: " + ", ".join(sorted(clock.sources))) if sclk_mhz else None,
-        "sclk_samples": len(clock.samples),
-        "pct_bf16_mfma_peak_at_sclk": (100.0 * step_flops / (ms_step * 1e-3) / (PEAK_BF16 * sclk_mhz / 2400.0)
-                                       if sclk_mhz else None),
         "algorithmic_tflop_per_step": step_flops / 1e12,
         "softmax_exps_per_step": step_exps,
         "roofline": roofline,

@@ -276,6 +276,24 @@ tsp_status tsp_zigzag_attn_bwd(const tsp_shape *shape, const void *q, const void
 tsp_status tsp_zigzag_attn_bwd_noalloc(const tsp_shape *shape, const void *q, const void *k, const void *v,
                                        const void *dout, float *dq, float *dk, float *dv, void *stream);
 
+/* Flags of tsp_zigzag_attn_bwd_ex. */
+enum { TSP_ATTN_BWD_PLAIN_PDS = 1 };
+
+/* tsp_zigzag_attn_bwd with flags, and with the forward's statistics
+ * optional: o and lse both NULL (the kernels take the row statistics
+ * themselves, as tsp_zigzag_attn_bwd) or both given (as
+ * tsp_zigzag_attn_bwd_lse, bf16 only). TSP_ATTN_BWD_PLAIN_PDS (bf16 inputs,
+ * else TSP_ERR_UNSUPPORTED): P and dS enter their products rounded once to
+ * bf16, one matrix product each, instead of as the hi + lo pair; this saves
+ * a third of the matrix products and most of the conversions. The error is
+ * then that of common flash-attention backward kernels: norm-wise about the
+ * bf16 rounding unit, but single elements of the largest gradient rows can
+ * be off by several percent of the tensor's rms. tsp_layer_bwd uses it.
+ * Unknown flags: TSP_ERR_INVALID_ARG. Otherwise as tsp_zigzag_attn_bwd. */
+tsp_status tsp_zigzag_attn_bwd_ex(const tsp_shape *shape, const void *q, const void *k, const void *v,
+                                  const float *o, const float *lse, const void *dout, float *dq, float *dk,
+                                  float *dv, uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
 /* tsp_zigzag_attn for the backward's use: bf16 inputs (else
  * TSP_ERR_UNSUPPORTED), plain q, o in fp32 [S/D][H][Dh], and also lse
  * [H][S/D] fp32, the natural log of each row's softmax denominator,
@@ -381,8 +399,9 @@ tsp_status tsp_layer_fwd(const tsp_shape *shape, const tsp_layer_weights *w, con
  *    statistics), h1 = x + o W_O^T, hn = RMSNorm(h1) g_mlp; then the MLP
  *    ring backward of tsp_mlp_ring_bwd on hn and dy, the second RMSNorm's
  *    backward, dh1 = dy + that; do = dh1 W_O, dW_O = dh1^T o; the attention
- *    backward of tsp_zigzag_attn_bwd_lse, giving dq (kept in ws) and this
- *    rank's contribution dk_full, dv_full to every key/value row.
+ *    backward of tsp_zigzag_attn_bwd_ex (the forward's statistics given,
+ *    TSP_ATTN_BWD_PLAIN_PDS), giving dq (kept in ws) and this rank's
+ *    contribution dk_full, dv_full to every key/value row.
  *  TSP_BWD_QKV, once dk_loc, dv_loc hold the summed gradients of the rank's
  *    own K/V rows: dxn = [dq | dk | dv] W_QKV over the shards,
  *    dW_QKV,j = [dq_j | dk_j | dv_j]^T xn, and dx = dh1 + the first
@@ -405,9 +424,10 @@ tsp_status tsp_layer_fwd(const tsp_shape *shape, const tsp_layer_weights *w, con
  *    bytes; TSP_BWD_QKV reads what TSP_BWD_ATTN left there (dh1 and dq),
  *    so both phases use the same ws.
  * Rounding (bf16): xn, Q, o (for the products), hn, dy (for the MLP
- * products), dh1 (for its products), do, and dq/dk/dv (for the QKV products)
- * are rounded once to bf16; RMSNorm statistics, the residual-stream
- * gradients dh1 and dx and all accumulation are fp32. Outputs must not
+ * products), dh1 (for its products), do, the attention's P and dS, and
+ * dq/dk/dv (for the QKV products) are rounded once to bf16; RMSNorm
+ * statistics, the residual-stream gradients dh1 and dx and all
+ * accumulation are fp32. Outputs must not
  * overlap inputs or each other. */
 tsp_status tsp_layer_bwd(const tsp_shape *shape, const tsp_layer_weights *w, const float *x,
                          const void *k_full, const void *v_full, const float *dy, float *dk_full,

@@ -67,7 +67,9 @@ def assert_close(got, want, tol, what, rms=None):
 # same rounding points reaches 6.4% on one key row of the 7B K gradient
 # sampled over 14 queries. A wrong or missing row errs by about its whole
 # size, and one missing term of seven by about 40%, so 25% still catches
-# them. Rows whose expected value is exactly zero must come out exactly zero.
+# them. A row whose expected value is exactly zero (a query at position 0
+# has dq = 0) is held to the floor alone: its rounding residue is not zero
+# when Delta comes from the forward's stored output.
 TOL_BWD_BF16 = 1e-2
 TOL_BWD_BF16_ROW = 0.25
 
@@ -81,16 +83,13 @@ def assert_close_nw(got, want, what, tol=TOL_BWD_BF16, tol_row=TOL_BWD_BF16_ROW)
     if want.ndim > 1:
         G, W = got.reshape(want.shape[0], -1), want.reshape(want.shape[0], -1)
         wn = np.linalg.norm(W, axis=1)
-        zero = wn == 0
-        assert not np.any(G[zero]), f"{what}: rows expected zero are not"
-        nz = wn[~zero]
-        floor = 0.1 * float(np.median(nz)) if nz.size else 0.0
-        row = np.linalg.norm(G - W, axis=1)[~zero] / np.maximum(nz, floor)
-        worst = float(row.max()) if row.size else 0.0
-        where = ""
-        if row.size:
-            at = int(np.flatnonzero(~zero)[np.argmax(row)])
-            where = f" at row {at} (norm {wn[at]:.3e}, median {np.median(nz):.3e})"
+        nz = wn[wn > 0]
+        assert nz.size, f"{what}: expected tensor is zero"
+        floor = 0.1 * float(np.median(nz))
+        row = np.linalg.norm(G - W, axis=1) / np.maximum(wn, floor)
+        worst = float(row.max())
+        at = int(np.argmax(row))
+        where = f" at row {at} (norm {wn[at]:.3e}, median {np.median(nz):.3e})"
     else:
         worst, where = err, ""
     log(f"  {what}: norm-wise err = {err:.3e} (tol {tol:g}), worst row = {worst:.3e}{where} (tol {tol_row:g})")

@@ -259,6 +259,26 @@ def test_attn_bwd_workspace_and_errors():
     assert call(shape=_shape(dtype="bf16", Dh=32, H=8))[0] == tsp.TSP_ERR_UNSUPPORTED
 
 
+def test_attn_bwd_ex_errors():
+    s = _shape(dtype="bf16")
+    need = tsp.workspace_size(s, tsp.TSP_WS_ATTN_BWD)
+    q, k, v, do = (FAKE + (i << 32) for i in range(4))
+    dq, dk, dv, ws, o, lse = (FAKE + ((5 + i) << 32) for i in range(6))
+
+    def call(shape=s, o=None, lse=None, flags=tsp.TSP_ATTN_BWD_PLAIN_PDS):
+        with pytest.raises(tsp.TspError) as ei:
+            tsp.tsp_zigzag_attn_bwd_ex(shape, q, k, v, o, lse, do, dq, dk, dv, flags, ws, need - 1, stream=0)
+        return ei.value.status, tsp.lib().tsp_last_error()
+
+    assert call()[0] == tsp.TSP_ERR_WORKSPACE  # everything else valid
+    st, msg = call(flags=2)
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"flags" in msg
+    st, msg = call(o=o)  # o without lse
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"lse is NULL" in msg
+    assert call(o=o, lse=lse)[0] == tsp.TSP_ERR_WORKSPACE
+    assert call(shape=_shape())[0] == tsp.TSP_ERR_UNSUPPORTED  # plain P and dS in fp32
+
+
 def test_attn_bwd_noalloc_errors():
     """The entry point without a workspace checks every argument, and the size
     of its static scratch, before it looks the scratch up or enqueues

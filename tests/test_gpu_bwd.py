@@ -10,7 +10,7 @@ import pytest
 import oracle
 import synth
 import tsp_rank_local_amd as tsp
-from gpu_util import TOL_BF16, TOL_F32, assert_close, down, f64, log, torch_cuda, up
+from gpu_util import TOL_BF16, TOL_F32, assert_close, assert_close_nw, down, f64, log, torch_cuda, up
 
 pytestmark = pytest.mark.gpu
 
@@ -197,9 +197,10 @@ def test_mlp_ring_bwd_7b(torch):
 
 
 # ---------------------------------------------------------------- attention backward
-def _attn_bwd_run(torch, s, q, k, v, do, dtype, from_fwd=False):
+def _attn_bwd_run(torch, s, q, k, v, do, dtype, from_fwd=False, flags=None):
     """tsp_zigzag_attn_bwd, or (from_fwd) tsp_zigzag_attn_lse followed by
-    tsp_zigzag_attn_bwd_lse; returns dq, dk, dv (float64)."""
+    tsp_zigzag_attn_bwd_lse; with flags, tsp_zigzag_attn_bwd_ex (statistics
+    from the forward when from_fwd); returns dq, dk, dv (float64)."""
     N, H, Dh = q.shape
     S, Hkv = k.shape[0], k.shape[1]
     qd, kd, vd, dod = up(q, dtype), up(k, dtype), up(v, dtype), up(do, dtype)
@@ -211,7 +212,10 @@ def _attn_bwd_run(torch, s, q, k, v, do, dtype, from_fwd=False):
     dq = torch.full((N, H, Dh), float("nan"), dtype=torch.float32, device="cuda")
     dk = torch.full((S, Hkv, Dh), float("nan"), dtype=torch.float32, device="cuda")
     dv = torch.full((S, Hkv, Dh), float("nan"), dtype=torch.float32, device="cuda")
-    if from_fwd:
+    if flags is not None:
+        tsp.tsp_zigzag_attn_bwd_ex(s, qd, kd, vd, o if from_fwd else None, lse if from_fwd else None, dod, dq, dk,
+                                   dv, flags, ws)
+    elif from_fwd:
         tsp.tsp_zigzag_attn_bwd_lse(s, qd, kd, vd, o, lse, dod, dq, dk, dv, ws)
     else:
         tsp.tsp_zigzag_attn_bwd(s, qd, kd, vd, dod, dq, dk, dv, ws)
@@ -341,3 +345,52 @@ def test_attn_bwd_7b(torch, from_fwd):
     err = float(np.abs(dk.sum(axis=0)).max())
     log(f"  sum over keys of dK: max {err:.3e} (dK rms {rms_row:.3e})")
     assert err <= TOL_BF16 * rms_row * np.sqrt(S)
+
+
+# ---------------------------------------------------------------- plain bf16 P and dS
+@pytest.mark.parametrize("S,D,H,Hkv,Dh,dtype", [c for c in ATTN_BWD_CASES if c[-1] == "bf16"])
+@pytest.mark.parametrize("from_fwd", [False, True])
+def test_attn_bwd_plain_pds_every_rank(torch, S, D, H, Hkv, Dh, dtype, from_fwd):
+    """tsp_zigzag_attn_bwd_ex with TSP_ATTN_BWD_PLAIN_PDS (P and dS rounded
+    once to bf16, as the layer backward takes them), statistics computed or
+    from the forward, every rank: the norm-wise rule of the bf16 gradients
+    against the oracle."""
+    shape = synth.LayerShape(S=S, D=D, h=H * Dh, H=H, Dh=Dh, F=64 * D, dtype=dtype, Hkv=Hkv)
+    N = S // D
+    k, v = synth.remote_kv(shape, seed=51)
+    for r in range(D):
+        q = synth.normal((N, H, Dh), 51, synth.TID_Q, r, dtype=dtype)
+        do = synth.normal((N, H, Dh), 51, synth.TID_DY, r, dtype=dtype)
+        pos = oracle.zigzag_positions(S, D, r)
+        want = oracle.causal_attention_backward(f64(q, dtype), f64(k, dtype), f64(v, dtype), pos, shape.scale,
+                                                f64(do, dtype))
+        s = tsp.make_shape(S, D, r, H * Dh, H, Dh, 64 * D, dtype=dtype, Hkv=Hkv)
+        log(f"attention backward, plain P and dS, S={S} D={D} r={r} H={H} Hkv={Hkv} Dh={Dh} from_fwd={from_fwd}")
+        dq, dk, dv = _attn_bwd_run(torch, s, q, k, v, do, dtype, from_fwd, tsp.TSP_ATTN_BWD_PLAIN_PDS)
+        assert_close_nw(dq, want["dq"], f"dq r={r}")
+        assert_close_nw(dk, want["dk"], f"dk r={r}")
+        assert_close_nw(dv, want["dv"], f"dv r={r}")
+        assert not dk[pos.max() + 1:].any() and not dv[pos.max() + 1:].any()
+
+
+@pytest.mark.timeout(900)
+def test_attn_bwd_plain_pds_7b(torch):
+    """The 7B attention backward with plain bf16 P and dS and the forward's
+    statistics (the layer backward's call), rank 0: dq of every local row and
+    dK, dV of every key row for one whole head, norm-wise."""
+    SH = synth.SEVEN_B
+    N, S, H, Dh = SH.N, SH.S, SH.H, SH.Dh
+    q = synth.attn_queries(SH, seed=53)
+    k, v = synth.remote_kv(SH, seed=53)
+    do = synth.normal((N, H, Dh), 53, synth.TID_DY, 0, dtype="bf16")
+    s = tsp.make_shape(S, SH.D, 0, SH.h, H, Dh, SH.F, dtype="bf16")
+    log("attention backward 7B, rank 0, plain P and dS, statistics from the forward")
+    dq, dk, dv = _attn_bwd_run(torch, s, q, k, v, do, "bf16", True, tsp.TSP_ATTN_BWD_PLAIN_PDS)
+    pos = oracle.zigzag_positions(S, SH.D, 0)
+    hd = 5
+    sl = slice(hd, hd + 1)
+    want = oracle.causal_attention_backward(f64(q[:, sl], "bf16"), f64(k[:, sl], "bf16"), f64(v[:, sl], "bf16"),
+                                            pos, SH.scale, f64(do[:, sl], "bf16"))
+    assert_close_nw(dq[:, sl], want["dq"], f"dq of head {hd}, all {N} rows")
+    assert_close_nw(dk[:, sl], want["dk"], f"dK of head {hd}, all {S} keys")
+    assert_close_nw(dv[:, sl], want["dv"], f"dV of head {hd}, all {S} keys")

@@ -19,11 +19,12 @@ __all__ = [
     "TspError", "TspShape", "TspLayerWeights", "lib", "make_shape", "workspace_size",
     "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_zigzag_attn_ex", "tsp_mlp_ring",
     "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_zigzag_attn_bwd_noalloc", "tsp_zigzag_attn_lse",
-    "tsp_zigzag_attn_bwd_lse", "tsp_layer_fwd", "tsp_layer_bwd", "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z", "profile_enable",
+    "tsp_zigzag_attn_bwd_lse", "tsp_zigzag_attn_bwd_ex", "tsp_layer_fwd", "tsp_layer_bwd", "tsp_mlp_ring_z",
+    "tsp_mlp_ring_bwd_z", "profile_enable",
     "profile_reset", "profile_read", "TspLayerGrads",
     "TSP_F32", "TSP_BF16", "TSP_ATTN_Q_LOG2_SCALED", "TSP_PHASE_KV", "TSP_PHASE_REST", "TSP_PHASE_ALL",
     "TSP_WS_MLP", "TSP_WS_LAYER", "TSP_WS_MLP_BWD", "TSP_WS_ATTN_BWD", "TSP_WS_LAYER_BWD", "TSP_BWD_ATTN", "TSP_BWD_QKV",
-    "TSP_BWD_ALL", "TSP_MLP_GELU", "TSP_MLP_SWIGLU", "MLP_KINDS",
+    "TSP_BWD_ALL", "TSP_ATTN_BWD_PLAIN_PDS", "TSP_MLP_GELU", "TSP_MLP_SWIGLU", "MLP_KINDS",
     "KERNEL_CLASSES", "EXPORTED_SYMBOLS",
 ]
 
@@ -35,6 +36,7 @@ TSP_PHASE_KV, TSP_PHASE_REST, TSP_PHASE_ALL = 1, 2, 3
 TSP_WS_MLP, TSP_WS_LAYER, TSP_WS_MLP_BWD, TSP_WS_ATTN_BWD, TSP_WS_LAYER_BWD = 0, 1, 2, 3, 4
 TSP_BWD_ATTN, TSP_BWD_QKV, TSP_BWD_ALL = 1, 2, 3
 TSP_ATTN_Q_LOG2_SCALED = 1
+TSP_ATTN_BWD_PLAIN_PDS = 1
 TSP_MLP_GELU, TSP_MLP_SWIGLU = 0, 1
 MLP_KINDS = {"gelu": TSP_MLP_GELU, "swiglu": TSP_MLP_SWIGLU}
 TSP_MAX_D = 64
@@ -46,7 +48,8 @@ EXPORTED_SYMBOLS = [
     "tsp_status_string", "tsp_last_error", "tsp_abi_version", "tsp_workspace_size",
     "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_zigzag_attn_ex", "tsp_mlp_ring",
     "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_zigzag_attn_bwd_noalloc", "tsp_zigzag_attn_lse",
-    "tsp_zigzag_attn_bwd_lse", "tsp_layer_fwd", "tsp_layer_bwd", "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z", "tsp_profile_enable",
+    "tsp_zigzag_attn_bwd_lse", "tsp_zigzag_attn_bwd_ex", "tsp_layer_fwd", "tsp_layer_bwd", "tsp_mlp_ring_z",
+    "tsp_mlp_ring_bwd_z", "tsp_profile_enable",
     "tsp_profile_reset", "tsp_profile_read",
 ]
 
@@ -109,6 +112,7 @@ def lib() -> ctypes.CDLL:
     L.tsp_mlp_ring_bwd_z.argtypes = [shp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp,
                                      ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp]
     L.tsp_zigzag_attn_bwd_lse.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.tsp_zigzag_attn_bwd_ex.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz, vp]
     L.tsp_layer_fwd.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, ctypes.c_uint, vp, sz, vp]
     L.tsp_layer_bwd.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 ctypes.POINTER(TspLayerGrads), ctypes.c_uint, vp, sz, vp]
@@ -120,7 +124,8 @@ def lib() -> ctypes.CDLL:
     for name in ("tsp_workspace_size", "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn",
                  "tsp_zigzag_attn_ex", "tsp_mlp_ring", "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd",
                  "tsp_zigzag_attn_bwd_noalloc", "tsp_layer_fwd", "tsp_layer_bwd",
-                 "tsp_zigzag_attn_lse", "tsp_zigzag_attn_bwd_lse", "tsp_mlp_ring_z", "tsp_mlp_ring_bwd_z",
+                 "tsp_zigzag_attn_lse", "tsp_zigzag_attn_bwd_lse", "tsp_zigzag_attn_bwd_ex", "tsp_mlp_ring_z",
+                 "tsp_mlp_ring_bwd_z",
                  "tsp_profile_read"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -243,6 +248,16 @@ def tsp_zigzag_attn_bwd_lse(shape: TspShape, q, k, v, o, lse, dout, dq, dk, dv, 
     _check(lib().tsp_zigzag_attn_bwd_lse(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                          _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), int(ws_bytes),
                                          _stream(stream)))
+
+
+def tsp_zigzag_attn_bwd_ex(shape: TspShape, q, k, v, o, lse, dout, dq, dk, dv, flags, ws, ws_bytes=None,
+                           stream=None) -> None:
+    """o and lse: both None, or the forward's fp32 output and log-sum-exp."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().tsp_zigzag_attn_bwd_ex(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                        _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), int(flags), _ptr(ws),
+                                        int(ws_bytes), _stream(stream)))
 
 
 def tsp_mlp_ring_bwd(shape: TspShape, x, w1, w2, dy, dx_residual, dx, dw1, dw2, ws, ws_bytes=None,

@@ -535,9 +535,12 @@ tsp_status tsp_zigzag_attn_lse(const tsp_shape *s, const void *q, const void *k,
 // array (tsp_zigzag_attn_bwd_noalloc), looked up after every argument check.
 static tsp_status attn_bwd(const tsp_shape *s, const void *q, const void *k, const void *v, const float *o, const float *lse,
                     const void *dout, float *dq, float *dk, float *dv, void *ws, size_t ws_bytes, void *stream_,
-                    bool static_ws = false) {
+                    bool static_ws = false, uint32_t flags = 0) {
   tsp_status st = check_attn_shape(s);
   if (st) return st;
+  if (flags & ~(uint32_t)TSP_ATTN_BWD_PLAIN_PDS) return fail(TSP_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  const bool plain = (flags & TSP_ATTN_BWD_PLAIN_PDS) != 0;
+  if (plain && s->dtype != TSP_BF16) return fail(TSP_ERR_UNSUPPORTED, "TSP_ATTN_BWD_PLAIN_PDS takes bf16 inputs");
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(dout, "dout")) ||
       (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")) ||
       (!static_ws && (st = check_ptr(ws, "ws"))))
@@ -577,7 +580,7 @@ static tsp_status attn_bwd(const tsp_shape *s, const void *q, const void *k, con
   TSP_LAUNCH(TSP_K_ATTN_BWD,
              tsp::launch_attention_bwd(s->dtype, q, k, v, dout, dq, dk, dv, lse_ws, delta, s->S, (int32_t)N, s->H,
                                        kv_heads(s), s->Dh, s->scale, tsp::make_zigzag(s->S, s->D, s->r), stream, o,
-                                       lse),
+                                       lse, !plain),
              "attention backward");
   return ok();
 }
@@ -590,6 +593,13 @@ tsp_status tsp_zigzag_attn_bwd(const tsp_shape *s, const void *q, const void *k,
 tsp_status tsp_zigzag_attn_bwd_noalloc(const tsp_shape *s, const void *q, const void *k, const void *v, const void *dout,
                                        float *dq, float *dk, float *dv, void *stream) {
   return attn_bwd(s, q, k, v, nullptr, nullptr, dout, dq, dk, dv, nullptr, 0, stream, true);
+}
+
+tsp_status tsp_zigzag_attn_bwd_ex(const tsp_shape *s, const void *q, const void *k, const void *v, const float *o,
+                                  const float *lse, const void *dout, float *dq, float *dk, float *dv, uint32_t flags,
+                                  void *ws, size_t ws_bytes, void *stream) {
+  if ((o == nullptr) != (lse == nullptr)) return fail(TSP_ERR_INVALID_ARG, "%s is NULL", o ? "lse" : "o");
+  return attn_bwd(s, q, k, v, o, lse, dout, dq, dk, dv, ws, ws_bytes, stream, false, flags);
 }
 
 tsp_status tsp_zigzag_attn_bwd_lse(const tsp_shape *s, const void *q, const void *k, const void *v, const float *o,
@@ -965,7 +975,7 @@ tsp_status tsp_layer_bwd(const tsp_shape *s, const tsp_layer_weights *w, const f
     TSP_LAUNCH(TSP_K_ATTN_BWD,
                tsp::launch_attention_bwd(dt, q, k_full, v_full, dout, dq, dk_full, dv_full, stat_lse, stat_delta, s->S,
                                          N, s->H, Hkv, s->Dh, s->scale, zz, stream, pnl ? o : nullptr,
-                                         pnl ? lse : nullptr),
+                                         pnl ? lse : nullptr, false),
                "attention backward");
   }
   if (pq) {

@@ -27,11 +27,14 @@
 // The operands of the second products are the score registers themselves,
 // rounded to bf16, in the order the MFMA takes them; the transpose reads hand
 // each lane 4 consecutive rows of one feature in that order. Every product
-// runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation. P and dS enter
-// their products as a bf16 pair hi + lo (two MFMAs each), exact to about
-// 2^-16 of their size: a plain bf16 rounding (2^-9) of them leaves errors of
-// 2-4% of the rms gradient on ranks whose rows see thousands of keys, not
-// only on the first rows of the sequence as in the forward.
+// runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation. SPLIT: P and dS
+// enter their products as a bf16 pair hi + lo (two MFMAs each), exact to
+// about 2^-16 of their size: a plain bf16 rounding (2^-9) of them leaves
+// elements off by 2-4% of the tensor's rms gradient on ranks whose rows see
+// thousands of keys (the largest gradient rows carry the error), not only
+// on the first rows of the sequence as in the forward. Without SPLIT they
+// enter rounded once to bf16, one MFMA each, as in common flash-attention
+// backward kernels; norm-wise the error stays near the bf16 rounding unit.
 //
 // fp32 inputs run plain per-row kernels with exact expf.
 #include <math.h>
@@ -162,13 +165,17 @@ constexpr int kBwdKey = 64;  // keys per tile of the dQ walk
 
 // v0, v1 as bf16 at elements e, e + 1 of hi (one packed conversion), and
 // the remainders v - hi (exact in fp32) as bf16 at the same elements of lo.
+// Without SPLIT only hi is written.
+template <bool SPLIT>
 __device__ __forceinline__ void put_split2(bf16x8 &hi, bf16x8 &lo, int e, float v0, float v1) {
   const bf16x2 h = {(bf16)v0, (bf16)v1};
   hi[e] = h[0];
   hi[e + 1] = h[1];
-  const bf16x2 l = {(bf16)(v0 - (float)h[0]), (bf16)(v1 - (float)h[1])};
-  lo[e] = l[0];
-  lo[e + 1] = l[1];
+  if constexpr (SPLIT) {
+    const bf16x2 l = {(bf16)(v0 - (float)h[0]), (bf16)(v1 - (float)h[1])};
+    lo[e] = l[0];
+    lo[e + 1] = l[1];
+  }
 }
 
 // Row statistics from the forward: Delta = sum over features of dO * O
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(256) void attn_bwd_stats_kernel(BwdArgs a, int DH) 
 
 // Two waves per SIMD (two blocks per CU): the register budget of 256 costs a
 // few spilled registers at Dh = 128, which the second wave more than repays.
-template <int DH, bool GIVEN>
+template <int DH, bool GIVEN, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using G = BTile<DH>;
@@ -351,7 +358,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
       for (int e = 0; e < 8; e += 2) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v0 + e], a.c, -lse));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v0 + e + 1], a.c, -lse));
-        put_split2(ds[kq], dsl[kq], e, p0 * (pacc[kb][v0 + e] - dlt), p1 * (pacc[kb][v0 + e + 1] - dlt));
+        put_split2<SPLIT>(ds[kq], dsl[kq], e, p0 * (pacc[kb][v0 + e] - dlt), p1 * (pacc[kb][v0 + e + 1] - dlt));
       }
     }
 #pragma unroll
@@ -360,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
       for (int db = 0; db < ND; ++db) {
         const bf16x8 kt_frag = tr_frag<DH>(smem[1], fo.tr[db] + kq * 16 * G::ROWB);
         qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_frag, ds[kq], qacc[db], 0, 0, 0);
-        qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_frag, dsl[kq], qacc[db], 0, 0, 0);
+        if constexpr (SPLIT) qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_frag, dsl[kq], qacc[db], 0, 0, 0);
       }
   }
   // qacc[db][v] is dQ[query][32*db + 8*(v/4) + 4*g + v%4] / scale
@@ -380,7 +387,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------- dK, dV (bf16)
 constexpr int kBwdQ = 32;  // query rows per step of the dK/dV walk
 
-template <int DH>
+template <int DH, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using G = BTile<DH>;
@@ -505,9 +512,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; e += 2) {
               const int v = m4 * 4 + e;  // v, v + 1 share the fragment (v is even)
-              put_split2(ph[v >> 3], p_lo[v >> 3], v & 7, pv[e], pv[e + 1]);
-              put_split2(dh[v >> 3], ds_lo[v >> 3], v & 7, pv[e] * (pacc[v] - dlv[e]),
-                         pv[e + 1] * (pacc[v + 1] - dlv[e + 1]));
+              put_split2<SPLIT>(ph[v >> 3], p_lo[v >> 3], v & 7, pv[e], pv[e + 1]);
+              put_split2<SPLIT>(dh[v >> 3], ds_lo[v >> 3], v & 7, pv[e] * (pacc[v] - dlv[e]),
+                                pv[e + 1] * (pacc[v + 1] - dlv[e + 1]));
             }
           }
         };
@@ -523,8 +530,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
             const bf16x8 dot = tr_frag<DH>(smem[3], off), qt = tr_frag<DH>(smem[1], off);
             vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, ph[mu], vacc[db], 0, 0, 0);
             kacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dh[mu], kacc[db], 0, 0, 0);
-            vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, p_lo[mu], vacc[db], 0, 0, 0);
-            kacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, ds_lo[mu], kacc[db], 0, 0, 0);
+            if constexpr (SPLIT) {
+              vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, p_lo[mu], vacc[db], 0, 0, 0);
+              kacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, ds_lo[mu], kacc[db], 0, 0, 0);
+            }
           }
       }
     }
@@ -637,7 +646,7 @@ __global__ __launch_bounds__(64) void attn_bwd_dkv_f32_kernel(BwdArgs a) {
 hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout, float *dq,
                                 float *dk, float *dv, float *lse, float *delta, int64_t S, int32_t n, int32_t H,
                                 int32_t Hkv, int32_t Dh, float scale, ZigzagMap zz, hipStream_t s,
-                                const float *o_f32, const float *lse_in) {
+                                const float *o_f32, const float *lse_in, bool split) {
   if (n <= 0) return hipSuccess;
   if (Hkv < 1 || H % Hkv != 0 || (Dh != 64 && Dh != 128)) return hipErrorInvalidValue;
   const bool given = o_f32 != nullptr && lse_in != nullptr;
@@ -671,20 +680,29 @@ hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const v
     if (given) {  // statistics from the forward, then dQ without its first walk
       const int64_t rows = (int64_t)n * H;
       hipLaunchKernelGGL(attn_bwd_stats_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a, (int)Dh);
-      if (Dh == 128)
-        hipLaunchKernelGGL((attn_bwd_dq_kernel<128, true>), qgrid, dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((attn_bwd_dq_kernel<64, true>), qgrid, dim3(256), 0, s, a);
-    } else {
-      if (Dh == 128)
-        hipLaunchKernelGGL((attn_bwd_dq_kernel<128, false>), qgrid, dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((attn_bwd_dq_kernel<64, false>), qgrid, dim3(256), 0, s, a);
     }
-    if (Dh == 128)
-      hipLaunchKernelGGL(attn_bwd_dkv_kernel<128>, kgrid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL(attn_bwd_dkv_kernel<64>, kgrid, dim3(256), 0, s, a);
+    // one instantiation per (head width, statistics given, P/dS split)
+    auto launch = [&](auto dh, auto gv, auto sp) {
+      constexpr int DH = decltype(dh)::value;
+      constexpr bool GV = decltype(gv)::value, SP = decltype(sp)::value;
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, GV, SP>), qgrid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<DH, SP>), kgrid, dim3(256), 0, s, a);
+    };
+    using I128 = std::integral_constant<int, 128>;
+    using I64 = std::integral_constant<int, 64>;
+    using T = std::true_type;
+    using F = std::false_type;
+    if (Dh == 128) {
+      if (given)
+        split ? launch(I128{}, T{}, T{}) : launch(I128{}, T{}, F{});
+      else
+        split ? launch(I128{}, F{}, T{}) : launch(I128{}, F{}, F{});
+    } else {
+      if (given)
+        split ? launch(I64{}, T{}, T{}) : launch(I64{}, T{}, F{});
+      else
+        split ? launch(I64{}, F{}, T{}) : launch(I64{}, F{}, F{});
+    }
   } else {
     const dim3 qgrid((n + 63) / 64, H), kgrid((unsigned)((S + 63) / 64), Hkv);
     if (Dh == 128) {

@@ -187,10 +187,12 @@ hipError_t launch_lead_attention(const float *q, const float *k, const float *v,
 // With o_f32 and lse_in given (bf16 inputs; the forward's fp32 output and
 // natural log-sum-exp [H][n] of launch_attention), Delta is the row sum of
 // dout * o and the statistics walk of the dQ kernel is skipped.
+// split (bf16): P and dS enter their products as a bf16 pair hi + lo;
+// otherwise rounded once to bf16.
 hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout, float *dq,
                                 float *dk, float *dv, float *lse, float *delta, int64_t S, int32_t n, int32_t H,
                                 int32_t Hkv, int32_t Dh, float scale, ZigzagMap zz, hipStream_t s,
-                                const float *o_f32 = nullptr, const float *lse_in = nullptr);
+                                const float *o_f32 = nullptr, const float *lse_in = nullptr, bool split = true);
 
 // ---------------------------------------------------------------- static scratch
 // Size of the device array that tsp_zigzag_attn_bwd_noalloc uses in place of
