@@ -393,12 +393,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   using G = BTile<DH>;
   constexpr int ND = DH / 32, NK = DH / 16;
   constexpr int TB = kBwdQ * G::ROWB;
-  // Q (ROW), Q (TR), dO (ROW), dO (TR), then the rows' statistics and positions
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4][TB];
+  // two buffers (steps alternate): Q (ROW), Q (TR), dO (ROW), dO (TR), and
+  // the rows' statistics and positions
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][4][TB];
   // read as float4 / int4 below, so 16-byte alignment is part of the layout
-  __shared__ __attribute__((aligned(16))) float lse_s[kBwdQ];
-  __shared__ __attribute__((aligned(16))) float dlt_s[kBwdQ];
-  __shared__ __attribute__((aligned(16))) int pos_s[kBwdQ];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][kBwdQ];
+  __shared__ __attribute__((aligned(16))) float dlt_s[2][kBwdQ];
+  __shared__ __attribute__((aligned(16))) int pos_s[2][kBwdQ];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const FragOff<DH> fo = frag_off<DH>(lane);
@@ -429,6 +430,72 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
     for (int v = 0; v < 16; ++v) kacc[db][v] = vacc[db][v] = 0.f;
   const int wkey0 = (int)kb0 + wave * 32;  // first key of this wave
 
+  // S = Q K^T and dP = dO V^T of the step in buffer b, keys on the lanes:
+  // two accumulators per product (even and odd K slices), so that four
+  // independent MFMA chains interleave; each starts from a zero constant
+  auto scores = [&](int b, f32x16 &sacc, f32x16 &pacc) {
+    const f32x16 zero = {};
+    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][0], fo.row[0]), kf[0], zero, 0, 0, 0);
+    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][2], fo.row[0]), vf[0], zero, 0, 0, 0);
+    f32x16 sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][0], fo.row[1]), kf[1], zero, 0, 0, 0);
+    f32x16 pacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][2], fo.row[1]), vf[1], zero, 0, 0, 0);
+#pragma unroll
+    for (int kk = 2; kk < NK; kk += 2) {
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][0], fo.row[kk]), kf[kk], sacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][2], fo.row[kk]), vf[kk], pacc, 0, 0, 0);
+      sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][0], fo.row[kk + 1]), kf[kk + 1], sacc1, 0, 0, 0);
+      pacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][2], fo.row[kk + 1]), vf[kk + 1], pacc1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      sacc[v] += sacc1[v];
+      pacc[v] += pacc1[v];
+    }
+  };
+  // sacc[v]: S[row 8*(v/4) + 4*g + v%4][key]. P and dS of the step in buffer
+  // b in the B-operand order (rows past the chunk carry position -1, so the
+  // masked form zeroes them), then dV^T += dO^T P and dK^T += Q^T dS.
+  auto update = [&](auto masked, int b, const f32x16 &sacc, const f32x16 &pacc) {
+    bf16x8 ph[2], dh[2], p_lo[2], ds_lo[2];
+#pragma unroll
+    for (int m4 = 0; m4 < 4; ++m4) {
+      const int r = m4 * 8 + g * 4;
+      const float4 ls = *reinterpret_cast<const float4 *>(&lse_s[b][r]);
+      const float4 dl = *reinterpret_cast<const float4 *>(&dlt_s[b][r]);
+      const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, dlv[4] = {dl.x, dl.y, dl.z, dl.w};
+      float pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[m4 * 4 + e], a.c, -lsv[e]));
+      if constexpr (decltype(masked)::value) {
+        const int4 ps = *reinterpret_cast<const int4 *>(&pos_s[b][r]);
+        const int psv[4] = {ps.x, ps.y, ps.z, ps.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (key > psv[e]) pv[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const int v = m4 * 4 + e;  // v, v + 1 share the fragment (v is even)
+        put_split2<SPLIT>(ph[v >> 3], p_lo[v >> 3], v & 7, pv[e], pv[e + 1]);
+        put_split2<SPLIT>(dh[v >> 3], ds_lo[v >> 3], v & 7, pv[e] * (pacc[v] - dlv[e]),
+                          pv[e + 1] * (pacc[v + 1] - dlv[e + 1]));
+      }
+    }
+#pragma unroll
+    for (int mu = 0; mu < 2; ++mu)
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const int off = fo.tr[db] + mu * 16 * G::ROWB;
+        const bf16x8 dot = tr_frag<DH>(smem[b][3], off), qt = tr_frag<DH>(smem[b][1], off);
+        vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, ph[mu], vacc[db], 0, 0, 0);
+        kacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dh[mu], kacc[db], 0, 0, 0);
+        if constexpr (SPLIT) {
+          vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, p_lo[mu], vacc[db], 0, 0, 0);
+          kacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, ds_lo[mu], kacc[db], 0, 0, 0);
+        }
+      }
+  };
+
   for (int hi = 0; hi < a.grp; ++hi) {
     const int head = kvh * a.grp + hi;
     const bf16 *qg = reinterpret_cast<const bf16 *>(a.q) + head * DH;
@@ -437,9 +504,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       const int base = chh == 0 ? a.zz.base0 : a.zz.base1;  // position of the chunk's first row
       const int t_end = (chh + 1) * a.zz.C;
       const int t_lo = chh * a.zz.C + (int)max<int64_t>(0, kb0 - base);  // first row that sees a key of the block
+      if (t_lo >= t_end) continue;
       TileRegs<DH, kBwdQ> qr, dr;
       float st_lse = 0.f, st_dlt = 0.f;
-      auto fetch = [&](int t0) {  // the step's rows into registers (statistics: threads < 32)
+      auto fetch = [&](int t0) {  // a step's rows into registers (statistics: threads < 32)
         load_tile<DH, kBwdQ>(qr, qg, rs, t0, t_end);
         load_tile<DH, kBwdQ>(dr, dg, rs, t0, t_end);
         const int t = t0 + (int)threadIdx.x;
@@ -448,93 +516,73 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
           st_dlt = a.delta[(int64_t)head * a.n + t];
         }
       };
-      if (t_lo < t_end) fetch(t_lo);
-      for (int t0 = t_lo; t0 < t_end; t0 += kBwdQ) {
-        __syncthreads();
-        store_tile<DH, kBwdQ, false>(smem[0], qr);
-        store_tile<DH, kBwdQ, true>(smem[1], qr);
-        store_tile<DH, kBwdQ, false>(smem[2], dr);
-        store_tile<DH, kBwdQ, true>(smem[3], dr);
+      auto stage = [&](int b, int t0) {  // the fetched rows into buffer b
+        store_tile<DH, kBwdQ, false>(smem[b][0], qr);
+        store_tile<DH, kBwdQ, true>(smem[b][1], qr);
+        store_tile<DH, kBwdQ, false>(smem[b][2], dr);
+        store_tile<DH, kBwdQ, true>(smem[b][3], dr);
         if (threadIdx.x < kBwdQ) {
           const int t = t0 + threadIdx.x;
           const bool ok = t < t_end;
-          lse_s[threadIdx.x] = ok ? st_lse : 0.f;
-          dlt_s[threadIdx.x] = ok ? st_dlt : 0.f;
-          pos_s[threadIdx.x] = ok ? base + (t - chh * a.zz.C) : -1;
+          lse_s[b][threadIdx.x] = ok ? st_lse : 0.f;
+          dlt_s[b][threadIdx.x] = ok ? st_dlt : 0.f;
+          pos_s[b][threadIdx.x] = ok ? base + (t - chh * a.zz.C) : -1;
         }
-        __syncthreads();
-        if (t0 + kBwdQ < t_end) fetch(t0 + kBwdQ);
-        const int tmax = min(t_end, t0 + kBwdQ) - 1;
-        const int pmax = base + (tmax - chh * a.zz.C);  // last position of the step
-        if (wkey0 > pmax) continue;                     // every key of the wave is past every row
-        // two accumulators per product (even and odd K slices), so that four
-        // independent MFMA chains interleave
-        // each chain starts from a zero constant (no accumulator to clear)
-        const f32x16 zero = {};
-        f32x16 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[0], fo.row[0]), kf[0], zero, 0, 0, 0);
-        f32x16 pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[2], fo.row[0]), vf[0], zero, 0, 0, 0);
-        f32x16 sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[0], fo.row[1]), kf[1], zero, 0, 0, 0);
-        f32x16 pacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[2], fo.row[1]), vf[1], zero, 0, 0, 0);
+      };
+      // Rows past the chunk, or before some key of the wave, need the mask;
+      // the rest of the walk does not. A step whose rows all lie before the
+      // wave's keys runs masked (all its probabilities are zero).
+      auto need_mask = [&](int t0) {
+        return t0 + kBwdQ > t_end || base + (t0 - chh * a.zz.C) < wkey0 + 31;
+      };
+      // Software pipeline over the walk's steps: step i's scores are taken
+      // one iteration ahead, while step i-1's probabilities and products are
+      // formed, so that the exponentials and conversions issue under the
+      // score MFMAs of the next step.
+      fetch(t_lo);
+      __syncthreads();  // the previous walk's reads of both buffers are done
+      stage(0, t_lo);
+      __syncthreads();
+      if (t_lo + kBwdQ < t_end) fetch(t_lo + kBwdQ);
+      f32x16 s0, p0, s1, p1;
+      scores(0, s0, p0);
+      // issue order of the block: each of the 16 score MFMAs followed by
+      // five VALU instructions of the update, so that the update's
+      // exponentials and conversions run while the matrix core works
+      auto interleave = [] {
 #pragma unroll
-        for (int kk = 2; kk < NK; kk += 2) {
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[0], fo.row[kk]), kf[kk], sacc, 0, 0, 0);
-          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[2], fo.row[kk]), vf[kk], pacc, 0, 0, 0);
-          sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[0], fo.row[kk + 1]), kf[kk + 1], sacc1, 0, 0, 0);
-          pacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[2], fo.row[kk + 1]), vf[kk + 1], pacc1, 0, 0, 0);
+        for (int i = 0; i < 2 * NK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
         }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          sacc[v] += sacc1[v];
-          pacc[v] += pacc1[v];
+      };
+      // one pipeline iteration: stage step t0 + 32 into buffer b ^ 1, score
+      // it, and finish step t0 (buffer b); returns false after the last step.
+      // The scores and the update share one basic block, so that the
+      // scheduler can interleave them (after the last step the scores read
+      // a stale buffer and are dropped).
+      auto iter = [&](int b, int t0, f32x16 &sc, f32x16 &pc, f32x16 &sn, f32x16 &pn) {
+        const bool next = t0 + kBwdQ < t_end;
+        if (next) {
+          __syncthreads();  // every wave is done with buffer b ^ 1
+          stage(b ^ 1, t0 + kBwdQ);
+          __syncthreads();
+          if (t0 + 2 * kBwdQ < t_end) fetch(t0 + 2 * kBwdQ);
         }
-        // sacc[v]: S[row 8*(v/4) + 4*g + v%4][key]; P and dS in the B-operand
-        // order. Rows past the chunk, or before some key of the wave, need
-        // the mask; the rest of the walk does not.
-        const bool need_mask = t0 + kBwdQ > t_end || base + (t0 - chh * a.zz.C) < wkey0 + 31;
-        bf16x8 ph[2], dh[2], p_lo[2], ds_lo[2];
-        auto probs = [&](auto masked) {
-#pragma unroll
-          for (int m4 = 0; m4 < 4; ++m4) {
-            const int r = m4 * 8 + g * 4;
-            const float4 ls = *reinterpret_cast<const float4 *>(&lse_s[r]);
-            const float4 dl = *reinterpret_cast<const float4 *>(&dlt_s[r]);
-            const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, dlv[4] = {dl.x, dl.y, dl.z, dl.w};
-            float pv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[m4 * 4 + e], a.c, -lsv[e]));
-            if constexpr (decltype(masked)::value) {
-              const int4 ps = *reinterpret_cast<const int4 *>(&pos_s[r]);
-              const int psv[4] = {ps.x, ps.y, ps.z, ps.w};
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (key > psv[e]) pv[e] = 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < 4; e += 2) {
-              const int v = m4 * 4 + e;  // v, v + 1 share the fragment (v is even)
-              put_split2<SPLIT>(ph[v >> 3], p_lo[v >> 3], v & 7, pv[e], pv[e + 1]);
-              put_split2<SPLIT>(dh[v >> 3], ds_lo[v >> 3], v & 7, pv[e] * (pacc[v] - dlv[e]),
-                                pv[e + 1] * (pacc[v + 1] - dlv[e + 1]));
-            }
-          }
-        };
-        if (need_mask)
-          probs(std::true_type{});
-        else
-          probs(std::false_type{});
-#pragma unroll
-        for (int mu = 0; mu < 2; ++mu)
-#pragma unroll
-          for (int db = 0; db < ND; ++db) {
-            const int off = fo.tr[db] + mu * 16 * G::ROWB;
-            const bf16x8 dot = tr_frag<DH>(smem[3], off), qt = tr_frag<DH>(smem[1], off);
-            vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, ph[mu], vacc[db], 0, 0, 0);
-            kacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dh[mu], kacc[db], 0, 0, 0);
-            if constexpr (SPLIT) {
-              vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, p_lo[mu], vacc[db], 0, 0, 0);
-              kacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, ds_lo[mu], kacc[db], 0, 0, 0);
-            }
-          }
+        if (need_mask(t0)) {
+          scores(b ^ 1, sn, pn);
+          update(std::true_type{}, b, sc, pc);
+          interleave();
+        } else {
+          scores(b ^ 1, sn, pn);
+          update(std::false_type{}, b, sc, pc);
+          interleave();
+        }
+        return next;
+      };
+      for (int t0 = t_lo;; t0 += 2 * kBwdQ) {
+        if (!iter(0, t0, s0, p0, s1, p1)) break;
+        if (!iter(1, t0 + kBwdQ, s1, p1, s0, p0)) break;
       }
     }
   }
