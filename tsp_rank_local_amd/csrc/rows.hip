@@ -20,15 +20,40 @@ hipError_t launch_zigzag_index(ZigzagMap zz, int32_t n, int32_t *pos, hipStream_
 // One 256-thread block per row; h % 4 == 0. The sum of squares runs in fp32,
 // first per thread, then across the wave with shuffles, then across waves.
 // panel_stride > 0: out in panel layout (64-column panels of [rows][64]).
-template <typename G, typename O>
+// CACHED (h <= 8192): each thread keeps its float4 columns (4 * thread +
+// 1024 * i) in registers between the sum and the output, so the row is read
+// from memory once; otherwise it is read twice.
+template <typename T>
+__device__ __forceinline__ void put4(T *o, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<float4 *>(o) = make_float4(a, b, c, d);
+  } else {
+    const bf16x2 lo = {(bf16)a, (bf16)b}, hi = {(bf16)c, (bf16)d};
+    *reinterpret_cast<u32x2 *>(o) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  }
+}
+
+constexpr int kNormChunks = 8;  // float4 columns per thread with CACHED
+
+template <typename G, typename O, bool CACHED>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ x, const G *__restrict__ g,
                                                       O *__restrict__ out, int32_t h, float eps, int64_t panel_stride) {
   const int64_t row = blockIdx.x;
   const float *xr = x + row * h;
   float ss = 0.f;
-  for (int c = threadIdx.x * 4; c < h; c += 1024) {
-    float4 v = *reinterpret_cast<const float4 *>(xr + c);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  float4 xv[CACHED ? kNormChunks : 1];
+  if constexpr (CACHED) {
+#pragma unroll
+    for (int i = 0; i < kNormChunks; ++i) {
+      const int c = threadIdx.x * 4 + 1024 * i;
+      xv[i] = c < h ? *reinterpret_cast<const float4 *>(xr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      ss += xv[i].x * xv[i].x + xv[i].y * xv[i].y + xv[i].z * xv[i].z + xv[i].w * xv[i].w;
+    }
+  } else {
+    for (int c = threadIdx.x * 4; c < h; c += 1024) {
+      float4 v = *reinterpret_cast<const float4 *>(xr + c);
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
   }
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
   __shared__ float part[4];
@@ -37,31 +62,39 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ 
   __syncthreads();
   float tot = part[0] + part[1] + part[2] + part[3];
   const float rstd = 1.0f / sqrtf(tot / (float)h + eps);
-  for (int c = threadIdx.x * 4; c < h; c += 1024) {
-    float4 v = *reinterpret_cast<const float4 *>(xr + c);
-    float r0 = v.x * rstd * (float)g[c + 0];
-    float r1 = v.y * rstd * (float)g[c + 1];
-    float r2 = v.z * rstd * (float)g[c + 2];
-    float r3 = v.w * rstd * (float)g[c + 3];
+  auto emit = [&](int c, float4 v) {
     O *o = out + (panel_stride ? panel_index(row, c, panel_stride) : row * h + c);  // 4 elements, one panel
-    o[0] = (O)r0;
-    o[1] = (O)r1;
-    o[2] = (O)r2;
-    o[3] = (O)r3;
+    put4(o, v.x * rstd * (float)g[c + 0], v.y * rstd * (float)g[c + 1], v.z * rstd * (float)g[c + 2],
+         v.w * rstd * (float)g[c + 3]);
+  };
+  if constexpr (CACHED) {
+#pragma unroll
+    for (int i = 0; i < kNormChunks; ++i) {
+      const int c = threadIdx.x * 4 + 1024 * i;
+      if (c < h) emit(c, xv[i]);
+    }
+  } else {
+    for (int c = threadIdx.x * 4; c < h; c += 1024) emit(c, *reinterpret_cast<const float4 *>(xr + c));
   }
+}
+
+template <typename G, typename O>
+static void launch_rmsnorm_rows(const float *x, const G *g, O *out, int32_t rows, int32_t h, float eps, int64_t ps,
+                                hipStream_t s) {
+  if (h <= 1024 * kNormChunks)
+    hipLaunchKernelGGL((rmsnorm_kernel<G, O, true>), dim3(rows), dim3(256), 0, s, x, g, out, h, eps, ps);
+  else
+    hipLaunchKernelGGL((rmsnorm_kernel<G, O, false>), dim3(rows), dim3(256), 0, s, x, g, out, h, eps, ps);
 }
 
 hipError_t launch_rmsnorm(const float *x, const void *g, void *out, int32_t rows, int32_t h, float eps,
                           int dtype, bool out_panel, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   const int64_t ps = out_panel ? (int64_t)rows * kPanel : 0;
-  if (dtype == TSP_BF16) {
-    hipLaunchKernelGGL((rmsnorm_kernel<bf16, bf16>), dim3(rows), dim3(256), 0, s, x, (const bf16 *)g,
-                       (bf16 *)out, h, eps, ps);
-  } else {
-    hipLaunchKernelGGL((rmsnorm_kernel<float, float>), dim3(rows), dim3(256), 0, s, x, (const float *)g,
-                       (float *)out, h, eps, ps);
-  }
+  if (dtype == TSP_BF16)
+    launch_rmsnorm_rows(x, (const bf16 *)g, (bf16 *)out, rows, h, eps, ps, s);
+  else
+    launch_rmsnorm_rows(x, (const float *)g, (float *)out, rows, h, eps, ps, s);
   return hipGetLastError();
 }
 
@@ -291,11 +324,9 @@ hipError_t launch_rmsnorm_f32(const float *x, const void *g, int g_dtype, float 
                               float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (g_dtype == TSP_BF16)
-    hipLaunchKernelGGL((rmsnorm_kernel<bf16, float>), dim3(rows), dim3(256), 0, s, x, (const bf16 *)g, out, h, eps,
-                       (int64_t)0);
+    launch_rmsnorm_rows(x, (const bf16 *)g, out, rows, h, eps, (int64_t)0, s);
   else
-    hipLaunchKernelGGL((rmsnorm_kernel<float, float>), dim3(rows), dim3(256), 0, s, x, (const float *)g, out, h, eps,
-                       (int64_t)0);
+    launch_rmsnorm_rows(x, (const float *)g, out, rows, h, eps, (int64_t)0, s);
   return hipGetLastError();
 }
 
