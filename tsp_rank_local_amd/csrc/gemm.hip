@@ -15,11 +15,13 @@
 // (fp32) or 8-byte (bf16) vector.
 // K advances 64 at a time through 2 LDS stages (A and B tiles of 256 x 64,
 // 64 KB per stage): tiles go from HBM straight into LDS (buffer_load ... lds,
-// 16 bytes per lane), one block barrier per step. The copies of a step are
-// spread over the MFMAs of the last K slice of the step two earlier, and the
-// step after that is prefetched into L2 with one dword load per 128-byte
-// line, so the copies mostly hit L2. Fragment reads of the next K slice are
-// interleaved with the MFMAs of the current one. LDS rows are 128 bytes; the
+// 16 bytes per lane), one block barrier per step. Fragments are read two K
+// slices ahead of their MFMAs, so every read of a stage has been issued
+// after the second slice of its step; the copies of the step two later are
+// then spread over the MFMAs of the last two slices (the copy engine takes
+// about 62 bytes per clock per CU, and a burst within one slice stalled the
+// issuing waves), and the step after that is prefetched into L2 with one
+// dword load per 128-byte line, so the copies mostly hit L2. LDS rows are 128 bytes; the
 // 16-byte chunk index is XOR-swizzled by (row/2)%8 (the copying lane picks
 // its source chunk), so the lanes that read one chunk of 32 rows spread over
 // all bank groups.
@@ -477,7 +479,7 @@ struct TileCoord {
   int z, tm, tn;
 };
 __device__ __forceinline__ TileCoord tile_of(int L, int tiles_m, int tiles_n) {
-  constexpr int GM = 8;
+  constexpr int GM = 4;
   const int per_z = tiles_m * tiles_n;
   TileCoord t;
   t.z = L / per_z;
@@ -673,17 +675,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, 
   }
   wait_vmcnt<2>();
   __syncthreads();
-  GemmFrags f0, f1;
+  // fragments two K slices ahead: slice s of a step uses f[s]
+  GemmFrags f[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) read_pair(f0, 0, 0, q);
+  for (int q = 0; q < 4; ++q) read_pair(f[0], 0, 0, q);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) read_pair(f[1], 0, 1, q);
 
-  // ---- main loop. Step kt sits in stage kt&1. Each K slice runs as 4
-  // groups of 4 MFMAs, each group also issuing 2 fragment reads of the next
-  // slice. After slice 2 the wave waits for its copies of step kt+1 and the
-  // block synchronises (every wave is done reading stage kt&1); under slice
-  // 3 the wave then reads slice 0 of step kt+1, copies step kt+2 into stage
-  // kt&1 and prefetches step kt+3 into L2. The wait leaves only the 2
-  // prefetch loads issued after those copies in flight.
+  // ---- main loop. Step kt sits in stage kt&1. Slice s runs as 4 groups of
+  // 4 MFMAs on f[s]; slices 0 and 1 read slices 2 and 3 of this step, slices
+  // 2 and 3 read slices 0 and 1 of step kt+1. After slice 1 every read of
+  // stage kt&1 has been issued: the wave waits for them and for its copies
+  // of step kt+1, and the block synchronises; the copies of step kt+2 into
+  // stage kt&1 are then spread over slices 2 and 3 (one part every other
+  // group), and step kt+3 is prefetched into L2 at the end.
   for (int kt = 0; kt < KT; ++kt) {
     const int st = kt & 1;
     int koff2, koff3;
@@ -692,20 +697,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, 
     const bf16 *bseg3 = bptr_at(seg_of(kp, koff3));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      read_pair(f1, st, 1, i);
-      mfma_row(f0, i);
+      read_pair(f[2], st, 2, i);
+      mfma_row(f[0], i);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      read_pair(f0, st, 2, i);
-      mfma_row(f1, i);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      read_pair(f1, st, 3, i);
-      mfma_row(f0, i);
+      read_pair(f[3], st, 3, i);
+      mfma_row(f[1], i);
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_vmcnt<2>();
@@ -714,10 +713,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, 
     const StepSrc tc = step_src(kc, bseg2, koff2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      read_pair(f0, st ^ 1, 0, i);
-      copy_part(tc, st, i);
+      read_pair(f[0], st ^ 1, 0, i);
+      if ((i & 1) == 0) copy_part(tc, st, i >> 1);
+      mfma_row(f[2], i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      read_pair(f[1], st ^ 1, 1, i);
+      if ((i & 1) == 0) copy_part(tc, st, 2 + (i >> 1));
       if (i == 3) prefetch(step_src(kp, bseg3, koff3));
-      mfma_row(f1, i);
+      mfma_row(f[3], i);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
