@@ -6,10 +6,11 @@
 // block (head, p) takes the mirrored tile T-1-p of the second chunk and then
 // tile p of the first, so every block walks about S/64 + 2 key tiles and all
 // blocks carry equal causal work. The long (second-chunk) tile goes first: the
-// blocks of one head that share an XCD then stream the same key tiles together
-// and each tile comes from HBM about once per head. Key tiles past a tile's
-// last query are never loaded; only tiles that straddle the diagonal apply the
-// mask.
+// blocks of one head run together on one XCD and stream the same key tiles
+// through its L2 (at 7B the L2's requests to memory come to about twice the
+// K/V bytes, as the blocks drift apart and the short walks restart from key
+// 0). Key tiles past a tile's last query are never loaded; only tiles that
+// straddle the diagonal apply the mask.
 //
 // Per block: 4 waves x 32 queries, two blocks per CU. K and V tiles of 64 keys
 // go from HBM straight into LDS (buffer_load ... lds, 16 bytes per lane, no
