@@ -22,8 +22,9 @@
 //     dV^T += dO^T P and dK^T += Q^T dS, whose dO^T and Q^T operands are
 //     transpose reads of the query tiles.
 // When the forward's fp32 O and log-sum-exp are given, a small kernel forms
-// Delta = rowsum(dO * O) and the log2-domain statistics instead, and the dQ
-// kernel skips its first walk.
+// Delta = rowsum(dO * O) and the log2-domain statistics instead, and a dQ
+// kernel without the first walk (attn_bwd_dq_lds_kernel) stages its K/V tiles
+// the way the forward does: straight into LDS, double-buffered.
 // The operands of the second products are the score registers themselves,
 // rounded to bf16, in the order the MFMA takes them; the transpose reads hand
 // each lane 4 consecutive rows of one feature in that order. Every product
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(256) void attn_bwd_stats_kernel(BwdArgs a, int DH) 
 
 // Two waves per SIMD (two blocks per CU): the register budget of 256 costs a
 // few spilled registers at Dh = 128, which the second wave more than repays.
-template <int DH, bool GIVEN, bool SPLIT>
+template <int DH, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using G = BTile<DH>;
@@ -272,10 +273,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 
   TileRegs<DH, kBwdKey> kr, vr;
   float lse, dlt;
-  if constexpr (GIVEN) {  // statistics from the forward (attn_bwd_stats_kernel)
-    lse = my_valid ? a.lse[(int64_t)head * a.n + qrow] : 0.f;
-    dlt = my_valid ? a.delta[(int64_t)head * a.n + qrow] : 0.f;
-  } else {
+  {
     // ---- walk 1: row max, sum and Delta (log2 domain)
     float m = -INFINITY, l = 0.f, dsum = 0.f;
     load_tile<DH, kBwdKey>(kr, kg, kvs, 0, a.S);
@@ -380,6 +378,197 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         *reinterpret_cast<float4 *>(dq + db * 32 + vq * 8) =
             make_float4(qacc[db][vq * 4] * a.scale, qacc[db][vq * 4 + 1] * a.scale, qacc[db][vq * 4 + 2] * a.scale,
                         qacc[db][vq * 4 + 3] * a.scale);
+  }
+#endif
+}
+
+// ---------------------------------------------------------------- dQ from the forward's statistics (bf16)
+// The dQ walk with the forward attention's staging: K and V tiles go from
+// HBM straight into LDS (buffer_load ... lds, no registers on the way),
+// double-buffered, one block barrier per tile, and block (head, p) takes
+// query tile T-1-p of the second chunk and then tile p of the first, so that
+// every block carries the same causal work. K is stored once, in the row
+// layout: the score products read its rows, and the dQ product reads it
+// transposed from the same copy (transpose reads that land two rows on the
+// same banks, a 2-way conflict, against a second copy of every tile).
+#if defined(__HIP_DEVICE_COMPILE__)
+#define TSP_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+#endif
+
+template <int DH, bool SPLIT>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_lds_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using G = BTile<DH>;
+  constexpr int ND = DH / 32, NK = DH / 16;
+  constexpr int TB = kBwdKey * G::ROWB;          // one tile: 16 KB (DH 128) or 8 KB (DH 64)
+  constexpr int RPW = 1024 / G::ROWB;            // rows of a 1 KB copy window
+  constexpr int WPW = TB / 1024 / 4;             // copy windows per wave and tile
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][TB];  // [stage][K | V]
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const FragOff<DH> fo = frag_off<DH>(lane);
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int head = L / a.Tq, p = L - head * a.Tq;
+  const int kvh = head / a.grp;
+  const int64_t rs = (int64_t)a.H * DH, kvs = (int64_t)a.Hkv * DH;
+  const bf16 *kg = reinterpret_cast<const bf16 *>(a.k) + kvh * DH;
+  const bf16 *vg = reinterpret_cast<const bf16 *>(a.v) + kvh * DH;
+
+  // copy plan: window w of a tile is rows RPW*w..; the lane at row r, chunk
+  // position pos loads the logical chunk that the row layout puts there
+  int c_off[WPW];
+#pragma unroll
+  for (int i = 0; i < WPW; ++i) {
+    const int row = (wave * WPW + i) * RPW + lane / G::CPR, pos = lane % G::CPR;
+    c_off[i] = (int)(row * kvs * 2) + G::row_swz(row, pos) * 16;
+  }
+  auto copy_tile = [&](int kt, int st) {
+    const int64_t k0 = (int64_t)kt * kBwdKey;
+    const int rows = (int)min<int64_t>(kBwdKey, a.S - k0);
+    const auto kr = __builtin_amdgcn_make_buffer_rsrc((void *)(kg + k0 * kvs), (short)0, (int)(rows * kvs * 2),
+                                                      0x00020000);
+    const auto vr = __builtin_amdgcn_make_buffer_rsrc((void *)(vg + k0 * kvs), (short)0, (int)(rows * kvs * 2),
+                                                      0x00020000);
+#pragma unroll
+    for (int i = 0; i < WPW; ++i) {
+      const int win = wave * WPW + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, TSP_LDS_PTR(&smem[st][0][win * 1024]), 16, c_off[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, TSP_LDS_PTR(&smem[st][1][win * 1024]), 16, c_off[i], 0, 0, 0);
+    }
+  };
+  // transposed reads of the row-layout K tile: lane l gets feature 32*db +
+  // l%32's keys 16*kq + 8*hv + 4*(l/32) + {0..3} of half hv. The row swizzle
+  // depends on the row modulo 16 (or on row/2 modulo 8), which a step of 16
+  // keys keeps, so each (db, hv) has one lane-constant offset.
+  int trr[ND][2];
+  {
+    const int r16 = lane & 15, dsub = (lane >> 4) & 1;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int hv = 0; hv < 2; ++hv) {
+        const int row = 8 * hv + g * 4 + (r16 >> 2);
+        const int dstart = db * 32 + dsub * 16 + 4 * (r16 & 3);
+        trr[db][hv] = row * G::ROWB + G::row_swz(row, dstart >> 3) * 16 + (dstart & 7) * 2;
+      }
+  }
+  auto kt_frag = [&](const unsigned char *t, int db, int kq) {
+    s16x4_b part[2];
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv)
+      part[hv] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_b *)(t + trr[db][hv] + kq * 16 * G::ROWB));
+    const s16x8_t both = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
+    return __builtin_bit_cast(bf16x8, both);
+  };
+
+  for (int half = 0; half < 2; ++half) {
+    const int ch_half = half == 0 ? 1 : 0;
+    const int tile = half == 0 ? a.Tq - 1 - p : p;
+    const int row0 = ch_half * a.zz.C + tile * 128;
+    const int nvalid = min(128, (ch_half + 1) * a.zz.C - row0);
+    if (nvalid <= 0) continue;  // the same for the whole block
+    const int pos0 = a.zz.pos(row0);
+    const int n_kt = (pos0 + nvalid - 1) / kBwdKey + 1;
+    const int wrow0 = wave * 32;
+    const bool my_valid = wrow0 + l32 < nvalid;
+    const int qpos = pos0 + min(wrow0 + l32, nvalid - 1);
+    const int wmin = pos0 + wrow0;
+    const int64_t qrow = row0 + wrow0 + l32;
+
+    copy_tile(0, 0);
+    bf16x8 qf[NK], df[NK];
+    {
+      const bf16 *qp = reinterpret_cast<const bf16 *>(a.q) + qrow * rs + head * DH;
+      const bf16 *dp = reinterpret_cast<const bf16 *>(a.dout) + qrow * rs + head * DH;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        bf16x8 qv = {}, dv = {};
+        if (my_valid) {
+          qv = *reinterpret_cast<const bf16x8 *>(qp + kk * 16 + g * 8);
+          dv = *reinterpret_cast<const bf16x8 *>(dp + kk * 16 + g * 8);
+        }
+        qf[kk] = qv;
+        df[kk] = dv;
+      }
+    }
+    const float lse = my_valid ? a.lse[(int64_t)head * a.n + qrow] : 0.f;
+    const float dlt = my_valid ? a.delta[(int64_t)head * a.n + qrow] : 0.f;
+    f32x16 qacc[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) qacc[db][v] = 0.f;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+
+    // key tile kt in stage st: copy tile kt + 1 into the other stage, form
+    // dS from S^T = K Q^T and dP^T = V dO^T, add K^T dS^T into dQ^T; then
+    // wait for this wave's copies and for every wave to be done with st
+    auto step = [&](int kt, int st) {
+      if (kt + 1 < n_kt) copy_tile(kt + 1, st ^ 1);
+      const int k0 = kt * kBwdKey;
+      const unsigned char *Ks = smem[st][0], *Vs = smem[st][1];
+      const f32x16 zero = {};
+      f32x16 sacc[2], pacc[2];
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Ks, fo.row[kk] + kb * 32 * G::ROWB), qf[kk],
+                                                             kk == 0 ? zero : sacc[kb], 0, 0, 0);
+          pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Vs, fo.row[kk] + kb * 32 * G::ROWB), df[kk],
+                                                             kk == 0 ? zero : pacc[kb], 0, 0, 0);
+        }
+      if (k0 + kBwdKey - 1 > wmin) {  // keys past the lane's query get -inf
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = k0 + kb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+            if (key > qpos) sacc[kb][v] = -INFINITY;
+          }
+      }
+      bf16x8 ds[4], dsl[4];
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+        const int kb = kq >> 1, v0 = (kq & 1) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v0 + e], a.c, -lse));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v0 + e + 1], a.c, -lse));
+          put_split2<SPLIT>(ds[kq], dsl[kq], e, p0 * (pacc[kb][v0 + e] - dlt), p1 * (pacc[kb][v0 + e + 1] - dlt));
+        }
+      }
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const bf16x8 kt_f = kt_frag(Ks, db, kq);
+          qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_f, ds[kq], qacc[db], 0, 0, 0);
+          if constexpr (SPLIT) qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_f, dsl[kq], qacc[db], 0, 0, 0);
+        }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+    };
+    int kt = 0;
+    for (; kt + 1 < n_kt; kt += 2) {
+      step(kt, 0);
+      step(kt + 1, 1);
+    }
+    if (kt < n_kt) step(kt, 0);
+
+    // qacc[db][v] is dQ[query][32*db + 8*(v/4) + 4*g + v%4] / scale
+    if (my_valid) {
+      float *dq = a.dq + qrow * rs + head * DH + g * 4;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq)
+          *reinterpret_cast<float4 *>(dq + db * 32 + vq * 8) =
+              make_float4(qacc[db][vq * 4] * a.scale, qacc[db][vq * 4 + 1] * a.scale, qacc[db][vq * 4 + 2] * a.scale,
+                          qacc[db][vq * 4 + 3] * a.scale);
+    }
   }
 #endif
 }
@@ -733,7 +922,10 @@ hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const v
     auto launch = [&](auto dh, auto gv, auto sp) {
       constexpr int DH = decltype(dh)::value;
       constexpr bool GV = decltype(gv)::value, SP = decltype(sp)::value;
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, GV, SP>), qgrid, dim3(256), 0, s, a);
+      if constexpr (GV)  // paired query tiles: one block per (head, tile pair)
+        hipLaunchKernelGGL((attn_bwd_dq_lds_kernel<DH, SP>), dim3(H * a.Tq), dim3(256), 0, s, a);
+      else  // statistics walk, then dQ
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, SP>), qgrid, dim3(256), 0, s, a);
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<DH, SP>), kgrid, dim3(256), 0, s, a);
     };
     using I128 = std::integral_constant<int, 128>;
