@@ -78,27 +78,27 @@ struct BTile {
   }
 };
 
-// Rows [r0, r0 + R) of a bf16 [*][pitch] tensor (DH columns from src) go to
-// LDS in ROW or TR layout, rows at or past rmax as zeros, in two halves, so
-// that the global loads of the next tile can be issued before the current
-// tile's math and land in registers meanwhile: load_tile fills this thread's
-// chunks, store_tile writes them to LDS.
+// R rows of a bf16 [*][pitch] tensor (DH columns) go to LDS in ROW or TR
+// layout in two halves, so that the global loads of the next tile can be
+// issued before the current tile's math and land in registers meanwhile:
+// load_tile_buf fills this thread's chunks, store_tile writes them to LDS.
 template <int DH, int R>
 struct TileRegs {
   static constexpr int N = R * BTile<DH>::CPR / 256;  // 16-byte chunks per thread
   u32x4 v[N];
 };
+// Rows [0, nvalid) are read from src (its first row); the rest come back as
+// zeros from the buffer descriptor's range, so the loads need no per-lane
+// branch and no 64-bit address arithmetic.
 template <int DH, int R>
-__device__ __forceinline__ void load_tile(TileRegs<DH, R> &t, const bf16 *src, int64_t pitch, int64_t r0,
-                                          int64_t rmax) {
+__device__ __forceinline__ void load_tile_buf(TileRegs<DH, R> &t, const bf16 *src, int pitch, int nvalid) {
   using G = BTile<DH>;
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, nvalid * pitch * 2, 0x00020000);
 #pragma unroll
   for (int i = 0; i < TileRegs<DH, R>::N; ++i) {
     const int c = threadIdx.x + 256 * i;
     const int row = c / G::CPR, ch = c % G::CPR;
-    const int64_t gr = r0 + row;
-    t.v[i] = u32x4{0u, 0u, 0u, 0u};
-    if (gr < rmax) t.v[i] = *reinterpret_cast<const u32x4 *>(src + gr * pitch + ch * 8);
+    t.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, row * pitch * 2 + ch * 16, 0, 0));
   }
 }
 template <int DH, int R, bool TR>
@@ -276,8 +276,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   {
     // ---- walk 1: row max, sum and Delta (log2 domain)
     float m = -INFINITY, l = 0.f, dsum = 0.f;
-    load_tile<DH, kBwdKey>(kr, kg, kvs, 0, a.S);
-    load_tile<DH, kBwdKey>(vr, vg, kvs, 0, a.S);
+    load_tile_buf<DH, kBwdKey>(kr, kg, (int)kvs, (int)min<int64_t>(kBwdKey, a.S));
+    load_tile_buf<DH, kBwdKey>(vr, vg, (int)kvs, (int)min<int64_t>(kBwdKey, a.S));
     for (int kt = 0; kt < n_kt; ++kt) {
       const int k0 = kt * kBwdKey;
       __syncthreads();
@@ -285,8 +285,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
       store_tile<DH, kBwdKey, false>(smem[2], vr);
       __syncthreads();
       if (kt + 1 < n_kt) {  // next tile on its way during this one's math
-        load_tile<DH, kBwdKey>(kr, kg, kvs, k0 + kBwdKey, a.S);
-        load_tile<DH, kBwdKey>(vr, vg, kvs, k0 + kBwdKey, a.S);
+        load_tile_buf<DH, kBwdKey>(kr, kg + (int64_t)(k0 + kBwdKey) * kvs, (int)kvs,
+                                    (int)min<int64_t>(kBwdKey, a.S - (k0 + kBwdKey)));
+        load_tile_buf<DH, kBwdKey>(vr, vg + (int64_t)(k0 + kBwdKey) * kvs, (int)kvs,
+                                    (int)min<int64_t>(kBwdKey, a.S - (k0 + kBwdKey)));
       }
       if (!active) continue;
       f32x16 sacc[2], pacc[2];
@@ -330,8 +332,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   for (int db = 0; db < ND; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) qacc[db][v] = 0.f;
-  load_tile<DH, kBwdKey>(kr, kg, kvs, 0, a.S);
-  load_tile<DH, kBwdKey>(vr, vg, kvs, 0, a.S);
+  load_tile_buf<DH, kBwdKey>(kr, kg, (int)kvs, (int)min<int64_t>(kBwdKey, a.S));
+  load_tile_buf<DH, kBwdKey>(vr, vg, (int)kvs, (int)min<int64_t>(kBwdKey, a.S));
   for (int kt = 0; kt < n_kt; ++kt) {
     const int k0 = kt * kBwdKey;
     __syncthreads();
@@ -340,8 +342,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     store_tile<DH, kBwdKey, false>(smem[2], vr);
     __syncthreads();
     if (kt + 1 < n_kt) {
-      load_tile<DH, kBwdKey>(kr, kg, kvs, k0 + kBwdKey, a.S);
-      load_tile<DH, kBwdKey>(vr, vg, kvs, k0 + kBwdKey, a.S);
+      load_tile_buf<DH, kBwdKey>(kr, kg + (int64_t)(k0 + kBwdKey) * kvs, (int)kvs,
+                                    (int)min<int64_t>(kBwdKey, a.S - (k0 + kBwdKey)));
+      load_tile_buf<DH, kBwdKey>(vr, vg + (int64_t)(k0 + kBwdKey) * kvs, (int)kvs,
+                                    (int)min<int64_t>(kBwdKey, a.S - (k0 + kBwdKey)));
     }
     if (!active) continue;
     f32x16 sacc[2], pacc[2];
@@ -584,7 +588,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   constexpr int TB = kBwdQ * G::ROWB;
   // two buffers (steps alternate): Q (ROW), Q (TR), dO (ROW), dO (TR), and
   // the rows' statistics and positions
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][4][TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][TB];
   // read as float4 / int4 below, so 16-byte alignment is part of the layout
   __shared__ __attribute__((aligned(16))) float lse_s[2][kBwdQ];
   __shared__ __attribute__((aligned(16))) float dlt_s[2][kBwdQ];
@@ -592,8 +596,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const FragOff<DH> fo = frag_off<DH>(lane);
-  const int kvh = blockIdx.x / a.Tk;
-  const int64_t kb0 = (int64_t)(blockIdx.x % a.Tk) * 128;
+  // the key blocks of one K/V head run on one XCD, in key order, so that
+  // the blocks that run together walk nearby query rows through its L2
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int kvh = L / a.Tk;
+  const int64_t kb0 = (int64_t)(L % a.Tk) * 128;
   const int64_t key = kb0 + wave * 32 + l32;
   const int64_t rs = (int64_t)a.H * DH, kvs = (int64_t)a.Hkv * DH;
 
@@ -612,6 +619,31 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       }
     }
   }
+  // transposed reads of the row-layout tiles: lane l gets feature 32*db +
+  // l%32's rows 16*mu + 8*hv + 4*(l/32) + {0..3} of half hv (the row swizzle
+  // depends on the row modulo 16, or on row/2 modulo 8, which a step of 16
+  // rows keeps)
+  int trr[ND][2];
+  {
+    const int r16 = lane & 15, dsub = (lane >> 4) & 1;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int hv = 0; hv < 2; ++hv) {
+        const int row = 8 * hv + g * 4 + (r16 >> 2);
+        const int dstart = db * 32 + dsub * 16 + 4 * (r16 & 3);
+        trr[db][hv] = row * G::ROWB + G::row_swz(row, dstart >> 3) * 16 + (dstart & 7) * 2;
+      }
+  }
+  auto trr_frag = [&](const unsigned char *t, int db, int mu) {
+    s16x4_b part[2];
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv)
+      part[hv] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_b *)(t + trr[db][hv] + mu * 16 * G::ROWB));
+    const s16x8_t both = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
+    return __builtin_bit_cast(bf16x8, both);
+  };
   f32x16 kacc[ND], vacc[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db)
@@ -625,15 +657,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   auto scores = [&](int b, f32x16 &sacc, f32x16 &pacc) {
     const f32x16 zero = {};
     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][0], fo.row[0]), kf[0], zero, 0, 0, 0);
-    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][2], fo.row[0]), vf[0], zero, 0, 0, 0);
+    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][1], fo.row[0]), vf[0], zero, 0, 0, 0);
     f32x16 sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][0], fo.row[1]), kf[1], zero, 0, 0, 0);
-    f32x16 pacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][2], fo.row[1]), vf[1], zero, 0, 0, 0);
+    f32x16 pacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][1], fo.row[1]), vf[1], zero, 0, 0, 0);
 #pragma unroll
     for (int kk = 2; kk < NK; kk += 2) {
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][0], fo.row[kk]), kf[kk], sacc, 0, 0, 0);
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][2], fo.row[kk]), vf[kk], pacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][1], fo.row[kk]), vf[kk], pacc, 0, 0, 0);
       sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][0], fo.row[kk + 1]), kf[kk + 1], sacc1, 0, 0, 0);
-      pacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][2], fo.row[kk + 1]), vf[kk + 1], pacc1, 0, 0, 0);
+      pacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][1], fo.row[kk + 1]), vf[kk + 1], pacc1, 0, 0, 0);
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -674,8 +706,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
     for (int mu = 0; mu < 2; ++mu)
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
-        const int off = fo.tr[db] + mu * 16 * G::ROWB;
-        const bf16x8 dot = tr_frag<DH>(smem[b][3], off), qt = tr_frag<DH>(smem[b][1], off);
+        const bf16x8 dot = trr_frag(smem[b][1], db, mu), qt = trr_frag(smem[b][0], db, mu);
         vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, ph[mu], vacc[db], 0, 0, 0);
         kacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dh[mu], kacc[db], 0, 0, 0);
         if constexpr (SPLIT) {
@@ -697,19 +728,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       TileRegs<DH, kBwdQ> qr, dr;
       float st_lse = 0.f, st_dlt = 0.f;
       auto fetch = [&](int t0) {  // a step's rows into registers (statistics: threads < 32)
-        load_tile<DH, kBwdQ>(qr, qg, rs, t0, t_end);
-        load_tile<DH, kBwdQ>(dr, dg, rs, t0, t_end);
-        const int t = t0 + (int)threadIdx.x;
-        if (threadIdx.x < kBwdQ && t < t_end) {
-          st_lse = a.lse[(int64_t)head * a.n + t];
-          st_dlt = a.delta[(int64_t)head * a.n + t];
-        }
+        const int nv = min(kBwdQ, t_end - t0);
+        load_tile_buf<DH, kBwdQ>(qr, qg + (int64_t)t0 * rs, (int)rs, nv);
+        load_tile_buf<DH, kBwdQ>(dr, dg + (int64_t)t0 * rs, (int)rs, nv);
+        const auto lr = __builtin_amdgcn_make_buffer_rsrc((void *)(a.lse + (int64_t)head * a.n + t0), (short)0,
+                                                          nv * 4, 0x00020000);
+        const auto dr_ = __builtin_amdgcn_make_buffer_rsrc((void *)(a.delta + (int64_t)head * a.n + t0), (short)0,
+                                                           nv * 4, 0x00020000);
+        st_lse = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, (int)threadIdx.x * 4, 0, 0));
+        st_dlt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dr_, (int)threadIdx.x * 4, 0, 0));
       };
       auto stage = [&](int b, int t0) {  // the fetched rows into buffer b
         store_tile<DH, kBwdQ, false>(smem[b][0], qr);
-        store_tile<DH, kBwdQ, true>(smem[b][1], qr);
-        store_tile<DH, kBwdQ, false>(smem[b][2], dr);
-        store_tile<DH, kBwdQ, true>(smem[b][3], dr);
+        store_tile<DH, kBwdQ, false>(smem[b][1], dr);
         if (threadIdx.x < kBwdQ) {
           const int t = t0 + threadIdx.x;
           const bool ok = t < t_end;
