@@ -64,14 +64,20 @@ struct BwdArgs {
 typedef short s16x4_b __attribute__((ext_vector_type(4)));
 
 // Geometry of an R x DH bf16 tile in LDS: row-major, 16-byte chunks XOR-
-// swizzled by row. ROW layout: for ds_read_b128 row fragments; TR layout: for
-// the 4 x 4 transpose reads.
+// swizzled by row. ROW layout: for ds_read_b128 row fragments and, read
+// transposed, for the 4 x 4 transpose reads; both free of bank conflicts:
+// the 16 rows of a row read get 16 (DH 128) or 8 pairs of (DH 64) distinct
+// chunk positions, and the four rows 4k..4k+3 of a transpose read, which take
+// 2 or 4 neighbouring chunks each, get disjoint ones. The swizzle depends on
+// the row modulo 16 only. TR layout: for the transpose reads only (the dQ
+// kernel's second copy of K).
 template <int DH>
 struct BTile {
   static constexpr int ROWB = DH * 2;
   static constexpr int CPR = DH / 8;
   static __device__ __forceinline__ int row_swz(int row, int ch) {
-    return ch ^ (CPR == 16 ? (row & 15) : ((row >> 1) & 7));
+    return ch ^ (CPR == 16 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                           : (((row >> 1) & 3) | ((((row >> 1) ^ (row >> 3)) & 1) << 2)));
   }
   static __device__ __forceinline__ int tr_swz(int row, int ch) {
     return ch ^ (CPR == 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1));
@@ -116,7 +122,7 @@ __device__ __forceinline__ void store_tile(unsigned char *dst, const TileRegs<DH
 // Lane-constant LDS byte offsets of the fragment reads of a tile, computed
 // once per kernel. row[kk]: the ROW-layout chunk of row lane%32, logical
 // chunk 2*kk + lane/32; rows 32.. are 32*ROWB further (same swizzle, which
-// depends on the row modulo 16, or on (row/2) modulo 8). tr[db]: the
+// depends on the row modulo 16). tr[db]: the
 // transpose read for feature block db, row group 0, half 0; row group mu and
 // half hv are (16*mu + 8*hv)*ROWB further (the TR swizzle depends on the row
 // modulo 4 only).
@@ -393,8 +399,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 // query tile T-1-p of the second chunk and then tile p of the first, so that
 // every block carries the same causal work. K is stored once, in the row
 // layout: the score products read its rows, and the dQ product reads it
-// transposed from the same copy (transpose reads that land two rows on the
-// same banks, a 2-way conflict, against a second copy of every tile).
+// transposed from the same copy.
 #if defined(__HIP_DEVICE_COMPILE__)
 #define TSP_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 #endif
@@ -442,8 +447,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_lds_kernel(BwdArgs a) {
   };
   // transposed reads of the row-layout K tile: lane l gets feature 32*db +
   // l%32's keys 16*kq + 8*hv + 4*(l/32) + {0..3} of half hv. The row swizzle
-  // depends on the row modulo 16 (or on row/2 modulo 8), which a step of 16
-  // keys keeps, so each (db, hv) has one lane-constant offset.
+  // depends on the row modulo 16, which a step of 16 keys keeps, so each
+  // (db, hv) has one lane-constant offset.
   int trr[ND][2];
   {
     const int r16 = lane & 15, dsub = (lane >> 4) & 1;
@@ -621,8 +626,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   }
   // transposed reads of the row-layout tiles: lane l gets feature 32*db +
   // l%32's rows 16*mu + 8*hv + 4*(l/32) + {0..3} of half hv (the row swizzle
-  // depends on the row modulo 16, or on row/2 modulo 8, which a step of 16
-  // rows keeps)
+  // depends on the row modulo 16, which a step of 16 rows keeps)
   int trr[ND][2];
   {
     const int r16 = lane & 15, dsub = (lane >> 4) & 1;
