@@ -229,6 +229,20 @@ KTRACE_WORKLOADS = {
               "attn_layer7b_kernel_stats.md", ""),
     "layer_bwd": ("one 7B TSP layer backward, both halves (rank 0 of D=8, S=131072, 16384 local tokens, bf16)",
                   "layer_bwd_7b_kernel_stats.md", "--workload layer_bwd --steps 5 --warmup 1"),
+    "attn_bwd": ("the 7B zigzag attention backward, statistics recomputed, P and dS as hi + lo (rank 0 of D=8, "
+                 "S=131072, 32 heads x 128, bf16)", "attn_bwd_7b_kernel_stats.md",
+                 "--workload attn_bwd --steps 3 --warmup 1"),
+    "attn_bwd_lse": ("the 7B zigzag attention backward from the forward's statistics, P and dS as hi + lo (rank 0 of "
+                     "D=8, S=131072, 32 heads x 128, bf16)", "attn_bwd_lse_7b_kernel_stats.md",
+                     "--workload attn_bwd_lse --steps 3 --warmup 1"),
+    "attn_bwd_lse_plain": ("the 7B zigzag attention backward from the forward's statistics, P and dS rounded once to "
+                           "bf16, the layer backward's call (rank 0 of D=8, S=131072, 32 heads x 128, bf16)",
+                           "attn_bwd_lse_plain_7b_kernel_stats.md",
+                           "--workload attn_bwd_lse --plain-pds --steps 3 --warmup 1"),
+    "mlp_bwd": ("the 7B MLP ring backward, Z recomputed (16384 tokens, h 4096, F 16384, D=8, bf16)",
+                "mlp_bwd_7b_kernel_stats.md", "--workload mlp_bwd --steps 10 --warmup 2"),
+    "mlp_bwd_z": ("the 7B MLP ring backward from the forward's Z (16384 tokens, h 4096, F 16384, D=8, bf16)",
+                  "mlp_bwd_z_7b_kernel_stats.md", "--workload mlp_bwd_z --steps 10 --warmup 2"),
 }
 
 
@@ -260,6 +274,12 @@ def summarize_ktrace(stats_csv, bench_json, workload="layer"):
     if rf:
         lines.append(f"- roofline ({rf['kernel']}): {rf['achieved']:.0f} {rf['unit']} of {rf['peak']:.0f}, "
                      f"frac {rf['frac']:.3f}; traffic {rf['traffic']}")
+    bwd = [r for r in rows if "attn_bwd_" in r["Name"]]
+    if bwd and "attn_bwd" in k:
+        b_ms = sum(float(r["AverageNs"]) for r in bwd) / 1e6
+        lines.append(f"- attention backward: profiler averages of its kernels add to {b_ms:.3f} ms vs HIP events "
+                     f"{k['attn_bwd']['ms_per_launch']:.3f} ms per call "
+                     f"({100 * (k['attn_bwd']['ms_per_launch'] / b_ms - 1):+.1f}%)")
     att = [r for r in rows if "attn_bf16_kernel" in r["Name"]]
     if att and "attention" in k:
         a_ms = float(att[0]["AverageNs"]) / 1e6
@@ -421,7 +441,7 @@ def main():
         summarize_traffic(args.summarize_traffic, copy_mib=args.copy_mib or 1024)
         return
     if args.summarize_ktrace:
-        summarize_ktrace(*args.summarize_ktrace, args.workload)
+        summarize_ktrace(*args.summarize_ktrace, args.workload + ("_plain" if args.plain_pds else ""))
         return
     if args.summarize_sq:
         summarize_sq(args.summarize_sq, args.workload)
