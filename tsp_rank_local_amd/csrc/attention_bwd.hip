@@ -656,25 +656,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   const int wkey0 = (int)kb0 + wave * 32;  // first key of this wave
 
   // S = Q K^T and dP = dO V^T of the step in buffer b, keys on the lanes:
-  // two accumulators per product (even and odd K slices), so that four
-  // independent MFMA chains interleave; each starts from a zero constant
+  // one MFMA chain each, started from a zero constant; the two chains
+  // interleave with each other and with the previous step's update (the
+  // chains split into even and odd K slices measured 2% slower: their
+  // merge costs 32 additions and, with the accumulators in AGPRs, 64 reads
+  // back per step)
   auto scores = [&](int b, f32x16 &sacc, f32x16 &pacc) {
     const f32x16 zero = {};
-    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][0], fo.row[0]), kf[0], zero, 0, 0, 0);
-    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][1], fo.row[0]), vf[0], zero, 0, 0, 0);
-    f32x16 sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][0], fo.row[1]), kf[1], zero, 0, 0, 0);
-    f32x16 pacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][1], fo.row[1]), vf[1], zero, 0, 0, 0);
 #pragma unroll
-    for (int kk = 2; kk < NK; kk += 2) {
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][0], fo.row[kk]), kf[kk], sacc, 0, 0, 0);
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][1], fo.row[kk]), vf[kk], pacc, 0, 0, 0);
-      sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][0], fo.row[kk + 1]), kf[kk + 1], sacc1, 0, 0, 0);
-      pacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][1], fo.row[kk + 1]), vf[kk + 1], pacc1, 0, 0, 0);
-    }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      sacc[v] += sacc1[v];
-      pacc[v] += pacc1[v];
+    for (int kk = 0; kk < NK; ++kk) {
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][0], fo.row[kk]), kf[kk], kk == 0 ? zero : sacc,
+                                                     0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][1], fo.row[kk]), vf[kk], kk == 0 ? zero : pacc,
+                                                     0, 0, 0);
     }
   };
   // sacc[v]: S[row 8*(v/4) + 4*g + v%4][key]. P and dS of the step in buffer
