@@ -730,7 +730,7 @@ def main():
         # the attention backward: 4.40e13 of the step's 5.72e13 algorithmic flops
         t_b = kernels["attn_bwd"]["ms_per_launch"] * 1e-3
         achieved = 2.5 * flops["attention"] / t_b / 1e12
-        roofline = {"kernel": "attn_bwd_stats_kernel + attn_bwd_dq_kernel + attn_bwd_dkv_kernel<128>",
+        roofline = {"kernel": "attn_bwd_stats_kernel + attn_bwd_dq_lds_kernel<128> + attn_bwd_dkv_kernel<128>",
                     "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
                     "frac": achieved * 1e12 / PEAK_BF16, "traffic": None}
     elif "attention" in kernels:
@@ -747,7 +747,9 @@ def main():
     elif "attn_bwd" in kernels:
         t_b = kernels["attn_bwd"]["ms_per_launch"] * 1e-3
         achieved = 2.5 * flops["attention"] / t_b / 1e12
-        roofline = {"kernel": "attn_bwd_dq_kernel + attn_bwd_dkv_kernel<128>", "bound": "mfma", "achieved": achieved,
+        names = ("attn_bwd_dq_kernel<128> + attn_bwd_dkv_kernel<128>" if args.workload == "attn_bwd" else
+                 "attn_bwd_stats_kernel + attn_bwd_dq_lds_kernel<128> + attn_bwd_dkv_kernel<128>")
+        roofline = {"kernel": names, "bound": "mfma", "achieved": achieved,
                     "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_BF16, "traffic": None}
     elif "bwd_gemm" in kernels:
         # launches of one product size each (Z recomputation unless Z is given, dZ, dW1, dW2, dx)
