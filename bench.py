@@ -229,6 +229,9 @@ KTRACE_WORKLOADS = {
               "attn_layer7b_kernel_stats.md", ""),
     "layer_bwd": ("one 7B TSP layer backward, both halves (rank 0 of D=8, S=131072, 16384 local tokens, bf16)",
                   "layer_bwd_7b_kernel_stats.md", "--workload layer_bwd --steps 5 --warmup 1"),
+    "train": ("one 7B TSP layer training step: the forward keeping the attention output and statistics, both "
+              "halves of the backward from them (rank 0 of D=8, S=131072, 16384 local tokens, bf16)",
+              "train_7b_kernel_stats.md", "--workload train --steps 5 --warmup 1"),
     "attn_bwd": ("the 7B zigzag attention backward, statistics recomputed, P and dS as hi + lo (rank 0 of D=8, "
                  "S=131072, 32 heads x 128, bf16)", "attn_bwd_7b_kernel_stats.md",
                  "--workload attn_bwd --steps 3 --warmup 1"),
@@ -412,7 +415,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", choices=["layer", "mlp", "attn", "layers32", "mlp_bwd", "mlp_bwd_z", "attn_bwd",
-                                           "attn_bwd_lse", "layer_bwd"], default="layer")
+                                           "attn_bwd_lse", "layer_bwd", "train"], default="layer")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--rope-base", type=float, default=0.0,
                     help="rotary embedding base for the layer workloads (0 = none, the pages' model)")
@@ -471,7 +474,7 @@ def main():
     stream = torch.cuda.current_stream()
     flops = layer_flops(sh, r)
 
-    if args.workload in ("layer", "mlp", "mlp_bwd", "mlp_bwd_z", "layer_bwd"):
+    if args.workload in ("layer", "mlp", "mlp_bwd", "mlp_bwd_z", "layer_bwd", "train"):
         w = synth.layer_weights(sh, seed=seed)
         wd = {k: ([tsp.to_device(a, "bf16") for a in v] if isinstance(v, list) else tsp.to_device(v, "bf16"))
               for k, v in w.items()}
@@ -523,6 +526,45 @@ def main():
         workload = (f"tsp_layer_bwd: backward of one 7B dense decoder layer (h=4096, 32x128 heads{kv_note}, FFN 16384, "
                     f"bf16) on rank {r} of D=8 at S=131072, 16384 local zigzag tokens, both halves (forward "
                     f"recomputed from x; dx, dK/dV of every key row and all weight and gain gradients in fp32)")
+    elif args.workload == "train":
+        # one training step of the layer on one rank: the forward that keeps
+        # the attention output and statistics, then both halves of the
+        # backward that take them (no second attention forward); the summed
+        # K/V-row gradients of the second half are seeded values as above
+        x = synth.activations(N, sh.h, seed=seed)
+        dy = synth.activations(N, sh.h, seed=seed, tid=synth.TID_DY)
+        k_rem, v_rem = synth.remote_kv(sh, seed=seed)
+        dkl = synth.normal((N, sh.kv_heads, sh.Dh), seed, synth.TID_DK_LOC, std=0.05)
+        dvl = synth.normal((N, sh.kv_heads, sh.Dh), seed, synth.TID_DV_LOC, std=0.05)
+        xd, dyd = tsp.to_device(x, "f32"), tsp.to_device(dy, "f32")
+        kf, vf = tsp.to_device(k_rem, "bf16"), tsp.to_device(v_rem, "bf16")
+        dkld, dvld = tsp.to_device(dkl, "f32"), tsp.to_device(dvl, "f32")
+        y = torch.empty((N, sh.h), dtype=torch.float32, device="cuda")
+        o_sv = torch.empty((N, sh.H, sh.Dh), dtype=torch.float32, device="cuda")
+        lse_sv = torch.empty((sh.H, N), dtype=torch.float32, device="cuda")
+        dkf = torch.empty((sh.S, sh.kv_heads, sh.Dh), dtype=torch.float32, device="cuda")
+        dvf = torch.empty_like(dkf)
+        dx = torch.empty((N, sh.h), dtype=torch.float32, device="cuda")
+        grads = {k: [torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in wd[k]]
+                 for k in ("wqkv", "wo", "w1", "w2")}
+        grads.update(g_attn=torch.empty(sh.h, dtype=torch.float32, device="cuda"),
+                     g_mlp=torch.empty(sh.h, dtype=torch.float32, device="cuda"))
+        ws_f = torch.empty(tsp.workspace_size(shape, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(tsp.workspace_size(shape, tsp.TSP_WS_LAYER_BWD), dtype=torch.uint8, device="cuda")
+
+        def step():
+            tsp.tsp_layer_fwd_save(shape, wd, xd, kf, vf, y, o_sv, lse_sv, tsp.TSP_PHASE_ALL, ws_f)
+            tsp.tsp_layer_bwd_ex(shape, wd, xd, kf, vf, dyd, o_sv, lse_sv, dkf, dvf, None, None, None, grads,
+                                 tsp.TSP_BWD_ATTN, ws)
+            tsp.tsp_layer_bwd_ex(shape, wd, xd, None, None, None, None, None, None, None, dkld, dvld, dx, grads,
+                                 tsp.TSP_BWD_QKV, ws)
+        # algorithmic: the forward's flops and the backward's chain-rule products
+        step_flops = flops["total"] + 2.0 * (flops["qkv"] + flops["outproj"] + flops["mlp"]) + 2.5 * flops["attention"]
+        step_exps = 3 * sh.H * attn_pairs(sh.S, sh.D, r)
+        workload = (f"tsp_layer_fwd_save + tsp_layer_bwd_ex: one training step of one 7B dense decoder layer (h=4096, "
+                    f"32x128 heads{kv_note}, FFN 16384, bf16) on rank {r} of D=8 at S=131072, 16384 local zigzag "
+                    f"tokens: the forward keeping the attention output and statistics, both halves of the backward "
+                    f"from them")
     elif args.workload == "mlp":
         x = synth.activations(N, sh.h, seed=2, dtype="bf16")
         xd = tsp.to_device(x, "bf16")
@@ -726,7 +768,7 @@ def main():
         if cls in kernels:
             kernels[cls].update(v)
     roofline = None
-    if args.workload == "layer_bwd" and "attn_bwd" in kernels:
+    if args.workload in ("layer_bwd", "train") and "attn_bwd" in kernels:
         # the attention backward: 4.40e13 of the step's 5.72e13 algorithmic flops
         t_b = kernels["attn_bwd"]["ms_per_launch"] * 1e-3
         achieved = 2.5 * flops["attention"] / t_b / 1e12

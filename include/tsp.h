@@ -385,6 +385,24 @@ tsp_status tsp_layer_fwd(const tsp_shape *shape, const tsp_layer_weights *w, con
                          void *k_full, void *v_full, float *y, unsigned phases, void *ws,
                          size_t ws_bytes, void *stream);
 
+/* tsp_layer_fwd for training: the same layer (the passages and arguments
+ * above, y the same bit for bit), and in the same pass the attention output
+ * and its rows' statistics, kept for tsp_layer_bwd_ex so that the backward
+ * does not run the attention forward again (the pages report training
+ * throughput: the ageofai.tools review "Zyphra TSP: 2.6x Faster AI Training
+ * Review", key features and benefits). bf16 only (else
+ * TSP_ERR_UNSUPPORTED).
+ *  o_save: [S/D][H][Dh] fp32, the attention output O before the output
+ *    projection (which reads it rounded to bf16), written by PHASE_REST. On
+ *    rank 0 the first rows are those of the bf16 path (their y is
+ *    recomputed in fp32 as above, their O is not).
+ *  lse_save: [H][S/D] fp32, each row's natural log-sum-exp of its scaled
+ *    scores (over its visible keys), written by PHASE_REST.
+ * Both must be given and must not overlap any other argument. */
+tsp_status tsp_layer_fwd_save(const tsp_shape *shape, const tsp_layer_weights *w, const float *x,
+                              void *k_full, void *v_full, float *y, float *o_save, float *lse_save,
+                              unsigned phases, void *ws, size_t ws_bytes, void *stream);
+
 /* Backward of tsp_layer_fwd on rank r (an optional extension, like
  * tsp_mlp_ring_bwd: the pages report training throughput, the ageofai.tools
  * review "Zyphra TSP: 2.6x Faster AI Training Review", key features and
@@ -434,6 +452,23 @@ tsp_status tsp_layer_bwd(const tsp_shape *shape, const tsp_layer_weights *w, con
                          float *dv_full, const float *dk_loc, const float *dv_loc, float *dx,
                          const tsp_layer_grads *grads, unsigned phases, void *ws, size_t ws_bytes,
                          void *stream);
+
+/* tsp_layer_bwd with the attention output and statistics that
+ * tsp_layer_fwd_save kept (same passages and arguments as tsp_layer_bwd).
+ * o_saved [S/D][H][Dh] and lse_saved [H][S/D] fp32, both NULL (then the call
+ * is tsp_layer_bwd) or both given (bf16 only, else TSP_ERR_UNSUPPORTED;
+ * read by TSP_BWD_ATTN): the attention forward is not run again. Q is
+ * recomputed with the forward's pre-scaling by scale * log2(e), which
+ * reproduces the forward's Q bit for bit, so the saved statistics belong to
+ * the scores the backward forms; dK is then ln 2 * dS^T Q' (Q' the
+ * pre-scaled Q), the same gradient. They must come from the forward of the
+ * same x, weights and K/V. */
+tsp_status tsp_layer_bwd_ex(const tsp_shape *shape, const tsp_layer_weights *w, const float *x,
+                            const void *k_full, const void *v_full, const float *dy,
+                            const float *o_saved, const float *lse_saved, float *dk_full,
+                            float *dv_full, const float *dk_loc, const float *dv_loc, float *dx,
+                            const tsp_layer_grads *grads, unsigned phases, void *ws,
+                            size_t ws_bytes, void *stream);
 
 /* Optional launch timing. When enabled, every kernel the library enqueues is
  * bracketed by HIP events recorded on the same stream; tsp_profile_read

@@ -384,6 +384,70 @@ def test_zigzag_index_errors():
     assert list(pos) == [2, 3, 12, 13]
 
 
+def test_layer_fwd_save_errors():
+    """The training forward checks o_save and lse_save like every other
+    argument and needs bf16; nothing is enqueued on any error."""
+    w = dict(g_attn=FAKE, g_mlp=FAKE, wqkv=[FAKE] * 4, wo=[FAKE] * 4, w1=[FAKE] * 4, w2=[FAKE] * 4)
+    a = dict(x=FAKE + (1 << 32), k_full=FAKE + (2 << 32), v_full=FAKE + (3 << 32), y=FAKE + (4 << 32),
+             ws=FAKE + (5 << 32), o=FAKE + (6 << 32), lse=FAKE + (7 << 32))
+
+    def call(shape=None, **kw):
+        s = shape or _shape(dtype="bf16")
+        b = dict(a)
+        b.update(kw)
+        with pytest.raises(tsp.TspError) as ei:
+            tsp.tsp_layer_fwd_save(s, w, b["x"], b["k_full"], b["v_full"], b["y"], b["o"], b["lse"], 3, b["ws"],
+                                   tsp.workspace_size(s, tsp.TSP_WS_LAYER), stream=0)
+        return ei.value.status, tsp.lib().tsp_last_error()
+
+    st, msg = call(o=None)
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"o_save is NULL" in msg
+    st, msg = call(lse=None)
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"lse_save is NULL" in msg
+    assert call(shape=_shape(dtype="f32"))[0] == tsp.TSP_ERR_UNSUPPORTED
+    st, msg = call(o=a["y"] + 1024)  # O over y
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"overlaps" in msg
+    st, msg = call(lse=a["ws"] + 4096)  # statistics inside the workspace
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"overlaps" in msg
+    assert call(o=a["o"] + 8)[0] == tsp.TSP_ERR_INVALID_ARG  # misaligned
+
+
+def test_layer_bwd_ex_errors():
+    """tsp_layer_bwd_ex: the saved O and statistics come together, need bf16
+    and must not overlap an output; nothing is enqueued on any error."""
+    s = _shape(dtype="bf16")
+    need = tsp.workspace_size(s, tsp.TSP_WS_LAYER_BWD)
+    w = dict(g_attn=FAKE, g_mlp=FAKE, wqkv=[FAKE] * 4, wo=[FAKE] * 4, w1=[FAKE] * 4, w2=[FAKE] * 4)
+
+    def gl(base):
+        return [FAKE + (base << 32) + (i << 28) for i in range(4)]
+
+    grads = dict(g_attn=FAKE + (20 << 32), g_mlp=FAKE + (21 << 32), wqkv=gl(22), wo=gl(23), w1=gl(24), w2=gl(25))
+    a = dict(x=FAKE + (1 << 32), k_full=FAKE + (2 << 32), v_full=FAKE + (3 << 32), dy=FAKE + (4 << 32),
+             dk_full=FAKE + (5 << 32), dv_full=FAKE + (6 << 32), dk_loc=FAKE + (7 << 32), dv_loc=FAKE + (8 << 32),
+             dx=FAKE + (9 << 32), ws=FAKE + (10 << 32), o=FAKE + (11 << 32), lse=FAKE + (12 << 32))
+
+    def call(shape=s, **kw):
+        b = dict(a)
+        b.update(kw)
+        with pytest.raises(tsp.TspError) as ei:
+            tsp.tsp_layer_bwd_ex(shape, w, b["x"], b["k_full"], b["v_full"], b["dy"], b["o"], b["lse"], b["dk_full"],
+                                 b["dv_full"], b["dk_loc"], b["dv_loc"], b["dx"], grads, tsp.TSP_BWD_ATTN, b["ws"],
+                                 need if shape is s else 1 << 40, stream=0)
+        return ei.value.status, tsp.lib().tsp_last_error()
+
+    st, msg = call(lse=None)
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"both" in msg
+    st, msg = call(o=None)
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"both" in msg
+    assert call(shape=_shape(dtype="f32"))[0] == tsp.TSP_ERR_UNSUPPORTED
+    st, msg = call(dk_full=a["o"] + 4096)  # an output over the saved O
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"overlaps" in msg
+    st, msg = call(o=a["ws"])  # the saved O inside the workspace
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"overlaps" in msg
+    assert call(lse=a["lse"] + 8)[0] == tsp.TSP_ERR_INVALID_ARG  # misaligned
+
+
 def test_layer_bwd_workspace_and_errors():
     # dh1, dq fp32 [N][h]; then the larger phase: nine [N][h] in dtype, three
     # fp32 [N][h], W_O^T, the forward's lse [H][N], the attention backward's

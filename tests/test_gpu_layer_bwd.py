@@ -97,8 +97,33 @@ LAYER_BWD_CASES = [
 ]
 
 
+def _saved_forward(torch, s, wd, x, kd, vd):
+    """tsp_layer_fwd_save on the given K/V: PHASE_KV on scratch copies (the
+    rank's own rows stay the given ones in kd, vd), then PHASE_REST on kd,
+    vd with the same workspace. Returns the kept O and log-sum-exp."""
+    N, H, Dh = s.S // s.D, s.H, s.Dh
+    ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
+    y = _nan(torch, N, s.h)
+    o = _nan(torch, N, H, Dh)
+    lse = _nan(torch, H, N)
+    tsp.tsp_layer_fwd_save(s, wd, x, kd.clone(), vd.clone(), y, o, lse, tsp.TSP_PHASE_KV, ws)
+    tsp.tsp_layer_fwd_save(s, wd, x, kd, vd, y, o, lse, tsp.TSP_PHASE_REST, ws)
+    return o, lse
+
+
 @pytest.mark.parametrize("S,D,h,H,Dh,F,Hkv,dtype", LAYER_BWD_CASES)
 def test_layer_bwd_every_rank(torch, S, D, h, H, Dh, F, Hkv, dtype):
+    _layer_bwd_every_rank(torch, S, D, h, H, Dh, F, Hkv, dtype, saved=False)
+
+
+@pytest.mark.parametrize("S,D,h,H,Dh,F,Hkv,dtype", [c for c in LAYER_BWD_CASES if c[-1] == "bf16"])
+def test_layer_bwd_saved_every_rank(torch, S, D, h, H, Dh, F, Hkv, dtype):
+    """tsp_layer_bwd_ex with the attention output and statistics that
+    tsp_layer_fwd_save kept, held to the same oracle and tolerances."""
+    _layer_bwd_every_rank(torch, S, D, h, H, Dh, F, Hkv, dtype, saved=True)
+
+
+def _layer_bwd_every_rank(torch, S, D, h, H, Dh, F, Hkv, dtype, saved):
     shape = synth.LayerShape(S=S, D=D, h=h, H=H, Dh=Dh, F=F, dtype=dtype, Hkv=Hkv)
     N, Hk = S // D, shape.kv_heads
     w = synth.layer_weights(shape, seed=61, gain="random")
@@ -119,9 +144,16 @@ def test_layer_bwd_every_rank(torch, S, D, h, H, Dh, F, Hkv, dtype):
     dvf = [_nan(torch, S, Hk, Dh) for _ in range(D)]
     g = [_grads(torch, wd) for _ in range(D)]
     for r in range(D):
-        log(f"layer bwd ATTN S={S} D={D} r={r} h={h} H={H} Hkv={Hk} Dh={Dh} F={F} {dtype}")
-        tsp.tsp_layer_bwd(shapes[r], wd, xs[r], kd, vd, dys[r], dkf[r], dvf[r], None, None, None,
-                          {**g[r], "wqkv": None, "g_attn": None}, tsp.TSP_BWD_ATTN, wss[r])
+        log(f"layer bwd ATTN S={S} D={D} r={r} h={h} H={H} Hkv={Hk} Dh={Dh} F={F} {dtype}"
+            f"{' from the saved forward' if saved else ''}")
+        ga = {**g[r], "wqkv": None, "g_attn": None}
+        if saved:
+            o, lse = _saved_forward(torch, shapes[r], wd, xs[r], kd, vd)
+            tsp.tsp_layer_bwd_ex(shapes[r], wd, xs[r], kd, vd, dys[r], o, lse, dkf[r], dvf[r], None, None, None, ga,
+                                 tsp.TSP_BWD_ATTN, wss[r])
+        else:
+            tsp.tsp_layer_bwd(shapes[r], wd, xs[r], kd, vd, dys[r], dkf[r], dvf[r], None, None, None, ga,
+                              tsp.TSP_BWD_ATTN, wss[r])
     torch.cuda.synchronize()
     a = [oracle.layer_bwd_attn_part(x_all[pos[r]], pos[r], w64, kf64, vf64, dy_all[pos[r]], H, Dh, shape.eps,
                                     shape.scale, Hk) for r in range(D)]
@@ -212,8 +244,10 @@ def _sample_rows(N, C):
     return np.array(sorted(set(t)), dtype=np.int64)
 
 
-@pytest.mark.parametrize("r", [0, 5])
-def test_layer_bwd_7b_sampled_rows(torch, r):
+@pytest.mark.parametrize("r,saved", [(0, False), (5, False), (0, True)])
+def test_layer_bwd_7b_sampled_rows(torch, r, saved):
+    """saved: the first half takes the attention output and statistics of
+    tsp_layer_fwd_save instead of running the attention forward again."""
     shape = synth.SEVEN_B
     S, D, h, H, Dh, F = shape.S, shape.D, shape.h, shape.H, shape.Dh, shape.F
     N, C = S // D, S // (2 * D)
@@ -232,10 +266,13 @@ def test_layer_bwd_7b_sampled_rows(torch, r):
     ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER_BWD), dtype=torch.uint8, device="cuda")
     dkf, dvf, dx = _nan(torch, S, H, Dh), _nan(torch, S, H, Dh), _nan(torch, N, h)
     g = _grads(torch, wd)
-    log(f"layer bwd 7B S={S} D={D} r={r}: both phases, {len(T)} rows of dy")
+    log(f"layer bwd 7B S={S} D={D} r={r}: both phases, {len(T)} rows of dy{' from the saved forward' if saved else ''}")
     xd = up(x, "f32")
-    tsp.tsp_layer_bwd(s, wd, xd, up(k_rem, "bf16"), up(v_rem, "bf16"), up(dy, "f32"), dkf, dvf, None, None, None,
-                      {**g, "wqkv": None, "g_attn": None}, tsp.TSP_BWD_ATTN, ws)
+    kd, vd = up(k_rem, "bf16"), up(v_rem, "bf16")
+    o, lse = _saved_forward(torch, s, wd, xd, kd, vd) if saved else (None, None)
+    tsp.tsp_layer_bwd_ex(s, wd, xd, kd, vd, up(dy, "f32"), o, lse, dkf, dvf, None, None, None,
+                         {**g, "wqkv": None, "g_attn": None}, tsp.TSP_BWD_ATTN, ws)
+    del o, lse, kd, vd
     tsp.tsp_layer_bwd(s, wd, xd, None, None, None, None, None, up(dkl, "f32"), up(dvl, "f32"), dx,
                       {**g, "wo": None, "w1": None, "w2": None, "g_mlp": None}, tsp.TSP_BWD_QKV, ws)
     torch.cuda.synchronize()
@@ -258,3 +295,65 @@ def test_layer_bwd_7b_sampled_rows(torch, r):
     assert_close_nw(dv_got[:lim], a["dv"][:lim], f"dv_full r={r}")
     _close_grads(g, {**a, **b}, "bf16", f"r={r}",
                  ("wqkv", "wo", "w1", "w2", "g_attn", "g_mlp"))
+
+
+@pytest.mark.parametrize("S,D,h,H,Dh,F,Hkv", [(1024, 4, 256, 4, 64, 1024, 0), (2048, 2, 512, 8, 64, 1024, 2),
+                                              (2048, 4, 512, 4, 128, 2048, 0)])
+def test_layer_fwd_save_every_rank(torch, S, D, h, H, Dh, F, Hkv):
+    """tsp_layer_fwd_save: y and the rank's K/V rows bit for bit those of
+    tsp_layer_fwd; the kept O against the oracle's attention output (the
+    backward's norm-wise rule), the kept log-sum-exp against the oracle's
+    within the bf16 rounding of the scores."""
+    shape = synth.LayerShape(S=S, D=D, h=h, H=H, Dh=Dh, F=F, dtype="bf16", Hkv=Hkv)
+    N, Hk = S // D, shape.kv_heads
+    w = synth.layer_weights(shape, seed=63, gain="random")
+    w64, wd = _w64(w, "bf16"), _dev_weights(w, "bf16")
+    k_rem, v_rem = synth.remote_kv(shape, seed=63)
+    wq = oracle.unshard_attention_weights(w64["wqkv"], w64["wo"], H, Dh, Hk)[0]
+    for r in range(D):
+        x = synth.activations(N, h, seed=63 + r)
+        s = tsp.make_shape(S, D, r, h, H, Dh, F, eps=shape.eps, dtype="bf16", Hkv=Hkv)
+        log(f"layer fwd with the attention output kept: S={S} D={D} r={r} h={h} H={H} Hkv={Hk} Dh={Dh} F={F}")
+        xd = up(x, "f32")
+        ys, ks, vs = [], [], []
+        o, lse = _nan(torch, N, H, Dh), _nan(torch, H, N)
+        for save in (False, True):
+            kd, vd = up(k_rem, "bf16"), up(v_rem, "bf16")
+            ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
+            y = _nan(torch, N, h)
+            if save:
+                tsp.tsp_layer_fwd_save(s, wd, xd, kd, vd, y, o, lse, tsp.TSP_PHASE_ALL, ws)
+            else:
+                tsp.tsp_layer_fwd(s, wd, xd, kd, vd, y, tsp.TSP_PHASE_ALL, ws)
+            torch.cuda.synchronize()
+            ys.append(down(y))
+            ks.append(down(kd))
+            vs.append(down(vd))
+        assert np.array_equal(ys[0], ys[1]), "y differs from tsp_layer_fwd"
+        assert np.array_equal(ks[0], ks[1]) and np.array_equal(vs[0], vs[1])
+        pos = oracle.zigzag_positions(S, D, r)
+        k_all, v_all = f64(k_rem, "bf16").copy(), f64(v_rem, "bf16").copy()
+        k_all[pos], v_all[pos] = oracle.local_kv(x, w64, H, Dh, shape.eps, pos, 0.0, Hk)
+        q = (oracle.rms_norm(x, w64["g_attn"], shape.eps) @ wq.T).reshape(N, H, Dh)
+        # O is an intermediate of bf16 Q, K and V (rounded once each): rows
+        # that see few keys carry their rounding unaveraged (rank 0's first
+        # rows near 2e-2 of the tensor's rms, and the forward recomputes
+        # their y in fp32, not their kept O). The backward consumes O, so it
+        # is held to the backward's norm-wise rule; y itself is bit for bit
+        # that of tsp_layer_fwd, whose parity the forward tests hold.
+        assert_close_nw(down(o), oracle.causal_attention(q, k_all, v_all, pos, shape.scale), f"o r={r}")
+        want = oracle.causal_attention_lse(q, k_all, pos, shape.scale)
+        got = down(lse)
+        assert np.all(np.isfinite(got))
+        # each score carries the bf16 rounding of its q and k (and of the
+        # normed input behind q), at most about 2^-8 |q| |k| scale; the row's
+        # log-sum-exp moves by at most its largest such change (bound taken
+        # with a factor 2 to spare and the largest key norm of the head)
+        qn = np.linalg.norm(q, axis=2)                                     # [N, H]
+        kn = np.linalg.norm(k_all, axis=2).max(axis=0)                     # [Hkv]
+        kn = np.repeat(kn, H // Hk)                                        # per query head
+        tol = 2.0 ** -7 * shape.scale * (qn * kn[None, :]).T + 1e-4        # [H, N]
+        err = np.abs(got - want)
+        log(f"  lse: max|err| = {err.max():.3e}, worst err/bound = {(err / tol).max():.3f}")
+        assert np.all(err <= tol), "log-sum-exp outside the rounding bound"
+

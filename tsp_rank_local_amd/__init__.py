@@ -20,7 +20,7 @@ __all__ = [
     "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_zigzag_attn_ex", "tsp_mlp_ring",
     "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_zigzag_attn_bwd_noalloc", "tsp_zigzag_attn_lse",
     "tsp_zigzag_attn_bwd_lse", "tsp_zigzag_attn_bwd_ex", "tsp_layer_fwd", "tsp_layer_bwd", "tsp_mlp_ring_z",
-    "tsp_mlp_ring_bwd_z", "profile_enable",
+    "tsp_mlp_ring_bwd_z", "tsp_layer_fwd_save", "tsp_layer_bwd_ex", "profile_enable",
     "profile_reset", "profile_read", "TspLayerGrads",
     "TSP_F32", "TSP_BF16", "TSP_ATTN_Q_LOG2_SCALED", "TSP_PHASE_KV", "TSP_PHASE_REST", "TSP_PHASE_ALL",
     "TSP_WS_MLP", "TSP_WS_LAYER", "TSP_WS_MLP_BWD", "TSP_WS_ATTN_BWD", "TSP_WS_LAYER_BWD", "TSP_BWD_ATTN", "TSP_BWD_QKV",
@@ -49,7 +49,7 @@ EXPORTED_SYMBOLS = [
     "tsp_zigzag_index_host", "tsp_zigzag_index", "tsp_zigzag_attn", "tsp_zigzag_attn_ex", "tsp_mlp_ring",
     "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd", "tsp_zigzag_attn_bwd_noalloc", "tsp_zigzag_attn_lse",
     "tsp_zigzag_attn_bwd_lse", "tsp_zigzag_attn_bwd_ex", "tsp_layer_fwd", "tsp_layer_bwd", "tsp_mlp_ring_z",
-    "tsp_mlp_ring_bwd_z", "tsp_profile_enable",
+    "tsp_mlp_ring_bwd_z", "tsp_layer_fwd_save", "tsp_layer_bwd_ex", "tsp_profile_enable",
     "tsp_profile_reset", "tsp_profile_read",
 ]
 
@@ -116,6 +116,10 @@ def lib() -> ctypes.CDLL:
     L.tsp_layer_fwd.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, ctypes.c_uint, vp, sz, vp]
     L.tsp_layer_bwd.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 ctypes.POINTER(TspLayerGrads), ctypes.c_uint, vp, sz, vp]
+    L.tsp_layer_fwd_save.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, vp, vp, ctypes.c_uint, vp,
+                                     sz, vp]
+    L.tsp_layer_bwd_ex.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   ctypes.POINTER(TspLayerGrads), ctypes.c_uint, vp, sz, vp]
     L.tsp_profile_enable.argtypes = [ctypes.c_int]
     L.tsp_profile_enable.restype = None
     L.tsp_profile_reset.argtypes = []
@@ -125,7 +129,7 @@ def lib() -> ctypes.CDLL:
                  "tsp_zigzag_attn_ex", "tsp_mlp_ring", "tsp_mlp_ring_bwd", "tsp_zigzag_attn_bwd",
                  "tsp_zigzag_attn_bwd_noalloc", "tsp_layer_fwd", "tsp_layer_bwd",
                  "tsp_zigzag_attn_lse", "tsp_zigzag_attn_bwd_lse", "tsp_zigzag_attn_bwd_ex", "tsp_mlp_ring_z",
-                 "tsp_mlp_ring_bwd_z",
+                 "tsp_mlp_ring_bwd_z", "tsp_layer_fwd_save", "tsp_layer_bwd_ex",
                  "tsp_profile_read"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -280,6 +284,20 @@ def tsp_layer_fwd(shape: TspShape, w: dict, x, k_full, v_full, y, phases, ws, ws
                                int(phases), _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
+def tsp_layer_fwd_save(shape: TspShape, w: dict, x, k_full, v_full, y, o_save, lse_save, phases, ws, ws_bytes=None,
+                       stream=None) -> None:
+    """tsp_layer_fwd that also keeps the attention output o_save [N][H][Dh]
+    and the rows' natural log-sum-exp lse_save [H][N] (fp32) for
+    tsp_layer_bwd_ex."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    cw, keep_w = _weights(w)
+    _check(lib().tsp_layer_fwd_save(ctypes.byref(shape), ctypes.byref(cw), _ptr(x), _ptr(k_full), _ptr(v_full),
+                                    _ptr(y), _ptr(o_save), _ptr(lse_save), int(phases), _ptr(ws), int(ws_bytes),
+                                    _stream(stream)))
+    del keep_w
+
+
 def _weights(w: dict) -> tuple:
     """A TspLayerWeights for a dict of g_attn, g_mlp and shard lists, plus the
     pointer arrays it refers to (kept alive by the caller)."""
@@ -301,6 +319,23 @@ def tsp_layer_bwd(shape: TspShape, w: dict, x, k_full, v_full, dy, dk_full, dv_f
     _check(lib().tsp_layer_bwd(ctypes.byref(shape), ctypes.byref(cw), _ptr(x), _ptr(k_full), _ptr(v_full), _ptr(dy),
                                _ptr(dk_full), _ptr(dv_full), _ptr(dk_loc), _ptr(dv_loc), _ptr(dx), ctypes.byref(cg),
                                int(phases), _ptr(ws), int(ws_bytes), _stream(stream)))
+    del keep_w
+
+
+def tsp_layer_bwd_ex(shape: TspShape, w: dict, x, k_full, v_full, dy, o_saved, lse_saved, dk_full, dv_full, dk_loc,
+                     dv_loc, dx, grads: dict, phases, ws, ws_bytes=None, stream=None) -> None:
+    """tsp_layer_bwd with the saved attention output and statistics of
+    tsp_layer_fwd_save (both None: the same as tsp_layer_bwd)."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    cw, keep_w = _weights(w)
+    garr = {k: (_ptr_array(grads[k]) if grads.get(k) is not None else None) for k in ("wqkv", "wo", "w1", "w2")}
+    cg = TspLayerGrads(_ptr(grads.get("g_attn")), _ptr(grads.get("g_mlp")), garr["wqkv"], garr["wo"], garr["w1"],
+                       garr["w2"])
+    _check(lib().tsp_layer_bwd_ex(ctypes.byref(shape), ctypes.byref(cw), _ptr(x), _ptr(k_full), _ptr(v_full),
+                                  _ptr(dy), _ptr(o_saved), _ptr(lse_saved), _ptr(dk_full), _ptr(dv_full),
+                                  _ptr(dk_loc), _ptr(dv_loc), _ptr(dx), ctypes.byref(cg), int(phases), _ptr(ws),
+                                  int(ws_bytes), _stream(stream)))
     del keep_w
 
 

@@ -720,10 +720,18 @@ tsp_status tsp_mlp_ring_bwd_z(const tsp_shape *s, const void *x, const void *z, 
   return mlp_ring_bwd(s, x, z, w1, w2, dy, dx_residual, dx, dw1, dw2, ws, ws_bytes, stream);
 }
 
-tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const float *x, void *k_full,
-                         void *v_full, float *y, unsigned phases, void *ws_, size_t ws_bytes, void *stream_) {
+// The layer forward; with o_save and lse_save (bf16), the attention also
+// writes its fp32 output and the rows' natural log-sum-exp there for the
+// backward, and the output projection reads O packed from o_save.
+static tsp_status layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const float *x, void *k_full,
+                            void *v_full, float *y, float *o_save, float *lse_save, unsigned phases, void *ws_,
+                            size_t ws_bytes, void *stream_) {
   tsp_status st = check_layer_shape(s);
   if (st) return st;
+  const bool save = o_save != nullptr || lse_save != nullptr;
+  if (save && (!o_save || !lse_save)) return fail(TSP_ERR_INVALID_ARG, "o_save and lse_save must both be given");
+  if (save && s->dtype != TSP_BF16) return fail(TSP_ERR_UNSUPPORTED, "saving the attention output needs bf16");
+  if (save && ((st = check_ptr(o_save, "o_save")) || (st = check_ptr(lse_save, "lse_save")))) return st;
   if (!w) return fail(TSP_ERR_INVALID_ARG, "weights is NULL");
   if (phases == 0 || (phases & ~3u)) return fail(TSP_ERR_INVALID_ARG, "phases=%u must be 1, 2 or 3", phases);
   if ((st = check_ptr(x, "x")) || (st = check_ptr(k_full, "k_full")) || (st = check_ptr(v_full, "v_full")) ||
@@ -742,9 +750,12 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
   const size_t e = elem_bytes(s->dtype);
   const Range rx{x, (size_t)N * h * 4, "x"}, ry{y, (size_t)N * h * 4, "y"}, rws{ws_, L.total, "ws"};
   const Range rk{k_full, (size_t)s->S * hkv * e, "k_full"}, rv{v_full, (size_t)s->S * hkv * e, "v_full"};
-  const Range all[] = {rx, ry, rws, rk, rv};
-  for (int i = 0; i < 5; ++i)
-    for (int j = i + 1; j < 5; ++j)
+  const Range ro{o_save, save ? (size_t)N * h * 4 : 0, "o_save"};
+  const Range rl{lse_save, save ? (size_t)s->H * N * 4 : 0, "lse_save"};
+  const Range all[] = {rx, ry, rws, rk, rv, ro, rl};
+  const int n_ranges = save ? 7 : 5;
+  for (int i = 0; i < n_ranges; ++i)
+    for (int j = i + 1; j < n_ranges; ++j)
       if (overlap(all[i], all[j])) return fail(TSP_ERR_INVALID_ARG, "%s overlaps %s", all[i].name, all[j].name);
 
   unsigned char *ws = static_cast<unsigned char *>(ws_);
@@ -783,10 +794,19 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
     }
   }
   if (phases & TSP_PHASE_REST) {
-    TSP_LAUNCH(TSP_K_ATTN,
-               tsp::launch_attention(s->dtype, qbuf, k_full, v_full, x2, s->dtype, pnl, s->S, N, s->H, Hkv, s->Dh,
-                                     s->scale, zz, pnl, stream),
-               "attention");
+    if (save) {  // the same attention, fp32 O and the row statistics kept; O to bf16 panels
+      TSP_LAUNCH(TSP_K_ATTN,
+                 tsp::launch_attention(s->dtype, qbuf, k_full, v_full, o_save, TSP_F32, false, s->S, N, s->H, Hkv,
+                                       s->Dh, s->scale, zz, true, stream, lse_save),
+                 "attention");
+      TSP_LAUNCH(TSP_K_ROWS_BWD, tsp::launch_pack_cols(s->dtype, o_save, nullptr, nullptr, N, 1, h, 0, x2, true, stream),
+                 "o conversion");
+    } else {
+      TSP_LAUNCH(TSP_K_ATTN,
+                 tsp::launch_attention(s->dtype, qbuf, k_full, v_full, x2, s->dtype, pnl, s->S, N, s->H, Hkv, s->Dh,
+                                       s->scale, zz, pnl, stream),
+                 "attention");
+    }
     TSP_LAUNCH(TSP_K_OUTPROJ,
                tsp::launch_outproj(s->dtype, x2, pnl, N, h, to_list(w->wo, D), D, hd, x, y, stream),
                "output projection");
@@ -833,13 +853,34 @@ tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const f
   }
   return ok();
 }
+tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const float *x, void *k_full,
+                         void *v_full, float *y, unsigned phases, void *ws, size_t ws_bytes, void *stream) {
+  return layer_fwd(s, w, x, k_full, v_full, y, nullptr, nullptr, phases, ws, ws_bytes, stream);
+}
 
-tsp_status tsp_layer_bwd(const tsp_shape *s, const tsp_layer_weights *w, const float *x, const void *k_full,
-                         const void *v_full, const float *dy, float *dk_full, float *dv_full, const float *dk_loc,
-                         const float *dv_loc, float *dx, const tsp_layer_grads *gr, unsigned phases, void *ws_,
-                         size_t ws_bytes, void *stream_) {
+tsp_status tsp_layer_fwd_save(const tsp_shape *s, const tsp_layer_weights *w, const float *x, void *k_full,
+                              void *v_full, float *y, float *o_save, float *lse_save, unsigned phases, void *ws,
+                              size_t ws_bytes, void *stream) {
+  if (!o_save) return fail(TSP_ERR_INVALID_ARG, "o_save is NULL");
+  if (!lse_save) return fail(TSP_ERR_INVALID_ARG, "lse_save is NULL");
+  return layer_fwd(s, w, x, k_full, v_full, y, o_save, lse_save, phases, ws, ws_bytes, stream);
+}
+
+
+// The layer backward; with o_saved and lse_saved (bf16, from
+// tsp_layer_fwd_save), the attention forward is not run again: Q is
+// recomputed pre-scaled, as the forward had it, and the attention backward
+// takes the saved output and statistics.
+static tsp_status layer_bwd(const tsp_shape *s, const tsp_layer_weights *w, const float *x, const void *k_full,
+                            const void *v_full, const float *dy, const float *o_saved, const float *lse_saved,
+                            float *dk_full, float *dv_full, const float *dk_loc, const float *dv_loc, float *dx,
+                            const tsp_layer_grads *gr, unsigned phases, void *ws_, size_t ws_bytes, void *stream_) {
   tsp_status st = check_layer_bwd_shape(s);
   if (st) return st;
+  const bool saved = o_saved != nullptr || lse_saved != nullptr;
+  if (saved && (!o_saved || !lse_saved)) return fail(TSP_ERR_INVALID_ARG, "o_saved and lse_saved must both be given");
+  if (saved && s->dtype != TSP_BF16) return fail(TSP_ERR_UNSUPPORTED, "the saved attention output needs bf16");
+  if (saved && ((st = check_ptr(o_saved, "o_saved")) || (st = check_ptr(lse_saved, "lse_saved")))) return st;
   if (!w) return fail(TSP_ERR_INVALID_ARG, "weights is NULL");
   if (!gr) return fail(TSP_ERR_INVALID_ARG, "grads is NULL");
   if (phases == 0 || (phases & ~3u)) return fail(TSP_ERR_INVALID_ARG, "phases=%u must be 1, 2 or 3", phases);
@@ -880,6 +921,10 @@ tsp_status tsp_layer_bwd(const tsp_shape *s, const tsp_layer_weights *w, const f
     in.push_back({v_full, kvf * e, "v_full"});
     in.push_back({dy, nh4, "dy"});
     in.push_back({w->g_mlp, (size_t)h * e, "g_mlp"});
+    if (saved) {
+      in.push_back({o_saved, nh4, "o_saved"});
+      in.push_back({lse_saved, (size_t)s->H * N * 4, "lse_saved"});
+    }
     out.push_back({dk_full, kvf * 4, "dk_full"});
     out.push_back({dv_full, kvf * 4, "dv_full"});
     out.push_back({gr->g_mlp, (size_t)h * 4, "grads->g_mlp"});
@@ -927,18 +972,23 @@ tsp_status tsp_layer_bwd(const tsp_shape *s, const tsp_layer_weights *w, const f
     float *o = (float *)(ws + L.o), *h1 = (float *)(ws + L.h1), *dhn = (float *)(ws + L.dhn);
     float *lse = (float *)(ws + L.lse), *part = (float *)(ws + L.part);
     float *stat_lse = (float *)(ws + L.stat), *stat_delta = (float *)(ws + L.stat + attn_bwd_ws(s) / 2);
-    // the rank's forward again: xn, Q (no pre-scaling), o with its row
-    // statistics, h1, hn
+    // the rank's forward again: xn, Q, o with its row statistics (or the
+    // saved ones), h1, hn. With the saved statistics Q is recomputed with
+    // the forward's pre-scaling, which gives the forward's Q bit for bit
+    // (same products, same epilogue), so the saved statistics match it.
+    const float q_scale = saved ? s->scale * 1.4426950408889634f : 1.0f;
     TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(x, w->g_attn, xn, N, h, s->eps, dt, pnl, stream), "RMSNorm");
     TSP_LAUNCH(TSP_K_QKV,
-               tsp::launch_qkv(dt, xn, pnl, N, h, to_list(w->wqkv, D), D, hq, 0, q, nullptr, nullptr, zz, 1.0f,
+               tsp::launch_qkv(dt, xn, pnl, N, h, to_list(w->wqkv, D), D, hq, 0, q, nullptr, nullptr, zz, q_scale,
                                nullptr, s->Dh, stream),
                "Q");
-    TSP_LAUNCH(TSP_K_ATTN,
-               tsp::launch_attention(dt, q, k_full, v_full, o, TSP_F32, false, s->S, N, s->H, Hkv, s->Dh, s->scale, zz,
-                                     false, stream, pnl ? lse : nullptr),
-               "attention");
-    TSP_LAUNCH(TSP_K_ROWS_BWD, tsp::launch_pack_cols(dt, o, nullptr, nullptr, N, 1, h, 0, olo, pnl, stream),
+    const float *o_in = saved ? o_saved : o, *lse_in = saved ? lse_saved : lse;
+    if (!saved)
+      TSP_LAUNCH(TSP_K_ATTN,
+                 tsp::launch_attention(dt, q, k_full, v_full, o, TSP_F32, false, s->S, N, s->H, Hkv, s->Dh, s->scale,
+                                       zz, false, stream, pnl ? lse : nullptr),
+                 "attention");
+    TSP_LAUNCH(TSP_K_ROWS_BWD, tsp::launch_pack_cols(dt, o_in, nullptr, nullptr, N, 1, h, 0, olo, pnl, stream),
                "o conversion");
     TSP_LAUNCH(TSP_K_OUTPROJ, tsp::launch_outproj(dt, olo, pnl, N, h, to_list(w->wo, D), D, hd, x, h1, stream),
                "output projection");
@@ -974,8 +1024,8 @@ tsp_status tsp_layer_bwd(const tsp_shape *s, const tsp_layer_weights *w, const f
     // every key/value row's gradient
     TSP_LAUNCH(TSP_K_ATTN_BWD,
                tsp::launch_attention_bwd(dt, q, k_full, v_full, dout, dq, dk_full, dv_full, stat_lse, stat_delta, s->S,
-                                         N, s->H, Hkv, s->Dh, s->scale, zz, stream, pnl ? o : nullptr,
-                                         pnl ? lse : nullptr, false),
+                                         N, s->H, Hkv, s->Dh, s->scale, zz, stream, pnl ? o_in : nullptr,
+                                         pnl ? lse_in : nullptr, false, saved),
                "attention backward");
   }
   if (pq) {
@@ -1006,6 +1056,22 @@ tsp_status tsp_layer_bwd(const tsp_shape *s, const tsp_layer_weights *w, const f
                "RMSNorm backward");
   }
   return ok();
+}
+
+tsp_status tsp_layer_bwd(const tsp_shape *s, const tsp_layer_weights *w, const float *x, const void *k_full,
+                         const void *v_full, const float *dy, float *dk_full, float *dv_full, const float *dk_loc,
+                         const float *dv_loc, float *dx, const tsp_layer_grads *gr, unsigned phases, void *ws,
+                         size_t ws_bytes, void *stream) {
+  return layer_bwd(s, w, x, k_full, v_full, dy, nullptr, nullptr, dk_full, dv_full, dk_loc, dv_loc, dx, gr, phases, ws,
+                   ws_bytes, stream);
+}
+
+tsp_status tsp_layer_bwd_ex(const tsp_shape *s, const tsp_layer_weights *w, const float *x, const void *k_full,
+                            const void *v_full, const float *dy, const float *o_saved, const float *lse_saved,
+                            float *dk_full, float *dv_full, const float *dk_loc, const float *dv_loc, float *dx,
+                            const tsp_layer_grads *gr, unsigned phases, void *ws, size_t ws_bytes, void *stream) {
+  return layer_bwd(s, w, x, k_full, v_full, dy, o_saved, lse_saved, dk_full, dv_full, dk_loc, dv_loc, dx, gr, phases,
+                   ws, ws_bytes, stream);
 }
 
 void tsp_profile_enable(int on) { g_prof.on = on != 0; }

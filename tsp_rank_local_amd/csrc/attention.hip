@@ -533,8 +533,8 @@ hipError_t launch_attention(int dtype, const void *q, const void *k, const void 
   if (n <= 0) return hipSuccess;
   if (Hkv < 1 || H % Hkv != 0) return hipErrorInvalidValue;
   if (o_panel && (dtype != TSP_BF16 || o_dtype != TSP_BF16)) return hipErrorInvalidValue;
-  if (q_prescaled && (dtype != TSP_BF16 || o_dtype != TSP_BF16)) return hipErrorInvalidValue;
-  if (lse && (dtype != TSP_BF16 || o_dtype != TSP_F32 || q_prescaled)) return hipErrorInvalidValue;
+  if (q_prescaled && (dtype != TSP_BF16 || (o_dtype != TSP_BF16 && !lse))) return hipErrorInvalidValue;
+  if (lse && (dtype != TSP_BF16 || o_dtype != TSP_F32)) return hipErrorInvalidValue;
   AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -558,10 +558,17 @@ hipError_t launch_attention(int dtype, const void *q, const void *k, const void 
     dim3 grid(H * a.T);
     const bool f32out = o_dtype == TSP_F32;
     if (lse) {
-      if (Dh == 128)
-        hipLaunchKernelGGL((attn_bf16_kernel<128, true, false, true>), grid, dim3(kAttnThreads), 0, s, a);
-      else
-        hipLaunchKernelGGL((attn_bf16_kernel<64, true, false, true>), grid, dim3(kAttnThreads), 0, s, a);
+      if (Dh == 128) {
+        if (q_prescaled)
+          hipLaunchKernelGGL((attn_bf16_kernel<128, true, true, true>), grid, dim3(kAttnThreads), 0, s, a);
+        else
+          hipLaunchKernelGGL((attn_bf16_kernel<128, true, false, true>), grid, dim3(kAttnThreads), 0, s, a);
+      } else {
+        if (q_prescaled)
+          hipLaunchKernelGGL((attn_bf16_kernel<64, true, true, true>), grid, dim3(kAttnThreads), 0, s, a);
+        else
+          hipLaunchKernelGGL((attn_bf16_kernel<64, true, false, true>), grid, dim3(kAttnThreads), 0, s, a);
+      }
     } else if (Dh == 128) {
       if (f32out)
         hipLaunchKernelGGL((attn_bf16_kernel<128, true, false>), grid, dim3(kAttnThreads), 0, s, a);

@@ -55,7 +55,8 @@ struct BwdArgs {
   float *delta;  // [H][n]: sum over the row's keys of P dP
   int64_t S;
   int32_t n, H, Hkv, grp;
-  float scale, c;  // c = scale * log2(e) (at least the smallest normal float)
+  float scale, c;  // c = scale * log2(e) (at least the smallest normal float); 1 with pre-scaled q
+  float dk_scale;  // multiplier of dK: scale, or ln 2 with pre-scaled q (dK = ln 2 * dS^T q')
   ZigzagMap zz;
   int32_t Tq;  // 128-row query tiles per chunk (dQ kernel)
   int32_t Tk;  // 128-key tiles over the sequence (dK/dV kernel)
@@ -813,8 +814,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
       for (int vq = 0; vq < 4; ++vq) {
         *reinterpret_cast<float4 *>(dk + db * 32 + vq * 8) =
-            make_float4(kacc[db][vq * 4] * a.scale, kacc[db][vq * 4 + 1] * a.scale, kacc[db][vq * 4 + 2] * a.scale,
-                        kacc[db][vq * 4 + 3] * a.scale);
+            make_float4(kacc[db][vq * 4] * a.dk_scale, kacc[db][vq * 4 + 1] * a.dk_scale,
+                        kacc[db][vq * 4 + 2] * a.dk_scale, kacc[db][vq * 4 + 3] * a.dk_scale);
         *reinterpret_cast<float4 *>(dv + db * 32 + vq * 8) =
             make_float4(vacc[db][vq * 4], vacc[db][vq * 4 + 1], vacc[db][vq * 4 + 2], vacc[db][vq * 4 + 3]);
       }
@@ -912,11 +913,12 @@ __global__ __launch_bounds__(64) void attn_bwd_dkv_f32_kernel(BwdArgs a) {
 hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout, float *dq,
                                 float *dk, float *dv, float *lse, float *delta, int64_t S, int32_t n, int32_t H,
                                 int32_t Hkv, int32_t Dh, float scale, ZigzagMap zz, hipStream_t s,
-                                const float *o_f32, const float *lse_in, bool split) {
+                                const float *o_f32, const float *lse_in, bool split, bool q_prescaled) {
   if (n <= 0) return hipSuccess;
   if (Hkv < 1 || H % Hkv != 0 || (Dh != 64 && Dh != 128)) return hipErrorInvalidValue;
   const bool given = o_f32 != nullptr && lse_in != nullptr;
   if (given && dtype != TSP_BF16) return hipErrorInvalidValue;
+  if (q_prescaled && !given) return hipErrorInvalidValue;
   BwdArgs a{};
   a.q = q;
   a.k = k;
@@ -938,6 +940,11 @@ hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const v
   // multiplier of the scores in the exp2 domain, kept at least the smallest
   // normal float so that masked scores (-inf) stay -inf with a zero scale
   a.c = fmaxf(scale * 1.4426950408889634f, 1.17549435e-38f);
+  a.dk_scale = scale;
+  if (q_prescaled) {  // the scores come out of the products in the log2 domain
+    a.c = 1.0f;
+    a.dk_scale = 0.69314718055994531f;
+  }
   a.zz = zz;
   a.Tq = (zz.C + 127) / 128;
   a.Tk = (int32_t)((S + 127) / 128);

@@ -168,8 +168,9 @@ hipError_t launch_lead_mlp_down(const float *hid, int32_t m, const PtrList &w2, 
 // panel layout of [n][H*Dh] when o_panel. q_prescaled (bf16 q and o only): q
 // already holds q * scale * log2(e), as launch_qkv writes it with that
 // q_scale.
-// lse (bf16 inputs, fp32 o, plain q only; else null): also write each row's
-// natural log-sum-exp of its scaled scores, [H][n] fp32.
+// lse (bf16 inputs, fp32 o; else null): also write each row's natural
+// log-sum-exp of its scaled scores, [H][n] fp32 (with q_prescaled as well:
+// the training forward of the layer).
 hipError_t launch_attention(int dtype, const void *q, const void *k, const void *v, void *o, int o_dtype,
                             bool o_panel, int64_t S, int32_t n, int32_t H, int32_t Hkv, int32_t Dh, float scale,
                             ZigzagMap zz, bool q_prescaled, hipStream_t s, float *lse = nullptr);
@@ -189,10 +190,14 @@ hipError_t launch_lead_attention(const float *q, const float *k, const float *v,
 // dout * o and the statistics walk of the dQ kernel is skipped.
 // split (bf16): P and dS enter their products as a bf16 pair hi + lo;
 // otherwise rounded once to bf16.
+// q_prescaled (with o_f32 and lse_in only): q holds q * scale * log2(e) as
+// the layer's QKV epilogue writes it (and lse_in came from the forward on
+// that q); dq is still the gradient of the unscaled q.
 hipError_t launch_attention_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout, float *dq,
                                 float *dk, float *dv, float *lse, float *delta, int64_t S, int32_t n, int32_t H,
                                 int32_t Hkv, int32_t Dh, float scale, ZigzagMap zz, hipStream_t s,
-                                const float *o_f32 = nullptr, const float *lse_in = nullptr, bool split = true);
+                                const float *o_f32 = nullptr, const float *lse_in = nullptr, bool split = true,
+                                bool q_prescaled = false);
 
 // ---------------------------------------------------------------- static scratch
 // Size of the device array that tsp_zigzag_attn_bwd_noalloc uses in place of
