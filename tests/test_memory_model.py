@@ -92,6 +92,11 @@ def test_training_terms():
     kvw = 2 * m.kv_heads * m.Dh
     assert trn["backward_peak"] == ((m.S + m.N) * kvw * 4 + _lib_ws(m, tsp.TSP_WS_LAYER_BWD) + 2 * m.N * m.h * 4
                                     + W * 4 * 7 // 8)
+    # the training path that keeps each layer's attention output and
+    # statistics (the buffers tsp_layer_fwd_save fills): fp32 O and lse
+    sv = mm.rank_memory(m, train=True, save_attention=True)
+    assert sv["saved_attention"] == 32 * (m.N * 4096 + 32 * m.N) * 4
+    assert sv["total"] == trn["total"] + sv["saved_attention"]
 
 
 def test_single_gpu_bytes():

@@ -169,7 +169,7 @@ def layer_weight_elems(m: Model) -> int:
 
 
 # --------------------------------------------------------------- rank budget
-def rank_memory(m: Model, train: bool = False) -> dict:
+def rank_memory(m: Model, train: bool = False, save_attention: bool = False) -> dict:
     """Bytes on one rank's device at the peak of a forward over all layers
     (the layer being computed holds the transients), by component:
 
@@ -194,7 +194,10 @@ def rank_memory(m: Model, train: bool = False) -> dict:
     before the reduce-scatter that returns each row to its owner) and the
     summed rows the rank gets back, the layer backward's workspace
     (WS_LAYER_BWD), the fp32 output gradient and input gradient [N][h], and
-    the fp32 weight gradients of the received shards."""
+    the fp32 weight gradients of the received shards. save_attention (with
+    train) adds each layer's kept attention output and row statistics, fp32
+    [N][H][Dh] and [H][N], that tsp_layer_fwd_save writes so that
+    tsp_layer_bwd_ex does not run the attention forward again."""
     e = _elem(m.dtype)
     W = layer_weight_elems(m)
     kvw = 2 * m.kv_heads * m.Dh  # K and V elements per token
@@ -210,6 +213,8 @@ def rank_memory(m: Model, train: bool = False) -> dict:
         out["grads_owned"] = m.layers * W * 4 // m.D
         out["optimizer_owned"] = m.layers * W * 12 // m.D
         out["saved_layer_inputs"] = m.layers * m.N * m.h * 4
+        if save_attention:
+            out["saved_attention"] = m.layers * (m.N * m.H * m.Dh + m.H * m.N) * 4
         out["backward_peak"] = ((m.S + m.N) * kvw * 4 + workspace_bytes(m, WS_LAYER_BWD) + 2 * m.N * m.h * 4
                                 + (W * 4 - W * 4 // m.D))
     out["total"] = sum(out.values())
