@@ -853,6 +853,7 @@ static tsp_status layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, cons
   }
   return ok();
 }
+
 tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const float *x, void *k_full,
                          void *v_full, float *y, unsigned phases, void *ws, size_t ws_bytes, void *stream) {
   return layer_fwd(s, w, x, k_full, v_full, y, nullptr, nullptr, phases, ws, ws_bytes, stream);
@@ -865,7 +866,6 @@ tsp_status tsp_layer_fwd_save(const tsp_shape *s, const tsp_layer_weights *w, co
   if (!lse_save) return fail(TSP_ERR_INVALID_ARG, "lse_save is NULL");
   return layer_fwd(s, w, x, k_full, v_full, y, o_save, lse_save, phases, ws, ws_bytes, stream);
 }
-
 
 // The layer backward; with o_saved and lse_saved (bf16, from
 // tsp_layer_fwd_save), the attention forward is not run again: Q is
@@ -975,7 +975,8 @@ static tsp_status layer_bwd(const tsp_shape *s, const tsp_layer_weights *w, cons
     // the rank's forward again: xn, Q, o with its row statistics (or the
     // saved ones), h1, hn. With the saved statistics Q is recomputed with
     // the forward's pre-scaling, which gives the forward's Q bit for bit
-    // (same products, same epilogue), so the saved statistics match it.
+    // (the same inputs, the same reduction order for every element, the
+    // same epilogue), so the saved statistics belong to it.
     const float q_scale = saved ? s->scale * 1.4426950408889634f : 1.0f;
     TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(x, w->g_attn, xn, N, h, s->eps, dt, pnl, stream), "RMSNorm");
     TSP_LAUNCH(TSP_K_QKV,
