@@ -65,13 +65,12 @@ struct BwdArgs {
 typedef short s16x4_b __attribute__((ext_vector_type(4)));
 
 // Geometry of an R x DH bf16 tile in LDS: row-major, 16-byte chunks XOR-
-// swizzled by row. ROW layout: for ds_read_b128 row fragments and, read
-// transposed, for the 4 x 4 transpose reads; both free of bank conflicts:
-// the 16 rows of a row read get 16 (DH 128) or 8 pairs of (DH 64) distinct
-// chunk positions, and the four rows 4k..4k+3 of a transpose read, which take
-// 2 or 4 neighbouring chunks each, get disjoint ones. The swizzle depends on
-// the row modulo 16 only. TR layout: for the transpose reads only (the dQ
-// kernel's second copy of K).
+// swizzled by row, for ds_read_b128 row fragments and, read transposed, for
+// the 4 x 4 transpose reads; both free of bank conflicts: the 16 rows of a
+// row read get 16 (DH 128) or 8 pairs of (DH 64) distinct chunk positions,
+// and the four rows 4k..4k+3 of a transpose read, which take 2 or 4
+// neighbouring chunks each, get disjoint ones. The swizzle depends on the
+// row modulo 16 only.
 template <int DH>
 struct BTile {
   static constexpr int ROWB = DH * 2;
@@ -79,9 +78,6 @@ struct BTile {
   static __device__ __forceinline__ int row_swz(int row, int ch) {
     return ch ^ (CPR == 16 ? (((row & 3) << 2) | ((row >> 2) & 3))
                            : (((row >> 1) & 3) | ((((row >> 1) ^ (row >> 3)) & 1) << 2)));
-  }
-  static __device__ __forceinline__ int tr_swz(int row, int ch) {
-    return ch ^ (CPR == 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1));
   }
 };
 
@@ -108,29 +104,27 @@ __device__ __forceinline__ void load_tile_buf(TileRegs<DH, R> &t, const bf16 *sr
     t.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, row * pitch * 2 + ch * 16, 0, 0));
   }
 }
-template <int DH, int R, bool TR>
+template <int DH, int R>
 __device__ __forceinline__ void store_tile(unsigned char *dst, const TileRegs<DH, R> &t) {
   using G = BTile<DH>;
 #pragma unroll
   for (int i = 0; i < TileRegs<DH, R>::N; ++i) {
     const int c = threadIdx.x + 256 * i;
     const int row = c / G::CPR, ch = c % G::CPR;
-    const int pos = TR ? G::tr_swz(row, ch) : G::row_swz(row, ch);
-    *reinterpret_cast<u32x4 *>(dst + row * G::ROWB + pos * 16) = t.v[i];
+    *reinterpret_cast<u32x4 *>(dst + row * G::ROWB + G::row_swz(row, ch) * 16) = t.v[i];
   }
 }
 
 // Lane-constant LDS byte offsets of the fragment reads of a tile, computed
-// once per kernel. row[kk]: the ROW-layout chunk of row lane%32, logical
-// chunk 2*kk + lane/32; rows 32.. are 32*ROWB further (same swizzle, which
-// depends on the row modulo 16). tr[db]: the
-// transpose read for feature block db, row group 0, half 0; row group mu and
-// half hv are (16*mu + 8*hv)*ROWB further (the TR swizzle depends on the row
-// modulo 4 only).
+// once per kernel. row[kk]: the chunk of row lane%32, logical chunk 2*kk +
+// lane/32; rows 32.. are 32*ROWB further (same swizzle, which depends on the
+// row modulo 16). tr[db][hv]: the transpose read that gives lane l feature
+// 32*db + l%32's rows 8*hv + 4*(l/32) + {0..3}; rows 16*s.. of a step s of 16
+// rows are 16*s*ROWB further (the swizzle again repeats every 16 rows).
 template <int DH>
 struct FragOff {
   int row[DH / 16];
-  int tr[DH / 32];
+  int tr[DH / 32][2];
 };
 template <int DH>
 __device__ __forceinline__ FragOff<DH> frag_off(int lane) {
@@ -140,11 +134,13 @@ __device__ __forceinline__ FragOff<DH> frag_off(int lane) {
 #pragma unroll
   for (int kk = 0; kk < DH / 16; ++kk) f.row[kk] = l32 * G::ROWB + G::row_swz(l32, 2 * kk + g) * 16;
 #pragma unroll
-  for (int db = 0; db < DH / 32; ++db) {
-    const int row = g * 4 + (r16 >> 2);
-    const int dstart = db * 32 + dsub * 16 + 4 * (r16 & 3);
-    f.tr[db] = row * G::ROWB + G::tr_swz(row, dstart >> 3) * 16 + (dstart & 7) * 2;
-  }
+  for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv) {
+      const int row = 8 * hv + g * 4 + (r16 >> 2);
+      const int dstart = db * 32 + dsub * 16 + 4 * (r16 & 3);
+      f.tr[db][hv] = row * G::ROWB + G::row_swz(row, dstart >> 3) * 16 + (dstart & 7) * 2;
+    }
   return f;
 }
 
@@ -153,17 +149,17 @@ __device__ __forceinline__ bf16x8 row_frag(const unsigned char *t, int off) {
   return *reinterpret_cast<const bf16x8 *>(t + off);
 }
 
-// Transpose fragment (TR layout) at precomputed offset off (row group and
-// half included): lane l receives, for feature 32*db + l%32, rows 16*mu +
-// 4*(l/32) + {0..3} and 16*mu + 8 + 4*(l/32) + {0..3}: the A operand whose k
-// index runs over those rows in the order of the score registers.
+// Transpose fragment of a row-layout tile: lane l receives, for feature
+// 32*db + l%32, rows 16*st + 4*(l/32) + {0..3} and 16*st + 8 + 4*(l/32) +
+// {0..3}: the A operand whose k index runs over those rows in the order of
+// the score registers.
 template <int DH>
-__device__ __forceinline__ bf16x8 tr_frag(const unsigned char *t, int off) {
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char *t, const FragOff<DH> &fo, int db, int st) {
   s16x4_b part[2];
 #pragma unroll
   for (int hv = 0; hv < 2; ++hv)
     part[hv] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4_b *)(t + off + hv * 8 * BTile<DH>::ROWB));
+        (__attribute__((address_space(3))) s16x4_b *)(t + fo.tr[db][hv] + st * 16 * BTile<DH>::ROWB));
   const s16x8_t both = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
   return __builtin_bit_cast(bf16x8, both);
 }
@@ -217,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   using G = BTile<DH>;
   constexpr int ND = DH / 32, NK = DH / 16;
   constexpr int TB = kBwdKey * G::ROWB;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[3][TB];  // K (ROW), K (TR), V (ROW)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][TB];  // K, V (row layout)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const FragOff<DH> fo = frag_off<DH>(lane);
@@ -288,8 +284,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     for (int kt = 0; kt < n_kt; ++kt) {
       const int k0 = kt * kBwdKey;
       __syncthreads();
-      store_tile<DH, kBwdKey, false>(smem[0], kr);
-      store_tile<DH, kBwdKey, false>(smem[2], vr);
+      store_tile<DH, kBwdKey>(smem[0], kr);
+      store_tile<DH, kBwdKey>(smem[1], vr);
       __syncthreads();
       if (kt + 1 < n_kt) {  // next tile on its way during this one's math
         load_tile_buf<DH, kBwdKey>(kr, kg + (int64_t)(k0 + kBwdKey) * kvs, (int)kvs,
@@ -300,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
       if (!active) continue;
       f32x16 sacc[2], pacc[2];
       scores(smem[0], qf, sacc);
-      scores(smem[2], df, pacc);
+      scores(smem[1], df, pacc);
       mask(sacc, k0);
       float mx = -INFINITY;
 #pragma unroll
@@ -344,9 +340,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   for (int kt = 0; kt < n_kt; ++kt) {
     const int k0 = kt * kBwdKey;
     __syncthreads();
-    store_tile<DH, kBwdKey, false>(smem[0], kr);
-    store_tile<DH, kBwdKey, true>(smem[1], kr);
-    store_tile<DH, kBwdKey, false>(smem[2], vr);
+    store_tile<DH, kBwdKey>(smem[0], kr);
+    store_tile<DH, kBwdKey>(smem[1], vr);
     __syncthreads();
     if (kt + 1 < n_kt) {
       load_tile_buf<DH, kBwdKey>(kr, kg + (int64_t)(k0 + kBwdKey) * kvs, (int)kvs,
@@ -357,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     if (!active) continue;
     f32x16 sacc[2], pacc[2];
     scores(smem[0], qf, sacc);
-    scores(smem[2], df, pacc);  // dP^T = V dO^T
+    scores(smem[1], df, pacc);  // dP^T = V dO^T
     mask(sacc, k0);
     bf16x8 ds[4], dsl[4];
 #pragma unroll
@@ -374,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
-        const bf16x8 kt_frag = tr_frag<DH>(smem[1], fo.tr[db] + kq * 16 * G::ROWB);
+        const bf16x8 kt_frag = tr_frag<DH>(smem[0], fo, db, kq);
         qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_frag, ds[kq], qacc[db], 0, 0, 0);
         if constexpr (SPLIT) qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_frag, dsl[kq], qacc[db], 0, 0, 0);
       }
@@ -446,32 +441,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_lds_kernel(BwdArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, TSP_LDS_PTR(&smem[st][1][win * 1024]), 16, c_off[i], 0, 0, 0);
     }
   };
-  // transposed reads of the row-layout K tile: lane l gets feature 32*db +
-  // l%32's keys 16*kq + 8*hv + 4*(l/32) + {0..3} of half hv. The row swizzle
-  // depends on the row modulo 16, which a step of 16 keys keeps, so each
-  // (db, hv) has one lane-constant offset.
-  int trr[ND][2];
-  {
-    const int r16 = lane & 15, dsub = (lane >> 4) & 1;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int hv = 0; hv < 2; ++hv) {
-        const int row = 8 * hv + g * 4 + (r16 >> 2);
-        const int dstart = db * 32 + dsub * 16 + 4 * (r16 & 3);
-        trr[db][hv] = row * G::ROWB + G::row_swz(row, dstart >> 3) * 16 + (dstart & 7) * 2;
-      }
-  }
-  auto kt_frag = [&](const unsigned char *t, int db, int kq) {
-    s16x4_b part[2];
-#pragma unroll
-    for (int hv = 0; hv < 2; ++hv)
-      part[hv] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4_b *)(t + trr[db][hv] + kq * 16 * G::ROWB));
-    const s16x8_t both = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
-    return __builtin_bit_cast(bf16x8, both);
-  };
-
   for (int half = 0; half < 2; ++half) {
     const int ch_half = half == 0 ? 1 : 0;
     const int tile = half == 0 ? a.Tq - 1 - p : p;
@@ -554,7 +523,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_lds_kernel(BwdArgs a) {
       for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-          const bf16x8 kt_f = kt_frag(Ks, db, kq);
+          const bf16x8 kt_f = tr_frag<DH>(Ks, fo, db, kq);
           qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_f, ds[kq], qacc[db], 0, 0, 0);
           if constexpr (SPLIT) qacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_f, dsl[kq], qacc[db], 0, 0, 0);
         }
@@ -625,30 +594,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       }
     }
   }
-  // transposed reads of the row-layout tiles: lane l gets feature 32*db +
-  // l%32's rows 16*mu + 8*hv + 4*(l/32) + {0..3} of half hv (the row swizzle
-  // depends on the row modulo 16, which a step of 16 rows keeps)
-  int trr[ND][2];
-  {
-    const int r16 = lane & 15, dsub = (lane >> 4) & 1;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int hv = 0; hv < 2; ++hv) {
-        const int row = 8 * hv + g * 4 + (r16 >> 2);
-        const int dstart = db * 32 + dsub * 16 + 4 * (r16 & 3);
-        trr[db][hv] = row * G::ROWB + G::row_swz(row, dstart >> 3) * 16 + (dstart & 7) * 2;
-      }
-  }
-  auto trr_frag = [&](const unsigned char *t, int db, int mu) {
-    s16x4_b part[2];
-#pragma unroll
-    for (int hv = 0; hv < 2; ++hv)
-      part[hv] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4_b *)(t + trr[db][hv] + mu * 16 * G::ROWB));
-    const s16x8_t both = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
-    return __builtin_bit_cast(bf16x8, both);
-  };
   f32x16 kacc[ND], vacc[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db)
@@ -705,7 +650,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
     for (int mu = 0; mu < 2; ++mu)
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
-        const bf16x8 dot = trr_frag(smem[b][1], db, mu), qt = trr_frag(smem[b][0], db, mu);
+        const bf16x8 dot = tr_frag<DH>(smem[b][1], fo, db, mu), qt = tr_frag<DH>(smem[b][0], fo, db, mu);
         vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, ph[mu], vacc[db], 0, 0, 0);
         kacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dh[mu], kacc[db], 0, 0, 0);
         if constexpr (SPLIT) {
@@ -738,8 +683,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
         st_dlt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dr_, (int)threadIdx.x * 4, 0, 0));
       };
       auto stage = [&](int b, int t0) {  // the fetched rows into buffer b
-        store_tile<DH, kBwdQ, false>(smem[b][0], qr);
-        store_tile<DH, kBwdQ, false>(smem[b][1], dr);
+        store_tile<DH, kBwdQ>(smem[b][0], qr);
+        store_tile<DH, kBwdQ>(smem[b][1], dr);
         if (threadIdx.x < kBwdQ) {
           const int t = t0 + threadIdx.x;
           const bool ok = t < t_end;
