@@ -528,8 +528,9 @@ def main():
                     f"recomputed from x; dx, dK/dV of every key row and all weight and gain gradients in fp32)")
     elif args.workload == "train":
         # one training step of the layer on one rank: the forward that keeps
-        # the attention output and statistics, then both halves of the
-        # backward that take them (no second attention forward); the summed
+        # the attention output and statistics and the MLP pre-activation, then
+        # both halves of the backward that take them (no second attention
+        # forward, no second MLP up product); the summed
         # K/V-row gradients of the second half are seeded values as above
         x = synth.activations(N, sh.h, seed=seed)
         dy = synth.activations(N, sh.h, seed=seed, tid=synth.TID_DY)
@@ -542,6 +543,7 @@ def main():
         y = torch.empty((N, sh.h), dtype=torch.float32, device="cuda")
         o_sv = torch.empty((N, sh.H, sh.Dh), dtype=torch.float32, device="cuda")
         lse_sv = torch.empty((sh.H, N), dtype=torch.float32, device="cuda")
+        z_sv = torch.empty((N, sh.F), dtype=torch.bfloat16, device="cuda")
         dkf = torch.empty((sh.S, sh.kv_heads, sh.Dh), dtype=torch.float32, device="cuda")
         dvf = torch.empty_like(dkf)
         dx = torch.empty((N, sh.h), dtype=torch.float32, device="cuda")
@@ -553,9 +555,9 @@ def main():
         ws = torch.empty(tsp.workspace_size(shape, tsp.TSP_WS_LAYER_BWD), dtype=torch.uint8, device="cuda")
 
         def step():
-            tsp.tsp_layer_fwd_save(shape, wd, xd, kf, vf, y, o_sv, lse_sv, tsp.TSP_PHASE_ALL, ws_f)
+            tsp.tsp_layer_fwd_save(shape, wd, xd, kf, vf, y, o_sv, lse_sv, tsp.TSP_PHASE_ALL, ws_f, z_save=z_sv)
             tsp.tsp_layer_bwd_ex(shape, wd, xd, kf, vf, dyd, o_sv, lse_sv, dkf, dvf, None, None, None, grads,
-                                 tsp.TSP_BWD_ATTN, ws)
+                                 tsp.TSP_BWD_ATTN, ws, z_saved=z_sv)
             tsp.tsp_layer_bwd_ex(shape, wd, xd, None, None, None, None, None, None, None, dkld, dvld, dx, grads,
                                  tsp.TSP_BWD_QKV, ws)
         # algorithmic: the forward's flops and the backward's chain-rule products
@@ -563,8 +565,8 @@ def main():
         step_exps = 3 * sh.H * attn_pairs(sh.S, sh.D, r)
         workload = (f"tsp_layer_fwd_save + tsp_layer_bwd_ex: one training step of one 7B dense decoder layer (h=4096, "
                     f"32x128 heads{kv_note}, FFN 16384, bf16) on rank {r} of D=8 at S=131072, 16384 local zigzag "
-                    f"tokens: the forward keeping the attention output and statistics, both halves of the backward "
-                    f"from them")
+                    f"tokens: the forward keeping the attention output and statistics and the MLP pre-activation, "
+                    f"both halves of the backward from them")
     elif args.workload == "mlp":
         x = synth.activations(N, sh.h, seed=2, dtype="bf16")
         xd = tsp.to_device(x, "bf16")

@@ -398,10 +398,14 @@ tsp_status tsp_layer_fwd(const tsp_shape *shape, const tsp_layer_weights *w, con
  *    recomputed in fp32 as above, their O is not).
  *  lse_save: [H][S/D] fp32, each row's natural log-sum-exp of its scaled
  *    scores (over its visible keys), written by PHASE_REST.
- * Both must be given and must not overlap any other argument. */
+ *  z_save: optional (NULL: not kept), [S/D][F] bf16, the MLP pre-activation
+ *    Z of every ring step (as tsp_mlp_ring_z writes it), written by
+ *    PHASE_REST; GELU MLP only (else TSP_ERR_UNSUPPORTED).
+ * o_save and lse_save must both be given; none may overlap any other
+ * argument. */
 tsp_status tsp_layer_fwd_save(const tsp_shape *shape, const tsp_layer_weights *w, const float *x,
                               void *k_full, void *v_full, float *y, float *o_save, float *lse_save,
-                              unsigned phases, void *ws, size_t ws_bytes, void *stream);
+                              void *z_save, unsigned phases, void *ws, size_t ws_bytes, void *stream);
 
 /* Backward of tsp_layer_fwd on rank r (an optional extension, like
  * tsp_mlp_ring_bwd: the pages report training throughput, the ageofai.tools
@@ -461,13 +465,15 @@ tsp_status tsp_layer_bwd(const tsp_shape *shape, const tsp_layer_weights *w, con
  * recomputed with the forward's pre-scaling by scale * log2(e), which
  * reproduces the forward's Q bit for bit, so the saved statistics belong to
  * the scores the backward forms; dK is then ln 2 * dS^T Q' (Q' the
- * pre-scaled Q), the same gradient. They must come from the forward of the
- * same x, weights and K/V. */
+ * pre-scaled Q), the same gradient. z_saved (optional, with o_saved and
+ * lse_saved; tsp_layer_fwd_save's z_save): the MLP ring backward then takes
+ * Z as tsp_mlp_ring_bwd_z does instead of recomputing it. They must come from
+ * the forward of the same x, weights and K/V. */
 tsp_status tsp_layer_bwd_ex(const tsp_shape *shape, const tsp_layer_weights *w, const float *x,
                             const void *k_full, const void *v_full, const float *dy,
-                            const float *o_saved, const float *lse_saved, float *dk_full,
-                            float *dv_full, const float *dk_loc, const float *dv_loc, float *dx,
-                            const tsp_layer_grads *grads, unsigned phases, void *ws,
+                            const float *o_saved, const float *lse_saved, const void *z_saved,
+                            float *dk_full, float *dv_full, const float *dk_loc, const float *dv_loc,
+                            float *dx, const tsp_layer_grads *grads, unsigned phases, void *ws,
                             size_t ws_bytes, void *stream);
 
 /* Optional launch timing. When enabled, every kernel the library enqueues is

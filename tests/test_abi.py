@@ -389,7 +389,7 @@ def test_layer_fwd_save_errors():
     argument and needs bf16; nothing is enqueued on any error."""
     w = dict(g_attn=FAKE, g_mlp=FAKE, wqkv=[FAKE] * 4, wo=[FAKE] * 4, w1=[FAKE] * 4, w2=[FAKE] * 4)
     a = dict(x=FAKE + (1 << 32), k_full=FAKE + (2 << 32), v_full=FAKE + (3 << 32), y=FAKE + (4 << 32),
-             ws=FAKE + (5 << 32), o=FAKE + (6 << 32), lse=FAKE + (7 << 32))
+             ws=FAKE + (5 << 32), o=FAKE + (6 << 32), lse=FAKE + (7 << 32), z=None)
 
     def call(shape=None, **kw):
         s = shape or _shape(dtype="bf16")
@@ -397,7 +397,7 @@ def test_layer_fwd_save_errors():
         b.update(kw)
         with pytest.raises(tsp.TspError) as ei:
             tsp.tsp_layer_fwd_save(s, w, b["x"], b["k_full"], b["v_full"], b["y"], b["o"], b["lse"], 3, b["ws"],
-                                   tsp.workspace_size(s, tsp.TSP_WS_LAYER), stream=0)
+                                   tsp.workspace_size(s, tsp.TSP_WS_LAYER), stream=0, z_save=b["z"])
         return ei.value.status, tsp.lib().tsp_last_error()
 
     st, msg = call(o=None)
@@ -410,6 +410,12 @@ def test_layer_fwd_save_errors():
     st, msg = call(lse=a["ws"] + 4096)  # statistics inside the workspace
     assert st == tsp.TSP_ERR_INVALID_ARG and b"overlaps" in msg
     assert call(o=a["o"] + 8)[0] == tsp.TSP_ERR_INVALID_ARG  # misaligned
+    # the kept MLP pre-activation: GELU MLP only, checked like the rest
+    z = FAKE + (8 << 32)
+    assert call(shape=_shape(dtype="bf16", mlp="swiglu"), z=z)[0] == tsp.TSP_ERR_UNSUPPORTED
+    st, msg = call(z=a["y"] + 4096)  # Z over y
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"overlaps" in msg
+    assert call(z=z + 8)[0] == tsp.TSP_ERR_INVALID_ARG  # misaligned
 
 
 def test_layer_bwd_ex_errors():
@@ -425,7 +431,7 @@ def test_layer_bwd_ex_errors():
     grads = dict(g_attn=FAKE + (20 << 32), g_mlp=FAKE + (21 << 32), wqkv=gl(22), wo=gl(23), w1=gl(24), w2=gl(25))
     a = dict(x=FAKE + (1 << 32), k_full=FAKE + (2 << 32), v_full=FAKE + (3 << 32), dy=FAKE + (4 << 32),
              dk_full=FAKE + (5 << 32), dv_full=FAKE + (6 << 32), dk_loc=FAKE + (7 << 32), dv_loc=FAKE + (8 << 32),
-             dx=FAKE + (9 << 32), ws=FAKE + (10 << 32), o=FAKE + (11 << 32), lse=FAKE + (12 << 32))
+             dx=FAKE + (9 << 32), ws=FAKE + (10 << 32), o=FAKE + (11 << 32), lse=FAKE + (12 << 32), z=None)
 
     def call(shape=s, **kw):
         b = dict(a)
@@ -433,7 +439,7 @@ def test_layer_bwd_ex_errors():
         with pytest.raises(tsp.TspError) as ei:
             tsp.tsp_layer_bwd_ex(shape, w, b["x"], b["k_full"], b["v_full"], b["dy"], b["o"], b["lse"], b["dk_full"],
                                  b["dv_full"], b["dk_loc"], b["dv_loc"], b["dx"], grads, tsp.TSP_BWD_ATTN, b["ws"],
-                                 need if shape is s else 1 << 40, stream=0)
+                                 need if shape is s else 1 << 40, stream=0, z_saved=b["z"])
         return ei.value.status, tsp.lib().tsp_last_error()
 
     st, msg = call(lse=None)
@@ -446,6 +452,10 @@ def test_layer_bwd_ex_errors():
     st, msg = call(o=a["ws"])  # the saved O inside the workspace
     assert st == tsp.TSP_ERR_INVALID_ARG and b"overlaps" in msg
     assert call(lse=a["lse"] + 8)[0] == tsp.TSP_ERR_INVALID_ARG  # misaligned
+    st, msg = call(o=None, lse=None, z=FAKE + (13 << 32))  # Z alone
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"z_saved needs" in msg
+    st, msg = call(z=a["dk_full"])  # Z over an output
+    assert st == tsp.TSP_ERR_INVALID_ARG and b"overlaps" in msg
 
 
 def test_layer_bwd_workspace_and_errors():

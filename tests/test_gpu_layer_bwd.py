@@ -97,18 +97,20 @@ LAYER_BWD_CASES = [
 ]
 
 
-def _saved_forward(torch, s, wd, x, kd, vd):
+def _saved_forward(torch, s, wd, x, kd, vd, keep_z):
     """tsp_layer_fwd_save on the given K/V: PHASE_KV on scratch copies (the
     rank's own rows stay the given ones in kd, vd), then PHASE_REST on kd,
-    vd with the same workspace. Returns the kept O and log-sum-exp."""
+    vd with the same workspace. Returns the kept O, log-sum-exp and (keep_z)
+    MLP pre-activation."""
     N, H, Dh = s.S // s.D, s.H, s.Dh
     ws = torch.empty(tsp.workspace_size(s, tsp.TSP_WS_LAYER), dtype=torch.uint8, device="cuda")
     y = _nan(torch, N, s.h)
     o = _nan(torch, N, H, Dh)
     lse = _nan(torch, H, N)
-    tsp.tsp_layer_fwd_save(s, wd, x, kd.clone(), vd.clone(), y, o, lse, tsp.TSP_PHASE_KV, ws)
-    tsp.tsp_layer_fwd_save(s, wd, x, kd, vd, y, o, lse, tsp.TSP_PHASE_REST, ws)
-    return o, lse
+    z = torch.full((N, s.F), float("nan"), dtype=torch.bfloat16, device="cuda") if keep_z else None
+    tsp.tsp_layer_fwd_save(s, wd, x, kd.clone(), vd.clone(), y, o, lse, tsp.TSP_PHASE_KV, ws, z_save=z)
+    tsp.tsp_layer_fwd_save(s, wd, x, kd, vd, y, o, lse, tsp.TSP_PHASE_REST, ws, z_save=z)
+    return o, lse, z
 
 
 @pytest.mark.parametrize("S,D,h,H,Dh,F,Hkv,dtype", LAYER_BWD_CASES)
@@ -116,14 +118,17 @@ def test_layer_bwd_every_rank(torch, S, D, h, H, Dh, F, Hkv, dtype):
     _layer_bwd_every_rank(torch, S, D, h, H, Dh, F, Hkv, dtype, saved=False)
 
 
-@pytest.mark.parametrize("S,D,h,H,Dh,F,Hkv,dtype", [c for c in LAYER_BWD_CASES if c[-1] == "bf16"])
-def test_layer_bwd_saved_every_rank(torch, S, D, h, H, Dh, F, Hkv, dtype):
-    """tsp_layer_bwd_ex with the attention output and statistics that
-    tsp_layer_fwd_save kept, held to the same oracle and tolerances."""
-    _layer_bwd_every_rank(torch, S, D, h, H, Dh, F, Hkv, dtype, saved=True)
+@pytest.mark.parametrize("S,D,h,H,Dh,F,Hkv,dtype,keep_z",
+                         [c + (True,) for c in LAYER_BWD_CASES if c[-1] == "bf16"] +
+                         [LAYER_BWD_CASES[1] + (False,)])
+def test_layer_bwd_saved_every_rank(torch, S, D, h, H, Dh, F, Hkv, dtype, keep_z):
+    """tsp_layer_bwd_ex with the attention output and statistics (and the
+    MLP pre-activation, keep_z) that tsp_layer_fwd_save kept, held to the same
+    oracle and tolerances."""
+    _layer_bwd_every_rank(torch, S, D, h, H, Dh, F, Hkv, dtype, saved=True, keep_z=keep_z)
 
 
-def _layer_bwd_every_rank(torch, S, D, h, H, Dh, F, Hkv, dtype, saved):
+def _layer_bwd_every_rank(torch, S, D, h, H, Dh, F, Hkv, dtype, saved, keep_z=False):
     shape = synth.LayerShape(S=S, D=D, h=h, H=H, Dh=Dh, F=F, dtype=dtype, Hkv=Hkv)
     N, Hk = S // D, shape.kv_heads
     w = synth.layer_weights(shape, seed=61, gain="random")
@@ -148,9 +153,9 @@ def _layer_bwd_every_rank(torch, S, D, h, H, Dh, F, Hkv, dtype, saved):
             f"{' from the saved forward' if saved else ''}")
         ga = {**g[r], "wqkv": None, "g_attn": None}
         if saved:
-            o, lse = _saved_forward(torch, shapes[r], wd, xs[r], kd, vd)
+            o, lse, z = _saved_forward(torch, shapes[r], wd, xs[r], kd, vd, keep_z)
             tsp.tsp_layer_bwd_ex(shapes[r], wd, xs[r], kd, vd, dys[r], o, lse, dkf[r], dvf[r], None, None, None, ga,
-                                 tsp.TSP_BWD_ATTN, wss[r])
+                                 tsp.TSP_BWD_ATTN, wss[r], z_saved=z)
         else:
             tsp.tsp_layer_bwd(shapes[r], wd, xs[r], kd, vd, dys[r], dkf[r], dvf[r], None, None, None, ga,
                               tsp.TSP_BWD_ATTN, wss[r])
@@ -246,8 +251,9 @@ def _sample_rows(N, C):
 
 @pytest.mark.parametrize("r,saved", [(0, False), (5, False), (0, True)])
 def test_layer_bwd_7b_sampled_rows(torch, r, saved):
-    """saved: the first half takes the attention output and statistics of
-    tsp_layer_fwd_save instead of running the attention forward again."""
+    """saved: the first half takes the attention output, statistics and MLP
+    pre-activation of tsp_layer_fwd_save instead of running the attention
+    forward and the MLP up product again."""
     shape = synth.SEVEN_B
     S, D, h, H, Dh, F = shape.S, shape.D, shape.h, shape.H, shape.Dh, shape.F
     N, C = S // D, S // (2 * D)
@@ -269,10 +275,10 @@ def test_layer_bwd_7b_sampled_rows(torch, r, saved):
     log(f"layer bwd 7B S={S} D={D} r={r}: both phases, {len(T)} rows of dy{' from the saved forward' if saved else ''}")
     xd = up(x, "f32")
     kd, vd = up(k_rem, "bf16"), up(v_rem, "bf16")
-    o, lse = _saved_forward(torch, s, wd, xd, kd, vd) if saved else (None, None)
+    o, lse, z = _saved_forward(torch, s, wd, xd, kd, vd, True) if saved else (None, None, None)
     tsp.tsp_layer_bwd_ex(s, wd, xd, kd, vd, up(dy, "f32"), o, lse, dkf, dvf, None, None, None,
-                         {**g, "wqkv": None, "g_attn": None}, tsp.TSP_BWD_ATTN, ws)
-    del o, lse, kd, vd
+                         {**g, "wqkv": None, "g_attn": None}, tsp.TSP_BWD_ATTN, ws, z_saved=z)
+    del o, lse, z, kd, vd
     tsp.tsp_layer_bwd(s, wd, xd, None, None, None, None, None, up(dkl, "f32"), up(dvl, "f32"), dx,
                       {**g, "wo": None, "w1": None, "w2": None, "g_mlp": None}, tsp.TSP_BWD_QKV, ws)
     torch.cuda.synchronize()

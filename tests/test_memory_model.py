@@ -93,10 +93,12 @@ def test_training_terms():
     assert trn["backward_peak"] == ((m.S + m.N) * kvw * 4 + _lib_ws(m, tsp.TSP_WS_LAYER_BWD) + 2 * m.N * m.h * 4
                                     + W * 4 * 7 // 8)
     # the training path that keeps each layer's attention output and
-    # statistics (the buffers tsp_layer_fwd_save fills): fp32 O and lse
+    # statistics and its MLP pre-activation (the buffers tsp_layer_fwd_save
+    # fills): fp32 O and lse, Z
     sv = mm.rank_memory(m, train=True, save_attention=True)
     assert sv["saved_attention"] == 32 * (m.N * 4096 + 32 * m.N) * 4
-    assert sv["total"] == trn["total"] + sv["saved_attention"]
+    assert sv["saved_mlp_preact"] == 32 * m.N * 16384 * 2  # Z in bf16
+    assert sv["total"] == trn["total"] + sv["saved_attention"] + sv["saved_mlp_preact"]
 
 
 def test_single_gpu_bytes():

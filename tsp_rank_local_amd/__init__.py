@@ -116,10 +116,10 @@ def lib() -> ctypes.CDLL:
     L.tsp_layer_fwd.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, ctypes.c_uint, vp, sz, vp]
     L.tsp_layer_bwd.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 ctypes.POINTER(TspLayerGrads), ctypes.c_uint, vp, sz, vp]
-    L.tsp_layer_fwd_save.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, vp, vp, ctypes.c_uint, vp,
-                                     sz, vp]
+    L.tsp_layer_fwd_save.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint,
+                                     vp, sz, vp]
     L.tsp_layer_bwd_ex.argtypes = [shp, ctypes.POINTER(TspLayerWeights), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                   ctypes.POINTER(TspLayerGrads), ctypes.c_uint, vp, sz, vp]
+                                   vp, ctypes.POINTER(TspLayerGrads), ctypes.c_uint, vp, sz, vp]
     L.tsp_profile_enable.argtypes = [ctypes.c_int]
     L.tsp_profile_enable.restype = None
     L.tsp_profile_reset.argtypes = []
@@ -285,16 +285,16 @@ def tsp_layer_fwd(shape: TspShape, w: dict, x, k_full, v_full, y, phases, ws, ws
 
 
 def tsp_layer_fwd_save(shape: TspShape, w: dict, x, k_full, v_full, y, o_save, lse_save, phases, ws, ws_bytes=None,
-                       stream=None) -> None:
+                       stream=None, z_save=None) -> None:
     """tsp_layer_fwd that also keeps the attention output o_save [N][H][Dh]
-    and the rows' natural log-sum-exp lse_save [H][N] (fp32) for
-    tsp_layer_bwd_ex."""
+    and the rows' natural log-sum-exp lse_save [H][N] (fp32), and optionally
+    the MLP pre-activation z_save [N][F] (bf16), for tsp_layer_bwd_ex."""
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size()
     cw, keep_w = _weights(w)
     _check(lib().tsp_layer_fwd_save(ctypes.byref(shape), ctypes.byref(cw), _ptr(x), _ptr(k_full), _ptr(v_full),
-                                    _ptr(y), _ptr(o_save), _ptr(lse_save), int(phases), _ptr(ws), int(ws_bytes),
-                                    _stream(stream)))
+                                    _ptr(y), _ptr(o_save), _ptr(lse_save), _ptr(z_save), int(phases), _ptr(ws),
+                                    int(ws_bytes), _stream(stream)))
     del keep_w
 
 
@@ -323,9 +323,9 @@ def tsp_layer_bwd(shape: TspShape, w: dict, x, k_full, v_full, dy, dk_full, dv_f
 
 
 def tsp_layer_bwd_ex(shape: TspShape, w: dict, x, k_full, v_full, dy, o_saved, lse_saved, dk_full, dv_full, dk_loc,
-                     dv_loc, dx, grads: dict, phases, ws, ws_bytes=None, stream=None) -> None:
-    """tsp_layer_bwd with the saved attention output and statistics of
-    tsp_layer_fwd_save (both None: the same as tsp_layer_bwd)."""
+                     dv_loc, dx, grads: dict, phases, ws, ws_bytes=None, stream=None, z_saved=None) -> None:
+    """tsp_layer_bwd with the saved attention output and statistics (and
+    optionally Z) of tsp_layer_fwd_save (all None: the same as tsp_layer_bwd)."""
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size()
     cw, keep_w = _weights(w)
@@ -333,9 +333,9 @@ def tsp_layer_bwd_ex(shape: TspShape, w: dict, x, k_full, v_full, dy, o_saved, l
     cg = TspLayerGrads(_ptr(grads.get("g_attn")), _ptr(grads.get("g_mlp")), garr["wqkv"], garr["wo"], garr["w1"],
                        garr["w2"])
     _check(lib().tsp_layer_bwd_ex(ctypes.byref(shape), ctypes.byref(cw), _ptr(x), _ptr(k_full), _ptr(v_full),
-                                  _ptr(dy), _ptr(o_saved), _ptr(lse_saved), _ptr(dk_full), _ptr(dv_full),
-                                  _ptr(dk_loc), _ptr(dv_loc), _ptr(dx), ctypes.byref(cg), int(phases), _ptr(ws),
-                                  int(ws_bytes), _stream(stream)))
+                                  _ptr(dy), _ptr(o_saved), _ptr(lse_saved), _ptr(z_saved), _ptr(dk_full),
+                                  _ptr(dv_full), _ptr(dk_loc), _ptr(dv_loc), _ptr(dx), ctypes.byref(cg), int(phases),
+                                  _ptr(ws), int(ws_bytes), _stream(stream)))
     del keep_w
 
 

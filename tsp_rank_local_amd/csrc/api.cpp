@@ -724,14 +724,19 @@ tsp_status tsp_mlp_ring_bwd_z(const tsp_shape *s, const void *x, const void *z, 
 // writes its fp32 output and the rows' natural log-sum-exp there for the
 // backward, and the output projection reads O packed from o_save.
 static tsp_status layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const float *x, void *k_full,
-                            void *v_full, float *y, float *o_save, float *lse_save, unsigned phases, void *ws_,
-                            size_t ws_bytes, void *stream_) {
+                            void *v_full, float *y, float *o_save, float *lse_save, void *z_save, unsigned phases,
+                            void *ws_, size_t ws_bytes, void *stream_) {
   tsp_status st = check_layer_shape(s);
   if (st) return st;
   const bool save = o_save != nullptr || lse_save != nullptr;
   if (save && (!o_save || !lse_save)) return fail(TSP_ERR_INVALID_ARG, "o_save and lse_save must both be given");
   if (save && s->dtype != TSP_BF16) return fail(TSP_ERR_UNSUPPORTED, "saving the attention output needs bf16");
   if (save && ((st = check_ptr(o_save, "o_save")) || (st = check_ptr(lse_save, "lse_save")))) return st;
+  if (z_save) {
+    if (!save) return fail(TSP_ERR_INVALID_ARG, "z_save needs o_save and lse_save");
+    if (s->mlp != TSP_MLP_GELU) return fail(TSP_ERR_UNSUPPORTED, "keeping the MLP pre-activation needs the GELU MLP");
+    if ((st = check_ptr(z_save, "z_save"))) return st;
+  }
   if (!w) return fail(TSP_ERR_INVALID_ARG, "weights is NULL");
   if (phases == 0 || (phases & ~3u)) return fail(TSP_ERR_INVALID_ARG, "phases=%u must be 1, 2 or 3", phases);
   if ((st = check_ptr(x, "x")) || (st = check_ptr(k_full, "k_full")) || (st = check_ptr(v_full, "v_full")) ||
@@ -752,8 +757,9 @@ static tsp_status layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, cons
   const Range rk{k_full, (size_t)s->S * hkv * e, "k_full"}, rv{v_full, (size_t)s->S * hkv * e, "v_full"};
   const Range ro{o_save, save ? (size_t)N * h * 4 : 0, "o_save"};
   const Range rl{lse_save, save ? (size_t)s->H * N * 4 : 0, "lse_save"};
-  const Range all[] = {rx, ry, rws, rk, rv, ro, rl};
-  const int n_ranges = save ? 7 : 5;
+  const Range rz{z_save, z_save ? (size_t)N * s->F * 2 : 0, "z_save"};
+  const Range all[] = {rx, ry, rws, rk, rv, ro, rl, rz};
+  const int n_ranges = z_save ? 8 : save ? 7 : 5;
   for (int i = 0; i < n_ranges; ++i)
     for (int j = i + 1; j < n_ranges; ++j)
       if (overlap(all[i], all[j])) return fail(TSP_ERR_INVALID_ARG, "%s overlaps %s", all[i].name, all[j].name);
@@ -813,7 +819,8 @@ static tsp_status layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, cons
     TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(y, w->g_mlp, qbuf, N, h, s->eps, s->dtype, pnl, stream),
                "RMSNorm");
     TSP_LAUNCH(TSP_K_MLP_UP,
-               tsp::launch_mlp_up(s->dtype, qbuf, pnl, N, h, ring_list(w->w1, D, s->r), D, fd, gated, hid, pnl, stream),
+               tsp::launch_mlp_up(s->dtype, qbuf, pnl, N, h, ring_list(w->w1, D, s->r), D, fd, gated, hid, pnl, stream,
+                                  z_save),
                "MLP up");
     TSP_LAUNCH(TSP_K_MLP_DOWN,
                tsp::launch_mlp_down(s->dtype, hid, pnl, N, ring_list(w->w2, D, s->r), D, fd, h, y, y, stream),
@@ -856,15 +863,15 @@ static tsp_status layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, cons
 
 tsp_status tsp_layer_fwd(const tsp_shape *s, const tsp_layer_weights *w, const float *x, void *k_full,
                          void *v_full, float *y, unsigned phases, void *ws, size_t ws_bytes, void *stream) {
-  return layer_fwd(s, w, x, k_full, v_full, y, nullptr, nullptr, phases, ws, ws_bytes, stream);
+  return layer_fwd(s, w, x, k_full, v_full, y, nullptr, nullptr, nullptr, phases, ws, ws_bytes, stream);
 }
 
 tsp_status tsp_layer_fwd_save(const tsp_shape *s, const tsp_layer_weights *w, const float *x, void *k_full,
-                              void *v_full, float *y, float *o_save, float *lse_save, unsigned phases, void *ws,
-                              size_t ws_bytes, void *stream) {
+                              void *v_full, float *y, float *o_save, float *lse_save, void *z_save, unsigned phases,
+                              void *ws, size_t ws_bytes, void *stream) {
   if (!o_save) return fail(TSP_ERR_INVALID_ARG, "o_save is NULL");
   if (!lse_save) return fail(TSP_ERR_INVALID_ARG, "lse_save is NULL");
-  return layer_fwd(s, w, x, k_full, v_full, y, o_save, lse_save, phases, ws, ws_bytes, stream);
+  return layer_fwd(s, w, x, k_full, v_full, y, o_save, lse_save, z_save, phases, ws, ws_bytes, stream);
 }
 
 // The layer backward; with o_saved and lse_saved (bf16, from
@@ -873,7 +880,7 @@ tsp_status tsp_layer_fwd_save(const tsp_shape *s, const tsp_layer_weights *w, co
 // takes the saved output and statistics.
 static tsp_status layer_bwd(const tsp_shape *s, const tsp_layer_weights *w, const float *x, const void *k_full,
                             const void *v_full, const float *dy, const float *o_saved, const float *lse_saved,
-                            float *dk_full, float *dv_full, const float *dk_loc, const float *dv_loc, float *dx,
+                            const void *z_saved, float *dk_full, float *dv_full, const float *dk_loc, const float *dv_loc, float *dx,
                             const tsp_layer_grads *gr, unsigned phases, void *ws_, size_t ws_bytes, void *stream_) {
   tsp_status st = check_layer_bwd_shape(s);
   if (st) return st;
@@ -881,6 +888,10 @@ static tsp_status layer_bwd(const tsp_shape *s, const tsp_layer_weights *w, cons
   if (saved && (!o_saved || !lse_saved)) return fail(TSP_ERR_INVALID_ARG, "o_saved and lse_saved must both be given");
   if (saved && s->dtype != TSP_BF16) return fail(TSP_ERR_UNSUPPORTED, "the saved attention output needs bf16");
   if (saved && ((st = check_ptr(o_saved, "o_saved")) || (st = check_ptr(lse_saved, "lse_saved")))) return st;
+  if (z_saved) {
+    if (!saved) return fail(TSP_ERR_INVALID_ARG, "z_saved needs o_saved and lse_saved");
+    if ((st = check_ptr(z_saved, "z_saved"))) return st;
+  }
   if (!w) return fail(TSP_ERR_INVALID_ARG, "weights is NULL");
   if (!gr) return fail(TSP_ERR_INVALID_ARG, "grads is NULL");
   if (phases == 0 || (phases & ~3u)) return fail(TSP_ERR_INVALID_ARG, "phases=%u must be 1, 2 or 3", phases);
@@ -925,6 +936,7 @@ static tsp_status layer_bwd(const tsp_shape *s, const tsp_layer_weights *w, cons
       in.push_back({o_saved, nh4, "o_saved"});
       in.push_back({lse_saved, (size_t)s->H * N * 4, "lse_saved"});
     }
+    if (z_saved) in.push_back({z_saved, (size_t)N * s->F * 2, "z_saved"});
     out.push_back({dk_full, kvf * 4, "dk_full"});
     out.push_back({dv_full, kvf * 4, "dv_full"});
     out.push_back({gr->g_mlp, (size_t)h * 4, "grads->g_mlp"});
@@ -994,10 +1006,10 @@ static tsp_status layer_bwd(const tsp_shape *s, const tsp_layer_weights *w, cons
     TSP_LAUNCH(TSP_K_OUTPROJ, tsp::launch_outproj(dt, olo, pnl, N, h, to_list(w->wo, D), D, hd, x, h1, stream),
                "output projection");
     TSP_LAUNCH(TSP_K_RMSNORM, tsp::launch_rmsnorm(h1, w->g_mlp, hn, N, h, s->eps, dt, false, stream), "RMSNorm");
-    // MLP branch: dhn, and the ring shards' dW1, dW2
+    // MLP branch: dhn, and the ring shards' dW1, dW2 (Z from the forward when kept)
     TSP_LAUNCH(TSP_K_ROWS_BWD, tsp::launch_pack_cols(dt, dy, nullptr, nullptr, N, 1, h, 0, dylo, false, stream),
                "dy conversion");
-    if ((st = mlp_ring_bwd(s, hn, nullptr, w->w1, w->w2, dylo, nullptr, dhn, gr->w1, gr->w2, ws + L.mlp,
+    if ((st = mlp_ring_bwd(s, hn, z_saved, w->w1, w->w2, dylo, nullptr, dhn, gr->w1, gr->w2, ws + L.mlp,
                            L.mlp_bytes, stream_)))
       return st;
     // dh1 = dy + the second RMSNorm's backward of dhn
@@ -1063,16 +1075,17 @@ tsp_status tsp_layer_bwd(const tsp_shape *s, const tsp_layer_weights *w, const f
                          const void *v_full, const float *dy, float *dk_full, float *dv_full, const float *dk_loc,
                          const float *dv_loc, float *dx, const tsp_layer_grads *gr, unsigned phases, void *ws,
                          size_t ws_bytes, void *stream) {
-  return layer_bwd(s, w, x, k_full, v_full, dy, nullptr, nullptr, dk_full, dv_full, dk_loc, dv_loc, dx, gr, phases, ws,
-                   ws_bytes, stream);
+  return layer_bwd(s, w, x, k_full, v_full, dy, nullptr, nullptr, nullptr, dk_full, dv_full, dk_loc, dv_loc, dx, gr,
+                   phases, ws, ws_bytes, stream);
 }
 
 tsp_status tsp_layer_bwd_ex(const tsp_shape *s, const tsp_layer_weights *w, const float *x, const void *k_full,
                             const void *v_full, const float *dy, const float *o_saved, const float *lse_saved,
-                            float *dk_full, float *dv_full, const float *dk_loc, const float *dv_loc, float *dx,
-                            const tsp_layer_grads *gr, unsigned phases, void *ws, size_t ws_bytes, void *stream) {
-  return layer_bwd(s, w, x, k_full, v_full, dy, o_saved, lse_saved, dk_full, dv_full, dk_loc, dv_loc, dx, gr, phases,
-                   ws, ws_bytes, stream);
+                            const void *z_saved, float *dk_full, float *dv_full, const float *dk_loc,
+                            const float *dv_loc, float *dx, const tsp_layer_grads *gr, unsigned phases, void *ws,
+                            size_t ws_bytes, void *stream) {
+  return layer_bwd(s, w, x, k_full, v_full, dy, o_saved, lse_saved, z_saved, dk_full, dv_full, dk_loc, dv_loc, dx, gr,
+                   phases, ws, ws_bytes, stream);
 }
 
 void tsp_profile_enable(int on) { g_prof.on = on != 0; }

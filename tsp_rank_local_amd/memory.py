@@ -195,9 +195,11 @@ def rank_memory(m: Model, train: bool = False, save_attention: bool = False) -> 
     summed rows the rank gets back, the layer backward's workspace
     (WS_LAYER_BWD), the fp32 output gradient and input gradient [N][h], and
     the fp32 weight gradients of the received shards. save_attention (with
-    train) adds each layer's kept attention output and row statistics, fp32
-    [N][H][Dh] and [H][N], that tsp_layer_fwd_save writes so that
-    tsp_layer_bwd_ex does not run the attention forward again."""
+    train) adds what tsp_layer_fwd_save keeps of each layer for
+    tsp_layer_bwd_ex, so that the backward runs neither the attention
+    forward nor the MLP up product again: the attention output and row
+    statistics, fp32 [N][H][Dh] and [H][N], and the MLP pre-activation Z,
+    [N][F] in dtype."""
     e = _elem(m.dtype)
     W = layer_weight_elems(m)
     kvw = 2 * m.kv_heads * m.Dh  # K and V elements per token
@@ -215,6 +217,7 @@ def rank_memory(m: Model, train: bool = False, save_attention: bool = False) -> 
         out["saved_layer_inputs"] = m.layers * m.N * m.h * 4
         if save_attention:
             out["saved_attention"] = m.layers * (m.N * m.H * m.Dh + m.H * m.N) * 4
+            out["saved_mlp_preact"] = m.layers * m.N * m.F * e
         out["backward_peak"] = ((m.S + m.N) * kvw * 4 + workspace_bytes(m, WS_LAYER_BWD) + 2 * m.N * m.h * 4
                                 + (W * 4 - W * 4 // m.D))
     out["total"] = sum(out.values())
