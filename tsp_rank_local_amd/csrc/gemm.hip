@@ -14,14 +14,18 @@
 // consecutive output columns of one row and every epilogue access is a 16-
 // (fp32) or 8-byte (bf16) vector.
 // K advances 64 at a time through 2 LDS stages (A and B tiles of 256 x 64,
-// 64 KB per stage): tiles go from HBM straight into LDS (buffer_load ... lds,
-// 16 bytes per lane), one block barrier per step. Fragments are read two K
-// slices ahead of their MFMAs, so every read of a stage has been issued
-// after the second slice of its step; the copies of the step two later are
-// then spread over the MFMAs of the last two slices (the copy engine takes
-// about 62 bytes per clock per CU, and a burst within one slice stalled the
-// issuing waves), and the step after that is prefetched into L2 with one
-// dword load per 128-byte line, so the copies mostly hit L2. LDS rows are 128 bytes; the
+// 64 KB per stage; the two A tiles, then the two B tiles, so every fragment
+// read and copy target is a base register plus an immediate): tiles go from
+// HBM straight into LDS (buffer_load ... lds, 16 bytes per lane), one block
+// barrier per step, and the loop is unrolled over the two stages. Fragments
+// are read two K slices ahead of their MFMAs, so every read of a stage has
+// been issued after the second slice of its step; the copies of the step two
+// later then go out two per group of MFMAs over the last two slices. Where a
+// step's tiles come from is advanced one step at a time in scalar registers
+// (the B pointer is read only when a step enters a new segment). Each block
+// also pulls its share of the step after that into L2, one dword load per
+// 128-byte line: the blocks that run together on one XCD share A and B
+// tiles, so each touches only its part of them. LDS rows are 128 bytes; the
 // 16-byte chunk index is XOR-swizzled by (row/2)%8 (the copying lane picks
 // its source chunk), so the lanes that read one chunk of 32 rows spread over
 // all bank groups.
@@ -32,6 +36,7 @@
 // fp32 operands use a plain LDS-tiled FMA kernel (64x64 tiles, 4x4 per thread).
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 #include "tsp_internal.h"
@@ -478,8 +483,9 @@ struct EpiShardF32 {
 struct TileCoord {
   int z, tm, tn;
 };
+constexpr int kTileGM = 4;  // tile rows per group
 __device__ __forceinline__ TileCoord tile_of(int L, int tiles_m, int tiles_n) {
-  constexpr int GM = 4;
+  constexpr int GM = kTileGM;
   const int per_z = tiles_m * tiles_n;
   TileCoord t;
   t.z = L / per_z;
@@ -515,6 +521,33 @@ struct GemmFrags {
   bf16x8 a[4], b[4];
 };
 
+// One 16-byte-per-lane copy into LDS at sbase + IMM (lane i -> +16*i); M0 is
+// set with one add. Same contract as lds_copy16.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int IMM>
+__device__ __forceinline__ void lds_copy16_at(u32x4 rsrc, int voffset, int soffset, uint32_t sbase) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile(
+      "s_add_u32 m0, %3, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voffset), "s"(rsrc), "s"(soffset), "s"(sbase), "n"(IMM)
+      : "memory", "m0", "scc");
+#endif
+}
+#pragma clang diagnostic pop
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <class Epi>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, Epi epi) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -530,10 +563,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, 
   const int wm = wave >> 1, wn = wave & 1;  // wave tile: rows wm*128.., columns wn*128..
   const int g = lane >> 5, l32 = lane & 31;
 
+  // LDS: the A tiles of stages 0 and 1, then the B tiles of stages 0 and 1
+  // (32 KB each), so every fragment read and copy target of a stage is a
+  // base plus an immediate below 64 KB.
   // ---- copy plan: each wave copies windows kWinPerWave*wave.. of the A and
   // B tiles of a step; window w = tile rows 8w..8w+7 (1 KB). Lane -> (row,
   // chunk position); it loads the logical chunk that belongs there.
-  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t wbase = lds_addr(smem) + kWinPerWave * wave * 1024;
   const bool a_panel = a.a_panel != 0;
   const int64_t a_pitch = a_panel ? kPanel : a.lda;  // elements between A rows
   int a_off[kWinPerWave], b_off[kWinPerWave];
@@ -550,92 +586,124 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, 
   const int a_rows = min(kBM, a.M - m0), b_rows = min(kBN, a.N - n0);
   const bf16 *Ab = reinterpret_cast<const bf16 *>(a.A) + (int64_t)m0 * a_pitch;
 
-  // B segment pointers are read from LDS inside the loop: a scalar load
-  // there would turn every wait on the LDS counter into a full wait.
+  // B segment pointers are read from LDS when a step enters a new segment: a
+  // scalar load would turn every wait on the LDS counter into a full wait.
   __shared__ uint64_t bptr_s[TSP_MAX_D];
   if (tid < TSP_MAX_D) bptr_s[tid] = (uint64_t)(uintptr_t)a.B.p[tid];
-  auto seg_of = [&](int kt, int &koff) {
-    const int k0 = kt * kBK;
-    if (a.nz > 1) {
-      koff = k0;
-      return z;
-    }
-    const int seg = k0 / a.kseg;
-    koff = k0 - seg * a.kseg;
-    return seg;
-  };
   auto bptr_at = [&](int seg) {
     const uint64_t v = bptr_s[seg];
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
     return reinterpret_cast<const bf16 *>((uintptr_t)(((uint64_t)hi << 32) | lo));
   };
-  // Where step kt's tiles come from: row-major A keeps one descriptor over
-  // the block's rows and moves along K with soffset; panel A takes one
-  // descriptor per step over the block's rows of that panel.
+  auto b_rsrc = [&](const bf16 *bseg) {
+    if constexpr (kGatedB)  // the tile's rows are spread over the gate and up halves
+      return buffer_rsrc(bseg, (uint32_t)(2 * a.gate_rows * a.ldb * 2));
+    else
+      return buffer_rsrc(bseg + (int64_t)n0 * a.ldb, (uint32_t)(b_rows * a.ldb * 2));
+  };
+  // Where a step's tiles come from, advanced one step at a time: row-major A
+  // keeps one descriptor over the block's rows and moves along K with
+  // soffset; panel A moves the descriptor base by one panel; B moves along K
+  // with soffset inside a segment and takes the next segment's descriptor at
+  // its start.
   struct StepSrc {
     u32x4 ar, br;
     int a_soff, b_soff;
+    const bf16 *a_base;
+    int kt, seg, koff;
   };
-  auto step_src = [&](int kt, const bf16 *bseg, int koff) {
+  auto src_at = [&](int kt) {
     StepSrc t;
-    if constexpr (kGatedB)  // the tile's rows are spread over the gate and up halves
-      t.br = buffer_rsrc(bseg, (uint32_t)(2 * a.gate_rows * a.ldb * 2));
-    else
-      t.br = buffer_rsrc(bseg + (int64_t)n0 * a.ldb, (uint32_t)(b_rows * a.ldb * 2));
-    t.b_soff = koff * 2;
+    t.kt = kt;
+    const int k0 = kt * kBK;
+    t.seg = a.nz > 1 ? z : k0 / a.kseg;
+    t.koff = a.nz > 1 ? k0 : k0 - t.seg * a.kseg;
+    t.br = b_rsrc(reinterpret_cast<const bf16 *>(a.B.p[t.seg]));
+    t.b_soff = t.koff * 2;
     if (a_panel) {
-      t.ar = buffer_rsrc(Ab + (int64_t)kt * a.a_panel, (uint32_t)(a_rows * kRowBytes));
+      t.a_base = Ab + (int64_t)kt * a.a_panel;
+      t.ar = buffer_rsrc(t.a_base, (uint32_t)(a_rows * kRowBytes));
       t.a_soff = 0;
     } else {
+      t.a_base = Ab;
       t.ar = buffer_rsrc(Ab, (uint32_t)(a_rows * a_pitch * 2));
-      t.a_soff = kt * kBK * 2;
+      t.a_soff = k0 * 2;
     }
     return t;
   };
-  // copies of windows 2q, 2q+1 of the A and B tiles into stage st
-  auto copy_part = [&](const StepSrc &t, int st, int q) {
-    const uint32_t base = lds0 + st * kGemmStageBytes;
-#pragma unroll
-    for (int i = 2 * q; i < 2 * q + 2; ++i) {
-      const uint32_t win = kWinPerWave * wave + i;
-      lds_copy16(t.ar, a_off[i], t.a_soff, base + win * 1024);
-      lds_copy16(t.br, b_off[i], t.b_soff, base + kTileBytes + win * 1024);
+  // next step, or the same one past the last step (its copies then land in
+  // a stage nobody reads again)
+  const int KT = a.K / kBK;
+  auto advance = [&](StepSrc &t) {
+    if (t.kt + 1 >= KT) return;
+    ++t.kt;
+    if (a_panel) {
+      t.a_base += a.a_panel;
+      t.ar = buffer_rsrc(t.a_base, (uint32_t)(a_rows * kRowBytes));
+    } else {
+      t.a_soff += kBK * 2;
     }
+    t.koff += kBK;
+    if (a.nz == 1 && t.koff >= a.kseg) {
+      t.koff -= a.kseg;
+      ++t.seg;
+      t.br = b_rsrc(bptr_at(t.seg));
+    }
+    t.b_soff = t.koff * 2;
   };
-  // L2 prefetch of a step's tiles: each lane touches one 128-byte line of the
-  // A tile and one of the B tile (row wave*64 + lane) with a dword load into
-  // a scratch LDS area that nobody reads.
+  // copies of window Q of the A and B tiles of source t into stage ST
+  auto copy_win = [&](const StepSrc &t, auto stc, auto qc) {
+    constexpr int ST = decltype(stc)::value, Q = decltype(qc)::value;
+    lds_copy16_at<ST * kTileBytes + Q * 1024>(t.ar, a_off[Q], t.a_soff, wbase);
+    lds_copy16_at<(2 + ST) * kTileBytes + Q * 1024>(t.br, b_off[Q], t.b_soff, wbase);
+  };
+  // L2 prefetch of a step's tiles, one dword load per 128-byte line into a
+  // scratch LDS area that nobody reads. The blocks that run together on one
+  // XCD come in groups of kTileGM tile rows walked column-major (tile_of):
+  // about min(tiles_n, 8) of them share each A tile and the group's rows
+  // share each B tile, so a block touches only its share of each, A rows
+  // with waves 0 and 2 and B rows with waves 1 and 3 (up to 128 rows each).
+  // Lanes outside the share get an offset past the buffer and touch
+  // nothing; every wave still issues both loads, so the wait counts stay
+  // uniform.
   __shared__ uint32_t pf_sink[64];
   const uint32_t sink = lds_addr(pf_sink);
-  const int pf_va = (wave * 64 + lane) * (int)(a_pitch * 2);
-  const int pf_vb = (kGatedB ? gated_row_blocks(n0 + wave * 64 + lane, a.gate_rows) : wave * 64 + lane) *
-                    (int)(a.ldb * 2);
+  constexpr int kOut = 0x7fffff00;  // past any buffer range
+  const int share_a = min(tiles_n, 8), rows_a = (kBM + share_a - 1) / share_a;
+  const int first_m = tc.tm - tc.tm % kTileGM, share_b = min(tiles_m - first_m, kTileGM);
+  const int rows_b = (kBN + share_b - 1) / share_b;
+  const int pf_r = lane + ((wave >> 1) << 6);  // waves 0, 1: 0..63; waves 2, 3: 64..127
+  const int pf_arow = (tc.tn % share_a) * rows_a + pf_r, pf_brow = (tc.tm - first_m) * rows_b + pf_r;
+  const bool pf_aok = (wave & 1) == 0 && pf_r < rows_a && pf_arow < kBM;
+  const bool pf_bok = (wave & 1) == 1 && pf_r < rows_b && pf_brow < kBN;
+  const int pf_va = pf_aok ? pf_arow * (int)(a_pitch * 2) : kOut;
+  const int pf_vb =
+      pf_bok ? (kGatedB ? gated_row_blocks(n0 + pf_brow, a.gate_rows) : pf_brow) * (int)(a.ldb * 2) : kOut;
   auto prefetch = [&](const StepSrc &t) {
     lds_touch4(t.ar, pf_va, t.a_soff, sink);
     lds_touch4(t.br, pf_vb, t.b_soff, sink);
   };
 
-  // fragment read offsets inside a stage for K slice kk: A rows wm*128 +
-  // j*32 + l32, B rows wn*128 + i*32 + l32, chunk 2*kk + g
-  int fa_a[kGemmSlices][4], fa_b[kGemmSlices][4];
+  // fragment read bases for K slice kk: A rows wm*128 + l32, B rows wn*128 +
+  // l32, chunk 2*kk + g; block i of 32 rows and the stage are immediates (the
+  // swizzle depends on the row modulo 16 only)
+  const unsigned char *fa_a[kGemmSlices], *fa_b[kGemmSlices];
 #pragma unroll
-  for (int kk = 0; kk < kGemmSlices; ++kk)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa_a[kk][i] = gswz(wm * 128 + i * 32 + l32, 2 * kk + g);
-      fa_b[kk][i] = kTileBytes + gswz(wn * 128 + i * 32 + l32, 2 * kk + g);
-    }
+  for (int kk = 0; kk < kGemmSlices; ++kk) {
+    fa_a[kk] = smem + gswz(wm * 128 + l32, 2 * kk + g);
+    fa_b[kk] = smem + 2 * kTileBytes + gswz(wn * 128 + l32, 2 * kk + g);
+  }
   // fragment pair q of K slice kk: q = 0, 1 -> A blocks 2q, 2q+1; q = 2, 3 ->
   // B blocks 2q-4, 2q-3 (the first MFMA row of a slice needs every A block)
-  auto read_pair = [&](GemmFrags &f, int st, int kk, int q) {
-    const unsigned char *sb = smem + st * kGemmStageBytes;
+  auto read_pair = [&](GemmFrags &f, auto stc, int kk, int q) {
+    constexpr int ST = decltype(stc)::value;
     if (q < 2) {
-      f.a[2 * q] = *reinterpret_cast<const bf16x8 *>(sb + fa_a[kk][2 * q]);
-      f.a[2 * q + 1] = *reinterpret_cast<const bf16x8 *>(sb + fa_a[kk][2 * q + 1]);
+      f.a[2 * q] = *reinterpret_cast<const bf16x8 *>(fa_a[kk] + ST * kTileBytes + (2 * q) * 32 * kRowBytes);
+      f.a[2 * q + 1] = *reinterpret_cast<const bf16x8 *>(fa_a[kk] + ST * kTileBytes + (2 * q + 1) * 32 * kRowBytes);
     } else {
-      f.b[2 * q - 4] = *reinterpret_cast<const bf16x8 *>(sb + fa_b[kk][2 * q - 4]);
-      f.b[2 * q - 3] = *reinterpret_cast<const bf16x8 *>(sb + fa_b[kk][2 * q - 3]);
+      f.b[2 * q - 4] = *reinterpret_cast<const bf16x8 *>(fa_b[kk] + ST * kTileBytes + (2 * q - 4) * 32 * kRowBytes);
+      f.b[2 * q - 3] = *reinterpret_cast<const bf16x8 *>(fa_b[kk] + ST * kTileBytes + (2 * q - 3) * 32 * kRowBytes);
     }
   };
 
@@ -651,82 +719,75 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, 
     for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[i], f.a[j], acc[i][j], 0, 0, 0);
   };
 
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
   // ---- prologue: steps 0 and 1 into stages 0 and 1, step 2 towards L2.
-  // Past the last step the copies and prefetches repeat step KT-1 into a
-  // stage nobody reads again, which keeps the loop free of branches.
-  const int KT = a.K / kBK;
-  {
-    int koff;
-    const int s0 = seg_of(0, koff);
-    const StepSrc t0 = step_src(0, reinterpret_cast<const bf16 *>(a.B.p[s0]), koff);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) copy_part(t0, 0, q);
-    const int k1 = min(1, KT - 1);
-    const int s1 = seg_of(k1, koff);
-    const StepSrc t1 = step_src(k1, reinterpret_cast<const bf16 *>(a.B.p[s1]), koff);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) copy_part(t1, 1, q);
-  }
-  __syncthreads();  // bptr_s visible
-  {
-    int koff;
-    const int k2 = min(2, KT - 1);
-    prefetch(step_src(k2, bptr_at(seg_of(k2, koff)), koff));
-  }
+  StepSrc cs = src_at(0);
+  static_for<kWinPerWave>([&](auto q) { copy_win(cs, S0{}, q); });
+  __syncthreads();  // bptr_s visible before advance() may read it
+  advance(cs);
+  static_for<kWinPerWave>([&](auto q) { copy_win(cs, S1{}, q); });
+  advance(cs);  // step 2: copied under step 0, which then moves on to step 3 and prefetches it
+  prefetch(cs);
   wait_vmcnt<2>();
   __syncthreads();
   // fragments two K slices ahead: slice s of a step uses f[s]
   GemmFrags f[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) read_pair(f[0], 0, 0, q);
+  for (int q = 0; q < 4; ++q) read_pair(f[0], S0{}, 0, q);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) read_pair(f[1], 0, 1, q);
+  for (int q = 0; q < 4; ++q) read_pair(f[1], S0{}, 1, q);
 
-  // ---- main loop. Step kt sits in stage kt&1. Slice s runs as 4 groups of
-  // 4 MFMAs on f[s]; slices 0 and 1 read slices 2 and 3 of this step, slices
-  // 2 and 3 read slices 0 and 1 of step kt+1. After slice 1 every read of
-  // stage kt&1 has been issued: the wave waits for them and for its copies
-  // of step kt+1, and the block synchronises; the copies of step kt+2 into
-  // stage kt&1 are then spread over slices 2 and 3 (one part every other
-  // group), and step kt+3 is prefetched into L2 at the end.
-  for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt & 1;
-    int koff2, koff3;
-    const int kc = min(kt + 2, KT - 1), kp = min(kt + 3, KT - 1);
-    const bf16 *bseg2 = bptr_at(seg_of(kc, koff2));
-    const bf16 *bseg3 = bptr_at(seg_of(kp, koff3));
+  // ---- one step in stage ST. Slice s runs as 4 groups of 4 MFMAs on f[s];
+  // slices 0 and 1 read slices 2 and 3 of this step, slices 2 and 3 read
+  // slices 0 and 1 of the next. After slice 1 every read of stage ST has
+  // been issued: the wave waits for them and for its copies of the next step,
+  // and the block synchronises; the copies of the step two later into stage
+  // ST then go out two per MFMA group over slices 2 and 3; the source then
+  // moves on one step, which is prefetched into L2.
+  auto step = [&](auto stc) {
+    constexpr int ST = decltype(stc)::value;
+    using SN = std::integral_constant<int, 1 - ST>;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      read_pair(f[2], st, 2, i);
+      read_pair(f[2], stc, 2, i);
       mfma_row(f[0], i);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      read_pair(f[3], st, 3, i);
+      read_pair(f[3], stc, 3, i);
       mfma_row(f[1], i);
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_vmcnt<2>();
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    const StepSrc tc = step_src(kc, bseg2, koff2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      read_pair(f[0], st ^ 1, 0, i);
-      if ((i & 1) == 0) copy_part(tc, st, i >> 1);
+    static_for<4>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      read_pair(f[0], SN{}, 0, i);
+      copy_win(cs, stc, std::integral_constant<int, i>{});
       mfma_row(f[2], i);
       __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      read_pair(f[1], st ^ 1, 1, i);
-      if ((i & 1) == 0) copy_part(tc, st, 2 + (i >> 1));
-      if (i == 3) prefetch(step_src(kp, bseg3, koff3));
+    });
+    static_for<4>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      read_pair(f[1], SN{}, 1, i);
+      copy_win(cs, stc, std::integral_constant<int, 4 + i>{});
+      if constexpr (i == 3) {
+        advance(cs);
+        prefetch(cs);
+      }
       mfma_row(f[3], i);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
+  };
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    step(S0{});
+    step(S1{});
   }
+  if (kt < KT) step(S0{});
   // no copy may still be landing in LDS when the block exits
   wait_vmcnt<0>();
 
