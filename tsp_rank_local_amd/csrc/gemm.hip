@@ -483,7 +483,8 @@ struct EpiShardF32 {
 struct TileCoord {
   int z, tm, tn;
 };
-constexpr int kTileGM = 4;  // tile rows per group
+constexpr int kTileGM = 4;    // tile rows per group
+constexpr int kXcdBlocks = 32;  // blocks that run together on one XCD (its CUs, one block each)
 __device__ __forceinline__ TileCoord tile_of(int L, int tiles_m, int tiles_n) {
   constexpr int GM = kTileGM;
   const int per_z = tiles_m * tiles_n;
@@ -661,16 +662,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(GemmArgs a, 
   // L2 prefetch of a step's tiles, one dword load per 128-byte line into a
   // scratch LDS area that nobody reads. The blocks that run together on one
   // XCD come in groups of kTileGM tile rows walked column-major (tile_of):
-  // about min(tiles_n, 8) of them share each A tile and the group's rows
-  // share each B tile, so a block touches only its share of each, A rows
-  // with waves 0 and 2 and B rows with waves 1 and 3 (up to 128 rows each).
-  // Lanes outside the share get an offset past the buffer and touch
-  // nothing; every wave still issues both loads, so the wait counts stay
-  // uniform.
+  // about min(tiles_n, kXcdBlocks / kTileGM) of them share each A tile and
+  // the group's rows share each B tile, so a block touches only its share of
+  // each, A rows with waves 0 and 2 and B rows with waves 1 and 3 (up to 128
+  // rows each). Lanes outside the share get an offset past the buffer and
+  // touch nothing; every wave still issues both loads, so the wait counts
+  // stay uniform.
   __shared__ uint32_t pf_sink[64];
   const uint32_t sink = lds_addr(pf_sink);
   constexpr int kOut = 0x7fffff00;  // past any buffer range
-  const int share_a = min(tiles_n, 8), rows_a = (kBM + share_a - 1) / share_a;
+  const int share_a = min(tiles_n, kXcdBlocks / kTileGM), rows_a = (kBM + share_a - 1) / share_a;
   const int first_m = tc.tm - tc.tm % kTileGM, share_b = min(tiles_m - first_m, kTileGM);
   const int rows_b = (kBN + share_b - 1) / share_b;
   const int pf_r = lane + ((wave >> 1) << 6);  // waves 0, 1: 0..63; waves 2, 3: 64..127
