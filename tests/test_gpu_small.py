@@ -192,6 +192,9 @@ MLP_CASES = [
     (2400, 4, 512, 2048, "bf16", True, "swiglu"),  # gated: 64 gate + 64 up columns per 128, ragged rows
     (1024, 2, 256, 128, "bf16", False, "swiglu"),  # gated, F/D = 64: 128 product columns, half a tile
     (4096, 8, 640, 1024, "bf16", True, "swiglu"),
+    (1024, 1, 192, 192, "bf16", True, "gelu"),    # 3 K steps in both products (odd: the loop's lone last step)
+    (1152, 3, 64, 192, "bf16", True, "gelu"),     # 1 K step in the up product; down: 3 steps, a new shard each
+    (1024, 1, 192, 192, "bf16", False, "swiglu"),  # gated, 3 K steps
 ]
 
 
