@@ -392,6 +392,8 @@ def test_tiny_layer_rank_mode_given_remote_kv(torch):
     (2048, 4, 4, 128, 2048, 0.0, 0, "swiglu"),      # gated MLP
     (96, 3, 6, 64, 576, 0.0, 0, "swiglu"),          # gated MLP on the 16 leading rows
     (2048, 4, 8, 128, 2048, 10000.0, 4, "swiglu"),  # rotation, grouped K/V and the gated MLP together
+    (192, 3, 3, 64, 192, 0.0, 0, "gelu"),    # h = 192: 3 K steps in every product, a new W_O / W2 shard every step
+    (192, 3, 3, 64, 192, 0.0, 0, "swiglu"),  # the same with the gated MLP
 ])
 def test_bf16_layer_vs_oracle(torch, S, D, H, Dh, F, rope, Hkv, mlp):
     h = H * Dh
