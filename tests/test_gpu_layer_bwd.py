@@ -94,6 +94,8 @@ LAYER_BWD_CASES = [
     (1280, 2, 384, 6, 64, 768, 0, "bf16"),     # 640 tokens, h = 384, F/D = 384: ragged tiles everywhere
     (2048, 2, 512, 8, 64, 1024, 2, "bf16"),    # grouped K/V: one K/V head per shard
     (2048, 4, 512, 4, 128, 2048, 0, "bf16"),   # 128-wide heads
+    (576, 3, 192, 3, 64, 192, 0, "bf16"),      # 192 tokens, h = F = 192: 3 K steps in every product, a new shard
+                                               # every step in the ring-order ones, 96-row chunks
 ]
 
 
