@@ -230,6 +230,10 @@ ATTN_BWD_CASES = [
     (640, 2, 2, 2, 64, "bf16"),    # chunks of 160: a ragged query tile and step
     (1024, 2, 4, 2, 128, "bf16"),  # two query heads per K/V head
     (256, 1, 2, 2, 128, "bf16"),   # D = 1: plain causal attention
+    # chunks of 100: the dK/dV walks (16 to 100 rows) end inside a 32-row
+    # step and inside a 64-row stage
+    (600, 3, 3, 3, 64, "bf16"),
+    (600, 3, 6, 3, 128, "bf16"),   # and two query heads per K/V head: a walk per head
 ]
 
 

@@ -16,9 +16,10 @@
 //     dS^T. The K^T operand comes from transpose reads of a second copy of the
 //     K tile, laid out for them.
 //  2. dK and dV, key-major: block = 4 waves x 32 keys of one K/V head. It walks
-//     the rank's query rows that can see its keys, 32 at a time, over every
-//     query head that reads the K/V head: S = Q K^T and dP = dO V^T with the
-//     keys on the lanes, P and dS from the row statistics of launch 1, then
+//     the rank's query rows that can see its keys, 32 at a time (staged into
+//     LDS 64 at a time), over every query head that reads the K/V head:
+//     S = Q K^T and dP = dO V^T with the keys on the lanes, P and dS from
+//     the row statistics of launch 1, then
 //     dV^T += dO^T P and dK^T += Q^T dS, whose dO^T and Q^T operands are
 //     transpose reads of the query tiles.
 // When the forward's fp32 O and log-sum-exp are given, a small kernel forms
@@ -561,13 +562,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   using G = BTile<DH>;
   constexpr int ND = DH / 32, NK = DH / 16;
   constexpr int TB = kBwdQ * G::ROWB;
-  // two buffers (steps alternate): Q (ROW), Q (TR), dO (ROW), dO (TR), and
-  // the rows' statistics and positions
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][TB];
+  // Query rows are staged 64 at a time (two steps per pair of block
+  // barriers; one step per pair measured 3-4% slower at 7B) into two
+  // buffers that alternate: Q and dO in the row layout, and the rows'
+  // statistics and positions.
+  constexpr int kStage = 2 * kBwdQ;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][2 * TB];
   // read as float4 / int4 below, so 16-byte alignment is part of the layout
-  __shared__ __attribute__((aligned(16))) float lse_s[2][kBwdQ];
-  __shared__ __attribute__((aligned(16))) float dlt_s[2][kBwdQ];
-  __shared__ __attribute__((aligned(16))) int pos_s[2][kBwdQ];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][kStage];
+  __shared__ __attribute__((aligned(16))) float dlt_s[2][kStage];
+  __shared__ __attribute__((aligned(16))) int pos_s[2][kStage];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const FragOff<DH> fo = frag_off<DH>(lane);
@@ -607,24 +611,24 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   // chains split into even and odd K slices measured 2% slower: their
   // merge costs 32 additions and, with the accumulators in AGPRs, 64 reads
   // back per step)
-  auto scores = [&](int b, f32x16 &sacc, f32x16 &pacc) {
+  auto scores = [&](int b, int sub, f32x16 &sacc, f32x16 &pacc) {
     const f32x16 zero = {};
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][0], fo.row[kk]), kf[kk], kk == 0 ? zero : sacc,
-                                                     0, 0, 0);
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][1], fo.row[kk]), vf[kk], kk == 0 ? zero : pacc,
-                                                     0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][0] + sub * TB, fo.row[kk]), kf[kk],
+                                                     kk == 0 ? zero : sacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(smem[b][1] + sub * TB, fo.row[kk]), vf[kk],
+                                                     kk == 0 ? zero : pacc, 0, 0, 0);
     }
   };
   // sacc[v]: S[row 8*(v/4) + 4*g + v%4][key]. P and dS of the step in buffer
   // b in the B-operand order (rows past the chunk carry position -1, so the
   // masked form zeroes them), then dV^T += dO^T P and dK^T += Q^T dS.
-  auto update = [&](auto masked, int b, const f32x16 &sacc, const f32x16 &pacc) {
+  auto update = [&](auto masked, int b, int sub, const f32x16 &sacc, const f32x16 &pacc) {
     bf16x8 ph[2], dh[2], p_lo[2], ds_lo[2];
 #pragma unroll
     for (int m4 = 0; m4 < 4; ++m4) {
-      const int r = m4 * 8 + g * 4;
+      const int r = sub * kBwdQ + m4 * 8 + g * 4;
       const float4 ls = *reinterpret_cast<const float4 *>(&lse_s[b][r]);
       const float4 dl = *reinterpret_cast<const float4 *>(&dlt_s[b][r]);
       const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, dlv[4] = {dl.x, dl.y, dl.z, dl.w};
@@ -650,7 +654,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
     for (int mu = 0; mu < 2; ++mu)
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
-        const bf16x8 dot = tr_frag<DH>(smem[b][1], fo, db, mu), qt = tr_frag<DH>(smem[b][0], fo, db, mu);
+        const bf16x8 dot = tr_frag<DH>(smem[b][1] + sub * TB, fo, db, mu);
+        const bf16x8 qt = tr_frag<DH>(smem[b][0] + sub * TB, fo, db, mu);
         vacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, ph[mu], vacc[db], 0, 0, 0);
         kacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dh[mu], kacc[db], 0, 0, 0);
         if constexpr (SPLIT) {
@@ -669,12 +674,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       const int t_end = (chh + 1) * a.zz.C;
       const int t_lo = chh * a.zz.C + (int)max<int64_t>(0, kb0 - base);  // first row that sees a key of the block
       if (t_lo >= t_end) continue;
-      TileRegs<DH, kBwdQ> qr, dr;
+      TileRegs<DH, kStage> qr, dr;
       float st_lse = 0.f, st_dlt = 0.f;
-      auto fetch = [&](int t0) {  // a step's rows into registers (statistics: threads < 32)
-        const int nv = min(kBwdQ, t_end - t0);
-        load_tile_buf<DH, kBwdQ>(qr, qg + (int64_t)t0 * rs, (int)rs, nv);
-        load_tile_buf<DH, kBwdQ>(dr, dg + (int64_t)t0 * rs, (int)rs, nv);
+      auto fetch = [&](int t0) {  // a stage's rows into registers (statistics: threads < kStage)
+        const int nv = min(kStage, t_end - t0);
+        load_tile_buf<DH, kStage>(qr, qg + (int64_t)t0 * rs, (int)rs, nv);
+        load_tile_buf<DH, kStage>(dr, dg + (int64_t)t0 * rs, (int)rs, nv);
         const auto lr = __builtin_amdgcn_make_buffer_rsrc((void *)(a.lse + (int64_t)head * a.n + t0), (short)0,
                                                           nv * 4, 0x00020000);
         const auto dr_ = __builtin_amdgcn_make_buffer_rsrc((void *)(a.delta + (int64_t)head * a.n + t0), (short)0,
@@ -683,9 +688,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
         st_dlt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dr_, (int)threadIdx.x * 4, 0, 0));
       };
       auto stage = [&](int b, int t0) {  // the fetched rows into buffer b
-        store_tile<DH, kBwdQ>(smem[b][0], qr);
-        store_tile<DH, kBwdQ>(smem[b][1], dr);
-        if (threadIdx.x < kBwdQ) {
+        store_tile<DH, kStage>(smem[b][0], qr);
+        store_tile<DH, kStage>(smem[b][1], dr);
+        if (threadIdx.x < kStage) {
           const int t = t0 + threadIdx.x;
           const bool ok = t < t_end;
           lse_s[b][threadIdx.x] = ok ? st_lse : 0.f;
@@ -702,14 +707,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       // Software pipeline over the walk's steps: step i's scores are taken
       // one iteration ahead, while step i-1's probabilities and products are
       // formed, so that the exponentials and conversions issue under the
-      // score MFMAs of the next step.
+      // score MFMAs of the next step. The stage after next is fetched into
+      // registers while the current one is in use.
       fetch(t_lo);
       __syncthreads();  // the previous walk's reads of both buffers are done
       stage(0, t_lo);
       __syncthreads();
-      if (t_lo + kBwdQ < t_end) fetch(t_lo + kBwdQ);
+      if (t_lo + kStage < t_end) fetch(t_lo + kStage);
       f32x16 s0, p0, s1, p1;
-      scores(0, s0, p0);
+      scores(0, 0, s0, p0);
       // issue order of the block: each of the 16 score MFMAs followed by
       // five VALU instructions of the update, so that the update's
       // exponentials and conversions run while the matrix core works
@@ -720,33 +726,37 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
           __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
         }
       };
-      // one pipeline iteration: stage step t0 + 32 into buffer b ^ 1, score
-      // it, and finish step t0 (buffer b); returns false after the last step.
-      // The scores and the update share one basic block, so that the
-      // scheduler can interleave them (after the last step the scores read
-      // a stale buffer and are dropped).
-      auto iter = [&](int b, int t0, f32x16 &sc, f32x16 &pc, f32x16 &sn, f32x16 &pn) {
+      // One pipeline iteration: score the next step and finish step t0,
+      // which sits in half `sub` of buffer b; the next step is the other
+      // half of b (sub 0) or the first half of b ^ 1, staged here (sub 1).
+      // Returns false after the last step. The scores and the update share
+      // one basic block, so that the scheduler can interleave them (after
+      // the last step the scores read a stale buffer and are dropped).
+      auto iter = [&](int b, int sub, int t0, f32x16 &sc, f32x16 &pc, f32x16 &sn, f32x16 &pn) {
         const bool next = t0 + kBwdQ < t_end;
-        if (next) {
+        const int nb = sub ? b ^ 1 : b, nsub = sub ^ 1;
+        if (sub && next) {
           __syncthreads();  // every wave is done with buffer b ^ 1
           stage(b ^ 1, t0 + kBwdQ);
           __syncthreads();
-          if (t0 + 2 * kBwdQ < t_end) fetch(t0 + 2 * kBwdQ);
+          if (t0 + kBwdQ + kStage < t_end) fetch(t0 + kBwdQ + kStage);
         }
         if (need_mask(t0)) {
-          scores(b ^ 1, sn, pn);
-          update(std::true_type{}, b, sc, pc);
+          scores(nb, nsub, sn, pn);
+          update(std::true_type{}, b, sub, sc, pc);
           interleave();
         } else {
-          scores(b ^ 1, sn, pn);
-          update(std::false_type{}, b, sc, pc);
+          scores(nb, nsub, sn, pn);
+          update(std::false_type{}, b, sub, sc, pc);
           interleave();
         }
         return next;
       };
-      for (int t0 = t_lo;; t0 += 2 * kBwdQ) {
-        if (!iter(0, t0, s0, p0, s1, p1)) break;
-        if (!iter(1, t0 + kBwdQ, s1, p1, s0, p0)) break;
+      for (int t0 = t_lo;; t0 += 4 * kBwdQ) {
+        if (!iter(0, 0, t0, s0, p0, s1, p1)) break;
+        if (!iter(0, 1, t0 + kBwdQ, s1, p1, s0, p0)) break;
+        if (!iter(1, 0, t0 + 2 * kBwdQ, s0, p0, s1, p1)) break;
+        if (!iter(1, 1, t0 + 3 * kBwdQ, s1, p1, s0, p0)) break;
       }
     }
   }
