@@ -717,14 +717,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       f32x16 s0, p0, s1, p1;
       scores(0, 0, s0, p0);
       // issue order of the block: each of the 16 score MFMAs followed by
-      // four VALU instructions of the update, so that the update's
+      // four VALU instructions of the update (five with P and dS split,
+      // whose update has three conversions per value), so that the update's
       // exponentials and conversions run while the matrix core works (with
-      // 64-row stages three, five and six measured slower)
+      // 64-row stages, three, five and six measured slower for plain P and
+      // dS; four cost the split form 4%)
       auto interleave = [] {
 #pragma unroll
         for (int i = 0; i < 2 * NK; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, SPLIT ? 5 : 4, 0);
         }
       };
       // One pipeline iteration: score the next step and finish step t0,
